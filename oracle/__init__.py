@@ -1,0 +1,242 @@
+"""ctypes front end of the plain C oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests, by the smoke check and by the
+benchmark's CPU-baseline leg.  The product path never imports it.
+
+Arrays are numpy: bf16 tensors travel as uint16 bit patterns.  Weights are
+stored output-major ([out, in]); see oracle.h for every layout.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
+_u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "T", "d_model", "latent", "n_experts", "n_ranks", "top_k", "n_waves",
+        "d_ff", "n_shared", "d_ff_shared", "cap_send", "cap_recv")]
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc (single-threaded, IEEE, no fast-math)."""
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-fPIC", "-shared",
+                           _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(Dims)
+        vp = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        sig = {
+            "orc_bf16_from_double": (ctypes.c_uint16, [ctypes.c_double]),
+            "orc_bf16_to_double": (ctypes.c_double, [ctypes.c_uint16]),
+            "orc_tokens_per_wave": (i32, [i32, i32]),
+            "orc_capacity": (i64, [i64, i32, i32, i64, i64]),
+            "orc_route": (None, [_f32p, i64, i32, i32, _i32p, _f32p]),
+            "orc_latent_rows": (None, [_u16p, i32, _u16p, i32, vp, i64, _u16p]),
+            "orc_sender": (i64, [dp, _i32p, _i32p, _i32p, _i32p, vp]),
+            "orc_pack_rows": (None, [dp, _u16p, _i32p, _i32p, vp, _u8p, i64]),
+            "orc_bank_slots": (i64, [dp, i32, _i32p, vp, i64, vp, _i32p, _i32p,
+                                     _i32p, ctypes.POINTER(i32)]),
+            "orc_bank_rows": (None, [dp, _u8p, vp, _i32p, _i32p, _u16p]),
+            "orc_ffn_row": (None, [i32, i32, _u16p, _u16p, _u16p, _u16p, _u16p]),
+            "orc_expert_ffn": (None, [dp, _u16p, vp, _i32p, _i32p, _u16p, _u16p,
+                                      _u16p, _u16p, i64]),
+            "orc_combine_tokens": (None, [dp, _u16p, vp, _i32p, _i32p, _f32p,
+                                          _u16p, _u16p, _u16p, _u16p, _u16p, vp,
+                                          i64, _u16p, _u16p]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ----------------------------------------------------------------------------
+# dims and sizes
+# ----------------------------------------------------------------------------
+
+def tokens_per_wave(T: int, W: int) -> int:
+    return lib().orc_tokens_per_wave(T, W)
+
+
+def capacity(tokens_per_wave_: int, top_k: int, groups: int, num: int, den: int) -> int:
+    return lib().orc_capacity(tokens_per_wave_, top_k, groups, num, den)
+
+
+def dims(cfg, T=None) -> Dims:
+    """Dims of a workload, capacities from the oracle's own formula."""
+    T = cfg.T if T is None else T
+    tw = tokens_per_wave(T, cfg.n_waves)
+    if cfg.cf_send is None:
+        cs = cr = 0
+    else:
+        cs = capacity(tw, cfg.top_k, cfg.n_ranks, cfg.cf_send.numerator, cfg.cf_send.denominator)
+        cr = capacity(tw, cfg.top_k, cfg.experts_per_rank, cfg.cf_recv.numerator,
+                      cfg.cf_recv.denominator)
+    return Dims(T, cfg.d_model, cfg.latent, cfg.n_experts, cfg.n_ranks, cfg.top_k,
+                cfg.n_waves, cfg.d_ff, cfg.n_shared, cfg.d_ff_shared, cs, cr)
+
+
+def row_bytes(d: Dims) -> int:
+    return d.latent * 2 + 16
+
+
+def n_pool_rows(d: Dims) -> int:
+    return d.n_ranks * d.n_waves * d.cap_send if d.cap_send else d.T * d.top_k
+
+
+def n_bank_rows(d: Dims, n_recv_rows: int) -> int:
+    El = d.n_experts // d.n_ranks
+    return d.n_waves * El * d.cap_recv if d.cap_send else n_recv_rows
+
+
+# ----------------------------------------------------------------------------
+# stages
+# ----------------------------------------------------------------------------
+
+def bf16_from_double(v: float) -> int:
+    return lib().orc_bf16_from_double(v)
+
+
+def bf16_to_double(b: int) -> float:
+    return lib().orc_bf16_to_double(b)
+
+
+def route(logits: np.ndarray, k: int):
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    topk = np.empty((T, k), np.int32)
+    gates = np.empty((T, k), np.float32)
+    lib().orc_route(logits, T, E, k, topk, gates)
+    return topk, gates
+
+
+def latent(x: np.ndarray, w_ld_t: np.ndarray, rows=None) -> np.ndarray:
+    x = np.ascontiguousarray(x, np.uint16)
+    w = np.ascontiguousarray(w_ld_t, np.uint16)
+    L, D = w.shape
+    r = None if rows is None else np.ascontiguousarray(rows, np.int64)
+    n = x.shape[0] if r is None else len(r)
+    z = np.empty((n, L), np.uint16)
+    lib().orc_latent_rows(x, D, w, L, _ptr(r), n, z)
+    return z
+
+
+def sender(d: Dims, topk: np.ndarray):
+    topk = np.ascontiguousarray(topk, np.int32)
+    P = d.n_ranks * d.n_waves
+    slot = np.empty((d.T, d.top_k), np.int32)
+    fill = np.empty(P, np.int32)
+    demand = np.empty(P, np.int32)
+    offs = np.zeros(P + 1, np.int64) if d.cap_send == 0 else None
+    drops = lib().orc_sender(ctypes.byref(d), topk, slot, fill, demand, _ptr(offs))
+    return dict(slot=slot, fill=fill, demand=demand, pool_offsets=offs, drops=drops)
+
+
+def pack_rows(d: Dims, z, topk, slot, pool_offsets=None) -> np.ndarray:
+    n = n_pool_rows(d)
+    pools = np.empty((n, row_bytes(d)), np.uint8)
+    lib().orc_pack_rows(ctypes.byref(d), np.ascontiguousarray(z, np.uint16),
+                        np.ascontiguousarray(topk, np.int32),
+                        np.ascontiguousarray(slot, np.int32), _ptr(pool_offsets),
+                        pools, n)
+    return pools
+
+
+def headers(rows: np.ndarray, latent_: int) -> np.ndarray:
+    """Tail ids of a [n, row_bytes] uint8 array of pool / receive rows."""
+    return np.ascontiguousarray(rows[:, latent_ * 2:latent_ * 2 + 4]).view(np.int32).reshape(-1)
+
+
+def bank_slots(d: Dims, rank: int, hdr: np.ndarray, recv_offsets=None):
+    hdr = np.ascontiguousarray(hdr, np.int32)
+    El = d.n_experts // d.n_ranks
+    G = d.n_waves * El
+    n_recv = len(hdr)
+    nb = n_bank_rows(d, n_recv)
+    bank_src = np.empty(nb, np.int32)
+    bfill = np.empty(G, np.int32)
+    bdemand = np.empty(G, np.int32)
+    boffs = np.zeros(G + 1, np.int64) if d.cap_send == 0 else None
+    bad = ctypes.c_int32(0)
+    ro = None if recv_offsets is None else np.ascontiguousarray(recv_offsets, np.int64)
+    drops = lib().orc_bank_slots(ctypes.byref(d), rank, hdr, _ptr(ro), n_recv,
+                                 _ptr(boffs), bank_src, bfill, bdemand, ctypes.byref(bad))
+    return dict(bank_src=bank_src, bfill=bfill, bdemand=bdemand, bank_offsets=boffs,
+                bad_rows=bad.value, drops=drops)
+
+
+def bank_rows(d: Dims, recv: np.ndarray, bank_offsets, bank_src, bfill) -> np.ndarray:
+    bank = np.zeros((len(bank_src), d.latent), np.uint16)
+    lib().orc_bank_rows(ctypes.byref(d), np.ascontiguousarray(recv, np.uint8),
+                        _ptr(bank_offsets), np.ascontiguousarray(bank_src, np.int32),
+                        np.ascontiguousarray(bfill, np.int32), bank)
+    return bank
+
+
+def ffn_row(u, wg_t, wu_t, wd_t) -> np.ndarray:
+    F, L = wg_t.shape
+    y = np.empty(L, np.uint16)
+    lib().orc_ffn_row(L, F, np.ascontiguousarray(u, np.uint16),
+                      np.ascontiguousarray(wg_t, np.uint16),
+                      np.ascontiguousarray(wu_t, np.uint16),
+                      np.ascontiguousarray(wd_t, np.uint16), y)
+    return y
+
+
+def expert_ffn(d: Dims, bank, bank_offsets, bank_src, bfill, w_gate, w_up, w_down,
+               n_ret_rows: int) -> np.ndarray:
+    ret = np.empty((n_ret_rows, d.latent), np.uint16)
+    lib().orc_expert_ffn(ctypes.byref(d), np.ascontiguousarray(bank, np.uint16),
+                         _ptr(bank_offsets), np.ascontiguousarray(bank_src, np.int32),
+                         np.ascontiguousarray(bfill, np.int32),
+                         np.ascontiguousarray(w_gate, np.uint16),
+                         np.ascontiguousarray(w_up, np.uint16),
+                         np.ascontiguousarray(w_down, np.uint16), ret, n_ret_rows)
+    return ret
+
+
+def combine(d: Dims, returned, ret_offsets, topk, slot, gates, x, w_lu_t,
+            ws_gate, ws_up, ws_down, tokens=None):
+    tk = None if tokens is None else np.ascontiguousarray(tokens, np.int64)
+    n = d.T if tk is None else len(tk)
+    ylat = np.empty((n, d.latent), np.uint16)
+    out = np.empty((n, d.d_model), np.uint16)
+    lib().orc_combine_tokens(
+        ctypes.byref(d), np.ascontiguousarray(returned, np.uint16), _ptr(ret_offsets),
+        np.ascontiguousarray(topk, np.int32), np.ascontiguousarray(slot, np.int32),
+        np.ascontiguousarray(gates, np.float32), np.ascontiguousarray(x, np.uint16),
+        np.ascontiguousarray(w_lu_t, np.uint16), np.ascontiguousarray(ws_gate, np.uint16),
+        np.ascontiguousarray(ws_up, np.uint16), np.ascontiguousarray(ws_down, np.uint16),
+        _ptr(tk), n, ylat, out)
+    return ylat, out

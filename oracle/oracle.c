@@ -1,0 +1,456 @@
+/*
+ * oracle.c -- plain, slow, single-threaded CPU reference of the pooled-wave
+ * MoE dispatch share.  TEST INFRASTRUCTURE ONLY (see oracle.h).
+ *
+ * Every floating-point sum runs in double, in the written loop order, and is
+ * rounded once to the stored type (bf16 with round-to-nearest-even, or fp32).
+ * There is no blocking, fusion or reordering beyond the definitions below.
+ *
+ * Sources, cited by page title and section:
+ *   [P2] "Marin 開始公開訓練 535B 參數 MoE 模型" (lamjinlab.com, zh-HK)
+ *   [P3] "Marin、535BパラメータMoEモデルのオープントレーニングを開始"
+ *        (lamjinlab.com, ja), translation of [P2]
+ *   [P1] "从玩具到前沿:训练一个真正的大模型,到底难在哪里" (devpress.csdn.net)
+ *
+ * Readings of points the pages leave open are marked READING below.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* bf16 conversion                                                          */
+/* ------------------------------------------------------------------------ */
+
+double orc_bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Nearest bf16 to v (ties to even), computed from the double directly so
+ * there is exactly one rounding.  bf16 has 8 significant bits and the fp32
+ * exponent range; below 2^-126 the spacing stays 2^-133 (subnormals). */
+uint16_t orc_bf16_from_double(double v) {
+  if (v != v) return 0x7fc0;
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e); /* a in [2^(e-1), 2^e) */
+  int q = (e - 1 >= -126) ? (e - 1) - 7 : -133;
+  double r = nearbyint(ldexp(a, -q)); /* default rounding mode: ties to even */
+  double res = ldexp(r, q);
+  if (res > 3.3895313892515355e38) return sign | 0x7f80; /* beyond max bf16 */
+  float f = (float)res;                                     /* exact */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return sign | (uint16_t)((u >> 16) & 0x7fff);
+}
+
+static double bf(uint16_t b) { return orc_bf16_to_double(b); }
+static uint16_t to_bf(double v) { return orc_bf16_from_double(v); }
+
+/* ------------------------------------------------------------------------ */
+/* Sizes                                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* READING: the three waves of [P2] section 二 split each shard's tokens into
+ * contiguous thirds: wave(t) = floor(t / T_w) with T_w = ceil(T / W). */
+int32_t orc_tokens_per_wave(int32_t T, int32_t n_waves) {
+  return (T + n_waves - 1) / n_waves;
+}
+
+/* Capacity of one fixed buffer ([P2]/[P3] section 二: a sender factor caps the
+ * rows one source sends to one destination, a receiver factor caps the rows
+ * one local expert takes).  READING: the factor multiplies the mean load of
+ * the buffer for one wave -- T_w*k/R rows per (source, destination) pool and
+ * T_w*k/E_l rows per local expert (R sources times T_w*k/R rows spread over
+ * E_l experts) -- and the product is rounded up.  Exact integers throughout. */
+int64_t orc_capacity(int64_t tokens_per_wave, int32_t top_k, int32_t groups,
+                     int64_t cf_num, int64_t cf_den) {
+  int64_t a = cf_num * tokens_per_wave * (int64_t)top_k;
+  int64_t b = cf_den * (int64_t)groups;
+  return (a + b - 1) / b;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router: softmax over all experts, then the top k                         */
+/* ------------------------------------------------------------------------ */
+
+/* [P2]/[P3] section 二 and [P1] section 四: the router picks 8 of the 384
+ * routed experts per token.  READING: the gate of a chosen expert is its
+ * probability under the softmax over all E logits (no renormalisation over
+ * the k chosen).  Selection runs on the fp32 logits themselves (softmax is
+ * monotone, so this is the same choice) in order of decreasing logit; equal
+ * logits go to the lower expert index.  topk[t, j] is the j-th choice. */
+void orc_route(const float *logits, int64_t T, int32_t E, int32_t k,
+               int32_t *topk, float *gates) {
+  char *taken = (char *)malloc((size_t)E);
+  for (int64_t t = 0; t < T; ++t) {
+    const float *l = logits + t * E;
+    double m = l[0];
+    for (int32_t e = 1; e < E; ++e)
+      if (l[e] > m) m = l[e];
+    double Z = 0.0;
+    for (int32_t e = 0; e < E; ++e) Z += exp((double)l[e] - m);
+    memset(taken, 0, (size_t)E);
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t best = -1;
+      for (int32_t e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || l[e] > l[best]) best = e; /* strict: lower index wins ties */
+      }
+      taken[best] = 1;
+      topk[t * k + j] = best;
+      gates[t * k + j] = (float)(exp((double)l[best] - m) / Z);
+    }
+  }
+  free(taken);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Latent down-projection                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* [P2]/[P3] section 二: the routed activations are projected from the model
+ * width to the latent width before they cross GPUs.  z[t] = x[t] . W_ld,
+ * one rounding to bf16.  rows == NULL means rows 0 .. n-1. */
+void orc_latent_rows(const uint16_t *x, int32_t D, const uint16_t *w_ld_t,
+                     int32_t L, const int64_t *rows, int64_t n, uint16_t *z) {
+  double *xr = (double *)malloc(sizeof(double) * (size_t)D);
+  for (int64_t r = 0; r < n; ++r) {
+    int64_t t = rows ? rows[r] : r;
+    for (int32_t i = 0; i < D; ++i) xr[i] = bf(x[t * D + i]);
+    for (int32_t c = 0; c < L; ++c) {
+      const uint16_t *w = w_ld_t + (int64_t)c * D;
+      double acc = 0.0;
+      for (int32_t i = 0; i < D; ++i) acc += xr[i] * bf(w[i]);
+      z[r * L + c] = to_bf(acc);
+    }
+  }
+  free(xr);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sender: fixed pool per destination and wave                              */
+/* ------------------------------------------------------------------------ */
+
+static int32_t dest_of(const orc_dims *d, int32_t e) {
+  /* READING: experts are placed contiguously, E_l = E / R per rank. */
+  return e / (d->n_experts / d->n_ranks);
+}
+
+/* [P2]/[P3] section 二: one fixed pool per destination GPU (not per expert),
+ * three waves of equal shape, overflow beyond the sender capacity dropped and
+ * counted apart.  [P1] appendix A.3 describes the same fixed per-destination
+ * pools sent in three waves.
+ * Walk the assignments in (token, choice) order; an assignment takes the next
+ * free position of pool (dest(e), wave(t)); it is kept when that position is
+ * below the capacity (always, in ragged mode).  slot[t,j] = position or -1.
+ * fill = kept rows per pool, demand = all rows asked of the pool; pool index
+ * is dest * W + wave.  Ragged mode also writes pool_offsets (exclusive prefix
+ * of demand, plus the total).  Returns the number of dropped assignments. */
+int64_t orc_sender(const orc_dims *d, const int32_t *topk, int32_t *slot,
+                   int32_t *fill, int32_t *demand, int64_t *pool_offsets) {
+  const int32_t W = d->n_waves, R = d->n_ranks, k = d->top_k;
+  const int32_t Tw = orc_tokens_per_wave(d->T, W);
+  const int32_t cap = d->cap_send;
+  int64_t drops = 0;
+  int32_t *n = (int32_t *)calloc((size_t)R * W, sizeof(int32_t));
+  for (int32_t t = 0; t < d->T; ++t) {
+    int32_t w = t / Tw;
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t e = topk[(int64_t)t * k + j];
+      int32_t p = dest_of(d, e) * W + w;
+      int32_t pos = n[p]++;
+      if (cap == 0 || pos < cap) {
+        slot[(int64_t)t * k + j] = pos;
+      } else {
+        slot[(int64_t)t * k + j] = -1;
+        ++drops;
+      }
+    }
+  }
+  for (int32_t p = 0; p < R * W; ++p) {
+    demand[p] = n[p];
+    fill[p] = (cap == 0 || n[p] < cap) ? n[p] : cap;
+  }
+  if (cap == 0 && pool_offsets) {
+    pool_offsets[0] = 0;
+    for (int32_t p = 0; p < R * W; ++p) pool_offsets[p + 1] = pool_offsets[p] + n[p];
+  }
+  free(n);
+  return drops;
+}
+
+/* Row record: latent bf16 values then {expert id, 0, 0, 0}.  [P2]/[P3]
+ * section 二: the expert id travels inside the payload, so no counts or
+ * routing metadata are exchanged.  READING: one row per kept assignment, so a
+ * token with several experts on one rank is sent once per such expert. */
+static void put_header(uint8_t *row, int32_t L, int32_t id) {
+  int32_t h[4] = {id, 0, 0, 0};
+  memcpy(row + (size_t)L * 2, h, 16);
+}
+
+static int32_t get_header(const uint8_t *row, int32_t L) {
+  int32_t id;
+  memcpy(&id, row + (size_t)L * 2, 4);
+  return id;
+}
+
+void orc_pack_rows(const orc_dims *d, const uint16_t *z, const int32_t *topk,
+                   const int32_t *slot, const int64_t *pool_offsets,
+                   uint8_t *pools, int64_t n_pool_rows) {
+  const int32_t L = d->latent, W = d->n_waves, k = d->top_k;
+  const size_t rb = (size_t)L * 2 + 16;
+  const int32_t Tw = orc_tokens_per_wave(d->T, W);
+  for (int64_t r = 0; r < n_pool_rows; ++r) {
+    memset(pools + r * rb, 0, rb - 16);
+    put_header(pools + r * rb, L, -1);
+  }
+  for (int32_t t = 0; t < d->T; ++t) {
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t s = slot[(int64_t)t * k + j];
+      if (s < 0) continue;
+      int32_t e = topk[(int64_t)t * k + j];
+      int32_t p = dest_of(d, e) * W + t / Tw;
+      int64_t row = d->cap_send ? (int64_t)p * d->cap_send + s : pool_offsets[p] + s;
+      memcpy(pools + row * rb, z + (int64_t)t * L, (size_t)L * 2);
+      put_header(pools + row * rb, L, e);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Receiver: bank rows into the local experts                               */
+/* ------------------------------------------------------------------------ */
+
+/* [P2]/[P3] section 二: a receiver factor caps the rows of each local expert;
+ * overflow is dropped and counted apart; the bank holds six local experts
+ * and the three waves keep only part of it live at a time.  [P1] section 四
+ * and appendix A.3: every wave runs all local experts.
+ * READING: the receiver capacity applies per wave and local expert; rows are
+ * taken in (source, row) order within each wave.  hdr[row] is the tail id
+ * of each receive row: -1 = empty (skipped); an id that is not hosted by
+ * `rank` is counted in bad_rows and skipped.  bank_src[pos] = receive row of
+ * bank position pos (-1 where unused).  Returns dropped rows. */
+int64_t orc_bank_slots(const orc_dims *d, int32_t rank, const int32_t *hdr,
+                       const int64_t *recv_offsets, int64_t n_recv_rows,
+                       int64_t *bank_offsets, int32_t *bank_src,
+                       int32_t *bfill, int32_t *bdemand, int32_t *bad_rows) {
+  const int32_t R = d->n_ranks, W = d->n_waves;
+  const int32_t El = d->n_experts / d->n_ranks;
+  const int32_t cap = d->cap_recv;
+  const int ragged = d->cap_send == 0;
+  const int32_t G = W * El;
+  int32_t *c = (int32_t *)calloc((size_t)G, sizeof(int32_t));
+  int32_t bad = 0;
+  /* pass 1: counts */
+  for (int32_t w = 0; w < W; ++w) {
+    for (int32_t s = 0; s < R; ++s) {
+      int64_t a = ragged ? recv_offsets[s * W + w] : ((int64_t)s * W + w) * d->cap_send;
+      int64_t b = ragged ? recv_offsets[s * W + w + 1] : a + d->cap_send;
+      for (int64_t row = a; row < b; ++row) {
+        int32_t h = hdr[row];
+        if (h == -1) continue;
+        if (h < 0 || h >= d->n_experts || h / El != rank) {
+          ++bad;
+          continue;
+        }
+        c[w * El + h % El]++;
+      }
+    }
+  }
+  int64_t drops = 0;
+  for (int32_t g = 0; g < G; ++g) {
+    bdemand[g] = c[g];
+    bfill[g] = (ragged || c[g] < cap) ? c[g] : cap;
+    drops += c[g] - bfill[g];
+  }
+  int64_t n_bank = ragged ? n_recv_rows : (int64_t)G * cap;
+  if (ragged) {
+    bank_offsets[0] = 0;
+    for (int32_t g = 0; g < G; ++g) bank_offsets[g + 1] = bank_offsets[g] + c[g];
+  }
+  for (int64_t i = 0; i < n_bank; ++i) bank_src[i] = -1;
+  /* pass 2: positions in (source, row) order within each wave */
+  memset(c, 0, sizeof(int32_t) * (size_t)G);
+  for (int32_t w = 0; w < W; ++w) {
+    for (int32_t s = 0; s < R; ++s) {
+      int64_t a = ragged ? recv_offsets[s * W + w] : ((int64_t)s * W + w) * d->cap_send;
+      int64_t b = ragged ? recv_offsets[s * W + w + 1] : a + d->cap_send;
+      for (int64_t row = a; row < b; ++row) {
+        int32_t h = hdr[row];
+        if (h < 0 || h >= d->n_experts || h / El != rank) continue;
+        int32_t g = w * El + h % El;
+        int32_t p = c[g]++;
+        if (ragged) bank_src[bank_offsets[g] + p] = (int32_t)row;
+        else if (p < cap) bank_src[(int64_t)g * cap + p] = (int32_t)row;
+      }
+    }
+  }
+  *bad_rows = bad;
+  free(c);
+  return drops;
+}
+
+/* Copy each kept receive row's payload into its bank position. */
+void orc_bank_rows(const orc_dims *d, const uint8_t *recv,
+                   const int64_t *bank_offsets, const int32_t *bank_src,
+                   const int32_t *bfill, uint16_t *bank) {
+  const int32_t L = d->latent;
+  const int32_t G = d->n_waves * (d->n_experts / d->n_ranks);
+  const size_t rb = (size_t)L * 2 + 16;
+  for (int32_t g = 0; g < G; ++g) {
+    int64_t start = d->cap_send ? (int64_t)g * d->cap_recv : bank_offsets[g];
+    for (int32_t p = 0; p < bfill[g]; ++p) {
+      int64_t pos = start + p;
+      memcpy(bank + pos * L, recv + (int64_t)bank_src[pos] * rb, (size_t)L * 2);
+    }
+  }
+}
+
+/* Helper for tests that only have receive headers. */
+int32_t orc_row_header(const uint8_t *row, int32_t L) { return get_header(row, L); }
+
+/* ------------------------------------------------------------------------ */
+/* Expert FFN                                                               */
+/* ------------------------------------------------------------------------ */
+
+static double silu(double a) { return a / (1.0 + exp(-a)); }
+
+/* READING: the pages do not fix the routed expert's form or size; a SwiGLU
+ * is used: h = bf16(silu(u.W_g) * (u.W_u)), y = bf16(h.W_d), silu(a) =
+ * a / (1 + e^-a).  wg_t, wu_t are [F][L] and wd_t is [L][F]. */
+void orc_ffn_row(int32_t L, int32_t F, const uint16_t *u, const uint16_t *wg_t,
+                 const uint16_t *wu_t, const uint16_t *wd_t, uint16_t *y) {
+  double *ud = (double *)malloc(sizeof(double) * (size_t)L);
+  double *h = (double *)malloc(sizeof(double) * (size_t)F);
+  for (int32_t i = 0; i < L; ++i) ud[i] = bf(u[i]);
+  for (int32_t f = 0; f < F; ++f) {
+    double a = 0.0, b = 0.0;
+    const uint16_t *g = wg_t + (int64_t)f * L, *v = wu_t + (int64_t)f * L;
+    for (int32_t i = 0; i < L; ++i) a += ud[i] * bf(g[i]);
+    for (int32_t i = 0; i < L; ++i) b += ud[i] * bf(v[i]);
+    h[f] = bf(to_bf(silu(a) * b));
+  }
+  for (int32_t c = 0; c < L; ++c) {
+    const uint16_t *w = wd_t + (int64_t)c * F;
+    double acc = 0.0;
+    for (int32_t f = 0; f < F; ++f) acc += h[f] * bf(w[f]);
+    y[c] = to_bf(acc);
+  }
+  free(ud);
+  free(h);
+}
+
+/* [P1] section 四 and appendix A.3: each wave the receiver runs all of its
+ * local experts.  Every kept bank row of group (wave, j) goes through local
+ * expert j; the result is written to the return buffer at the row's receive
+ * position (bank_src); every other return row is zero. */
+void orc_expert_ffn(const orc_dims *d, const uint16_t *bank,
+                    const int64_t *bank_offsets, const int32_t *bank_src,
+                    const int32_t *bfill, const uint16_t *w_gate,
+                    const uint16_t *w_up, const uint16_t *w_down,
+                    uint16_t *ret, int64_t n_ret_rows) {
+  const int32_t L = d->latent, F = d->d_ff;
+  const int32_t El = d->n_experts / d->n_ranks;
+  const int32_t G = d->n_waves * El;
+  memset(ret, 0, sizeof(uint16_t) * (size_t)n_ret_rows * (size_t)L);
+  for (int32_t g = 0; g < G; ++g) {
+    int32_t j = g % El;
+    int64_t start = d->cap_send ? (int64_t)g * d->cap_recv : bank_offsets[g];
+    for (int32_t p = 0; p < bfill[g]; ++p) {
+      int64_t pos = start + p;
+      orc_ffn_row(L, F, bank + pos * L, w_gate + (int64_t)j * F * L,
+                  w_up + (int64_t)j * F * L, w_down + (int64_t)j * L * F,
+                  ret + (int64_t)bank_src[pos] * L);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Combine, latent up-projection and shared experts                         */
+/* ------------------------------------------------------------------------ */
+
+/* [P2]/[P3] section 二: the routed outputs are projected back to the model
+ * width and then joined with the shared-expert path; the two shared experts
+ * see every token regardless of routing.  [P2]/[P3] section 四: a dropped
+ * assignment only loses its routed contribution.
+ *   ylat[t] = bf16( sum_j [slot >= 0] g[t,j] * returned[dest(e), wave(t), slot] )
+ *   out[t]  = bf16( ylat[t].W_lu + sum_s h_s(x[t]).W_sd,s ),
+ *   h_s(x)  = bf16( silu(x.W_sg,s) * (x.W_su,s) ),
+ * with the final sum in one double accumulator (W_lu terms, then shared
+ * expert 0, then 1), rounded once.  returned is indexed like the sender's
+ * pools (destination, wave, row).  Ragged mode: ret_offsets holds the segment
+ * offsets in (destination, wave) order; a slot at or past its segment's
+ * length reads as zero.  tokens == NULL means tokens 0 .. n-1; ylat and out
+ * receive n rows. */
+void orc_combine_tokens(const orc_dims *d, const uint16_t *returned,
+                        const int64_t *ret_offsets, const int32_t *topk,
+                        const int32_t *slot, const float *gates,
+                        const uint16_t *x, const uint16_t *w_lu_t,
+                        const uint16_t *ws_gate, const uint16_t *ws_up,
+                        const uint16_t *ws_down, const int64_t *tokens,
+                        int64_t n, uint16_t *ylat, uint16_t *out) {
+  const int32_t L = d->latent, D = d->d_model, k = d->top_k, W = d->n_waves;
+  const int32_t S = d->n_shared, Fs = d->d_ff_shared;
+  const int32_t Tw = orc_tokens_per_wave(d->T, W);
+  double *acc = (double *)malloc(sizeof(double) * (size_t)L);
+  double *yl = (double *)malloc(sizeof(double) * (size_t)L);
+  double *xr = (double *)malloc(sizeof(double) * (size_t)D);
+  double *h = (double *)malloc(sizeof(double) * (size_t)S * Fs);
+  for (int64_t r = 0; r < n; ++r) {
+    int64_t t = tokens ? tokens[r] : r;
+    int32_t w = (int32_t)(t / Tw);
+    for (int32_t c = 0; c < L; ++c) acc[c] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t s = slot[t * k + j];
+      if (s < 0) continue;
+      int32_t e = topk[t * k + j];
+      int32_t seg = dest_of(d, e) * W + w;
+      int64_t row;
+      if (d->cap_send) {
+        row = (int64_t)seg * d->cap_send + s;
+      } else {
+        if (s >= ret_offsets[seg + 1] - ret_offsets[seg]) continue;
+        row = ret_offsets[seg] + s;
+      }
+      double g = gates[t * k + j];
+      for (int32_t c = 0; c < L; ++c) acc[c] += g * bf(returned[row * L + c]);
+    }
+    for (int32_t c = 0; c < L; ++c) {
+      ylat[r * L + c] = to_bf(acc[c]);
+      yl[c] = bf(ylat[r * L + c]);
+    }
+    for (int32_t i = 0; i < D; ++i) xr[i] = bf(x[t * D + i]);
+    for (int32_t sh = 0; sh < S; ++sh) {
+      for (int32_t f = 0; f < Fs; ++f) {
+        const uint16_t *g = ws_gate + ((int64_t)sh * Fs + f) * D;
+        const uint16_t *v = ws_up + ((int64_t)sh * Fs + f) * D;
+        double a = 0.0, b = 0.0;
+        for (int32_t i = 0; i < D; ++i) a += xr[i] * bf(g[i]);
+        for (int32_t i = 0; i < D; ++i) b += xr[i] * bf(v[i]);
+        h[sh * Fs + f] = bf(to_bf(silu(a) * b));
+      }
+    }
+    for (int32_t c = 0; c < D; ++c) {
+      double o = 0.0;
+      const uint16_t *wl = w_lu_t + (int64_t)c * L;
+      for (int32_t i = 0; i < L; ++i) o += yl[i] * bf(wl[i]);
+      for (int32_t sh = 0; sh < S; ++sh) {
+        const uint16_t *wd = ws_down + ((int64_t)sh * D + c) * Fs;
+        for (int32_t f = 0; f < Fs; ++f) o += h[sh * Fs + f] * bf(wd[f]);
+      }
+      out[r * D + c] = to_bf(o);
+    }
+  }
+  free(acc);
+  free(yl);
+  free(xr);
+  free(h);
+}

@@ -1,0 +1,97 @@
+/*
+ * oracle.h -- plain single-threaded CPU reference of one GPU's share of the
+ * pooled-wave MoE dispatch path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  It is called from tests, from the smoke check
+ * and from the CPU-baseline leg of the benchmark, never from the product
+ * path.  It shares no code, header or table with the HIP library.
+ *
+ * Sources, cited by page title and section:
+ *   [P2] "Marin 開始公開訓練 535B 參數 MoE 模型" (lamjinlab.com, zh-HK)
+ *   [P3] "Marin、535BパラメータMoEモデルのオープントレーニングを開始"
+ *        (lamjinlab.com, ja) -- a paragraph-by-paragraph translation of [P2]
+ *   [P1] "从玩具到前沿:训练一个真正的大模型,到底难在哪里" (devpress.csdn.net)
+ *
+ * Layouts (row-major, element units unless stated):
+ *   bf16 values are passed as uint16_t bit patterns.
+ *   Weights are stored output-major ("out x in"): a weight W of the product
+ *   y = x.W with W of shape [in, out] is stored as W^T, shape [out, in].
+ *   A pool / receive row is `latent` bf16 values followed by a 16-byte tail
+ *   {int32 global expert id (-1 = empty slot), 0, 0, 0}.
+ *   Fixed mode (cap_send, cap_recv > 0):
+ *     pools [R][W][cap_send] rows, recv [R_src][W][cap_send] rows,
+ *     bank [W][E_l][cap_recv][latent], ret [R][W][cap_send][latent].
+ *   Ragged mode (cap_send == cap_recv == 0): segments at int64 offsets,
+ *     pools in (dest, wave) order, recv/ret in (source, wave) order,
+ *     bank in (wave, local expert) order; each offsets array has one entry
+ *     per segment plus a final total.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t T, d_model, latent, n_experts, n_ranks, top_k, n_waves, d_ff,
+      n_shared, d_ff_shared, cap_send, cap_recv;
+} orc_dims;
+
+/* bf16 <-> double, round to nearest even, straight from double. */
+uint16_t orc_bf16_from_double(double v);
+double orc_bf16_to_double(uint16_t b);
+
+int32_t orc_tokens_per_wave(int32_t T, int32_t n_waves);
+/* ceil(cf * tokens_per_wave * top_k / groups) in exact integer arithmetic,
+ * cf = cf_num / cf_den.  groups = n_ranks (sender) or E_l (receiver). */
+int64_t orc_capacity(int64_t tokens_per_wave, int32_t top_k, int32_t groups,
+                     int64_t cf_num, int64_t cf_den);
+
+void orc_route(const float *logits, int64_t T, int32_t E, int32_t k,
+               int32_t *topk, float *gates);
+
+void orc_latent_rows(const uint16_t *x, int32_t D, const uint16_t *w_ld_t,
+                     int32_t L, const int64_t *rows, int64_t n, uint16_t *z);
+
+int64_t orc_sender(const orc_dims *d, const int32_t *topk, int32_t *slot,
+                   int32_t *fill, int32_t *demand, int64_t *pool_offsets);
+
+void orc_pack_rows(const orc_dims *d, const uint16_t *z, const int32_t *topk,
+                   const int32_t *slot, const int64_t *pool_offsets,
+                   uint8_t *pools, int64_t n_pool_rows);
+
+int64_t orc_bank_slots(const orc_dims *d, int32_t rank, const int32_t *hdr,
+                       const int64_t *recv_offsets, int64_t n_recv_rows,
+                       int64_t *bank_offsets, int32_t *bank_src,
+                       int32_t *bfill, int32_t *bdemand, int32_t *bad_rows);
+
+/* Tail id of one pool / receive row. */
+int32_t orc_row_header(const uint8_t *row, int32_t L);
+
+void orc_bank_rows(const orc_dims *d, const uint8_t *recv,
+                   const int64_t *bank_offsets, const int32_t *bank_src,
+                   const int32_t *bfill, uint16_t *bank);
+
+void orc_ffn_row(int32_t L, int32_t F, const uint16_t *u, const uint16_t *wg_t,
+                 const uint16_t *wu_t, const uint16_t *wd_t, uint16_t *y);
+
+void orc_expert_ffn(const orc_dims *d, const uint16_t *bank,
+                    const int64_t *bank_offsets, const int32_t *bank_src,
+                    const int32_t *bfill, const uint16_t *w_gate,
+                    const uint16_t *w_up, const uint16_t *w_down,
+                    uint16_t *ret, int64_t n_ret_rows);
+
+void orc_combine_tokens(const orc_dims *d, const uint16_t *returned,
+                        const int64_t *ret_offsets, const int32_t *topk,
+                        const int32_t *slot, const float *gates,
+                        const uint16_t *x, const uint16_t *w_lu_t,
+                        const uint16_t *ws_gate, const uint16_t *ws_up,
+                        const uint16_t *ws_down, const int64_t *tokens,
+                        int64_t n, uint16_t *ylat, uint16_t *out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

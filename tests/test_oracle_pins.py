@@ -1,0 +1,435 @@
+"""Pins of the oracle against facts that do not come from the oracle itself.
+
+Each test checks the C oracle against one of: numbers the pages fix, closed
+forms, library routines (scipy / numpy / torch), O(n^2) brute force on tiny
+inputs, invariants and special cases.  They are chosen so that a plausible
+slip (a transposed weight, a swapped gate/up, an off-by-one in a slot, a
+wrong tie-break, a dropped shared expert) fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from conftest import f64, u16, ulp_diff
+from synth import configs, gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# input generator
+# ----------------------------------------------------------------------------
+
+def test_splitmix64_published_sequence():
+    # First outputs of SplitMix64 seeded with 1234567 (Vigna's reference
+    # implementation, the test vector used by the xoshiro family).
+    want = [6457827717110365317, 3203168211198807973, 9817491932198370423,
+            4593380528125082431, 16408922859458223821]
+    got = [b & ((1 << 64) - 1) for b in gen.uniform_bits(1234567, 0, 5, "cpu").tolist()]
+    assert got == want
+
+
+def test_generator_deterministic_and_normal():
+    a = gen.normal_bf16((1000, 100), 1.0, gen.X, 3)
+    b = gen.normal_bf16((1000, 100), 1.0, gen.X, 3)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    v = a.double()
+    assert abs(v.mean().item()) < 0.01 and abs(v.std().item() - 1) < 0.01
+    c = gen.normal_bf16((1000, 100), 1.0, gen.X, 4)
+    assert not torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+def test_workload_constants_match_pages():
+    g = json.load(open(os.path.join(GOLDEN, "constants.json")))
+    c = configs.SHARE_4K
+    assert (c.n_experts, c.top_k, c.n_shared, c.d_model, c.latent, c.n_ranks,
+            c.experts_per_rank, c.n_waves) == (g["n_experts"], g["top_k"], g["n_shared"],
+                                               g["d_model"], g["latent"], g["n_ranks"],
+                                               g["experts_per_rank"], g["n_waves"])
+    assert c.cf_send == Fraction(g["cf_send"]) and c.cf_recv == Fraction(g["cf_recv"])
+    assert c.T == g["T_start"] and configs.LONG_65K.T == g["T_long"]
+
+
+# ----------------------------------------------------------------------------
+# bf16 rounding
+# ----------------------------------------------------------------------------
+
+def test_bf16_rounding_matches_torch_on_fp32_values(orc):
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-30, 30, 4000),
+                           [0.0, -0.0, 1.0, -1.0, 3.3895313892515355e38, 1e-40, -2e-41]])
+    vals = vals.astype(np.float32)
+    want = u16(torch.from_numpy(vals).to(torch.bfloat16))
+    got = np.array([orc.bf16_from_double(float(v)) for v in vals], np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_bf16_rounding_ties_and_overflow(orc):
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to even -> 1.
+    assert orc.bf16_from_double(1.0 + 2 ** -8) == 0x3F80
+    # 1 + 3*2^-8 is halfway between 1+2^-7 (odd) and 1+2^-6 (even) -> up.
+    assert orc.bf16_from_double(1.0 + 3 * 2 ** -8) == 0x3F82
+    # just above the tie rounds up; a double-rounding through fp32 would not.
+    assert orc.bf16_from_double(1.0 + 2 ** -8 + 2 ** -40) == 0x3F81
+    assert orc.bf16_from_double(1e39) == 0x7F80
+    assert orc.bf16_from_double(-1e39) == 0xFF80
+    assert orc.bf16_to_double(0x3F80) == 1.0
+
+
+# ----------------------------------------------------------------------------
+# capacity
+# ----------------------------------------------------------------------------
+
+def _golden_capacity():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "capacity.txt")):
+        if line.strip() and not line.startswith("#"):
+            rows.append(line.split())
+    return rows
+
+
+def test_capacity_table(orc):
+    for T, Tw, cfs, cs, cfr, cr, R, El in _golden_capacity():
+        T, Tw, cs, cr, R, El = map(int, (T, Tw, cs, cr, R, El))
+        fs, fr = Fraction(cfs), Fraction(cfr)
+        assert orc.tokens_per_wave(T, 3) == Tw
+        assert orc.capacity(Tw, 8, R, fs.numerator, fs.denominator) == cs
+        assert orc.capacity(Tw, 8, El, fr.numerator, fr.denominator) == cr
+        # C is the least integer not below cf * mean load per wave.
+        for C, f, g in ((cs, fs, R), (cr, fr, El)):
+            x = f * Tw * 8 / g
+            assert C >= x and C - 1 < x
+
+
+# ----------------------------------------------------------------------------
+# router
+# ----------------------------------------------------------------------------
+
+def test_route_brute_force_and_ties(orc):
+    rng = np.random.default_rng(1)
+    for trial in range(40):
+        T, E = 5, int(rng.integers(8, 40))
+        k = int(rng.integers(1, min(E, 9)))
+        if trial % 2:   # integer-valued logits force many ties
+            lg = rng.integers(-3, 4, (T, E)).astype(np.float32)
+        else:
+            lg = rng.standard_normal((T, E)).astype(np.float32)
+        topk, gates = orc.route(lg, k)
+        for t in range(T):
+            order = sorted(range(E), key=lambda e: (-float(lg[t, e]), e))
+            assert list(topk[t]) == order[:k]
+        p = scipy.special.softmax(lg.astype(np.float64), axis=1)
+        np.testing.assert_allclose(gates, np.take_along_axis(p, topk, 1), rtol=1e-6)
+
+
+def test_route_special_cases(orc):
+    lg = np.zeros((3, 48), np.float32)
+    topk, gates = orc.route(lg, 8)
+    assert (topk == np.arange(8)).all()
+    assert np.allclose(gates, 1 / 48)
+    rng = np.random.default_rng(2)
+    lg = rng.standard_normal((4, 16)).astype(np.float32)
+    topk, gates = orc.route(lg, 16)                       # k = E: all experts
+    assert all(sorted(r) == list(range(16)) for r in topk.tolist())
+    assert np.allclose(gates.astype(np.float64).sum(1), 1.0, atol=1e-6)
+    # shifting every logit by a constant changes nothing
+    t2, g2 = orc.route(lg + np.float32(8.0), 16)
+    assert (t2 == topk).all() and np.allclose(g2, gates, rtol=1e-5)
+    # the softmax is over all E, not renormalised over the k chosen
+    t3, g3 = orc.route(lg, 2)
+    assert g3.sum(1).max() < 1.0
+
+
+# ----------------------------------------------------------------------------
+# sender pools
+# ----------------------------------------------------------------------------
+
+def _tiny_dims(orc, T=23, E=12, R=4, k=3, W=3, cs=4, cr=5, L=8):
+    return orc.Dims(T, 16, L, E, R, k, W, 16, 2, 16, cs, cr)
+
+
+def _rand_topk(rng, T, E, k):
+    return np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+
+
+def test_sender_brute_force(orc):
+    rng = np.random.default_rng(3)
+    for cs in (1, 2, 4, 7, 0):
+        d = _tiny_dims(orc, cs=cs, cr=0 if cs == 0 else 5)
+        topk = _rand_topk(rng, d.T, d.n_experts, d.top_k)
+        r = orc.sender(d, topk)
+        El, Tw = d.n_experts // d.n_ranks, math.ceil(d.T / d.n_waves)
+        items = [(t, j) for t in range(d.T) for j in range(d.top_k)]
+        key = {(t, j): (int(topk[t, j]) // El, t // Tw) for t, j in items}
+        drops = 0
+        for n, (t, j) in enumerate(items):
+            pos = sum(1 for (t2, j2) in items[:n] if key[(t2, j2)] == key[(t, j)])
+            want = pos if (cs == 0 or pos < cs) else -1
+            drops += want < 0
+            assert r["slot"][t, j] == want
+        assert r["drops"] == drops
+        dem = np.zeros(d.n_ranks * d.n_waves, int)
+        for v in key.values():
+            dem[v[0] * d.n_waves + v[1]] += 1
+        assert (r["demand"] == dem).all()
+        assert (r["fill"] == (dem if cs == 0 else np.minimum(dem, cs))).all()
+        assert r["fill"].sum() + r["drops"] == d.T * d.top_k
+
+
+def test_sender_ragged_is_stable_counting_sort(orc):
+    rng = np.random.default_rng(4)
+    d = _tiny_dims(orc, T=50, cs=0, cr=0)
+    topk = _rand_topk(rng, d.T, d.n_experts, d.top_k)
+    r = orc.sender(d, topk)
+    assert r["drops"] == 0 and (r["slot"] >= 0).all()
+    El, Tw = d.n_experts // d.n_ranks, math.ceil(d.T / d.n_waves)
+    keys = ((topk // El) * d.n_waves + (np.arange(d.T) // Tw)[:, None]).reshape(-1)
+    order = np.argsort(keys, kind="stable")
+    pos = np.empty_like(order)
+    pos[order] = np.arange(len(order))
+    offs = r["pool_offsets"]
+    assert (offs == np.concatenate([[0], np.cumsum(np.bincount(keys, minlength=len(offs) - 1))])).all()
+    assert ((offs[keys] + r["slot"].reshape(-1)) == pos).all()
+
+
+def test_sender_nesting_and_suffix(orc):
+    rng = np.random.default_rng(5)
+    d0 = _tiny_dims(orc, T=60)
+    topk = _rand_topk(rng, d0.T, d0.n_experts, d0.top_k)
+    prev = None
+    for cs in range(1, 30):
+        d = _tiny_dims(orc, T=60, cs=cs)
+        keep = orc.sender(d, topk)["slot"] >= 0
+        if prev is not None:
+            assert (keep | ~prev).all()          # raising C never drops a kept item
+        prev = keep
+    # drops are a suffix of each pool's order
+    d = _tiny_dims(orc, T=60, cs=3)
+    slot = orc.sender(d, topk)["slot"]
+    El, Tw = d.n_experts // d.n_ranks, math.ceil(d.T / d.n_waves)
+    seen_drop = {}
+    for t in range(d.T):
+        for j in range(d.top_k):
+            p = (int(topk[t, j]) // El, t // Tw)
+            if slot[t, j] < 0:
+                seen_drop[p] = True
+            else:
+                assert not seen_drop.get(p, False)
+
+
+def test_pack_rows_content(orc):
+    rng = np.random.default_rng(6)
+    d = _tiny_dims(orc, T=30, cs=4)
+    topk = _rand_topk(rng, d.T, d.n_experts, d.top_k)
+    z = rng.integers(0, 2 ** 16, (d.T, d.latent)).astype(np.uint16)
+    s = orc.sender(d, topk)
+    pools = orc.pack_rows(d, z, topk, s["slot"])
+    hdr = orc.headers(pools, d.latent)
+    El, Tw = d.n_experts // d.n_ranks, math.ceil(d.T / d.n_waves)
+    used = np.zeros(len(pools), bool)
+    for t in range(d.T):
+        for j in range(d.top_k):
+            if s["slot"][t, j] < 0:
+                continue
+            row = ((topk[t, j] // El) * d.n_waves + t // Tw) * d.cap_send + s["slot"][t, j]
+            assert hdr[row] == topk[t, j]
+            assert (pools[row, :d.latent * 2].view(np.uint16) == z[t]).all()
+            assert not used[row]
+            used[row] = True
+    assert (hdr[~used] == -1).all()
+    assert (pools[:, d.latent * 2 + 4:] == 0).all()
+
+
+# ----------------------------------------------------------------------------
+# receiver bank
+# ----------------------------------------------------------------------------
+
+def _rand_headers(rng, d, rank, n_rows, p_empty=0.2, p_bad=0.05):
+    El = d.n_experts // d.n_ranks
+    h = (rank * El + rng.integers(0, El, n_rows)).astype(np.int32)
+    h[rng.random(n_rows) < p_empty] = -1
+    bad = rng.random(n_rows) < p_bad
+    h[bad] = ((rank + 1) % d.n_ranks) * El
+    return h, int(bad.sum())
+
+
+def test_bank_brute_force(orc):
+    rng = np.random.default_rng(7)
+    for cr in (1, 3, 6, 50):
+        d = _tiny_dims(orc, cs=5, cr=cr)
+        rank = 2
+        n = d.n_ranks * d.n_waves * d.cap_send
+        hdr, nbad = _rand_headers(rng, d, rank, n)
+        r = orc.bank_slots(d, rank, hdr)
+        El, W, Cs = d.n_experts // d.n_ranks, d.n_waves, d.cap_send
+        assert r["bad_rows"] == nbad
+        want_src = -np.ones(W * El * cr, np.int64)
+        order = [(w, s, i) for w in range(W) for s in range(d.n_ranks) for i in range(Cs)]
+        valid = lambda row: hdr[row] >= 0 and hdr[row] // El == rank
+        rowof = lambda w, s, i: (s * W + w) * Cs + i
+        cnt = np.zeros(W * El, int)
+        for n_, (w, s, i) in enumerate(order):
+            row = rowof(w, s, i)
+            if not valid(row):
+                continue
+            g = w * El + hdr[row] % El
+            pos = sum(1 for (w2, s2, i2) in order[:n_]
+                      if valid(rowof(w2, s2, i2)) and w2 * El + hdr[rowof(w2, s2, i2)] % El == g)
+            cnt[g] += 1
+            if pos < cr:
+                want_src[g * cr + pos] = row
+        assert (r["bank_src"] == want_src).all()
+        assert (r["bdemand"] == cnt).all()
+        assert (r["bfill"] == np.minimum(cnt, cr)).all()
+        assert r["drops"] == (cnt - np.minimum(cnt, cr)).sum()
+
+
+def test_bank_ragged_no_drops_and_rows(orc):
+    rng = np.random.default_rng(8)
+    d = _tiny_dims(orc, cs=0, cr=0)
+    rank, R, W = 1, d.n_ranks, d.n_waves
+    seg = rng.integers(0, 9, R * W)
+    offs = np.concatenate([[0], np.cumsum(seg)]).astype(np.int64)
+    n = int(offs[-1])
+    hdr, _ = _rand_headers(rng, d, rank, n, p_empty=0.0, p_bad=0.0)
+    r = orc.bank_slots(d, rank, hdr, offs)
+    assert r["drops"] == 0 and r["bad_rows"] == 0
+    assert (r["bfill"] == r["bdemand"]).all() and r["bfill"].sum() == n
+    assert sorted(r["bank_src"].tolist()) == list(range(n))
+    # rows are copied verbatim
+    recv = rng.integers(0, 256, (n, d.latent * 2 + 16)).astype(np.uint8)
+    recv[:, d.latent * 2:d.latent * 2 + 4] = hdr.view(np.uint8).reshape(n, 4)
+    bank = orc.bank_rows(d, recv, r["bank_offsets"], r["bank_src"], r["bfill"])
+    for pos, row in enumerate(r["bank_src"]):
+        assert (bank[pos] == recv[row, :d.latent * 2].view(np.uint16)).all()
+
+
+# ----------------------------------------------------------------------------
+# GEMM stages: latent, FFN, combine
+# ----------------------------------------------------------------------------
+
+def _bits(a):
+    return u16(torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16))
+
+
+def test_latent_identity_and_library(orc):
+    rng = np.random.default_rng(9)
+    T, D, L = 7, 24, 16
+    x = _bits(rng.standard_normal((T, D)))
+    eye = np.zeros((L, D), np.float32)
+    eye[np.arange(L), np.arange(L)] = 1.0                 # W_ld = [I; 0]
+    z = orc.latent(x, _bits(eye))
+    assert (z == x[:, :L]).all()
+    w = _bits(rng.standard_normal((L, D)) / 5)
+    z = orc.latent(x, w)
+    ref = _bits(f64(x) @ f64(w).T)                        # numpy float64 product
+    assert ulp_diff(z, ref).max() <= 1
+    z2 = orc.latent(x, w, rows=[6, 0])
+    assert (z2 == z[[6, 0]]).all()
+    assert (orc.latent(np.zeros_like(x), w) == 0).all()
+
+
+def _eye_bits(rows, cols, scale=1.0):
+    m = np.zeros((rows, cols), np.float32)
+    n = min(rows, cols)
+    m[np.arange(n), np.arange(n)] = scale
+    return _bits(m)
+
+
+def test_ffn_swiglu_closed_forms(orc):
+    L, F = 8, 8
+    u = _bits(np.eye(L)[0])                               # u = e_0
+    alpha = np.array([0, 1, 64, -64, 2, 1, 0.5, -1], np.float32)
+    beta = np.array([5, 1, 2, 3, 0, -1, 4, 2], np.float32)
+    wg = np.zeros((F, L), np.float32); wg[:, 0] = alpha   # a_f = alpha_f
+    wu = np.zeros((F, L), np.float32); wu[:, 0] = beta    # b_f = beta_f
+    y = orc.ffn_row(u, _bits(wg), _bits(wu), _eye_bits(L, F))   # W_d = I: y = h
+    sig1 = 0.7310585786300049                             # 1/(1+e^-1)
+    sig2 = 0.8807970779778823                             # 1/(1+e^-2)
+    want = [0.0, sig1, 128.0, -64 * 3 * math.exp(-64), 0.0, -sig1, 0.5 / (1 + math.exp(-0.5)) * 4,
+            -(1 - sig1) * 2]
+    assert (y == _bits(np.array(want, np.float64))).all(), (f64(y), want)
+    # gate and up are not interchangeable: silu(2)*0 != silu(0)*2 is trivial, use (64, 2)
+    assert f64(y)[2] == 128.0 and abs(2 * sig2 * 64 - 128.0) > 10
+    # scaling W_d by 2 scales y by exactly 2
+    y2 = orc.ffn_row(u, _bits(wg), _bits(wu), _eye_bits(L, F, 2.0))
+    assert np.array_equal(f64(y2), 2 * f64(y))
+
+
+def test_ffn_second_product_orientation(orc):
+    rng = np.random.default_rng(10)
+    L, F = 6, 10
+    u = _bits(rng.standard_normal(L))
+    wg = _bits(rng.standard_normal((F, L)))
+    wu = _bits(rng.standard_normal((F, L)))
+    wd = np.zeros((L, F), np.float32)
+    wd[2, 7] = 1.0                                        # y[2] = h[7], rest 0
+    y = orc.ffn_row(u, wg, wu, _bits(wd))
+    e7 = np.zeros((L, F), np.float32); e7[0, 7] = 1.0
+    h7 = orc.ffn_row(u, wg, wu, _bits(e7))[0]
+    assert y[2] == h7 and (np.delete(y, 2) == 0).all()
+    a = f64(u) @ f64(wg)[7]
+    b = f64(u) @ f64(wu)[7]
+    ref = a * scipy.special.expit(a) * b                  # silu via scipy's logistic
+    assert ulp_diff(np.array([h7]), _bits([ref]))[0] <= 1
+
+
+def test_combine_special_cases(orc):
+    rng = np.random.default_rng(11)
+    T, D, L, E, R, k, W, S, Fs = 6, 16, 8, 12, 4, 3, 3, 2, 8
+    d = orc.Dims(T, D, L, E, R, k, W, 8, S, Fs, 2, 4)
+    El, Tw = E // R, math.ceil(T / W)
+    topk = _rand_topk(rng, T, E, k)
+    gates = rng.random((T, k)).astype(np.float32)
+    slot = rng.integers(-1, 2, (T, k)).astype(np.int32)
+    returned = _bits(rng.standard_normal((R * W * 2, L)))
+    x = _bits(rng.standard_normal((T, D)))
+    zero_sd = np.zeros((S, D, Fs), np.uint16)
+    wsg = _bits(rng.standard_normal((S, Fs, D)))
+    wsu = _bits(rng.standard_normal((S, Fs, D)))
+    ylat, out = orc.combine(d, returned, None, topk, slot, gates, x, _eye_bits(D, L),
+                            wsg, wsu, zero_sd)
+    for t in range(T):
+        acc = np.zeros(L)
+        for j in range(k):
+            if slot[t, j] >= 0:
+                row = ((topk[t, j] // El) * W + t // Tw) * 2 + slot[t, j]
+                acc += float(gates[t, j]) * f64(returned[row])
+        assert ulp_diff(ylat[t], _bits(acc)).max() <= 1
+    # W_lu = [I; 0], shared down = 0  ->  out = [ylat, 0]
+    assert (out[:, :L] == ylat).all() and (out[:, L:] == 0).all()
+    # every assignment dropped -> ylat = 0 and out = shared path only
+    ylat0, out0 = orc.combine(d, returned, None, topk, -np.ones_like(slot), gates, x,
+                              _eye_bits(D, L), wsg, wsu, _bits(rng.standard_normal((S, D, Fs))))
+    assert (ylat0 == 0).all() and (out0 != 0).any()
+    # shared experts with W_sd = I pick up h_s: shared expert s=1 alone
+    sd = np.zeros((S, D, Fs), np.float32); sd[1, np.arange(Fs), np.arange(Fs)] = 1
+    _, out1 = orc.combine(d, returned, None, topk, -np.ones_like(slot), gates, x,
+                          _eye_bits(D, L), wsg, wsu, _bits(sd))
+    a = f64(x) @ f64(wsg[1]).T
+    b = f64(x) @ f64(wsu[1]).T
+    href = _bits(a * scipy.special.expit(a) * b)
+    assert ulp_diff(out1[:, :Fs], href).max() <= 1 and (out1[:, Fs:] == 0).all()
+
+
+def test_combine_ragged_bounds(orc):
+    T, D, L, E, R, k, W, S, Fs = 3, 8, 4, 8, 2, 2, 1, 1, 4
+    d = orc.Dims(T, D, L, E, R, k, W, 4, S, Fs, 0, 0)
+    topk = np.array([[0, 4], [1, 5], [2, 6]], np.int32)  # dest 0 and dest 1
+    slot = np.array([[0, 0], [1, 5], [2, 1]], np.int32)
+    gates = np.ones((T, k), np.float32)
+    offs = np.array([0, 3, 5], np.int64)                 # seg 0: 3 rows, seg 1: 2 rows
+    returned = _bits(np.arange(5 * L).reshape(5, L) + 1.0)
+    ylat, _ = orc.combine(d, returned, offs, topk, slot, gates, np.zeros((T, D), np.uint16),
+                          np.zeros((D, L), np.uint16), np.zeros((S, Fs, D), np.uint16),
+                          np.zeros((S, Fs, D), np.uint16), np.zeros((S, D, Fs), np.uint16))
+    r = f64(returned)
+    assert np.array_equal(f64(ylat[0]), r[0] + r[3])
+    assert np.array_equal(f64(ylat[1]), r[1])            # slot 5 >= len 2 -> zero
+    assert np.array_equal(f64(ylat[2]), r[2] + r[4])
