@@ -1,0 +1,301 @@
+"""Benchmark: routed tokens/s through one MI355X's share of the pooled-wave
+MoE layer (route -> pack_waves -> bank -> expert_ffn -> combine), with the
+roofline position of the dominant kernel and the oracle timed on the host.
+
+One step = the whole path for one rank over one source shard of T tokens:
+route the shard's logits, project and pack its pools, bank the receive
+buffer (pools that all source shards packed for this rank -- built once,
+untimed, by a device-copy loopback that stands in for the all-to-all),
+run the six local experts, and combine (identity return loopback).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--rank R]
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class State:
+    pass
+
+
+def setup(cfg, rank=0, device="cuda", seed=0, progress=False):
+    """Inputs in HBM for one rank: its own shard, its experts' weights, and
+    the receive buffer made from every source shard's pools (loopback)."""
+    import torch
+    from dispatch_softmax_top_amd import share
+    from synth import gen
+
+    st = State()
+    st.cfg, st.rank = cfg, rank
+    d = st.d = share.make_dims(cfg)
+    st.wr = gen.router_weight(cfg, device, seed)
+    st.wld = gen.latent_down(cfg, device, seed)
+    st.wg, st.wu, st.wd = gen.rank_experts(cfg, rank, device, seed)
+    st.wlu = gen.latent_up(cfg, device, seed)
+    st.wsg, st.wsu, st.wsd = gen.shared(cfg, device, seed)
+
+    snd = share.Sender(d, device)
+    R, W = d.n_ranks, d.n_waves
+    st.sent_demand = 0
+    st.sent_fill = 0
+    if d.cap_send:
+        st.n_recv_rows = R * W * d.cap_send
+        st.recv = torch.empty(st.n_recv_rows, share.row_bytes(d), dtype=torch.uint8,
+                              device=device)
+        rv = st.recv.view(R, W, d.cap_send, -1)
+    else:
+        parts, lens = [], []
+    t0 = time.time()
+    for s in range(cfg.n_shards):
+        x = gen.hidden(cfg, s, device, seed)
+        lg = gen.logits(cfg, s, x, st.wr, seed)
+        snd.route(lg)
+        snd.pack(x, st.wld)
+        st.sent_demand += int(snd.demand.sum())
+        st.sent_fill += int(snd.fill.sum())
+        if d.cap_send:
+            rv[s].copy_(snd.pools.view(R, W, d.cap_send, -1)[rank])
+        else:
+            o = snd.pool_offsets.cpu().tolist()
+            for w in range(W):
+                a, b = o[rank * W + w], o[rank * W + w + 1]
+                parts.append(snd.pools[a:b].clone())
+                lens.append(b - a)
+        if s == rank:
+            st.x, st.logits = x, lg
+        if progress and (s % 16 == 15 or s == cfg.n_shards - 1):
+            log(f"setup: shard {s + 1}/{cfg.n_shards} packed ({time.time() - t0:.1f}s)")
+    if d.cap_send:
+        st.recv_offsets = None
+    else:
+        st.recv = torch.cat(parts)
+        st.n_recv_rows = st.recv.shape[0]
+        import itertools
+        st.recv_offsets = torch.tensor([0] + list(itertools.accumulate(lens)),
+                                       dtype=torch.int64, device=device)
+    st.snd = share.Sender(d, device)
+    st.rcv = share.Receiver(d, st.n_recv_rows, device)
+    st.cmb = share.Combiner(d, device)
+    torch.cuda.synchronize()
+    return st
+
+
+def step(st):
+    st.snd.route(st.logits)
+    st.snd.pack(st.x, st.wld)
+    st.rcv.bank_rows(st.rank, st.recv, st.recv_offsets)
+    st.rcv.ffn(st.wg, st.wu, st.wd)
+    st.cmb.combine(st.rcv.ret, st.recv_offsets, st.snd, st.x, st.wlu, st.wsg, st.wsu, st.wsd)
+
+
+def algorithmic_work(st):
+    """Per-kernel algorithmic flops / bytes of one step from the actual counts."""
+    d = st.d
+    T, k, L, D, F, S, Fs = d.T, d.top_k, d.latent, d.d_model, d.d_ff, d.n_shared, d.d_ff_shared
+    kept_s = int(st.snd.fill.sum())
+    n_slots = int(st.snd.pools.shape[0])
+    kept_r = int(st.rcv.bfill.sum())
+    w = {}
+    w["gemm_latent_down"] = ("flop", 2.0 * T * D * L)
+    w["gemm_expert_swiglu"] = ("flop", 4.0 * kept_r * L * F)
+    w["gemm_expert_down"] = ("flop", 2.0 * kept_r * F * L)
+    w["gemm_shared_swiglu"] = ("flop", 4.0 * T * D * S * Fs)
+    w["gemm_up_shared"] = ("flop", 2.0 * T * (L + S * Fs) * D)
+    w["route_topk_softmax"] = ("byte", T * d.n_experts * 4.0 + T * k * 8.0)
+    w["pack_rows"] = ("byte", T * L * 2.0 + kept_s * (2 * L + 16) + (n_slots - kept_s) * 16.0)
+    w["bank_rows"] = ("byte", 2.0 * kept_r * 2 * L)
+    w["combine_gather"] = ("byte", kept_s * 2.0 * L + T * k * 8.0 + T * L * 2.0)
+    return w
+
+
+def _u16(t):
+    import numpy as np
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def run_cpu_baseline(st, rows=(32, 96, 16)):
+    """Oracle timing on the host.  Sample: route + sender slots of the whole
+    shard (full), latent rows for `rows[0]` tokens, expert FFN for `rows[1]`
+    bank rows, combine (gather + up-projection + shared experts) for
+    `rows[2]` tokens; each sampled stage is scaled linearly to its full row
+    count.  Returns (tokens/s, description)."""
+    import numpy as np
+    import oracle as orc
+    cfg = st.cfg
+    dd = orc.dims(cfg)
+    lg = st.logits.cpu().numpy()
+    x = _u16(st.x)
+    est = 0.0
+    t0 = time.perf_counter()
+    topk, gates = orc.route(lg, cfg.top_k)
+    snd = orc.sender(dd, topk)
+    t1 = time.perf_counter()
+    est += t1 - t0
+    rng = np.random.default_rng(0)
+    toks = rng.choice(cfg.T, rows[0], replace=False)
+    wld = _u16(st.wld)
+    t0 = time.perf_counter()
+    orc.latent(x, wld, rows=toks)
+    t1 = time.perf_counter()
+    est += (t1 - t0) * cfg.T / rows[0]
+    # pack rows + bank copy: memcpy-class work, timed in full on the oracle
+    z = np.zeros((cfg.T, cfg.latent), np.uint16)
+    t0 = time.perf_counter()
+    pools = orc.pack_rows(dd, z, topk, snd["slot"], snd["pool_offsets"])
+    t1 = time.perf_counter()
+    est += t1 - t0
+    recv = st.recv.cpu().numpy()
+    hdr = orc.headers(recv, cfg.latent)
+    t0 = time.perf_counter()
+    bo = orc.bank_slots(dd, st.rank, hdr, None if st.recv_offsets is None else st.recv_offsets.cpu().numpy())
+    bank = orc.bank_rows(dd, recv, bo["bank_offsets"], bo["bank_src"], bo["bfill"])
+    t1 = time.perf_counter()
+    est += t1 - t0
+    kept = int(bo["bfill"].sum())
+    wg, wu, wd = (_u16(w) for w in (st.wg, st.wu, st.wd))
+    t0 = time.perf_counter()
+    for r in range(rows[1]):
+        orc.ffn_row(bank[r], wg[0], wu[0], wd[0])
+    t1 = time.perf_counter()
+    est += (t1 - t0) * kept / rows[1]
+    ret = np.zeros((st.n_recv_rows, cfg.latent), np.uint16)
+    wlu = _u16(st.wlu)
+    wsg, wsu, wsd = (_u16(w) for w in (st.wsg, st.wsu, st.wsd))
+    t0 = time.perf_counter()
+    orc.combine(dd, ret, None if st.recv_offsets is None else st.recv_offsets.cpu().numpy(),
+                topk, snd["slot"], gates, x, wlu, wsg, wsu, wsd, tokens=toks[:rows[2]])
+    t1 = time.perf_counter()
+    est += (t1 - t0) * cfg.T / rows[2]
+    desc = (f"oracle, 1 thread: route+sender slots+pack rows+bank slots/copy in full for the "
+            f"{cfg.T}-token shard; latent on {rows[0]} tokens, expert FFN on {rows[1]} of "
+            f"{kept} bank rows, combine on {rows[2]} tokens; sampled stages scaled by rows")
+    return cfg.T / est, desc
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the expert-parallel layer; the exchange "
+              "between GPUs is a loopback and runs on one GPU only. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dispatch_softmax_top_amd as moe
+    from synth import configs
+
+    cfg = configs.WORKLOADS[args.config]
+    log(f"bench: {cfg.name} rank {args.rank}: setup")
+    st = setup(cfg, args.rank, progress=True)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step(st)
+    torch.cuda.synchronize()
+    log("bench: warmup done")
+
+    # timed region: K steps, events on the stream the kernels run on
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step(st)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"bench: {args.steps} steps, {ms:.3f} ms/step")
+
+    # per-kernel durations: the library brackets each launch with hipEvents
+    moe.moe_profile_reset()
+    moe.moe_profile_enable(True)
+    for _ in range(args.steps):
+        step(st)
+    moe.moe_profile_collect()
+    moe.moe_profile_enable(False)
+    prof = moe.moe_profile_read()
+    work = algorithmic_work(st)
+    kernels = {}
+    for name, (tot, n) in prof.items():
+        avg = tot / n
+        kind, amount = work.get(name, (None, 0.0))
+        entry = {"avg_us": round(avg * 1e3, 3), "launches_per_step": n // args.steps}
+        if kind == "flop":
+            entry["tflops"] = round(amount / (avg * 1e-3) / 1e12, 2)
+            entry["mfma_frac"] = round(entry["tflops"] / PEAK_BF16_TFLOPS, 4)
+        elif kind == "byte":
+            entry["gbs"] = round(amount / (avg * 1e-3) / 1e9, 1)
+            entry["hbm_frac"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[name] = entry
+    dom = "gemm_expert_swiglu"
+    dom_avg_s = prof[dom][0] / prof[dom][1] * 1e-3
+    achieved = work[dom][1] / dom_avg_s / 1e12
+
+    d = st.d
+    kept_s, dem_s = int(st.snd.fill.sum()), int(st.snd.demand.sum())
+    kept_r, dem_r = int(st.rcv.bfill.sum()), int(st.rcv.bdemand.sum())
+    drops = {
+        "sender_pct_own_shard": round(100.0 * (dem_s - kept_s) / max(dem_s, 1), 3),
+        "sender_pct_all_shards": round(100.0 * (st.sent_demand - st.sent_fill) / max(st.sent_demand, 1), 3),
+        "receiver_pct_rank": round(100.0 * (dem_r - kept_r) / max(dem_r, 1), 3),
+        "bad_rows": int(st.rcv.bad_rows[0]),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        val, desc = run_cpu_baseline(st)
+        cpu = {"value": round(val, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": desc, "wall_s": round(time.time() - t0, 1)}
+
+    tok_s = d.T / (ms * 1e-3)
+    line = {
+        "metric": "routed tokens/s through the MoE layer share on 1 MI355X",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller inputs; random-init weights)",
+        "config": {"workload": cfg.name, "rank": args.rank, "T": d.T, "d_model": d.d_model,
+                   "latent": d.latent, "n_experts": d.n_experts, "n_ranks": d.n_ranks,
+                   "top_k": d.top_k, "n_waves": d.n_waves, "d_ff": d.d_ff,
+                   "n_shared": d.n_shared, "cap_send": d.cap_send, "cap_recv": d.cap_recv,
+                   "source_shards": cfg.n_shards},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "drops": drops,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

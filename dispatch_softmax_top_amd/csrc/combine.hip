@@ -1,0 +1,145 @@
+// combine.hip -- gate-weighted combine of the returned rows, latent
+// up-projection, and the shared experts.
+//
+// "Marin 開始公開訓練 535B 參數 MoE 模型" (lamjinlab.com, zh-HK), section 二
+// (and the Japanese translation): the routed outputs are projected back to
+// the model width and then joined with the shared-expert path; the two shared
+// experts process every token independently of routing.  Section 四: an
+// assignment dropped for capacity only loses its routed contribution.
+//
+// Kernels, in stream order:
+//   combine_gather      one wave per token: ylat = bf16(sum_j g_j * row_j),
+//                       fp32 accumulation, 16-byte row reads
+//   gemm_shared_swiglu  h_s = bf16(silu(x.W_sg,s) * (x.W_su,s)) -> ws
+//   gemm_up_shared      out = bf16(ylat.W_lu + sum_s h_s.W_sd,s): one product
+//                       over the concatenated K = latent + n_shared*d_ff_shared
+#include "kernels.h"
+
+namespace moe {
+
+template <int CH>
+__global__ __launch_bounds__(256) void combine_gather_kernel(
+    const uint16_t *__restrict__ returned, const int64_t *__restrict__ ret_offsets,
+    const int32_t *__restrict__ topk, const int32_t *__restrict__ slot,
+    const float *__restrict__ gates, uint16_t *__restrict__ ylat, int T, int k, int L, int El,
+    int W, int Tw, int cap) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  int64_t my_row = -1;
+  float my_g = 0.f;
+  if (lane < k) {
+    const int s = slot[(int64_t)t * k + lane];
+    if (s >= 0) {
+      const int e = topk[(int64_t)t * k + lane];
+      const int p = (e / El) * W + t / Tw;
+      if (cap) {
+        my_row = (int64_t)p * cap + s;
+      } else if (s < ret_offsets[p + 1] - ret_offsets[p]) {
+        my_row = ret_offsets[p] + s;
+      }
+      my_g = gates[(int64_t)t * k + lane];
+    }
+  }
+  const int nch = L / 8;
+  float acc[CH][8];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int64_t row = ((int64_t)__shfl((int)(my_row >> 32), j) << 32) |
+                        (uint32_t)__shfl((int)my_row, j);
+    if (row < 0) continue;
+    const float g = __shfl(my_g, j);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(returned + row * L);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ci = lane + 64 * c;
+      if (ci < nch) {
+        const u32x4 v = src[ci];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[c][2 * q] = fmaf(g, __uint_as_float(v[q] << 16), acc[c][2 * q]);
+          acc[c][2 * q + 1] = fmaf(g, __uint_as_float(v[q] & 0xffff0000u), acc[c][2 * q + 1]);
+        }
+      }
+    }
+  }
+  u32x4 *dst = reinterpret_cast<u32x4 *>(ylat + (int64_t)t * L);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int ci = lane + 64 * c;
+    if (ci < nch) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[c][2 * q], acc[c][2 * q + 1]);
+      dst[ci] = o;
+    }
+  }
+}
+
+template <int CH>
+static int gather(const moe_dims &d, const uint16_t *returned, const int64_t *ret_offsets,
+                  const int32_t *topk, const int32_t *slot, const float *gates, uint16_t *ylat,
+                  hipStream_t s) {
+  return launch("combine_gather", combine_gather_kernel<CH>, dim3((unsigned)cdiv(d.T, 4)),
+                dim3(256), 0, s, returned, ret_offsets, topk, slot, gates, ylat, d.T, d.top_k,
+                d.latent, experts_per_rank(d), d.n_waves, tokens_per_wave(d), d.cap_send);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_combine(const moe_dims *d, const moe_bf16 *returned, const int64_t *ret_offsets,
+                           const int32_t *topk, const int32_t *slot, const float *gates,
+                           const moe_bf16 *x, const moe_bf16 *w_lat_up, const moe_bf16 *ws_gate,
+                           const moe_bf16 *ws_up, const moe_bf16 *ws_down, moe_bf16 *ylat,
+                           moe_bf16 *out, void *ws, int64_t ws_bytes, void *stream) {
+  clear_error();
+  MOE_TRY(check_dims(d));
+  const bool rg = ragged(*d);
+  MOE_TRY(check_ptr(returned, "returned"));
+  MOE_TRY(check_ptr(topk, "topk"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(gates, "gates"));
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(w_lat_up, "w_lat_up"));
+  MOE_TRY(check_ptr(ylat, "ylat"));
+  MOE_TRY(check_ptr(out, "out"));
+  if (d->n_shared > 0) {
+    MOE_TRY(check_ptr(ws_gate, "ws_gate"));
+    MOE_TRY(check_ptr(ws_up, "ws_up"));
+    MOE_TRY(check_ptr(ws_down, "ws_down"));
+  }
+  if (rg) MOE_TRY(check_ptr(ret_offsets, "ret_offsets (ragged mode)"));
+  const int64_t need = moe_workspace_bytes(d, MOE_CALL_COMBINE, 0);
+  if (need < 0) return (int)need;
+  if (ws_bytes < need || (need > 0 && !ws))
+    return fail(MOE_ERR_WORKSPACE, "moe_combine: workspace %lld < %lld bytes",
+                (long long)ws_bytes, (long long)need);
+  if (ws) MOE_TRY(check_ptr(ws, "ws"));
+  if (d->latent > 8 * 64 * 16) return fail(MOE_ERR_UNSUPPORTED, "moe_combine: latent <= 8192");
+  hipStream_t s = (hipStream_t)stream;
+
+  const int ch = (int)cdiv(d->latent / 8, 64);
+  int rc;
+  if (ch <= 1) rc = gather<1>(*d, returned, ret_offsets, topk, slot, gates, ylat, s);
+  else if (ch <= 2) rc = gather<2>(*d, returned, ret_offsets, topk, slot, gates, ylat, s);
+  else if (ch <= 4) rc = gather<4>(*d, returned, ret_offsets, topk, slot, gates, ylat, s);
+  else if (ch <= 6) rc = gather<6>(*d, returned, ret_offsets, topk, slot, gates, ylat, s);
+  else if (ch <= 8) rc = gather<8>(*d, returned, ret_offsets, topk, slot, gates, ylat, s);
+  else rc = gather<16>(*d, returned, ret_offsets, topk, slot, gates, ylat, s);
+  MOE_TRY(rc);
+
+  const int S = d->n_shared, Fs = d->d_ff_shared;
+  uint16_t *H = (uint16_t *)ws;
+  MOE_TRY(gemm_shared_swiglu(d->T, x, d->d_model, d->d_model, ws_gate, ws_up, S, Fs, H, s));
+  DenseSeg segs[1 + 4];
+  segs[0] = DenseSeg{ylat, d->latent, w_lat_up, d->latent, d->latent};
+  for (int i = 0; i < S; ++i)
+    segs[1 + i] = DenseSeg{H + (int64_t)i * Fs, (int64_t)S * Fs,
+                           ws_down + (int64_t)i * d->d_model * Fs, Fs, Fs};
+  return gemm_up_shared(d->T, d->d_model, 1 + S, segs, out, d->d_model, s);
+}

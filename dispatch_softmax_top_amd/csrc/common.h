@@ -1,0 +1,113 @@
+// common.h -- shared pieces of libmoe: host-side checks, errors, launch
+// bookkeeping, and device helpers for gfx950 (wave64, bf16 MFMA).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+int hip_status(hipError_t e, const char *what);
+
+// Argument checks shared by the entry points; return MOE_OK or an error.
+int check_dims(const moe_dims *d);
+int check_ptr(const void *p, const char *name, bool may_be_null = false);
+
+inline int32_t experts_per_rank(const moe_dims &d) { return d.n_experts / d.n_ranks; }
+inline int32_t tokens_per_wave(const moe_dims &d) { return (d.T + d.n_waves - 1) / d.n_waves; }
+inline bool ragged(const moe_dims &d) { return d.cap_send == 0; }
+inline int64_t row_bytes(const moe_dims &d) { return 2 * (int64_t)d.latent + 16; }
+
+// Launch bookkeeping: records hipEvents around a launch when timing is on.
+struct ProfScope {
+  ProfScope(const char *name, hipStream_t s);
+  ~ProfScope();
+  int slot;
+  hipStream_t stream;
+};
+
+// Launch a kernel and report a launch error as MOE_ERR_HIP.
+template <typename... KArgs, typename... Args>
+int launch(const char *name, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+           size_t lds, hipStream_t s, Args... args) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return MOE_OK;
+  ProfScope p(name, s);
+  hipLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<KArgs>(args)...);
+  return hip_status(hipGetLastError(), name);
+}
+
+#define MOE_TRY(x)                 \
+  do {                             \
+    int _rc = (x);                 \
+    if (_rc != MOE_OK) return _rc; \
+  } while (0)
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t align_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// ---------------------------------------------------------------------------
+// device side
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Lanes below this one.
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Mask of the active lanes holding the same key (keys < 2^bits).
+__device__ __forceinline__ uint64_t match_key(uint32_t key, int bits) {
+  uint64_t m = ballot(true);
+  for (int b = 0; b < bits; ++b) {
+    uint64_t v = ballot((key >> b) & 1u);
+    m &= ((key >> b) & 1u) ? v : ~v;
+  }
+  return m;
+}
+
+__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
+
+// Dispatch order of workgroups is round-robin over the 8 XCDs.  Map the
+// hardware block id to a logical tile id so that each XCD gets one
+// contiguous range of tiles (neighbouring tiles share operand panels in
+// that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int NX = 8;
+  int xcd = bid % NX, local = bid / NX;
+  int per = nblocks / NX, rem = nblocks % NX;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+}  // namespace moe

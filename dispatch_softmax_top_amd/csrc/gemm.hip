@@ -1,0 +1,323 @@
+// gemm.hip -- the dense contractions of the path, all on the bf16 MFMA core
+// of gemm.h:
+//   gemm_latent_down    z = x . W_ld                  (model width -> latent)
+//   gemm_shared_swiglu  h_s = silu(x.W_sg,s) * (x.W_su,s) for each shared expert
+//   gemm_up_shared      out = ylat . W_lu + sum_s h_s . W_sd,s (one K-concatenated
+//                       product, one rounding)
+//   gemm_expert_swiglu  h = silu(u.W_g,j) * (u.W_u,j) over every bank group
+//   gemm_expert_down    y = h . W_d,j, rows scattered to their receive position
+//
+// SwiGLU tiles: a block owns 128 intermediate columns f0 .. f0+127 and loads
+// 256 weight rows: for wave column wn (0..3) and MFMA column tile j (0..1),
+// rows are gate (j = 0) / up (j = 1) of f = f0 + 32 wn + (0..31).  The same
+// lane then holds a = u.W_g and b = u.W_u for one (row, f) in tiles 0 and 1,
+// and the epilogue writes bf16(silu(a) * b) directly.
+#include "gemm.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int MAXSEG = 5;
+
+struct DenseArgs {
+  int M, N, nseg;
+  const uint16_t *A[MAXSEG];
+  int64_t lda[MAXSEG];
+  const uint16_t *B[MAXSEG];
+  int64_t ldb[MAXSEG];
+  int ktiles[MAXSEG];
+  uint16_t *C;
+  int64_t ldc;
+};
+
+__device__ __forceinline__ void dense_body(const DenseArgs &g, uint16_t *lds) {
+  const int tm = (g.M + GBM - 1) / GBM, tn = (g.N + GBN - 1) / GBN;
+  int mt, nt;
+  g_tile_coords(xcd_remap(blockIdx.x, gridDim.x), tm, tn, mt, nt);
+  GAcc acc;
+  gemm_zero(acc);
+  for (int s = 0; s < g.nseg; ++s) {
+    const uint16_t *ap[GROWS], *bp[GROWS];
+#pragma unroll
+    for (int i = 0; i < GROWS; ++i) {
+      const int r = min(mt * GBM + g_load_row(i), g.M - 1);
+      const int c = min(nt * GBN + g_load_row(i), g.N - 1);
+      ap[i] = g.A[s] + (int64_t)r * g.lda[s];
+      bp[i] = g.B[s] + (int64_t)c * g.ldb[s];
+    }
+    gemm_mainloop(ap, bp, g.ktiles[s], acc, lds);
+  }
+#pragma unroll
+  for (int i = 0; i < GTM; ++i)
+#pragma unroll
+    for (int j = 0; j < GTN; ++j) {
+      const int n = nt * GBN + g_acc_col(j);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = mt * GBM + g_acc_row(i, v);
+        if (m < g.M && n < g.N) g.C[(int64_t)m * g.ldc + n] = f32_to_bf16(acc[i][j][v]);
+      }
+    }
+}
+
+__global__ __launch_bounds__(GNT) void gemm_latent_down_kernel(DenseArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GSTAGE];
+  dense_body(g, lds);
+}
+
+__global__ __launch_bounds__(GNT) void gemm_up_shared_kernel(DenseArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GSTAGE];
+  dense_body(g, lds);
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU
+// ---------------------------------------------------------------------------
+
+struct SwigluArgs {
+  const uint16_t *A;  // rows
+  int64_t lda;
+  int ktiles;
+  const uint16_t *Bg, *Bu;  // [experts][F][K]
+  int64_t ldb;
+  int F, ftiles;  // ftiles = F / 128
+  uint16_t *H;
+  int64_t ldh;
+  // dense (shared experts): M rows, expert = f-tile / ftiles along N
+  int M, S;
+  // grouped (routed experts)
+  int G, El, cap;
+  const int32_t *count;      // [G] rows per group
+  const int64_t *offsets;    // ragged: [G+1] first row per group; NULL if fixed
+};
+
+__device__ __forceinline__ void swiglu_tile(const SwigluArgs &g, int row0, int rows, int expert,
+                                            int ft, int h_col0, uint16_t *lds) {
+  const int f0 = ft * 128;
+  const uint16_t *ap[GROWS], *bp[GROWS];
+  const int64_t eoff = (int64_t)expert * g.F * g.ldb;
+#pragma unroll
+  for (int i = 0; i < GROWS; ++i) {
+    const int r = row0 + min(g_load_row(i), rows - 1);
+    ap[i] = g.A + (int64_t)r * g.lda;
+    // load slot i covers B-tile row 64 i + (t >> 3): wave column i, MFMA
+    // tile (t >> 3) / 32 (0 = gate, 1 = up), f = f0 + 32 i + ((t >> 3) & 31)
+    const int f = f0 + i * 32 + (int)((threadIdx.x >> 3) & 31);
+    bp[i] = ((threadIdx.x >> 8) ? g.Bu : g.Bg) + eoff + (int64_t)f * g.ldb;
+  }
+  GAcc acc;
+  gemm_zero(acc);
+  gemm_mainloop(ap, bp, g.ktiles, acc, lds);
+  const int lane = lane_id(), wn = (threadIdx.x >> 6) & 3;
+  const int f = f0 + wn * 32 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < GTM; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = g_acc_row(i, v);
+      if (m < rows) {
+        const float a = acc[i][0][v], b = acc[i][1][v];
+        g.H[(int64_t)(row0 + m) * g.ldh + h_col0 + f] = f32_to_bf16(silu_f32(a) * b);
+      }
+    }
+}
+
+__global__ __launch_bounds__(GNT) void gemm_shared_swiglu_kernel(SwigluArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GSTAGE];
+  const int tm = (g.M + GBM - 1) / GBM, tn = g.S * g.ftiles;
+  int mt, nt;
+  g_tile_coords(xcd_remap(blockIdx.x, gridDim.x), tm, tn, mt, nt);
+  const int s = nt / g.ftiles, ft = nt % g.ftiles;
+  swiglu_tile(g, mt * GBM, min(GBM, g.M - mt * GBM), s, ft, s * g.F, lds);
+}
+
+// Find (group, m-tile, n-tile) of logical tile id `logical`; groups in order,
+// each contributing ceil(rows / 256) * tn tiles.  Returns false past the end.
+__device__ __forceinline__ bool group_tile(int logical, int G, const int32_t *count,
+                                           const int64_t *offsets, int cap, int tn, int &g,
+                                           int &row0, int &rows, int &mt, int &nt) {
+  int rem = logical;
+  for (g = 0; g < G; ++g) {
+    const int c = count[g];
+    const int tiles = ((c + GBM - 1) / GBM) * tn;
+    if (rem < tiles) {
+      const int tmg = (c + GBM - 1) / GBM;
+      g_tile_coords(rem, tmg, tn, mt, nt);
+      const int64_t start = offsets ? offsets[g] : (int64_t)g * cap;
+      row0 = (int)start + mt * GBM;
+      rows = min(GBM, c - mt * GBM);
+      return true;
+    }
+    rem -= tiles;
+  }
+  return false;
+}
+
+__global__ __launch_bounds__(GNT) void gemm_expert_swiglu_kernel(SwigluArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GSTAGE];
+  int grp, row0, rows, mt, nt;
+  if (!group_tile(xcd_remap(blockIdx.x, gridDim.x), g.G, g.count, g.offsets, g.cap, g.ftiles,
+                  grp, row0, rows, mt, nt))
+    return;
+  swiglu_tile(g, row0, rows, grp % g.El, nt, 0, lds);
+}
+
+// ---------------------------------------------------------------------------
+// expert down-projection with scatter to the receive layout
+// ---------------------------------------------------------------------------
+
+struct DownArgs {
+  const uint16_t *H;  // [bank rows][F]
+  int F, ktiles;
+  const uint16_t *Wd;  // [El][L][F]
+  int L, tn;
+  int G, El, cap;
+  const int32_t *count;
+  const int64_t *offsets;
+  const int32_t *bank_src;
+  uint16_t *ret;  // [ret rows][L]
+  int64_t n_ret;
+};
+
+__global__ __launch_bounds__(GNT) void gemm_expert_down_kernel(DownArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GSTAGE];
+  int grp, row0, rows, mt, nt;
+  if (!group_tile(xcd_remap(blockIdx.x, gridDim.x), g.G, g.count, g.offsets, g.cap, g.tn, grp,
+                  row0, rows, mt, nt))
+    return;
+  const uint16_t *ap[GROWS], *bp[GROWS];
+  const uint16_t *W = g.Wd + (int64_t)(grp % g.El) * g.L * g.F;
+#pragma unroll
+  for (int i = 0; i < GROWS; ++i) {
+    ap[i] = g.H + (int64_t)(row0 + min(g_load_row(i), rows - 1)) * g.F;
+    bp[i] = W + (int64_t)min(nt * GBN + g_load_row(i), g.L - 1) * g.F;
+  }
+  GAcc acc;
+  gemm_zero(acc);
+  gemm_mainloop(ap, bp, g.ktiles, acc, lds);
+#pragma unroll
+  for (int i = 0; i < GTM; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = g_acc_row(i, v);
+      if (m >= rows) continue;
+      const int64_t dr = g.bank_src[row0 + m];
+      if (dr < 0 || dr >= g.n_ret) continue;
+      const int64_t dst = dr * g.L;
+#pragma unroll
+      for (int j = 0; j < GTN; ++j) {
+        const int n = nt * GBN + g_acc_col(j);
+        if (n < g.L) g.ret[dst + n] = f32_to_bf16(acc[i][j][v]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+static int dense(const char *name, void (*k)(DenseArgs), int M, int N, int nseg,
+                 const DenseSeg *segs, uint16_t *C, int64_t ldc, hipStream_t s) {
+  if (nseg < 1 || nseg > MAXSEG) return fail(MOE_ERR_INVALID, "%s: bad segment count", name);
+  DenseArgs a{};
+  a.M = M;
+  a.N = N;
+  a.nseg = nseg;
+  for (int i = 0; i < nseg; ++i) {
+    if (segs[i].K % GBK) return fail(MOE_ERR_UNSUPPORTED, "%s: K %% 64 != 0", name);
+    a.A[i] = segs[i].A;
+    a.lda[i] = segs[i].lda;
+    a.B[i] = segs[i].B;
+    a.ldb[i] = segs[i].ldb;
+    a.ktiles[i] = segs[i].K / GBK;
+  }
+  a.C = C;
+  a.ldc = ldc;
+  const int64_t tiles = cdiv(M, GBM) * cdiv(N, GBN);
+  return launch(name, k, dim3((unsigned)tiles), dim3(GNT), 0, s, a);
+}
+
+int gemm_latent_down(int M, int N, const DenseSeg &seg, uint16_t *C, int64_t ldc, hipStream_t s) {
+  return dense("gemm_latent_down", gemm_latent_down_kernel, M, N, 1, &seg, C, ldc, s);
+}
+
+int gemm_up_shared(int M, int N, int nseg, const DenseSeg *segs, uint16_t *C, int64_t ldc,
+                   hipStream_t s) {
+  return dense("gemm_up_shared", gemm_up_shared_kernel, M, N, nseg, segs, C, ldc, s);
+}
+
+int gemm_shared_swiglu(int M, const uint16_t *x, int64_t ldx, int K, const uint16_t *wg,
+                       const uint16_t *wu, int S, int F, uint16_t *H, hipStream_t s) {
+  if (S == 0) return MOE_OK;
+  SwigluArgs a{};
+  a.A = x;
+  a.lda = ldx;
+  a.ktiles = K / GBK;
+  a.Bg = wg;
+  a.Bu = wu;
+  a.ldb = K;
+  a.F = F;
+  a.ftiles = F / 128;
+  a.H = H;
+  a.ldh = (int64_t)S * F;
+  a.M = M;
+  a.S = S;
+  const int64_t tiles = cdiv(M, GBM) * (int64_t)S * a.ftiles;
+  return launch("gemm_shared_swiglu", gemm_shared_swiglu_kernel, dim3((unsigned)tiles), dim3(GNT),
+                0, s, a);
+}
+
+static int64_t grouped_tiles_bound(const moe_dims &d, int64_t n_bank_rows, int tn) {
+  const int64_t G = (int64_t)d.n_waves * experts_per_rank(d);
+  const int64_t mt = ragged(d) ? cdiv(n_bank_rows, GBM) + G : G * cdiv(d.cap_recv, GBM);
+  return mt * tn;
+}
+
+int gemm_expert_swiglu(const moe_dims &d, const uint16_t *bank, const int64_t *bank_offsets,
+                       const int32_t *bfill, int64_t n_bank_rows, const uint16_t *wg,
+                       const uint16_t *wu, uint16_t *H, hipStream_t s) {
+  SwigluArgs a{};
+  a.A = bank;
+  a.lda = d.latent;
+  a.ktiles = d.latent / GBK;
+  a.Bg = wg;
+  a.Bu = wu;
+  a.ldb = d.latent;
+  a.F = d.d_ff;
+  a.ftiles = d.d_ff / 128;
+  a.H = H;
+  a.ldh = d.d_ff;
+  a.G = d.n_waves * experts_per_rank(d);
+  a.El = experts_per_rank(d);
+  a.cap = d.cap_recv;
+  a.count = bfill;
+  a.offsets = ragged(d) ? bank_offsets : nullptr;
+  const int64_t tiles = grouped_tiles_bound(d, n_bank_rows, a.ftiles);
+  return launch("gemm_expert_swiglu", gemm_expert_swiglu_kernel, dim3((unsigned)tiles), dim3(GNT),
+                0, s, a);
+}
+
+int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_offsets,
+                     const int32_t *bfill, const int32_t *bank_src, int64_t n_bank_rows,
+                     const uint16_t *wd, uint16_t *ret, int64_t n_ret, hipStream_t s) {
+  DownArgs a{};
+  a.n_ret = n_ret;
+  a.H = H;
+  a.F = d.d_ff;
+  a.ktiles = d.d_ff / GBK;
+  a.Wd = wd;
+  a.L = d.latent;
+  a.tn = (int)cdiv(d.latent, GBN);
+  a.G = d.n_waves * experts_per_rank(d);
+  a.El = experts_per_rank(d);
+  a.cap = d.cap_recv;
+  a.count = bfill;
+  a.offsets = ragged(d) ? bank_offsets : nullptr;
+  a.bank_src = bank_src;
+  a.ret = ret;
+  const int64_t tiles = grouped_tiles_bound(d, n_bank_rows, a.tn);
+  return launch("gemm_expert_down", gemm_expert_down_kernel, dim3((unsigned)tiles), dim3(GNT), 0,
+                s, a);
+}
+
+}  // namespace moe

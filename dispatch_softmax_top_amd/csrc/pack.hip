@@ -1,0 +1,157 @@
+// pack.hip -- sender side: latent down-projection, slot assignment into one
+// fixed pool per (destination rank, wave), and the row scatter.
+//
+// "Marin 開始公開訓練 535B 參數 MoE 模型" (lamjinlab.com, zh-HK), section 二
+// (same in the Japanese translation, section 二): activations are projected
+// to the latent width before the exchange; the sender keeps one fixed pool
+// per destination GPU (not per expert), sends in three waves of one array
+// shape, puts the expert id inside the payload so no counts or metadata are
+// exchanged, caps each (source, destination) pool with the sender capacity
+// factor, and drops and counts the overflow.
+//
+// Kernels, in stream order:
+//   rank_count / rank_assign  positions of (token, choice) assignments in
+//                             their pool, in (token, choice) order
+//   gemm_latent_down          z = x . W_ld (bf16 MFMA)
+//   pack_rows                 one wave per token: z[t] read once, written to
+//                             each kept destination row with 16-byte stores;
+//                             extra blocks stamp id -1 on unfilled slots
+#include "gemm.h"
+#include "kernels.h"
+#include "rank.h"
+
+namespace moe {
+
+struct SenderSrc {
+  const int32_t *topk;
+  int k, E, El, W, Tw;
+  __device__ void prepare(int64_t *) {}
+  __device__ int32_t key(int64_t item, int32_t &aux) const {
+    aux = 0;
+    const int e = topk[item];
+    if ((unsigned)e >= (unsigned)E) return KEY_BAD;  // not a valid choice: never kept
+    const int t = (int)(item / k);
+    return (e / El) * W + t / Tw;
+  }
+};
+
+template <bool RAGGED>
+struct SenderEmit {
+  static constexpr bool needs_offsets = RAGGED;
+  int32_t *slot, *fill, *demand;
+  int64_t *pool_offsets;
+  int cap;
+  __device__ void item(int64_t it, int key, int32_t, int rank, const int64_t *) const {
+    slot[it] = (key >= 0 && (RAGGED || rank < cap)) ? rank : -1;
+  }
+  __device__ void totals(int K, const int32_t *tot, const int64_t *koff, int32_t) const {
+    for (int kk = threadIdx.x; kk < K; kk += blockDim.x) {
+      demand[kk] = tot[kk];
+      fill[kk] = RAGGED ? tot[kk] : min(tot[kk], cap);
+      if (RAGGED) pool_offsets[kk] = koff[kk];
+    }
+    if (RAGGED && threadIdx.x == 0) pool_offsets[K] = koff[K];
+  }
+};
+
+__global__ __launch_bounds__(256) void pack_rows_kernel(
+    const uint16_t *__restrict__ z, const int32_t *__restrict__ topk,
+    const int32_t *__restrict__ slot, const int32_t *__restrict__ fill,
+    const int64_t *__restrict__ pool_offsets, uint8_t *__restrict__ pools, int T, int k, int L,
+    int El, int W, int Tw, int cap, int token_blocks, int64_t n_slots) {
+  const int64_t RB = 2 * (int64_t)L + 16;
+  const int lane = lane_id();
+  if ((int)blockIdx.x < token_blocks) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    int my_row = -1, my_e = -1;
+    if (lane < k) {
+      const int s = slot[(int64_t)t * k + lane];
+      if (s >= 0) {
+        const int e = topk[(int64_t)t * k + lane];
+        const int p = (e / El) * W + t / Tw;
+        my_row = cap ? p * cap + s : (int)pool_offsets[p] + s;
+        my_e = e;
+      }
+    }
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(z + (int64_t)t * L);
+    for (int c = lane; c < L / 8; c += 64) {
+      const u32x4 v = src[c];
+      for (int j = 0; j < k; ++j) {
+        const int row = __shfl(my_row, j);
+        if (row >= 0) *reinterpret_cast<u32x4 *>(pools + row * RB + c * 16) = v;
+      }
+    }
+    if (my_row >= 0) {
+      u32x4 h = {(uint32_t)my_e, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(pools + my_row * RB + 2 * (int64_t)L) = h;
+    }
+  } else {
+    const int64_t idx = (int64_t)(blockIdx.x - token_blocks) * 256 + threadIdx.x;
+    if (idx >= n_slots) return;
+    const int p = (int)(idx / cap), i = (int)(idx - (int64_t)p * cap);
+    if (i >= fill[p]) {
+      u32x4 h = {0xffffffffu, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(pools + idx * RB + 2 * (int64_t)L) = h;
+    }
+  }
+}
+
+template <bool RAGGED>
+static int sender_slots(const moe_dims &d, const int32_t *topk, int32_t *slot, int32_t *fill,
+                        int32_t *demand, int64_t *pool_offsets, int32_t *tile_counts,
+                        hipStream_t s) {
+  const int64_t n = (int64_t)d.T * d.top_k;
+  const int K = d.n_ranks * d.n_waves;
+  const int tiles = (int)rank_tiles(n);
+  SenderSrc src{topk, d.top_k, d.n_experts, experts_per_rank(d), d.n_waves, tokens_per_wave(d)};
+  SenderEmit<RAGGED> em{slot, fill, demand, pool_offsets, d.cap_send};
+  MOE_TRY(launch("rank_count_sender", rank_count<SenderSrc>, dim3(tiles), dim3(RK_THREADS), 0, s,
+                 src, n, K, tile_counts, (int32_t *)nullptr, (int64_t)0));
+  return launch("rank_assign_sender", rank_assign<SenderSrc, SenderEmit<RAGGED>>, dim3(tiles),
+                dim3(RK_THREADS), 0, s, src, em, n, K, tiles, (const int32_t *)tile_counts);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_pack_waves(const moe_dims *d, const moe_bf16 *x, const moe_bf16 *w_lat_down,
+                              const int32_t *topk, moe_bf16 *z, uint8_t *pools,
+                              int64_t *pool_offsets, int32_t *slot, int32_t *fill,
+                              int32_t *demand, void *ws, int64_t ws_bytes, void *stream) {
+  clear_error();
+  MOE_TRY(check_dims(d));
+  const bool rg = ragged(*d);
+  MOE_TRY(check_ptr(x, "x"));
+  MOE_TRY(check_ptr(w_lat_down, "w_lat_down"));
+  MOE_TRY(check_ptr(topk, "topk"));
+  MOE_TRY(check_ptr(z, "z"));
+  MOE_TRY(check_ptr(pools, "pools"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(fill, "fill"));
+  MOE_TRY(check_ptr(demand, "demand"));
+  if (rg) MOE_TRY(check_ptr(pool_offsets, "pool_offsets (ragged mode)"));
+  const int64_t need = moe_workspace_bytes(d, MOE_CALL_PACK, 0);
+  if (need < 0) return (int)need;
+  if (ws_bytes < need || (need > 0 && !ws))
+    return fail(MOE_ERR_WORKSPACE, "moe_pack_waves: workspace %lld < %lld bytes",
+                (long long)ws_bytes, (long long)need);
+  if (ws) MOE_TRY(check_ptr(ws, "ws"));
+  if ((int64_t)d->n_ranks * d->n_waves * d->cap_send >= (1ll << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_pack_waves: pool rows must fit in int32");
+  hipStream_t s = (hipStream_t)stream;
+  int32_t *tc = (int32_t *)ws;
+
+  MOE_TRY(rg ? sender_slots<true>(*d, topk, slot, fill, demand, pool_offsets, tc, s)
+             : sender_slots<false>(*d, topk, slot, fill, demand, pool_offsets, tc, s));
+  DenseSeg seg{x, d->d_model, w_lat_down, d->d_model, d->d_model};
+  MOE_TRY(gemm_latent_down(d->T, d->latent, seg, z, d->latent, s));
+  const int token_blocks = (int)cdiv(d->T, 4);
+  const int64_t n_slots = rg ? 0 : (int64_t)d->n_ranks * d->n_waves * d->cap_send;
+  const int64_t blocks = token_blocks + cdiv(n_slots, 256);
+  return launch("pack_rows", pack_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, z, topk,
+                slot, fill, pool_offsets, pools, d->T, d->top_k, d->latent,
+                experts_per_rank(*d), d->n_waves, tokens_per_wave(*d), d->cap_send, token_blocks,
+                n_slots);
+}

@@ -1,0 +1,219 @@
+/*
+ * moe.h -- C ABI of libmoe.so: one GPU's share of a pooled-wave
+ * mixture-of-experts dispatch path, hand-written HIP for gfx950 (MI355X).
+ *
+ * Sources, cited by page title and section:
+ *   [P2] "Marin 開始公開訓練 535B 參數 MoE 模型" (lamjinlab.com, zh-HK)
+ *   [P3] "Marin、535BパラメータMoEモデルのオープントレーニングを開始"
+ *        (lamjinlab.com, ja) -- translation of [P2]
+ *   [P1] "从玩具到前沿:训练一个真正的大模型,到底难在哪里" (devpress.csdn.net)
+ *
+ * The path, per source shard of T tokens ([P2]/[P3] section 二):
+ *   moe_route       softmax over E routed experts, top-k choice and gates
+ *   moe_pack_waves  latent down-projection, then one fixed pool per
+ *                   destination rank and wave, expert id inside each row,
+ *                   sender capacity, overflow dropped and counted
+ *   (exchange)      outside this library: the caller moves pools to the
+ *                   destination ranks' receive buffers
+ *   moe_bank        rows received for this rank banked per wave and local
+ *                   expert, receiver capacity, overflow dropped and counted
+ *   moe_expert_ffn  every local expert run on its bank rows, each wave
+ *   (return)        outside this library
+ *   moe_combine     gate-weighted sum of each token's returned rows, latent
+ *                   up-projection, plus the shared experts
+ *
+ * Conventions shared by every call
+ *   - All array arguments are DEVICE pointers, 16-byte aligned, owned by the
+ *     caller.  The library never allocates, frees or synchronises inside a
+ *     hot-path call; scratch comes only through (ws, ws_bytes).
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = null stream)
+ *     and return at once.  Calls on distinct buffers are re-entrant.
+ *   - bf16 tensors are passed as uint16_t bit patterns (moe_bf16).
+ *   - Weights are output-major: the weight W of y = x.W (W of shape
+ *     [in, out]) is stored as W^T, shape [out, in], row-major.
+ *   - A pool / receive row is `latent` bf16 values followed by a 16-byte
+ *     tail {int32 global expert id, 0, 0, 0}; id -1 marks an empty slot
+ *     (its payload bytes are unspecified).  Row stride = 2*latent + 16.
+ *   - Fixed mode (cap_send > 0 and cap_recv > 0):
+ *       pools  [n_ranks][n_waves][cap_send] rows   (destination, wave, slot)
+ *       recv   [n_ranks][n_waves][cap_send] rows   (source, wave, slot)
+ *       bank   [n_waves][E_l][cap_recv][latent]    (wave, local expert, pos)
+ *       ret    [n_ranks][n_waves][cap_send][latent] (recv layout, no tail)
+ *     Ragged / dropless mode (cap_send == cap_recv == 0): the same orders,
+ *     but each (outer, wave) segment has its own length and starts at an
+ *     int64 offset; an offsets array has one entry per segment plus the
+ *     total at the end.
+ *   - Waves split a shard's tokens into contiguous runs: wave(t) =
+ *     floor(t / T_w), T_w = ceil(T / n_waves).  Expert e lives on rank
+ *     floor(e / E_l) as local expert e mod E_l, E_l = n_experts / n_ranks.
+ *   - Every output is fully written except where stated unspecified.
+ *   - Errors: arguments are checked on the host before any launch; a
+ *     negative moe_status is returned and moe_last_error() (per thread)
+ *     says why.  Nothing is enqueued when a call returns an error.
+ *     Data-dependent faults found on the device (a receive row whose id is
+ *     neither -1 nor hosted by `rank`) are counted, never trapped.
+ */
+#ifndef MOE_H
+#define MOE_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef uint16_t moe_bf16;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,     /* bad pointer, size or layout */
+  MOE_ERR_UNSUPPORTED = -2, /* valid, but outside what the kernels handle */
+  MOE_ERR_HIP = -3,         /* the HIP runtime reported an error */
+  MOE_ERR_WORKSPACE = -4    /* ws too small */
+} moe_status;
+
+/* Sizes of one layer share.  cap_send / cap_recv: rows per
+ * (destination, wave) pool and per (wave, local expert) bank; both 0 selects
+ * ragged / dropless mode.  Supported: n_experts % n_ranks == 0,
+ * n_experts <= 1024, 1 <= top_k <= min(32, n_experts), latent % 64 == 0,
+ * d_model % 64 == 0, d_ff % 128 == 0, d_ff_shared % 128 == 0,
+ * n_ranks * n_waves <= 1024, n_waves * E_l <= 1024, n_shared <= 4. */
+typedef struct {
+  int32_t T, d_model, latent, n_experts, n_ranks, top_k, n_waves, d_ff,
+      n_shared, d_ff_shared, cap_send, cap_recv;
+} moe_dims;
+
+int moe_abi_version(void);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+/* Capacities from rational capacity factors cf = num/den ([P2]/[P3]
+ * section 二: the sender factor caps rows from one source to one destination,
+ * the receiver factor caps rows of one local expert).  Each factor multiplies
+ * the mean load of its buffer for one wave -- T_w*k/n_ranks rows per pool and
+ * T_w*k/E_l rows per local expert -- and the product is rounded up, in exact
+ * integer arithmetic.  Reads T, n_waves, top_k, n_ranks, n_experts from d. */
+int moe_capacity(const moe_dims *d, int64_t cf_send_num, int64_t cf_send_den,
+                 int64_t cf_recv_num, int64_t cf_recv_den, int32_t *cap_send,
+                 int32_t *cap_recv);
+
+enum { MOE_CALL_ROUTE = 0, MOE_CALL_PACK = 1, MOE_CALL_BANK = 2,
+       MOE_CALL_FFN = 3, MOE_CALL_COMBINE = 4 };
+
+/* Bytes of scratch a call needs.  n_rows: bank rows allocated (FFN, ragged
+ * mode); ignored otherwise.  Returns a negative moe_status on bad dims. */
+int64_t moe_workspace_bytes(const moe_dims *d, int call, int64_t n_rows);
+
+/* Router ([P2]/[P3] section 二, [P1] section 四: k of E routed experts per
+ * token).  logits [T, E] fp32 (any routing bias already added).  Choice by
+ * decreasing logit, equal logits to the lower index; topk [T, k] int32 in
+ * that order; gates [T, k] fp32 = the chosen experts' probabilities under the
+ * softmax over all E logits (not renormalised).  NaN logits unsupported. */
+int moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
+              int32_t *topk, float *gates, void *stream);
+
+/* Sender ([P2]/[P3] section 二; [P1] appendix A.3): latent projection
+ * z = x . W_ld, then every assignment (t, j) in (token, choice) order takes
+ * the next position of pool (dest(e), wave(t)); kept iff the position is
+ * below cap_send (always in ragged mode).
+ *   x           [T, d_model] bf16
+ *   w_lat_down  [latent, d_model] bf16 (W_ld^T)
+ *   topk        [T, k] int32 from moe_route
+ *   z           [T, latent] bf16 out
+ *   pools       fixed: [n_ranks*n_waves*cap_send] rows out (kept rows carry
+ *               z[t] and id e; the rest only the id -1);
+ *               ragged: [T*k] rows out, pool p at pool_offsets[p]
+ *   pool_offsets ragged: [n_ranks*n_waves + 1] int64 out; NULL if fixed
+ *   slot        [T, k] int32 out: position in its pool, or -1 if dropped
+ *   fill        [n_ranks*n_waves] int32 out: kept rows per pool
+ *   demand      [n_ranks*n_waves] int32 out: rows asked of each pool
+ *   Pool index p = dest * n_waves + wave.  Sender drops = sum(demand-fill). */
+int moe_pack_waves(const moe_dims *d, const moe_bf16 *x,
+                   const moe_bf16 *w_lat_down, const int32_t *topk,
+                   moe_bf16 *z, uint8_t *pools, int64_t *pool_offsets,
+                   int32_t *slot, int32_t *fill, int32_t *demand, void *ws,
+                   int64_t ws_bytes, void *stream);
+
+/* Receiver ([P2]/[P3] section 二; [P1] section 四 and appendix A.3): rows
+ * received by `rank` are banked per (wave, local expert) in (source, row)
+ * order within each wave; kept iff the position is below cap_recv.
+ *   recv         fixed: [n_ranks*n_waves*cap_send] rows;
+ *                ragged: n_recv_rows rows, segment (s, w) at
+ *                recv_offsets[s*n_waves + w]
+ *   recv_offsets ragged: [n_ranks*n_waves + 1] int64; NULL if fixed
+ *   n_recv_rows  rows in recv (must equal n_ranks*n_waves*cap_send if fixed)
+ *   bank         fixed: [n_waves*E_l*cap_recv, latent] bf16 out;
+ *                ragged: [n_recv_rows, latent], group g at bank_offsets[g];
+ *                rows past each group's fill are unspecified
+ *   bank_offsets ragged: [n_waves*E_l + 1] int64 out; NULL if fixed
+ *   bank_src     [bank rows] int32 out: receive row of each bank row, -1
+ *                where unused
+ *   bfill        [n_waves*E_l] int32 out: kept rows per group
+ *   bdemand      [n_waves*E_l] int32 out: rows that asked for each group
+ *   bad_rows     [1] int32 out: rows whose id is not -1 and not on `rank`
+ *   Group g = wave * E_l + local expert.  Receiver drops = sum(bdemand-bfill). */
+int moe_bank(const moe_dims *d, int32_t rank, const uint8_t *recv,
+             const int64_t *recv_offsets, int64_t n_recv_rows, moe_bf16 *bank,
+             int64_t *bank_offsets, int32_t *bank_src, int32_t *bfill,
+             int32_t *bdemand, int32_t *bad_rows, void *ws, int64_t ws_bytes,
+             void *stream);
+
+/* Expert FFN ([P1] section 四 and appendix A.3: each wave the receiver runs
+ * all of its local experts).  For every kept bank row u of group (w, j):
+ * y = bf16( bf16(silu(u.W_g,j) * (u.W_u,j)) . W_d,j ), silu(a) = a/(1+e^-a)
+ * (SwiGLU: the pages leave the expert's form open), written to ret at row
+ * bank_src; every other ret row is zero.
+ *   bank, bank_offsets, bank_src, bfill  from moe_bank
+ *   n_bank_rows  rows allocated in bank (bounds the launch)
+ *   w_gate, w_up [E_l, d_ff, latent] bf16; w_down [E_l, latent, d_ff] bf16
+ *   ret          [n_ret_rows, latent] bf16 out, recv layout
+ *   ws           scratch of moe_workspace_bytes(d, MOE_CALL_FFN, n_bank_rows) */
+int moe_expert_ffn(const moe_dims *d, const moe_bf16 *bank,
+                   const int64_t *bank_offsets, const int32_t *bank_src,
+                   const int32_t *bfill, int64_t n_bank_rows,
+                   const moe_bf16 *w_gate, const moe_bf16 *w_up,
+                   const moe_bf16 *w_down, moe_bf16 *ret, int64_t n_ret_rows,
+                   void *ws, int64_t ws_bytes, void *stream);
+
+/* Combine ([P2]/[P3] section 二: routed outputs go back to model width and
+ * join the shared-expert path; section 四: a dropped assignment only loses its
+ * routed contribution, the two shared experts see every token).
+ *   ylat[t] = bf16( sum_j [slot>=0] gates[t,j] * returned[dest(e), wave(t), slot] )
+ *   out[t]  = bf16( ylat[t].W_lu + sum_s bf16(silu(x.W_sg,s)*(x.W_su,s)).W_sd,s )
+ *   returned     rows of the pools' layout (destination, wave, slot), latent
+ *                wide, no tail; ragged: segment p at ret_offsets[p], a slot
+ *                at or past its segment's length reads as zero
+ *   ret_offsets  ragged: [n_ranks*n_waves + 1] int64; NULL if fixed
+ *   topk, slot, gates  from moe_route / moe_pack_waves
+ *   x            [T, d_model] bf16
+ *   w_lat_up     [d_model, latent] bf16 (W_lu^T)
+ *   ws_gate, ws_up [n_shared, d_ff_shared, d_model]; ws_down
+ *                [n_shared, d_model, d_ff_shared] bf16
+ *   ylat         [T, latent] bf16 out; out [T, d_model] bf16 out
+ *   ws           scratch of moe_workspace_bytes(d, MOE_CALL_COMBINE, 0) */
+int moe_combine(const moe_dims *d, const moe_bf16 *returned,
+                const int64_t *ret_offsets, const int32_t *topk,
+                const int32_t *slot, const float *gates, const moe_bf16 *x,
+                const moe_bf16 *w_lat_up, const moe_bf16 *ws_gate,
+                const moe_bf16 *ws_up, const moe_bf16 *ws_down, moe_bf16 *ylat,
+                moe_bf16 *out, void *ws, int64_t ws_bytes, void *stream);
+
+/* Kernel timing.  While enabled, every kernel the library launches is
+ * bracketed by two hipEvents on its stream.  moe_profile_collect()
+ * waits for the recorded events and folds them into per-kernel totals;
+ * moe_profile_get(i, ...) reads entry i (returns MOE_ERR_INVALID past the
+ * end); moe_profile_reset() clears the totals.  Not for concurrent use from
+ * several threads. */
+int moe_profile_enable(int on);
+int moe_profile_collect(void);
+int moe_profile_get(int i, char *name, int name_len, double *total_ms,
+                    int64_t *launches);
+void moe_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

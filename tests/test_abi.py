@@ -1,0 +1,103 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/moe.h declares, and rejects bad arguments on the host
+(returning a negative status and an error text) before any launch."""
+import ctypes
+import os
+import re
+from fractions import Fraction
+
+import pytest
+
+from synth import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import dispatch_softmax_top_amd as m
+    m.lib()
+    return m
+
+
+def test_exports_every_declared_symbol(moe):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(moe.lib(), n), n
+    assert set(names) == set(moe.EXPORTS)
+
+
+def test_abi_version(moe):
+    assert moe.moe_abi_version() == 1
+
+
+def test_capacity_matches_table(moe):
+    from dispatch_softmax_top_amd import share
+    for cfg, cs, cr in ((configs.TINY, 25, 34), (configs.SHARE_4K, 188, 2095),
+                        (configs.ZIPF_16K, 752, 8376), (configs.LONG_65K, 3004, 33498),
+                        (configs.SWEEP_16K["1.5/1.5"], 1025, 10924),
+                        (configs.SWEEP_16K["2.0/2.0"], 1366, 14566)):
+        d = share.make_dims(cfg)
+        assert (d.cap_send, d.cap_recv) == (cs, cr), cfg.name
+
+
+def test_capacity_agrees_with_oracle(moe, orc):
+    from dispatch_softmax_top_amd import share
+    import itertools
+    for T, cs, cr in itertools.product((1, 7, 64, 601, 4096, 65536), ("11/10", "3/2", "7/3"),
+                                       ("23/20", "1", "5/2")):
+        cfg = configs.scaled(configs.SHARE_4K, "x", T=T, cf_send=Fraction(cs),
+                             cf_recv=Fraction(cr))
+        d, dd = share.make_dims(cfg), orc.dims(cfg)
+        assert (d.cap_send, d.cap_recv) == (dd.cap_send, dd.cap_recv)
+
+
+def _dims(moe, **kw):
+    from dispatch_softmax_top_amd import share
+    d = share.make_dims(configs.TINY)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("field,value", [("latent", 100), ("d_model", 0), ("n_ranks", 5),
+                                         ("top_k", 60), ("d_ff", 200), ("cap_recv", 0),
+                                         ("n_experts", 2048)])
+def test_bad_dims_rejected(moe, field, value):
+    d = _dims(moe, **{field: value})
+    rc = moe.lib().moe_workspace_bytes(ctypes.byref(d), moe.MOE_CALL_FFN, 0)
+    assert rc < 0
+    assert moe.lib().moe_last_error().decode()
+
+
+def test_calls_reject_null_and_misaligned(moe):
+    L = moe.lib()
+    d = _dims(moe)
+    assert L.moe_route(None, 4, 16, 8, None, None, None) == -1
+    assert L.moe_route(ctypes.c_void_p(16), 4, 16, 17, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                       None) == -1
+    assert L.moe_route(ctypes.c_void_p(18), 4, 16, 8, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                       None) == -1                                  # misaligned
+    assert "aligned" in L.moe_last_error().decode()
+    p = ctypes.c_void_p(256)
+    assert L.moe_pack_waves(ctypes.byref(d), p, p, p, p, p, None, p, p, p, None, 0, None) < 0
+    assert L.moe_bank(ctypes.byref(d), 99, p, None, 0, p, None, p, p, p, p, None, 0, None) == -1
+    assert L.moe_bank(ctypes.byref(d), 0, p, None, 5, p, None, p, p, p, p, None, 0, None) == -1
+    assert L.moe_expert_ffn(ctypes.byref(d), p, None, p, p, 1, p, p, p, p, 1, p, 1 << 30,
+                            None) == -1
+    assert L.moe_combine(ctypes.byref(d), p, None, p, p, p, p, p, p, p, p, p, p, None, 0,
+                         None) == -4                                # workspace too small
+
+
+def test_workspace_sizes_grow_with_rows(moe):
+    d = _dims(moe, cap_send=0, cap_recv=0)
+    a = moe.moe_workspace_bytes(d, moe.MOE_CALL_FFN, 100)
+    b = moe.moe_workspace_bytes(d, moe.MOE_CALL_FFN, 1000)
+    assert 0 < a < b
