@@ -32,9 +32,10 @@ class State:
     pass
 
 
-def setup(cfg, rank=0, device="cuda", seed=0, progress=False):
+def setup(cfg, rank=0, device="cuda", seed=0, progress=False, keep_logits=False):
     """Inputs in HBM for one rank: its own shard, its experts' weights, and
-    the receive buffer made from every source shard's pools (loopback)."""
+    the receive buffer made from every source shard's pools (loopback).
+    keep_logits: also keep a host copy of every shard's router logits."""
     import torch
     from dispatch_softmax_top_amd import share
     from synth import gen
@@ -52,6 +53,7 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False):
     R, W = d.n_ranks, d.n_waves
     st.sent_demand = 0
     st.sent_fill = 0
+    st.host_logits = [] if keep_logits else None
     if d.cap_send:
         st.n_recv_rows = R * W * d.cap_send
         st.recv = torch.empty(st.n_recv_rows, share.row_bytes(d), dtype=torch.uint8,
@@ -77,6 +79,8 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False):
                 lens.append(b - a)
         if s == rank:
             st.x, st.logits = x, lg
+        if keep_logits:
+            st.host_logits.append(lg.cpu().numpy())
         if progress and (s % 16 == 15 or s == cfg.n_shards - 1):
             log(f"setup: shard {s + 1}/{cfg.n_shards} packed ({time.time() - t0:.1f}s)")
     if d.cap_send:
@@ -120,6 +124,31 @@ def algorithmic_work(st):
     w["bank_rows"] = ("byte", 2.0 * kept_r * 2 * L)
     w["combine_gather"] = ("byte", kept_s * 2.0 * L + T * k * 8.0 + T * L * 2.0)
     return w
+
+
+TRAFFIC_SOURCES = ("dispatch_softmax_top_amd/csrc/gemm.h", "dispatch_softmax_top_amd/csrc/gemm.hip",
+                   "dispatch_softmax_top_amd/csrc/common.h")
+
+
+def counted_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading),
+    or None if none was taken for this workload or the kernel's sources have
+    changed since."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    sha = h.hexdigest()
+    for f in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_bytes.txt")):
+        for line in open(f):
+            if not line.startswith(f"traffic {kernel} "):
+                continue
+            kv = dict(x.split("=", 1) for x in line.split()[2:])
+            if kv.get("workload") == workload and kv.get("source_sha256") == sha:
+                return int(kv["bytes_per_launch"])
+    return None
 
 
 def _u16(t):
@@ -195,6 +224,9 @@ def main():
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise device copy of MIB mebibytes, three "
+                         "times: the reference for hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the expert-parallel layer; the exchange "
@@ -205,6 +237,16 @@ def main():
     import torch
     import dispatch_softmax_top_amd as moe
     from synth import configs
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)   # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n}))
+        return
 
     cfg = configs.WORKLOADS[args.config]
     log(f"bench: {cfg.name} rank {args.rank}: setup")
@@ -289,7 +331,8 @@ def main():
                    "source_shards": cfg.n_shards},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": counted_traffic(dom, cfg.name)},
         "cpu_baseline": cpu,
         "drops": drops,
         "kernels": kernels,

@@ -1,0 +1,55 @@
+"""The pins must catch plausible slips: plant each one in a scratch copy of
+the oracle (on the CPU) and check that the pin suite then fails."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = [
+    ("tie-break", "if (best < 0 || l[e] > l[best]) best = e;",
+     "if (best < 0 || l[e] >= l[best]) best = e;", "test_oracle_pins.py"),
+    ("gate/up swap", "h[f] = bf(to_bf(silu(a) * b));", "h[f] = bf(to_bf(silu(b) * a));",
+     "test_oracle_pins.py"),
+    ("wave index", "int32_t w = t / Tw;", "int32_t w = t % W;", "test_oracle_pins.py"),
+    ("gates renormalised away", "gates[t * k + j] = (float)(exp((double)l[best] - m) / Z);",
+     "gates[t * k + j] = (float)(exp((double)l[best] - m));", "test_oracle_pins.py"),
+    ("latent weight transposed", "for (int32_t i = 0; i < D; ++i) acc += xr[i] * bf(w[i]);",
+     "for (int32_t i = 0; i < D; ++i) acc += xr[i] * bf(w_ld_t[(int64_t)(i % L) * D + c]);",
+     "test_oracle_pins.py"),
+    ("shared expert dropped", "for (int32_t f = 0; f < Fs; ++f) o += h[sh * Fs + f] * bf(wd[f]);",
+     "for (int32_t f = 0; f < Fs; ++f) o += (sh == 0) * h[sh * Fs + f] * bf(wd[f]);",
+     "test_oracle_pins.py"),
+    ("capacity off by one", "if (cap == 0 || pos < cap) {", "if (cap == 0 || pos <= cap) {",
+     "test_oracle_pins.py"),
+    ("receiver source order", "for (int32_t s = 0; s < R; ++s) {\n      int64_t a = ragged ? recv_offsets[s * W + w] : ((int64_t)s * W + w) * d->cap_send;\n      int64_t b = ragged ? recv_offsets[s * W + w + 1] : a + d->cap_send;\n      for (int64_t row = a; row < b; ++row) {\n        int32_t h = hdr[row];\n        if (h < 0",
+     "for (int32_t s = R - 1; s >= 0; --s) {\n      int64_t a = ragged ? recv_offsets[s * W + w] : ((int64_t)s * W + w) * d->cap_send;\n      int64_t b = ragged ? recv_offsets[s * W + w + 1] : a + d->cap_send;\n      for (int64_t row = a; row < b; ++row) {\n        int32_t h = hdr[row];\n        if (h < 0",
+     "test_oracle_pins.py"),
+    ("fill not capped", "fill[p] = (cap == 0 || n[p] < cap) ? n[p] : cap;", "fill[p] = n[p];",
+     "test_oracle_pins.py"),
+    ("gate not applied", "for (int32_t c = 0; c < L; ++c) acc[c] += g * bf(returned[row * L + c]);",
+     "for (int32_t c = 0; c < L; ++c) acc[c] += bf(returned[row * L + c]);", "test_oracle_pins.py"),
+    ("down weight transposed", "acc += h[f] * bf(w[f]);",
+     "acc += h[f] * bf(wd_t[(int64_t)f * L + (c % F)]);", "test_oracle_pins.py"),
+    ("return segment order", "int32_t seg = dest_of(d, e) * W + w;",
+     "int32_t seg = w * d->n_ranks + dest_of(d, e);", "test_oracle_e2e.py"),
+    ("expert placement", "return e / (d->n_experts / d->n_ranks);", "return e % d->n_ranks;",
+     "test_oracle_pins.py"),
+]
+
+
+@pytest.mark.parametrize("name,old,new,suite", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(tmp_path, name, old, new, suite):
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    assert src.count(old) >= 1, f"mutation site for {name!r} not found"
+    for d in ("oracle", "synth", "tests"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    (tmp_path / "oracle" / "oracle.c").write_text(src.replace(old, new, 1))
+    p = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join("tests", suite)], cwd=tmp_path, capture_output=True,
+                       text=True, timeout=600)
+    assert p.returncode != 0, f"pins did not catch {name!r}:\n{p.stdout[-2000:]}"
