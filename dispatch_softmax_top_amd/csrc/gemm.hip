@@ -8,10 +8,9 @@
 //   gemm_expert_down    y = h . W_d,j, rows scattered to their receive position
 //
 // SwiGLU tiles: a block owns 128 intermediate columns f0 .. f0+127 and loads
-// 256 weight rows: for wave column wn (0..3) and MFMA column tile j (0..1),
-// rows are gate (j = 0) / up (j = 1) of f = f0 + 32 wn + (0..31).  The same
-// lane then holds a = u.W_g and b = u.W_u for one (row, f) in tiles 0 and 1,
-// and the epilogue writes bf16(silu(a) * b) directly.
+// their 128 gate and 128 up weight rows, interleaved per 32-row MFMA tile
+// (g_swiglu_brow), so one lane holds a = u.W_g and b = u.W_u of the same
+// (row, f) and the epilogue writes bf16(silu(a) * b) directly.
 #include "gemm.h"
 #include "kernels.h"
 
@@ -30,21 +29,18 @@ struct DenseArgs {
   int64_t ldc;
 };
 
-__device__ __forceinline__ void dense_body(const DenseArgs &g, uint16_t *lds) {
+__device__ __forceinline__ void dense_body(const DenseArgs &g, const GemmLds &lds) {
   const int tm = (g.M + GBM - 1) / GBM, tn = (g.N + GBN - 1) / GBN;
   int mt, nt;
   g_tile_coords(xcd_remap(blockIdx.x, gridDim.x), tm, tn, mt, nt);
   GAcc acc;
   gemm_zero(acc);
   for (int s = 0; s < g.nseg; ++s) {
-    const uint16_t *ap[GROWS], *bp[GROWS];
-#pragma unroll
-    for (int i = 0; i < GROWS; ++i) {
-      const int r = min(mt * GBM + g_load_row(i), g.M - 1);
-      const int c = min(nt * GBN + g_load_row(i), g.N - 1);
-      ap[i] = g.A[s] + (int64_t)r * g.lda[s];
-      bp[i] = g.B[s] + (int64_t)c * g.ldb[s];
-    }
+    const int mv = g.M - mt * GBM, nv = g.N - nt * GBN;  // valid rows / columns
+    const auto ap = g_operand<GCA>(g.A[s] + (int64_t)mt * GBM * g.lda[s], g.lda[s],
+                                   [&](int r) { return min(r, mv - 1); });
+    const auto bp = g_operand<GCB>(g.B[s] + (int64_t)nt * GBN * g.ldb[s], g.ldb[s],
+                                   [&](int r) { return min(r, nv - 1); });
     gemm_mainloop(ap, bp, g.ktiles[s], acc, lds);
   }
 #pragma unroll
@@ -60,13 +56,13 @@ __device__ __forceinline__ void dense_body(const DenseArgs &g, uint16_t *lds) {
     }
 }
 
-__global__ __launch_bounds__(GNT) void gemm_latent_down_kernel(DenseArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GSTAGE];
+__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_latent_down_kernel(DenseArgs g) {
+  MOE_GEMM_LDS(lds);
   dense_body(g, lds);
 }
 
-__global__ __launch_bounds__(GNT) void gemm_up_shared_kernel(DenseArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GSTAGE];
+__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_up_shared_kernel(DenseArgs g) {
+  MOE_GEMM_LDS(lds);
   dense_body(g, lds);
 }
 
@@ -92,38 +88,43 @@ struct SwigluArgs {
 };
 
 __device__ __forceinline__ void swiglu_tile(const SwigluArgs &g, int row0, int rows, int expert,
-                                            int ft, int h_col0, uint16_t *lds) {
+                                            int ft, int h_col0, const GemmLds &lds) {
   const int f0 = ft * 128;
-  const uint16_t *ap[GROWS], *bp[GROWS];
-  const int64_t eoff = (int64_t)expert * g.F * g.ldb;
-#pragma unroll
-  for (int i = 0; i < GROWS; ++i) {
-    const int r = row0 + min(g_load_row(i), rows - 1);
-    ap[i] = g.A + (int64_t)r * g.lda;
-    // load slot i covers B-tile row 64 i + (t >> 3): wave column i, MFMA
-    // tile (t >> 3) / 32 (0 = gate, 1 = up), f = f0 + 32 i + ((t >> 3) & 31)
-    const int f = f0 + i * 32 + (int)((threadIdx.x >> 3) & 31);
-    bp[i] = ((threadIdx.x >> 8) ? g.Bu : g.Bg) + eoff + (int64_t)f * g.ldb;
-  }
+  const int64_t eoff = (int64_t)expert * g.F * g.ldb + (int64_t)f0 * g.ldb;
+  const auto ap = g_operand<GCA>(g.A + (int64_t)row0 * g.lda, g.lda,
+                                 [&](int r) { return min(r, rows - 1); });
+  // whether a thread copies gate or up rows depends on the thread only
+  // (g_swiglu_brow of its copy rows), so the base stays wave-uniform
+  bool up;
+  int foff;
+  g_swiglu_brow(g_load_row(0), up, foff);
+  const auto bp = g_operand<GCB>((up ? g.Bu : g.Bg) + eoff, g.ldb, [&](int r) {
+    bool u;
+    int f;
+    g_swiglu_brow(r, u, f);
+    return f;
+  });
   GAcc acc;
   gemm_zero(acc);
   gemm_mainloop(ap, bp, g.ktiles, acc, lds);
-  const int lane = lane_id(), wn = (threadIdx.x >> 6) & 3;
-  const int f = f0 + wn * 32 + (lane & 31);
 #pragma unroll
-  for (int i = 0; i < GTM; ++i)
+  for (int p = 0; p < GTN / 2; ++p) {
+    const int f = f0 + g_swiglu_col(p);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = g_acc_row(i, v);
-      if (m < rows) {
-        const float a = acc[i][0][v], b = acc[i][1][v];
-        g.H[(int64_t)(row0 + m) * g.ldh + h_col0 + f] = f32_to_bf16(silu_f32(a) * b);
+    for (int i = 0; i < GTM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = g_acc_row(i, v);
+        if (m < rows) {
+          const float a = acc[i][2 * p][v], b = acc[i][2 * p + 1][v];
+          g.H[(int64_t)(row0 + m) * g.ldh + h_col0 + f] = f32_to_bf16(silu_f32(a) * b);
+        }
       }
-    }
+  }
 }
 
-__global__ __launch_bounds__(GNT) void gemm_shared_swiglu_kernel(SwigluArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GSTAGE];
+__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_shared_swiglu_kernel(SwigluArgs g) {
+  MOE_GEMM_LDS(lds);
   const int tm = (g.M + GBM - 1) / GBM, tn = g.S * g.ftiles;
   int mt, nt;
   g_tile_coords(xcd_remap(blockIdx.x, gridDim.x), tm, tn, mt, nt);
@@ -153,8 +154,8 @@ __device__ __forceinline__ bool group_tile(int logical, int G, const int32_t *co
   return false;
 }
 
-__global__ __launch_bounds__(GNT) void gemm_expert_swiglu_kernel(SwigluArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GSTAGE];
+__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_swiglu_kernel(SwigluArgs g) {
+  MOE_GEMM_LDS(lds);
   int grp, row0, rows, mt, nt;
   if (!group_tile(xcd_remap(blockIdx.x, gridDim.x), g.G, g.count, g.offsets, g.cap, g.ftiles,
                   grp, row0, rows, mt, nt))
@@ -179,19 +180,18 @@ struct DownArgs {
   int64_t n_ret;
 };
 
-__global__ __launch_bounds__(GNT) void gemm_expert_down_kernel(DownArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GSTAGE];
+__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_down_kernel(DownArgs g) {
+  MOE_GEMM_LDS(lds);
   int grp, row0, rows, mt, nt;
   if (!group_tile(xcd_remap(blockIdx.x, gridDim.x), g.G, g.count, g.offsets, g.cap, g.tn, grp,
                   row0, rows, mt, nt))
     return;
-  const uint16_t *ap[GROWS], *bp[GROWS];
   const uint16_t *W = g.Wd + (int64_t)(grp % g.El) * g.L * g.F;
-#pragma unroll
-  for (int i = 0; i < GROWS; ++i) {
-    ap[i] = g.H + (int64_t)(row0 + min(g_load_row(i), rows - 1)) * g.F;
-    bp[i] = W + (int64_t)min(nt * GBN + g_load_row(i), g.L - 1) * g.F;
-  }
+  const int nv = g.L - nt * GBN;
+  const auto ap = g_operand<GCA>(g.H + (int64_t)row0 * g.F, g.F,
+                                 [&](int r) { return min(r, rows - 1); });
+  const auto bp = g_operand<GCB>(W + (int64_t)nt * GBN * g.F, g.F,
+                                 [&](int r) { return min(r, nv - 1); });
   GAcc acc;
   gemm_zero(acc);
   gemm_mainloop(ap, bp, g.ktiles, acc, lds);
@@ -224,7 +224,7 @@ static int dense(const char *name, void (*k)(DenseArgs), int M, int N, int nseg,
   a.N = N;
   a.nseg = nseg;
   for (int i = 0; i < nseg; ++i) {
-    if (segs[i].K % GBK) return fail(MOE_ERR_UNSUPPORTED, "%s: K %% 64 != 0", name);
+    if (segs[i].K % GBK) return fail(MOE_ERR_UNSUPPORTED, "%s: K %% %d != 0", name, GBK);
     a.A[i] = segs[i].A;
     a.lda[i] = segs[i].lda;
     a.B[i] = segs[i].B;
