@@ -3,55 +3,68 @@
 // K-contiguous ("out x in" weights), so every copy and every LDS fragment
 // read is 16 bytes per lane.
 //
-// Block tile GBM x GBN over a GWM x GWN grid of waves, each wave 128 x 64 =
-// 4 x 2 MFMA tiles (128 fp32 accumulators per lane, at most 256 registers,
-// two waves per SIMD).  Two configurations:
-//   MOE_GEMM_CFG 1 (default): 256 x 256 tile, 8 waves, K tiles of 64,
-//                   2-stage ring (2 x 64 KB): one block per CU.
-//   MOE_GEMM_CFG 2: 128 x 256 tile, 4 waves, K tiles of 32, 3-stage ring
-//                   (3 x 24 KB): two blocks per CU, so one block's MFMAs
-//                   can cover the other's barrier waits.  On MI355X it ran
-//                   8-15% slower than configuration 1 on every GEMM of the
-//                   4096-token share (half the operand reuse per tile costs
-//                   more L2 traffic than the overlap wins back).
+// Block tile 256 x 256 over 8 waves in a 2 x 4 grid, each wave 128 x 64 =
+// 4 x 2 MFMA tiles (128 fp32 accumulators per lane, two waves per SIMD, one
+// block per CU).  Global -> LDS moves use the gfx950 direct path
+// (global_load_lds_dwordx4: no register staging).  The copy engine writes
+// each wave's 64 x 16 B contiguously, so lane l of a copy slot fetches the
+// chunk that belongs at position 64 * (slot's wave position) + l.  Two main
+// loops (MOE_GEMM_CFG):
 //
-// Global -> LDS moves use the gfx950 direct path (global_load_lds_dwordx4:
-// no register staging), issued GNST - 1 tiles ahead.  Per K tile: wait until
-// this thread's copies of the tile have landed (vmcnt), barrier (then every
-// wave's copies have landed and every wave is done reading the stage that
-// is refilled next), issue the copy of tile + GNST - 1 into that stage, then
-// run the MFMAs.  The loop is unrolled by the ring size so every stage
-// address is static.  The copy engine writes each wave's 64 x 16 B
-// contiguously, so lane l of copy slot i in wave w fetches the chunk that
-// belongs at stage position GNT * i + 64 w + l.
+//   1: K tiles of 64 in a 2-stage ring (2 x 64 KB).  Per K tile every wave
+//      waits for its copies (vmcnt), barrier, issues the copy of the next
+//      tile into the other stage, and runs 4 k-steps of MFMAs, reading the
+//      fragments of k-step kk + 1 while those of kk run.
+//
+//   2 (default): ping-pong.  The waves of rows 0..127 (group 0, waves 0-3,
+//      one per SIMD) and of rows 128..255 (group 1, waves 4-7) alternate
+//      roles every phase: one group runs the 16 MFMAs of one K tile (32
+//      wide) from registers while the other group issues copies and reads
+//      its fragments of the next tile from LDS.  Each SIMD then always has
+//      one wave with MFMAs ready, and a barrier falls while the other wave's
+//      last MFMA is still in the pipe.  K tiles sit in a 5-stage ring
+//      (5 x 32 KB = 160 KB), issued 4 tiles ahead, so about 7 phases of MFMA
+//      time cover each copy's latency.
 //
 // A stage row is GBK * 2 bytes = GCPR chunks of 16 B; chunk c of row r is
-// stored at c ^ g_swz(r).  A fragment read has 16 consecutive lanes on 16
-// consecutive rows at one logical chunk; g_swz makes both the 8 lanes of a
-// 128-byte LDS phase and the 16 lanes of a 256-byte phase land on distinct
-// 16-byte bank groups.
+// stored at c ^ g_swz(r), so that the ds_read_b128 of a fragment (32
+// consecutive rows, two adjacent chunks) runs at the full LDS rate
+// (measured on gfx950: about 240 of 256 B/clk/CU for both row widths).
 #pragma once
 #include "common.h"
 
 namespace moe {
 
 #ifndef MOE_GEMM_CFG
-#define MOE_GEMM_CFG 1
+#define MOE_GEMM_CFG 2
 #endif
 #if MOE_GEMM_CFG == 1
-constexpr int GBM = 256, GBN = 256, GBK = 64, GWM = 2, GWN = 4, GNST = 2;
+constexpr int GBK = 64, GNST = 2;
+constexpr bool GPP = false;
 #else
-constexpr int GBM = 128, GBN = 256, GBK = 32, GWM = 1, GWN = 4, GNST = 3;
+constexpr int GBK = 32, GNST = 5;
+constexpr bool GPP = true;
 #endif
+constexpr int GBM = 256, GBN = 256, GWM = 2, GWN = 4;
 constexpr int GNT = 64 * GWM * GWN;                 // threads per block
 constexpr int GWTM = GBM / GWM, GWTN = GBN / GWN;   // wave tile (128 x 64)
 constexpr int GTM = GWTM / 32, GTN = GWTN / 32;     // MFMA tiles per wave
 constexpr int GCPR = GBK / 8;                       // 16-byte chunks per stage row
 constexpr int GSA = GBM * GBK, GSB = GBN * GBK;     // elements per operand stage
-constexpr int GCA = GBM * GCPR / GNT, GCB = GBN * GCPR / GNT;  // copies per thread per stage
+// threads that copy one operand, and copies per such thread per K tile
+constexpr int GCT = GPP ? GNT / 2 : GNT;
+constexpr int GCA = GBM * GCPR / GCT, GCB = GBN * GCPR / GCT;
 constexpr int GMINWAVES = 2;                        // waves per SIMD the kernels are built for
 static_assert(GWTM == 128 && GWTN == 64, "wave tile 128 x 64");
-static_assert(GNST * (GSA + GSB) * 2 <= (MOE_GEMM_CFG == 1 ? 131072 : 81920), "LDS ring");
+static_assert(GNST * (GSA + GSB) * 2 <= 163840, "LDS ring");
+static_assert(!GPP || (GCA == GCB && GWM == 2 && GBK == 32 && GNST == 5),
+              "ping-pong: one operand per group, one 32-wide K tile per phase, 5 stages");
+
+// Ping-pong group of this wave (0: waves 0-3, 1: waves 4-7), as a
+// wave-uniform (scalar) value so that role branches stay scalar.
+__device__ __forceinline__ bool g_group1() {
+  return __builtin_amdgcn_readfirstlane((int)threadIdx.x) >= GCT;
+}
 
 typedef f32x16 GAcc[GTM][GTN];
 
@@ -70,14 +83,18 @@ struct GemmLds {
 
 // Chunk permutation of a stage row.  It depends on row bits 0..4 only, so
 // fragment tiles 32 rows apart share it and their addresses differ by an
-// immediate.  For 8 chunks per row it is a permutation of 0..7 over any 8
-// consecutive rows and over the even (and the odd) rows of any 16.
+// immediate.  Both forms were chosen by measurement: for 4 chunks per row,
+// ((r >> 1) ^ (r >> 3)) & 3 reads at half rate while (r ^ (r >> 2)) & 3 is
+// conflict-free; for 8 chunks per row the form below is conflict-free.
 __device__ __forceinline__ int g_swz(int row) {
-  return GCPR == 4 ? (((row >> 1) ^ (row >> 3)) & 3) : ((row & 6) | ((row ^ (row >> 3)) & 1));
+  return GCPR == 4 ? ((row ^ (row >> 2)) & 3) : ((row & 6) | ((row ^ (row >> 3)) & 1));
 }
 
-// Tile row whose chunk thread t copies in copy slot i (either operand).
-__device__ __forceinline__ int g_load_row(int i) { return (i * GNT + (int)threadIdx.x) / GCPR; }
+// Tile row whose chunk this thread copies in copy slot i (in the ping-pong
+// loop group 1 copies A and group 0 copies B, 256 threads each).
+__device__ __forceinline__ int g_load_row(int i) {
+  return (i * GCT + (int)threadIdx.x % GCT) / GCPR;
+}
 
 // Operand source of one block tile: a wave-uniform base address (row 0 of
 // the tile region, K column 0) and, per copy slot of this thread, the byte
@@ -122,6 +139,7 @@ __device__ __forceinline__ void g_copy16(const uint16_t *sbase, uint32_t voff,
                                          const uint16_t *lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_base);
+  sbase = g_uniform(sbase);  // uniform by construction; keep it in SGPRs for the asm
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -133,15 +151,81 @@ __device__ __forceinline__ void g_copy16(const uint16_t *sbase, uint32_t voff,
       : "memory");
 }
 
-// Copy K tile `kt` of both operands into one stage.
-__device__ __forceinline__ void g_copy_tile(const GOperand<GCA> &a, const GOperand<GCB> &b,
-                                            int kt, uint16_t *As, uint16_t *Bs) {
-  const int w = threadIdx.x >> 6;
-  const uint16_t *ab = a.base + kt * GBK, *bb = b.base + kt * GBK;
+// LDS position of copy slot i of this thread's wave within a stage:
+// i * GCT + 64 * (wave within the copying threads), in 16-byte chunks.
+__device__ __forceinline__ uint16_t *g_slot_dst(uint16_t *stage, int i) {
+  const int w = ((int)threadIdx.x % GCT) >> 6;
+  return stage + (i * GCT + w * 64) * 8;
+}
+
+// Copy K tile `kt` of one operand into its stage.
+template <int NC>
+__device__ __forceinline__ void g_copy_operand(const GOperand<NC> &o, int kt, uint16_t *dst) {
+  const uint16_t *src = o.base + kt * GBK;
 #pragma unroll
-  for (int i = 0; i < GCA; ++i) g_copy16(ab, a.off[i], As + (i * GNT + w * 64) * 8);
+  for (int i = 0; i < NC; ++i) g_copy16(src, o.off[i], g_slot_dst(dst, i));
+}
+
+// An operand whose K range is split into NS segments, each with its own
+// base and row stride (a product over a concatenated K with one rounding).
+// Each slot keeps its byte offset in every segment; a copy takes the scalar
+// branch of its segment, so every copy site sees constant indices.
+constexpr int GMAXSEG = 5;
+template <int NC, int NS>
+struct GSegOperand {
+  const uint16_t *base[NS];  // row 0 of the tile region, K column 0
+  int kend[NS];              // K tiles up to the end of each segment
+  uint32_t off[NS][NC];
+};
+
+template <int S, int NC, int NS, class RowOf>
+__device__ __forceinline__ void g_seg_set(GSegOperand<NC, NS> &o, const uint16_t *base,
+                                          int64_t ld, int kend, RowOf row_of) {
+  o.base[S] = g_uniform(base);
+  o.kend[S] = __builtin_amdgcn_readfirstlane(kend);
 #pragma unroll
-  for (int i = 0; i < GCB; ++i) g_copy16(bb, b.off[i], Bs + (i * GNT + w * 64) * 8);
+  for (int i = 0; i < NC; ++i) {
+    const int r = g_load_row(i);
+    const int c = (lane_id() % GCPR) ^ g_swz(r);
+    o.off[S][i] = (uint32_t)((int64_t)row_of(r) * ld * 2 + c * 16);
+  }
+}
+
+template <int S, int NC, int NS>
+__device__ __forceinline__ void g_copy_seg(const GSegOperand<NC, NS> &o, int kt, uint16_t *dst) {
+  if constexpr (S + 1 < NS) {
+    if (kt >= o.kend[S]) {
+      g_copy_seg<S + 1>(o, kt, dst);
+      return;
+    }
+  }
+  const uint16_t *src = o.base[S] + (kt - (S ? o.kend[S ? S - 1 : 0] : 0)) * GBK;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) g_copy16(src, o.off[S][i], g_slot_dst(dst, i));
+}
+
+template <int NC, int NS>
+__device__ __forceinline__ void g_copy_operand(const GSegOperand<NC, NS> &o, int kt,
+                                               uint16_t *dst) {
+  g_copy_seg<0>(o, kt, dst);
+}
+
+// The copy sources of one block tile: both operands (every thread copies
+// both), or in the ping-pong loop the operand of this thread's group (the
+// other one is never read).
+template <class OA, class OB>
+struct GOps {
+  OA a;
+  OB b;
+};
+
+template <class RowA, class RowB>
+__device__ __forceinline__ GOps<GOperand<GCA>, GOperand<GCB>> g_operands(
+    const uint16_t *a, int64_t lda, RowA row_a, const uint16_t *b, int64_t ldb, RowB row_b) {
+  GOps<GOperand<GCA>, GOperand<GCB>> o;
+  if (!GPP || g_group1()) o.a = g_operand<GCA>(a, lda, row_a);
+  if (!GPP || !g_group1()) o.b = g_operand<GCB>(b, ldb, row_b);
+  return o;
 }
 
 typedef const __attribute__((address_space(3))) bf16x8 *lds_frag_ptr;
@@ -202,38 +286,151 @@ __device__ __forceinline__ void g_mma_stage(const uint16_t *As, const uint16_t *
 #define MOE_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x70 | 0xF00)
 
-template <int S>
-__device__ __forceinline__ void g_ring_step(const GOperand<GCA> &ap, const GOperand<GCB> &bp,
-                                            int kt, int ktiles, GAcc &acc, const GemmLds &L) {
+// s_waitcnt vmcnt(PER_TILE * min(tiles, 3)): at most `tiles` later K tiles'
+// copies of this thread outstanding (an immediate per case).
+template <int PER_TILE>
+__device__ __forceinline__ void g_wait_tiles(int tiles) {
+  if (tiles >= 3) MOE_WAIT_VMCNT(3 * PER_TILE);
+  else if (tiles == 2) MOE_WAIT_VMCNT(2 * PER_TILE);
+  else if (tiles == 1) MOE_WAIT_VMCNT(PER_TILE);
+  else MOE_WAIT_VMCNT(0);
+}
+
+// ---- two-stage ring (MOE_GEMM_CFG 1)
+template <int S, class Ops>
+__device__ __forceinline__ void g_ring_step(const Ops &o, int kt, int ktiles, GAcc &acc,
+                                            const GemmLds &L) {
   if (kt >= ktiles) return;
-  // copies issued after those of tile kt: min(GNST - 2, ktiles - 1 - kt) tiles
-  constexpr int PER_TILE = GCA + GCB;
-  if constexpr (GNST >= 3) {
-    if (kt + 1 < ktiles) MOE_WAIT_VMCNT(PER_TILE);
-    else MOE_WAIT_VMCNT(0);
-  } else {
-    MOE_WAIT_VMCNT(0);
-  }
+  MOE_WAIT_VMCNT(0);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  constexpr int NX = (S + GNST - 1) % GNST;  // stage of tile kt + GNST - 1
-  if (kt + GNST - 1 < ktiles) g_copy_tile(ap, bp, kt + GNST - 1, L.A[NX], L.B[NX]);
+  constexpr int NX = (S + 1) % GNST;
+  if (kt + 1 < ktiles) {
+    g_copy_operand(o.a, kt + 1, L.A[NX]);
+    g_copy_operand(o.b, kt + 1, L.B[NX]);
+  }
   __builtin_amdgcn_sched_barrier(0);
   g_mma_stage(L.A[S], L.B[S], acc);
 }
 
-// Accumulate ktiles K tiles (GBK wide) of the two operands.
-__device__ __forceinline__ void gemm_mainloop(const GOperand<GCA> &ap, const GOperand<GCB> &bp,
-                                              int ktiles, GAcc &acc, const GemmLds &L) {
-  __builtin_amdgcn_s_barrier();  // the ring may still be read from a previous call
+// ---- ping-pong (MOE_GEMM_CFG 2)
+//
+// Phases 2s and 2s + 1 belong to K tile s.  Phase 2s: group 0 runs tile s's
+// MFMAs; group 1 copies A of tile s + 4 and reads its fragments of tile s.
+// Phase 2s + 1: group 1 runs tile s's MFMAs; group 0 copies B of tile s + 4
+// and reads its fragments of tile s + 1.  Every phase ends in a barrier
+// (reads of the phase are waited for before it: lgkmcnt).  Tile s is read in
+// phases 2s - 1 and 2s, so it must have landed at the barrier closing phase
+// 2s - 2 (each thread first waits for its own copies of it: vmcnt), and its
+// stage is refilled (with tile s + 5) from phase 2s + 2 on.
+constexpr int GPP_AHEAD = GNST - 1;
+
+__device__ __forceinline__ void g_pp_mma(const bf16x8 (&a)[2][GTM], const bf16x8 (&b)[2][GTN],
+                                         GAcc &acc) {
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int p = 0; p < GNST - 1; ++p)
-    if (p < ktiles) g_copy_tile(ap, bp, p, L.A[p], L.B[p]);
-  for (int kt = 0; kt < ktiles; kt += GNST) {
-    g_ring_step<0>(ap, bp, kt, ktiles, acc, L);
-    g_ring_step<1>(ap, bp, kt + 1, ktiles, acc, L);
-    if constexpr (GNST >= 3) g_ring_step<2 % GNST>(ap, bp, kt + 2, ktiles, acc, L);
+  for (int kk = 0; kk < 2; ++kk) g_mma(a[kk], b[kk], acc);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void g_pp_frags(const uint16_t *As, const uint16_t *Bs,
+                                           bf16x8 (&a)[2][GTM], bf16x8 (&b)[2][GTN]) {
+  const lds_frag_ptr A = g_stage_ptr(As), B = g_stage_ptr(Bs);
+  g_read_frags(A, B, 0, a[0], b[0]);
+  g_read_frags(A, B, 1, a[1], b[1]);
+}
+
+__device__ __forceinline__ void g_pp_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this phase's LDS reads are done
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One K tile s (phases 2s, 2s + 1) as group 0 sees it ...
+template <int S, class Ops>
+__device__ __forceinline__ void g_pp_tile_g0(const Ops &o, int s, int ktiles, GAcc &acc,
+                                             const GemmLds &L, bf16x8 (&a)[2][GTM],
+                                             bf16x8 (&b)[2][GTN]) {
+  if (s >= ktiles) return;
+  g_pp_mma(a, b, acc);
+  // tile s + 1 lands before phase 2s + 1; B is copied up to tile s + 3
+  g_wait_tiles<GCB>(min(GPP_AHEAD - 2, ktiles - 2 - s));
+  g_pp_sync();
+  if (s + GPP_AHEAD < ktiles) g_copy_operand(o.b, s + GPP_AHEAD, L.B[(S + GPP_AHEAD) % GNST]);
+  if (s + 1 < ktiles) g_pp_frags(L.A[(S + 1) % GNST], L.B[(S + 1) % GNST], a, b);
+  // nothing is shared after the last phase (a later call starts with a barrier)
+  if (s + 1 < ktiles) g_pp_sync();
+}
+
+// ... and as group 1 sees it.
+template <int S, class Ops>
+__device__ __forceinline__ void g_pp_tile_g1(const Ops &o, int s, int ktiles, GAcc &acc,
+                                             const GemmLds &L, bf16x8 (&a)[2][GTM],
+                                             bf16x8 (&b)[2][GTN]) {
+  if (s >= ktiles) return;
+  if (s + GPP_AHEAD < ktiles) g_copy_operand(o.a, s + GPP_AHEAD, L.A[(S + GPP_AHEAD) % GNST]);
+  g_pp_frags(L.A[S], L.B[S], a, b);
+  // tile s + 1 lands before phase 2s + 1; A is copied up to tile s + 4
+  g_wait_tiles<GCA>(min(GPP_AHEAD - 1, ktiles - 2 - s));
+  g_pp_sync();
+  g_pp_mma(a, b, acc);
+  if (s + 1 < ktiles) g_pp_sync();
+}
+
+// Accumulate ktiles K tiles (GBK wide) of the two operands.
+template <class Ops>
+__device__ __forceinline__ void gemm_mainloop(const Ops &o, int ktiles, GAcc &acc,
+                                              const GemmLds &L) {
+  __builtin_amdgcn_s_barrier();  // the ring may still be read from a previous call
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!GPP) {
+    if (ktiles > 0) {
+      g_copy_operand(o.a, 0, L.A[0]);
+      g_copy_operand(o.b, 0, L.B[0]);
+    }
+    for (int kt = 0; kt < ktiles; kt += 2) {
+      g_ring_step<0>(o, kt, ktiles, acc, L);
+      g_ring_step<1>(o, kt + 1, ktiles, acc, L);
+    }
+  } else {
+    if (ktiles <= 0) return;
+    // The two groups run separate loops with the same sequence of barriers.
+    bf16x8 a[2][GTM], b[2][GTN];
+    if (g_group1()) {
+      // prologue: A of tiles 0..3; tile 0 landed; phase -1 idle
+#pragma unroll
+      for (int p = 0; p < GPP_AHEAD; ++p)
+        if (p < ktiles) g_copy_operand(o.a, p, L.A[p]);
+      g_wait_tiles<GCA>(min(GPP_AHEAD - 1, ktiles - 1));
+      g_pp_sync();
+      g_pp_sync();
+      for (int s = 0; s < ktiles; s += GNST) {
+        g_pp_tile_g1<0>(o, s, ktiles, acc, L, a, b);
+        g_pp_tile_g1<1>(o, s + 1, ktiles, acc, L, a, b);
+        g_pp_tile_g1<2>(o, s + 2, ktiles, acc, L, a, b);
+        g_pp_tile_g1<3>(o, s + 3, ktiles, acc, L, a, b);
+        g_pp_tile_g1<4>(o, s + 4, ktiles, acc, L, a, b);
+      }
+    } else {
+      // prologue: B of tiles 0..2; tile 0 landed; phase -1: B of tile 3 and
+      // the fragments of tile 0
+#pragma unroll
+      for (int p = 0; p < GPP_AHEAD - 1; ++p)
+        if (p < ktiles) g_copy_operand(o.b, p, L.B[p]);
+      g_wait_tiles<GCB>(min(GPP_AHEAD - 2, ktiles - 1));
+      g_pp_sync();
+      if (GPP_AHEAD - 1 < ktiles) g_copy_operand(o.b, GPP_AHEAD - 1, L.B[GPP_AHEAD - 1]);
+      g_pp_frags(L.A[0], L.B[0], a, b);
+      g_pp_sync();
+      for (int s = 0; s < ktiles; s += GNST) {
+        g_pp_tile_g0<0>(o, s, ktiles, acc, L, a, b);
+        g_pp_tile_g0<1>(o, s + 1, ktiles, acc, L, a, b);
+        g_pp_tile_g0<2>(o, s + 2, ktiles, acc, L, a, b);
+        g_pp_tile_g0<3>(o, s + 3, ktiles, acc, L, a, b);
+        g_pp_tile_g0<4>(o, s + 4, ktiles, acc, L, a, b);
+      }
+    }
   }
 }
 

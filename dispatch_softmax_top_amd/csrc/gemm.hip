@@ -16,7 +16,7 @@
 
 namespace moe {
 
-constexpr int MAXSEG = 5;
+constexpr int MAXSEG = GMAXSEG;
 
 struct DenseArgs {
   int M, N, nseg;
@@ -29,20 +29,7 @@ struct DenseArgs {
   int64_t ldc;
 };
 
-__device__ __forceinline__ void dense_body(const DenseArgs &g, const GemmLds &lds) {
-  const int tm = (g.M + GBM - 1) / GBM, tn = (g.N + GBN - 1) / GBN;
-  int mt, nt;
-  g_tile_coords(xcd_remap(blockIdx.x, gridDim.x), tm, tn, mt, nt);
-  GAcc acc;
-  gemm_zero(acc);
-  for (int s = 0; s < g.nseg; ++s) {
-    const int mv = g.M - mt * GBM, nv = g.N - nt * GBN;  // valid rows / columns
-    const auto ap = g_operand<GCA>(g.A[s] + (int64_t)mt * GBM * g.lda[s], g.lda[s],
-                                   [&](int r) { return min(r, mv - 1); });
-    const auto bp = g_operand<GCB>(g.B[s] + (int64_t)nt * GBN * g.ldb[s], g.ldb[s],
-                                   [&](int r) { return min(r, nv - 1); });
-    gemm_mainloop(ap, bp, g.ktiles[s], acc, lds);
-  }
+__device__ __forceinline__ void dense_store(const DenseArgs &g, int mt, int nt, const GAcc &acc) {
 #pragma unroll
   for (int i = 0; i < GTM; ++i)
 #pragma unroll
@@ -56,14 +43,54 @@ __device__ __forceinline__ void dense_body(const DenseArgs &g, const GemmLds &ld
     }
 }
 
-__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_latent_down_kernel(DenseArgs g) {
-  MOE_GEMM_LDS(lds);
-  dense_body(g, lds);
+// Segment S of the operand sources (compile-time indices throughout).
+template <int S, int NS, class RowA, class RowB>
+__device__ __forceinline__ void dense_segs(const DenseArgs &g, int mt, int nt, RowA row_a,
+                                           RowB row_b, int &kend,
+                                           GOps<GSegOperand<GCA, NS>, GSegOperand<GCB, NS>> &ops) {
+  kend += g.ktiles[S];
+  // in the ping-pong loop a group copies one operand only
+  if (!GPP || g_group1())
+    g_seg_set<S>(ops.a, g.A[S] + (int64_t)mt * GBM * g.lda[S], g.lda[S], kend, row_a);
+  if (!GPP || !g_group1())
+    g_seg_set<S>(ops.b, g.B[S] + (int64_t)nt * GBN * g.ldb[S], g.ldb[S], kend, row_b);
+  if constexpr (S + 1 < NS) dense_segs<S + 1>(g, mt, nt, row_a, row_b, kend, ops);
 }
 
+// NS: number of K segments (one K range, one rounding).
+template <int NS>
+__device__ __forceinline__ void dense_body(const DenseArgs &g, const GemmLds &lds) {
+  const int tm = (g.M + GBM - 1) / GBM, tn = (g.N + GBN - 1) / GBN;
+  int mt, nt;
+  g_tile_coords(xcd_remap(blockIdx.x, gridDim.x), tm, tn, mt, nt);
+  const int mv = g.M - mt * GBM, nv = g.N - nt * GBN;  // valid rows / columns
+  const auto row_a = [&](int r) { return min(r, mv - 1); };
+  const auto row_b = [&](int r) { return min(r, nv - 1); };
+  GAcc acc;
+  gemm_zero(acc);
+  if constexpr (NS == 1) {
+    const auto ops = g_operands(g.A[0] + (int64_t)mt * GBM * g.lda[0], g.lda[0], row_a,
+                                g.B[0] + (int64_t)nt * GBN * g.ldb[0], g.ldb[0], row_b);
+    gemm_mainloop(ops, g.ktiles[0], acc, lds);
+  } else {
+    GOps<GSegOperand<GCA, NS>, GSegOperand<GCB, NS>> ops;
+    int kend = 0;
+    dense_segs<0>(g, mt, nt, row_a, row_b, kend, ops);
+    gemm_mainloop(ops, kend, acc, lds);
+  }
+  dense_store(g, mt, nt, acc);
+}
+
+__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_latent_down_kernel(DenseArgs g) {
+  MOE_GEMM_LDS(lds);
+  dense_body<1>(g, lds);
+}
+
+// up-projection + shared experts: 1 + S segments
+template <int NS>
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_up_shared_kernel(DenseArgs g) {
   MOE_GEMM_LDS(lds);
-  dense_body(g, lds);
+  dense_body<NS>(g, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -91,22 +118,23 @@ __device__ __forceinline__ void swiglu_tile(const SwigluArgs &g, int row0, int r
                                             int ft, int h_col0, const GemmLds &lds) {
   const int f0 = ft * 128;
   const int64_t eoff = (int64_t)expert * g.F * g.ldb + (int64_t)f0 * g.ldb;
-  const auto ap = g_operand<GCA>(g.A + (int64_t)row0 * g.lda, g.lda,
-                                 [&](int r) { return min(r, rows - 1); });
-  // whether a thread copies gate or up rows depends on the thread only
-  // (g_swiglu_brow of its copy rows), so the base stays wave-uniform
+  // whether a thread copies gate or up rows depends on the thread only (its
+  // copy rows are 64 apart, g_swiglu_brow sees row % 64), so the base stays
+  // wave-uniform
   bool up;
   int foff;
   g_swiglu_brow(g_load_row(0), up, foff);
-  const auto bp = g_operand<GCB>((up ? g.Bu : g.Bg) + eoff, g.ldb, [&](int r) {
-    bool u;
-    int f;
-    g_swiglu_brow(r, u, f);
-    return f;
-  });
+  const auto ops = g_operands(
+      g.A + (int64_t)row0 * g.lda, g.lda, [&](int r) { return min(r, rows - 1); },
+      (up ? g.Bu : g.Bg) + eoff, g.ldb, [&](int r) {
+        bool u;
+        int f;
+        g_swiglu_brow(r, u, f);
+        return f;
+      });
   GAcc acc;
   gemm_zero(acc);
-  gemm_mainloop(ap, bp, g.ktiles, acc, lds);
+  gemm_mainloop(ops, g.ktiles, acc, lds);
 #pragma unroll
   for (int p = 0; p < GTN / 2; ++p) {
     const int f = f0 + g_swiglu_col(p);
@@ -132,12 +160,24 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
   swiglu_tile(g, mt * GBM, min(GBM, g.M - mt * GBM), s, ft, s * g.F, lds);
 }
 
-// Find (group, m-tile, n-tile) of logical tile id `logical`; groups in order,
-// each contributing ceil(rows / 256) * tn tiles.  Returns false past the end.
-__device__ __forceinline__ bool group_tile(int logical, int G, const int32_t *count,
-                                           const int64_t *offsets, int cap, int tn, int &g,
-                                           int &row0, int &rows, int &mt, int &nt) {
-  int rem = logical;
+// Tiles of the grouped product: groups in order, each contributing
+// ceil(rows / 256) * tn tiles.  The grid is an upper bound; the real count
+// is known only here, so blocks remap over it (each XCD gets a contiguous
+// range of real tiles) and blocks past it exit.
+__device__ __forceinline__ int group_tiles_total(int G, const int32_t *count, int tn) {
+  int total = 0;
+  for (int g = 0; g < G; ++g) total += ((count[g] + GBM - 1) / GBM) * tn;
+  return total;
+}
+
+// Find (group, m-tile, n-tile) of this block's tile.  Returns false for a
+// block past the real tile count.
+__device__ __forceinline__ bool group_tile(int G, const int32_t *count, const int64_t *offsets,
+                                           int cap, int tn, int &g, int &row0, int &rows,
+                                           int &mt, int &nt) {
+  const int total = group_tiles_total(G, count, tn);
+  if ((int)blockIdx.x >= total) return false;
+  int rem = xcd_remap(blockIdx.x, total);
   for (g = 0; g < G; ++g) {
     const int c = count[g];
     const int tiles = ((c + GBM - 1) / GBM) * tn;
@@ -157,8 +197,7 @@ __device__ __forceinline__ bool group_tile(int logical, int G, const int32_t *co
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_swiglu_kernel(SwigluArgs g) {
   MOE_GEMM_LDS(lds);
   int grp, row0, rows, mt, nt;
-  if (!group_tile(xcd_remap(blockIdx.x, gridDim.x), g.G, g.count, g.offsets, g.cap, g.ftiles,
-                  grp, row0, rows, mt, nt))
+  if (!group_tile(g.G, g.count, g.offsets, g.cap, g.ftiles, grp, row0, rows, mt, nt))
     return;
   swiglu_tile(g, row0, rows, grp % g.El, nt, 0, lds);
 }
@@ -183,18 +222,16 @@ struct DownArgs {
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_down_kernel(DownArgs g) {
   MOE_GEMM_LDS(lds);
   int grp, row0, rows, mt, nt;
-  if (!group_tile(xcd_remap(blockIdx.x, gridDim.x), g.G, g.count, g.offsets, g.cap, g.tn, grp,
-                  row0, rows, mt, nt))
+  if (!group_tile(g.G, g.count, g.offsets, g.cap, g.tn, grp, row0, rows, mt, nt))
     return;
   const uint16_t *W = g.Wd + (int64_t)(grp % g.El) * g.L * g.F;
   const int nv = g.L - nt * GBN;
-  const auto ap = g_operand<GCA>(g.H + (int64_t)row0 * g.F, g.F,
-                                 [&](int r) { return min(r, rows - 1); });
-  const auto bp = g_operand<GCB>(W + (int64_t)nt * GBN * g.F, g.F,
-                                 [&](int r) { return min(r, nv - 1); });
+  const auto ops = g_operands(
+      g.H + (int64_t)row0 * g.F, g.F, [&](int r) { return min(r, rows - 1); },
+      W + (int64_t)nt * GBN * g.F, g.F, [&](int r) { return min(r, nv - 1); });
   GAcc acc;
   gemm_zero(acc);
-  gemm_mainloop(ap, bp, g.ktiles, acc, lds);
+  gemm_mainloop(ops, g.ktiles, acc, lds);
 #pragma unroll
   for (int i = 0; i < GTM; ++i)
 #pragma unroll
@@ -225,6 +262,10 @@ static int dense(const char *name, void (*k)(DenseArgs), int M, int N, int nseg,
   a.nseg = nseg;
   for (int i = 0; i < nseg; ++i) {
     if (segs[i].K % GBK) return fail(MOE_ERR_UNSUPPORTED, "%s: K %% %d != 0", name, GBK);
+    // copy offsets within one 256-row tile are 32-bit
+    if ((segs[i].lda | segs[i].ldb) < 0 || segs[i].lda * 2 * GBM > INT32_MAX ||
+        segs[i].ldb * 2 * GBN > INT32_MAX)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: row stride too large", name);
     a.A[i] = segs[i].A;
     a.lda[i] = segs[i].lda;
     a.B[i] = segs[i].B;
@@ -243,7 +284,11 @@ int gemm_latent_down(int M, int N, const DenseSeg &seg, uint16_t *C, int64_t ldc
 
 int gemm_up_shared(int M, int N, int nseg, const DenseSeg *segs, uint16_t *C, int64_t ldc,
                    hipStream_t s) {
-  return dense("gemm_up_shared", gemm_up_shared_kernel, M, N, nseg, segs, C, ldc, s);
+  static void (*const k[MAXSEG])(DenseArgs) = {gemm_up_shared_kernel<1>, gemm_up_shared_kernel<2>,
+                                               gemm_up_shared_kernel<3>, gemm_up_shared_kernel<4>,
+                                               gemm_up_shared_kernel<5>};
+  if (nseg < 1 || nseg > MAXSEG) return fail(MOE_ERR_INVALID, "gemm_up_shared: bad segment count");
+  return dense("gemm_up_shared", k[nseg - 1], M, N, nseg, segs, C, ldc, s);
 }
 
 int gemm_shared_swiglu(int M, const uint16_t *x, int64_t ldx, int K, const uint16_t *wg,
