@@ -8,7 +8,7 @@ buffer (pools that all source shards packed for this rank -- built once,
 untimed, by a device-copy loopback that stands in for the all-to-all),
 run the six local experts, and combine (identity return loopback).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--rank R]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--rank R|hot]
 Prints one JSON line.
 """
 import argparse
@@ -51,8 +51,13 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False, keep_logits=False)
 
     snd = share.Sender(d, device)
     R, W = d.n_ranks, d.n_waves
+    El = cfg.experts_per_rank
     st.sent_demand = 0
     st.sent_fill = 0
+    # kept sender rows per (destination rank, wave, local expert), all shards:
+    # what every rank's bank step would see (drop statistics, hottest rank)
+    st.recv_counts = torch.zeros(R * W * El, dtype=torch.int64, device=device)
+    wave_of = torch.arange(cfg.T, device=device) // -(-cfg.T // W)
     st.host_logits = [] if keep_logits else None
     if d.cap_send:
         st.n_recv_rows = R * W * d.cap_send
@@ -69,6 +74,9 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False, keep_logits=False)
         snd.pack(x, st.wld)
         st.sent_demand += int(snd.demand.sum())
         st.sent_fill += int(snd.fill.sum())
+        e = snd.topk.long()
+        key = ((e // El) * W + wave_of[:, None]) * El + e % El
+        st.recv_counts += torch.bincount(key[snd.slot >= 0], minlength=R * W * El)
         if d.cap_send:
             rv[s].copy_(snd.pools.view(R, W, d.cap_send, -1)[rank])
         else:
@@ -96,6 +104,60 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False, keep_logits=False)
     st.cmb = share.Combiner(d, device)
     torch.cuda.synchronize()
     return st
+
+
+def receiver_stats(st):
+    """(receiver drop % over all ranks, rank with the most kept received rows)
+    from the kept sender rows of every shard."""
+    d = st.d
+    c = st.recv_counts.view(d.n_ranks, -1)
+    kept = c.clamp(max=d.cap_recv) if d.cap_recv else c
+    total = int(c.sum())
+    pct = 100.0 * (total - int(kept.sum())) / max(total, 1)
+    return pct, int(kept.sum(1).argmax())
+
+
+def path_roofline(kernels, work, ms):
+    """Time the step's kernels would take at the HBM or MFMA peak (whichever
+    bounds each), over the measured step time.  Kernels without an
+    algorithmic figure (slot ranking, flag kernels) count as zero."""
+    t = 0.0
+    for name, (kind, amount) in work.items():
+        n = kernels.get(name, {}).get("launches_per_step", 0)
+        if kind == "flop":
+            t += n * amount / (PEAK_BF16_TFLOPS * 1e12)
+        else:
+            t += n * amount / (PEAK_HBM_GBS * 1e9)
+    return {"ms_at_peaks": round(t * 1e3, 4), "frac": round(t * 1e3 / ms, 4)}
+
+
+def cold_steps(st, steps, flush_bytes=1 << 30):
+    """ms per step when every step starts after a write sweep of flush_bytes
+    (inputs and weights evicted from L2 and the 256 MB MALL, still in HBM);
+    each step is timed alone on the stream the kernels run on."""
+    import torch
+    stream = torch.cuda.current_stream()
+    buf = torch.empty(flush_bytes // 2, dtype=torch.bfloat16, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
+        buf.fill_(1.0)
+        e0.record(stream)
+        step(st)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    del buf
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+
+
+def host_cpu():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def step(st):
@@ -222,7 +284,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=1)
-    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--rank", default="0",
+                    help="rank to measure, or 'hot': the rank with the most kept received rows")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timing (steps after a 1 GiB write sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise device copy of MIB mebibytes, three "
@@ -249,8 +314,15 @@ def main():
         return
 
     cfg = configs.WORKLOADS[args.config]
+    rank = 0 if args.rank == "hot" else int(args.rank)
     log(f"bench: {cfg.name} rank {args.rank}: setup")
-    st = setup(cfg, args.rank, progress=True)
+    st = setup(cfg, rank, progress=True)
+    if args.rank == "hot":
+        rank = receiver_stats(st)[1]
+        if rank != 0:
+            log(f"bench: hottest rank is {rank}: setup again")
+            del st
+            st = setup(cfg, rank, progress=True)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         step(st)
@@ -300,6 +372,7 @@ def main():
         "sender_pct_own_shard": round(100.0 * (dem_s - kept_s) / max(dem_s, 1), 3),
         "sender_pct_all_shards": round(100.0 * (st.sent_demand - st.sent_fill) / max(st.sent_demand, 1), 3),
         "receiver_pct_rank": round(100.0 * (dem_r - kept_r) / max(dem_r, 1), 3),
+        "receiver_pct_all_ranks": round(receiver_stats(st)[0], 3),
         "bad_rows": int(st.rcv.bad_rows[0]),
     }
 
@@ -308,7 +381,15 @@ def main():
         t0 = time.time()
         val, desc = run_cpu_baseline(st)
         cpu = {"value": round(val, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": desc, "wall_s": round(time.time() - t0, 1)}
+               "sample": desc, "wall_s": round(time.time() - t0, 1),
+               "cpu_model": host_cpu(), "host_cpus": os.cpu_count()}
+
+    cold = None
+    if not args.no_cold:
+        cms = cold_steps(st, args.steps)
+        cold = {"ms_per_step": round(cms, 4), "tokens_per_s": round(d.T / (cms * 1e-3), 1),
+                "flush_bytes": 1 << 30}
+        log(f"bench: cold-cache {cms:.3f} ms/step")
 
     tok_s = d.T / (ms * 1e-3)
     line = {
@@ -324,7 +405,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded SplitMix64/Box-Muller inputs; random-init weights)",
-        "config": {"workload": cfg.name, "rank": args.rank, "T": d.T, "d_model": d.d_model,
+        "config": {"workload": cfg.name, "rank": rank, "T": d.T, "d_model": d.d_model,
                    "latent": d.latent, "n_experts": d.n_experts, "n_ranks": d.n_ranks,
                    "top_k": d.top_k, "n_waves": d.n_waves, "d_ff": d.d_ff,
                    "n_shared": d.n_shared, "cap_send": d.cap_send, "cap_recv": d.cap_recv,
@@ -334,6 +415,10 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": counted_traffic(dom, cfg.name)},
         "cpu_baseline": cpu,
+        "path_roofline": path_roofline(kernels, work, ms),
+        "rates": {"assignments_per_s": round(d.T * d.top_k / (ms * 1e-3), 1),
+                  "kept_rows_per_s": round(kept_r / (ms * 1e-3), 1)},
+        "cold_cache": cold,
         "drops": drops,
         "kernels": kernels,
     }
