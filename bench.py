@@ -6,7 +6,9 @@ One step = the whole path for one rank over one source shard of T tokens:
 route the shard's logits, project and pack its pools, bank the receive
 buffer (pools that all source shards packed for this rank -- built once,
 untimed, by a device-copy loopback that stands in for the all-to-all),
-run the six local experts, and combine (identity return loopback).
+run the six local experts, and combine (identity return loopback).  Bank +
+expert FFN and the shared experts run on two more streams beside route +
+pack (no data dependence between them); the combine waits for all three.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--rank R|hot]
 Prints one JSON line.
@@ -102,6 +104,8 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False, keep_logits=False)
     st.snd = share.Sender(d, device)
     st.rcv = share.Receiver(d, st.n_recv_rows, device)
     st.cmb = share.Combiner(d, device)
+    st.s_ffn, st.s_shared = torch.cuda.Stream(device), torch.cuda.Stream(device)
+    st.ev_start, st.ev_ffn, st.ev_shared = (torch.cuda.Event() for _ in range(3))
     torch.cuda.synchronize()
     return st
 
@@ -131,11 +135,12 @@ def path_roofline(kernels, work, ms):
     return {"ms_at_peaks": round(t * 1e3, 4), "frac": round(t * 1e3 / ms, 4)}
 
 
-def cold_steps(st, steps, flush_bytes=1 << 30):
+def cold_steps(st, steps, stepper=None, flush_bytes=1 << 30):
     """ms per step when every step starts after a write sweep of flush_bytes
     (inputs and weights evicted from L2 and the 256 MB MALL, still in HBM);
     each step is timed alone on the stream the kernels run on."""
     import torch
+    stepper = stepper or step
     stream = torch.cuda.current_stream()
     buf = torch.empty(flush_bytes // 2, dtype=torch.bfloat16, device="cuda")
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -143,7 +148,7 @@ def cold_steps(st, steps, flush_bytes=1 << 30):
     for e0, e1 in evs:
         buf.fill_(1.0)
         e0.record(stream)
-        step(st)
+        stepper(st)
         e1.record(stream)
     torch.cuda.synchronize()
     del buf
@@ -161,6 +166,33 @@ def host_cpu():
 
 
 def step(st):
+    """One pass of the path.  Bank + expert FFN (they read the receive buffer
+    of the last exchange) and the shared experts (they read x) do not depend
+    on this step's route and pack, so they run on two more streams, started
+    behind everything already on the main stream; the combine waits for
+    both."""
+    import torch
+    main = torch.cuda.current_stream()
+    st.ev_start.record(main)
+    st.s_ffn.wait_event(st.ev_start)
+    st.s_shared.wait_event(st.ev_start)
+    with torch.cuda.stream(st.s_ffn):
+        st.rcv.bank_rows(st.rank, st.recv, st.recv_offsets)
+        st.rcv.ffn(st.wg, st.wu, st.wd)
+        st.ev_ffn.record(st.s_ffn)
+    with torch.cuda.stream(st.s_shared):
+        st.cmb.shared(st.x, st.wsg, st.wsu)
+        st.ev_shared.record(st.s_shared)
+    st.snd.route(st.logits)
+    st.snd.pack(st.x, st.wld)
+    main.wait_event(st.ev_ffn)
+    main.wait_event(st.ev_shared)
+    st.cmb.combine_shared(st.rcv.ret, st.recv_offsets, st.snd, st.wlu, st.wsd)
+
+
+def step_serial(st):
+    """The same path with every call on one stream, in path order (moe_combine
+    as one call): each kernel runs alone."""
     st.snd.route(st.logits)
     st.snd.pack(st.x, st.wld)
     st.rcv.bank_rows(st.rank, st.recv, st.recv_offsets)
@@ -286,8 +318,10 @@ def main():
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--rank", default="0",
                     help="rank to measure, or 'hot': the rank with the most kept received rows")
-    ap.add_argument("--no-cold", action="store_true",
-                    help="skip the cold-cache timing (steps after a 1 GiB write sweep)")
+    ap.add_argument("--serial", action="store_true",
+                    help="issue the step's calls on one stream (each kernel alone)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps that each follow a 1 GiB write sweep (cold caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise device copy of MIB mebibytes, three "
@@ -323,9 +357,10 @@ def main():
             log(f"bench: hottest rank is {rank}: setup again")
             del st
             st = setup(cfg, rank, progress=True)
+    stepfn = step_serial if args.serial else step
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        step(st)
+        stepfn(st)
     torch.cuda.synchronize()
     log("bench: warmup done")
 
@@ -334,17 +369,20 @@ def main():
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
-        step(st)
+        stepfn(st)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"bench: {args.steps} steps, {ms:.3f} ms/step")
 
-    # per-kernel durations: the library brackets each launch with hipEvents
+    # per-kernel durations: the library brackets each launch with hipEvents.
+    # This pass issues the calls on one stream, so that each kernel runs alone
+    # (in the three-stream step a kernel's duration depends on what it
+    # happens to share the GPU with).
     moe.moe_profile_reset()
     moe.moe_profile_enable(True)
     for _ in range(args.steps):
-        step(st)
+        step_serial(st)
     moe.moe_profile_collect()
     moe.moe_profile_enable(False)
     prof = moe.moe_profile_read()
@@ -385,8 +423,8 @@ def main():
                "cpu_model": host_cpu(), "host_cpus": os.cpu_count()}
 
     cold = None
-    if not args.no_cold:
-        cms = cold_steps(st, args.steps)
+    if args.cold:
+        cms = cold_steps(st, args.steps, stepfn)
         cold = {"ms_per_step": round(cms, 4), "tokens_per_s": round(d.T / (cms * 1e-3), 1),
                 "flush_bytes": 1 << 30}
         log(f"bench: cold-cache {cms:.3f} ms/step")
@@ -409,8 +447,10 @@ def main():
                    "latent": d.latent, "n_experts": d.n_experts, "n_ranks": d.n_ranks,
                    "top_k": d.top_k, "n_waves": d.n_waves, "d_ff": d.d_ff,
                    "n_shared": d.n_shared, "cap_send": d.cap_send, "cap_recv": d.cap_recv,
-                   "source_shards": cfg.n_shards},
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                   "source_shards": cfg.n_shards, "streams": 1 if args.serial else 3},
+        "roofline": {"kernel": dom, "bound": "mfma", "measured": "per-kernel pass after the "
+                     "timed steps, calls on one stream (each kernel alone)",
+                     "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": counted_traffic(dom, cfg.name)},

@@ -53,6 +53,9 @@ _SIGS = {
                                       _VP, _I64, _VP]),
     "moe_combine": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                    _VP, _VP, _I64, _VP]),
+    "moe_shared_swiglu": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP]),
+    "moe_combine_shared": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                          _VP]),
     "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_profile_collect": (ctypes.c_int, []),
     "moe_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.c_char_p, ctypes.c_int,
@@ -154,6 +157,18 @@ def moe_combine(d, returned, ret_offsets, topk, slot, gates, x, w_lat_up, ws_gat
     _check(lib().moe_combine(ctypes.byref(d), _p(returned), _p(ret_offsets), _p(topk),
                              _p(slot), _p(gates), _p(x), _p(w_lat_up), _p(ws_gate), _p(ws_up),
                              _p(ws_down), _p(ylat), _p(out), _p(ws), nbytes, _stream(stream)))
+
+
+def moe_shared_swiglu(d, x, ws_gate, ws_up, h_shared, stream=None):
+    _check(lib().moe_shared_swiglu(ctypes.byref(d), _p(x), _p(ws_gate), _p(ws_up), _p(h_shared),
+                                   _stream(stream)))
+
+
+def moe_combine_shared(d, returned, ret_offsets, topk, slot, gates, w_lat_up, h_shared, ws_down,
+                       ylat, out, stream=None):
+    _check(lib().moe_combine_shared(ctypes.byref(d), _p(returned), _p(ret_offsets), _p(topk),
+                                    _p(slot), _p(gates), _p(w_lat_up), _p(h_shared),
+                                    _p(ws_down), _p(ylat), _p(out), _stream(stream)))
 
 
 def moe_profile_enable(on: bool):

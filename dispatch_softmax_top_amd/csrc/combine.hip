@@ -88,41 +88,12 @@ static int gather(const moe_dims &d, const uint16_t *returned, const int64_t *re
                 d.latent, experts_per_rank(d), d.n_waves, tokens_per_wave(d), d.cap_send);
 }
 
-}  // namespace moe
-
-using namespace moe;
-
-extern "C" int moe_combine(const moe_dims *d, const moe_bf16 *returned, const int64_t *ret_offsets,
-                           const int32_t *topk, const int32_t *slot, const float *gates,
-                           const moe_bf16 *x, const moe_bf16 *w_lat_up, const moe_bf16 *ws_gate,
-                           const moe_bf16 *ws_up, const moe_bf16 *ws_down, moe_bf16 *ylat,
-                           moe_bf16 *out, void *ws, int64_t ws_bytes, void *stream) {
-  clear_error();
-  MOE_TRY(check_dims(d));
-  const bool rg = ragged(*d);
-  MOE_TRY(check_ptr(returned, "returned"));
-  MOE_TRY(check_ptr(topk, "topk"));
-  MOE_TRY(check_ptr(slot, "slot"));
-  MOE_TRY(check_ptr(gates, "gates"));
-  MOE_TRY(check_ptr(x, "x"));
-  MOE_TRY(check_ptr(w_lat_up, "w_lat_up"));
-  MOE_TRY(check_ptr(ylat, "ylat"));
-  MOE_TRY(check_ptr(out, "out"));
-  if (d->n_shared > 0) {
-    MOE_TRY(check_ptr(ws_gate, "ws_gate"));
-    MOE_TRY(check_ptr(ws_up, "ws_up"));
-    MOE_TRY(check_ptr(ws_down, "ws_down"));
-  }
-  if (rg) MOE_TRY(check_ptr(ret_offsets, "ret_offsets (ragged mode)"));
-  const int64_t need = moe_workspace_bytes(d, MOE_CALL_COMBINE, 0);
-  if (need < 0) return (int)need;
-  if (ws_bytes < need || (need > 0 && !ws))
-    return fail(MOE_ERR_WORKSPACE, "moe_combine: workspace %lld < %lld bytes",
-                (long long)ws_bytes, (long long)need);
-  if (ws) MOE_TRY(check_ptr(ws, "ws"));
-  if (d->latent > 8 * 64 * 16) return fail(MOE_ERR_UNSUPPORTED, "moe_combine: latent <= 8192");
-  hipStream_t s = (hipStream_t)stream;
-
+// gather + up-projection with the shared experts' intermediate H [T, S*Fs]
+static int combine_rest(const moe_dims *d, const uint16_t *returned, const int64_t *ret_offsets,
+                        const int32_t *topk, const int32_t *slot, const float *gates,
+                        const uint16_t *w_lat_up, const uint16_t *H, const uint16_t *ws_down,
+                        uint16_t *ylat, uint16_t *out, hipStream_t s) {
+  if (d->latent > 8 * 64 * 16) return fail(MOE_ERR_UNSUPPORTED, "combine: latent <= 8192");
   const int ch = (int)cdiv(d->latent / 8, 64);
   int rc;
   if (ch <= 1) rc = gather<1>(*d, returned, ret_offsets, topk, slot, gates, ylat, s);
@@ -132,14 +103,87 @@ extern "C" int moe_combine(const moe_dims *d, const moe_bf16 *returned, const in
   else if (ch <= 8) rc = gather<8>(*d, returned, ret_offsets, topk, slot, gates, ylat, s);
   else rc = gather<16>(*d, returned, ret_offsets, topk, slot, gates, ylat, s);
   MOE_TRY(rc);
-
   const int S = d->n_shared, Fs = d->d_ff_shared;
-  uint16_t *H = (uint16_t *)ws;
-  MOE_TRY(gemm_shared_swiglu(d->T, x, d->d_model, d->d_model, ws_gate, ws_up, S, Fs, H, s));
   DenseSeg segs[1 + 4];
   segs[0] = DenseSeg{ylat, d->latent, w_lat_up, d->latent, d->latent};
   for (int i = 0; i < S; ++i)
     segs[1 + i] = DenseSeg{H + (int64_t)i * Fs, (int64_t)S * Fs,
                            ws_down + (int64_t)i * d->d_model * Fs, Fs, Fs};
   return gemm_up_shared(d->T, d->d_model, 1 + S, segs, out, d->d_model, s);
+}
+
+static int check_rest(const moe_dims *d, const moe_bf16 *returned, const int64_t *ret_offsets,
+                      const int32_t *topk, const int32_t *slot, const float *gates,
+                      const moe_bf16 *w_lat_up, const moe_bf16 *ws_down, moe_bf16 *ylat,
+                      moe_bf16 *out) {
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_ptr(returned, "returned"));
+  MOE_TRY(check_ptr(topk, "topk"));
+  MOE_TRY(check_ptr(slot, "slot"));
+  MOE_TRY(check_ptr(gates, "gates"));
+  MOE_TRY(check_ptr(w_lat_up, "w_lat_up"));
+  MOE_TRY(check_ptr(ylat, "ylat"));
+  MOE_TRY(check_ptr(out, "out"));
+  if (d->n_shared > 0) MOE_TRY(check_ptr(ws_down, "ws_down"));
+  if (ragged(*d)) MOE_TRY(check_ptr(ret_offsets, "ret_offsets (ragged mode)"));
+  return MOE_OK;
+}
+
+static int check_shared(const moe_dims *d, const moe_bf16 *x, const moe_bf16 *ws_gate,
+                        const moe_bf16 *ws_up) {
+  MOE_TRY(check_ptr(x, "x"));
+  if (d->n_shared > 0) {
+    MOE_TRY(check_ptr(ws_gate, "ws_gate"));
+    MOE_TRY(check_ptr(ws_up, "ws_up"));
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_shared_swiglu(const moe_dims *d, const moe_bf16 *x, const moe_bf16 *ws_gate,
+                                 const moe_bf16 *ws_up, moe_bf16 *h_shared, void *stream) {
+  clear_error();
+  MOE_TRY(check_dims(d));
+  MOE_TRY(check_shared(d, x, ws_gate, ws_up));
+  if (d->n_shared > 0) MOE_TRY(check_ptr(h_shared, "h_shared"));
+  return gemm_shared_swiglu(d->T, x, d->d_model, d->d_model, ws_gate, ws_up, d->n_shared,
+                            d->d_ff_shared, h_shared, (hipStream_t)stream);
+}
+
+extern "C" int moe_combine_shared(const moe_dims *d, const moe_bf16 *returned,
+                                  const int64_t *ret_offsets, const int32_t *topk,
+                                  const int32_t *slot, const float *gates,
+                                  const moe_bf16 *w_lat_up, const moe_bf16 *h_shared,
+                                  const moe_bf16 *ws_down, moe_bf16 *ylat, moe_bf16 *out,
+                                  void *stream) {
+  clear_error();
+  MOE_TRY(check_rest(d, returned, ret_offsets, topk, slot, gates, w_lat_up, ws_down, ylat, out));
+  if (d->n_shared > 0) MOE_TRY(check_ptr(h_shared, "h_shared"));
+  return combine_rest(d, returned, ret_offsets, topk, slot, gates, w_lat_up, h_shared, ws_down,
+                      ylat, out, (hipStream_t)stream);
+}
+
+extern "C" int moe_combine(const moe_dims *d, const moe_bf16 *returned, const int64_t *ret_offsets,
+                           const int32_t *topk, const int32_t *slot, const float *gates,
+                           const moe_bf16 *x, const moe_bf16 *w_lat_up, const moe_bf16 *ws_gate,
+                           const moe_bf16 *ws_up, const moe_bf16 *ws_down, moe_bf16 *ylat,
+                           moe_bf16 *out, void *ws, int64_t ws_bytes, void *stream) {
+  clear_error();
+  MOE_TRY(check_rest(d, returned, ret_offsets, topk, slot, gates, w_lat_up, ws_down, ylat, out));
+  MOE_TRY(check_shared(d, x, ws_gate, ws_up));
+  const int64_t need = moe_workspace_bytes(d, MOE_CALL_COMBINE, 0);
+  if (need < 0) return (int)need;
+  if (ws_bytes < need || (need > 0 && !ws))
+    return fail(MOE_ERR_WORKSPACE, "moe_combine: workspace %lld < %lld bytes",
+                (long long)ws_bytes, (long long)need);
+  if (ws) MOE_TRY(check_ptr(ws, "ws"));
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t *H = (uint16_t *)ws;
+  MOE_TRY(gemm_shared_swiglu(d->T, x, d->d_model, d->d_model, ws_gate, ws_up, d->n_shared,
+                             d->d_ff_shared, H, s));
+  return combine_rest(d, returned, ret_offsets, topk, slot, gates, w_lat_up, H, ws_down, ylat,
+                      out, s);
 }

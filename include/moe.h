@@ -201,6 +201,26 @@ int moe_combine(const moe_dims *d, const moe_bf16 *returned,
                 const moe_bf16 *ws_up, const moe_bf16 *ws_down, moe_bf16 *ylat,
                 moe_bf16 *out, void *ws, int64_t ws_bytes, void *stream);
 
+/* The same combine as two calls.  The shared experts read only x, so a
+ * caller can run them on another stream while the routed experts run.
+ *   moe_shared_swiglu   h_shared[t, s*d_ff_shared + f] =
+ *                       bf16(silu(x.W_sg,s) * (x.W_su,s))[t, f]
+ *     x, ws_gate, ws_up  as in moe_combine
+ *     h_shared     [T, n_shared*d_ff_shared] bf16 out (n_shared == 0: no-op)
+ *   moe_combine_shared  ylat and out exactly as moe_combine, with the shared
+ *                       experts' intermediate read from h_shared; no
+ *                       workspace.  Other arguments as in moe_combine.
+ * moe_combine equals moe_shared_swiglu into its workspace followed by
+ * moe_combine_shared, bit for bit.  Errors as for moe_combine. */
+int moe_shared_swiglu(const moe_dims *d, const moe_bf16 *x, const moe_bf16 *ws_gate,
+                      const moe_bf16 *ws_up, moe_bf16 *h_shared, void *stream);
+int moe_combine_shared(const moe_dims *d, const moe_bf16 *returned,
+                       const int64_t *ret_offsets, const int32_t *topk,
+                       const int32_t *slot, const float *gates,
+                       const moe_bf16 *w_lat_up, const moe_bf16 *h_shared,
+                       const moe_bf16 *ws_down, moe_bf16 *ylat, moe_bf16 *out,
+                       void *stream);
+
 /* Kernel timing.  While enabled, every kernel the library launches is
  * bracketed by two hipEvents on its stream.  moe_profile_collect()
  * waits for the recorded events and folds them into per-kernel totals;

@@ -94,6 +94,12 @@ def test_calls_reject_null_and_misaligned(moe):
                             None) == -1
     assert L.moe_combine(ctypes.byref(d), p, None, p, p, p, p, p, p, p, p, p, p, None, 0,
                          None) == -4                                # workspace too small
+    assert L.moe_shared_swiglu(ctypes.byref(d), None, p, p, p, None) == -1
+    assert L.moe_shared_swiglu(ctypes.byref(d), p, p, p, None, None) == -1   # h_shared
+    assert L.moe_combine_shared(ctypes.byref(d), p, None, p, p, p, p, None, p, p, p,
+                                None) == -1                        # h_shared
+    assert L.moe_combine_shared(ctypes.byref(d), p, None, p, p, p, p, p, p, None, p,
+                                None) == -1                        # ylat
 
 
 def test_workspace_sizes_grow_with_rows(moe):

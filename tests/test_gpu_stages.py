@@ -245,3 +245,32 @@ def test_combine(moe, orc, share, name):
                          u16(wlu), u16(wsg), u16(wsu), u16(wsd))
     gc.assert_rows_close(gc.host(cmb.ylat), yo, "ylat")
     gc.assert_rows_close(gc.host(cmb.out), oo, "out")
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_ragged"])
+def test_combine_split_equals_combine(moe, share, name):
+    """moe_shared_swiglu + moe_combine_shared give moe_combine's outputs bit
+    for bit (same kernels, the shared intermediate in a caller buffer)."""
+    cfg = CASES[name]
+    d = share.make_dims(cfg)
+    R, W = cfg.n_ranks, cfg.n_waves
+    n = R * W * d.cap_send if d.cap_send else 3 * R * W
+    returned = gen.payload_rows(n, d.latent, 21, "cuda")
+    offs = None if d.cap_send else torch.arange(0, n + 1, 3, dtype=torch.int64, device="cuda")
+    g = torch.Generator().manual_seed(5)
+    snd = share.Sender(d)
+    snd.topk.copy_(torch.randint(0, cfg.n_experts, (cfg.T, cfg.top_k), generator=g))
+    snd.slot.copy_(torch.randint(-1, 3, (cfg.T, cfg.top_k), generator=g))
+    snd.gates.copy_(torch.rand(cfg.T, cfg.top_k, generator=g))
+    x = gen.hidden(cfg, 0, "cuda")
+    wlu = gen.latent_up(cfg, "cuda")
+    wsg, wsu, wsd = gen.shared(cfg, "cuda")
+    a = share.Combiner(d)
+    a.combine(returned, offs, snd, x, wlu, wsg, wsu, wsd)
+    b = share.Combiner(d)
+    b.shared(x, wsg, wsu)
+    b.combine_shared(returned, offs, snd, wlu, wsd)
+    torch.cuda.synchronize()
+    assert torch.equal(a.ylat.view(torch.int16), b.ylat.view(torch.int16))
+    assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+
