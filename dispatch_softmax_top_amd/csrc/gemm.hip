@@ -94,6 +94,86 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
 }
 
 // ---------------------------------------------------------------------------
+// grouped rows: the bank's groups (wave w, local expert j) = group w * El + j
+// ---------------------------------------------------------------------------
+
+constexpr int GMAXW = 4;  // waves merged into one product group at most
+
+// nw == 1: every bank group is a product group.  nw == n_waves: product
+// group j holds local expert j's rows of every wave (same weights), in wave
+// order, so its last 256-row tile is padded once instead of once per wave.
+struct GroupArgs {
+  int G, El, cap, nw;
+  const int32_t *count;    // [G] rows per bank group
+  const int64_t *offsets;  // ragged: [G+1] first row per bank group; NULL if fixed
+};
+
+// One block tile of a grouped product: its product group's segments (one
+// per merged wave) and the tile's first row within the group.
+struct GTile {
+  int expert, rows, mt, nt, nseg, v0;
+  int64_t start[GMAXW];  // bank row of each segment's first row
+  int cum[GMAXW];        // group rows up to the end of each segment
+  // bank row of tile row m (m < rows)
+  __device__ __forceinline__ int64_t row(int m) const {
+    const int v = v0 + m;
+    int64_t r = start[0] + v;
+#pragma unroll
+    for (int s = 1; s < GMAXW; ++s)
+      if (s < nseg && v >= cum[s - 1]) r = start[s] + (v - cum[s - 1]);
+    return r;
+  }
+};
+
+__device__ __forceinline__ int group_seg(const GroupArgs &a, int pg, int s) {
+  return a.nw == 1 ? pg : s * a.El + pg;
+}
+
+__device__ __forceinline__ int group_rows(const GroupArgs &a, int pg) {
+  int c = 0;
+  for (int s = 0; s < a.nw; ++s) c += a.count[group_seg(a, pg, s)];
+  return c;
+}
+
+// This block's tile: product groups in order, each contributing
+// ceil(rows / 256) * tn tiles.  The grid is an upper bound; the real count
+// is known only here, so blocks remap over it (each XCD gets a contiguous
+// range of real tiles) and blocks past it exit (returns false).
+__device__ __forceinline__ bool group_tile(const GroupArgs &a, int tn, GTile &t) {
+  const int npg = a.G / a.nw;
+  int total = 0;
+  for (int pg = 0; pg < npg; ++pg) total += ((group_rows(a, pg) + GBM - 1) / GBM) * tn;
+  if ((int)blockIdx.x >= total) return false;
+  int rem = xcd_remap(blockIdx.x, total);
+  for (int pg = 0; pg < npg; ++pg) {
+    const int c = group_rows(a, pg);
+    const int tmg = (c + GBM - 1) / GBM;
+    if (rem < tmg * tn) {
+      g_tile_coords(rem, tmg, tn, t.mt, t.nt);
+      t.expert = group_seg(a, pg, 0) % a.El;
+      t.v0 = t.mt * GBM;
+      t.rows = min(GBM, c - t.v0);
+      t.nseg = a.nw;
+      int cum = 0;
+#pragma unroll
+      for (int s = 0; s < GMAXW; ++s) {
+        if (s < a.nw) {
+          const int g = group_seg(a, pg, s);
+          t.start[s] = a.offsets ? a.offsets[g] : (int64_t)g * a.cap;
+          cum += a.count[g];
+        } else {
+          t.start[s] = 0;
+        }
+        t.cum[s] = cum;
+      }
+      return true;
+    }
+    rem -= tmg * tn;
+  }
+  return false;
+}
+
+// ---------------------------------------------------------------------------
 // SwiGLU
 // ---------------------------------------------------------------------------
 
@@ -109,12 +189,13 @@ struct SwigluArgs {
   // dense (shared experts): M rows, expert = f-tile / ftiles along N
   int M, S;
   // grouped (routed experts)
-  int G, El, cap;
-  const int32_t *count;      // [G] rows per group
-  const int64_t *offsets;    // ragged: [G+1] first row per group; NULL if fixed
+  GroupArgs grp;
 };
 
-__device__ __forceinline__ void swiglu_tile(const SwigluArgs &g, int row0, int rows, int expert,
+// row_of(m): row of A and H for tile row m < rows (contiguous rows, or the
+// bank rows of a grouped tile).
+template <class RowOf>
+__device__ __forceinline__ void swiglu_tile(const SwigluArgs &g, RowOf row_of, int rows, int expert,
                                             int ft, int h_col0, const GemmLds &lds) {
   const int f0 = ft * 128;
   const int64_t eoff = (int64_t)expert * g.F * g.ldb + (int64_t)f0 * g.ldb;
@@ -124,8 +205,9 @@ __device__ __forceinline__ void swiglu_tile(const SwigluArgs &g, int row0, int r
   bool up;
   int foff;
   g_swiglu_brow(g_load_row(0), up, foff);
+  const int64_t r0 = row_of(0);
   const auto ops = g_operands(
-      g.A + (int64_t)row0 * g.lda, g.lda, [&](int r) { return min(r, rows - 1); },
+      g.A + r0 * g.lda, g.lda, [&](int r) { return (int)(row_of(min(r, rows - 1)) - r0); },
       (up ? g.Bu : g.Bg) + eoff, g.ldb, [&](int r) {
         bool u;
         int f;
@@ -136,19 +218,18 @@ __device__ __forceinline__ void swiglu_tile(const SwigluArgs &g, int row0, int r
   gemm_zero(acc);
   gemm_mainloop(ops, g.ktiles, acc, lds);
 #pragma unroll
-  for (int p = 0; p < GTN / 2; ++p) {
-    const int f = f0 + g_swiglu_col(p);
+  for (int i = 0; i < GTM; ++i)
 #pragma unroll
-    for (int i = 0; i < GTM; ++i)
+    for (int v = 0; v < 16; ++v) {
+      const int m = g_acc_row(i, v);
+      if (m >= rows) continue;
+      uint16_t *h = g.H + row_of(m) * g.ldh + h_col0 + f0;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = g_acc_row(i, v);
-        if (m < rows) {
-          const float a = acc[i][2 * p][v], b = acc[i][2 * p + 1][v];
-          g.H[(int64_t)(row0 + m) * g.ldh + h_col0 + f] = f32_to_bf16(silu_f32(a) * b);
-        }
+      for (int p = 0; p < GTN / 2; ++p) {
+        const float a = acc[i][2 * p][v], b = acc[i][2 * p + 1][v];
+        h[g_swiglu_col(p)] = f32_to_bf16(silu_f32(a) * b);
       }
-  }
+    }
 }
 
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_shared_swiglu_kernel(SwigluArgs g) {
@@ -157,49 +238,15 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
   int mt, nt;
   g_tile_coords(xcd_remap(blockIdx.x, gridDim.x), tm, tn, mt, nt);
   const int s = nt / g.ftiles, ft = nt % g.ftiles;
-  swiglu_tile(g, mt * GBM, min(GBM, g.M - mt * GBM), s, ft, s * g.F, lds);
-}
-
-// Tiles of the grouped product: groups in order, each contributing
-// ceil(rows / 256) * tn tiles.  The grid is an upper bound; the real count
-// is known only here, so blocks remap over it (each XCD gets a contiguous
-// range of real tiles) and blocks past it exit.
-__device__ __forceinline__ int group_tiles_total(int G, const int32_t *count, int tn) {
-  int total = 0;
-  for (int g = 0; g < G; ++g) total += ((count[g] + GBM - 1) / GBM) * tn;
-  return total;
-}
-
-// Find (group, m-tile, n-tile) of this block's tile.  Returns false for a
-// block past the real tile count.
-__device__ __forceinline__ bool group_tile(int G, const int32_t *count, const int64_t *offsets,
-                                           int cap, int tn, int &g, int &row0, int &rows,
-                                           int &mt, int &nt) {
-  const int total = group_tiles_total(G, count, tn);
-  if ((int)blockIdx.x >= total) return false;
-  int rem = xcd_remap(blockIdx.x, total);
-  for (g = 0; g < G; ++g) {
-    const int c = count[g];
-    const int tiles = ((c + GBM - 1) / GBM) * tn;
-    if (rem < tiles) {
-      const int tmg = (c + GBM - 1) / GBM;
-      g_tile_coords(rem, tmg, tn, mt, nt);
-      const int64_t start = offsets ? offsets[g] : (int64_t)g * cap;
-      row0 = (int)start + mt * GBM;
-      rows = min(GBM, c - mt * GBM);
-      return true;
-    }
-    rem -= tiles;
-  }
-  return false;
+  const int64_t row0 = (int64_t)mt * GBM;
+  swiglu_tile(g, [&](int m) { return row0 + m; }, min(GBM, g.M - mt * GBM), s, ft, s * g.F, lds);
 }
 
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_swiglu_kernel(SwigluArgs g) {
   MOE_GEMM_LDS(lds);
-  int grp, row0, rows, mt, nt;
-  if (!group_tile(g.G, g.count, g.offsets, g.cap, g.ftiles, grp, row0, rows, mt, nt))
-    return;
-  swiglu_tile(g, row0, rows, grp % g.El, nt, 0, lds);
+  GTile t;
+  if (!group_tile(g.grp, g.ftiles, t)) return;
+  swiglu_tile(g, [&](int m) { return t.row(m); }, t.rows, t.expert, t.nt, 0, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -211,9 +258,7 @@ struct DownArgs {
   int F, ktiles;
   const uint16_t *Wd;  // [El][L][F]
   int L, tn;
-  int G, El, cap;
-  const int32_t *count;
-  const int64_t *offsets;
+  GroupArgs grp;
   const int32_t *bank_src;
   uint16_t *ret;  // [ret rows][L]
   int64_t n_ret;
@@ -221,14 +266,14 @@ struct DownArgs {
 
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_down_kernel(DownArgs g) {
   MOE_GEMM_LDS(lds);
-  int grp, row0, rows, mt, nt;
-  if (!group_tile(g.G, g.count, g.offsets, g.cap, g.tn, grp, row0, rows, mt, nt))
-    return;
-  const uint16_t *W = g.Wd + (int64_t)(grp % g.El) * g.L * g.F;
-  const int nv = g.L - nt * GBN;
+  GTile t;
+  if (!group_tile(g.grp, g.tn, t)) return;
+  const uint16_t *W = g.Wd + (int64_t)t.expert * g.L * g.F;
+  const int nv = g.L - t.nt * GBN, rows = t.rows;
+  const int64_t r0 = t.row(0);
   const auto ops = g_operands(
-      g.H + (int64_t)row0 * g.F, g.F, [&](int r) { return min(r, rows - 1); },
-      W + (int64_t)nt * GBN * g.F, g.F, [&](int r) { return min(r, nv - 1); });
+      g.H + r0 * g.F, g.F, [&](int r) { return (int)(t.row(min(r, rows - 1)) - r0); },
+      W + (int64_t)t.nt * GBN * g.F, g.F, [&](int r) { return min(r, nv - 1); });
   GAcc acc;
   gemm_zero(acc);
   gemm_mainloop(ops, g.ktiles, acc, lds);
@@ -238,12 +283,12 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
     for (int v = 0; v < 16; ++v) {
       const int m = g_acc_row(i, v);
       if (m >= rows) continue;
-      const int64_t dr = g.bank_src[row0 + m];
+      const int64_t dr = g.bank_src[t.row(m)];
       if (dr < 0 || dr >= g.n_ret) continue;
       const int64_t dst = dr * g.L;
 #pragma unroll
       for (int j = 0; j < GTN; ++j) {
-        const int n = nt * GBN + g_acc_col(j);
+        const int n = t.nt * GBN + g_acc_col(j);
         if (n < g.L) g.ret[dst + n] = f32_to_bf16(acc[i][j][v]);
       }
     }
@@ -312,6 +357,23 @@ int gemm_shared_swiglu(int M, const uint16_t *x, int64_t ldx, int K, const uint1
                 0, s, a);
 }
 
+// Product groups of the bank: each local expert over every wave when the
+// merged rows stay within 32-bit copy offsets of a tile's first row, else
+// every (wave, expert) group alone.
+static GroupArgs group_args(const moe_dims &d, const int64_t *bank_offsets, const int32_t *bfill,
+                            int64_t n_bank_rows) {
+  GroupArgs g{};
+  g.El = experts_per_rank(d);
+  g.G = d.n_waves * g.El;
+  g.cap = d.cap_recv;
+  g.count = bfill;
+  g.offsets = ragged(d) ? bank_offsets : nullptr;
+  const int64_t width = d.latent > d.d_ff ? d.latent : d.d_ff;
+  const bool merge = d.n_waves <= GMAXW && n_bank_rows * width * 2 < INT32_MAX;
+  g.nw = merge ? d.n_waves : 1;
+  return g;
+}
+
 static int64_t grouped_tiles_bound(const moe_dims &d, int64_t n_bank_rows, int tn) {
   const int64_t G = (int64_t)d.n_waves * experts_per_rank(d);
   const int64_t mt = ragged(d) ? cdiv(n_bank_rows, GBM) + G : G * cdiv(d.cap_recv, GBM);
@@ -332,11 +394,7 @@ int gemm_expert_swiglu(const moe_dims &d, const uint16_t *bank, const int64_t *b
   a.ftiles = d.d_ff / 128;
   a.H = H;
   a.ldh = d.d_ff;
-  a.G = d.n_waves * experts_per_rank(d);
-  a.El = experts_per_rank(d);
-  a.cap = d.cap_recv;
-  a.count = bfill;
-  a.offsets = ragged(d) ? bank_offsets : nullptr;
+  a.grp = group_args(d, bank_offsets, bfill, n_bank_rows);
   const int64_t tiles = grouped_tiles_bound(d, n_bank_rows, a.ftiles);
   return launch("gemm_expert_swiglu", gemm_expert_swiglu_kernel, dim3((unsigned)tiles), dim3(GNT),
                 0, s, a);
@@ -353,11 +411,7 @@ int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_o
   a.Wd = wd;
   a.L = d.latent;
   a.tn = (int)cdiv(d.latent, GBN);
-  a.G = d.n_waves * experts_per_rank(d);
-  a.El = experts_per_rank(d);
-  a.cap = d.cap_recv;
-  a.count = bfill;
-  a.offsets = ragged(d) ? bank_offsets : nullptr;
+  a.grp = group_args(d, bank_offsets, bfill, n_bank_rows);
   a.bank_src = bank_src;
   a.ret = ret;
   const int64_t tiles = grouped_tiles_bound(d, n_bank_rows, a.tn);

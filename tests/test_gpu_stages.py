@@ -23,6 +23,9 @@ CASES = {
     "mid_ragged": gc.ragged(gc.MID),
     "mid_zipf": gc.skewed(gc.MID),
     "mid_tight": gc.with_cf(gc.MID, "1/2", "3/5"),
+    # more waves than the grouped GEMM merges into one product group: every
+    # (wave, expert) bank group is its own product group
+    "mid_w5": configs.scaled(gc.MID, gc.MID.name + "_W5", n_waves=5),
 }
 
 
