@@ -51,6 +51,8 @@ int check_dims(const moe_dims *d) {
     return fail(MOE_ERR_UNSUPPORTED, "dims: n_experts <= 1024 and top_k <= 32 supported");
   if (d->latent % 64 || d->d_model % 64)
     return fail(MOE_ERR_UNSUPPORTED, "dims: latent and d_model must be multiples of 64");
+  // the row-copy kernels keep a whole latent row in registers (16 chunks per lane)
+  if (d->latent > 8192) return fail(MOE_ERR_UNSUPPORTED, "dims: latent <= 8192");
   if (d->d_ff % 128 || d->d_ff_shared % 128)
     return fail(MOE_ERR_UNSUPPORTED, "dims: d_ff and d_ff_shared must be multiples of 128");
   if ((int64_t)d->n_ranks * d->n_waves > 1024 ||
@@ -59,6 +61,8 @@ int check_dims(const moe_dims *d) {
   if (d->n_shared > 4) return fail(MOE_ERR_UNSUPPORTED, "dims: n_shared <= 4");
   if ((int64_t)d->T * d->top_k >= (1ll << 31))
     return fail(MOE_ERR_UNSUPPORTED, "dims: T * top_k must fit in int32");
+  // the combine runs up to 16 waves per token (one per part of its row)
+  if (d->T > (1 << 27)) return fail(MOE_ERR_UNSUPPORTED, "dims: T <= 2^27");
   return MOE_OK;
 }
 

@@ -15,6 +15,8 @@
 // Kernels, in stream order:
 //   rank_count (also sets bank_src to -1) / rank_assign  bank positions
 //   bank_rows   one wave per bank position: 16-byte copy of the payload
+#include <type_traits>
+
 #include "kernels.h"
 #include "rank.h"
 
@@ -93,6 +95,12 @@ struct BankEmit {
   }
 };
 
+// One wave per bank position; each lane loads all CH of its 16-byte chunks
+// before storing any, so a wave keeps its whole row in flight.  The loads
+// are non-temporal (each received row is read once); the stores are plain,
+// since the expert GEMM reads the bank next (measured: non-temporal loads
+// 69 us, plain 86 us, non-temporal loads and stores 74 us at 4096 tokens).
+template <int CH>
 __global__ __launch_bounds__(256) void bank_rows_kernel(const uint8_t *__restrict__ recv,
                                                         const int32_t *__restrict__ bank_src,
                                                         uint16_t *__restrict__ bank, int L,
@@ -103,7 +111,27 @@ __global__ __launch_bounds__(256) void bank_rows_kernel(const uint8_t *__restric
   if (src < 0) return;
   const u32x4 *in = reinterpret_cast<const u32x4 *>(recv + (int64_t)src * (2 * (int64_t)L + 16));
   u32x4 *out = reinterpret_cast<u32x4 *>(bank + pos * L);
-  for (int c = lane_id(); c < L / 8; c += 64) out[c] = in[c];
+  const int nch = L / 8, lane = lane_id();
+  // loads are never predicated (an index past the row is clamped to its last
+  // chunk), so all CH issue back to back; only a partial row's stores are
+  u32x4 v[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) v[c] = ld16<true>(in + min(lane + 64 * c, nch - 1));
+  if (nch == 64 * CH) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) out[lane + 64 * c] = v[c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (lane + 64 * c < nch) out[lane + 64 * c] = v[c];
+  }
+}
+
+template <int CH>
+static int bank_copy(const moe_dims &d, const uint8_t *recv, const int32_t *bank_src,
+                     uint16_t *bank, int64_t n_bank, hipStream_t s) {
+  return launch("bank_rows", bank_rows_kernel<CH>, dim3((unsigned)cdiv(n_bank, 4)), dim3(256), 0,
+                s, recv, bank_src, bank, d.latent, n_bank);
 }
 
 template <bool RAGGED>
@@ -164,6 +192,15 @@ extern "C" int moe_bank(const moe_dims *d, int32_t rank, const uint8_t *recv,
                                 bdemand, bank_offsets, bad_rows, tc, s)
              : bank_slots<false>(*d, rank, recv, nullptr, n_recv_rows, n_bank, bank_src, bfill,
                                  bdemand, nullptr, bad_rows, tc, s));
-  return launch("bank_rows", bank_rows_kernel, dim3((unsigned)cdiv(n_bank, 4)), dim3(256), 0, s,
-                recv, (const int32_t *)bank_src, bank, d->latent, n_bank);
+  const int ch = (int)cdiv(d->latent / 8, 64);  // latent <= 8192 (check_dims)
+  auto run = [&](auto kernel_ch) {
+    constexpr int CH = decltype(kernel_ch)::value;
+    return bank_copy<CH>(*d, recv, bank_src, bank, n_bank, s);
+  };
+  if (ch <= 1) return run(std::integral_constant<int, 1>());
+  if (ch <= 2) return run(std::integral_constant<int, 2>());
+  if (ch <= 4) return run(std::integral_constant<int, 4>());
+  if (ch <= 6) return run(std::integral_constant<int, 6>());
+  if (ch <= 8) return run(std::integral_constant<int, 8>());
+  return run(std::integral_constant<int, 16>());
 }

@@ -16,6 +16,8 @@
 //   pack_rows                 one wave per token: z[t] read once, written to
 //                             each kept destination row with 16-byte stores;
 //                             extra blocks stamp id -1 on unfilled slots
+#include <type_traits>
+
 #include "gemm.h"
 #include "kernels.h"
 #include "rank.h"
@@ -54,6 +56,9 @@ struct SenderEmit {
   }
 };
 
+// One wave per token: each lane loads all CH of its 16-byte chunks of z[t]
+// first (the whole row in flight), then writes them to every kept row.
+template <int CH>
 __global__ __launch_bounds__(256) void pack_rows_kernel(
     const uint16_t *__restrict__ z, const int32_t *__restrict__ topk,
     const int32_t *__restrict__ slot, const int32_t *__restrict__ fill,
@@ -64,22 +69,32 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(
   if ((int)blockIdx.x < token_blocks) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
+    const int nch = L / 8;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(z + (int64_t)t * L);
+    u32x4 v[CH];  // unpredicated loads (clamped index): all CH in flight at once
+#pragma unroll
+    for (int c = 0; c < CH; ++c) v[c] = src[min(lane + 64 * c, nch - 1)];
     int my_row = -1, my_e = -1;
     if (lane < k) {
       const int s = slot[(int64_t)t * k + lane];
+      const int e = topk[(int64_t)t * k + lane];  // independent of s: same round trip
       if (s >= 0) {
-        const int e = topk[(int64_t)t * k + lane];
         const int p = (e / El) * W + t / Tw;
         my_row = cap ? p * cap + s : (int)pool_offsets[p] + s;
         my_e = e;
       }
     }
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(z + (int64_t)t * L);
-    for (int c = lane; c < L / 8; c += 64) {
-      const u32x4 v = src[c];
-      for (int j = 0; j < k; ++j) {
-        const int row = __shfl(my_row, j);
-        if (row >= 0) *reinterpret_cast<u32x4 *>(pools + row * RB + c * 16) = v;
+    for (int j = 0; j < k; ++j) {
+      const int row = __shfl(my_row, j);
+      if (row < 0) continue;
+      u32x4 *dst = reinterpret_cast<u32x4 *>(pools + row * RB);
+      if (nch == 64 * CH) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) dst[lane + 64 * c] = v[c];
+      } else {
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+          if (lane + 64 * c < nch) dst[lane + 64 * c] = v[c];
       }
     }
     if (my_row >= 0) {
@@ -95,6 +110,17 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(
       *reinterpret_cast<u32x4 *>(pools + idx * RB + 2 * (int64_t)L) = h;
     }
   }
+}
+
+template <int CH>
+static int pack_copy(const moe_dims &d, const uint16_t *z, const int32_t *topk,
+                     const int32_t *slot, const int32_t *fill, const int64_t *pool_offsets,
+                     uint8_t *pools, int token_blocks, int64_t n_slots, hipStream_t s) {
+  const int64_t blocks = token_blocks + cdiv(n_slots, 256);
+  return launch("pack_rows", pack_rows_kernel<CH>, dim3((unsigned)blocks), dim3(256), 0, s, z,
+                topk, slot, fill, pool_offsets, pools, d.T, d.top_k, d.latent,
+                experts_per_rank(d), d.n_waves, tokens_per_wave(d), d.cap_send, token_blocks,
+                n_slots);
 }
 
 template <bool RAGGED>
@@ -149,9 +175,15 @@ extern "C" int moe_pack_waves(const moe_dims *d, const moe_bf16 *x, const moe_bf
   MOE_TRY(gemm_latent_down(d->T, d->latent, seg, z, d->latent, s));
   const int token_blocks = (int)cdiv(d->T, 4);
   const int64_t n_slots = rg ? 0 : (int64_t)d->n_ranks * d->n_waves * d->cap_send;
-  const int64_t blocks = token_blocks + cdiv(n_slots, 256);
-  return launch("pack_rows", pack_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, z, topk,
-                slot, fill, pool_offsets, pools, d->T, d->top_k, d->latent,
-                experts_per_rank(*d), d->n_waves, tokens_per_wave(*d), d->cap_send, token_blocks,
-                n_slots);
+  const int ch = (int)cdiv(d->latent / 8, 64);  // latent <= 8192 (check_dims)
+  auto run = [&](auto kernel_ch) {
+    constexpr int CH = decltype(kernel_ch)::value;
+    return pack_copy<CH>(*d, z, topk, slot, fill, pool_offsets, pools, token_blocks, n_slots, s);
+  };
+  if (ch <= 1) return run(std::integral_constant<int, 1>());
+  if (ch <= 2) return run(std::integral_constant<int, 2>());
+  if (ch <= 4) return run(std::integral_constant<int, 4>());
+  if (ch <= 6) return run(std::integral_constant<int, 6>());
+  if (ch <= 8) return run(std::integral_constant<int, 8>());
+  return run(std::integral_constant<int, 16>());
 }

@@ -78,6 +78,7 @@ typedef enum {
  * (destination, wave) pool and per (wave, local expert) bank; both 0 selects
  * ragged / dropless mode.  Supported: n_experts % n_ranks == 0,
  * n_experts <= 1024, 1 <= top_k <= min(32, n_experts), latent % 64 == 0,
+ * latent <= 8192, T <= 2^27, T * top_k < 2^31,
  * d_model % 64 == 0, d_ff % 128 == 0, d_ff_shared % 128 == 0,
  * n_ranks * n_waves <= 1024, n_waves * E_l <= 1024, n_shared <= 4. */
 typedef struct {
