@@ -271,19 +271,27 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
   const uint16_t *W = g.Wd + (int64_t)t.expert * g.L * g.F;
   const int nv = g.L - t.nt * GBN, rows = t.rows;
   const int64_t r0 = t.row(0);
+  // receive row of tile row threadIdx.x: fetched before the main loop (its
+  // latency hides there), handed to the epilogue through LDS
+  int32_t my_dst = -1;
+  if ((int)threadIdx.x < rows) my_dst = g.bank_src[t.row(threadIdx.x)];
   const auto ops = g_operands(
       g.H + r0 * g.F, g.F, [&](int r) { return (int)(t.row(min(r, rows - 1)) - r0); },
       W + (int64_t)t.nt * GBN * g.F, g.F, [&](int r) { return min(r, nv - 1); });
   GAcc acc;
   gemm_zero(acc);
   gemm_mainloop(ops, g.ktiles, acc, lds);
+  int32_t *dst_rows = reinterpret_cast<int32_t *>(lds.A[0]);
+  __syncthreads();  // every wave is past its last fragment read of the ring
+  if ((int)threadIdx.x < GBM) dst_rows[threadIdx.x] = my_dst;
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < GTM; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int m = g_acc_row(i, v);
       if (m >= rows) continue;
-      const int64_t dr = g.bank_src[t.row(m)];
+      const int64_t dr = dst_rows[m];
       if (dr < 0 || dr >= g.n_ret) continue;
       const int64_t dst = dr * g.L;
 #pragma unroll
