@@ -14,7 +14,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_CALL_ROUTE, MOE_CALL_PACK, MOE_CALL_BANK, MOE_CALL_FFN, MOE_CALL_COMBINE = range(5)
+(MOE_CALL_ROUTE, MOE_CALL_PACK, MOE_CALL_BANK, MOE_CALL_FFN, MOE_CALL_COMBINE,
+ MOE_CALL_COMBINE_SHARED) = range(6)
 
 
 class MoeError(RuntimeError):
@@ -55,7 +56,7 @@ _SIGS = {
                                    _VP, _VP, _I64, _VP]),
     "moe_shared_swiglu": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP]),
     "moe_combine_shared": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                                          _VP]),
+                                          _VP, _I64, _VP]),
     "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_profile_collect": (ctypes.c_int, []),
     "moe_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.c_char_p, ctypes.c_int,
@@ -165,10 +166,12 @@ def moe_shared_swiglu(d, x, ws_gate, ws_up, h_shared, stream=None):
 
 
 def moe_combine_shared(d, returned, ret_offsets, topk, slot, gates, w_lat_up, h_shared, ws_down,
-                       ylat, out, stream=None):
+                       ylat, out, ws=None, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().moe_combine_shared(ctypes.byref(d), _p(returned), _p(ret_offsets), _p(topk),
                                     _p(slot), _p(gates), _p(w_lat_up), _p(h_shared),
-                                    _p(ws_down), _p(ylat), _p(out), _stream(stream)))
+                                    _p(ws_down), _p(ylat), _p(out), _p(ws), nbytes,
+                                    _stream(stream)))
 
 
 def moe_profile_enable(on: bool):

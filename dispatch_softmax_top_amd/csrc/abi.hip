@@ -7,7 +7,7 @@
 #include <string>
 #include <vector>
 
-#include "common.h"
+#include "kernels.h"
 #include "rank.h"
 
 namespace moe {
@@ -154,14 +154,16 @@ int64_t moe_workspace_bytes(const moe_dims *d, int call, int64_t n_rows) {
       if (items < 0) return fail(MOE_ERR_INVALID, "moe_workspace_bytes: n_rows < 0");
       return rank_ws_bytes(items, (int)(W * El));
     }
-    case MOE_CALL_FFN: {
+    case MOE_CALL_FFN: {  // intermediate h, return-row flags, split partial tiles
       int64_t bank_rows = ragged(*d) ? n_rows : W * El * d->cap_recv;
       int64_t ret_rows = ragged(*d) ? n_rows : R * W * d->cap_send;
       if (bank_rows < 0) return fail(MOE_ERR_INVALID, "moe_workspace_bytes: n_rows < 0");
-      return align_up(bank_rows * d->d_ff * 2, 256) + align_up(ret_rows * 4, 256);
+      return ffn_h_bytes(*d, bank_rows) + ffn_flag_bytes(ret_rows) + gemm_split_bytes();
     }
-    case MOE_CALL_COMBINE:
-      return align_up((int64_t)d->T * d->n_shared * d->d_ff_shared * 2, 256);
+    case MOE_CALL_COMBINE:  // shared experts' intermediate, split partial tiles
+      return shared_h_bytes(*d) + gemm_split_bytes();
+    case MOE_CALL_COMBINE_SHARED:  // split partial tiles
+      return gemm_split_bytes();
     default:
       return fail(MOE_ERR_INVALID, "moe_workspace_bytes: unknown call %d", call);
   }

@@ -109,7 +109,7 @@ static int gather(const moe_dims &d, const uint16_t *returned, const int64_t *re
 static int combine_rest(const moe_dims *d, const uint16_t *returned, const int64_t *ret_offsets,
                         const int32_t *topk, const int32_t *slot, const float *gates,
                         const uint16_t *w_lat_up, const uint16_t *H, const uint16_t *ws_down,
-                        uint16_t *ylat, uint16_t *out, hipStream_t s) {
+                        uint16_t *ylat, uint16_t *out, float *part, hipStream_t s) {
   // chunks per lane: the row's 64-chunk rounds, at most CMB_MAX_CH per wave
   const int ch = (int)std::min<int64_t>(cdiv(d->latent / 8, 64), CMB_MAX_CH);
   MOE_TRY(ch <= 1   ? gather<1>(*d, returned, ret_offsets, topk, slot, gates, ylat, s)
@@ -121,7 +121,7 @@ static int combine_rest(const moe_dims *d, const uint16_t *returned, const int64
   for (int i = 0; i < S; ++i)
     segs[1 + i] = DenseSeg{H + (int64_t)i * Fs, (int64_t)S * Fs,
                            ws_down + (int64_t)i * d->d_model * Fs, Fs, Fs};
-  return gemm_up_shared(d->T, d->d_model, 1 + S, segs, out, d->d_model, s);
+  return gemm_up_shared(d->T, d->d_model, 1 + S, segs, out, d->d_model, part, s);
 }
 
 static int check_rest(const moe_dims *d, const moe_bf16 *returned, const int64_t *ret_offsets,
@@ -162,7 +162,7 @@ extern "C" int moe_shared_swiglu(const moe_dims *d, const moe_bf16 *x, const moe
   MOE_TRY(check_shared(d, x, ws_gate, ws_up));
   if (d->n_shared > 0) MOE_TRY(check_ptr(h_shared, "h_shared"));
   return gemm_shared_swiglu(d->T, x, d->d_model, d->d_model, ws_gate, ws_up, d->n_shared,
-                            d->d_ff_shared, h_shared, (hipStream_t)stream);
+                            d->d_ff_shared, h_shared, nullptr, (hipStream_t)stream);
 }
 
 extern "C" int moe_combine_shared(const moe_dims *d, const moe_bf16 *returned,
@@ -170,12 +170,21 @@ extern "C" int moe_combine_shared(const moe_dims *d, const moe_bf16 *returned,
                                   const int32_t *slot, const float *gates,
                                   const moe_bf16 *w_lat_up, const moe_bf16 *h_shared,
                                   const moe_bf16 *ws_down, moe_bf16 *ylat, moe_bf16 *out,
-                                  void *stream) {
+                                  void *ws, int64_t ws_bytes, void *stream) {
   clear_error();
   MOE_TRY(check_rest(d, returned, ret_offsets, topk, slot, gates, w_lat_up, ws_down, ylat, out));
   if (d->n_shared > 0) MOE_TRY(check_ptr(h_shared, "h_shared"));
+  // the workspace only holds the partial tiles of a split last round
+  if (ws || ws_bytes) {
+    const int64_t need = moe_workspace_bytes(d, MOE_CALL_COMBINE_SHARED, 0);
+    if (need < 0) return (int)need;
+    if (ws_bytes < need || !ws)
+      return fail(MOE_ERR_WORKSPACE, "moe_combine_shared: workspace %lld < %lld bytes",
+                  (long long)ws_bytes, (long long)need);
+    MOE_TRY(check_ptr(ws, "ws"));
+  }
   return combine_rest(d, returned, ret_offsets, topk, slot, gates, w_lat_up, h_shared, ws_down,
-                      ylat, out, (hipStream_t)stream);
+                      ylat, out, (float *)ws, (hipStream_t)stream);
 }
 
 extern "C" int moe_combine(const moe_dims *d, const moe_bf16 *returned, const int64_t *ret_offsets,
@@ -193,9 +202,13 @@ extern "C" int moe_combine(const moe_dims *d, const moe_bf16 *returned, const in
                 (long long)ws_bytes, (long long)need);
   if (ws) MOE_TRY(check_ptr(ws, "ws"));
   hipStream_t s = (hipStream_t)stream;
+  // workspace: the shared experts' intermediate, then the partial tiles of
+  // the up-projection's split last round (the shared experts run whole, as
+  // in moe_shared_swiglu)
   uint16_t *H = (uint16_t *)ws;
+  float *part = (float *)((char *)ws + shared_h_bytes(*d));
   MOE_TRY(gemm_shared_swiglu(d->T, x, d->d_model, d->d_model, ws_gate, ws_up, d->n_shared,
-                             d->d_ff_shared, H, s));
+                             d->d_ff_shared, H, nullptr, s));
   return combine_rest(d, returned, ret_offsets, topk, slot, gates, w_lat_up, H, ws_down, ylat,
-                      out, s);
+                      out, part, s);
 }

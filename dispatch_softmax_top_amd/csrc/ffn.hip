@@ -75,16 +75,21 @@ extern "C" int moe_expert_ffn(const moe_dims *d, const moe_bf16 *bank, const int
     return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %lld < %lld bytes",
                 (long long)ws_bytes, (long long)need);
   hipStream_t s = (hipStream_t)stream;
+  // workspace: intermediate h, return-row flags, partial tiles of the
+  // GEMMs' split last rounds (shared by both: stream order)
+  const int64_t ret_rows = rg ? n_bank_rows : n_ret_rows;
   uint16_t *H = (uint16_t *)ws;
-  int32_t *flags = (int32_t *)((char *)ws + align_up(n_bank_rows * d->d_ff * 2, 256));
+  int32_t *flags = (int32_t *)((char *)ws + ffn_h_bytes(*d, n_bank_rows));
+  float *part = (float *)((char *)flags + ffn_flag_bytes(ret_rows));
 
   MOE_TRY(launch("ffn_flags_clear", ffn_flags_clear, dim3((unsigned)cdiv(n_ret_rows, 256)),
                  dim3(256), 0, s, flags, n_ret_rows));
   MOE_TRY(launch("ffn_flags_mark", ffn_flags_mark, dim3((unsigned)cdiv(n_bank_rows, 256)),
                  dim3(256), 0, s, bank_src, n_bank_rows, flags, n_ret_rows));
-  MOE_TRY(gemm_expert_swiglu(*d, bank, bank_offsets, bfill, n_bank_rows, w_gate, w_up, H, s));
+  MOE_TRY(gemm_expert_swiglu(*d, bank, bank_offsets, bfill, n_bank_rows, w_gate, w_up, H, part,
+                             s));
   MOE_TRY(gemm_expert_down(*d, H, bank_offsets, bfill, bank_src, n_bank_rows, w_down, ret,
-                           n_ret_rows, s));
+                           n_ret_rows, part, s));
   return launch("ffn_zero_rows", ffn_zero_rows, dim3((unsigned)cdiv(n_ret_rows, 4)), dim3(256), 0,
                 s, (const int32_t *)flags, ret, d->latent, n_ret_rows);
 }

@@ -158,12 +158,36 @@ __device__ __forceinline__ uint16_t *g_slot_dst(uint16_t *stage, int i) {
   return stage + (i * GCT + w * 64) * 8;
 }
 
+// The same position as an LDS byte address in a scalar register (the M0
+// value of the copy), computed from the stage's address and the wave index
+// without a per-lane pointer.
+__device__ __forceinline__ uint32_t g_slot_m0(const uint16_t *stage, int i) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)stage);
+  const uint32_t w = __builtin_amdgcn_readfirstlane(((int)threadIdx.x % GCT) >> 6);
+  return base + (uint32_t)(i * GCT + w * 64) * 16;
+}
+
+// Direct copy with the LDS destination given as a scalar byte address.
+__device__ __forceinline__ void g_copy16_m0(const uint16_t *sbase, uint32_t voff, uint32_t m0) {
+  sbase = g_uniform(sbase);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
 // Copy K tile `kt` of one operand into its stage.
 template <int NC>
 __device__ __forceinline__ void g_copy_operand(const GOperand<NC> &o, int kt, uint16_t *dst) {
   const uint16_t *src = o.base + kt * GBK;
 #pragma unroll
-  for (int i = 0; i < NC; ++i) g_copy16(src, o.off[i], g_slot_dst(dst, i));
+  for (int i = 0; i < NC; ++i) g_copy16_m0(src, o.off[i], g_slot_m0(dst, i));
 }
 
 // An operand whose K range is split into NS segments, each with its own
@@ -176,6 +200,7 @@ struct GSegOperand {
   const uint16_t *base[NS];  // row 0 of the tile region, K column 0
   int kend[NS];              // K tiles up to the end of each segment
   uint32_t off[NS][NC];
+  int kbeg;                  // K tile where segment 0 starts (0, or -k0 to copy from k0 on)
 };
 
 template <int S, int NC, int NS, class RowOf>
@@ -199,9 +224,9 @@ __device__ __forceinline__ void g_copy_seg(const GSegOperand<NC, NS> &o, int kt,
       return;
     }
   }
-  const uint16_t *src = o.base[S] + (kt - (S ? o.kend[S ? S - 1 : 0] : 0)) * GBK;
+  const uint16_t *src = o.base[S] + (kt - (S ? o.kend[S ? S - 1 : 0] : o.kbeg)) * GBK;
 #pragma unroll
-  for (int i = 0; i < NC; ++i) g_copy16(src, o.off[S][i], g_slot_dst(dst, i));
+  for (int i = 0; i < NC; ++i) g_copy16_m0(src, o.off[S][i], g_slot_m0(dst, i));
 }
 
 template <int NC, int NS>

@@ -11,12 +11,152 @@
 // their 128 gate and 128 up weight rows, interleaved per 32-row MFMA tile
 // (g_swiglu_brow), so one lane holds a = u.W_g and b = u.W_u of the same
 // (row, f) and the epilogue writes bf16(silu(a) * b) directly.
+#include <algorithm>
+
 #include "gemm.h"
 #include "kernels.h"
 
 namespace moe {
 
 constexpr int MAXSEG = GMAXSEG;
+
+// ---------------------------------------------------------------------------
+// Tail split.  total block tiles on ncu CUs (one resident block per CU) run
+// in ceil(total / ncu) rounds, the last holding only r = total % ncu tiles.
+// When r <= ncu / 2, each of those r tiles is cut along K into S parts,
+// S = min(ncu / r, GSPLIT_MAX), run as r * S blocks of the last round; the
+// parts write fp32 partial tiles and a second kernel sums each tile's parts
+// in part order and runs the tile's epilogue.
+// ---------------------------------------------------------------------------
+
+constexpr int GSPLIT_MAX = 8;      // parts per split tile at most
+constexpr int GSPLIT_MIN_KT = 16;  // K tiles per part at least
+constexpr int GSPLIT_UNITS = 256;  // partial tiles a split buffer holds
+
+struct GSplit {
+  float *part;    // partial tiles (see g_part_store); NULL: no split
+  int ncu;        // CUs of the device
+  int max_units;  // partial tiles the buffer holds
+  int max_parts;  // parts per split tile at most (K tiles / GSPLIT_MIN_KT)
+};
+
+struct GUnit {
+  int tile;    // logical tile
+  int part;    // K part of a split tile (0 if whole)
+  int nparts;  // 1 if whole
+  int tail;    // index among the split tiles
+};
+
+__device__ __forceinline__ int g_split_parts(const GSplit &sp, int total) {
+  if (!sp.part) return 1;
+  const int r = total % sp.ncu;
+  if (r == 0 || 2 * r > sp.ncu) return 1;
+  return max(1, min(min(sp.ncu / r, sp.max_parts), sp.max_units / r));
+}
+
+// Block b of a launch: whole tiles first (each XCD a contiguous range of
+// them), then the parts of the split tiles.  False past the last unit.
+__device__ __forceinline__ bool g_unit(const GSplit &sp, int total, int b, GUnit &u) {
+  const int S = g_split_parts(sp, total);
+  const int whole = S > 1 ? total - total % sp.ncu : total;
+  u.part = 0;
+  u.nparts = 1;
+  u.tail = 0;
+  if (b < whole) {
+    u.tile = __builtin_amdgcn_readfirstlane(xcd_remap(b, whole));
+    return true;
+  }
+  const int t = b - whole;
+  if (S == 1 || t >= (total - whole) * S) return false;
+  u.tail = __builtin_amdgcn_readfirstlane(t / S);
+  u.tile = whole + u.tail;
+  u.part = __builtin_amdgcn_readfirstlane(t - u.tail * S);
+  u.nparts = __builtin_amdgcn_readfirstlane(S);
+  return true;
+}
+
+// K tiles [k0, k1) of the unit's part of kt K tiles (wave-uniform values,
+// kept in scalar registers).
+__device__ __forceinline__ void g_part_range(int kt, const GUnit &u, int &k0, int &k1) {
+  k0 = __builtin_amdgcn_readfirstlane((int)((int64_t)kt * u.part / u.nparts));
+  k1 = __builtin_amdgcn_readfirstlane((int)((int64_t)kt * (u.part + 1) / u.nparts));
+}
+
+// Partial tile `unit`: chunk c (4 accumulators) of thread x at
+// (unit * GACC_CHUNKS + c) * GNT + x, in 16-byte units.
+constexpr int GACC_CHUNKS = GTM * GTN * 4;
+constexpr int64_t GPART_BYTES = (int64_t)GACC_CHUNKS * GNT * 16;
+
+__device__ __forceinline__ void g_part_store(float *part, int unit, const GAcc &acc) {
+  f32x4 *p = reinterpret_cast<f32x4 *>(part) + (int64_t)unit * GACC_CHUNKS * GNT + threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < GTM; ++i)
+#pragma unroll
+    for (int j = 0; j < GTN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                         acc[i][j][4 * q + 3]};
+        __builtin_nontemporal_store(v, p + ((i * GTN + j) * 4 + q) * GNT);
+      }
+}
+
+// acc[I][*] = sum of the S parts of split tile `tail` (MFMA row group I of
+// every wave), added in part order; a part's loads are all issued first.
+template <int I>
+__device__ __forceinline__ void g_part_sum_rows(const float *part, int tail, int S, GAcc &acc) {
+#pragma unroll
+  for (int j = 0; j < GTN; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[I][j][v] = 0.f;
+  // two parts' loads in flight at a time (a missing second part re-reads
+  // the first and is not added)
+  for (int k = 0; k < S; k += 2) {
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(part) +
+                     (int64_t)(tail * S + k) * GACC_CHUNKS * GNT + threadIdx.x;
+    const int64_t next = k + 1 < S ? (int64_t)GACC_CHUNKS * GNT : 0;
+    f32x4 v[2][GTN * 4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < GTN * 4; ++c)
+        v[h][c] = __builtin_nontemporal_load(p + h * next + (I * GTN * 4 + c) * GNT);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1 && k + 1 >= S) break;
+#pragma unroll
+      for (int j = 0; j < GTN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[I][j][4 * q + e] += v[h][j * 4 + q][e];
+    }
+  }
+}
+
+// Tail kernels run GTM blocks per split tile, one per MFMA row group.  The
+// split tile of tail block b: false if there is none (no split, or fewer
+// split tiles than tail blocks).
+__device__ __forceinline__ bool g_tail_tile(const GSplit &sp, int total, int b, GUnit &u) {
+  const int S = g_split_parts(sp, total);
+  if (S == 1 || b >= total % sp.ncu) return false;
+  u.tail = b;
+  u.tile = total - total % sp.ncu + u.tail;
+  u.part = 0;
+  u.nparts = S;
+  return true;
+}
+
+// Row group I of a tail tile: sum of parts, then store(acc) (which stores
+// only row group I).
+#define MOE_TAIL_ROWS(store_rows)                      \
+  switch (blockIdx.x % GTM) {                          \
+    case 0: store_rows(0); break;                      \
+    case 1: store_rows(1); break;                      \
+    case 2: store_rows(2); break;                      \
+    default: store_rows(3); break;                     \
+  }
+static_assert(GTM == 4, "tail kernels: four MFMA row groups per wave");
 
 struct DenseArgs {
   int M, N, nseg;
@@ -27,13 +167,17 @@ struct DenseArgs {
   int ktiles[MAXSEG];
   uint16_t *C;
   int64_t ldc;
+  GSplit sp;
 };
 
+// ONLY >= 0: store MFMA row group ONLY alone.
+template <int ONLY = -1>
 __device__ __forceinline__ void dense_store(const DenseArgs &g, int mt, int nt, const GAcc &acc) {
 #pragma unroll
   for (int i = 0; i < GTM; ++i)
 #pragma unroll
     for (int j = 0; j < GTN; ++j) {
+      if (ONLY >= 0 && i != ONLY) continue;
       const int n = nt * GBN + g_acc_col(j);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -61,22 +205,40 @@ __device__ __forceinline__ void dense_segs(const DenseArgs &g, int mt, int nt, R
 template <int NS>
 __device__ __forceinline__ void dense_body(const DenseArgs &g, const GemmLds &lds) {
   const int tm = (g.M + GBM - 1) / GBM, tn = (g.N + GBN - 1) / GBN;
+  GUnit u;
+  if (!g_unit(g.sp, tm * tn, blockIdx.x, u)) return;
   int mt, nt;
-  g_tile_coords(xcd_remap(blockIdx.x, gridDim.x), tm, tn, mt, nt);
+  g_tile_coords(u.tile, tm, tn, mt, nt);
   const int mv = g.M - mt * GBM, nv = g.N - nt * GBN;  // valid rows / columns
   const auto row_a = [&](int r) { return min(r, mv - 1); };
   const auto row_b = [&](int r) { return min(r, nv - 1); };
+  int kt = 0;
+  for (int i = 0; i < NS; ++i) kt += g.ktiles[i];
+  int k0, k1;
+  g_part_range(kt, u, k0, k1);
   GAcc acc;
   gemm_zero(acc);
   if constexpr (NS == 1) {
-    const auto ops = g_operands(g.A[0] + (int64_t)mt * GBM * g.lda[0], g.lda[0], row_a,
-                                g.B[0] + (int64_t)nt * GBN * g.ldb[0], g.ldb[0], row_b);
-    gemm_mainloop(ops, g.ktiles[0], acc, lds);
+    const auto ops =
+        g_operands(g.A[0] + (int64_t)mt * GBM * g.lda[0] + k0 * GBK, g.lda[0], row_a,
+                   g.B[0] + (int64_t)nt * GBN * g.ldb[0] + k0 * GBK, g.ldb[0], row_b);
+    gemm_mainloop(ops, k1 - k0, acc, lds);
   } else {
     GOps<GSegOperand<GCA, NS>, GSegOperand<GCB, NS>> ops;
     int kend = 0;
     dense_segs<0>(g, mt, nt, row_a, row_b, kend, ops);
-    gemm_mainloop(ops, kend, acc, lds);
+    // copy K tiles k0 .. k1 - 1 of the concatenated range as tiles 0 .. k1 - k0 - 1
+    ops.a.kbeg = ops.b.kbeg = -k0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      ops.a.kend[i] -= k0;
+      ops.b.kend[i] -= k0;
+    }
+    gemm_mainloop(ops, k1 - k0, acc, lds);
+  }
+  if (u.nparts > 1) {
+    g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
+    return;
   }
   dense_store(g, mt, nt, acc);
 }
@@ -91,6 +253,21 @@ template <int NS>
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_up_shared_kernel(DenseArgs g) {
   MOE_GEMM_LDS(lds);
   dense_body<NS>(g, lds);
+}
+
+// the split tiles of a dense product: sum of parts, then the store
+__global__ __launch_bounds__(GNT) void gemm_dense_tail_kernel(DenseArgs g) {
+  const int tm = (g.M + GBM - 1) / GBM, tn = (g.N + GBN - 1) / GBN;
+  GUnit u;
+  if (!g_tail_tile(g.sp, tm * tn, blockIdx.x / GTM, u)) return;
+  int mt, nt;
+  g_tile_coords(u.tile, tm, tn, mt, nt);
+  GAcc acc;
+#define MOE_ROWS(I)                                       \
+  g_part_sum_rows<I>(g.sp.part, u.tail, u.nparts, acc); \
+  dense_store<I>(g, mt, nt, acc)
+  MOE_TAIL_ROWS(MOE_ROWS)
+#undef MOE_ROWS
 }
 
 // ---------------------------------------------------------------------------
@@ -135,16 +312,21 @@ __device__ __forceinline__ int group_rows(const GroupArgs &a, int pg) {
   return c;
 }
 
-// This block's tile: product groups in order, each contributing
-// ceil(rows / 256) * tn tiles.  The grid is an upper bound; the real count
-// is known only here, so blocks remap over it (each XCD gets a contiguous
-// range of real tiles) and blocks past it exit (returns false).
-__device__ __forceinline__ bool group_tile(const GroupArgs &a, int tn, GTile &t) {
+// Tiles of a grouped product: product groups in order, each contributing
+// ceil(rows / 256) * tn tiles.  The counts are known only on the device, so
+// the launch grid is an upper bound and blocks past the last unit exit.
+__device__ __forceinline__ int group_total(const GroupArgs &a, int tn) {
   const int npg = a.G / a.nw;
   int total = 0;
   for (int pg = 0; pg < npg; ++pg) total += ((group_rows(a, pg) + GBM - 1) / GBM) * tn;
-  if ((int)blockIdx.x >= total) return false;
-  int rem = xcd_remap(blockIdx.x, total);
+  return total;
+}
+
+// Logical tile `rem` of a grouped product; false (t.rows = 0) if rem is not
+// below group_total.
+__device__ __forceinline__ bool group_tile_at(const GroupArgs &a, int tn, int rem, GTile &t) {
+  const int npg = a.G / a.nw;
+  t.rows = 0;
   for (int pg = 0; pg < npg; ++pg) {
     const int c = group_rows(a, pg);
     const int tmg = (c + GBM - 1) / GBM;
@@ -166,7 +348,7 @@ __device__ __forceinline__ bool group_tile(const GroupArgs &a, int tn, GTile &t)
         }
         t.cum[s] = cum;
       }
-      return true;
+      return t.rows > 0;
     }
     rem -= tmg * tn;
   }
@@ -190,15 +372,17 @@ struct SwigluArgs {
   int M, S;
   // grouped (routed experts)
   GroupArgs grp;
+  GSplit sp;
 };
 
 // row_of(m): row of A and H for tile row m < rows (contiguous rows, or the
-// bank rows of a grouped tile).
+// bank rows of a grouped tile).  K tiles [k0, k1) into acc.
 template <class RowOf>
-__device__ __forceinline__ void swiglu_tile(const SwigluArgs &g, RowOf row_of, int rows, int expert,
-                                            int ft, int h_col0, const GemmLds &lds) {
+__device__ __forceinline__ void swiglu_acc(const SwigluArgs &g, RowOf row_of, int rows, int expert,
+                                           int ft, int k0, int k1, const GemmLds &lds,
+                                           GAcc &acc) {
   const int f0 = ft * 128;
-  const int64_t eoff = (int64_t)expert * g.F * g.ldb + (int64_t)f0 * g.ldb;
+  const int64_t eoff = (int64_t)expert * g.F * g.ldb + (int64_t)f0 * g.ldb + k0 * GBK;
   // whether a thread copies gate or up rows depends on the thread only (its
   // copy rows are 64 apart, g_swiglu_brow sees row % 64), so the base stays
   // wave-uniform
@@ -207,20 +391,27 @@ __device__ __forceinline__ void swiglu_tile(const SwigluArgs &g, RowOf row_of, i
   g_swiglu_brow(g_load_row(0), up, foff);
   const int64_t r0 = row_of(0);
   const auto ops = g_operands(
-      g.A + r0 * g.lda, g.lda, [&](int r) { return (int)(row_of(min(r, rows - 1)) - r0); },
-      (up ? g.Bu : g.Bg) + eoff, g.ldb, [&](int r) {
+      g.A + r0 * g.lda + k0 * GBK, g.lda,
+      [&](int r) { return (int)(row_of(min(r, rows - 1)) - r0); }, (up ? g.Bu : g.Bg) + eoff,
+      g.ldb, [&](int r) {
         bool u;
         int f;
         g_swiglu_brow(r, u, f);
         return f;
       });
-  GAcc acc;
   gemm_zero(acc);
-  gemm_mainloop(ops, g.ktiles, acc, lds);
+  gemm_mainloop(ops, k1 - k0, acc, lds);
+}
+
+template <int ONLY = -1, class RowOf>
+__device__ __forceinline__ void swiglu_store(const SwigluArgs &g, RowOf row_of, int rows, int ft,
+                                             int h_col0, const GAcc &acc) {
+  const int f0 = ft * 128;
 #pragma unroll
   for (int i = 0; i < GTM; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
+      if (ONLY >= 0 && i != ONLY) continue;
       const int m = g_acc_row(i, v);
       if (m >= rows) continue;
       uint16_t *h = g.H + row_of(m) * g.ldh + h_col0 + f0;
@@ -235,18 +426,75 @@ __device__ __forceinline__ void swiglu_tile(const SwigluArgs &g, RowOf row_of, i
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_shared_swiglu_kernel(SwigluArgs g) {
   MOE_GEMM_LDS(lds);
   const int tm = (g.M + GBM - 1) / GBM, tn = g.S * g.ftiles;
+  GUnit u;
+  if (!g_unit(g.sp, tm * tn, blockIdx.x, u)) return;
   int mt, nt;
-  g_tile_coords(xcd_remap(blockIdx.x, gridDim.x), tm, tn, mt, nt);
+  g_tile_coords(u.tile, tm, tn, mt, nt);
   const int s = nt / g.ftiles, ft = nt % g.ftiles;
   const int64_t row0 = (int64_t)mt * GBM;
-  swiglu_tile(g, [&](int m) { return row0 + m; }, min(GBM, g.M - mt * GBM), s, ft, s * g.F, lds);
+  const auto row_of = [&](int m) { return row0 + m; };
+  const int rows = min(GBM, g.M - mt * GBM);
+  int k0, k1;
+  g_part_range(g.ktiles, u, k0, k1);
+  GAcc acc;
+  swiglu_acc(g, row_of, rows, s, ft, k0, k1, lds, acc);
+  if (u.nparts > 1) {
+    g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
+    return;
+  }
+  swiglu_store(g, row_of, rows, ft, s * g.F, acc);
+}
+
+__global__ __launch_bounds__(GNT) void gemm_shared_swiglu_tail_kernel(SwigluArgs g) {
+  const int tm = (g.M + GBM - 1) / GBM, tn = g.S * g.ftiles;
+  GUnit u;
+  if (!g_tail_tile(g.sp, tm * tn, blockIdx.x / GTM, u)) return;
+  int mt, nt;
+  g_tile_coords(u.tile, tm, tn, mt, nt);
+  const int s = nt / g.ftiles, ft = nt % g.ftiles;
+  const int64_t row0 = (int64_t)mt * GBM;
+  const int rows = min(GBM, g.M - mt * GBM);
+  const auto row_of = [&](int m) { return row0 + m; };
+  GAcc acc;
+#define MOE_ROWS(I)                                       \
+  g_part_sum_rows<I>(g.sp.part, u.tail, u.nparts, acc); \
+  swiglu_store<I>(g, row_of, rows, ft, s * g.F, acc)
+  MOE_TAIL_ROWS(MOE_ROWS)
+#undef MOE_ROWS
 }
 
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_swiglu_kernel(SwigluArgs g) {
   MOE_GEMM_LDS(lds);
+  GUnit u;
   GTile t;
-  if (!group_tile(g.grp, g.ftiles, t)) return;
-  swiglu_tile(g, [&](int m) { return t.row(m); }, t.rows, t.expert, t.nt, 0, lds);
+  if (!g_unit(g.sp, group_total(g.grp, g.ftiles), blockIdx.x, u) ||
+      !group_tile_at(g.grp, g.ftiles, u.tile, t))
+    return;
+  const auto row_of = [&](int m) { return t.row(m); };
+  int k0, k1;
+  g_part_range(g.ktiles, u, k0, k1);
+  GAcc acc;
+  swiglu_acc(g, row_of, t.rows, t.expert, t.nt, k0, k1, lds, acc);
+  if (u.nparts > 1) {
+    g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
+    return;
+  }
+  swiglu_store(g, row_of, t.rows, t.nt, 0, acc);
+}
+
+__global__ __launch_bounds__(GNT) void gemm_expert_swiglu_tail_kernel(SwigluArgs g) {
+  GUnit u;
+  GTile t;
+  if (!g_tail_tile(g.sp, group_total(g.grp, g.ftiles), blockIdx.x / GTM, u) ||
+      !group_tile_at(g.grp, g.ftiles, u.tile, t))
+    return;
+  const auto row_of = [&](int m) { return t.row(m); };
+  GAcc acc;
+#define MOE_ROWS(I)                                       \
+  g_part_sum_rows<I>(g.sp.part, u.tail, u.nparts, acc); \
+  swiglu_store<I>(g, row_of, t.rows, t.nt, 0, acc)
+  MOE_TAIL_ROWS(MOE_ROWS)
+#undef MOE_ROWS
 }
 
 // ---------------------------------------------------------------------------
@@ -262,36 +510,21 @@ struct DownArgs {
   const int32_t *bank_src;
   uint16_t *ret;  // [ret rows][L]
   int64_t n_ret;
+  GSplit sp;
 };
 
-__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_down_kernel(DownArgs g) {
-  MOE_GEMM_LDS(lds);
-  GTile t;
-  if (!group_tile(g.grp, g.tn, t)) return;
-  const uint16_t *W = g.Wd + (int64_t)t.expert * g.L * g.F;
-  const int nv = g.L - t.nt * GBN, rows = t.rows;
-  const int64_t r0 = t.row(0);
-  // receive row of tile row threadIdx.x: fetched before the main loop (its
-  // latency hides there), handed to the epilogue through LDS
-  int32_t my_dst = -1;
-  if ((int)threadIdx.x < rows) my_dst = g.bank_src[t.row(threadIdx.x)];
-  const auto ops = g_operands(
-      g.H + r0 * g.F, g.F, [&](int r) { return (int)(t.row(min(r, rows - 1)) - r0); },
-      W + (int64_t)t.nt * GBN * g.F, g.F, [&](int r) { return min(r, nv - 1); });
-  GAcc acc;
-  gemm_zero(acc);
-  gemm_mainloop(ops, g.ktiles, acc, lds);
-  int32_t *dst_rows = reinterpret_cast<int32_t *>(lds.A[0]);
-  __syncthreads();  // every wave is past its last fragment read of the ring
-  if ((int)threadIdx.x < GBM) dst_rows[threadIdx.x] = my_dst;
-  __syncthreads();
+// dst_of(m): receive row of tile row m (negative or >= n_ret: not stored).
+template <int ONLY = -1, class DstOf>
+__device__ __forceinline__ void down_store(const DownArgs &g, const GTile &t, DstOf dst_of,
+                                           const GAcc &acc) {
 #pragma unroll
   for (int i = 0; i < GTM; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
+      if (ONLY >= 0 && i != ONLY) continue;
       const int m = g_acc_row(i, v);
-      if (m >= rows) continue;
-      const int64_t dr = dst_rows[m];
+      if (m >= t.rows) continue;
+      const int64_t dr = dst_of(m);
       if (dr < 0 || dr >= g.n_ret) continue;
       const int64_t dst = dr * g.L;
 #pragma unroll
@@ -302,12 +535,106 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
     }
 }
 
+__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_down_kernel(DownArgs g) {
+  MOE_GEMM_LDS(lds);
+  GUnit u;
+  GTile t;
+  if (!g_unit(g.sp, group_total(g.grp, g.tn), blockIdx.x, u) ||
+      !group_tile_at(g.grp, g.tn, u.tile, t))
+    return;
+  const uint16_t *W = g.Wd + (int64_t)t.expert * g.L * g.F;
+  const int nv = g.L - t.nt * GBN, rows = t.rows;
+  const int64_t r0 = t.row(0);
+  const bool whole = u.nparts == 1;
+  // receive row of tile row threadIdx.x: fetched before the main loop (its
+  // latency hides there), handed to the epilogue through LDS
+  int32_t my_dst = -1;
+  if (whole && (int)threadIdx.x < rows) my_dst = g.bank_src[t.row(threadIdx.x)];
+  int k0, k1;
+  g_part_range(g.ktiles, u, k0, k1);
+  const auto ops = g_operands(
+      g.H + r0 * g.F + k0 * GBK, g.F,
+      [&](int r) { return (int)(t.row(min(r, rows - 1)) - r0); },
+      W + (int64_t)t.nt * GBN * g.F + k0 * GBK, g.F, [&](int r) { return min(r, nv - 1); });
+  GAcc acc;
+  gemm_zero(acc);
+  gemm_mainloop(ops, k1 - k0, acc, lds);
+  if (!whole) {
+    g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
+    return;
+  }
+  int32_t *dst_rows = reinterpret_cast<int32_t *>(lds.A[0]);
+  __syncthreads();  // every wave is past its last fragment read of the ring
+  if ((int)threadIdx.x < GBM) dst_rows[threadIdx.x] = my_dst;
+  __syncthreads();
+  down_store(g, t, [&](int m) { return (int64_t)dst_rows[m]; }, acc);
+}
+
+__global__ __launch_bounds__(GNT) void gemm_expert_down_tail_kernel(DownArgs g) {
+  __shared__ int32_t dst_rows[GBM];
+  GUnit u;
+  GTile t;
+  if (!g_tail_tile(g.sp, group_total(g.grp, g.tn), blockIdx.x / GTM, u) ||
+      !group_tile_at(g.grp, g.tn, u.tile, t))
+    return;
+  if ((int)threadIdx.x < GBM)
+    dst_rows[threadIdx.x] = (int)threadIdx.x < t.rows ? g.bank_src[t.row(threadIdx.x)] : -1;
+  __syncthreads();
+  const auto dst_of = [&](int m) { return (int64_t)dst_rows[m]; };
+  GAcc acc;
+#define MOE_ROWS(I)                                       \
+  g_part_sum_rows<I>(g.sp.part, u.tail, u.nparts, acc); \
+  down_store<I>(g, t, dst_of, acc)
+  MOE_TAIL_ROWS(MOE_ROWS)
+#undef MOE_ROWS
+}
+
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 
-static int dense(const char *name, void (*k)(DenseArgs), int M, int N, int nseg,
-                 const DenseSeg *segs, uint16_t *C, int64_t ldc, hipStream_t s) {
+// CUs of the current device (cached per device).
+static int cu_count(int *ncu) {
+  static int cache[64];
+  int dev = 0;
+  MOE_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *ncu = cache[dev];
+    return MOE_OK;
+  }
+  int n = 0;
+  MOE_TRY(hip_status(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev),
+                     "hipDeviceGetAttribute"));
+  if (n < 1) return fail(MOE_ERR_HIP, "device reports %d compute units", n);
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  *ncu = n;
+  return MOE_OK;
+}
+
+int64_t gemm_split_bytes() { return (int64_t)GSPLIT_UNITS * GPART_BYTES; }
+
+// Split description for a product of kt K tiles; part == NULL, or too few
+// K tiles for two parts, turns splitting off.
+static int make_split(float *part, int kt, GSplit &sp) {
+  sp.max_parts = std::min(GSPLIT_MAX, kt / GSPLIT_MIN_KT);
+  sp.part = sp.max_parts >= 2 ? part : nullptr;
+  sp.ncu = 1;
+  sp.max_units = sp.part ? GSPLIT_UNITS : 0;
+  return sp.part ? cu_count(&sp.ncu) : MOE_OK;
+}
+
+// Host mirror of g_split_parts.
+static int split_parts(const GSplit &sp, int64_t total) {
+  if (!sp.part) return 1;
+  const int64_t r = total % sp.ncu;
+  if (r == 0 || 2 * r > sp.ncu) return 1;
+  return (int)std::max<int64_t>(
+      1, std::min<int64_t>(std::min<int64_t>(sp.ncu / r, sp.max_parts), sp.max_units / r));
+}
+
+static int dense(const char *name, const char *tail_name, void (*k)(DenseArgs), int M, int N,
+                 int nseg, const DenseSeg *segs, uint16_t *C, int64_t ldc, float *part,
+                 hipStream_t s) {
   if (nseg < 1 || nseg > MAXSEG) return fail(MOE_ERR_INVALID, "%s: bad segment count", name);
   DenseArgs a{};
   a.M = M;
@@ -328,24 +655,37 @@ static int dense(const char *name, void (*k)(DenseArgs), int M, int N, int nseg,
   a.C = C;
   a.ldc = ldc;
   const int64_t tiles = cdiv(M, GBM) * cdiv(N, GBN);
-  return launch(name, k, dim3((unsigned)tiles), dim3(GNT), 0, s, a);
+  int kt = 0;
+  for (int i = 0; i < nseg; ++i) kt += a.ktiles[i];
+  MOE_TRY(make_split(part, kt, a.sp));
+  const int S = split_parts(a.sp, tiles);
+  if (S == 1) {
+    a.sp.part = nullptr;
+    return launch(name, k, dim3((unsigned)tiles), dim3(GNT), 0, s, a);
+  }
+  const int64_t r = tiles % a.sp.ncu;
+  MOE_TRY(launch(name, k, dim3((unsigned)(tiles - r + r * S)), dim3(GNT), 0, s, a));
+  return launch(tail_name, gemm_dense_tail_kernel, dim3((unsigned)(r * GTM)), dim3(GNT), 0, s, a);
 }
 
 int gemm_latent_down(int M, int N, const DenseSeg &seg, uint16_t *C, int64_t ldc, hipStream_t s) {
-  return dense("gemm_latent_down", gemm_latent_down_kernel, M, N, 1, &seg, C, ldc, s);
+  return dense("gemm_latent_down", "gemm_latent_down_tail", gemm_latent_down_kernel, M, N, 1, &seg,
+               C, ldc, nullptr, s);
 }
 
 int gemm_up_shared(int M, int N, int nseg, const DenseSeg *segs, uint16_t *C, int64_t ldc,
-                   hipStream_t s) {
+                   float *part, hipStream_t s) {
   static void (*const k[MAXSEG])(DenseArgs) = {gemm_up_shared_kernel<1>, gemm_up_shared_kernel<2>,
                                                gemm_up_shared_kernel<3>, gemm_up_shared_kernel<4>,
                                                gemm_up_shared_kernel<5>};
   if (nseg < 1 || nseg > MAXSEG) return fail(MOE_ERR_INVALID, "gemm_up_shared: bad segment count");
-  return dense("gemm_up_shared", k[nseg - 1], M, N, nseg, segs, C, ldc, s);
+  return dense("gemm_up_shared", "gemm_up_shared_tail", k[nseg - 1], M, N, nseg, segs, C, ldc,
+               part, s);
 }
 
 int gemm_shared_swiglu(int M, const uint16_t *x, int64_t ldx, int K, const uint16_t *wg,
-                       const uint16_t *wu, int S, int F, uint16_t *H, hipStream_t s) {
+                       const uint16_t *wu, int S, int F, uint16_t *H, float *part,
+                       hipStream_t s) {
   if (S == 0) return MOE_OK;
   SwigluArgs a{};
   a.A = x;
@@ -360,9 +700,19 @@ int gemm_shared_swiglu(int M, const uint16_t *x, int64_t ldx, int K, const uint1
   a.ldh = (int64_t)S * F;
   a.M = M;
   a.S = S;
+  MOE_TRY(make_split(part, a.ktiles, a.sp));
   const int64_t tiles = cdiv(M, GBM) * (int64_t)S * a.ftiles;
-  return launch("gemm_shared_swiglu", gemm_shared_swiglu_kernel, dim3((unsigned)tiles), dim3(GNT),
-                0, s, a);
+  const int P = split_parts(a.sp, tiles);
+  if (P == 1) {
+    a.sp.part = nullptr;
+    return launch("gemm_shared_swiglu", gemm_shared_swiglu_kernel, dim3((unsigned)tiles),
+                  dim3(GNT), 0, s, a);
+  }
+  const int64_t r = tiles % a.sp.ncu;
+  MOE_TRY(launch("gemm_shared_swiglu", gemm_shared_swiglu_kernel,
+                 dim3((unsigned)(tiles - r + r * P)), dim3(GNT), 0, s, a));
+  return launch("gemm_shared_swiglu_tail", gemm_shared_swiglu_tail_kernel,
+                dim3((unsigned)(r * GTM)), dim3(GNT), 0, s, a);
 }
 
 // Product groups of the bank: each local expert over every wave when the
@@ -388,9 +738,25 @@ static int64_t grouped_tiles_bound(const moe_dims &d, int64_t n_bank_rows, int t
   return mt * tn;
 }
 
+// A grouped product and, when splitting is on, its tail kernel.  The real
+// tile count is known only on the device: the grid bounds it plus the ncu
+// extra blocks a split can add; the tail kernel gets GTM blocks for each of
+// ncu / 2 possible split tiles (a split never has more) and exits where
+// there is none.
+template <class Args>
+static int grouped(const char *name, const char *tail_name, void (*k)(Args),
+                   void (*tk)(Args), int64_t bound, int ktiles, Args &a, float *part,
+                   hipStream_t s) {
+  MOE_TRY(make_split(part, ktiles, a.sp));
+  MOE_TRY(launch(name, k, dim3((unsigned)(bound + (a.sp.part ? a.sp.ncu : 0))), dim3(GNT), 0, s,
+                 a));
+  if (!a.sp.part || a.sp.ncu < 2) return MOE_OK;
+  return launch(tail_name, tk, dim3((unsigned)(a.sp.ncu / 2 * GTM)), dim3(GNT), 0, s, a);
+}
+
 int gemm_expert_swiglu(const moe_dims &d, const uint16_t *bank, const int64_t *bank_offsets,
                        const int32_t *bfill, int64_t n_bank_rows, const uint16_t *wg,
-                       const uint16_t *wu, uint16_t *H, hipStream_t s) {
+                       const uint16_t *wu, uint16_t *H, float *part, hipStream_t s) {
   SwigluArgs a{};
   a.A = bank;
   a.lda = d.latent;
@@ -403,14 +769,15 @@ int gemm_expert_swiglu(const moe_dims &d, const uint16_t *bank, const int64_t *b
   a.H = H;
   a.ldh = d.d_ff;
   a.grp = group_args(d, bank_offsets, bfill, n_bank_rows);
-  const int64_t tiles = grouped_tiles_bound(d, n_bank_rows, a.ftiles);
-  return launch("gemm_expert_swiglu", gemm_expert_swiglu_kernel, dim3((unsigned)tiles), dim3(GNT),
-                0, s, a);
+  return grouped("gemm_expert_swiglu", "gemm_expert_swiglu_tail", gemm_expert_swiglu_kernel,
+                 gemm_expert_swiglu_tail_kernel, grouped_tiles_bound(d, n_bank_rows, a.ftiles),
+                 a.ktiles, a, part, s);
 }
 
 int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_offsets,
                      const int32_t *bfill, const int32_t *bank_src, int64_t n_bank_rows,
-                     const uint16_t *wd, uint16_t *ret, int64_t n_ret, hipStream_t s) {
+                     const uint16_t *wd, uint16_t *ret, int64_t n_ret, float *part,
+                     hipStream_t s) {
   DownArgs a{};
   a.n_ret = n_ret;
   a.H = H;
@@ -422,9 +789,9 @@ int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_o
   a.grp = group_args(d, bank_offsets, bfill, n_bank_rows);
   a.bank_src = bank_src;
   a.ret = ret;
-  const int64_t tiles = grouped_tiles_bound(d, n_bank_rows, a.tn);
-  return launch("gemm_expert_down", gemm_expert_down_kernel, dim3((unsigned)tiles), dim3(GNT), 0,
-                s, a);
+  return grouped("gemm_expert_down", "gemm_expert_down_tail", gemm_expert_down_kernel,
+                 gemm_expert_down_tail_kernel, grouped_tiles_bound(d, n_bank_rows, a.tn),
+                 a.ktiles, a, part, s);
 }
 
 }  // namespace moe

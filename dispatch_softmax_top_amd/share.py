@@ -109,9 +109,11 @@ class Combiner:
         self.ylat = torch.empty(d.T, d.latent, dtype=torch.bfloat16, device=dev)
         self.out = torch.empty(d.T, d.d_model, dtype=torch.bfloat16, device=dev)
         self.ws = _ws(d, L.MOE_CALL_COMBINE, 0, dev)
-        # the shared experts' intermediate when the combine runs as two calls
+        # the shared experts' intermediate and the split partial tiles when
+        # the combine runs as two calls
         self.h_shared = torch.empty(d.T, max(d.n_shared * d.d_ff_shared, 1), dtype=torch.bfloat16,
                                     device=dev)
+        self.ws_shared = _ws(d, L.MOE_CALL_COMBINE_SHARED, 0, dev)
 
     def combine(self, returned, ret_offsets, snd: Sender, x, w_lat_up, ws_gate, ws_up, ws_down,
                 stream=None):
@@ -123,7 +125,8 @@ class Combiner:
 
     def combine_shared(self, returned, ret_offsets, snd: Sender, w_lat_up, ws_down, stream=None):
         L.moe_combine_shared(self.d, returned, ret_offsets, snd.topk, snd.slot, snd.gates,
-                             w_lat_up, self.h_shared, ws_down, self.ylat, self.out, stream)
+                             w_lat_up, self.h_shared, ws_down, self.ylat, self.out,
+                             self.ws_shared, stream)
 
 
 # ----------------------------------------------------------------------------

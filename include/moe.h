@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef uint16_t moe_bf16;
 
@@ -102,7 +102,7 @@ int moe_capacity(const moe_dims *d, int64_t cf_send_num, int64_t cf_send_den,
                  int32_t *cap_recv);
 
 enum { MOE_CALL_ROUTE = 0, MOE_CALL_PACK = 1, MOE_CALL_BANK = 2,
-       MOE_CALL_FFN = 3, MOE_CALL_COMBINE = 4 };
+       MOE_CALL_FFN = 3, MOE_CALL_COMBINE = 4, MOE_CALL_COMBINE_SHARED = 5 };
 
 /* Bytes of scratch a call needs.  n_rows: bank rows allocated (FFN, ragged
  * mode); ignored otherwise.  Returns a negative moe_status on bad dims. */
@@ -209,10 +209,16 @@ int moe_combine(const moe_dims *d, const moe_bf16 *returned,
  *     x, ws_gate, ws_up  as in moe_combine
  *     h_shared     [T, n_shared*d_ff_shared] bf16 out (n_shared == 0: no-op)
  *   moe_combine_shared  ylat and out exactly as moe_combine, with the shared
- *                       experts' intermediate read from h_shared; no
- *                       workspace.  Other arguments as in moe_combine.
+ *                       experts' intermediate read from h_shared.
+ *     ws           scratch of moe_workspace_bytes(d, MOE_CALL_COMBINE_SHARED, 0)
+ *                  for the partial tiles of the up-projection's last round
+ *                  (cut along K when it would fill at most half the CUs);
+ *                  NULL with ws_bytes 0 runs that round whole (results
+ *                  then differ in fp32 summation order only)
+ *     Other arguments as in moe_combine.
  * moe_combine equals moe_shared_swiglu into its workspace followed by
- * moe_combine_shared, bit for bit.  Errors as for moe_combine. */
+ * moe_combine_shared with a workspace, bit for bit.  Errors as for
+ * moe_combine. */
 int moe_shared_swiglu(const moe_dims *d, const moe_bf16 *x, const moe_bf16 *ws_gate,
                       const moe_bf16 *ws_up, moe_bf16 *h_shared, void *stream);
 int moe_combine_shared(const moe_dims *d, const moe_bf16 *returned,
@@ -220,7 +226,7 @@ int moe_combine_shared(const moe_dims *d, const moe_bf16 *returned,
                        const int32_t *slot, const float *gates,
                        const moe_bf16 *w_lat_up, const moe_bf16 *h_shared,
                        const moe_bf16 *ws_down, moe_bf16 *ylat, moe_bf16 *out,
-                       void *stream);
+                       void *ws, int64_t ws_bytes, void *stream);
 
 /* Kernel timing.  While enabled, every kernel the library launches is
  * bracketed by two hipEvents on its stream.  moe_profile_collect()

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(moe):
 
 
 def test_abi_version(moe):
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
 
 
 def test_capacity_matches_table(moe):
@@ -97,9 +97,11 @@ def test_calls_reject_null_and_misaligned(moe):
     assert L.moe_shared_swiglu(ctypes.byref(d), None, p, p, p, None) == -1
     assert L.moe_shared_swiglu(ctypes.byref(d), p, p, p, None, None) == -1   # h_shared
     assert L.moe_combine_shared(ctypes.byref(d), p, None, p, p, p, p, None, p, p, p,
-                                None) == -1                        # h_shared
+                                None, 0, None) == -1               # h_shared
     assert L.moe_combine_shared(ctypes.byref(d), p, None, p, p, p, p, p, p, None, p,
-                                None) == -1                        # ylat
+                                None, 0, None) == -1               # ylat
+    assert L.moe_combine_shared(ctypes.byref(d), p, None, p, p, p, p, p, p, p, p,
+                                p, 16, None) == -4                 # workspace too small
 
 
 def test_workspace_sizes_grow_with_rows(moe):
