@@ -56,6 +56,9 @@ def lib():
             "orc_tokens_per_wave": (i32, [i32, i32]),
             "orc_capacity": (i64, [i64, i32, i32, i64, i64]),
             "orc_route": (None, [_f32p, i64, i32, i32, _i32p, _f32p]),
+            "orc_route_biased": (None, [_f32p, _f32p, i64, i32, i32, _i32p, _f32p]),
+            "orc_expert_counts": (None, [_i32p, i64, i32, _i32p]),
+            "orc_balance_bias": (None, [_i32p, i32, i32, ctypes.c_double, _f32p]),
             "orc_latent_rows": (None, [_u16p, i32, _u16p, i32, vp, i64, _u16p]),
             "orc_sender": (i64, [dp, _i32p, _i32p, _i32p, _i32p, vp]),
             "orc_pack_rows": (None, [dp, _u16p, _i32p, _i32p, vp, _u8p, i64]),
@@ -139,6 +142,34 @@ def route(logits: np.ndarray, k: int):
     gates = np.empty((T, k), np.float32)
     lib().orc_route(logits, T, E, k, topk, gates)
     return topk, gates
+
+
+def route_biased(logits: np.ndarray, bias: np.ndarray, k: int):
+    """Router on fp32(logits + bias) ([P1] section 四, appendix A.2)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    bias = np.ascontiguousarray(bias, dtype=np.float32)
+    T, E = logits.shape
+    topk = np.empty((T, k), np.int32)
+    gates = np.empty((T, k), np.float32)
+    lib().orc_route_biased(logits, bias, T, E, k, topk, gates)
+    return topk, gates
+
+
+def expert_counts(topk: np.ndarray, E: int) -> np.ndarray:
+    """Selections of each expert in one batch ([P1] appendix A.2)."""
+    topk = np.ascontiguousarray(topk, dtype=np.int32)
+    counts = np.empty(E, np.int32)
+    lib().orc_expert_counts(topk.reshape(-1), topk.size, E, counts)
+    return counts
+
+
+def balance_bias(window: np.ndarray, alpha: float) -> np.ndarray:
+    """b_i = -alpha (f_i - 1/E) over the batches of `window` [N, E] ([P1] appendix A.2)."""
+    window = np.ascontiguousarray(window, dtype=np.int32)
+    n, E = window.shape
+    bias = np.empty(E, np.float32)
+    lib().orc_balance_bias(window.reshape(-1), n, E, float(alpha), bias)
+    return bias
 
 
 def latent(x: np.ndarray, w_ld_t: np.ndarray, rows=None) -> np.ndarray:

@@ -113,6 +113,53 @@ void orc_route(const float *logits, int64_t T, int32_t E, int32_t k,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Quantile balancing                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* [P1] section 四 and appendix A.2: a routing bias is added to the router
+ * logits (stop-gradient: it changes only which experts are chosen next).
+ * The biased logit is rounded to fp32 -- the precision the routing decision
+ * is taken in -- and the router above then runs on it unchanged. */
+void orc_route_biased(const float *logits, const float *bias, int64_t T,
+                      int32_t E, int32_t k, int32_t *topk, float *gates) {
+  float *lb = (float *)malloc(sizeof(float) * (size_t)E);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t e = 0; e < E; ++e) lb[e] = logits[t * E + e] + bias[e];
+    orc_route(lb, 1, E, k, topk + t * k, gates + t * k);
+  }
+  free(lb);
+}
+
+/* [P1] appendix A.2: H counts how often each expert was chosen.  One batch's
+ * counts: counts[e] = number of choices (t, j) with topk[t, j] == e; entries
+ * outside [0, E) are not choices of an expert and are not counted. */
+void orc_expert_counts(const int32_t *topk, int64_t n, int32_t E,
+                       int32_t *counts) {
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t i = 0; i < n; ++i)
+    if (topk[i] >= 0 && topk[i] < E) counts[topk[i]] += 1;
+}
+
+/* [P1] appendix A.2: with H[i] the selections of expert i over the past N
+ * batches, f_i = H[i] / sum(H) and the bias is b_i = -alpha * (f_i - 1/E).
+ * window[b * E + i] holds batch b's counts.  READING: the formula sets the
+ * bias (it does not add to the previous one); with no selections at all
+ * (sum(H) == 0) the frequencies are taken as uniform, so every bias is 0.
+ * Computed in double, rounded once to fp32. */
+void orc_balance_bias(const int32_t *window, int32_t n_batches, int32_t E,
+                      double alpha, float *bias) {
+  int64_t total = 0;
+  for (int32_t b = 0; b < n_batches; ++b)
+    for (int32_t i = 0; i < E; ++i) total += window[(int64_t)b * E + i];
+  for (int32_t i = 0; i < E; ++i) {
+    int64_t h = 0;
+    for (int32_t b = 0; b < n_batches; ++b) h += window[(int64_t)b * E + i];
+    double f = total > 0 ? (double)h / (double)total : 1.0 / (double)E;
+    bias[i] = (float)(-alpha * (f - 1.0 / (double)E));
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Latent down-projection                                                   */
 /* ------------------------------------------------------------------------ */
 

@@ -52,6 +52,13 @@ int64_t orc_capacity(int64_t tokens_per_wave, int32_t top_k, int32_t groups,
 void orc_route(const float *logits, int64_t T, int32_t E, int32_t k,
                int32_t *topk, float *gates);
 
+void orc_route_biased(const float *logits, const float *bias, int64_t T,
+                      int32_t E, int32_t k, int32_t *topk, float *gates);
+void orc_expert_counts(const int32_t *topk, int64_t n, int32_t E,
+                       int32_t *counts);
+void orc_balance_bias(const int32_t *window, int32_t n_batches, int32_t E,
+                      double alpha, float *bias);
+
 void orc_latent_rows(const uint16_t *x, int32_t D, const uint16_t *w_ld_t,
                      int32_t L, const int64_t *rows, int64_t n, uint16_t *z);
 

@@ -38,6 +38,17 @@ MUTATIONS = [
      "int32_t seg = w * d->n_ranks + dest_of(d, e);", "test_oracle_e2e.py"),
     ("expert placement", "return e / (d->n_experts / d->n_ranks);", "return e % d->n_ranks;",
      "test_oracle_pins.py"),
+    ("balance bias sign", "bias[i] = (float)(-alpha * (f - 1.0 / (double)E));",
+     "bias[i] = (float)(alpha * (f - 1.0 / (double)E));", "test_oracle_balance.py"),
+    ("bias subtracted", "for (int32_t e = 0; e < E; ++e) lb[e] = logits[t * E + e] + bias[e];",
+     "for (int32_t e = 0; e < E; ++e) lb[e] = logits[t * E + e] - bias[e];",
+     "test_oracle_balance.py"),
+    ("expert 0 not counted", "if (topk[i] >= 0 && topk[i] < E) counts[topk[i]] += 1;",
+     "if (topk[i] > 0 && topk[i] < E) counts[topk[i]] += 1;", "test_oracle_balance.py"),
+    ("window: last batch only",
+     "    for (int32_t b = 0; b < n_batches; ++b) h += window[(int64_t)b * E + i];",
+     "    for (int32_t b = n_batches - 1; b < n_batches; ++b) h += window[(int64_t)b * E + i];",
+     "test_oracle_balance.py"),
 ]
 
 
