@@ -107,6 +107,7 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False, keep_logits=False)
     st.s_ffn, st.s_shared = torch.cuda.Stream(device), torch.cuda.Stream(device)
     st.ev_start, st.ev_ffn, st.ev_shared = (torch.cuda.Event() for _ in range(3))
     torch.cuda.synchronize()
+    st.bal = None  # quantile balancing state (bench --balance-alpha)
     return st
 
 
@@ -183,17 +184,28 @@ def step(st):
     with torch.cuda.stream(st.s_shared):
         st.cmb.shared(st.x, st.wsg, st.wsu)
         st.ev_shared.record(st.s_shared)
-    st.snd.route(st.logits)
+    route_shard(st)
     st.snd.pack(st.x, st.wld)
     main.wait_event(st.ev_ffn)
     main.wait_event(st.ev_shared)
     st.cmb.combine_shared(st.rcv.ret, st.recv_offsets, st.snd, st.wlu, st.wsd)
 
 
+def route_shard(st):
+    """Route the shard; with quantile balancing on, on the logits plus the bias
+    of the past batches, then count this batch's choices and set the bias the
+    next step routes with."""
+    if st.bal is None:
+        st.snd.route(st.logits)
+    else:
+        st.snd.route(st.logits, bias=st.bal.bias)
+        st.bal.update(st.snd.topk)
+
+
 def step_serial(st):
     """The same path with every call on one stream, in path order (moe_combine
     as one call): each kernel runs alone."""
-    st.snd.route(st.logits)
+    route_shard(st)
     st.snd.pack(st.x, st.wld)
     st.rcv.bank_rows(st.rank, st.recv, st.recv_offsets)
     st.rcv.ffn(st.wg, st.wu, st.wd)
@@ -323,6 +335,10 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time steps that each follow a 1 GiB write sweep (cold caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--balance-alpha", type=float, default=None, metavar="ALPHA",
+                    help="quantile balancing on: route with the bias -ALPHA (f - 1/E) from the "
+                         "selection counts of the past --balance-window batches")
+    ap.add_argument("--balance-window", type=int, default=8)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise device copy of MIB mebibytes, three "
                          "times: the reference for hardware byte counters")
@@ -357,6 +373,9 @@ def main():
             log(f"bench: hottest rank is {rank}: setup again")
             del st
             st = setup(cfg, rank, progress=True)
+    if args.balance_alpha is not None:
+        from dispatch_softmax_top_amd import share
+        st.bal = share.Balancer(cfg.n_experts, args.balance_window, args.balance_alpha)
     stepfn = step_serial if args.serial else step
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -456,7 +475,9 @@ def main():
                    "latent": d.latent, "n_experts": d.n_experts, "n_ranks": d.n_ranks,
                    "top_k": d.top_k, "n_waves": d.n_waves, "d_ff": d.d_ff,
                    "n_shared": d.n_shared, "cap_send": d.cap_send, "cap_recv": d.cap_recv,
-                   "source_shards": cfg.n_shards, "streams": 1 if args.serial else 3},
+                   "source_shards": cfg.n_shards, "streams": 1 if args.serial else 3,
+                   "balance": None if st.bal is None else
+                   {"alpha": args.balance_alpha, "window": args.balance_window}},
         "roofline": {"kernel": dom, "bound": "mfma", "measured": "per-kernel pass after the "
                      "timed steps, calls on one stream (each kernel alone); duration of the "
                      "kernel plus its split-tail kernel",

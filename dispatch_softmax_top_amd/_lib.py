@@ -46,6 +46,9 @@ _SIGS = {
                                     ctypes.POINTER(_I32)]),
     "moe_workspace_bytes": (_I64, [_DP, ctypes.c_int, _I64]),
     "moe_route": (ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _VP, _VP]),
+    "moe_route_biased": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP]),
+    "moe_expert_counts": (ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _VP]),
+    "moe_balance_bias": (ctypes.c_int, [_VP, _I32, _I32, ctypes.c_double, _VP, _VP]),
     "moe_pack_waves": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                       _I64, _VP]),
     "moe_bank": (ctypes.c_int, [_DP, _I32, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -126,6 +129,22 @@ def moe_workspace_bytes(d: MoeDims, call: int, n_rows: int = 0) -> int:
 def moe_route(logits, k, topk, gates, stream=None):
     T, E = logits.shape
     _check(lib().moe_route(_p(logits), T, E, k, _p(topk), _p(gates), _stream(stream)))
+
+
+def moe_route_biased(logits, bias, k, topk, gates, stream=None):
+    T, E = logits.shape
+    _check(lib().moe_route_biased(_p(logits), _p(bias), T, E, k, _p(topk), _p(gates),
+                                  _stream(stream)))
+
+
+def moe_expert_counts(topk, E, counts, stream=None):
+    T, k = topk.shape
+    _check(lib().moe_expert_counts(_p(topk), T, k, E, _p(counts), _stream(stream)))
+
+
+def moe_balance_bias(window, alpha, bias, stream=None):
+    n, E = window.shape
+    _check(lib().moe_balance_bias(_p(window), n, E, float(alpha), _p(bias), _stream(stream)))
 
 
 def moe_pack_waves(d, x, w_lat_down, topk, z, pools, pool_offsets, slot, fill, demand, ws,

@@ -11,6 +11,13 @@
 // Each lane keeps its candidates sorted; k rounds of a wave-wide max take
 // the head of the winning lane.  Gates are exp(l - max) / sum exp(l - max)
 // over all E logits, in fp32.
+//
+// Quantile balancing ("从玩具到前沿:训练一个真正的大模型,到底难在哪里",
+// section 四 and appendix A.2): a per-expert bias is added to the logits
+// before routing (fp32 sum; it only changes the next choices), from a count
+// of each expert's selections over the past batches:
+//   expert_counts   per-block LDS histogram of topk, added to counts[E]
+//   balance_bias    b_i = -alpha (H_i / sum H - 1/E) over a window of counts
 #include <math.h>
 
 #include "common.h"
@@ -49,8 +56,10 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
+// bias: NULL, or [E] fp32 added to every token's logits (one fp32 rounding).
 template <int VPL>
 __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restrict__ logits,
+                                                          const float *__restrict__ bias,
                                                           int T, int E, int k,
                                                           int32_t *__restrict__ topk,
                                                           float *__restrict__ gates) {
@@ -65,7 +74,7 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     int e = lane + 64 * i;
-    v[i] = e < E ? l[e] : -INFINITY;
+    v[i] = e < E ? (bias ? l[e] + bias[e] : l[e]) : -INFINITY;
     m = fmaxf(m, v[i]);
     key[i] = e < E ? (((uint64_t)ord_f32(v[i]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e)) : 0ull;
   }
@@ -108,10 +117,87 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
 }
 
 template <int VPL>
-static int launch_route(const float *logits, int T, int E, int k, int32_t *topk, float *gates,
-                        hipStream_t s) {
+static int launch_route(const float *logits, const float *bias, int T, int E, int k,
+                        int32_t *topk, float *gates, hipStream_t s) {
   return launch("route_topk_softmax", route_topk_softmax<VPL>, dim3((unsigned)cdiv(T, 4)),
-                dim3(256), 0, s, logits, T, E, k, topk, gates);
+                dim3(256), 0, s, logits, bias, T, E, k, topk, gates);
+}
+
+static int route(const float *logits, const float *bias, int32_t T, int32_t E, int32_t k,
+                 int32_t *topk, float *gates, hipStream_t s) {
+  if (T < 1 || E < 1 || k < 1 || k > E)
+    return fail(MOE_ERR_INVALID, "moe_route: need T >= 1 and 1 <= k <= E");
+  if (E > 1024 || k > 32) return fail(MOE_ERR_UNSUPPORTED, "moe_route: E <= 1024, k <= 32");
+  MOE_TRY(check_ptr(logits, "logits"));
+  MOE_TRY(check_ptr(topk, "topk"));
+  MOE_TRY(check_ptr(gates, "gates"));
+  const int vpl = (int)cdiv(E, 64);
+  if (vpl <= 1) return launch_route<1>(logits, bias, T, E, k, topk, gates, s);
+  if (vpl <= 2) return launch_route<2>(logits, bias, T, E, k, topk, gates, s);
+  if (vpl <= 4) return launch_route<4>(logits, bias, T, E, k, topk, gates, s);
+  if (vpl <= 6) return launch_route<6>(logits, bias, T, E, k, topk, gates, s);
+  if (vpl <= 8) return launch_route<8>(logits, bias, T, E, k, topk, gates, s);
+  if (vpl <= 12) return launch_route<12>(logits, bias, T, E, k, topk, gates, s);
+  return launch_route<16>(logits, bias, T, E, k, topk, gates, s);
+}
+
+// ---------------------------------------------------------------------------
+// quantile balancing
+// ---------------------------------------------------------------------------
+
+constexpr int CNT_THREADS = 256, CNT_ITEMS = 16;  // items per thread
+
+__global__ __launch_bounds__(256) void counts_clear(int32_t *counts, int E) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) counts[e] = 0;
+}
+
+// Choices (t, j) of one block's items counted in LDS (integer adds: the
+// totals do not depend on the order), then added to counts.
+__global__ __launch_bounds__(CNT_THREADS) void expert_counts(const int32_t *__restrict__ topk,
+                                                             int64_t n, int E,
+                                                             int32_t *__restrict__ counts) {
+  __shared__ int32_t hist[1024];
+  for (int e = threadIdx.x; e < E; e += CNT_THREADS) hist[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * CNT_THREADS * CNT_ITEMS + threadIdx.x;
+  int32_t v[CNT_ITEMS];
+#pragma unroll
+  for (int i = 0; i < CNT_ITEMS; ++i) {
+    const int64_t it = base + (int64_t)i * CNT_THREADS;
+    v[i] = it < n ? topk[it] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < CNT_ITEMS; ++i)
+    if ((unsigned)v[i] < (unsigned)E) atomicAdd(&hist[v[i]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += CNT_THREADS)
+    if (hist[e]) atomicAdd(&counts[e], hist[e]);
+}
+
+// One block: H_i = sum over the window's batches, f_i = H_i / sum H (1/E when
+// nothing was chosen), b_i = -alpha (f_i - 1/E), in double, rounded to fp32.
+__global__ __launch_bounds__(1024) void balance_bias(const int32_t *__restrict__ window, int nb,
+                                                     int E, double alpha,
+                                                     float *__restrict__ bias) {
+  __shared__ int64_t part[1024 / 64];
+  const int i = threadIdx.x;
+  int64_t h = 0;
+  if (i < E)
+    for (int b = 0; b < nb; ++b) h += window[(int64_t)b * E + i];
+  int64_t w = h;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)w, m), hi = __shfl_xor((uint32_t)((uint64_t)w >> 32), m);
+    w += (int64_t)(((uint64_t)hi << 32) | lo);
+  }
+  if (lane_id() == 0) part[i >> 6] = w;
+  __syncthreads();
+  int64_t total = 0;
+  for (int q = 0; q < (int)(blockDim.x >> 6); ++q) total += part[q];
+  if (i < E) {
+    const double f = total > 0 ? (double)h / (double)total : 1.0 / (double)E;
+    bias[i] = (float)(-alpha * (f - 1.0 / (double)E));
+  }
 }
 
 }  // namespace moe
@@ -121,19 +207,41 @@ using namespace moe;
 extern "C" int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk,
                          float *gates, void *stream) {
   clear_error();
-  if (T < 1 || E < 1 || k < 1 || k > E)
-    return fail(MOE_ERR_INVALID, "moe_route: need T >= 1 and 1 <= k <= E");
-  if (E > 1024 || k > 32) return fail(MOE_ERR_UNSUPPORTED, "moe_route: E <= 1024, k <= 32");
-  MOE_TRY(check_ptr(logits, "logits"));
+  return route(logits, nullptr, T, E, k, topk, gates, (hipStream_t)stream);
+}
+
+extern "C" int moe_route_biased(const float *logits, const float *bias, int32_t T, int32_t E,
+                                int32_t k, int32_t *topk, float *gates, void *stream) {
+  clear_error();
+  MOE_TRY(check_ptr(bias, "bias", true));
+  return route(logits, bias, T, E, k, topk, gates, (hipStream_t)stream);
+}
+
+extern "C" int moe_expert_counts(const int32_t *topk, int32_t T, int32_t k, int32_t E,
+                                 int32_t *counts, void *stream) {
+  clear_error();
+  if (T < 1 || k < 1 || E < 1) return fail(MOE_ERR_INVALID, "moe_expert_counts: sizes must be >= 1");
+  if (E > 1024) return fail(MOE_ERR_UNSUPPORTED, "moe_expert_counts: E <= 1024");
+  if ((int64_t)T * k >= (1ll << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_counts: T * k must fit in int32");
   MOE_TRY(check_ptr(topk, "topk"));
-  MOE_TRY(check_ptr(gates, "gates"));
+  MOE_TRY(check_ptr(counts, "counts"));
   hipStream_t s = (hipStream_t)stream;
-  int vpl = (int)cdiv(E, 64);
-  if (vpl <= 1) return launch_route<1>(logits, T, E, k, topk, gates, s);
-  if (vpl <= 2) return launch_route<2>(logits, T, E, k, topk, gates, s);
-  if (vpl <= 4) return launch_route<4>(logits, T, E, k, topk, gates, s);
-  if (vpl <= 6) return launch_route<6>(logits, T, E, k, topk, gates, s);
-  if (vpl <= 8) return launch_route<8>(logits, T, E, k, topk, gates, s);
-  if (vpl <= 12) return launch_route<12>(logits, T, E, k, topk, gates, s);
-  return launch_route<16>(logits, T, E, k, topk, gates, s);
+  const int64_t n = (int64_t)T * k;
+  MOE_TRY(launch("counts_clear", counts_clear, dim3(1), dim3(256), 0, s, counts, E));
+  return launch("expert_counts", expert_counts,
+                dim3((unsigned)cdiv(n, (int64_t)CNT_THREADS * CNT_ITEMS)), dim3(CNT_THREADS), 0,
+                s, topk, n, E, counts);
+}
+
+extern "C" int moe_balance_bias(const int32_t *window, int32_t n_batches, int32_t E,
+                                double alpha, float *bias, void *stream) {
+  clear_error();
+  if (n_batches < 1 || E < 1) return fail(MOE_ERR_INVALID, "moe_balance_bias: sizes must be >= 1");
+  if (E > 1024) return fail(MOE_ERR_UNSUPPORTED, "moe_balance_bias: E <= 1024");
+  if (!(alpha == alpha)) return fail(MOE_ERR_INVALID, "moe_balance_bias: alpha is NaN");
+  MOE_TRY(check_ptr(window, "window"));
+  MOE_TRY(check_ptr(bias, "bias"));
+  return launch("balance_bias", balance_bias, dim3(1), dim3(1024), 0, (hipStream_t)stream,
+                window, n_batches, E, alpha, bias);
 }

@@ -62,8 +62,11 @@ class Sender:
         self.demand = torch.empty(R * W, dtype=torch.int32, device=dev)
         self.ws = _ws(d, L.MOE_CALL_PACK, 0, dev)
 
-    def route(self, logits, stream=None):
-        L.moe_route(logits, self.d.top_k, self.topk, self.gates, stream)
+    def route(self, logits, stream=None, bias=None):
+        if bias is None:
+            L.moe_route(logits, self.d.top_k, self.topk, self.gates, stream)
+        else:
+            L.moe_route_biased(logits, bias, self.d.top_k, self.topk, self.gates, stream)
 
     def pack(self, x, w_lat_down, stream=None):
         L.moe_pack_waves(self.d, x, w_lat_down, self.topk, self.z, self.pools, self.pool_offsets,
@@ -100,6 +103,26 @@ class Receiver:
         L.moe_expert_ffn(self.d, self.bank, self.bank_offsets, self.bank_src, self.bfill,
                          self.n_bank_rows, w_gate, w_up, w_down, self.ret, self.n_recv_rows,
                          self.ws_ffn, stream)
+
+
+class Balancer:
+    """Quantile balancing state of one router: the selection counts of the
+    last `window` batches (a ring of rows) and the bias they give."""
+
+    def __init__(self, n_experts, window, alpha, device="cuda"):
+        dev = torch.device(device)
+        self.E, self.window, self.alpha = n_experts, window, alpha
+        self.counts = torch.zeros(window, n_experts, dtype=torch.int32, device=dev)
+        self.bias = torch.zeros(n_experts, dtype=torch.float32, device=dev)
+        self.batches = 0
+
+    def update(self, topk, stream=None):
+        """Count this batch's choices into the ring, then recompute the bias."""
+        row = self.batches % self.window
+        L.moe_expert_counts(topk, self.E, self.counts[row], stream)
+        self.batches += 1
+        n = min(self.batches, self.window)
+        L.moe_balance_bias(self.counts[:n], self.alpha, self.bias, stream)
 
 
 class Combiner:

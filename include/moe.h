@@ -116,6 +116,28 @@ int64_t moe_workspace_bytes(const moe_dims *d, int call, int64_t n_rows);
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
               int32_t *topk, float *gates, void *stream);
 
+/* Quantile balancing ([P1] section 四 and appendix A.2): a per-expert bias,
+ * computed from how often each expert was chosen over the past batches, is
+ * added to the router logits; it changes only the next routing decisions.
+ *   moe_route_biased   moe_route on fp32(logits[t, e] + bias[e]) (selection
+ *                      and softmax both); bias [E] fp32, NULL = moe_route
+ *   moe_expert_counts  counts[e] = number of choices (t, j) with
+ *                      topk[t, j] == e (entries outside [0, E) not counted);
+ *                      topk [T, k] int32, counts [E] int32 out, fully written
+ *   moe_balance_bias   H_i = sum over the n_batches rows of window [n_batches,
+ *                      E] int32 (one row of counts per past batch; the caller
+ *                      keeps the rows), f_i = H_i / sum(H) (1/E if sum(H) is
+ *                      0), bias_i = -alpha * (f_i - 1/E) computed in double
+ *                      and rounded to fp32; bias [E] out.  The bias is set
+ *                      from the window, not accumulated.
+ * Supported: E <= 1024, k <= 32.  Errors as for moe_route. */
+int moe_route_biased(const float *logits, const float *bias, int32_t T, int32_t E,
+                     int32_t k, int32_t *topk, float *gates, void *stream);
+int moe_expert_counts(const int32_t *topk, int32_t T, int32_t k, int32_t E,
+                      int32_t *counts, void *stream);
+int moe_balance_bias(const int32_t *window, int32_t n_batches, int32_t E,
+                     double alpha, float *bias, void *stream);
+
 /* Sender ([P2]/[P3] section 二; [P1] appendix A.3): latent projection
  * z = x . W_ld, then every assignment (t, j) in (token, choice) order takes
  * the next position of pool (dest(e), wave(t)); kept iff the position is

@@ -109,3 +109,17 @@ def test_workspace_sizes_grow_with_rows(moe):
     a = moe.moe_workspace_bytes(d, moe.MOE_CALL_FFN, 100)
     b = moe.moe_workspace_bytes(d, moe.MOE_CALL_FFN, 1000)
     assert 0 < a < b
+
+
+def test_balancing_calls_reject_bad_arguments(moe):
+    L = moe.lib()
+    p = ctypes.c_void_p(256)
+    assert L.moe_route_biased(p, ctypes.c_void_p(18), 4, 16, 8, p, p, None) == -1  # misaligned bias
+    assert L.moe_route_biased(p, p, 4, 16, 17, p, p, None) == -1                   # k > E
+    assert L.moe_expert_counts(p, 4, 8, 2000, p, None) == -2                       # E > 1024
+    assert L.moe_expert_counts(p, 0, 8, 16, p, None) == -1
+    assert L.moe_expert_counts(None, 4, 8, 16, p, None) == -1
+    assert L.moe_balance_bias(p, 0, 16, 1.0, p, None) == -1                        # empty window
+    assert L.moe_balance_bias(p, 2, 16, float("nan"), p, None) == -1
+    assert L.moe_balance_bias(p, 2, 16, 1.0, None, None) == -1
+    assert "bias" in L.moe_last_error().decode()
