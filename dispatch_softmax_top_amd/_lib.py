@@ -46,7 +46,7 @@ _SIGS = {
                                     ctypes.POINTER(_I32)]),
     "moe_workspace_bytes": (_I64, [_DP, ctypes.c_int, _I64]),
     "moe_route": (ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _VP, _VP]),
-    "moe_route_biased": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _VP, _VP, _VP]),
+    "moe_route_biased": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP, _VP]),
     "moe_expert_counts": (ctypes.c_int, [_VP, _I32, _I32, _I32, _VP, _VP]),
     "moe_balance_bias": (ctypes.c_int, [_VP, _I32, _I32, ctypes.c_double, _VP, _VP]),
     "moe_pack_waves": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
@@ -131,9 +131,12 @@ def moe_route(logits, k, topk, gates, stream=None):
     _check(lib().moe_route(_p(logits), T, E, k, _p(topk), _p(gates), _stream(stream)))
 
 
-def moe_route_biased(logits, bias, k, topk, gates, stream=None):
+MOE_ROUTE_RENORM = 1
+
+
+def moe_route_biased(logits, bias, k, topk, gates, stream=None, flags=0):
     T, E = logits.shape
-    _check(lib().moe_route_biased(_p(logits), _p(bias), T, E, k, _p(topk), _p(gates),
+    _check(lib().moe_route_biased(_p(logits), _p(bias), T, E, k, flags, _p(topk), _p(gates),
                                   _stream(stream)))
 
 

@@ -57,10 +57,11 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 }
 
 // bias: NULL, or [E] fp32 added to every token's logits (one fp32 rounding).
+// renorm: gates divided by their sum over the k chosen.
 template <int VPL>
 __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restrict__ logits,
                                                           const float *__restrict__ bias,
-                                                          int T, int E, int k,
+                                                          int T, int E, int k, int renorm,
                                                           int32_t *__restrict__ topk,
                                                           float *__restrict__ gates) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
   }
 
   int my_idx = 0;
-  float my_gate = 0.f;
+  float my_gate = 0.f, my_logit = 0.f;
   for (int j = 0; j < k; ++j) {
     uint64_t best = wave_max_u64(key[0]);
     uint32_t e = 0xffffffffu - (uint32_t)best;
@@ -107,8 +108,16 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
     }
     if (lane == j) {
       my_idx = (int)e;
-      my_gate = expf(unord_f32((uint32_t)(best >> 32)) - m) / s;
+      my_logit = unord_f32((uint32_t)(best >> 32));
+      my_gate = expf(my_logit - m) / s;
     }
+  }
+  if (renorm) {
+    // the k chosen probabilities over their sum: the softmax over the chosen
+    // logits, from exp(l - the first choice's logit), in fp32
+    const float top = __shfl(my_logit, 0);
+    const float ej = lane < k ? expf(my_logit - top) : 0.f;
+    my_gate = ej / wave_sum_f32(ej);
   }
   if (lane < k) {
     topk[(int64_t)t * k + lane] = my_idx;
@@ -118,13 +127,13 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
 
 template <int VPL>
 static int launch_route(const float *logits, const float *bias, int T, int E, int k,
-                        int32_t *topk, float *gates, hipStream_t s) {
+                        int renorm, int32_t *topk, float *gates, hipStream_t s) {
   return launch("route_topk_softmax", route_topk_softmax<VPL>, dim3((unsigned)cdiv(T, 4)),
-                dim3(256), 0, s, logits, bias, T, E, k, topk, gates);
+                dim3(256), 0, s, logits, bias, T, E, k, renorm, topk, gates);
 }
 
 static int route(const float *logits, const float *bias, int32_t T, int32_t E, int32_t k,
-                 int32_t *topk, float *gates, hipStream_t s) {
+                 int renorm, int32_t *topk, float *gates, hipStream_t s) {
   if (T < 1 || E < 1 || k < 1 || k > E)
     return fail(MOE_ERR_INVALID, "moe_route: need T >= 1 and 1 <= k <= E");
   if (E > 1024 || k > 32) return fail(MOE_ERR_UNSUPPORTED, "moe_route: E <= 1024, k <= 32");
@@ -132,13 +141,13 @@ static int route(const float *logits, const float *bias, int32_t T, int32_t E, i
   MOE_TRY(check_ptr(topk, "topk"));
   MOE_TRY(check_ptr(gates, "gates"));
   const int vpl = (int)cdiv(E, 64);
-  if (vpl <= 1) return launch_route<1>(logits, bias, T, E, k, topk, gates, s);
-  if (vpl <= 2) return launch_route<2>(logits, bias, T, E, k, topk, gates, s);
-  if (vpl <= 4) return launch_route<4>(logits, bias, T, E, k, topk, gates, s);
-  if (vpl <= 6) return launch_route<6>(logits, bias, T, E, k, topk, gates, s);
-  if (vpl <= 8) return launch_route<8>(logits, bias, T, E, k, topk, gates, s);
-  if (vpl <= 12) return launch_route<12>(logits, bias, T, E, k, topk, gates, s);
-  return launch_route<16>(logits, bias, T, E, k, topk, gates, s);
+  if (vpl <= 1) return launch_route<1>(logits, bias, T, E, k, renorm, topk, gates, s);
+  if (vpl <= 2) return launch_route<2>(logits, bias, T, E, k, renorm, topk, gates, s);
+  if (vpl <= 4) return launch_route<4>(logits, bias, T, E, k, renorm, topk, gates, s);
+  if (vpl <= 6) return launch_route<6>(logits, bias, T, E, k, renorm, topk, gates, s);
+  if (vpl <= 8) return launch_route<8>(logits, bias, T, E, k, renorm, topk, gates, s);
+  if (vpl <= 12) return launch_route<12>(logits, bias, T, E, k, renorm, topk, gates, s);
+  return launch_route<16>(logits, bias, T, E, k, renorm, topk, gates, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -207,14 +216,17 @@ using namespace moe;
 extern "C" int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk,
                          float *gates, void *stream) {
   clear_error();
-  return route(logits, nullptr, T, E, k, topk, gates, (hipStream_t)stream);
+  return route(logits, nullptr, T, E, k, 0, topk, gates, (hipStream_t)stream);
 }
 
 extern "C" int moe_route_biased(const float *logits, const float *bias, int32_t T, int32_t E,
-                                int32_t k, int32_t *topk, float *gates, void *stream) {
+                                int32_t k, int32_t flags, int32_t *topk, float *gates,
+                                void *stream) {
   clear_error();
   MOE_TRY(check_ptr(bias, "bias", true));
-  return route(logits, bias, T, E, k, topk, gates, (hipStream_t)stream);
+  if (flags & ~MOE_ROUTE_RENORM) return fail(MOE_ERR_INVALID, "moe_route_biased: unknown flags");
+  return route(logits, bias, T, E, k, (flags & MOE_ROUTE_RENORM) != 0, topk, gates,
+               (hipStream_t)stream);
 }
 
 extern "C" int moe_expert_counts(const int32_t *topk, int32_t T, int32_t k, int32_t E,

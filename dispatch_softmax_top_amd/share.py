@@ -62,11 +62,12 @@ class Sender:
         self.demand = torch.empty(R * W, dtype=torch.int32, device=dev)
         self.ws = _ws(d, L.MOE_CALL_PACK, 0, dev)
 
-    def route(self, logits, stream=None, bias=None):
-        if bias is None:
+    def route(self, logits, stream=None, bias=None, renorm=False):
+        if bias is None and not renorm:
             L.moe_route(logits, self.d.top_k, self.topk, self.gates, stream)
         else:
-            L.moe_route_biased(logits, bias, self.d.top_k, self.topk, self.gates, stream)
+            L.moe_route_biased(logits, bias, self.d.top_k, self.topk, self.gates, stream,
+                               L.MOE_ROUTE_RENORM if renorm else 0)
 
     def pack(self, x, w_lat_down, stream=None):
         L.moe_pack_waves(self.d, x, w_lat_down, self.topk, self.z, self.pools, self.pool_offsets,

@@ -120,7 +120,11 @@ int moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
  * computed from how often each expert was chosen over the past batches, is
  * added to the router logits; it changes only the next routing decisions.
  *   moe_route_biased   moe_route on fp32(logits[t, e] + bias[e]) (selection
- *                      and softmax both); bias [E] fp32, NULL = moe_route
+ *                      and softmax both); bias [E] fp32, NULL = no bias.
+ *                      flags: MOE_ROUTE_RENORM divides each token's k gates
+ *                      by their sum (= softmax over the k chosen logits; the
+ *                      pages leave renormalisation open), 0 = moe_route's
+ *                      gates; other bits are rejected
  *   moe_expert_counts  counts[e] = number of choices (t, j) with
  *                      topk[t, j] == e (entries outside [0, E) not counted);
  *                      topk [T, k] int32, counts [E] int32 out, fully written
@@ -131,8 +135,9 @@ int moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
  *                      and rounded to fp32; bias [E] out.  The bias is set
  *                      from the window, not accumulated.
  * Supported: E <= 1024, k <= 32.  Errors as for moe_route. */
+enum { MOE_ROUTE_RENORM = 1 };
 int moe_route_biased(const float *logits, const float *bias, int32_t T, int32_t E,
-                     int32_t k, int32_t *topk, float *gates, void *stream);
+                     int32_t k, int32_t flags, int32_t *topk, float *gates, void *stream);
 int moe_expert_counts(const int32_t *topk, int32_t T, int32_t k, int32_t E,
                       int32_t *counts, void *stream);
 int moe_balance_bias(const int32_t *window, int32_t n_batches, int32_t E,

@@ -58,6 +58,7 @@ def lib():
             "orc_route": (None, [_f32p, i64, i32, i32, _i32p, _f32p]),
             "orc_route_biased": (None, [_f32p, _f32p, i64, i32, i32, _i32p, _f32p]),
             "orc_expert_counts": (None, [_i32p, i64, i32, _i32p]),
+            "orc_route_ex": (None, [_f32p, vp, i64, i32, i32, i32, _i32p, _f32p]),
             "orc_balance_bias": (None, [_i32p, i32, i32, ctypes.c_double, _f32p]),
             "orc_latent_rows": (None, [_u16p, i32, _u16p, i32, vp, i64, _u16p]),
             "orc_sender": (i64, [dp, _i32p, _i32p, _i32p, _i32p, vp]),
@@ -152,6 +153,18 @@ def route_biased(logits: np.ndarray, bias: np.ndarray, k: int):
     topk = np.empty((T, k), np.int32)
     gates = np.empty((T, k), np.float32)
     lib().orc_route_biased(logits, bias, T, E, k, topk, gates)
+    return topk, gates
+
+
+def route_ex(logits: np.ndarray, k: int, bias=None, renorm=False):
+    """Router with an optional bias and optionally renormalised gates."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    topk = np.empty((T, k), np.int32)
+    gates = np.empty((T, k), np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    lib().orc_route_ex(logits, None if b is None else b.ctypes.data, T, E, k, int(renorm),
+                       topk, gates)
     return topk, gates
 
 

@@ -130,6 +130,28 @@ void orc_route_biased(const float *logits, const float *bias, int64_t T,
   free(lb);
 }
 
+/* Variant of the gates (the pages leave it open whether the chosen experts'
+ * weights are renormalised): with renorm, gate j of token t is the chosen
+ * expert's probability divided by the sum over the k chosen, which is the
+ * softmax over the k chosen logits.  In double, rounded once to fp32. */
+void orc_route_ex(const float *logits, const float *bias, int64_t T,
+                  int32_t E, int32_t k, int32_t renorm, int32_t *topk,
+                  float *gates) {
+  float *lb = (float *)malloc(sizeof(float) * (size_t)E);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t e = 0; e < E; ++e)
+      lb[e] = bias ? logits[t * E + e] + bias[e] : logits[t * E + e];
+    orc_route(lb, 1, E, k, topk + t * k, gates + t * k);
+    if (renorm) {
+      double m = lb[topk[t * k]], z = 0.0; /* the first choice holds the largest logit */
+      for (int32_t j = 0; j < k; ++j) z += exp((double)lb[topk[t * k + j]] - m);
+      for (int32_t j = 0; j < k; ++j)
+        gates[t * k + j] = (float)(exp((double)lb[topk[t * k + j]] - m) / z);
+    }
+  }
+  free(lb);
+}
+
 /* [P1] appendix A.2: H counts how often each expert was chosen.  One batch's
  * counts: counts[e] = number of choices (t, j) with topk[t, j] == e; entries
  * outside [0, E) are not choices of an expert and are not counted. */

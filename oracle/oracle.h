@@ -54,6 +54,9 @@ void orc_route(const float *logits, int64_t T, int32_t E, int32_t k,
 
 void orc_route_biased(const float *logits, const float *bias, int64_t T,
                       int32_t E, int32_t k, int32_t *topk, float *gates);
+void orc_route_ex(const float *logits, const float *bias, int64_t T,
+                  int32_t E, int32_t k, int32_t renorm, int32_t *topk,
+                  float *gates);
 void orc_expert_counts(const int32_t *topk, int64_t n, int32_t E,
                        int32_t *counts);
 void orc_balance_bias(const int32_t *window, int32_t n_batches, int32_t E,

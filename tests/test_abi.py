@@ -114,8 +114,9 @@ def test_workspace_sizes_grow_with_rows(moe):
 def test_balancing_calls_reject_bad_arguments(moe):
     L = moe.lib()
     p = ctypes.c_void_p(256)
-    assert L.moe_route_biased(p, ctypes.c_void_p(18), 4, 16, 8, p, p, None) == -1  # misaligned bias
-    assert L.moe_route_biased(p, p, 4, 16, 17, p, p, None) == -1                   # k > E
+    assert L.moe_route_biased(p, ctypes.c_void_p(18), 4, 16, 8, 0, p, p, None) == -1  # misaligned
+    assert L.moe_route_biased(p, p, 4, 16, 17, 0, p, p, None) == -1                # k > E
+    assert L.moe_route_biased(p, p, 4, 16, 8, 6, p, p, None) == -1                 # unknown flag
     assert L.moe_expert_counts(p, 4, 8, 2000, p, None) == -2                       # E > 1024
     assert L.moe_expert_counts(p, 0, 8, 16, p, None) == -1
     assert L.moe_expert_counts(None, 4, 8, 16, p, None) == -1

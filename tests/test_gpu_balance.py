@@ -119,3 +119,19 @@ def test_balance_errors(moe):
         moe.moe_balance_bias(torch.zeros(0, 16, dtype=torch.int32, device="cuda"), 1.0, b)
     with pytest.raises(moe.MoeError):
         moe.moe_balance_bias(torch.zeros(2, 16, dtype=torch.int32, device="cuda"), float("nan"), b)
+
+
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_route_renormalised_gates(moe, orc, with_bias):
+    rng = np.random.default_rng(11)
+    T, E, k = 4096, 384, 8
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.5 * rng.standard_normal(E)).astype(np.float32) if with_bias else None
+    topk = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    gates = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    moe.moe_route_biased(gc.dev(lg), None if bias is None else gc.dev(bias), k, topk, gates,
+                         flags=moe.MOE_ROUTE_RENORM)
+    torch.cuda.synchronize()
+    ot, og = orc.route_ex(lg, k, bias=bias, renorm=True)
+    assert np.array_equal(gc.host(topk), ot)
+    np.testing.assert_allclose(gc.host(gates), og, rtol=2e-5, atol=1e-12)

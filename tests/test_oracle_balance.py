@@ -100,3 +100,25 @@ def test_balancing_evens_out_skewed_routing(orc):
         ratio[alpha] = np.mean(r[1:])
     assert ratio[0.0] > 5.5                  # unbalanced: the hottest expert takes every token
     assert ratio[40.0] < 0.85 * ratio[0.0]
+
+
+def test_renormalised_gates_are_softmax_over_the_chosen(orc):
+    """Gate variant: with renormalisation the k gates of a token are the
+    softmax over its k chosen logits (closed form), sum to 1, and keep the
+    ratios of the full-softmax gates; the choices do not change."""
+    rng = np.random.default_rng(8)
+    T, E, k = 150, 48, 8
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.2 * rng.standard_normal(E)).astype(np.float32)
+    for b in (None, bias):
+        t0, g0 = orc.route_ex(lg, k, bias=b)
+        t1, g1 = orc.route_ex(lg, k, bias=b, renorm=True)
+        assert np.array_equal(t0, t1)
+        lb = lg if b is None else lg + b[None, :]
+        chosen = np.take_along_axis(lb, t1, 1).astype(np.float64)
+        z = np.exp(chosen - chosen.max(1, keepdims=True))
+        assert np.abs(g1 - z / z.sum(1, keepdims=True)).max() < 1e-7
+        assert np.abs(g1.astype(np.float64).sum(1) - 1).max() < 1e-6
+        np.testing.assert_allclose(g1 / g1[:, :1], g0 / g0[:, :1], rtol=1e-6)
+    assert np.array_equal(orc.route_ex(lg, k)[1], orc.route(lg, k)[1])
+    assert np.array_equal(orc.route_ex(lg, k, bias=bias)[1], orc.route_biased(lg, bias, k)[1])

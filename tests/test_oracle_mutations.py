@@ -45,6 +45,10 @@ MUTATIONS = [
      "test_oracle_balance.py"),
     ("expert 0 not counted", "if (topk[i] >= 0 && topk[i] < E) counts[topk[i]] += 1;",
      "if (topk[i] > 0 && topk[i] < E) counts[topk[i]] += 1;", "test_oracle_balance.py"),
+    ("renormalised over k - 1",
+     "      for (int32_t j = 0; j < k; ++j) z += exp((double)lb[topk[t * k + j]] - m);",
+     "      for (int32_t j = 1; j < k; ++j) z += exp((double)lb[topk[t * k + j]] - m);",
+     "test_oracle_balance.py"),
     ("window: last batch only",
      "    for (int32_t b = 0; b < n_batches; ++b) h += window[(int64_t)b * E + i];",
      "    for (int32_t b = n_batches - 1; b < n_batches; ++b) h += window[(int64_t)b * E + i];",
