@@ -26,7 +26,7 @@ _f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "d_model", "latent", "n_experts", "n_ranks", "top_k", "n_waves",
-        "d_ff", "n_shared", "d_ff_shared", "cap_send", "cap_recv")]
+        "d_ff", "n_shared", "d_ff_shared", "cap_send", "cap_recv", "wave_mode")]
 
 
 def build() -> str:
@@ -107,8 +107,11 @@ def dims(cfg, T=None) -> Dims:
         cs = capacity(tw, cfg.top_k, cfg.n_ranks, cfg.cf_send.numerator, cfg.cf_send.denominator)
         cr = capacity(tw, cfg.top_k, cfg.experts_per_rank, cfg.cf_recv.numerator,
                       cfg.cf_recv.denominator)
+    if cfg.waves == "chunks" and not cs:
+        raise ValueError("chunked waves need a fixed sender capacity")
     return Dims(T, cfg.d_model, cfg.latent, cfg.n_experts, cfg.n_ranks, cfg.top_k,
-                cfg.n_waves, cfg.d_ff, cfg.n_shared, cfg.d_ff_shared, cs, cr)
+                cfg.n_waves, cfg.d_ff, cfg.n_shared, cfg.d_ff_shared, cs, cr,
+                1 if cfg.waves == "chunks" else 0)
 
 
 def row_bytes(d: Dims) -> int:

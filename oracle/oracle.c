@@ -213,6 +213,41 @@ static int32_t dest_of(const orc_dims *d, int32_t e) {
   return e / (d->n_experts / d->n_ranks);
 }
 
+/* READING (other wave reading, wave_mode 1): one pool of W*cap_send rows
+ * per destination, filled in (token, choice) order; position i lies in chunk
+ * (wave) i / cap_send.  fill and demand are reported per chunk: chunk w holds
+ * min(max(n - w*cap, 0), cap) rows, and the rows past the last chunk count as
+ * that chunk's unmet demand. */
+static int64_t orc_sender_chunks(const orc_dims *d, const int32_t *topk,
+                                 int32_t *slot, int32_t *fill,
+                                 int32_t *demand) {
+  const int32_t W = d->n_waves, R = d->n_ranks, k = d->top_k;
+  const int64_t cap = d->cap_send, pool = (int64_t)W * cap;
+  int64_t drops = 0;
+  int64_t *n = (int64_t *)calloc((size_t)R, sizeof(int64_t));
+  for (int32_t t = 0; t < d->T; ++t) {
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t e = topk[(int64_t)t * k + j];
+      int64_t pos = n[dest_of(d, e)]++;
+      if (pos < pool) {
+        slot[(int64_t)t * k + j] = (int32_t)pos;
+      } else {
+        slot[(int64_t)t * k + j] = -1;
+        ++drops;
+      }
+    }
+  }
+  for (int32_t r = 0; r < R; ++r)
+    for (int32_t w = 0; w < W; ++w) {
+      int64_t left = n[r] - w * cap;
+      if (left < 0) left = 0;
+      fill[r * W + w] = (int32_t)(left < cap ? left : cap);
+      demand[r * W + w] = (int32_t)(w + 1 < W ? fill[r * W + w] : left);
+    }
+  free(n);
+  return drops;
+}
+
 /* [P2]/[P3] section 二: one fixed pool per destination GPU (not per expert),
  * three waves of equal shape, overflow beyond the sender capacity dropped and
  * counted apart.  [P1] appendix A.3 describes the same fixed per-destination
@@ -228,6 +263,7 @@ int64_t orc_sender(const orc_dims *d, const int32_t *topk, int32_t *slot,
   const int32_t W = d->n_waves, R = d->n_ranks, k = d->top_k;
   const int32_t Tw = orc_tokens_per_wave(d->T, W);
   const int32_t cap = d->cap_send;
+  if (d->wave_mode == 1) return orc_sender_chunks(d, topk, slot, fill, demand);
   int64_t drops = 0;
   int32_t *n = (int32_t *)calloc((size_t)R * W, sizeof(int32_t));
   for (int32_t t = 0; t < d->T; ++t) {
@@ -288,6 +324,7 @@ void orc_pack_rows(const orc_dims *d, const uint16_t *z, const int32_t *topk,
       int32_t e = topk[(int64_t)t * k + j];
       int32_t p = dest_of(d, e) * W + t / Tw;
       int64_t row = d->cap_send ? (int64_t)p * d->cap_send + s : pool_offsets[p] + s;
+      if (d->wave_mode == 1) row = (int64_t)dest_of(d, e) * W * d->cap_send + s;
       memcpy(pools + row * rb, z + (int64_t)t * L, (size_t)L * 2);
       put_header(pools + row * rb, L, e);
     }
@@ -483,7 +520,9 @@ void orc_combine_tokens(const orc_dims *d, const uint16_t *returned,
       int32_t e = topk[t * k + j];
       int32_t seg = dest_of(d, e) * W + w;
       int64_t row;
-      if (d->cap_send) {
+      if (d->wave_mode == 1) {
+        row = (int64_t)dest_of(d, e) * W * d->cap_send + s; /* slot: position in the dest's pool */
+      } else if (d->cap_send) {
         row = (int64_t)seg * d->cap_send + s;
       } else {
         if (s >= ret_offsets[seg + 1] - ret_offsets[seg]) continue;

@@ -34,9 +34,14 @@
 extern "C" {
 #endif
 
+/* wave_mode 0: wave(t) = t / T_w, one pool of cap_send rows per (dest,
+ * wave).  wave_mode 1 (the other reading of the waves, fixed mode only): one
+ * pool of n_waves*cap_send rows per dest, filled in (token, choice) order and
+ * cut into n_waves chunks of cap_send rows; chunk w is wave w.  The layout
+ * [R][W][cap_send] is the same; slot is then the position in the dest's pool. */
 typedef struct {
   int32_t T, d_model, latent, n_experts, n_ranks, top_k, n_waves, d_ff,
-      n_shared, d_ff_shared, cap_send, cap_recv;
+      n_shared, d_ff_shared, cap_send, cap_recv, wave_mode;
 } orc_dims;
 
 /* bf16 <-> double, round to nearest even, straight from double. */

@@ -35,6 +35,9 @@ class Workload:
     cf_recv: Optional[Fraction]
     routing: str = "plain"        # "plain" | "zipf" | "longctx"
     shards: int = 0               # number of source shards (0 = n_ranks)
+    # "tokens": wave(t) = t / T_w, a pool per (destination, wave); "chunks": one
+    # pool of n_waves * C_s rows per destination, cut into n_waves chunks
+    waves: str = "tokens"
 
     @property
     def experts_per_rank(self) -> int:

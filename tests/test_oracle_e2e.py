@@ -109,11 +109,13 @@ def brute_force(cfg, d, W_, S):
     Tw = math.ceil(T / Wv)
     Cs = d.cap_send or 10 ** 9
     Cr = d.cap_recv or 10 ** 9
-    # sender position: rank of (t, j) among same (dest, wave) items in (t, j) order
+    chunks = cfg.waves == "chunks"
+    # sender position: rank of (t, j) among same (dest, wave) items in (t, j) order;
+    # with chunked waves among same-dest items (one pool of Wv * Cs rows per dest)
     send_pos = []
     for s in range(R):
         topk = S[s]["topk"]
-        key = (topk // El) * Wv + (np.arange(T) // Tw)[:, None]
+        key = topk // El if chunks else (topk // El) * Wv + (np.arange(T) // Tw)[:, None]
         flat = key.reshape(-1)
         pos = np.zeros_like(flat)
         for kk in np.unique(flat):
@@ -125,8 +127,10 @@ def brute_force(cfg, d, W_, S):
     for s in range(R):
         for t in range(T):
             for j in range(k):
-                if send_pos[s][t, j] < Cs:
-                    recs.append((int(S[s]["topk"][t, j]), t // Tw, s, int(send_pos[s][t, j]), t, j))
+                p = int(send_pos[s][t, j])
+                if p < (Wv * Cs if chunks else Cs):
+                    w = p // Cs if chunks else t // Tw
+                    recs.append((int(S[s]["topk"][t, j]), w, s, p, t, j))
     recs.sort()
     keep = [np.zeros((T, k), bool) for _ in range(R)]
     cur, n = None, 0
@@ -159,15 +163,17 @@ def brute_force(cfg, d, W_, S):
     return outs
 
 
-@pytest.mark.parametrize("cf", ["1.10/1.15", "inf", "tight"])
+@pytest.mark.parametrize("cf", ["1.10/1.15", "inf", "tight", "chunks", "chunks_tight"])
 def test_e2e_tiny_matches_brute_force(orc, cf):
     from dataclasses import replace
     from fractions import Fraction
     cfg = configs.TINY
     if cf == "inf":
         cfg = replace(cfg, cf_send=None, cf_recv=None)
-    elif cf == "tight":   # forces sender and receiver drops
+    elif cf.endswith("tight"):   # forces sender and receiver drops
         cfg = replace(cfg, cf_send=Fraction(1, 2), cf_recv=Fraction(1, 2))
+    if cf.startswith("chunks"):  # the other reading of the waves
+        cfg = replace(cfg, waves="chunks")
     d, W_, S, BK, OUT = simulate(orc, cfg)
     ref = brute_force(cfg, d, W_, S)
     El, W, Tw = cfg.experts_per_rank, cfg.n_waves, math.ceil(cfg.T / cfg.n_waves)
@@ -184,7 +190,9 @@ def test_e2e_tiny_matches_brute_force(orc, cf):
                 if sl < 0:
                     continue
                 r, w = S[s]["topk"][t, j] // El, t // Tw
-                if d.cap_send:
+                if d.wave_mode == 1:
+                    row = (s * W + sl // d.cap_send) * d.cap_send + sl % d.cap_send
+                elif d.cap_send:
                     row = (s * W + w) * d.cap_send + sl
                 else:
                     lens = [S[q]["demand"][r * W + ww] for q in range(cfg.n_ranks) for ww in range(W)]
@@ -200,5 +208,5 @@ def test_e2e_tiny_matches_brute_force(orc, cf):
     assert n_exact / n_all > 0.999
     if cf == "inf":
         assert total_drop == 0
-    if cf == "tight":
+    if cf.endswith("tight"):
         assert total_drop > 0

@@ -53,6 +53,19 @@ MUTATIONS = [
      "    for (int32_t b = 0; b < n_batches; ++b) h += window[(int64_t)b * E + i];",
      "    for (int32_t b = n_batches - 1; b < n_batches; ++b) h += window[(int64_t)b * E + i];",
      "test_oracle_balance.py"),
+    ("chunk demand: last chunk capped",
+     "      demand[r * W + w] = (int32_t)(w + 1 < W ? fill[r * W + w] : left);",
+     "      demand[r * W + w] = fill[r * W + w];", "test_oracle_pins.py"),
+    ("chunk pool one chunk short",
+     "  const int64_t cap = d->cap_send, pool = (int64_t)W * cap;",
+     "  const int64_t cap = d->cap_send, pool = (int64_t)(W - 1) * cap;", "test_oracle_pins.py"),
+    ("chunk rows offset by wave",
+     "      if (d->wave_mode == 1) row = (int64_t)dest_of(d, e) * W * d->cap_send + s;",
+     "      if (d->wave_mode == 1) row = (int64_t)(dest_of(d, e) * W + t / Tw) * d->cap_send + s;",
+     "test_oracle_pins.py"),
+    ("chunk combine row",
+     "        row = (int64_t)dest_of(d, e) * W * d->cap_send + s; /* slot: position in the dest's pool */",
+     "        row = (int64_t)seg * d->cap_send + s % d->cap_send;", "test_oracle_e2e.py"),
 ]
 
 

@@ -246,6 +246,84 @@ def test_pack_rows_content(orc):
     assert (pools[:, d.latent * 2 + 4:] == 0).all()
 
 
+def _chunk_dims(orc, **kw):
+    d = _tiny_dims(orc, **kw)
+    d.wave_mode = 1
+    return d
+
+
+def test_sender_chunks_brute_force(orc):
+    """Other reading of the waves: one pool of W*C_s rows per destination,
+    position p in chunk p // C_s; brute force over (token, choice) order."""
+    rng = np.random.default_rng(13)
+    for cs in (1, 2, 3, 5, 9):
+        d = _chunk_dims(orc, T=29, cs=cs)
+        topk = _rand_topk(rng, d.T, d.n_experts, d.top_k)
+        r = orc.sender(d, topk)
+        El, W = d.n_experts // d.n_ranks, d.n_waves
+        items = [(t, j) for t in range(d.T) for j in range(d.top_k)]
+        per_dest = np.zeros(d.n_ranks, int)
+        for n, (t, j) in enumerate(items):
+            dst = int(topk[t, j]) // El
+            pos = sum(1 for (t2, j2) in items[:n] if int(topk[t2, j2]) // El == dst)
+            assert r["slot"][t, j] == (pos if pos < W * cs else -1)
+            per_dest[dst] += 1
+        for dst in range(d.n_ranks):
+            for w in range(W):
+                left = max(per_dest[dst] - w * cs, 0)
+                assert r["fill"][dst * W + w] == min(left, cs)
+                assert r["demand"][dst * W + w] == (min(left, cs) if w < W - 1 else left)
+        assert r["demand"].reshape(d.n_ranks, W).sum(1).tolist() == per_dest.tolist()
+        assert r["fill"].sum() + r["drops"] == d.T * d.top_k
+        assert r["drops"] == np.maximum(per_dest - W * cs, 0).sum()
+
+
+def test_sender_chunks_never_drop_more_than_token_waves(orc):
+    """sum_w min(n_w, C) <= min(sum_w n_w, W C): for the same routing the
+    chunked reading keeps at least as many assignments as waves by token."""
+    rng = np.random.default_rng(14)
+    for cs in range(1, 12):
+        topk = _rand_topk(rng, 40, 12, 3)
+        a = orc.sender(_tiny_dims(orc, T=40, cs=cs), topk)["drops"]
+        b = orc.sender(_chunk_dims(orc, T=40, cs=cs), topk)["drops"]
+        assert b <= a
+    # skewed routing: every token to destination 0; token waves keep W*C only
+    # when each wave alone has C of them, chunks keep W*C regardless of order
+    topk = np.tile(np.arange(3, dtype=np.int32), (40, 1))
+    a = orc.sender(_tiny_dims(orc, T=40, cs=5), topk)
+    b = orc.sender(_chunk_dims(orc, T=40, cs=5), topk)
+    assert a["drops"] == b["drops"] == 120 - 15
+    assert b["fill"].tolist() == [5, 5, 5] + [0] * 9
+
+
+def test_pack_rows_chunks_content(orc):
+    rng = np.random.default_rng(15)
+    d = _chunk_dims(orc, T=30, cs=3)
+    topk = _rand_topk(rng, d.T, d.n_experts, d.top_k)
+    z = rng.integers(0, 2 ** 16, (d.T, d.latent)).astype(np.uint16)
+    s = orc.sender(d, topk)
+    pools = orc.pack_rows(d, z, topk, s["slot"])
+    hdr = orc.headers(pools, d.latent)
+    El, W = d.n_experts // d.n_ranks, d.n_waves
+    used = np.zeros(len(pools), bool)
+    for t in range(d.T):
+        for j in range(d.top_k):
+            sl = s["slot"][t, j]
+            if sl < 0:
+                continue
+            row = (topk[t, j] // El) * W * d.cap_send + sl
+            assert hdr[row] == topk[t, j]
+            assert (pools[row, :d.latent * 2].view(np.uint16) == z[t]).all()
+            used[row] = True
+    assert used.sum() == s["fill"].sum()
+    assert (hdr[~used] == -1).all()
+    # chunk w of dest r occupies rows (r*W + w)*C_s .. +fill: a prefix of the chunk
+    for p in range(d.n_ranks * W):
+        f = s["fill"][p]
+        assert used[p * d.cap_send:p * d.cap_send + f].all()
+        assert not used[p * d.cap_send + f:(p + 1) * d.cap_send].any()
+
+
 # ----------------------------------------------------------------------------
 # receiver bank
 # ----------------------------------------------------------------------------
