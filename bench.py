@@ -77,7 +77,11 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False, keep_logits=False)
         st.sent_demand += int(snd.demand.sum())
         st.sent_fill += int(snd.fill.sum())
         e = snd.topk.long()
-        key = ((e // El) * W + wave_of[:, None]) * El + e % El
+        if d.wave_mode == moe_waves_chunks():   # the wave is the chunk of the slot
+            wv = snd.slot.long().clamp(min=0) // d.cap_send
+        else:
+            wv = wave_of[:, None]
+        key = ((e // El) * W + wv) * El + e % El
         st.recv_counts += torch.bincount(key[snd.slot >= 0], minlength=R * W * El)
         if d.cap_send:
             rv[s].copy_(snd.pools.view(R, W, d.cap_send, -1)[rank])
@@ -109,6 +113,11 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False, keep_logits=False)
     torch.cuda.synchronize()
     st.bal = None  # quantile balancing state (bench --balance-alpha)
     return st
+
+
+def moe_waves_chunks():
+    from dispatch_softmax_top_amd import MOE_WAVES_CHUNKS
+    return MOE_WAVES_CHUNKS
 
 
 def receiver_stats(st):
@@ -339,6 +348,9 @@ def main():
                     help="quantile balancing on: route with the bias -ALPHA (f - 1/E) from the "
                          "selection counts of the past --balance-window batches")
     ap.add_argument("--balance-window", type=int, default=8)
+    ap.add_argument("--waves", choices=("tokens", "chunks"), default="tokens",
+                    help="tokens: wave(t) = t / T_w, a pool per (destination, wave); chunks: "
+                         "one pool of n_waves * C_s rows per destination cut into n_waves chunks")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise device copy of MIB mebibytes, three "
                          "times: the reference for hardware byte counters")
@@ -364,6 +376,9 @@ def main():
         return
 
     cfg = configs.WORKLOADS[args.config]
+    if args.waves != cfg.waves:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, waves=args.waves)
     rank = 0 if args.rank == "hot" else int(args.rank)
     log(f"bench: {cfg.name} rank {args.rank}: setup")
     st = setup(cfg, rank, progress=True)
@@ -476,6 +491,7 @@ def main():
                    "top_k": d.top_k, "n_waves": d.n_waves, "d_ff": d.d_ff,
                    "n_shared": d.n_shared, "cap_send": d.cap_send, "cap_recv": d.cap_recv,
                    "source_shards": cfg.n_shards, "streams": 1 if args.serial else 3,
+                   "waves": cfg.waves,
                    "balance": None if st.bal is None else
                    {"alpha": args.balance_alpha, "window": args.balance_window}},
         "roofline": {"kernel": dom, "bound": "mfma", "measured": "per-kernel pass after the "

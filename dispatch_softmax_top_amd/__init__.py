@@ -2,7 +2,7 @@
 (libmoe.so, include/moe.h) with a thin ctypes binding of the same names."""
 from ._lib import (EXPORTS, MOE_CALL_BANK, MOE_CALL_COMBINE, MOE_CALL_COMBINE_SHARED,  # noqa: F401
                    MOE_CALL_FFN, MOE_CALL_PACK, MOE_CALL_ROUTE, MOE_ROUTE_RENORM, LIB_PATH, MoeDims,
-                   MoeError, lib,
+                   MOE_WAVES_CHUNKS, MOE_WAVES_TOKENS, MoeError, lib,
                    moe_abi_version, moe_balance_bias, moe_bank, moe_capacity, moe_combine,
                    moe_combine_shared, moe_expert_counts, moe_expert_ffn, moe_pack_waves,
                    moe_profile_collect, moe_profile_enable, moe_profile_read, moe_profile_reset,

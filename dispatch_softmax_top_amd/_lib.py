@@ -27,7 +27,7 @@ class MoeError(RuntimeError):
 class MoeDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "d_model", "latent", "n_experts", "n_ranks", "top_k", "n_waves",
-        "d_ff", "n_shared", "d_ff_shared", "cap_send", "cap_recv")]
+        "d_ff", "n_shared", "d_ff_shared", "cap_send", "cap_recv", "wave_mode")]
 
     def __repr__(self):
         return "MoeDims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -132,6 +132,7 @@ def moe_route(logits, k, topk, gates, stream=None):
 
 
 MOE_ROUTE_RENORM = 1
+MOE_WAVES_TOKENS, MOE_WAVES_CHUNKS = 0, 1
 
 
 def moe_route_biased(logits, bias, k, topk, gates, stream=None, flags=0):

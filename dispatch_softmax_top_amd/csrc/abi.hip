@@ -47,6 +47,10 @@ int check_dims(const moe_dims *d) {
     return fail(MOE_ERR_INVALID, "dims: cap_send and cap_recv must be both 0 (ragged) or both > 0");
   if (d->top_k > d->n_experts)
     return fail(MOE_ERR_INVALID, "dims: top_k > n_experts");
+  if (d->wave_mode != MOE_WAVES_TOKENS && d->wave_mode != MOE_WAVES_CHUNKS)
+    return fail(MOE_ERR_INVALID, "dims: wave_mode must be MOE_WAVES_TOKENS or MOE_WAVES_CHUNKS");
+  if (d->wave_mode == MOE_WAVES_CHUNKS && d->cap_send == 0)
+    return fail(MOE_ERR_INVALID, "dims: chunked waves need fixed capacities");
   if (d->n_experts > 1024 || d->top_k > 32)
     return fail(MOE_ERR_UNSUPPORTED, "dims: n_experts <= 1024 and top_k <= 32 supported");
   if (d->latent % 64 || d->d_model % 64)

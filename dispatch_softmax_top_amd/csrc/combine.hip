@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void combine_gather_kernel(
     const uint16_t *__restrict__ returned, const int64_t *__restrict__ ret_offsets,
     const int32_t *__restrict__ topk, const int32_t *__restrict__ slot,
     const float *__restrict__ gates, uint16_t *__restrict__ ylat, int T, int k, int L, int El,
-    int W, int Tw, int cap, int parts) {
+    int Wk, int Tw, int pool_rows, int cap, int parts) {
   const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);  // < 2^31: T <= 2^27, parts <= 16
   const int t = wv / parts;
   if (t >= T) return;
@@ -46,9 +46,9 @@ __global__ __launch_bounds__(256) void combine_gather_kernel(
     const int e = topk[(int64_t)t * k + lane];
     const float g = gates[(int64_t)t * k + lane];
     if (s >= 0) {
-      const int p = (e / El) * W + t / Tw;
+      const int p = (e / El) * Wk + t / Tw;
       if (cap) {
-        my_row = (int64_t)p * cap + s;
+        my_row = (int64_t)p * pool_rows + s;
       } else if (s < ret_offsets[p + 1] - ret_offsets[p]) {
         my_row = ret_offsets[p] + s;
       }
@@ -99,10 +99,11 @@ static int gather(const moe_dims &d, const uint16_t *returned, const int64_t *re
                   const int32_t *topk, const int32_t *slot, const float *gates, uint16_t *ylat,
                   hipStream_t s) {
   const int parts = (int)cdiv(cdiv(d.latent / 8, 64), CH);
+  const PoolKey pk = pool_key(d);
   return launch("combine_gather", combine_gather_kernel<CH>,
                 dim3((unsigned)cdiv((int64_t)d.T * parts, 4)), dim3(256), 0, s, returned,
                 ret_offsets, topk, slot, gates, ylat, d.T, d.top_k, d.latent,
-                experts_per_rank(d), d.n_waves, tokens_per_wave(d), d.cap_send, parts);
+                experts_per_rank(d), pk.Wk, pk.Tw, pk.rows, d.cap_send, parts);
 }
 
 // gather + up-projection with the shared experts' intermediate H [T, S*Fs]

@@ -24,6 +24,17 @@ inline int32_t experts_per_rank(const moe_dims &d) { return d.n_experts / d.n_ra
 inline int32_t tokens_per_wave(const moe_dims &d) { return (d.T + d.n_waves - 1) / d.n_waves; }
 inline bool ragged(const moe_dims &d) { return d.cap_send == 0; }
 inline int64_t row_bytes(const moe_dims &d) { return 2 * (int64_t)d.latent + 16; }
+// How a (token, choice) assignment finds its sender pool: key = dest * Wk +
+// t / Tw, row = key * rows + slot.  Waves by token: (W, T_w, C_s).  Chunked
+// waves: the key is the destination alone (Wk = 1, Tw past every token) and
+// its pool holds all W chunks (rows = W * C_s).
+struct PoolKey {
+  int Wk, Tw, rows;
+};
+inline PoolKey pool_key(const moe_dims &d) {
+  if (d.wave_mode == MOE_WAVES_CHUNKS) return {1, d.T + 1, d.n_waves * d.cap_send};
+  return {d.n_waves, tokens_per_wave(d), d.cap_send};
+}
 
 // Launch bookkeeping: records hipEvents around a launch when timing is on.
 struct ProfScope {

@@ -12,6 +12,12 @@
 // Kernels, in stream order:
 //   rank_count / rank_assign  positions of (token, choice) assignments in
 //                             their pool, in (token, choice) order
+//
+// Pools are keyed by (dest, wave(t)) when waves split the tokens, and by
+// dest alone when they cut each destination's pool of W*C_s rows into W
+// chunks; both cases share the kernels through (pool key, rows per key):
+// key = dest * Wk + t / Tw with Wk = W (or 1, and Tw past T), and a kept
+// row lands at key * pool_rows + slot with pool_rows = C_s (or W * C_s).
 //   gemm_latent_down          z = x . W_ld (bf16 MFMA)
 //   pack_rows                 one wave per token: z[t] read once, written to
 //                             each kept destination row with 16-byte stores;
@@ -37,16 +43,28 @@ struct SenderSrc {
   }
 };
 
+// chunks = W when the key is the destination alone (its pool holds W chunks
+// of cap rows), 0 when the key already names the wave.
 template <bool RAGGED>
 struct SenderEmit {
   static constexpr bool needs_offsets = RAGGED;
   int32_t *slot, *fill, *demand;
   int64_t *pool_offsets;
-  int cap;
+  int cap, chunks;
   __device__ void item(int64_t it, int key, int32_t, int rank, const int64_t *) const {
-    slot[it] = (key >= 0 && (RAGGED || rank < cap)) ? rank : -1;
+    const int limit = chunks ? chunks * cap : cap;  // W * cap < 2^31 (checked on the host)
+    slot[it] = (key >= 0 && (RAGGED || rank < limit)) ? rank : -1;
   }
   __device__ void totals(int K, const int32_t *tot, const int64_t *koff, int32_t) const {
+    if (chunks) {  // fill / demand per (dest, chunk); the overflow is the last chunk's
+      for (int q = threadIdx.x; q < K * chunks; q += blockDim.x) {
+        const int w = q % chunks;
+        const int left = max(tot[q / chunks] - w * cap, 0);
+        fill[q] = min(left, cap);
+        demand[q] = w + 1 < chunks ? min(left, cap) : left;
+      }
+      return;
+    }
     for (int kk = threadIdx.x; kk < K; kk += blockDim.x) {
       demand[kk] = tot[kk];
       fill[kk] = RAGGED ? tot[kk] : min(tot[kk], cap);
@@ -56,6 +74,7 @@ struct SenderEmit {
   }
 };
 
+
 // One wave per token: each lane loads all CH of its 16-byte chunks of z[t]
 // first (the whole row in flight), then writes them to every kept row.
 template <int CH>
@@ -63,7 +82,7 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(
     const uint16_t *__restrict__ z, const int32_t *__restrict__ topk,
     const int32_t *__restrict__ slot, const int32_t *__restrict__ fill,
     const int64_t *__restrict__ pool_offsets, uint8_t *__restrict__ pools, int T, int k, int L,
-    int El, int W, int Tw, int cap, int token_blocks, int64_t n_slots) {
+    int El, int Wk, int Tw, int pool_rows, int cap, int token_blocks, int64_t n_slots) {
   const int64_t RB = 2 * (int64_t)L + 16;
   const int lane = lane_id();
   if ((int)blockIdx.x < token_blocks) {
@@ -79,8 +98,8 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(
       const int s = slot[(int64_t)t * k + lane];
       const int e = topk[(int64_t)t * k + lane];  // independent of s: same round trip
       if (s >= 0) {
-        const int p = (e / El) * W + t / Tw;
-        my_row = cap ? p * cap + s : (int)pool_offsets[p] + s;
+        const int p = (e / El) * Wk + t / Tw;
+        my_row = cap ? p * pool_rows + s : (int)pool_offsets[p] + s;
         my_e = e;
       }
     }
@@ -117,10 +136,10 @@ static int pack_copy(const moe_dims &d, const uint16_t *z, const int32_t *topk,
                      const int32_t *slot, const int32_t *fill, const int64_t *pool_offsets,
                      uint8_t *pools, int token_blocks, int64_t n_slots, hipStream_t s) {
   const int64_t blocks = token_blocks + cdiv(n_slots, 256);
+  const PoolKey pk = pool_key(d);
   return launch("pack_rows", pack_rows_kernel<CH>, dim3((unsigned)blocks), dim3(256), 0, s, z,
                 topk, slot, fill, pool_offsets, pools, d.T, d.top_k, d.latent,
-                experts_per_rank(d), d.n_waves, tokens_per_wave(d), d.cap_send, token_blocks,
-                n_slots);
+                experts_per_rank(d), pk.Wk, pk.Tw, pk.rows, d.cap_send, token_blocks, n_slots);
 }
 
 template <bool RAGGED>
@@ -128,10 +147,12 @@ static int sender_slots(const moe_dims &d, const int32_t *topk, int32_t *slot, i
                         int32_t *demand, int64_t *pool_offsets, int32_t *tile_counts,
                         hipStream_t s) {
   const int64_t n = (int64_t)d.T * d.top_k;
-  const int K = d.n_ranks * d.n_waves;
+  const PoolKey pk = pool_key(d);
+  const int K = d.n_ranks * pk.Wk;
   const int tiles = (int)rank_tiles(n);
-  SenderSrc src{topk, d.top_k, d.n_experts, experts_per_rank(d), d.n_waves, tokens_per_wave(d)};
-  SenderEmit<RAGGED> em{slot, fill, demand, pool_offsets, d.cap_send};
+  SenderSrc src{topk, d.top_k, d.n_experts, experts_per_rank(d), pk.Wk, pk.Tw};
+  SenderEmit<RAGGED> em{slot, fill, demand, pool_offsets, d.cap_send,
+                        d.wave_mode == MOE_WAVES_CHUNKS ? d.n_waves : 0};
   MOE_TRY(launch("rank_count_sender", rank_count<SenderSrc>, dim3(tiles), dim3(RK_THREADS), 0, s,
                  src, n, K, tile_counts, (int32_t *)nullptr, (int64_t)0));
   return launch("rank_assign_sender", rank_assign<SenderSrc, SenderEmit<RAGGED>>, dim3(tiles),

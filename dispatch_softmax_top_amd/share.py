@@ -20,8 +20,9 @@ RANK_TILE = 8192  # items per slot-assignment tile (keeps workspace sizes honest
 def make_dims(cfg, T=None) -> L.MoeDims:
     """Dims of a workload; capacities from the library's own formula."""
     T = cfg.T if T is None else T
+    waves = {"tokens": L.MOE_WAVES_TOKENS, "chunks": L.MOE_WAVES_CHUNKS}[cfg.waves]
     d = L.MoeDims(T, cfg.d_model, cfg.latent, cfg.n_experts, cfg.n_ranks, cfg.top_k,
-                  cfg.n_waves, cfg.d_ff, cfg.n_shared, cfg.d_ff_shared, 0, 0)
+                  cfg.n_waves, cfg.d_ff, cfg.n_shared, cfg.d_ff_shared, 0, 0, waves)
     if cfg.cf_send is not None:
         d.cap_send, d.cap_recv = L.moe_capacity(d, Fraction(cfg.cf_send), Fraction(cfg.cf_recv))
     return d

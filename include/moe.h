@@ -43,8 +43,13 @@
  *     but each (outer, wave) segment has its own length and starts at an
  *     int64 offset; an offsets array has one entry per segment plus the
  *     total at the end.
- *   - Waves split a shard's tokens into contiguous runs: wave(t) =
- *     floor(t / T_w), T_w = ceil(T / n_waves).  Expert e lives on rank
+ *   - Waves (wave_mode MOE_WAVES_TOKENS) split a shard's tokens into
+ *     contiguous runs: wave(t) = floor(t / T_w), T_w = ceil(T / n_waves).
+ *     With MOE_WAVES_CHUNKS (fixed mode only) the waves instead cut one
+ *     pool of n_waves*cap_send rows per destination into n_waves chunks:
+ *     an assignment's slot is its position in the destination's pool and
+ *     its wave is slot / cap_send.  The buffer layouts above are the same
+ *     in both modes (pool (dest, w) is chunk w).  Expert e lives on rank
  *     floor(e / E_l) as local expert e mod E_l, E_l = n_experts / n_ranks.
  *   - Every output is fully written except where stated unspecified.
  *   - Errors: arguments are checked on the host before any launch; a
@@ -62,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef uint16_t moe_bf16;
 
@@ -80,11 +85,15 @@ typedef enum {
  * n_experts <= 1024, 1 <= top_k <= min(32, n_experts), latent % 64 == 0,
  * latent <= 8192, T <= 2^27, T * top_k < 2^31,
  * d_model % 64 == 0, d_ff % 128 == 0, d_ff_shared % 128 == 0,
- * n_ranks * n_waves <= 1024, n_waves * E_l <= 1024, n_shared <= 4. */
+ * n_ranks * n_waves <= 1024, n_waves * E_l <= 1024, n_shared <= 4.
+ * wave_mode: MOE_WAVES_TOKENS (0) or MOE_WAVES_CHUNKS (1, needs fixed
+ * mode); the two readings of how a shard is sent in waves. */
 typedef struct {
   int32_t T, d_model, latent, n_experts, n_ranks, top_k, n_waves, d_ff,
-      n_shared, d_ff_shared, cap_send, cap_recv;
+      n_shared, d_ff_shared, cap_send, cap_recv, wave_mode;
 } moe_dims;
+
+enum { MOE_WAVES_TOKENS = 0, MOE_WAVES_CHUNKS = 1 };
 
 int moe_abi_version(void);
 
@@ -146,7 +155,11 @@ int moe_balance_bias(const int32_t *window, int32_t n_batches, int32_t E,
 /* Sender ([P2]/[P3] section 二; [P1] appendix A.3): latent projection
  * z = x . W_ld, then every assignment (t, j) in (token, choice) order takes
  * the next position of pool (dest(e), wave(t)); kept iff the position is
- * below cap_send (always in ragged mode).
+ * below cap_send (always in ragged mode).  MOE_WAVES_CHUNKS: the next
+ * position of dest(e)'s pool of n_waves*cap_send rows, kept iff below that;
+ * row dest*n_waves*cap_send + slot; fill[p] / demand[p] are then chunk w's
+ * rows, clamp(n - w*cap_send, 0, cap_send), with the rows past the last
+ * chunk added to the last chunk's demand.
  *   x           [T, d_model] bf16
  *   w_lat_down  [latent, d_model] bf16 (W_ld^T)
  *   topk        [T, k] int32 from moe_route

@@ -34,6 +34,11 @@ def skewed(cfg):
     return replace(cfg, name=cfg.name + "_zipf", routing="zipf")
 
 
+def chunked(cfg):
+    """The other reading of the waves: one pool per destination cut into chunks."""
+    return replace(cfg, name=cfg.name + "_chunks", waves="chunks")
+
+
 def shard_inputs(cfg, s, device="cpu"):
     x = gen.hidden(cfg, s, device)
     wr = gen.router_weight(cfg, device)
@@ -79,6 +84,12 @@ def recv_headers(cfg, d_orc, senders, rank):
     segs, lens = [], []
     for snd in senders:
         topk, slot = snd["topk"], snd["slot"]
+        if d_orc.wave_mode == 1:         # one pool of W * C_s rows; slot = row in it
+            h = -np.ones(W * d_orc.cap_send, np.int32)
+            mine = (topk // El == rank) & (slot >= 0)
+            h[slot[mine]] = topk[mine]
+            segs.append(h)
+            continue
         for w in range(W):
             n = d_orc.cap_send if d_orc.cap_send else int(snd["demand"][rank * W + w])
             h = -np.ones(n, np.int32)

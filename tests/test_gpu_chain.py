@@ -22,6 +22,7 @@ CASES = {
     "mid": gc.MID,
     "mid_ragged": gc.ragged(gc.MID),
     "mid_zipf": gc.skewed(gc.MID),
+    "mid_zipf_chunks": gc.chunked(gc.skewed(gc.MID)),
 }
 
 

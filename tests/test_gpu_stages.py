@@ -23,6 +23,8 @@ CASES = {
     "mid_ragged": gc.ragged(gc.MID),
     "mid_zipf": gc.skewed(gc.MID),
     "mid_tight": gc.with_cf(gc.MID, "1/2", "3/5"),
+    "mid_chunks": gc.chunked(gc.MID),
+    "mid_chunks_tight": gc.chunked(gc.with_cf(gc.MID, "1/2", "3/5")),
     # more waves than the grouped GEMM merges into one product group: every
     # (wave, expert) bank group is its own product group
     "mid_w5": configs.scaled(gc.MID, gc.MID.name + "_W5", n_waves=5),
@@ -133,7 +135,10 @@ def test_pack(moe, orc, share, name):
             if s < 0:
                 continue
             p = (topk[t, j] // El) * cfg.n_waves + t // Tw
-            row = p * d.cap_send + s if d.cap_send else so["pool_offsets"][p] + s
+            if d.wave_mode == 1:
+                row = (topk[t, j] // El) * cfg.n_waves * d.cap_send + s
+            else:
+                row = p * d.cap_send + s if d.cap_send else so["pool_offsets"][p] + s
             assert np.array_equal(pg[row, :2 * d.latent].view(np.uint16), zg[t])
     assert kept.sum() == so["fill"].sum()
 
