@@ -72,6 +72,15 @@ def lib():
             "orc_combine_tokens": (None, [dp, _u16p, vp, _i32p, _i32p, _f32p,
                                           _u16p, _u16p, _u16p, _u16p, _u16p, vp,
                                           i64, _u16p, _u16p]),
+            "orc_route_backward": (None, [_f32p, vp, i64, i32, i32, i32, _i32p, _f32p,
+                                          _f32p]),
+            "orc_combine_backward": (None, [dp, _u16p, _i32p, _i32p, _f32p, _u16p, _u16p,
+                                            _u16p, _u16p, _u16p, _u16p, _u16p, _u16p,
+                                            _f32p, _u16p, _u16p, _u16p]),
+            "orc_expert_ffn_backward": (None, [dp, _u16p, _i32p, _i32p, _u16p, _u16p, _u16p,
+                                               _u16p, i64, _u16p, _u16p, _u16p, _u16p]),
+            "orc_pack_backward": (None, [dp, _u16p, _i32p, _i32p, _u16p, _u16p, _u16p, _u16p,
+                                         _u16p, _u16p, _u16p, _u16p, _u16p, _u16p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -287,3 +296,72 @@ def combine(d: Dims, returned, ret_offsets, topk, slot, gates, x, w_lu_t,
         np.ascontiguousarray(ws_up, np.uint16), np.ascontiguousarray(ws_down, np.uint16),
         _ptr(tk), n, ylat, out)
     return ylat, out
+
+
+# ----------------------------------------------------------------------------
+# backward of the branch (fixed capacities)
+# ----------------------------------------------------------------------------
+
+def _u16(a):
+    return np.ascontiguousarray(a, np.uint16)
+
+
+def route_backward(logits, topk, d_gates, bias=None, renorm=False):
+    """d_logits [T, E] fp32 from the gradient of the gates."""
+    logits = np.ascontiguousarray(logits, np.float32)
+    T, E = logits.shape
+    k = topk.shape[1]
+    out = np.empty((T, E), np.float32)
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    lib().orc_route_backward(logits, None if b is None else b.ctypes.data, T, E, k, int(renorm),
+                             np.ascontiguousarray(topk, np.int32),
+                             np.ascontiguousarray(d_gates, np.float32), out)
+    return out
+
+
+def combine_backward(d: Dims, returned, topk, slot, gates, x, ylat, w_lu_t, ws_gate, ws_up,
+                     ws_down, d_out):
+    """(d_returned, d_gates, d_shared [T, 2, S, Fs], dw_lat_up, dws_down)."""
+    T, L, D, S, Fs = d.T, d.latent, d.d_model, d.n_shared, d.d_ff_shared
+    n_rows = d.n_ranks * d.n_waves * d.cap_send
+    d_ret = np.empty((n_rows, L), np.uint16)
+    d_gates = np.empty((T, d.top_k), np.float32)
+    d_shared = np.empty((T, 2, S, Fs), np.uint16)
+    dw_lu = np.empty((D, L), np.uint16)
+    dws_down = np.empty((S, D, Fs), np.uint16)
+    lib().orc_combine_backward(
+        ctypes.byref(d), _u16(returned), np.ascontiguousarray(topk, np.int32),
+        np.ascontiguousarray(slot, np.int32), np.ascontiguousarray(gates, np.float32), _u16(x),
+        _u16(ylat), _u16(w_lu_t), _u16(ws_gate), _u16(ws_up), _u16(ws_down), _u16(d_out),
+        d_ret, d_gates, d_shared, dw_lu, dws_down)
+    return d_ret, d_gates, d_shared, dw_lu, dws_down
+
+
+def expert_ffn_backward(d: Dims, bank, bank_src, bfill, w_gate, w_up, w_down, d_ret):
+    """(d_recv, dw_gate, dw_up, dw_down) of one rank's experts."""
+    El = d.n_experts // d.n_ranks
+    n_ret = len(d_ret)
+    d_recv = np.empty((n_ret, d.latent), np.uint16)
+    dwg = np.empty((El, d.d_ff, d.latent), np.uint16)
+    dwu = np.empty_like(dwg)
+    dwd = np.empty((El, d.latent, d.d_ff), np.uint16)
+    lib().orc_expert_ffn_backward(
+        ctypes.byref(d), _u16(bank), np.ascontiguousarray(bank_src, np.int32),
+        np.ascontiguousarray(bfill, np.int32), _u16(w_gate), _u16(w_up), _u16(w_down),
+        _u16(d_ret), n_ret, d_recv, dwg, dwu, dwd)
+    return d_recv, dwg, dwu, dwd
+
+
+def pack_backward(d: Dims, d_pools, topk, slot, x, d_shared, w_ld_t, ws_gate, ws_up):
+    """(dz, dx, dw_lat_down, dws_gate, dws_up)."""
+    T, L, D, S, Fs = d.T, d.latent, d.d_model, d.n_shared, d.d_ff_shared
+    dz = np.empty((T, L), np.uint16)
+    dx = np.empty((T, D), np.uint16)
+    dw_ld = np.empty((L, D), np.uint16)
+    dwsg = np.empty((S, Fs, D), np.uint16)
+    dwsu = np.empty_like(dwsg)
+    lib().orc_pack_backward(
+        ctypes.byref(d), _u16(d_pools), np.ascontiguousarray(topk, np.int32),
+        np.ascontiguousarray(slot, np.int32), _u16(x), _u16(d_shared), _u16(w_ld_t),
+        _u16(ws_gate), _u16(ws_up), dz, dx, dw_ld, dwsg, dwsu)
+    return dz, dx, dw_ld, dwsg, dwsu

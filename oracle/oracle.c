@@ -562,3 +562,295 @@ void orc_combine_tokens(const orc_dims *d, const uint16_t *returned,
   free(xr);
   free(h);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward of the branch                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* [P2]/[P3] (the model is being trained) give the forward pass only; the
+ * gradients below follow from the forward definitions above by the chain
+ * rule, for a loss whose gradient with respect to out is d_out.
+ * READING (rounding points): every gradient tensor is stored like the value
+ * it belongs to -- activation and weight gradients in bf16 (a parameter's
+ * gradient has the parameter's type), gate and logit gradients in fp32 --
+ * and each is one double sum rounded once.  The intermediates a = u.W_g and
+ * b = u.W_u are recomputed from the forward inputs in double.  Fixed
+ * capacities only. */
+
+/* d silu / da = s (1 + a (1 - s)), s = 1 / (1 + e^-a) */
+static double silu_grad(double a) {
+  double s = 1.0 / (1.0 + exp(-a));
+  return s * (1.0 + a * (1.0 - s));
+}
+
+/* Row of assignment (t, e, slot s) in the sender's pools (fixed mode). */
+static int64_t pool_row(const orc_dims *d, int64_t t, int32_t e, int32_t s) {
+  const int32_t W = d->n_waves;
+  if (d->wave_mode == 1) return (int64_t)dest_of(d, e) * W * d->cap_send + s;
+  return ((int64_t)dest_of(d, e) * W + t / orc_tokens_per_wave(d->T, W)) * d->cap_send + s;
+}
+
+/* Router: with p = softmax(l) over all E (l = fp32(logit + bias)) and gate
+ * g_j = p[e_j], dL/dl[e] = sum_j d_gates[j] * g_j * ([e == e_j] - p[e]).
+ * Renormalised gates (q = softmax over the k chosen logits):
+ * dL/dl[e_j] = q_j (d_gates[j] - sum_i d_gates[i] q_i), 0 for the others.
+ * The bias is stop-gradient.  p and q are recomputed in double. */
+void orc_route_backward(const float *logits, const float *bias, int64_t T,
+                        int32_t E, int32_t k, int32_t renorm,
+                        const int32_t *topk, const float *d_gates,
+                        float *d_logits) {
+  double *p = (double *)malloc(sizeof(double) * (size_t)E);
+  double *dl = (double *)malloc(sizeof(double) * (size_t)E);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t e = 0; e < E; ++e) {
+      float lb = bias ? logits[t * E + e] + bias[e] : logits[t * E + e];
+      p[e] = lb;
+      dl[e] = 0.0;
+    }
+    const int32_t *tk = topk + t * k;
+    const float *dg = d_gates + t * k;
+    if (!renorm) {
+      double m = p[0], Z = 0.0, s = 0.0;
+      for (int32_t e = 1; e < E; ++e)
+        if (p[e] > m) m = p[e];
+      for (int32_t e = 0; e < E; ++e) Z += exp(p[e] - m);
+      for (int32_t e = 0; e < E; ++e) p[e] = exp(p[e] - m) / Z;
+      for (int32_t j = 0; j < k; ++j) s += (double)dg[j] * p[tk[j]];
+      for (int32_t e = 0; e < E; ++e) dl[e] = -p[e] * s;
+      for (int32_t j = 0; j < k; ++j) dl[tk[j]] += (double)dg[j] * p[tk[j]];
+    } else {
+      double m = p[tk[0]], z = 0.0, s = 0.0;
+      for (int32_t j = 1; j < k; ++j)
+        if (p[tk[j]] > m) m = p[tk[j]];
+      for (int32_t j = 0; j < k; ++j) z += exp(p[tk[j]] - m);
+      for (int32_t j = 0; j < k; ++j) s += (double)dg[j] * exp(p[tk[j]] - m) / z;
+      for (int32_t j = 0; j < k; ++j) {
+        double q = exp(p[tk[j]] - m) / z;
+        dl[tk[j]] = q * ((double)dg[j] - s);
+      }
+    }
+    for (int32_t e = 0; e < E; ++e) d_logits[t * E + e] = (float)dl[e];
+  }
+  free(p);
+  free(dl);
+}
+
+/* Combine side.  From out = ylat.W_lu + sum_s h_s.W_sd,s and
+ * ylat[t] = sum_j g[t,j] returned[row(t,j)]:
+ *   d_ylat[t]          = bf16(d_out[t] . W_lu^T)        (used, not stored)
+ *   d_h_s[t]           = bf16(d_out[t] . W_sd,s^T)
+ *   d_returned[row]    = bf16(g[t,j] d_ylat[t]) for kept (t, j); other rows 0
+ *   d_gates[t,j]       = fp32(returned[row] . d_ylat[t]); 0 if dropped
+ *   d_shared[t][0][s]  = bf16(d_h_s * b * silu'(a)),  a = x.W_sg,s, b = x.W_su,s
+ *   d_shared[t][1][s]  = bf16(d_h_s * silu(a))
+ *   dw_lat_up[c][i]    = bf16(sum_t d_out[t][c] ylat[t][i])      ([D][L])
+ *   dws_down[s][c][f]  = bf16(sum_t d_out[t][c] h_s[t][f])       ([S][D][Fs])
+ * with h_s = bf16(silu(a) b) as in the forward pass. */
+void orc_combine_backward(const orc_dims *d, const uint16_t *returned,
+                          const int32_t *topk, const int32_t *slot,
+                          const float *gates, const uint16_t *x,
+                          const uint16_t *ylat, const uint16_t *w_lu_t,
+                          const uint16_t *ws_gate, const uint16_t *ws_up,
+                          const uint16_t *ws_down, const uint16_t *d_out,
+                          uint16_t *d_returned, float *d_gates,
+                          uint16_t *d_shared, uint16_t *dw_lat_up,
+                          uint16_t *dws_down) {
+  const int64_t T = d->T;
+  const int32_t L = d->latent, D = d->d_model, k = d->top_k;
+  const int32_t S = d->n_shared, Fs = d->d_ff_shared;
+  const int64_t n_rows = (int64_t)d->n_ranks * d->n_waves * d->cap_send;
+  double *dyl = (double *)malloc(sizeof(double) * (size_t)L);
+  uint16_t *hs = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(T * S * Fs + 1));
+  memset(d_returned, 0, sizeof(uint16_t) * (size_t)(n_rows * L));
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t *go = d_out + t * D;
+    for (int32_t i = 0; i < L; ++i) {
+      double acc = 0.0;
+      for (int32_t c = 0; c < D; ++c) acc += bf(go[c]) * bf(w_lu_t[(int64_t)c * L + i]);
+      dyl[i] = bf(to_bf(acc));
+    }
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t s = slot[t * k + j];
+      if (s < 0) {
+        d_gates[t * k + j] = 0.0f;
+        continue;
+      }
+      int64_t row = pool_row(d, t, topk[t * k + j], s);
+      double g = gates[t * k + j], dot = 0.0;
+      for (int32_t i = 0; i < L; ++i) {
+        d_returned[row * L + i] = to_bf(g * dyl[i]);
+        dot += bf(returned[row * L + i]) * dyl[i];
+      }
+      d_gates[t * k + j] = (float)dot;
+    }
+    for (int32_t sh = 0; sh < S; ++sh)
+      for (int32_t f = 0; f < Fs; ++f) {
+        double dh = 0.0, a = 0.0, b = 0.0;
+        for (int32_t c = 0; c < D; ++c)
+          dh += bf(go[c]) * bf(ws_down[((int64_t)sh * D + c) * Fs + f]);
+        dh = bf(to_bf(dh));
+        const uint16_t *wg = ws_gate + ((int64_t)sh * Fs + f) * D;
+        const uint16_t *wu = ws_up + ((int64_t)sh * Fs + f) * D;
+        for (int32_t i = 0; i < D; ++i) a += bf(x[t * D + i]) * bf(wg[i]);
+        for (int32_t i = 0; i < D; ++i) b += bf(x[t * D + i]) * bf(wu[i]);
+        hs[(t * S + sh) * Fs + f] = to_bf(silu(a) * b);
+        d_shared[(t * 2 * S + sh) * Fs + f] = to_bf(dh * b * silu_grad(a));
+        d_shared[(t * 2 * S + S + sh) * Fs + f] = to_bf(dh * silu(a));
+      }
+  }
+  for (int32_t c = 0; c < D; ++c) {
+    for (int32_t i = 0; i < L; ++i) {
+      double acc = 0.0;
+      for (int64_t t = 0; t < T; ++t) acc += bf(d_out[t * D + c]) * bf(ylat[t * L + i]);
+      dw_lat_up[(int64_t)c * L + i] = to_bf(acc);
+    }
+    for (int32_t sh = 0; sh < S; ++sh)
+      for (int32_t f = 0; f < Fs; ++f) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t)
+          acc += bf(d_out[t * D + c]) * bf(hs[(t * S + sh) * Fs + f]);
+        dws_down[((int64_t)sh * D + c) * Fs + f] = to_bf(acc);
+      }
+  }
+  free(dyl);
+  free(hs);
+}
+
+/* Receiver side.  For every kept bank row u of group (wave, j) with
+ * dy = d_ret[bank_src] (the gradient of its expert output):
+ *   d_h[f] = bf16(sum_l dy[l] W_d,j[l][f])
+ *   a, b = u.W_g,j, u.W_u,j;  h = bf16(silu(a) b)
+ *   d_a = bf16(d_h b silu'(a)),  d_b = bf16(d_h silu(a))
+ *   d_recv[bank_src] = bf16(sum_f d_a[f] W_g[f] + d_b[f] W_u[f]); other rows 0
+ *   dw_down[j][l][f] = bf16(sum over expert j's rows of dy[l] h[f])
+ *   dw_gate[j][f][l] = bf16(sum of d_a[f] u[l]), dw_up likewise with d_b,
+ * the weight sums running over the rows in (wave, bank position) order. */
+void orc_expert_ffn_backward(const orc_dims *d, const uint16_t *bank,
+                             const int32_t *bank_src, const int32_t *bfill,
+                             const uint16_t *w_gate, const uint16_t *w_up,
+                             const uint16_t *w_down, const uint16_t *d_ret,
+                             int64_t n_ret_rows, uint16_t *d_recv,
+                             uint16_t *dw_gate, uint16_t *dw_up,
+                             uint16_t *dw_down) {
+  const int32_t L = d->latent, F = d->d_ff;
+  const int32_t El = d->n_experts / d->n_ranks;
+  const int64_t WL = (int64_t)F * L;
+  double *gd = (double *)calloc((size_t)(El * WL), sizeof(double));
+  double *gg = (double *)calloc((size_t)(El * WL), sizeof(double));
+  double *gu = (double *)calloc((size_t)(El * WL), sizeof(double));
+  double *u = (double *)malloc(sizeof(double) * (size_t)L);
+  double *dy = (double *)malloc(sizeof(double) * (size_t)L);
+  double *h = (double *)malloc(sizeof(double) * (size_t)F);
+  double *da = (double *)malloc(sizeof(double) * (size_t)F);
+  double *db = (double *)malloc(sizeof(double) * (size_t)F);
+  memset(d_recv, 0, sizeof(uint16_t) * (size_t)(n_ret_rows * L));
+  for (int32_t w = 0; w < d->n_waves; ++w)
+    for (int32_t j = 0; j < El; ++j) {
+      int32_t g = w * El + j;
+      const uint16_t *Wg = w_gate + j * WL, *Wu = w_up + j * WL, *Wd = w_down + j * WL;
+      for (int32_t p = 0; p < bfill[g]; ++p) {
+        int64_t pos = (int64_t)g * d->cap_recv + p, src = bank_src[pos];
+        for (int32_t l = 0; l < L; ++l) {
+          u[l] = bf(bank[pos * L + l]);
+          dy[l] = bf(d_ret[src * L + l]);
+        }
+        for (int32_t f = 0; f < F; ++f) {
+          double dh = 0.0, a = 0.0, b = 0.0;
+          for (int32_t l = 0; l < L; ++l) dh += dy[l] * bf(Wd[(int64_t)l * F + f]);
+          dh = bf(to_bf(dh));
+          for (int32_t l = 0; l < L; ++l) a += u[l] * bf(Wg[(int64_t)f * L + l]);
+          for (int32_t l = 0; l < L; ++l) b += u[l] * bf(Wu[(int64_t)f * L + l]);
+          h[f] = bf(to_bf(silu(a) * b));
+          da[f] = bf(to_bf(dh * b * silu_grad(a)));
+          db[f] = bf(to_bf(dh * silu(a)));
+        }
+        for (int32_t l = 0; l < L; ++l) {
+          double acc = 0.0;
+          for (int32_t f = 0; f < F; ++f)
+            acc += da[f] * bf(Wg[(int64_t)f * L + l]) + db[f] * bf(Wu[(int64_t)f * L + l]);
+          d_recv[src * L + l] = to_bf(acc);
+        }
+        for (int32_t l = 0; l < L; ++l)
+          for (int32_t f = 0; f < F; ++f) gd[j * WL + (int64_t)l * F + f] += dy[l] * h[f];
+        for (int32_t f = 0; f < F; ++f)
+          for (int32_t l = 0; l < L; ++l) {
+            gg[j * WL + (int64_t)f * L + l] += da[f] * u[l];
+            gu[j * WL + (int64_t)f * L + l] += db[f] * u[l];
+          }
+      }
+    }
+  for (int64_t i = 0; i < El * WL; ++i) {
+    dw_down[i] = to_bf(gd[i]);
+    dw_gate[i] = to_bf(gg[i]);
+    dw_up[i] = to_bf(gu[i]);
+  }
+  free(gd);
+  free(gg);
+  free(gu);
+  free(u);
+  free(dy);
+  free(h);
+  free(da);
+  free(db);
+}
+
+/* Sender side.  d_pools holds the gradients of the pool rows (the sender's
+ * [R][W][cap_send] layout, latent wide).  From z = x.W_ld, the pack copy and
+ * the shared experts' inputs:
+ *   dz[t]              = bf16(sum_j over kept (t, j) of d_pools[row(t,j)])
+ *   dx[t][i]           = bf16(sum_l dz[t][l] W_ld[l][i]
+ *                             + sum_s sum_f d_a[t,s,f] W_sg,s[f][i] + d_b[t,s,f] W_su,s[f][i])
+ *   dw_lat_down[l][i]  = bf16(sum_t dz[t][l] x[t][i])               ([L][D])
+ *   dws_gate[s][f][i]  = bf16(sum_t d_a[t,s,f] x[t][i]), dws_up likewise,
+ * with d_a, d_b from d_shared ([T][2][S][Fs], the combine side's output). */
+void orc_pack_backward(const orc_dims *d, const uint16_t *d_pools,
+                       const int32_t *topk, const int32_t *slot,
+                       const uint16_t *x, const uint16_t *d_shared,
+                       const uint16_t *w_ld_t, const uint16_t *ws_gate,
+                       const uint16_t *ws_up, uint16_t *dz, uint16_t *dx,
+                       uint16_t *dw_lat_down, uint16_t *dws_gate,
+                       uint16_t *dws_up) {
+  const int64_t T = d->T;
+  const int32_t L = d->latent, D = d->d_model, k = d->top_k;
+  const int32_t S = d->n_shared, Fs = d->d_ff_shared;
+  double *acc = (double *)malloc(sizeof(double) * (size_t)L);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int32_t l = 0; l < L; ++l) acc[l] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t s = slot[t * k + j];
+      if (s < 0) continue;
+      int64_t row = pool_row(d, t, topk[t * k + j], s);
+      for (int32_t l = 0; l < L; ++l) acc[l] += bf(d_pools[row * L + l]);
+    }
+    for (int32_t l = 0; l < L; ++l) dz[t * L + l] = to_bf(acc[l]);
+    for (int32_t i = 0; i < D; ++i) {
+      double o = 0.0;
+      for (int32_t l = 0; l < L; ++l) o += bf(dz[t * L + l]) * bf(w_ld_t[(int64_t)l * D + i]);
+      for (int32_t sh = 0; sh < S; ++sh)
+        for (int32_t f = 0; f < Fs; ++f) {
+          int64_t wi = ((int64_t)sh * Fs + f) * D + i;
+          o += bf(d_shared[(t * 2 * S + sh) * Fs + f]) * bf(ws_gate[wi]) +
+               bf(d_shared[(t * 2 * S + S + sh) * Fs + f]) * bf(ws_up[wi]);
+        }
+      dx[t * D + i] = to_bf(o);
+    }
+  }
+  for (int32_t i = 0; i < D; ++i) {
+    for (int32_t l = 0; l < L; ++l) {
+      double a = 0.0;
+      for (int64_t t = 0; t < T; ++t) a += bf(dz[t * L + l]) * bf(x[t * D + i]);
+      dw_lat_down[(int64_t)l * D + i] = to_bf(a);
+    }
+    for (int32_t sh = 0; sh < S; ++sh)
+      for (int32_t f = 0; f < Fs; ++f) {
+        double ag = 0.0, au = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+          ag += bf(d_shared[(t * 2 * S + sh) * Fs + f]) * bf(x[t * D + i]);
+          au += bf(d_shared[(t * 2 * S + S + sh) * Fs + f]) * bf(x[t * D + i]);
+        }
+        dws_gate[((int64_t)sh * Fs + f) * D + i] = to_bf(ag);
+        dws_up[((int64_t)sh * Fs + f) * D + i] = to_bf(au);
+      }
+  }
+  free(acc);
+}

@@ -106,6 +106,37 @@ void orc_combine_tokens(const orc_dims *d, const uint16_t *returned,
                         const uint16_t *ws_down, const int64_t *tokens,
                         int64_t n, uint16_t *ylat, uint16_t *out);
 
+/* Backward of the branch (fixed capacities).  Layouts as in the forward
+ * calls; d_shared is [T][2][n_shared][d_ff_shared]: the gradients of the
+ * shared experts' gate products, then of their up products. */
+void orc_route_backward(const float *logits, const float *bias, int64_t T,
+                        int32_t E, int32_t k, int32_t renorm,
+                        const int32_t *topk, const float *d_gates,
+                        float *d_logits);
+void orc_combine_backward(const orc_dims *d, const uint16_t *returned,
+                          const int32_t *topk, const int32_t *slot,
+                          const float *gates, const uint16_t *x,
+                          const uint16_t *ylat, const uint16_t *w_lu_t,
+                          const uint16_t *ws_gate, const uint16_t *ws_up,
+                          const uint16_t *ws_down, const uint16_t *d_out,
+                          uint16_t *d_returned, float *d_gates,
+                          uint16_t *d_shared, uint16_t *dw_lat_up,
+                          uint16_t *dws_down);
+void orc_expert_ffn_backward(const orc_dims *d, const uint16_t *bank,
+                             const int32_t *bank_src, const int32_t *bfill,
+                             const uint16_t *w_gate, const uint16_t *w_up,
+                             const uint16_t *w_down, const uint16_t *d_ret,
+                             int64_t n_ret_rows, uint16_t *d_recv,
+                             uint16_t *dw_gate, uint16_t *dw_up,
+                             uint16_t *dw_down);
+void orc_pack_backward(const orc_dims *d, const uint16_t *d_pools,
+                       const int32_t *topk, const int32_t *slot,
+                       const uint16_t *x, const uint16_t *d_shared,
+                       const uint16_t *w_ld_t, const uint16_t *ws_gate,
+                       const uint16_t *ws_up, uint16_t *dz, uint16_t *dx,
+                       uint16_t *dw_lat_down, uint16_t *dws_gate,
+                       uint16_t *dws_up);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,220 @@
+"""Pins of the oracle's backward of the branch.
+
+The oracle's gradients (chain rule written out by hand, bf16 rounding points
+of its own) are checked against numbers that do not come from it:
+
+- the router's logit gradient against central finite differences of a numpy
+  softmax, and against torch autograd;
+- the whole branch -- 8 ranks, exact exchanges in both directions -- against
+  torch autograd (float64, no rounding) of a plain per-token forward that
+  uses the keep decisions of the brute-force definition: every input and
+  weight gradient, summed over shards where the weight is shared.
+
+The two sides differ only by the oracle's bf16 rounding points, so the
+comparison is per tensor within a few bf16 units; a dropped term, a wrong
+sign, a transposed weight or a swapped gate / up gradient is far outside.
+"""
+import numpy as np
+import pytest
+import torch
+
+from conftest import f64, u16
+from test_oracle_e2e import brute_force, simulate
+from synth import configs
+
+F = torch.nn.functional
+ERRS = []
+
+
+def _close(got, ref, what, rel=1.5e-2, mx=5e-2):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, what
+    scale = np.abs(ref).max()
+    assert scale > 0, what
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    ERRS.append((what, err))
+    assert err < rel, f"{what}: relative error {err:.3g}"
+    assert np.abs(got - ref).max() <= mx * scale, f"{what}: max error"
+
+
+def _bf(v):
+    return f64(u16(torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16)))
+
+
+# ----------------------------------------------------------------------------
+# router
+# ----------------------------------------------------------------------------
+
+def _gates_np(l, topk, renorm):
+    l = l - l.max(axis=1, keepdims=True)
+    if renorm:
+        sel = np.take_along_axis(l, topk, 1)
+        return np.exp(sel) / np.exp(sel).sum(1, keepdims=True)
+    p = np.exp(l) / np.exp(l).sum(1, keepdims=True)
+    return np.take_along_axis(p, topk, 1)
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+@pytest.mark.parametrize("biased", [False, True])
+def test_route_backward_finite_differences(orc, renorm, biased):
+    rng = np.random.default_rng(40 + renorm + 2 * biased)
+    T, E, k = 5, 12, 4
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    bias = rng.standard_normal(E).astype(np.float32) if biased else None
+    topk, _ = orc.route_ex(lg, k, bias=bias, renorm=renorm)
+    dg = rng.standard_normal((T, k)).astype(np.float32)
+    got = orc.route_backward(lg, topk, dg, bias=bias, renorm=renorm)
+    lb = (lg + bias if biased else lg).astype(np.float32).astype(np.float64)
+    ref = np.zeros((T, E))
+    h = 1e-6
+    for t in range(T):
+        for e in range(E):
+            a, b = lb.copy(), lb.copy()
+            a[t, e] += h
+            b[t, e] -= h
+            ref[t, e] = ((_gates_np(a, topk, renorm) - _gates_np(b, topk, renorm)) * dg).sum() / (2 * h)
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-7)
+    # torch autograd on the same definition
+    lt = torch.tensor(lb, requires_grad=True)
+    idx = torch.from_numpy(topk.astype(np.int64))
+    g = (torch.softmax(lt.gather(1, idx), 1) if renorm else
+         torch.softmax(lt, 1).gather(1, idx))
+    (g * torch.from_numpy(dg.astype(np.float64))).sum().backward()
+    np.testing.assert_allclose(got, lt.grad.numpy(), rtol=1e-5, atol=1e-7)
+    if renorm:   # only the chosen logits move the renormalised gates
+        mask = np.zeros((T, E), bool)
+        np.put_along_axis(mask, topk, True, 1)
+        assert (got[~mask] == 0).all()
+    else:        # softmax is shift invariant: each row of the gradient sums to 0
+        np.testing.assert_allclose(got.sum(1), 0, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------
+# whole branch, 8 ranks
+# ----------------------------------------------------------------------------
+
+def oracle_backward(orc, cfg, d, W_, S, BK, OUT, d_out):
+    """Backward of every shard and rank with exact exchanges, from the oracle."""
+    R, W, Cs = cfg.n_ranks, cfg.n_waves, d.cap_send
+    CB = []
+    for s in range(R):
+        CB.append(orc.combine_backward(d, S[s]["returned"], S[s]["topk"], S[s]["slot"],
+                                       S[s]["gates"], W_["x"][s], OUT[s][0], W_["wlu"],
+                                       W_["wsg"], W_["wsu"], W_["wsd"], d_out[s]))
+    # return exchange, reversed: rank r's rows (s, w, i) are shard s's rows (r, w, i)
+    EB = []
+    for r in range(R):
+        d_ret = np.concatenate([CB[s][0][(r * W + w) * Cs:(r * W + w + 1) * Cs]
+                                for s in range(R) for w in range(W)])
+        EB.append(orc.expert_ffn_backward(d, BK[r]["bank"], BK[r]["bank_src"], BK[r]["bfill"],
+                                          *W_["ex"][r], d_ret))
+    PB, DL = [], []
+    for s in range(R):
+        d_pools = np.concatenate([EB[r][0][(s * W + w) * Cs:(s * W + w + 1) * Cs]
+                                  for r in range(R) for w in range(W)])
+        PB.append(orc.pack_backward(d, d_pools, S[s]["topk"], S[s]["slot"], W_["x"][s],
+                                    CB[s][2], W_["wld"], W_["wsg"], W_["wsu"]))
+        DL.append(orc.route_backward(W_["logits"][s], S[s]["topk"], CB[s][1]))
+    return CB, EB, PB, DL
+
+
+def torch_backward(cfg, W_, S, keep, d_out):
+    """float64 autograd of the per-token forward with the given keep mask."""
+    R, El = cfg.n_ranks, cfg.experts_per_rank
+    leaf = lambda a: torch.tensor(f64(a), requires_grad=True)
+    X = [leaf(x) for x in W_["x"]]
+    LG = [torch.tensor(np.asarray(l, np.float64), requires_grad=True) for l in W_["logits"]]
+    wld, wlu = leaf(W_["wld"]), leaf(W_["wlu"])
+    wsg, wsu, wsd = leaf(W_["wsg"]), leaf(W_["wsu"]), leaf(W_["wsd"])
+    ex = [[leaf(w) for w in W_["ex"][r]] for r in range(R)]
+    loss = 0
+    for s in range(R):
+        x = X[s]
+        z = x @ wld.T
+        topk = torch.from_numpy(S[s]["topk"].astype(np.int64))
+        g = torch.softmax(LG[s], 1).gather(1, topk)
+        kp = torch.from_numpy(keep[s])
+        ylat = torch.zeros(cfg.T, cfg.latent, dtype=torch.float64)
+        for e in range(cfg.n_experts):
+            t, j = torch.nonzero((topk == e) & kp, as_tuple=True)
+            if len(t) == 0:
+                continue
+            wg, wu, wd = (w[e % El] for w in ex[e // El])
+            u = z[t]
+            y = (F.silu(u @ wg.T) * (u @ wu.T)) @ wd.T
+            ylat = ylat.index_add(0, t, g[t, j][:, None] * y)
+        out = ylat @ wlu.T
+        for sh in range(cfg.n_shared):
+            out = out + (F.silu(x @ wsg[sh].T) * (x @ wsu[sh].T)) @ wsd[sh].T
+        loss = loss + (out * torch.from_numpy(f64(d_out[s]))).sum()
+    loss.backward()
+    return X, LG, wld, wlu, wsg, wsu, wsd, ex
+
+
+@pytest.mark.parametrize("case", ["1.10/1.15", "tight", "chunks"])
+def test_branch_backward_matches_autograd(orc, case):
+    from dataclasses import replace
+    from fractions import Fraction
+    cfg = configs.TINY
+    if case == "tight":
+        cfg = replace(cfg, cf_send=Fraction(1, 2), cf_recv=Fraction(1, 2))
+    elif case == "chunks":
+        cfg = replace(cfg, waves="chunks")
+    d, W_, S, BK, OUT = simulate(orc, cfg)
+    keep = [k for _, _, k in brute_force(cfg, d, W_, S)]
+    rng = np.random.default_rng(50)
+    d_out = [u16(torch.from_numpy(rng.standard_normal((cfg.T, cfg.d_model)).astype(np.float32))
+                 .to(torch.bfloat16)) for _ in range(cfg.n_ranks)]
+    CB, EB, PB, DL = oracle_backward(orc, cfg, d, W_, S, BK, OUT, d_out)
+    X, LG, wld, wlu, wsg, wsu, wsd, ex = torch_backward(cfg, W_, S, keep, d_out)
+    for s in range(cfg.n_ranks):
+        _close(f64(PB[s][1]), X[s].grad.numpy(), f"dx shard {s}")
+        _close(DL[s], LG[s].grad.numpy(), f"d_logits shard {s}")
+    R = cfg.n_ranks
+    _close(sum(f64(PB[s][2]) for s in range(R)), wld.grad.numpy(), "dw_lat_down")
+    _close(sum(f64(CB[s][3]) for s in range(R)), wlu.grad.numpy(), "dw_lat_up")
+    _close(sum(f64(PB[s][3]) for s in range(R)), wsg.grad.numpy(), "dws_gate")
+    _close(sum(f64(PB[s][4]) for s in range(R)), wsu.grad.numpy(), "dws_up")
+    _close(sum(f64(CB[s][4]) for s in range(R)), wsd.grad.numpy(), "dws_down")
+    for r in range(R):
+        for i, name in ((1, "dw_gate"), (2, "dw_up"), (3, "dw_down")):
+            ref = ex[r][i - 1].grad.numpy()
+            got = f64(EB[r][i])
+            for j in range(cfg.experts_per_rank):
+                if np.abs(ref[j]).max() == 0:      # an expert no kept row reached
+                    assert (got[j] == 0).all()
+                else:
+                    _close(got[j], ref[j], f"{name} rank {r} expert {j}")
+
+
+def test_backward_structure(orc):
+    """Zero rows and zero gates exactly where nothing was kept."""
+    from dataclasses import replace
+    from fractions import Fraction
+    cfg = replace(configs.TINY, cf_send=Fraction(1, 2), cf_recv=Fraction(1, 2))
+    d, W_, S, BK, OUT = simulate(orc, cfg)
+    rng = np.random.default_rng(51)
+    d_out = [u16(torch.from_numpy(rng.standard_normal((cfg.T, cfg.d_model)).astype(np.float32))
+                 .to(torch.bfloat16)) for _ in range(cfg.n_ranks)]
+    CB, EB, PB, DL = oracle_backward(orc, cfg, d, W_, S, BK, OUT, d_out)
+    Cs, W = d.cap_send, cfg.n_waves
+    for s in range(cfg.n_ranks):
+        d_ret, d_g = CB[s][0], CB[s][1]
+        assert (d_g[S[s]["slot"] < 0] == 0).all()
+        for p, f in enumerate(S[s]["fill"]):
+            assert (d_ret[p * Cs + f:(p + 1) * Cs] == 0).all()
+            assert (np.abs(f64(d_ret[p * Cs:p * Cs + f])).sum(1) > 0).all()
+    for r in range(cfg.n_ranks):
+        kept = np.zeros(len(EB[r][0]), bool)
+        kept[BK[r]["bank_src"][BK[r]["bank_src"] >= 0]] = True
+        assert (EB[r][0][~kept] == 0).all()
+    # d_returned of kept rows is exactly bf16(g * d_ylat): rows of one token are parallel
+    s = 0
+    t = int(np.nonzero((S[s]["slot"] >= 0).sum(1) >= 2)[0][0])
+    js = np.nonzero(S[s]["slot"][t] >= 0)[0][:2]
+    vecs = []
+    for j in js:
+        e, sl = int(S[s]["topk"][t, j]), int(S[s]["slot"][t, j])
+        row = ((e // cfg.experts_per_rank) * W + t // int(np.ceil(cfg.T / W))) * Cs + sl
+        vecs.append(f64(CB[s][0][row]) / float(S[s]["gates"][t, j]))
+    np.testing.assert_allclose(vecs[0], vecs[1], rtol=1e-2, atol=1e-6 * np.abs(vecs[0]).max())

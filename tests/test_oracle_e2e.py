@@ -82,7 +82,7 @@ def simulate(orc, cfg):
         bank = orc.bank_rows(d, recv, bs["bank_offsets"], bs["bank_src"], bs["bfill"])
         ret = orc.expert_ffn(d, bank, bs["bank_offsets"], bs["bank_src"], bs["bfill"],
                              *ex[r], len(recv))
-        RET.append(ret); RO.append(ro); BK.append(bs)
+        RET.append(ret); RO.append(ro); BK.append(dict(bs, bank=bank))
 
     # exact return and combine
     OUT = []
@@ -98,8 +98,9 @@ def simulate(orc, cfg):
         returned = np.concatenate(parts)
         ylat, out = orc.combine(d, returned, S[s]["pool_offsets"], S[s]["topk"],
                                 S[s]["slot"], S[s]["gates"], x[s], wlu, wsg, wsu, wsd)
+        S[s]["returned"] = returned
         OUT.append((ylat, out))
-    return d, dict(x=x, wld=wld, wlu=wlu, wsg=wsg, wsu=wsu, wsd=wsd, ex=ex), S, BK, OUT
+    return d, dict(x=x, wld=wld, wlu=wlu, wsg=wsg, wsu=wsu, wsd=wsd, ex=ex, logits=lgs), S, BK, OUT
 
 
 def brute_force(cfg, d, W_, S):

@@ -9,6 +9,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
+# the backward slips: one whole-branch autograd comparison catches each
+BWD = "test_oracle_backward.py::test_branch_backward_matches_autograd"
+
 MUTATIONS = [
     ("tie-break", "if (best < 0 || l[e] > l[best]) best = e;",
      "if (best < 0 || l[e] >= l[best]) best = e;", "test_oracle_pins.py"),
@@ -66,6 +69,25 @@ MUTATIONS = [
     ("chunk combine row",
      "        row = (int64_t)dest_of(d, e) * W * d->cap_send + s; /* slot: position in the dest's pool */",
      "        row = (int64_t)seg * d->cap_send + s % d->cap_send;", "test_oracle_e2e.py"),
+    ("silu derivative", "  return s * (1.0 + a * (1.0 - s));", "  return s;", BWD),
+    ("shared d_b from b", "d_shared[(t * 2 * S + S + sh) * Fs + f] = to_bf(dh * silu(a));",
+     "d_shared[(t * 2 * S + S + sh) * Fs + f] = to_bf(dh * b);", BWD),
+    ("gate gradient sign", "      d_gates[t * k + j] = (float)dot;", "      d_gates[t * k + j] = (float)-dot;",
+     BWD),
+    ("expert d_u gate/up weights swapped",
+     "acc += da[f] * bf(Wg[(int64_t)f * L + l]) + db[f] * bf(Wu[(int64_t)f * L + l]);",
+     "acc += da[f] * bf(Wu[(int64_t)f * L + l]) + db[f] * bf(Wg[(int64_t)f * L + l]);",
+     BWD),
+    ("softmax normaliser term dropped", "      for (int32_t e = 0; e < E; ++e) dl[e] = -p[e] * s;",
+     "      for (int32_t e = 0; e < E; ++e) dl[e] = 0.0;",
+     "test_oracle_backward.py::test_route_backward_finite_differences"),
+    ("return gradient not gated", "        d_returned[row * L + i] = to_bf(g * dyl[i]);",
+     "        d_returned[row * L + i] = to_bf(dyl[i]);", BWD),
+    ("dx without shared up path",
+     "               bf(d_shared[(t * 2 * S + S + sh) * Fs + f]) * bf(ws_up[wi]);",
+     "               0.0 * bf(ws_up[wi]);", BWD),
+    ("expert down grad with u for h", "gd[j * WL + (int64_t)l * F + f] += dy[l] * h[f];",
+     "gd[j * WL + (int64_t)l * F + f] += dy[l] * u[f % L];", BWD),
 ]
 
 
