@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 (MOE_CALL_ROUTE, MOE_CALL_PACK, MOE_CALL_BANK, MOE_CALL_FFN, MOE_CALL_COMBINE,
- MOE_CALL_COMBINE_SHARED) = range(6)
+ MOE_CALL_COMBINE_SHARED, MOE_CALL_COMBINE_BWD, MOE_CALL_FFN_BWD, MOE_CALL_PACK_BWD) = range(9)
 
 
 class MoeError(RuntimeError):
@@ -60,6 +60,10 @@ _SIGS = {
     "moe_shared_swiglu": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP]),
     "moe_combine_shared": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                           _VP, _I64, _VP]),
+    "moe_route_backward": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
+    "moe_combine_backward": (ctypes.c_int, [_DP] + [_VP] * 18 + [_I64, _VP]),
+    "moe_expert_ffn_backward": (ctypes.c_int, [_DP] + [_VP] * 12 + [_I64, _VP]),
+    "moe_pack_backward": (ctypes.c_int, [_DP] + [_VP] * 14 + [_I64, _VP]),
     "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_profile_collect": (ctypes.c_int, []),
     "moe_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.c_char_p, ctypes.c_int,
@@ -195,6 +199,42 @@ def moe_combine_shared(d, returned, ret_offsets, topk, slot, gates, w_lat_up, h_
                                     _p(slot), _p(gates), _p(w_lat_up), _p(h_shared),
                                     _p(ws_down), _p(ylat), _p(out), _p(ws), nbytes,
                                     _stream(stream)))
+
+
+def moe_route_backward(logits, topk, d_gates, d_logits, bias=None, stream=None, flags=0):
+    T, E = logits.shape
+    k = topk.shape[1]
+    _check(lib().moe_route_backward(_p(logits), _p(bias), T, E, k, flags, _p(topk), _p(d_gates),
+                                    _p(d_logits), _stream(stream)))
+
+
+def moe_combine_backward(d, returned, topk, slot, gates, fill, x, ylat, w_lat_up, ws_gate, ws_up,
+                         ws_down, d_out, d_returned, d_gates, d_shared, dw_lat_up, dws_down, ws,
+                         stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().moe_combine_backward(
+        ctypes.byref(d), _p(returned), _p(topk), _p(slot), _p(gates), _p(fill), _p(x), _p(ylat),
+        _p(w_lat_up), _p(ws_gate), _p(ws_up), _p(ws_down), _p(d_out), _p(d_returned),
+        _p(d_gates), _p(d_shared), _p(dw_lat_up), _p(dws_down), _p(ws), nbytes,
+        _stream(stream)))
+
+
+def moe_expert_ffn_backward(d, bank, bank_src, bfill, w_gate, w_up, w_down, d_ret, d_recv,
+                            dw_gate, dw_up, dw_down, ws, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().moe_expert_ffn_backward(
+        ctypes.byref(d), _p(bank), _p(bank_src), _p(bfill), _p(w_gate), _p(w_up), _p(w_down),
+        _p(d_ret), _p(d_recv), _p(dw_gate), _p(dw_up), _p(dw_down), _p(ws), nbytes,
+        _stream(stream)))
+
+
+def moe_pack_backward(d, d_pools, topk, slot, x, d_shared, w_lat_down, ws_gate, ws_up, dz, dx,
+                      dw_lat_down, dws_gate, dws_up, ws, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().moe_pack_backward(
+        ctypes.byref(d), _p(d_pools), _p(topk), _p(slot), _p(x), _p(d_shared), _p(w_lat_down),
+        _p(ws_gate), _p(ws_up), _p(dz), _p(dx), _p(dw_lat_down), _p(dws_gate), _p(dws_up),
+        _p(ws), nbytes, _stream(stream)))
 
 
 def moe_profile_enable(on: bool):

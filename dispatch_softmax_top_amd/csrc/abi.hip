@@ -168,6 +168,11 @@ int64_t moe_workspace_bytes(const moe_dims *d, int call, int64_t n_rows) {
       return shared_h_bytes(*d) + gemm_split_bytes();
     case MOE_CALL_COMBINE_SHARED:  // split partial tiles
       return gemm_split_bytes();
+    case MOE_CALL_COMBINE_BWD:
+    case MOE_CALL_FFN_BWD:
+    case MOE_CALL_PACK_BWD:  // transposed operands, intermediates, split partial tiles
+      if (ragged(*d)) return fail(MOE_ERR_UNSUPPORTED, "moe_workspace_bytes: backward needs fixed capacities");
+      return bwd_ws_bytes(*d, call);
     default:
       return fail(MOE_ERR_INVALID, "moe_workspace_bytes: unknown call %d", call);
   }

@@ -1,0 +1,510 @@
+// backward.hip -- gradients of the branch (fixed capacities), for training:
+// "Marin 開始公開訓練 535B 參數 MoE 模型" (lamjinlab.com, zh-HK) describes a
+// model in open training; its pages give the forward pass, and every
+// gradient here follows from the forward definitions by the chain rule.
+//
+// Rounding points: gradients are stored like the values they belong to
+// (bf16 activations and weights, fp32 gates and logits); a, b = u.W_g,
+// u.W_u are recomputed from the forward inputs by the forward's own GEMMs.
+//
+// Every contraction runs on the forward's bf16 MFMA engine, which takes both
+// operands K-contiguous (C = A . B^T).  Weight gradients (a sum over tokens
+// or bank rows) and input gradients through a weight stored output-major need
+// the other operand orders; they get them from 64x64 LDS-tiled transposes
+// into the workspace (HBM-bound copies).
+//
+// Calls and kernels, in stream order:
+//   moe_combine_backward  transposes of W_lu, W_sd; [d_ylat | d_h_s] =
+//                         d_out . [W_lu ; W_sd]; shared experts recomputed
+//                         with the SwiGLU gradient epilogue (d_shared, h_s);
+//                         combine_backward (d_returned, d_gates, zero rows);
+//                         transposes of d_out, ylat, h_s; dW_lu, dW_sd
+//   moe_expert_ffn_backward  transposes of W_d, [W_g | W_u]; gather of the
+//                         return gradients into bank order; d_h (grouped);
+//                         experts recomputed with the gradient epilogue
+//                         (d_a | d_b, h); d_u scattered to receive rows
+//                         (grouped); bank-order transposes; dW_d, dW_g, dW_u
+//                         (batched over the local experts)
+//   moe_pack_backward     dz (gather-sum of the pool-row gradients);
+//                         transposes of W_ld, W_sg, W_su; dx = [dz | d_shared]
+//                         . [W_ld ; W_sg ; W_su]; transposes of x, dz,
+//                         d_shared; dW_ld, dW_sg, dW_su
+#include <algorithm>
+#include <type_traits>
+
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// transpose: out[b][c][k] = in(b, row(b, k))[c] for c < cols, k < kpad, and 0
+// where row(b, k) does not exist.  Plain: row = k for k < rows.  Bank order
+// (bfill != NULL): k = w * cap + p is bank slot (wave w, local expert b,
+// position p), present when p < bfill[w * El + b].
+// ---------------------------------------------------------------------------
+
+struct TransposeArgs {
+  const uint16_t *in;
+  int64_t ld_in, bs_in;
+  uint16_t *out;
+  int64_t ld_out, bs_out;
+  int rows, cols, kpad;
+  const int32_t *bfill;
+  int cap, El;
+};
+
+constexpr int TP = 64;  // tile edge
+
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
+  __shared__ uint16_t tile[TP][TP + 8];  // [k][c]; 144-byte rows keep 16-byte alignment
+  const int k0 = blockIdx.x * TP, c0 = blockIdx.y * TP, b = blockIdx.z;
+  const uint16_t *in = a.in + b * a.bs_in;
+  for (int q = threadIdx.x; q < TP * TP / 8; q += 256) {
+    const int kk = q >> 3, ch = q & 7;
+    const int k = k0 + kk, c = c0 + ch * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k < a.kpad && c < a.cols && k < a.rows) {
+      int64_t row = k;
+      if (a.bfill) {
+        const int w = k / a.cap, p = k - w * a.cap, g = w * a.El + b;
+        row = p < a.bfill[g] ? (int64_t)g * a.cap + p : -1;
+      }
+      if (row >= 0) v = *reinterpret_cast<const u32x4 *>(in + row * a.ld_in + c);
+    }
+    *reinterpret_cast<u32x4 *>(&tile[kk][ch * 8]) = v;
+  }
+  __syncthreads();
+  uint16_t *out = a.out + b * a.bs_out;
+  for (int q = threadIdx.x; q < TP * TP / 8; q += 256) {
+    const int cc = q >> 3, ch = q & 7;
+    const int c = c0 + cc, k = k0 + ch * 8;
+    if (c >= a.cols || k >= a.kpad) continue;
+    u32x4 v;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      v[h] = (uint32_t)tile[ch * 8 + 2 * h][cc] | ((uint32_t)tile[ch * 8 + 2 * h + 1][cc] << 16);
+    *reinterpret_cast<u32x4 *>(out + (int64_t)c * a.ld_out + k) = v;
+  }
+}
+
+// Host side: every size and stride a multiple of 8 elements, pointers 16-byte
+// aligned (the callers' buffers and workspace offsets are).
+static int transpose(const char *name, const uint16_t *in, int64_t ld_in, int64_t bs_in,
+                     uint16_t *out, int64_t ld_out, int64_t bs_out, int rows, int cols, int kpad,
+                     int nbatch, hipStream_t s, const int32_t *bfill = nullptr, int cap = 0,
+                     int El = 0) {
+  if (cols % 8 || kpad % 8 || ld_in % 8 || ld_out % 8 || bs_in % 8 || bs_out % 8)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: sizes must be multiples of 8", name);
+  TransposeArgs a{in, ld_in, bs_in, out, ld_out, bs_out, rows, cols, kpad, bfill, cap, El};
+  return launch(name, transpose_kernel,
+                dim3((unsigned)cdiv(kpad, TP), (unsigned)cdiv(cols, TP), (unsigned)nbatch),
+                dim3(256), 0, s, a);
+}
+
+// ---------------------------------------------------------------------------
+// combine side: one wave per token.  For each kept choice j (pool row r):
+//   d_returned[r] = bf16(g[t,j] * d_ylat[t]),  d_gates[t,j] = returned[r] . d_ylat[t]
+// (fp32, lane partial sums then a wave sum); dropped choices get d_gates 0.
+// Extra blocks: one wave per pool row, zeroing rows past their pool's fill.
+// ---------------------------------------------------------------------------
+
+template <int CH>
+__global__ __launch_bounds__(256) void combine_backward_kernel(
+    const uint16_t *__restrict__ returned, const uint16_t *__restrict__ dy, int64_t ld_dy,
+    const int32_t *__restrict__ topk, const int32_t *__restrict__ slot,
+    const float *__restrict__ gates, const int32_t *__restrict__ fill,
+    uint16_t *__restrict__ d_returned, float *__restrict__ d_gates, int T, int k, int L, int El,
+    int Wk, int Tw, int pool_rows, int cap, int token_blocks, int64_t n_slots) {
+  const int lane = lane_id();
+  const int nch = L / 8;
+  if ((int)blockIdx.x >= token_blocks) {
+    const int64_t idx = (int64_t)(blockIdx.x - token_blocks) * 4 + (threadIdx.x >> 6);
+    if (idx >= n_slots) return;
+    const int p = (int)(idx / cap), i = (int)(idx - (int64_t)p * cap);
+    if (i < fill[p]) return;
+    u32x4 *o = reinterpret_cast<u32x4 *>(d_returned + idx * L);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int c = lane; c < nch; c += 64) o[c] = zero;
+    return;
+  }
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int64_t my_row = -1;
+  float my_g = 0.f;
+  if (lane < k) {
+    const int s = slot[(int64_t)t * k + lane];
+    const int e = topk[(int64_t)t * k + lane];
+    const float g = gates[(int64_t)t * k + lane];
+    if (s >= 0) {
+      my_row = (int64_t)((e / El) * Wk + t / Tw) * pool_rows + s;
+      my_g = g;
+    }
+  }
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(dy + (int64_t)t * ld_dy);
+  u32x4 v[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) v[c] = src[min(lane + 64 * c, nch - 1)];
+  float my_dg = 0.f;
+  const u32x4 *ret16 = reinterpret_cast<const u32x4 *>(returned);
+  u32x4 *dret16 = reinterpret_cast<u32x4 *>(d_returned);
+  uint64_t valid = ballot(my_row >= 0);
+  while (valid) {
+    const int j = (int)__builtin_ctzll(valid);
+    valid &= valid - 1;
+    const int64_t row = ((int64_t)__shfl((int)(my_row >> 32), j) << 32) |
+                        (uint32_t)__shfl((int)my_row, j);
+    const float g = __shfl(my_g, j);
+    u32x4 r[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) r[c] = ld16<true>(ret16 + row * nch + min(lane + 64 * c, nch - 1));
+    float dot = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (lane + 64 * c >= nch) continue;
+      u32x4 o;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float y0 = __uint_as_float(v[c][h] << 16), y1 = __uint_as_float(v[c][h] & 0xffff0000u);
+        dot = fmaf(__uint_as_float(r[c][h] << 16), y0, dot);
+        dot = fmaf(__uint_as_float(r[c][h] & 0xffff0000u), y1, dot);
+        o[h] = pack_bf16x2(g * y0, g * y1);
+      }
+      dret16[row * nch + lane + 64 * c] = o;
+    }
+    dot = wave_sum_f32(dot);
+    if (lane == j) my_dg = dot;
+  }
+  if (lane < k) d_gates[(int64_t)t * k + lane] = my_dg;
+}
+
+// ---------------------------------------------------------------------------
+// bank order: out[r] = in[src[r]] (latent-wide rows) for every bank row with
+// src[r] >= 0; other rows are left as they are (nothing reads them).  One wave
+// per row, the whole row in flight.
+// ---------------------------------------------------------------------------
+
+template <int CH>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__restrict__ in,
+                                                          int64_t n_in,
+                                                          const int32_t *__restrict__ src,
+                                                          int64_t n, uint16_t *__restrict__ out,
+                                                          int L) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  const int sr = src[r];
+  if (sr < 0 || sr >= n_in) return;
+  const int lane = lane_id(), nch = L / 8;
+  const u32x4 *a = reinterpret_cast<const u32x4 *>(in + (int64_t)sr * L);
+  u32x4 v[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) v[c] = ld16<true>(a + min(lane + 64 * c, nch - 1));
+  u32x4 *o = reinterpret_cast<u32x4 *>(out + r * L);
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+    if (lane + 64 * c < nch) o[lane + 64 * c] = v[c];
+}
+
+__global__ __launch_bounds__(256) void iota_kernel(int32_t *o, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) o[i] = (int32_t)i;
+}
+
+// Dispatch on the 16-byte chunks per lane a latent row needs (latent <= 8192).
+template <class F>
+static int by_chunks(int L, F f) {
+  const int ch = (int)cdiv(L / 8, 64);
+  if (ch <= 1) return f(std::integral_constant<int, 1>());
+  if (ch <= 2) return f(std::integral_constant<int, 2>());
+  if (ch <= 4) return f(std::integral_constant<int, 4>());
+  if (ch <= 6) return f(std::integral_constant<int, 6>());
+  if (ch <= 8) return f(std::integral_constant<int, 8>());
+  return f(std::integral_constant<int, 16>());
+}
+
+// ---------------------------------------------------------------------------
+// workspace layouts
+// ---------------------------------------------------------------------------
+
+// Buffers carved from ws in order, each 256-byte aligned.
+struct Carve {
+  char *base;
+  int64_t off = 0;
+  template <class T>
+  T *take(int64_t elems) {
+    T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+    off += align_up(elems * (int64_t)sizeof(T), 256);
+    return p;
+  }
+};
+
+inline int64_t pad32(int64_t n) { return align_up(n, 32); }
+
+struct CombineBwdWs {
+  uint16_t *Bt, *C1, *Hs, *doT, *ylT, *HsT;
+  float *part;
+};
+static int64_t combine_bwd_ws(const moe_dims &d, char *base, CombineBwdWs &w) {
+  const int64_t T = d.T, L = d.latent, D = d.d_model, SF = (int64_t)d.n_shared * d.d_ff_shared,
+                Tp = pad32(T);
+  Carve c{base};
+  w.Bt = c.take<uint16_t>((L + SF) * D);
+  w.C1 = c.take<uint16_t>(T * (L + SF));
+  w.Hs = c.take<uint16_t>(T * SF);
+  w.doT = c.take<uint16_t>(D * Tp);
+  w.ylT = c.take<uint16_t>(L * Tp);
+  w.HsT = c.take<uint16_t>(SF * Tp);
+  w.part = c.take<float>(gemm_split_bytes() / 4);
+  return c.off;
+}
+
+struct FfnBwdWs {
+  uint16_t *WdT, *WguT, *dY, *dH, *Hb, *dAB, *dYT, *HT, *dABT, *UT;
+  int32_t *iota, *flags;
+  float *part;
+};
+static int64_t ffn_bwd_ws(const moe_dims &d, char *base, FfnBwdWs &w) {
+  const int64_t El = experts_per_rank(d), L = d.latent, F = d.d_ff;
+  const int64_t nb = (int64_t)d.n_waves * El * d.cap_recv;
+  const int64_t nr = (int64_t)d.n_ranks * d.n_waves * d.cap_send;
+  const int64_t Kp = pad32((int64_t)d.n_waves * d.cap_recv);
+  Carve c{base};
+  w.WdT = c.take<uint16_t>(El * F * L);
+  w.WguT = c.take<uint16_t>(El * L * 2 * F);
+  w.dY = c.take<uint16_t>(nb * L);
+  w.dH = c.take<uint16_t>(nb * F);
+  w.Hb = c.take<uint16_t>(nb * F);
+  w.dAB = c.take<uint16_t>(nb * 2 * F);
+  w.dYT = c.take<uint16_t>(El * L * Kp);
+  w.HT = c.take<uint16_t>(El * F * Kp);
+  w.dABT = c.take<uint16_t>(El * 2 * F * Kp);
+  w.UT = c.take<uint16_t>(El * L * Kp);
+  w.iota = c.take<int32_t>(nb);
+  w.flags = c.take<int32_t>(nr);
+  w.part = c.take<float>(gemm_split_bytes() / 4);
+  return c.off;
+}
+
+struct PackBwdWs {
+  uint16_t *BldT, *BsT, *xT, *dzT, *dshT;
+  float *part;
+};
+static int64_t pack_bwd_ws(const moe_dims &d, char *base, PackBwdWs &w) {
+  const int64_t L = d.latent, D = d.d_model, SF = (int64_t)d.n_shared * d.d_ff_shared,
+                Tp = pad32(d.T);
+  Carve c{base};
+  w.BldT = c.take<uint16_t>(D * L);
+  w.BsT = c.take<uint16_t>(D * 2 * SF);
+  w.xT = c.take<uint16_t>(D * Tp);
+  w.dzT = c.take<uint16_t>(L * Tp);
+  w.dshT = c.take<uint16_t>(2 * SF * Tp);
+  w.part = c.take<float>(gemm_split_bytes() / 4);
+  return c.off;
+}
+
+int64_t bwd_ws_bytes(const moe_dims &d, int call) {
+  if (call == MOE_CALL_COMBINE_BWD) {
+    CombineBwdWs w;
+    return combine_bwd_ws(d, nullptr, w);
+  }
+  if (call == MOE_CALL_FFN_BWD) {
+    FfnBwdWs w;
+    return ffn_bwd_ws(d, nullptr, w);
+  }
+  PackBwdWs w;
+  return pack_bwd_ws(d, nullptr, w);
+}
+
+static int check_bwd(const moe_dims *d, int call, const char *name, const void *ws,
+                     int64_t ws_bytes) {
+  MOE_TRY(check_dims(d));
+  if (ragged(*d)) return fail(MOE_ERR_UNSUPPORTED, "%s: fixed capacities only", name);
+  MOE_TRY(check_ptr(ws, "ws"));
+  const int64_t need = bwd_ws_bytes(*d, call);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %lld < %lld bytes", name, (long long)ws_bytes,
+                (long long)need);
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
+                                    const int32_t *topk, const int32_t *slot, const float *gates,
+                                    const int32_t *fill, const moe_bf16 *x, const moe_bf16 *ylat,
+                                    const moe_bf16 *w_lat_up, const moe_bf16 *ws_gate,
+                                    const moe_bf16 *ws_up, const moe_bf16 *ws_down,
+                                    const moe_bf16 *d_out, moe_bf16 *d_returned, float *d_gates,
+                                    moe_bf16 *d_shared, moe_bf16 *dw_lat_up, moe_bf16 *dws_down,
+                                    void *ws, int64_t ws_bytes, void *stream) {
+  clear_error();
+  MOE_TRY(check_bwd(d, MOE_CALL_COMBINE_BWD, "moe_combine_backward", ws, ws_bytes));
+  const bool sh = d->n_shared > 0;
+  const void *need[] = {returned, topk, slot, gates, fill, x, ylat, w_lat_up, d_out, d_returned,
+                        d_gates, dw_lat_up};
+  const char *names[] = {"returned", "topk", "slot", "gates", "fill", "x", "ylat", "w_lat_up",
+                         "d_out", "d_returned", "d_gates", "dw_lat_up"};
+  for (int i = 0; i < 12; ++i) MOE_TRY(check_ptr(need[i], names[i]));
+  if (sh) {
+    MOE_TRY(check_ptr(ws_gate, "ws_gate"));
+    MOE_TRY(check_ptr(ws_up, "ws_up"));
+    MOE_TRY(check_ptr(ws_down, "ws_down"));
+    MOE_TRY(check_ptr(d_shared, "d_shared"));
+    MOE_TRY(check_ptr(dws_down, "dws_down"));
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const int T = d->T, L = d->latent, D = d->d_model, S = d->n_shared, Fs = d->d_ff_shared;
+  const int SF = S * Fs, Tp = (int)pad32(T);
+  CombineBwdWs w;
+  combine_bwd_ws(*d, (char *)ws, w);
+
+  // [d_ylat | d_h_s] = d_out . [W_lu^T ; W_sd,s^T]^T, one product
+  MOE_TRY(transpose("transpose_w_lat_up", w_lat_up, L, 0, w.Bt, D, 0, D, L, D, 1, s));
+  if (sh)
+    MOE_TRY(transpose("transpose_ws_down", ws_down, Fs, (int64_t)D * Fs, w.Bt + (int64_t)L * D, D,
+                      (int64_t)Fs * D, D, Fs, D, S, s));
+  DenseSeg g1{d_out, D, w.Bt, D, D};
+  MOE_TRY(gemm_nt("gemm_bwd_d_ylat", T, L + SF, 1, &g1, w.C1, L + SF, w.part, s));
+  // shared experts: recompute, SwiGLU gradient -> d_shared, h_s
+  if (sh)
+    MOE_TRY(gemm_shared_swiglu_bwd(T, x, D, D, ws_gate, ws_up, S, Fs, w.C1, L + SF, L, w.Hs,
+                                   d_shared, w.part, s));
+  // routed part: d_returned, d_gates
+  const PoolKey pk = pool_key(*d);
+  const int token_blocks = (int)cdiv(T, 4);
+  const int64_t n_slots = (int64_t)d->n_ranks * d->n_waves * d->cap_send;
+  MOE_TRY(by_chunks(L, [&](auto chv) {
+    constexpr int CH = decltype(chv)::value;
+    return launch("combine_backward", combine_backward_kernel<CH>,
+                  dim3((unsigned)(token_blocks + cdiv(n_slots, 4))), dim3(256), 0, s, returned,
+                  w.C1, (int64_t)(L + SF), topk, slot, gates, fill, d_returned, d_gates, T,
+                  d->top_k, L, experts_per_rank(*d), pk.Wk, pk.Tw, pk.rows, d->cap_send,
+                  token_blocks, n_slots);
+  }));
+  // weight gradients, summed over tokens
+  MOE_TRY(transpose("transpose_d_out", d_out, D, 0, w.doT, Tp, 0, T, D, Tp, 1, s));
+  MOE_TRY(transpose("transpose_ylat", ylat, L, 0, w.ylT, Tp, 0, T, L, Tp, 1, s));
+  DenseSeg g2{w.doT, Tp, w.ylT, Tp, Tp};
+  MOE_TRY(gemm_nt("gemm_bwd_dw_lat_up", D, L, 1, &g2, dw_lat_up, L, w.part, s));
+  if (!sh) return MOE_OK;
+  MOE_TRY(transpose("transpose_h_shared", w.Hs, SF, 0, w.HsT, Tp, 0, T, SF, Tp, 1, s));
+  DenseSeg g3{w.doT, Tp, w.HsT, Tp, Tp};
+  return gemm_nt_batched("gemm_bwd_dws_down", D, Fs, g3, S, 0, (int64_t)Fs * Tp, dws_down, Fs,
+                         (int64_t)D * Fs, w.part, s);
+}
+
+extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
+                                       const int32_t *bank_src, const int32_t *bfill,
+                                       const moe_bf16 *w_gate, const moe_bf16 *w_up,
+                                       const moe_bf16 *w_down, const moe_bf16 *d_ret,
+                                       moe_bf16 *d_recv, moe_bf16 *dw_gate, moe_bf16 *dw_up,
+                                       moe_bf16 *dw_down, void *ws, int64_t ws_bytes,
+                                       void *stream) {
+  clear_error();
+  MOE_TRY(check_bwd(d, MOE_CALL_FFN_BWD, "moe_expert_ffn_backward", ws, ws_bytes));
+  const void *need[] = {bank, bank_src, bfill, w_gate, w_up, w_down, d_ret, d_recv, dw_gate,
+                        dw_up, dw_down};
+  const char *names[] = {"bank", "bank_src", "bfill", "w_gate", "w_up", "w_down", "d_ret",
+                         "d_recv", "dw_gate", "dw_up", "dw_down"};
+  for (int i = 0; i < 11; ++i) MOE_TRY(check_ptr(need[i], names[i]));
+  hipStream_t s = (hipStream_t)stream;
+  const int El = experts_per_rank(*d), L = d->latent, F = d->d_ff, Cr = d->cap_recv;
+  const int64_t nb = (int64_t)d->n_waves * El * Cr;
+  const int64_t nr = (int64_t)d->n_ranks * d->n_waves * d->cap_send;
+  const int Kp = (int)pad32((int64_t)d->n_waves * Cr);
+  if (nb >= (1ll << 31) || nr >= (1ll << 31) || (int64_t)d->n_waves * Cr >= (1ll << 30))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn_backward: bank or receive rows >= 2^31");
+  FfnBwdWs w;
+  ffn_bwd_ws(*d, (char *)ws, w);
+  const int64_t WL = (int64_t)F * L;
+
+  // operands with K contiguous: W_d^T [El][F][L], [W_g^T | W_u^T] [El][L][2F]
+  MOE_TRY(transpose("transpose_w_down", w_down, F, WL, w.WdT, L, WL, L, F, L, El, s));
+  MOE_TRY(transpose("transpose_w_gate", w_gate, L, WL, w.WguT, 2 * F, 2 * WL, F, L, F, El, s));
+  MOE_TRY(transpose("transpose_w_up", w_up, L, WL, w.WguT + F, 2 * F, 2 * WL, F, L, F, El, s));
+  // dy in bank order
+  MOE_TRY(by_chunks(L, [&](auto chv) {
+    constexpr int CH = decltype(chv)::value;
+    return launch("gather_bank_grad", gather_rows_kernel<CH>, dim3((unsigned)cdiv(nb, 4)),
+                  dim3(256), 0, s, d_ret, nr, bank_src, nb, w.dY, L);
+  }));
+  MOE_TRY(launch("iota", iota_kernel, dim3((unsigned)cdiv(nb, 256)), dim3(256), 0, s, w.iota, nb));
+  // d_h = dy . W_d (grouped, bank order)
+  MOE_TRY(gemm_grouped_nt("gemm_bwd_d_h", *d, w.dY, L, bfill, w.iota, nb, w.WdT, F, w.dH, nb,
+                          w.part, s));
+  // a, b recomputed; d_a | d_b and h
+  MOE_TRY(gemm_expert_swiglu_bwd(*d, bank, bfill, nb, w_gate, w_up, w.dH, w.Hb, w.dAB, w.part, s));
+  // d_u = d_a . W_g + d_b . W_u, scattered to the receive rows; others zero
+  MOE_TRY(ret_rows_mark(bank_src, nb, w.flags, nr, s));
+  MOE_TRY(gemm_grouped_nt("gemm_bwd_d_u", *d, w.dAB, 2 * F, bfill, bank_src, nb, w.WguT, L, d_recv,
+                          nr, w.part, s));
+  MOE_TRY(ret_rows_zero_unmarked(w.flags, d_recv, L, nr, s));
+  // weight gradients: per local expert, summed over its rows of every wave
+  const int nw = d->n_waves * Cr;
+  MOE_TRY(transpose("transpose_bank_dy", w.dY, L, 0, w.dYT, Kp, (int64_t)L * Kp, nw, L, Kp, El, s,
+                    bfill, Cr, El));
+  MOE_TRY(transpose("transpose_bank_h", w.Hb, F, 0, w.HT, Kp, (int64_t)F * Kp, nw, F, Kp, El, s,
+                    bfill, Cr, El));
+  MOE_TRY(transpose("transpose_bank_dab", w.dAB, 2 * F, 0, w.dABT, Kp, (int64_t)2 * F * Kp, nw,
+                    2 * F, Kp, El, s, bfill, Cr, El));
+  MOE_TRY(transpose("transpose_bank_u", bank, L, 0, w.UT, Kp, (int64_t)L * Kp, nw, L, Kp, El, s,
+                    bfill, Cr, El));
+  DenseSeg gd{w.dYT, Kp, w.HT, Kp, Kp};
+  MOE_TRY(gemm_nt_batched("gemm_bwd_dw_down", L, F, gd, El, (int64_t)L * Kp, (int64_t)F * Kp,
+                          dw_down, F, WL, w.part, s));
+  DenseSeg gg{w.dABT, Kp, w.UT, Kp, Kp};
+  MOE_TRY(gemm_nt_batched("gemm_bwd_dw_gate", F, L, gg, El, (int64_t)2 * F * Kp, (int64_t)L * Kp,
+                          dw_gate, L, WL, w.part, s));
+  DenseSeg gu{w.dABT + (int64_t)F * Kp, Kp, w.UT, Kp, Kp};
+  return gemm_nt_batched("gemm_bwd_dw_up", F, L, gu, El, (int64_t)2 * F * Kp, (int64_t)L * Kp,
+                         dw_up, L, WL, w.part, s);
+}
+
+extern "C" int moe_pack_backward(const moe_dims *d, const moe_bf16 *d_pools, const int32_t *topk,
+                                 const int32_t *slot, const moe_bf16 *x,
+                                 const moe_bf16 *d_shared, const moe_bf16 *w_lat_down,
+                                 const moe_bf16 *ws_gate, const moe_bf16 *ws_up, moe_bf16 *dz,
+                                 moe_bf16 *dx, moe_bf16 *dw_lat_down, moe_bf16 *dws_gate,
+                                 moe_bf16 *dws_up, void *ws, int64_t ws_bytes, void *stream) {
+  clear_error();
+  MOE_TRY(check_bwd(d, MOE_CALL_PACK_BWD, "moe_pack_backward", ws, ws_bytes));
+  const bool sh = d->n_shared > 0;
+  const void *need[] = {d_pools, topk, slot, x, w_lat_down, dz, dx, dw_lat_down};
+  const char *names[] = {"d_pools", "topk", "slot", "x", "w_lat_down", "dz", "dx", "dw_lat_down"};
+  for (int i = 0; i < 8; ++i) MOE_TRY(check_ptr(need[i], names[i]));
+  if (sh) {
+    MOE_TRY(check_ptr(d_shared, "d_shared"));
+    MOE_TRY(check_ptr(ws_gate, "ws_gate"));
+    MOE_TRY(check_ptr(ws_up, "ws_up"));
+    MOE_TRY(check_ptr(dws_gate, "dws_gate"));
+    MOE_TRY(check_ptr(dws_up, "dws_up"));
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const int T = d->T, L = d->latent, D = d->d_model, SF = d->n_shared * d->d_ff_shared;
+  const int Tp = (int)pad32(T);
+  PackBwdWs w;
+  pack_bwd_ws(*d, (char *)ws, w);
+
+  // dz[t] = sum over kept choices of the pool-row gradients (the pack copy's adjoint)
+  MOE_TRY(combine_gather_rows(*d, d_pools, nullptr, topk, slot, nullptr, dz, s));
+  // dx = dz . W_ld + d_a . W_sg + d_b . W_su, one product with one rounding
+  MOE_TRY(transpose("transpose_w_lat_down", w_lat_down, D, 0, w.BldT, L, 0, L, D, L, 1, s));
+  DenseSeg gx[2] = {{dz, L, w.BldT, L, L}, {d_shared, 2 * SF, w.BsT, 2 * SF, 2 * SF}};
+  if (sh) {
+    MOE_TRY(transpose("transpose_ws_gate", ws_gate, D, 0, w.BsT, 2 * SF, 0, SF, D, SF, 1, s));
+    MOE_TRY(transpose("transpose_ws_up", ws_up, D, 0, w.BsT + SF, 2 * SF, 0, SF, D, SF, 1, s));
+  }
+  MOE_TRY(gemm_nt("gemm_bwd_dx", T, D, sh ? 2 : 1, gx, dx, D, w.part, s));
+  // weight gradients, summed over tokens
+  MOE_TRY(transpose("transpose_x", x, D, 0, w.xT, Tp, 0, T, D, Tp, 1, s));
+  MOE_TRY(transpose("transpose_dz", dz, L, 0, w.dzT, Tp, 0, T, L, Tp, 1, s));
+  DenseSeg gl{w.dzT, Tp, w.xT, Tp, Tp};
+  MOE_TRY(gemm_nt("gemm_bwd_dw_lat_down", L, D, 1, &gl, dw_lat_down, D, w.part, s));
+  if (!sh) return MOE_OK;
+  MOE_TRY(transpose("transpose_d_shared", d_shared, 2 * SF, 0, w.dshT, Tp, 0, T, 2 * SF, Tp, 1, s));
+  DenseSeg gsg{w.dshT, Tp, w.xT, Tp, Tp};
+  MOE_TRY(gemm_nt("gemm_bwd_dws_gate", SF, D, 1, &gsg, dws_gate, D, w.part, s));
+  DenseSeg gsu{w.dshT + (int64_t)SF * Tp, Tp, w.xT, Tp, Tp};
+  return gemm_nt("gemm_bwd_dws_up", SF, D, 1, &gsu, dws_up, D, w.part, s);
+}

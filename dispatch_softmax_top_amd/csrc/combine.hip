@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void combine_gather_kernel(
     // the three loads are independent: issued together, one round trip
     const int s = slot[(int64_t)t * k + lane];
     const int e = topk[(int64_t)t * k + lane];
-    const float g = gates[(int64_t)t * k + lane];
+    const float g = gates ? gates[(int64_t)t * k + lane] : 1.f;
     if (s >= 0) {
       const int p = (e / El) * Wk + t / Tw;
       if (cap) {
@@ -106,16 +106,22 @@ static int gather(const moe_dims &d, const uint16_t *returned, const int64_t *re
                 experts_per_rank(d), pk.Wk, pk.Tw, pk.rows, d.cap_send, parts);
 }
 
+int combine_gather_rows(const moe_dims &d, const uint16_t *rows, const int64_t *offsets,
+                        const int32_t *topk, const int32_t *slot, const float *gates,
+                        uint16_t *out, hipStream_t s) {
+  // chunks per lane: the row's 64-chunk rounds, at most CMB_MAX_CH per wave
+  const int ch = (int)std::min<int64_t>(cdiv(d.latent / 8, 64), CMB_MAX_CH);
+  return ch <= 1   ? gather<1>(d, rows, offsets, topk, slot, gates, out, s)
+         : ch <= 2 ? gather<2>(d, rows, offsets, topk, slot, gates, out, s)
+                   : gather<3>(d, rows, offsets, topk, slot, gates, out, s);
+}
+
 // gather + up-projection with the shared experts' intermediate H [T, S*Fs]
 static int combine_rest(const moe_dims *d, const uint16_t *returned, const int64_t *ret_offsets,
                         const int32_t *topk, const int32_t *slot, const float *gates,
                         const uint16_t *w_lat_up, const uint16_t *H, const uint16_t *ws_down,
                         uint16_t *ylat, uint16_t *out, float *part, hipStream_t s) {
-  // chunks per lane: the row's 64-chunk rounds, at most CMB_MAX_CH per wave
-  const int ch = (int)std::min<int64_t>(cdiv(d->latent / 8, 64), CMB_MAX_CH);
-  MOE_TRY(ch <= 1   ? gather<1>(*d, returned, ret_offsets, topk, slot, gates, ylat, s)
-          : ch <= 2 ? gather<2>(*d, returned, ret_offsets, topk, slot, gates, ylat, s)
-                    : gather<3>(*d, returned, ret_offsets, topk, slot, gates, ylat, s));
+  MOE_TRY(combine_gather_rows(*d, returned, ret_offsets, topk, slot, gates, ylat, s));
   const int S = d->n_shared, Fs = d->d_ff_shared;
   DenseSeg segs[1 + 4];
   segs[0] = DenseSeg{ylat, d->latent, w_lat_up, d->latent, d->latent};

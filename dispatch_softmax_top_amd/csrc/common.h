@@ -105,6 +105,18 @@ __device__ __forceinline__ void st16(u32x4 *p, u32x4 v) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Butterfly reductions over the 64 lanes of a wave (every lane gets the result).
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
 // Lanes below this one.
 __device__ __forceinline__ uint64_t lanemask_lt() {
   int l = lane_id();

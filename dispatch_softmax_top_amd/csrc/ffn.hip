@@ -36,6 +36,20 @@ __global__ __launch_bounds__(256) void ffn_zero_rows(const int32_t *__restrict__
   for (int c = lane_id(); c < L / 8; c += 64) out[c] = zero;
 }
 
+int ret_rows_mark(const int32_t *bank_src, int64_t n_bank, int32_t *flags, int64_t n_ret,
+                  hipStream_t s) {
+  MOE_TRY(launch("ffn_flags_clear", ffn_flags_clear, dim3((unsigned)cdiv(n_ret, 256)), dim3(256),
+                 0, s, flags, n_ret));
+  return launch("ffn_flags_mark", ffn_flags_mark, dim3((unsigned)cdiv(n_bank, 256)), dim3(256), 0,
+                s, bank_src, n_bank, flags, n_ret);
+}
+
+int ret_rows_zero_unmarked(const int32_t *flags, uint16_t *ret, int L, int64_t n_ret,
+                           hipStream_t s) {
+  return launch("ffn_zero_rows", ffn_zero_rows, dim3((unsigned)cdiv(n_ret, 4)), dim3(256), 0, s,
+                flags, ret, L, n_ret);
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -82,14 +96,10 @@ extern "C" int moe_expert_ffn(const moe_dims *d, const moe_bf16 *bank, const int
   int32_t *flags = (int32_t *)((char *)ws + ffn_h_bytes(*d, n_bank_rows));
   float *part = (float *)((char *)flags + ffn_flag_bytes(ret_rows));
 
-  MOE_TRY(launch("ffn_flags_clear", ffn_flags_clear, dim3((unsigned)cdiv(n_ret_rows, 256)),
-                 dim3(256), 0, s, flags, n_ret_rows));
-  MOE_TRY(launch("ffn_flags_mark", ffn_flags_mark, dim3((unsigned)cdiv(n_bank_rows, 256)),
-                 dim3(256), 0, s, bank_src, n_bank_rows, flags, n_ret_rows));
+  MOE_TRY(ret_rows_mark(bank_src, n_bank_rows, flags, n_ret_rows, s));
   MOE_TRY(gemm_expert_swiglu(*d, bank, bank_offsets, bfill, n_bank_rows, w_gate, w_up, H, part,
                              s));
   MOE_TRY(gemm_expert_down(*d, H, bank_offsets, bfill, bank_src, n_bank_rows, w_down, ret,
                            n_ret_rows, part, s));
-  return launch("ffn_zero_rows", ffn_zero_rows, dim3((unsigned)cdiv(n_ret_rows, 4)), dim3(256), 0,
-                s, (const int32_t *)flags, ret, d->latent, n_ret_rows);
+  return ret_rows_zero_unmarked(flags, ret, d->latent, n_ret_rows, s);
 }

@@ -167,12 +167,26 @@ struct DenseArgs {
   int ktiles[MAXSEG];
   uint16_t *C;
   int64_t ldc;
+  // batched products (one K segment): nbatch products of the same shape,
+  // product b at A + b*bsA, B + b*bsB, C + b*bsC
+  int nbatch;
+  int64_t bsA, bsB, bsC;
   GSplit sp;
 };
 
+// Product and tile of logical tile `tile` of a (possibly batched) product.
+template <bool BATCHED>
+__device__ __forceinline__ int dense_batch(const DenseArgs &g, int per, int &tile) {
+  if constexpr (!BATCHED) return 0;
+  const int b = tile / per;
+  tile -= b * per;
+  return b;
+}
+
 // ONLY >= 0: store MFMA row group ONLY alone.
 template <int ONLY = -1>
-__device__ __forceinline__ void dense_store(const DenseArgs &g, int mt, int nt, const GAcc &acc) {
+__device__ __forceinline__ void dense_store(const DenseArgs &g, uint16_t *C, int mt, int nt,
+                                            const GAcc &acc) {
 #pragma unroll
   for (int i = 0; i < GTM; ++i)
 #pragma unroll
@@ -182,7 +196,7 @@ __device__ __forceinline__ void dense_store(const DenseArgs &g, int mt, int nt, 
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = mt * GBM + g_acc_row(i, v);
-        if (m < g.M && n < g.N) g.C[(int64_t)m * g.ldc + n] = f32_to_bf16(acc[i][j][v]);
+        if (m < g.M && n < g.N) C[(int64_t)m * g.ldc + n] = f32_to_bf16(acc[i][j][v]);
       }
     }
 }
@@ -201,14 +215,18 @@ __device__ __forceinline__ void dense_segs(const DenseArgs &g, int mt, int nt, R
   if constexpr (S + 1 < NS) dense_segs<S + 1>(g, mt, nt, row_a, row_b, kend, ops);
 }
 
-// NS: number of K segments (one K range, one rounding).
-template <int NS>
+// NS: number of K segments (one K range, one rounding).  BATCHED: nbatch
+// products of one segment each.
+template <int NS, bool BATCHED = false>
 __device__ __forceinline__ void dense_body(const DenseArgs &g, const GemmLds &lds) {
+  static_assert(!BATCHED || NS == 1, "batched products have one K segment");
   const int tm = (g.M + GBM - 1) / GBM, tn = (g.N + GBN - 1) / GBN;
   GUnit u;
-  if (!g_unit(g.sp, tm * tn, blockIdx.x, u)) return;
+  if (!g_unit(g.sp, tm * tn * (BATCHED ? g.nbatch : 1), blockIdx.x, u)) return;
+  int tile = u.tile;
+  const int b = dense_batch<BATCHED>(g, tm * tn, tile);
   int mt, nt;
-  g_tile_coords(u.tile, tm, tn, mt, nt);
+  g_tile_coords(tile, tm, tn, mt, nt);
   const int mv = g.M - mt * GBM, nv = g.N - nt * GBN;  // valid rows / columns
   const auto row_a = [&](int r) { return min(r, mv - 1); };
   const auto row_b = [&](int r) { return min(r, nv - 1); };
@@ -219,9 +237,9 @@ __device__ __forceinline__ void dense_body(const DenseArgs &g, const GemmLds &ld
   GAcc acc;
   gemm_zero(acc);
   if constexpr (NS == 1) {
-    const auto ops =
-        g_operands(g.A[0] + (int64_t)mt * GBM * g.lda[0] + k0 * GBK, g.lda[0], row_a,
-                   g.B[0] + (int64_t)nt * GBN * g.ldb[0] + k0 * GBK, g.ldb[0], row_b);
+    const auto ops = g_operands(
+        g.A[0] + b * g.bsA + (int64_t)mt * GBM * g.lda[0] + k0 * GBK, g.lda[0], row_a,
+        g.B[0] + b * g.bsB + (int64_t)nt * GBN * g.ldb[0] + k0 * GBK, g.ldb[0], row_b);
     gemm_mainloop(ops, k1 - k0, acc, lds);
   } else {
     GOps<GSegOperand<GCA, NS>, GSegOperand<GCB, NS>> ops;
@@ -240,7 +258,7 @@ __device__ __forceinline__ void dense_body(const DenseArgs &g, const GemmLds &ld
     g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
     return;
   }
-  dense_store(g, mt, nt, acc);
+  dense_store(g, g.C + b * g.bsC, mt, nt, acc);
 }
 
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_latent_down_kernel(DenseArgs g) {
@@ -255,17 +273,28 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
   dense_body<NS>(g, lds);
 }
 
+// products of the backward pass: NS K segments, or a batch of products
+template <int NS, bool BATCHED>
+__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_nt_kernel(DenseArgs g) {
+  MOE_GEMM_LDS(lds);
+  dense_body<NS, BATCHED>(g, lds);
+}
+
 // the split tiles of a dense product: sum of parts, then the store
+template <bool BATCHED = false>
 __global__ __launch_bounds__(GNT) void gemm_dense_tail_kernel(DenseArgs g) {
   const int tm = (g.M + GBM - 1) / GBM, tn = (g.N + GBN - 1) / GBN;
   GUnit u;
-  if (!g_tail_tile(g.sp, tm * tn, blockIdx.x / GTM, u)) return;
+  if (!g_tail_tile(g.sp, tm * tn * (BATCHED ? g.nbatch : 1), blockIdx.x / GTM, u)) return;
+  int tile = u.tile;
+  const int b = dense_batch<BATCHED>(g, tm * tn, tile);
   int mt, nt;
-  g_tile_coords(u.tile, tm, tn, mt, nt);
+  g_tile_coords(tile, tm, tn, mt, nt);
+  uint16_t *C = g.C + b * g.bsC;
   GAcc acc;
 #define MOE_ROWS(I)                                       \
   g_part_sum_rows<I>(g.sp.part, u.tail, u.nparts, acc); \
-  dense_store<I>(g, mt, nt, acc)
+  dense_store<I>(g, C, mt, nt, acc)
   MOE_TAIL_ROWS(MOE_ROWS)
 #undef MOE_ROWS
 }
@@ -368,6 +397,14 @@ struct SwigluArgs {
   int F, ftiles;  // ftiles = F / 128
   uint16_t *H;
   int64_t ldh;
+  // backward epilogue: dH (gradient of h, read at column dh_col0 + the h
+  // column), AB (d_a at the h column, d_b ab_off columns further)
+  const uint16_t *dH;
+  int64_t ld_dh;
+  int dh_col0;
+  uint16_t *AB;
+  int64_t ld_ab;
+  int ab_off;
   // dense (shared experts): M rows, expert = f-tile / ftiles along N
   int M, S;
   // grouped (routed experts)
@@ -403,7 +440,10 @@ __device__ __forceinline__ void swiglu_acc(const SwigluArgs &g, RowOf row_of, in
   gemm_mainloop(ops, k1 - k0, acc, lds);
 }
 
-template <int ONLY = -1, class RowOf>
+// BWD: with dh = dH at the same (row, column), also
+//   d_a = bf16(dh * b * silu'(a)),  d_b = bf16(dh * silu(a)),
+//   silu'(a) = s (1 + a (1 - s)), s = 1 / (1 + e^-a).
+template <int ONLY = -1, bool BWD = false, class RowOf>
 __device__ __forceinline__ void swiglu_store(const SwigluArgs &g, RowOf row_of, int rows, int ft,
                                              int h_col0, const GAcc &acc) {
   const int f0 = ft * 128;
@@ -414,15 +454,33 @@ __device__ __forceinline__ void swiglu_store(const SwigluArgs &g, RowOf row_of, 
       if (ONLY >= 0 && i != ONLY) continue;
       const int m = g_acc_row(i, v);
       if (m >= rows) continue;
-      uint16_t *h = g.H + row_of(m) * g.ldh + h_col0 + f0;
+      const int64_t r = row_of(m);
+      uint16_t *h = g.H + r * g.ldh + h_col0 + f0;
+      if constexpr (!BWD) {
 #pragma unroll
-      for (int p = 0; p < GTN / 2; ++p) {
-        const float a = acc[i][2 * p][v], b = acc[i][2 * p + 1][v];
-        h[g_swiglu_col(p)] = f32_to_bf16(silu_f32(a) * b);
+        for (int p = 0; p < GTN / 2; ++p) {
+          const float a = acc[i][2 * p][v], b = acc[i][2 * p + 1][v];
+          h[g_swiglu_col(p)] = f32_to_bf16(silu_f32(a) * b);
+        }
+      } else {
+        const uint16_t *dh = g.dH + r * g.ld_dh + g.dh_col0 + h_col0 + f0;
+        uint16_t *da = g.AB + r * g.ld_ab + h_col0 + f0;
+#pragma unroll
+        for (int p = 0; p < GTN / 2; ++p) {
+          const float a = acc[i][2 * p][v], b = acc[i][2 * p + 1][v];
+          const int c = g_swiglu_col(p);
+          const float gh = bf16_to_f32(dh[c]);
+          const float s = 1.0f / (1.0f + __expf(-a));
+          const float sa = silu_f32(a);
+          h[c] = f32_to_bf16(sa * b);
+          da[c] = f32_to_bf16(gh * b * (s * (1.0f + a * (1.0f - s))));
+          da[g.ab_off + c] = f32_to_bf16(gh * sa);
+        }
       }
     }
 }
 
+template <bool BWD>
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_shared_swiglu_kernel(SwigluArgs g) {
   MOE_GEMM_LDS(lds);
   const int tm = (g.M + GBM - 1) / GBM, tn = g.S * g.ftiles;
@@ -442,9 +500,10 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
     g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
     return;
   }
-  swiglu_store(g, row_of, rows, ft, s * g.F, acc);
+  swiglu_store<-1, BWD>(g, row_of, rows, ft, s * g.F, acc);
 }
 
+template <bool BWD>
 __global__ __launch_bounds__(GNT) void gemm_shared_swiglu_tail_kernel(SwigluArgs g) {
   const int tm = (g.M + GBM - 1) / GBM, tn = g.S * g.ftiles;
   GUnit u;
@@ -458,11 +517,12 @@ __global__ __launch_bounds__(GNT) void gemm_shared_swiglu_tail_kernel(SwigluArgs
   GAcc acc;
 #define MOE_ROWS(I)                                       \
   g_part_sum_rows<I>(g.sp.part, u.tail, u.nparts, acc); \
-  swiglu_store<I>(g, row_of, rows, ft, s * g.F, acc)
+  swiglu_store<I, BWD>(g, row_of, rows, ft, s * g.F, acc)
   MOE_TAIL_ROWS(MOE_ROWS)
 #undef MOE_ROWS
 }
 
+template <bool BWD>
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_swiglu_kernel(SwigluArgs g) {
   MOE_GEMM_LDS(lds);
   GUnit u;
@@ -479,9 +539,10 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
     g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
     return;
   }
-  swiglu_store(g, row_of, t.rows, t.nt, 0, acc);
+  swiglu_store<-1, BWD>(g, row_of, t.rows, t.nt, 0, acc);
 }
 
+template <bool BWD>
 __global__ __launch_bounds__(GNT) void gemm_expert_swiglu_tail_kernel(SwigluArgs g) {
   GUnit u;
   GTile t;
@@ -492,7 +553,7 @@ __global__ __launch_bounds__(GNT) void gemm_expert_swiglu_tail_kernel(SwigluArgs
   GAcc acc;
 #define MOE_ROWS(I)                                       \
   g_part_sum_rows<I>(g.sp.part, u.tail, u.nparts, acc); \
-  swiglu_store<I>(g, row_of, t.rows, t.nt, 0, acc)
+  swiglu_store<I, BWD>(g, row_of, t.rows, t.nt, 0, acc)
   MOE_TAIL_ROWS(MOE_ROWS)
 #undef MOE_ROWS
 }
@@ -634,12 +695,19 @@ static int split_parts(const GSplit &sp, int64_t total) {
 
 static int dense(const char *name, const char *tail_name, void (*k)(DenseArgs), int M, int N,
                  int nseg, const DenseSeg *segs, uint16_t *C, int64_t ldc, float *part,
-                 hipStream_t s) {
+                 hipStream_t s, int nbatch = 1, int64_t bsA = 0, int64_t bsB = 0,
+                 int64_t bsC = 0) {
   if (nseg < 1 || nseg > MAXSEG) return fail(MOE_ERR_INVALID, "%s: bad segment count", name);
+  if (nbatch < 1 || (nbatch > 1 && nseg != 1))
+    return fail(MOE_ERR_INVALID, "%s: bad batch", name);
   DenseArgs a{};
   a.M = M;
   a.N = N;
   a.nseg = nseg;
+  a.nbatch = nbatch;
+  a.bsA = bsA;
+  a.bsB = bsB;
+  a.bsC = bsC;
   for (int i = 0; i < nseg; ++i) {
     if (segs[i].K % GBK) return fail(MOE_ERR_UNSUPPORTED, "%s: K %% %d != 0", name, GBK);
     // copy offsets within one 256-row tile are 32-bit
@@ -654,7 +722,8 @@ static int dense(const char *name, const char *tail_name, void (*k)(DenseArgs), 
   }
   a.C = C;
   a.ldc = ldc;
-  const int64_t tiles = cdiv(M, GBM) * cdiv(N, GBN);
+  const int64_t tiles = cdiv(M, GBM) * cdiv(N, GBN) * nbatch;
+  if (tiles > INT32_MAX / 2) return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", name);
   int kt = 0;
   for (int i = 0; i < nseg; ++i) kt += a.ktiles[i];
   MOE_TRY(make_split(part, kt, a.sp));
@@ -665,7 +734,8 @@ static int dense(const char *name, const char *tail_name, void (*k)(DenseArgs), 
   }
   const int64_t r = tiles % a.sp.ncu;
   MOE_TRY(launch(name, k, dim3((unsigned)(tiles - r + r * S)), dim3(GNT), 0, s, a));
-  return launch(tail_name, gemm_dense_tail_kernel, dim3((unsigned)(r * GTM)), dim3(GNT), 0, s, a);
+  return launch(tail_name, nbatch > 1 ? gemm_dense_tail_kernel<true> : gemm_dense_tail_kernel<false>,
+                dim3((unsigned)(r * GTM)), dim3(GNT), 0, s, a);
 }
 
 int gemm_latent_down(int M, int N, const DenseSeg &seg, uint16_t *C, int64_t ldc, hipStream_t s) {
@@ -683,11 +753,10 @@ int gemm_up_shared(int M, int N, int nseg, const DenseSeg *segs, uint16_t *C, in
                part, s);
 }
 
-int gemm_shared_swiglu(int M, const uint16_t *x, int64_t ldx, int K, const uint16_t *wg,
-                       const uint16_t *wu, int S, int F, uint16_t *H, float *part,
-                       hipStream_t s) {
-  if (S == 0) return MOE_OK;
-  SwigluArgs a{};
+static int shared_swiglu(const char *name, const char *tail_name, void (*k)(SwigluArgs),
+                         void (*tk)(SwigluArgs), SwigluArgs &a, int M, const uint16_t *x,
+                         int64_t ldx, int K, const uint16_t *wg, const uint16_t *wu, int S, int F,
+                         uint16_t *H, float *part, hipStream_t s) {
   a.A = x;
   a.lda = ldx;
   a.ktiles = K / GBK;
@@ -705,31 +774,53 @@ int gemm_shared_swiglu(int M, const uint16_t *x, int64_t ldx, int K, const uint1
   const int P = split_parts(a.sp, tiles);
   if (P == 1) {
     a.sp.part = nullptr;
-    return launch("gemm_shared_swiglu", gemm_shared_swiglu_kernel, dim3((unsigned)tiles),
-                  dim3(GNT), 0, s, a);
+    return launch(name, k, dim3((unsigned)tiles), dim3(GNT), 0, s, a);
   }
   const int64_t r = tiles % a.sp.ncu;
-  MOE_TRY(launch("gemm_shared_swiglu", gemm_shared_swiglu_kernel,
-                 dim3((unsigned)(tiles - r + r * P)), dim3(GNT), 0, s, a));
-  return launch("gemm_shared_swiglu_tail", gemm_shared_swiglu_tail_kernel,
-                dim3((unsigned)(r * GTM)), dim3(GNT), 0, s, a);
+  MOE_TRY(launch(name, k, dim3((unsigned)(tiles - r + r * P)), dim3(GNT), 0, s, a));
+  return launch(tail_name, tk, dim3((unsigned)(r * GTM)), dim3(GNT), 0, s, a);
 }
 
 // Product groups of the bank: each local expert over every wave when the
 // merged rows stay within 32-bit copy offsets of a tile's first row, else
 // every (wave, expert) group alone.
 static GroupArgs group_args(const moe_dims &d, const int64_t *bank_offsets, const int32_t *bfill,
-                            int64_t n_bank_rows) {
+                            int64_t n_bank_rows, int64_t width) {
   GroupArgs g{};
   g.El = experts_per_rank(d);
   g.G = d.n_waves * g.El;
   g.cap = d.cap_recv;
   g.count = bfill;
   g.offsets = ragged(d) ? bank_offsets : nullptr;
-  const int64_t width = d.latent > d.d_ff ? d.latent : d.d_ff;
   const bool merge = d.n_waves <= GMAXW && n_bank_rows * width * 2 < INT32_MAX;
   g.nw = merge ? d.n_waves : 1;
   return g;
+}
+
+int gemm_shared_swiglu(int M, const uint16_t *x, int64_t ldx, int K, const uint16_t *wg,
+                       const uint16_t *wu, int S, int F, uint16_t *H, float *part,
+                       hipStream_t s) {
+  if (S == 0) return MOE_OK;
+  SwigluArgs a{};
+  return shared_swiglu("gemm_shared_swiglu", "gemm_shared_swiglu_tail",
+                       gemm_shared_swiglu_kernel<false>, gemm_shared_swiglu_tail_kernel<false>, a,
+                       M, x, ldx, K, wg, wu, S, F, H, part, s);
+}
+
+int gemm_shared_swiglu_bwd(int M, const uint16_t *x, int64_t ldx, int K, const uint16_t *wg,
+                           const uint16_t *wu, int S, int F, const uint16_t *dH, int64_t ld_dh,
+                           int dh_col0, uint16_t *H, uint16_t *AB, float *part, hipStream_t s) {
+  if (S == 0) return MOE_OK;
+  SwigluArgs a{};
+  a.dH = dH;
+  a.ld_dh = ld_dh;
+  a.dh_col0 = dh_col0;
+  a.AB = AB;
+  a.ld_ab = 2ll * S * F;
+  a.ab_off = S * F;
+  return shared_swiglu("gemm_shared_swiglu_bwd", "gemm_shared_swiglu_bwd_tail",
+                       gemm_shared_swiglu_kernel<true>, gemm_shared_swiglu_tail_kernel<true>, a,
+                       M, x, ldx, K, wg, wu, S, F, H, part, s);
 }
 
 static int64_t grouped_tiles_bound(const moe_dims &d, int64_t n_bank_rows, int tn) {
@@ -754,10 +845,11 @@ static int grouped(const char *name, const char *tail_name, void (*k)(Args),
   return launch(tail_name, tk, dim3((unsigned)(a.sp.ncu / 2 * GTM)), dim3(GNT), 0, s, a);
 }
 
-int gemm_expert_swiglu(const moe_dims &d, const uint16_t *bank, const int64_t *bank_offsets,
-                       const int32_t *bfill, int64_t n_bank_rows, const uint16_t *wg,
-                       const uint16_t *wu, uint16_t *H, float *part, hipStream_t s) {
-  SwigluArgs a{};
+static int expert_swiglu(const char *name, const char *tail_name, void (*k)(SwigluArgs),
+                         void (*tk)(SwigluArgs), SwigluArgs &a, const moe_dims &d,
+                         const uint16_t *bank, const int64_t *bank_offsets, const int32_t *bfill,
+                         int64_t n_bank_rows, const uint16_t *wg, const uint16_t *wu, uint16_t *H,
+                         float *part, hipStream_t s) {
   a.A = bank;
   a.lda = d.latent;
   a.ktiles = d.latent / GBK;
@@ -768,30 +860,86 @@ int gemm_expert_swiglu(const moe_dims &d, const uint16_t *bank, const int64_t *b
   a.ftiles = d.d_ff / 128;
   a.H = H;
   a.ldh = d.d_ff;
-  a.grp = group_args(d, bank_offsets, bfill, n_bank_rows);
-  return grouped("gemm_expert_swiglu", "gemm_expert_swiglu_tail", gemm_expert_swiglu_kernel,
-                 gemm_expert_swiglu_tail_kernel, grouped_tiles_bound(d, n_bank_rows, a.ftiles),
-                 a.ktiles, a, part, s);
+  a.grp = group_args(d, bank_offsets, bfill, n_bank_rows, std::max(d.latent, d.d_ff));
+  return grouped(name, tail_name, k, tk, grouped_tiles_bound(d, n_bank_rows, a.ftiles), a.ktiles,
+                 a, part, s);
+}
+
+int gemm_expert_swiglu(const moe_dims &d, const uint16_t *bank, const int64_t *bank_offsets,
+                       const int32_t *bfill, int64_t n_bank_rows, const uint16_t *wg,
+                       const uint16_t *wu, uint16_t *H, float *part, hipStream_t s) {
+  SwigluArgs a{};
+  return expert_swiglu("gemm_expert_swiglu", "gemm_expert_swiglu_tail",
+                       gemm_expert_swiglu_kernel<false>, gemm_expert_swiglu_tail_kernel<false>, a,
+                       d, bank, bank_offsets, bfill, n_bank_rows, wg, wu, H, part, s);
+}
+
+int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int32_t *bfill,
+                           int64_t n_bank_rows, const uint16_t *wg, const uint16_t *wu,
+                           const uint16_t *dH, uint16_t *H, uint16_t *AB, float *part,
+                           hipStream_t s) {
+  SwigluArgs a{};
+  a.dH = dH;
+  a.ld_dh = d.d_ff;
+  a.AB = AB;
+  a.ld_ab = 2ll * d.d_ff;
+  a.ab_off = d.d_ff;
+  return expert_swiglu("gemm_expert_swiglu_bwd", "gemm_expert_swiglu_bwd_tail",
+                       gemm_expert_swiglu_kernel<true>, gemm_expert_swiglu_tail_kernel<true>, a,
+                       d, bank, nullptr, bfill, n_bank_rows, wg, wu, H, part, s);
+}
+
+// out[dst[r]] = bf16(A[r] . B_j^T) for the bank rows r of every group (w, j):
+// A [bank rows][K], B [E_l][N][K]; dst rows < 0 or >= n_out are not stored.
+static int grouped_nt(const char *name, const char *tail_name, const moe_dims &d,
+                      const uint16_t *A, int K, const int64_t *bank_offsets, const int32_t *bfill,
+                      const int32_t *dst, int64_t n_bank_rows, const uint16_t *B, int N,
+                      uint16_t *out, int64_t n_out, float *part, hipStream_t s) {
+  if (K % GBK) return fail(MOE_ERR_UNSUPPORTED, "%s: K %% %d != 0", name, GBK);
+  DownArgs a{};
+  a.n_ret = n_out;
+  a.H = A;
+  a.F = K;
+  a.ktiles = K / GBK;
+  a.Wd = B;
+  a.L = N;
+  a.tn = (int)cdiv(N, GBN);
+  a.grp = group_args(d, bank_offsets, bfill, n_bank_rows, std::max(K, N));
+  a.bank_src = dst;
+  a.ret = out;
+  return grouped(name, tail_name, gemm_expert_down_kernel, gemm_expert_down_tail_kernel,
+                 grouped_tiles_bound(d, n_bank_rows, a.tn), a.ktiles, a, part, s);
 }
 
 int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_offsets,
                      const int32_t *bfill, const int32_t *bank_src, int64_t n_bank_rows,
                      const uint16_t *wd, uint16_t *ret, int64_t n_ret, float *part,
                      hipStream_t s) {
-  DownArgs a{};
-  a.n_ret = n_ret;
-  a.H = H;
-  a.F = d.d_ff;
-  a.ktiles = d.d_ff / GBK;
-  a.Wd = wd;
-  a.L = d.latent;
-  a.tn = (int)cdiv(d.latent, GBN);
-  a.grp = group_args(d, bank_offsets, bfill, n_bank_rows);
-  a.bank_src = bank_src;
-  a.ret = ret;
-  return grouped("gemm_expert_down", "gemm_expert_down_tail", gemm_expert_down_kernel,
-                 gemm_expert_down_tail_kernel, grouped_tiles_bound(d, n_bank_rows, a.tn),
-                 a.ktiles, a, part, s);
+  return grouped_nt("gemm_expert_down", "gemm_expert_down_tail", d, H, d.d_ff, bank_offsets, bfill,
+                    bank_src, n_bank_rows, wd, d.latent, ret, n_ret, part, s);
+}
+
+int gemm_grouped_nt(const char *name, const moe_dims &d, const uint16_t *A, int K,
+                    const int32_t *bfill, const int32_t *dst, int64_t n_bank_rows,
+                    const uint16_t *B, int N, uint16_t *out, int64_t n_out, float *part,
+                    hipStream_t s) {
+  return grouped_nt(name, name, d, A, K, nullptr, bfill, dst, n_bank_rows, B, N, out, n_out, part,
+                    s);
+}
+
+int gemm_nt(const char *name, int M, int N, int nseg, const DenseSeg *segs, uint16_t *C,
+            int64_t ldc, float *part, hipStream_t s) {
+  static void (*const k[2])(DenseArgs) = {gemm_nt_kernel<1, false>, gemm_nt_kernel<2, false>};
+  if (nseg < 1 || nseg > 2) return fail(MOE_ERR_INVALID, "%s: bad segment count", name);
+  return dense(name, name, k[nseg - 1], M, N, nseg, segs, C, ldc, part, s);
+}
+
+int gemm_nt_batched(const char *name, int M, int N, const DenseSeg &seg, int nbatch, int64_t bsA,
+                    int64_t bsB, uint16_t *C, int64_t ldc, int64_t bsC, float *part,
+                    hipStream_t s) {
+  if (nbatch == 1) return gemm_nt(name, M, N, 1, &seg, C, ldc, part, s);
+  return dense(name, name, gemm_nt_kernel<1, true>, M, N, 1, &seg, C, ldc, part, s, nbatch, bsA,
+               bsB, bsC);
 }
 
 }  // namespace moe

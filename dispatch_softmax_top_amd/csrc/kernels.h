@@ -49,4 +49,50 @@ int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_o
                      const uint16_t *wd, uint16_t *ret, int64_t n_ret, float *part,
                      hipStream_t s);
 
+// Return rows: flags[r] = 1 for every row some kept bank row writes (bank_src),
+// then every unflagged row of ret [n_ret][L] set to zero.
+int ret_rows_mark(const int32_t *bank_src, int64_t n_bank, int32_t *flags, int64_t n_ret,
+                  hipStream_t s);
+int ret_rows_zero_unmarked(const int32_t *flags, uint16_t *ret, int L, int64_t n_ret,
+                           hipStream_t s);
+
+// Sum over each token's kept choices of gates[t, j] * rows[row(t, j)] (gates
+// NULL: weight 1), rounded to bf16: the combine's gather (combine.hip).
+int combine_gather_rows(const moe_dims &d, const uint16_t *rows, const int64_t *offsets,
+                        const int32_t *topk, const int32_t *slot, const float *gates,
+                        uint16_t *out, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// backward pass
+// ---------------------------------------------------------------------------
+
+// Workspace bytes of the backward calls (fixed mode).
+int64_t bwd_ws_bytes(const moe_dims &d, int call);
+
+// C[M, N] (ldc) = sum over nseg <= 2 segments of A . B^T (bf16 out).
+int gemm_nt(const char *name, int M, int N, int nseg, const DenseSeg *segs, uint16_t *C,
+            int64_t ldc, float *part, hipStream_t s);
+// nbatch products of one segment: product b at A + b*bsA, B + b*bsB, C + b*bsC.
+int gemm_nt_batched(const char *name, int M, int N, const DenseSeg &seg, int nbatch, int64_t bsA,
+                    int64_t bsB, uint16_t *C, int64_t ldc, int64_t bsC, float *part,
+                    hipStream_t s);
+// Shared experts recomputed with the SwiGLU gradient epilogue: dH[:, dh_col0 +
+// s*F + f] in, H = h_s [M, S*F] and AB [M, 2*S*F] (d_a of every expert, then
+// d_b) out.
+int gemm_shared_swiglu_bwd(int M, const uint16_t *x, int64_t ldx, int K, const uint16_t *wg,
+                           const uint16_t *wu, int S, int F, const uint16_t *dH, int64_t ld_dh,
+                           int dh_col0, uint16_t *H, uint16_t *AB, float *part, hipStream_t s);
+// Routed experts recomputed over the bank (fixed mode) with the SwiGLU
+// gradient epilogue: dH, H [bank rows, F], AB [bank rows, 2F].
+int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int32_t *bfill,
+                           int64_t n_bank_rows, const uint16_t *wg, const uint16_t *wu,
+                           const uint16_t *dH, uint16_t *H, uint16_t *AB, float *part,
+                           hipStream_t s);
+// Grouped over the bank's groups (fixed mode): out[dst[r]] = A[r] . B_j^T,
+// A [bank rows][K], B [E_l][N][K].
+int gemm_grouped_nt(const char *name, const moe_dims &d, const uint16_t *A, int K,
+                    const int32_t *bfill, const int32_t *dst, int64_t n_bank_rows,
+                    const uint16_t *B, int N, uint16_t *out, int64_t n_out, float *part,
+                    hipStream_t s);
+
 }  // namespace moe

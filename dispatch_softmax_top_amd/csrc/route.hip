@@ -44,18 +44,6 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
-
 // bias: NULL, or [E] fp32 added to every token's logits (one fp32 rounding).
 // renorm: gates divided by their sum over the k chosen.
 template <int VPL>
@@ -183,6 +171,81 @@ __global__ __launch_bounds__(CNT_THREADS) void expert_counts(const int32_t *__re
     if (hist[e]) atomicAdd(&counts[e], hist[e]);
 }
 
+// Backward of the router, one wave per token.  With p = softmax(l) over all
+// E (l = fp32(logit + bias), recomputed) and gate j = p[e_j]:
+//   d_l[e] = sum_j d_gates[j] p[e_j] ([e == e_j] - p[e]);
+// renormalised gates q = softmax over the k chosen logits:
+//   d_l[e_j] = q_j (d_gates[j] - sum_i d_gates[i] q_i), 0 elsewhere.
+template <int VPL>
+__global__ __launch_bounds__(256) void route_backward_kernel(
+    const float *__restrict__ logits, const float *__restrict__ bias, int T, int E, int k,
+    int renorm, const int32_t *__restrict__ topk, const float *__restrict__ d_gates,
+    float *__restrict__ d_logits) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  const float *l = logits + (int64_t)t * E;
+  int my_e = -1;
+  float my_dg = 0.f, my_l = -INFINITY;
+  if (lane < k) {
+    const int e = topk[(int64_t)t * k + lane];
+    my_dg = d_gates[(int64_t)t * k + lane];
+    if ((unsigned)e < (unsigned)E) {
+      my_e = e;
+      my_l = bias ? l[e] + bias[e] : l[e];
+    }
+  }
+  float out[VPL];
+  float add;  // this lane's chosen expert's own term
+  if (!renorm) {
+    float v[VPL];
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = e < E ? (bias ? l[e] + bias[e] : l[e]) : -INFINITY;
+      m = fmaxf(m, v[i]);
+    }
+    m = wave_max_f32(m);
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) z += (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
+    z = wave_sum_f32(z);
+    const float pj = my_e >= 0 ? expf(my_l - m) / z : 0.f;
+    add = my_dg * pj;
+    const float s = wave_sum_f32(add);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) out[i] = -(expf(v[i] - m) / z) * s;
+  } else {
+    const float mk = wave_max_f32(my_l);
+    const float ej = my_e >= 0 ? expf(my_l - mk) : 0.f;
+    const float q = ej / wave_sum_f32(ej);
+    const float s = wave_sum_f32(my_dg * q);
+    add = my_e >= 0 ? q * (my_dg - s) : 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) out[i] = 0.f;
+  }
+  for (int j = 0; j < k; ++j) {
+    const int ej = __shfl(my_e, j);
+    const float aj = __shfl(add, j);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (lane + 64 * i == ej) out[i] += aj;
+  }
+  float *o = d_logits + (int64_t)t * E;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i)
+    if (lane + 64 * i < E) o[lane + 64 * i] = out[i];
+}
+
+template <int VPL>
+static int launch_route_bwd(const float *logits, const float *bias, int T, int E, int k,
+                            int renorm, const int32_t *topk, const float *d_gates,
+                            float *d_logits, hipStream_t s) {
+  return launch("route_backward", route_backward_kernel<VPL>, dim3((unsigned)cdiv(T, 4)),
+                dim3(256), 0, s, logits, bias, T, E, k, renorm, topk, d_gates, d_logits);
+}
+
 // One block: H_i = sum over the window's batches, f_i = H_i / sum H (1/E when
 // nothing was chosen), b_i = -alpha (f_i - 1/E), in double, rounded to fp32.
 __global__ __launch_bounds__(1024) void balance_bias(const int32_t *__restrict__ window, int nb,
@@ -256,4 +319,30 @@ extern "C" int moe_balance_bias(const int32_t *window, int32_t n_batches, int32_
   MOE_TRY(check_ptr(bias, "bias"));
   return launch("balance_bias", balance_bias, dim3(1), dim3(1024), 0, (hipStream_t)stream,
                 window, n_batches, E, alpha, bias);
+}
+
+extern "C" int moe_route_backward(const float *logits, const float *bias, int32_t T, int32_t E,
+                                  int32_t k, int32_t flags, const int32_t *topk,
+                                  const float *d_gates, float *d_logits, void *stream) {
+  clear_error();
+  if (T < 1 || E < 1 || k < 1 || k > E)
+    return fail(MOE_ERR_INVALID, "moe_route_backward: need T >= 1 and 1 <= k <= E");
+  if (E > 1024 || k > 32) return fail(MOE_ERR_UNSUPPORTED, "moe_route_backward: E <= 1024, k <= 32");
+  if (flags & ~MOE_ROUTE_RENORM) return fail(MOE_ERR_INVALID, "moe_route_backward: unknown flags");
+  MOE_TRY(check_ptr(logits, "logits"));
+  MOE_TRY(check_ptr(bias, "bias", true));
+  MOE_TRY(check_ptr(topk, "topk"));
+  MOE_TRY(check_ptr(d_gates, "d_gates"));
+  MOE_TRY(check_ptr(d_logits, "d_logits"));
+  const int rn = (flags & MOE_ROUTE_RENORM) != 0;
+  hipStream_t s = (hipStream_t)stream;
+  const int vpl = (int)cdiv(E, 64);
+  if (vpl <= 1) return launch_route_bwd<1>(logits, bias, T, E, k, rn, topk, d_gates, d_logits, s);
+  if (vpl <= 2) return launch_route_bwd<2>(logits, bias, T, E, k, rn, topk, d_gates, d_logits, s);
+  if (vpl <= 4) return launch_route_bwd<4>(logits, bias, T, E, k, rn, topk, d_gates, d_logits, s);
+  if (vpl <= 6) return launch_route_bwd<6>(logits, bias, T, E, k, rn, topk, d_gates, d_logits, s);
+  if (vpl <= 8) return launch_route_bwd<8>(logits, bias, T, E, k, rn, topk, d_gates, d_logits, s);
+  if (vpl <= 12)
+    return launch_route_bwd<12>(logits, bias, T, E, k, rn, topk, d_gates, d_logits, s);
+  return launch_route_bwd<16>(logits, bias, T, E, k, rn, topk, d_gates, d_logits, s);
 }

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef uint16_t moe_bf16;
 
@@ -111,7 +111,8 @@ int moe_capacity(const moe_dims *d, int64_t cf_send_num, int64_t cf_send_den,
                  int32_t *cap_recv);
 
 enum { MOE_CALL_ROUTE = 0, MOE_CALL_PACK = 1, MOE_CALL_BANK = 2,
-       MOE_CALL_FFN = 3, MOE_CALL_COMBINE = 4, MOE_CALL_COMBINE_SHARED = 5 };
+       MOE_CALL_FFN = 3, MOE_CALL_COMBINE = 4, MOE_CALL_COMBINE_SHARED = 5,
+       MOE_CALL_COMBINE_BWD = 6, MOE_CALL_FFN_BWD = 7, MOE_CALL_PACK_BWD = 8 };
 
 /* Bytes of scratch a call needs.  n_rows: bank rows allocated (FFN, ragged
  * mode); ignored otherwise.  Returns a negative moe_status on bad dims. */
@@ -279,6 +280,88 @@ int moe_profile_collect(void);
 int moe_profile_get(int i, char *name, int name_len, double *total_ms,
                     int64_t *launches);
 void moe_profile_reset(void);
+
+/* ------------------------------------------------------------------------
+ * Backward of the branch (training; fixed capacities only, MOE_ERR_UNSUPPORTED
+ * in ragged mode).  [P2]/[P3] describe a model in open training and give its
+ * forward pass; each call below is the chain rule through the forward call
+ * of the same stage, for a loss whose gradient with respect to `out` is
+ * d_out.  Gradients are stored like their values: bf16 activations and
+ * weight gradients (written, not accumulated), fp32 gate and logit
+ * gradients.  The intermediates a = u.W_g and b = u.W_u are recomputed.
+ * Order on one rank: moe_combine_backward -> (return exchange reversed) ->
+ * moe_expert_ffn_backward -> (forward exchange reversed) ->
+ * moe_pack_backward, and moe_route_backward with the gate gradients.
+ * The router's own product (logits = x . W_r) is outside the boundary: its
+ * input gradient is the caller's.  Workspaces: moe_workspace_bytes(d,
+ * MOE_CALL_*_BWD, 0).
+ * ------------------------------------------------------------------------ */
+
+/* Router: d_logits [T, E] fp32 from d_gates [T, k].  With p the softmax of
+ * l = fp32(logit + bias) over all E and gate j = p[e_j]:
+ * d_l[e] = sum_j d_gates[j] p[e_j] ([e == e_j] - p[e]).  flags
+ * MOE_ROUTE_RENORM (gates = softmax over the k chosen, q):
+ * d_l[e_j] = q_j (d_gates[j] - sum_i d_gates[i] q_i), 0 elsewhere.  The
+ * bias (NULL = none) is stop-gradient.  topk as returned by the router. */
+int moe_route_backward(const float *logits, const float *bias, int32_t T,
+                       int32_t E, int32_t k, int32_t flags, const int32_t *topk,
+                       const float *d_gates, float *d_logits, void *stream);
+
+/* Combine side, on the sender.  Inputs as given to / produced by
+ * moe_combine (returned rows in the pools' layout, the sender's topk, slot,
+ * gates, fill, x, the forward's ylat) plus d_out [T, d_model] bf16.
+ *   d_returned [n_ranks*n_waves*cap_send, latent] out: bf16(g d_ylat[t]) in
+ *              each kept choice's row, 0 in every other row; d_ylat =
+ *              d_out . W_lu^T (rounded to bf16, not returned)
+ *   d_gates    [T, k] fp32 out: returned row . d_ylat[t], 0 if dropped
+ *   d_shared   [T, 2, n_shared, d_ff_shared] bf16 out: d_a, then d_b, of
+ *              every shared expert (input of moe_pack_backward)
+ *   dw_lat_up  [d_model, latent] bf16 out (W_lu's layout)
+ *   dws_down   [n_shared, d_model, d_ff_shared] bf16 out
+ * ws_gate / ws_up / ws_down / d_shared / dws_down may be NULL if n_shared = 0. */
+int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
+                         const int32_t *topk, const int32_t *slot,
+                         const float *gates, const int32_t *fill,
+                         const moe_bf16 *x, const moe_bf16 *ylat,
+                         const moe_bf16 *w_lat_up, const moe_bf16 *ws_gate,
+                         const moe_bf16 *ws_up, const moe_bf16 *ws_down,
+                         const moe_bf16 *d_out, moe_bf16 *d_returned,
+                         float *d_gates, moe_bf16 *d_shared,
+                         moe_bf16 *dw_lat_up, moe_bf16 *dws_down, void *ws,
+                         int64_t ws_bytes, void *stream);
+
+/* Receiver side.  bank, bank_src, bfill as produced by moe_bank; weights as
+ * given to moe_expert_ffn; d_ret [n_ranks*n_waves*cap_send, latent]: the
+ * gradients of this rank's return rows (receive layout).
+ *   d_recv   [n_ranks*n_waves*cap_send, latent] out: gradient of each kept
+ *            receive row's payload (d_a . W_g + d_b . W_u), 0 elsewhere
+ *   dw_gate, dw_up [E_l, d_ff, latent], dw_down [E_l, latent, d_ff] out,
+ *            each local expert's sum over its kept rows of every wave. */
+int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
+                            const int32_t *bank_src, const int32_t *bfill,
+                            const moe_bf16 *w_gate, const moe_bf16 *w_up,
+                            const moe_bf16 *w_down, const moe_bf16 *d_ret,
+                            moe_bf16 *d_recv, moe_bf16 *dw_gate,
+                            moe_bf16 *dw_up, moe_bf16 *dw_down, void *ws,
+                            int64_t ws_bytes, void *stream);
+
+/* Sender side.  d_pools [n_ranks*n_waves*cap_send, latent]: gradients of
+ * this shard's pool payloads (the pools' layout); topk, slot, x as in the
+ * forward pass; d_shared from moe_combine_backward.
+ *   dz          [T, latent] bf16 out: sum over kept choices of their rows
+ *   dx          [T, d_model] bf16 out: dz . W_ld^T + the shared experts'
+ *               input gradient, one sum, one rounding
+ *   dw_lat_down [latent, d_model], dws_gate, dws_up [n_shared, d_ff_shared,
+ *               d_model] bf16 out.
+ * d_shared, ws_gate, ws_up, dws_gate, dws_up may be NULL if n_shared = 0. */
+int moe_pack_backward(const moe_dims *d, const moe_bf16 *d_pools,
+                      const int32_t *topk, const int32_t *slot,
+                      const moe_bf16 *x, const moe_bf16 *d_shared,
+                      const moe_bf16 *w_lat_down, const moe_bf16 *ws_gate,
+                      const moe_bf16 *ws_up, moe_bf16 *dz, moe_bf16 *dx,
+                      moe_bf16 *dw_lat_down, moe_bf16 *dws_gate,
+                      moe_bf16 *dws_up, void *ws, int64_t ws_bytes,
+                      void *stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(moe):
 
 
 def test_abi_version(moe):
-    assert moe.moe_abi_version() == 3
+    assert moe.moe_abi_version() == 4
 
 
 def test_capacity_matches_table(moe):
@@ -132,3 +132,21 @@ def test_balancing_calls_reject_bad_arguments(moe):
     assert L.moe_balance_bias(p, 2, 16, float("nan"), p, None) == -1
     assert L.moe_balance_bias(p, 2, 16, 1.0, None, None) == -1
     assert "bias" in L.moe_last_error().decode()
+
+
+def test_backward_calls_check_arguments(moe):
+    L = moe.lib()
+    d = _dims(moe)
+    for call in (moe.MOE_CALL_COMBINE_BWD, moe.MOE_CALL_FFN_BWD, moe.MOE_CALL_PACK_BWD):
+        assert moe.moe_workspace_bytes(d, call, 0) > 0
+    rg = _dims(moe, cap_send=0, cap_recv=0)
+    assert L.moe_workspace_bytes(ctypes.byref(rg), moe.MOE_CALL_FFN_BWD, 0) == -2
+    p = ctypes.c_void_p(256)
+    big = 1 << 40
+    assert L.moe_combine_backward(ctypes.byref(rg), *([p] * 17), p, big, None) == -2  # ragged
+    assert L.moe_combine_backward(ctypes.byref(d), *([p] * 17), p, 16, None) == -4    # ws
+    assert L.moe_expert_ffn_backward(ctypes.byref(d), *([p] * 6), None, *([p] * 4), p, big,
+                                     None) == -1                                     # d_ret
+    assert L.moe_pack_backward(ctypes.byref(d), *([p] * 13), None, big, None) == -1  # ws NULL
+    assert L.moe_route_backward(p, None, 4, 16, 17, 0, p, p, p, None) == -1          # k > E
+    assert L.moe_route_backward(p, None, 4, 16, 8, 2, p, p, p, None) == -1           # flags

@@ -1,0 +1,224 @@
+"""GPU parity of the backward calls, on inputs shared with the oracle.
+
+Each call gets exactly the inputs the oracle gets (generator tensors, oracle
+routing, sender and bank decisions, stand-in payload and gradient rows), so
+errors do not compound between stages.  bf16 outputs: per row within
+2e-2 * max|ref| of the row (weight gradients per weight row); fp32 gate and
+logit gradients: within 1e-4 of the row's scale; rows that must be zero are
+exactly zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpucase as gc
+from conftest import f64, u16
+from synth import configs, gen
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny": configs.TINY,
+    "mid": gc.MID,
+    "mid_tight": gc.with_cf(gc.MID, "1/2", "3/5"),
+    "mid_chunks": gc.chunked(gc.MID),
+}
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import dispatch_softmax_top_amd as m
+    m.lib()
+    return m
+
+
+@pytest.fixture(scope="module")
+def share():
+    from dispatch_softmax_top_amd import share
+    return share
+
+
+def _ws(moe, d, call):
+    n = moe.moe_workspace_bytes(d, call, 0)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
+
+
+def _rows(got, ref, what):
+    """bf16 [.., n] tensors compared per last-axis row."""
+    n = ref.shape[-1]
+    gc.assert_rows_close(np.ascontiguousarray(got).reshape(-1, n),
+                         np.ascontiguousarray(ref).reshape(-1, n), what)
+
+
+def _grad_rows(rng_idx, shape):
+    return u16(gen.payload_rows(int(np.prod(shape[:-1])), shape[-1], rng_idx)).reshape(shape)
+
+
+# ----------------------------------------------------------------------------
+# router
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("renorm", [False, True])
+@pytest.mark.parametrize("biased", [False, True])
+def test_route_backward(moe, orc, renorm, biased):
+    rng = np.random.default_rng(60 + renorm + 2 * biased)
+    for T, E, k in ((257, 384, 8), (64, 48, 8), (33, 1024, 32), (5, 8, 8)):
+        lg = (rng.standard_normal((T, E)) * 2).astype(np.float32)
+        bias = rng.standard_normal(E).astype(np.float32) if biased else None
+        topk, _ = orc.route_ex(lg, k, bias=bias, renorm=renorm)
+        dg = rng.standard_normal((T, k)).astype(np.float32)
+        ref = orc.route_backward(lg, topk, dg, bias=bias, renorm=renorm)
+        out = torch.full((T, E), 7.0, device="cuda")
+        moe.moe_route_backward(gc.dev(lg), gc.dev(topk), gc.dev(dg), out,
+                               bias=None if bias is None else gc.dev(bias),
+                               flags=moe.MOE_ROUTE_RENORM if renorm else 0)
+        torch.cuda.synchronize()
+        got = gc.host(out)
+        scale = np.abs(ref).max(1, keepdims=True) + 1e-30
+        assert (np.abs(got - ref) <= 1e-4 * scale).all(), (T, E, k)
+        if renorm:
+            mask = np.zeros((T, E), bool)
+            np.put_along_axis(mask, topk, True, 1)
+            assert (got[~mask] == 0).all()
+
+
+# ----------------------------------------------------------------------------
+# combine side
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_combine_backward(moe, orc, share, name):
+    cfg = CASES[name]
+    d_orc, d = orc.dims(cfg), share.make_dims(cfg)
+    T, L, D, S, Fs = cfg.T, cfg.latent, cfg.d_model, cfg.n_shared, cfg.d_ff_shared
+    s0 = gc.oracle_sender_all(orc, cfg, d_orc, n_shards=1)[0]
+    n_rows = cfg.n_ranks * cfg.n_waves * d.cap_send
+    returned = u16(gen.payload_rows(n_rows, L, 31))
+    ylat = u16(gen.payload_rows(T, L, 32))
+    d_out = u16(gen.payload_rows(T, D, 33))
+    x = u16(s0["x"])
+    wlu = u16(gen.latent_up(cfg))
+    wsg, wsu, wsd = (u16(w) for w in gen.shared(cfg))
+    ref = orc.combine_backward(d_orc, returned, s0["topk"], s0["slot"], s0["gates"], x, ylat,
+                               wlu, wsg, wsu, wsd, d_out)
+    o_dret, o_dg, o_dsh, o_dwlu, o_dwsd = ref
+
+    dev = lambda a: gc.dev(np.ascontiguousarray(a))
+    d_ret = torch.full((n_rows, L), 3.0, dtype=torch.bfloat16, device="cuda")  # poison
+    d_g = torch.full((T, cfg.top_k), 5.0, device="cuda")
+    d_sh = torch.empty((T, 2, S, Fs), dtype=torch.bfloat16, device="cuda")
+    dwlu = torch.empty((D, L), dtype=torch.bfloat16, device="cuda")
+    dwsd = torch.empty((S, D, Fs), dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine_backward(d, dev(returned), dev(s0["topk"]), dev(s0["slot"]), dev(s0["gates"]),
+                             dev(s0["fill"]), dev(x), dev(ylat), dev(wlu), dev(wsg), dev(wsu),
+                             dev(wsd), dev(d_out), d_ret, d_g, d_sh, dwlu, dwsd,
+                             _ws(moe, d, moe.MOE_CALL_COMBINE_BWD))
+    torch.cuda.synchronize()
+    g_dret = gc.host(d_ret)
+    zero = ~np.abs(f64(o_dret)).any(1)
+    assert (g_dret[zero] == 0).all()
+    _rows(g_dret[~zero], o_dret[~zero], "d_returned")
+    gd = gc.host(d_g)
+    assert (gd[s0["slot"] < 0] == 0).all()
+    # each gate gradient is a dot product of a returned row with d_ylat[t]:
+    # allow 2e-3 of max|returned| * sum|d_ylat[t]| (fp32 against fp64
+    # accumulation, and one-unit differences in the bf16 d_ylat)
+    y = f64(d_out) @ f64(wlu)
+    tol = 2e-3 * np.abs(f64(returned)).max() * np.abs(y).sum(1, keepdims=True)
+    assert (np.abs(gd - o_dg) <= tol).all()
+    _rows(gc.host(d_sh), o_dsh, "d_shared")
+    _rows(gc.host(dwlu), o_dwlu, "dw_lat_up")
+    _rows(gc.host(dwsd), o_dwsd, "dws_down")
+
+
+# ----------------------------------------------------------------------------
+# receiver side
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_expert_ffn_backward(moe, orc, share, name):
+    cfg = CASES[name]
+    rank = 1
+    d_orc, d = orc.dims(cfg), share.make_dims(cfg)
+    L, F, El = cfg.latent, cfg.d_ff, cfg.experts_per_rank
+    senders = gc.oracle_sender_all(orc, cfg, d_orc)
+    hdr, offs = gc.recv_headers(cfg, d_orc, senders, rank)
+    n = len(hdr)
+    bo = orc.bank_slots(d_orc, rank, hdr, offs)
+    nb = len(bo["bank_src"])
+    bank = u16(gen.payload_rows(nb, L, 41))
+    d_ret = u16(gen.payload_rows(n, L, 42))
+    wg, wu, wd = (u16(w) for w in gen.rank_experts(cfg, rank))
+    o_drecv, o_dwg, o_dwu, o_dwd = orc.expert_ffn_backward(d_orc, bank, bo["bank_src"],
+                                                           bo["bfill"], wg, wu, wd, d_ret)
+    dev = lambda a: gc.dev(np.ascontiguousarray(a))
+    d_recv = torch.full((n, L), 2.0, dtype=torch.bfloat16, device="cuda")
+    dwg = torch.empty((El, F, L), dtype=torch.bfloat16, device="cuda")
+    dwu = torch.empty_like(dwg)
+    dwd = torch.empty((El, L, F), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_ffn_backward(d, dev(bank), dev(bo["bank_src"]), dev(bo["bfill"]), dev(wg),
+                                dev(wu), dev(wd), dev(d_ret), d_recv, dwg, dwu, dwd,
+                                _ws(moe, d, moe.MOE_CALL_FFN_BWD))
+    torch.cuda.synchronize()
+    kept = np.zeros(n, bool)
+    kept[bo["bank_src"][bo["bank_src"] >= 0]] = True
+    g = gc.host(d_recv)
+    assert (g[~kept] == 0).all()
+    _rows(g[kept], o_drecv[kept], "d_recv")
+    for got, want, what in ((dwg, o_dwg, "dw_gate"), (dwu, o_dwu, "dw_up"), (dwd, o_dwd, "dw_down")):
+        gg = gc.host(got)
+        for j in range(El):
+            if not np.abs(f64(want[j])).any():           # an expert with no kept rows
+                assert (gg[j] == 0).all(), what
+            else:
+                _rows(gg[j], want[j], f"{what} expert {j}")
+
+
+# ----------------------------------------------------------------------------
+# sender side
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_pack_backward(moe, orc, share, name):
+    cfg = CASES[name]
+    d_orc, d = orc.dims(cfg), share.make_dims(cfg)
+    T, L, D, S, Fs = cfg.T, cfg.latent, cfg.d_model, cfg.n_shared, cfg.d_ff_shared
+    s0 = gc.oracle_sender_all(orc, cfg, d_orc, n_shards=1)[0]
+    n_rows = cfg.n_ranks * cfg.n_waves * d.cap_send
+    d_pools = u16(gen.payload_rows(n_rows, L, 51))
+    d_shared = _grad_rows(52, (T, 2, S, Fs))
+    x = u16(s0["x"])
+    wld = u16(gen.latent_down(cfg))
+    wsg, wsu, _ = (u16(w) for w in gen.shared(cfg))
+    o_dz, o_dx, o_dwld, o_dwsg, o_dwsu = orc.pack_backward(d_orc, d_pools, s0["topk"], s0["slot"],
+                                                           x, d_shared, wld, wsg, wsu)
+    dev = lambda a: gc.dev(np.ascontiguousarray(a))
+    dz = torch.empty((T, L), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    dwld = torch.empty((L, D), dtype=torch.bfloat16, device="cuda")
+    dwsg = torch.empty((S, Fs, D), dtype=torch.bfloat16, device="cuda")
+    dwsu = torch.empty_like(dwsg)
+    moe.moe_pack_backward(d, dev(d_pools), dev(s0["topk"]), dev(s0["slot"]), dev(x),
+                          dev(d_shared), dev(wld), dev(wsg), dev(wsu), dz, dx, dwld, dwsg, dwsu,
+                          _ws(moe, d, moe.MOE_CALL_PACK_BWD))
+    torch.cuda.synchronize()
+    gz = gc.host(dz)
+    none = (s0["slot"] < 0).all(1)                        # tokens with every choice dropped
+    assert (gz[none] == 0).all()
+    _rows(gz[~none], o_dz[~none], "dz")
+    _rows(gc.host(dx), o_dx, "dx")
+    _rows(gc.host(dwld), o_dwld, "dw_lat_down")
+    _rows(gc.host(dwsg), o_dwsg, "dws_gate")
+    _rows(gc.host(dwsu), o_dwsu, "dws_up")
+
+
+def test_backward_rejects_ragged_and_small_workspace(moe, share):
+    d = share.make_dims(gc.ragged(configs.TINY))
+    with pytest.raises(moe.MoeError):
+        moe.moe_workspace_bytes(d, moe.MOE_CALL_FFN_BWD, 0)
+    d = share.make_dims(configs.TINY)
+    t = torch.zeros(16, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(moe.MoeError):
+        moe.moe_pack_backward(d, t, t, t, t, t, t, t, t, t, t, t, t, t,
+                              torch.empty(16, dtype=torch.uint8, device="cuda"))
