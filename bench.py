@@ -241,6 +241,143 @@ def algorithmic_work(st):
     return w
 
 
+def backward_step(st):
+    """Backward of the same share, every call on one stream: combine side,
+    router, experts (the return exchange reversed: a loopback identity, as in
+    the forward return), pack side (the forward exchange reversed, likewise)."""
+    b = st.bwd
+    b.combine(st.rcv.ret, st.snd, st.cmb, st.x, st.wlu, st.wsg, st.wsu, st.wsd, st.d_out)
+    b.route(st.logits, st.snd, bias=None if st.bal is None else st.bal.bias)
+    b.ffn(st.rcv, st.wg, st.wu, st.wd, b.d_returned)
+    b.pack(b.d_recv, st.snd, st.x, st.wld, st.wsg, st.wsu)
+
+
+def backward_work(st):
+    """Algorithmic flops / bytes of the backward's kernels, from the actual
+    counts (the same bookkeeping as the forward's)."""
+    d = st.d
+    T, k, L, D, F, S, Fs, E = (d.T, d.top_k, d.latent, d.d_model, d.d_ff, d.n_shared,
+                               d.d_ff_shared, d.n_experts)
+    El = E // d.n_ranks
+    SF = S * Fs
+    Tp = -(-T // 32) * 32
+    Kp = -(-(d.n_waves * d.cap_recv) // 32) * 32
+    kept_s = int(st.snd.fill.sum())
+    kept_r = int(st.rcv.bfill.sum())
+    n_slots = int(st.snd.pools.shape[0])
+    f = lambda v: ("flop", float(v))
+    b = lambda v: ("byte", float(v))
+    return {
+        "gemm_bwd_d_ylat": f(2 * T * D * (L + SF)),
+        "gemm_shared_swiglu_bwd": f(4 * T * D * SF),
+        "gemm_bwd_dw_lat_up": f(2 * D * L * T),
+        "gemm_bwd_dws_down": f(2 * D * SF * T),
+        "gemm_bwd_d_h": f(2 * kept_r * L * F),
+        "gemm_expert_swiglu_bwd": f(4 * kept_r * L * F),
+        "gemm_bwd_d_u": f(2 * kept_r * 2 * F * L),
+        "gemm_bwd_dw_down": f(2 * L * F * kept_r),
+        "gemm_bwd_dw_gate": f(2 * F * L * kept_r),
+        "gemm_bwd_dw_up": f(2 * F * L * kept_r),
+        "gemm_bwd_dx": f(2 * T * D * (L + 2 * SF)),
+        "gemm_bwd_dw_lat_down": f(2 * L * D * T),
+        "gemm_bwd_dws_gate": f(2 * SF * D * T),
+        "gemm_bwd_dws_up": f(2 * SF * D * T),
+        # d_ylat row + kept returned rows read; every d_returned row written
+        "combine_backward": b(T * L * 2 + kept_s * L * 2 + n_slots * L * 2 + T * k * 16),
+        "route_backward": b(T * E * 8 + T * k * 12),
+        "gather_bank_grad": b(kept_r * L * 4),
+        "combine_gather": b(kept_s * L * 2 + T * k * 8 + T * L * 2),
+        # transposes: elements read + elements written (padding included)
+        "transpose_w_lat_up": b(4 * D * L), "transpose_ws_down": b(4 * D * SF),
+        "transpose_d_out": b(2 * T * D + 2 * D * Tp), "transpose_ylat": b(2 * T * L + 2 * L * Tp),
+        "transpose_h_shared": b(2 * T * SF + 2 * SF * Tp),
+        "transpose_w_down": b(4 * El * L * F), "transpose_w_gate": b(4 * El * L * F),
+        "transpose_w_up": b(4 * El * L * F),
+        "transpose_bank_dy": b(2 * kept_r * L + 2 * El * L * Kp),
+        "transpose_bank_h": b(2 * kept_r * F + 2 * El * F * Kp),
+        "transpose_bank_dab": b(4 * kept_r * F + 4 * El * F * Kp),
+        "transpose_bank_u": b(2 * kept_r * L + 2 * El * L * Kp),
+        "transpose_w_lat_down": b(4 * L * D), "transpose_ws_gate": b(4 * SF * D),
+        "transpose_ws_up": b(4 * SF * D), "transpose_x": b(2 * T * D + 2 * D * Tp),
+        "transpose_dz": b(2 * T * L + 2 * L * Tp),
+        "transpose_d_shared": b(4 * T * SF + 4 * SF * Tp),
+    }
+
+
+def kernel_table(prof, work, steps):
+    """Per-kernel entries from the library's event timing; a split GEMM's
+    rate is taken over the kernel and its _tail launch."""
+    per_step = {name: tot / steps for name, (tot, n) in prof.items()}
+    kernels = {}
+    for name, (tot, n) in prof.items():
+        avg = tot / n
+        kind, amount = work.get(name, (None, 0.0))
+        entry = {"avg_us": round(avg * 1e3, 3), "launches_per_step": n // steps}
+        tail = name + "_tail"
+        if tail in per_step:
+            entry["tail_us"] = round(per_step[tail] * 1e3, 3)
+            avg = per_step[name] + per_step[tail]
+            entry["with_tail_us"] = round(avg * 1e3, 3)
+        if kind == "flop":
+            entry["tflops"] = round(amount / (avg * 1e-3) / 1e12, 2)
+            entry["mfma_frac"] = round(entry["tflops"] / PEAK_BF16_TFLOPS, 4)
+        elif kind == "byte":
+            entry["gbs"] = round(amount / (avg * 1e-3) / 1e9, 1)
+            entry["hbm_frac"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[name] = entry
+    return kernels, per_step
+
+
+def bench_backward(st, steps, warmup):
+    """Backward timing (its own timed region, after the forward's), the
+    per-kernel pass and the roofline of its dominant kernel."""
+    import torch
+    import dispatch_softmax_top_amd as moe
+    from dispatch_softmax_top_amd import share
+    from synth import gen
+    d = st.d
+    st.bwd = share.Backward(d, st.n_recv_rows)
+    # stand-in gradient of the layer output: seeded N(0, 1) bf16
+    st.d_out = gen.payload_rows(d.T, d.d_model, 71, "cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        backward_step(st)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        backward_step(st)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    log(f"bench: backward {steps} steps, {ms:.3f} ms/step")
+    moe.moe_profile_reset()
+    moe.moe_profile_enable(True)
+    for _ in range(steps):
+        backward_step(st)
+    moe.moe_profile_collect()
+    moe.moe_profile_enable(False)
+    work = backward_work(st)
+    kernels, per_step = kernel_table(moe.moe_profile_read(), work, steps)
+    gemms = [n for n, (kind, _) in work.items() if kind == "flop" and n in per_step]
+    dom = max(gemms, key=lambda n: per_step[n] + per_step.get(n + "_tail", 0.0))
+    dom_s = (per_step[dom] + per_step.get(dom + "_tail", 0.0)) * 1e-3
+    achieved = work[dom][1] / dom_s / 1e12
+    flops = sum(a for kind, a in work.values() if kind == "flop")
+    return {
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(d.T / (ms * 1e-3), 1),
+        "tflops_per_step": round(flops / 1e12, 4),
+        "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "data": "d_out: seeded N(0,1) bf16; both exchanges reversed as loopback identities",
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4)},
+        "path_roofline": path_roofline(kernels, work, ms),
+        "kernels": kernels,
+    }
+
+
 TRAFFIC_SOURCES = ("dispatch_softmax_top_amd/csrc/gemm.h", "dispatch_softmax_top_amd/csrc/gemm.hip",
                    "dispatch_softmax_top_amd/csrc/common.h")
 
@@ -344,6 +481,8 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="also time steps that each follow a 1 GiB write sweep (cold caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward measurement (fixed capacities only)")
     ap.add_argument("--balance-alpha", type=float, default=None, metavar="ALPHA",
                     help="quantile balancing on: route with the bias -ALPHA (f - 1/E) from the "
                          "selection counts of the past --balance-window batches")
@@ -424,24 +563,7 @@ def main():
     # A GEMM whose last round was split along K finishes in a second kernel
     # (<name>_tail: sum of the partial tiles and the epilogue); its rate is
     # taken over both launches.
-    per_step = {name: tot / args.steps for name, (tot, n) in prof.items()}
-    kernels = {}
-    for name, (tot, n) in prof.items():
-        avg = tot / n
-        kind, amount = work.get(name, (None, 0.0))
-        entry = {"avg_us": round(avg * 1e3, 3), "launches_per_step": n // args.steps}
-        tail = name + "_tail"
-        if tail in per_step:
-            entry["tail_us"] = round(per_step[tail] * 1e3, 3)
-            avg = per_step[name] + per_step[tail]
-            entry["with_tail_us"] = round(avg * 1e3, 3)
-        if kind == "flop":
-            entry["tflops"] = round(amount / (avg * 1e-3) / 1e12, 2)
-            entry["mfma_frac"] = round(entry["tflops"] / PEAK_BF16_TFLOPS, 4)
-        elif kind == "byte":
-            entry["gbs"] = round(amount / (avg * 1e-3) / 1e9, 1)
-            entry["hbm_frac"] = round(entry["gbs"] / PEAK_HBM_GBS, 4)
-        kernels[name] = entry
+    kernels, per_step = kernel_table(prof, work, args.steps)
     dom = "gemm_expert_swiglu"
     dom_avg_s = (per_step[dom] + per_step.get(dom + "_tail", 0.0)) * 1e-3
     achieved = work[dom][1] / dom_avg_s / 1e12
@@ -464,6 +586,12 @@ def main():
         cpu = {"value": round(val, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
                "sample": desc, "wall_s": round(time.time() - t0, 1),
                "cpu_model": host_cpu(), "host_cpus": os.cpu_count()}
+
+    backward = None
+    if not args.no_backward and d.cap_send:
+        backward = bench_backward(st, args.steps, args.warmup)
+        backward["train_step_ms"] = round(ms + backward["ms_per_step"], 4)
+        backward["train_tokens_per_s"] = round(d.T / ((ms + backward["ms_per_step"]) * 1e-3), 1)
 
     cold = None
     if args.cold:
@@ -506,6 +634,7 @@ def main():
         "rates": {"assignments_per_s": round(d.T * d.top_k / (ms * 1e-3), 1),
                   "kept_rows_per_s": round(kept_r / (ms * 1e-3), 1)},
         "cold_cache": cold,
+        "backward": backward,
         "drops": drops,
         "kernels": kernels,
     }

@@ -164,7 +164,8 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
       u32x4 o;
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const float y0 = __uint_as_float(v[c][h] << 16), y1 = __uint_as_float(v[c][h] & 0xffff0000u);
+        const float y0 = __uint_as_float(v[c][h] << 16),
+                                         y1 = __uint_as_float(v[c][h] & 0xffff0000u);
         dot = fmaf(__uint_as_float(r[c][h] << 16), y0, dot);
         dot = fmaf(__uint_as_float(r[c][h] & 0xffff0000u), y1, dot);
         o[h] = pack_bf16x2(g * y0, g * y1);
@@ -365,7 +366,8 @@ extern "C" int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
     MOE_TRY(transpose("transpose_ws_down", ws_down, Fs, (int64_t)D * Fs, w.Bt + (int64_t)L * D, D,
                       (int64_t)Fs * D, D, Fs, D, S, s));
   DenseSeg g1{d_out, D, w.Bt, D, D};
-  MOE_TRY(gemm_nt("gemm_bwd_d_ylat", T, L + SF, 1, &g1, w.C1, L + SF, w.part, s));
+  MOE_TRY(gemm_nt("gemm_bwd_d_ylat", "gemm_bwd_d_ylat_tail", T, L + SF, 1, &g1, w.C1, L + SF,
+                  w.part, s));
   // shared experts: recompute, SwiGLU gradient -> d_shared, h_s
   if (sh)
     MOE_TRY(gemm_shared_swiglu_bwd(T, x, D, D, ws_gate, ws_up, S, Fs, w.C1, L + SF, L, w.Hs,
@@ -386,12 +388,13 @@ extern "C" int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
   MOE_TRY(transpose("transpose_d_out", d_out, D, 0, w.doT, Tp, 0, T, D, Tp, 1, s));
   MOE_TRY(transpose("transpose_ylat", ylat, L, 0, w.ylT, Tp, 0, T, L, Tp, 1, s));
   DenseSeg g2{w.doT, Tp, w.ylT, Tp, Tp};
-  MOE_TRY(gemm_nt("gemm_bwd_dw_lat_up", D, L, 1, &g2, dw_lat_up, L, w.part, s));
+  MOE_TRY(gemm_nt("gemm_bwd_dw_lat_up", "gemm_bwd_dw_lat_up_tail", D, L, 1, &g2, dw_lat_up, L,
+                  w.part, s));
   if (!sh) return MOE_OK;
   MOE_TRY(transpose("transpose_h_shared", w.Hs, SF, 0, w.HsT, Tp, 0, T, SF, Tp, 1, s));
   DenseSeg g3{w.doT, Tp, w.HsT, Tp, Tp};
-  return gemm_nt_batched("gemm_bwd_dws_down", D, Fs, g3, S, 0, (int64_t)Fs * Tp, dws_down, Fs,
-                         (int64_t)D * Fs, w.part, s);
+  return gemm_nt_batched("gemm_bwd_dws_down", "gemm_bwd_dws_down_tail", D, Fs, g3, S, 0,
+                         (int64_t)Fs * Tp, dws_down, Fs, (int64_t)D * Fs, w.part, s);
 }
 
 extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
@@ -431,13 +434,15 @@ extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
   }));
   MOE_TRY(launch("iota", iota_kernel, dim3((unsigned)cdiv(nb, 256)), dim3(256), 0, s, w.iota, nb));
   // d_h = dy . W_d (grouped, bank order)
-  MOE_TRY(gemm_grouped_nt("gemm_bwd_d_h", *d, w.dY, L, bfill, w.iota, nb, w.WdT, F, w.dH, nb,
+  MOE_TRY(gemm_grouped_nt("gemm_bwd_d_h", "gemm_bwd_d_h_tail", *d, w.dY, L, bfill, w.iota, nb,
+                          w.WdT, F, w.dH, nb,
                           w.part, s));
   // a, b recomputed; d_a | d_b and h
   MOE_TRY(gemm_expert_swiglu_bwd(*d, bank, bfill, nb, w_gate, w_up, w.dH, w.Hb, w.dAB, w.part, s));
   // d_u = d_a . W_g + d_b . W_u, scattered to the receive rows; others zero
   MOE_TRY(ret_rows_mark(bank_src, nb, w.flags, nr, s));
-  MOE_TRY(gemm_grouped_nt("gemm_bwd_d_u", *d, w.dAB, 2 * F, bfill, bank_src, nb, w.WguT, L, d_recv,
+  MOE_TRY(gemm_grouped_nt("gemm_bwd_d_u", "gemm_bwd_d_u_tail", *d, w.dAB, 2 * F, bfill, bank_src,
+                          nb, w.WguT, L, d_recv,
                           nr, w.part, s));
   MOE_TRY(ret_rows_zero_unmarked(w.flags, d_recv, L, nr, s));
   // weight gradients: per local expert, summed over its rows of every wave
@@ -451,13 +456,16 @@ extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
   MOE_TRY(transpose("transpose_bank_u", bank, L, 0, w.UT, Kp, (int64_t)L * Kp, nw, L, Kp, El, s,
                     bfill, Cr, El));
   DenseSeg gd{w.dYT, Kp, w.HT, Kp, Kp};
-  MOE_TRY(gemm_nt_batched("gemm_bwd_dw_down", L, F, gd, El, (int64_t)L * Kp, (int64_t)F * Kp,
+  MOE_TRY(gemm_nt_batched("gemm_bwd_dw_down", "gemm_bwd_dw_down_tail", L, F, gd, El,
+                          (int64_t)L * Kp, (int64_t)F * Kp,
                           dw_down, F, WL, w.part, s));
   DenseSeg gg{w.dABT, Kp, w.UT, Kp, Kp};
-  MOE_TRY(gemm_nt_batched("gemm_bwd_dw_gate", F, L, gg, El, (int64_t)2 * F * Kp, (int64_t)L * Kp,
+  MOE_TRY(gemm_nt_batched("gemm_bwd_dw_gate", "gemm_bwd_dw_gate_tail", F, L, gg, El,
+                          (int64_t)2 * F * Kp, (int64_t)L * Kp,
                           dw_gate, L, WL, w.part, s));
   DenseSeg gu{w.dABT + (int64_t)F * Kp, Kp, w.UT, Kp, Kp};
-  return gemm_nt_batched("gemm_bwd_dw_up", F, L, gu, El, (int64_t)2 * F * Kp, (int64_t)L * Kp,
+  return gemm_nt_batched("gemm_bwd_dw_up", "gemm_bwd_dw_up_tail", F, L, gu, El,
+                         (int64_t)2 * F * Kp, (int64_t)L * Kp,
                          dw_up, L, WL, w.part, s);
 }
 
@@ -495,16 +503,18 @@ extern "C" int moe_pack_backward(const moe_dims *d, const moe_bf16 *d_pools, con
     MOE_TRY(transpose("transpose_ws_gate", ws_gate, D, 0, w.BsT, 2 * SF, 0, SF, D, SF, 1, s));
     MOE_TRY(transpose("transpose_ws_up", ws_up, D, 0, w.BsT + SF, 2 * SF, 0, SF, D, SF, 1, s));
   }
-  MOE_TRY(gemm_nt("gemm_bwd_dx", T, D, sh ? 2 : 1, gx, dx, D, w.part, s));
+  MOE_TRY(gemm_nt("gemm_bwd_dx", "gemm_bwd_dx_tail", T, D, sh ? 2 : 1, gx, dx, D, w.part, s));
   // weight gradients, summed over tokens
   MOE_TRY(transpose("transpose_x", x, D, 0, w.xT, Tp, 0, T, D, Tp, 1, s));
   MOE_TRY(transpose("transpose_dz", dz, L, 0, w.dzT, Tp, 0, T, L, Tp, 1, s));
   DenseSeg gl{w.dzT, Tp, w.xT, Tp, Tp};
-  MOE_TRY(gemm_nt("gemm_bwd_dw_lat_down", L, D, 1, &gl, dw_lat_down, D, w.part, s));
+  MOE_TRY(gemm_nt("gemm_bwd_dw_lat_down", "gemm_bwd_dw_lat_down_tail", L, D, 1, &gl, dw_lat_down,
+                  D, w.part, s));
   if (!sh) return MOE_OK;
   MOE_TRY(transpose("transpose_d_shared", d_shared, 2 * SF, 0, w.dshT, Tp, 0, T, 2 * SF, Tp, 1, s));
   DenseSeg gsg{w.dshT, Tp, w.xT, Tp, Tp};
-  MOE_TRY(gemm_nt("gemm_bwd_dws_gate", SF, D, 1, &gsg, dws_gate, D, w.part, s));
+  MOE_TRY(gemm_nt("gemm_bwd_dws_gate", "gemm_bwd_dws_gate_tail", SF, D, 1, &gsg, dws_gate, D,
+                  w.part, s));
   DenseSeg gsu{w.dshT + (int64_t)SF * Tp, Tp, w.xT, Tp, Tp};
-  return gemm_nt("gemm_bwd_dws_up", SF, D, 1, &gsu, dws_up, D, w.part, s);
+  return gemm_nt("gemm_bwd_dws_up", "gemm_bwd_dws_up_tail", SF, D, 1, &gsu, dws_up, D, w.part, s);
 }

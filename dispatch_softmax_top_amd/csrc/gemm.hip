@@ -919,27 +919,27 @@ int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_o
                     bank_src, n_bank_rows, wd, d.latent, ret, n_ret, part, s);
 }
 
-int gemm_grouped_nt(const char *name, const moe_dims &d, const uint16_t *A, int K,
-                    const int32_t *bfill, const int32_t *dst, int64_t n_bank_rows,
-                    const uint16_t *B, int N, uint16_t *out, int64_t n_out, float *part,
-                    hipStream_t s) {
-  return grouped_nt(name, name, d, A, K, nullptr, bfill, dst, n_bank_rows, B, N, out, n_out, part,
-                    s);
+int gemm_grouped_nt(const char *name, const char *tail_name, const moe_dims &d,
+                    const uint16_t *A, int K, const int32_t *bfill, const int32_t *dst,
+                    int64_t n_bank_rows, const uint16_t *B, int N, uint16_t *out, int64_t n_out,
+                    float *part, hipStream_t s) {
+  return grouped_nt(name, tail_name, d, A, K, nullptr, bfill, dst, n_bank_rows, B, N, out, n_out,
+                    part, s);
 }
 
-int gemm_nt(const char *name, int M, int N, int nseg, const DenseSeg *segs, uint16_t *C,
-            int64_t ldc, float *part, hipStream_t s) {
+int gemm_nt(const char *name, const char *tail_name, int M, int N, int nseg,
+            const DenseSeg *segs, uint16_t *C, int64_t ldc, float *part, hipStream_t s) {
   static void (*const k[2])(DenseArgs) = {gemm_nt_kernel<1, false>, gemm_nt_kernel<2, false>};
   if (nseg < 1 || nseg > 2) return fail(MOE_ERR_INVALID, "%s: bad segment count", name);
-  return dense(name, name, k[nseg - 1], M, N, nseg, segs, C, ldc, part, s);
+  return dense(name, tail_name, k[nseg - 1], M, N, nseg, segs, C, ldc, part, s);
 }
 
-int gemm_nt_batched(const char *name, int M, int N, const DenseSeg &seg, int nbatch, int64_t bsA,
-                    int64_t bsB, uint16_t *C, int64_t ldc, int64_t bsC, float *part,
-                    hipStream_t s) {
-  if (nbatch == 1) return gemm_nt(name, M, N, 1, &seg, C, ldc, part, s);
-  return dense(name, name, gemm_nt_kernel<1, true>, M, N, 1, &seg, C, ldc, part, s, nbatch, bsA,
-               bsB, bsC);
+int gemm_nt_batched(const char *name, const char *tail_name, int M, int N, const DenseSeg &seg,
+                    int nbatch, int64_t bsA, int64_t bsB, uint16_t *C, int64_t ldc, int64_t bsC,
+                    float *part, hipStream_t s) {
+  if (nbatch == 1) return gemm_nt(name, tail_name, M, N, 1, &seg, C, ldc, part, s);
+  return dense(name, tail_name, gemm_nt_kernel<1, true>, M, N, 1, &seg, C, ldc, part, s, nbatch,
+               bsA, bsB, bsC);
 }
 
 }  // namespace moe

@@ -70,12 +70,13 @@ int combine_gather_rows(const moe_dims &d, const uint16_t *rows, const int64_t *
 int64_t bwd_ws_bytes(const moe_dims &d, int call);
 
 // C[M, N] (ldc) = sum over nseg <= 2 segments of A . B^T (bf16 out).
-int gemm_nt(const char *name, int M, int N, int nseg, const DenseSeg *segs, uint16_t *C,
-            int64_t ldc, float *part, hipStream_t s);
+// tail_name: the launch name of the kernel finishing a split last round.
+int gemm_nt(const char *name, const char *tail_name, int M, int N, int nseg,
+            const DenseSeg *segs, uint16_t *C, int64_t ldc, float *part, hipStream_t s);
 // nbatch products of one segment: product b at A + b*bsA, B + b*bsB, C + b*bsC.
-int gemm_nt_batched(const char *name, int M, int N, const DenseSeg &seg, int nbatch, int64_t bsA,
-                    int64_t bsB, uint16_t *C, int64_t ldc, int64_t bsC, float *part,
-                    hipStream_t s);
+int gemm_nt_batched(const char *name, const char *tail_name, int M, int N, const DenseSeg &seg,
+                    int nbatch, int64_t bsA, int64_t bsB, uint16_t *C, int64_t ldc, int64_t bsC,
+                    float *part, hipStream_t s);
 // Shared experts recomputed with the SwiGLU gradient epilogue: dH[:, dh_col0 +
 // s*F + f] in, H = h_s [M, S*F] and AB [M, 2*S*F] (d_a of every expert, then
 // d_b) out.
@@ -90,9 +91,9 @@ int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int32_
                            hipStream_t s);
 // Grouped over the bank's groups (fixed mode): out[dst[r]] = A[r] . B_j^T,
 // A [bank rows][K], B [E_l][N][K].
-int gemm_grouped_nt(const char *name, const moe_dims &d, const uint16_t *A, int K,
-                    const int32_t *bfill, const int32_t *dst, int64_t n_bank_rows,
-                    const uint16_t *B, int N, uint16_t *out, int64_t n_out, float *part,
-                    hipStream_t s);
+int gemm_grouped_nt(const char *name, const char *tail_name, const moe_dims &d,
+                    const uint16_t *A, int K, const int32_t *bfill, const int32_t *dst,
+                    int64_t n_bank_rows, const uint16_t *B, int N, uint16_t *out, int64_t n_out,
+                    float *part, hipStream_t s);
 
 }  // namespace moe

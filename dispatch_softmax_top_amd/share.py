@@ -154,6 +154,60 @@ class Combiner:
                              self.ws_shared, stream)
 
 
+class Backward:
+    """Gradient buffers and workspaces of one rank's share (fixed mode): the
+    sender's combine and pack sides, the receiver's experts and the router.
+    On one GPU both exchanges are loopbacks, read as identities like the
+    forward return: the receiver's return-row gradients are the sender's
+    d_returned, and the sender's pool-row gradients are the receiver's d_recv."""
+
+    def __init__(self, d, n_recv_rows, device="cuda"):
+        self.d = d
+        dev = torch.device(device)
+        T, L_, D, E = d.T, d.latent, d.d_model, d.n_experts
+        S, Fs, F, El = d.n_shared, d.d_ff_shared, d.d_ff, experts_per_rank(d)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        self.d_returned = torch.empty(n_recv_rows, L_, **bf)
+        self.d_gates = torch.empty(T, d.top_k, dtype=torch.float32, device=dev)
+        self.d_logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+        self.d_shared = torch.empty(T, 2, max(S, 1), Fs, **bf)
+        self.dw_lat_up = torch.empty(D, L_, **bf)
+        self.dws_down = torch.empty(max(S, 1), D, Fs, **bf)
+        self.d_recv = torch.empty(n_recv_rows, L_, **bf)
+        self.dw_gate = torch.empty(El, F, L_, **bf)
+        self.dw_up = torch.empty(El, F, L_, **bf)
+        self.dw_down = torch.empty(El, L_, F, **bf)
+        self.dz = torch.empty(T, L_, **bf)
+        self.dx = torch.empty(T, D, **bf)
+        self.dw_lat_down = torch.empty(L_, D, **bf)
+        self.dws_gate = torch.empty(max(S, 1), Fs, D, **bf)
+        self.dws_up = torch.empty(max(S, 1), Fs, D, **bf)
+        self.ws_combine = _ws(d, L.MOE_CALL_COMBINE_BWD, 0, dev)
+        self.ws_ffn = _ws(d, L.MOE_CALL_FFN_BWD, 0, dev)
+        self.ws_pack = _ws(d, L.MOE_CALL_PACK_BWD, 0, dev)
+
+    def combine(self, returned, snd: Sender, cmb: Combiner, x, w_lat_up, ws_gate, ws_up, ws_down,
+                d_out, stream=None):
+        L.moe_combine_backward(self.d, returned, snd.topk, snd.slot, snd.gates, snd.fill, x,
+                               cmb.ylat, w_lat_up, ws_gate, ws_up, ws_down, d_out,
+                               self.d_returned, self.d_gates, self.d_shared, self.dw_lat_up,
+                               self.dws_down, self.ws_combine, stream)
+
+    def route(self, logits, snd: Sender, bias=None, renorm=False, stream=None):
+        L.moe_route_backward(logits, snd.topk, self.d_gates, self.d_logits, bias=bias,
+                             stream=stream, flags=L.MOE_ROUTE_RENORM if renorm else 0)
+
+    def ffn(self, rcv: Receiver, w_gate, w_up, w_down, d_ret, stream=None):
+        L.moe_expert_ffn_backward(self.d, rcv.bank, rcv.bank_src, rcv.bfill, w_gate, w_up, w_down,
+                                  d_ret, self.d_recv, self.dw_gate, self.dw_up, self.dw_down,
+                                  self.ws_ffn, stream)
+
+    def pack(self, d_pools, snd: Sender, x, w_lat_down, ws_gate, ws_up, stream=None):
+        L.moe_pack_backward(self.d, d_pools, snd.topk, snd.slot, x, self.d_shared, w_lat_down,
+                            ws_gate, ws_up, self.dz, self.dx, self.dw_lat_down, self.dws_gate,
+                            self.dws_up, self.ws_pack, stream)
+
+
 # ----------------------------------------------------------------------------
 # loopback exchange (harness side, stand-in for the all-to-all)
 # ----------------------------------------------------------------------------

@@ -222,3 +222,99 @@ def test_backward_rejects_ragged_and_small_workspace(moe, share):
     with pytest.raises(moe.MoeError):
         moe.moe_pack_backward(d, t, t, t, t, t, t, t, t, t, t, t, t, t,
                               torch.empty(16, dtype=torch.uint8, device="cuda"))
+
+
+# ----------------------------------------------------------------------------
+# whole backward chain on each side, after each side's own forward chain
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "mid_chunks"])
+def test_backward_chain(moe, orc, share, name):
+    """Forward then backward for rank 0 on each side: GPU calls only on the
+    GPU, oracle calls only in the oracle, both exchanges as loopback
+    identities.  Upstream differences of a bf16 unit propagate, so rows are
+    compared with the same per-row tolerance."""
+    cfg = CASES[name]
+    rank = 0
+    d_orc, d = orc.dims(cfg), share.make_dims(cfg)
+    wld, wlu = gen.latent_down(cfg), gen.latent_up(cfg)
+    wg, wu, wd = gen.rank_experts(cfg, rank)
+    wsg, wsu, wsd = gen.shared(cfg)
+    cu = lambda t: t.cuda()
+    # GPU forward
+    pools = []
+    for s in range(cfg.n_shards):
+        x, lg = gc.shard_inputs(cfg, s)
+        snd = share.Sender(d)
+        snd.route(lg.cuda())
+        snd.pack(x.cuda(), cu(wld))
+        pools.append(snd.pools)
+        if s == rank:
+            own, x_own, lg_own = snd, x, lg
+    recv = share.loopback_recv_fixed(d, pools, rank)
+    rcv = share.Receiver(d, recv.shape[0])
+    rcv.bank_rows(rank, recv, None)
+    rcv.ffn(cu(wg), cu(wu), cu(wd))
+    cmb = share.Combiner(d)
+    cmb.combine(rcv.ret, None, own, cu(x_own), cu(wlu), cu(wsg), cu(wsu), cu(wsd))
+    # GPU backward
+    d_out = gen.payload_rows(cfg.T, cfg.d_model, 61)
+    b = share.Backward(d, recv.shape[0])
+    b.combine(rcv.ret, own, cmb, cu(x_own), cu(wlu), cu(wsg), cu(wsu), cu(wsd), cu(d_out))
+    b.route(lg_own.cuda(), own)
+    b.ffn(rcv, cu(wg), cu(wu), cu(wd), b.d_returned)
+    b.pack(b.d_recv, own, cu(x_own), cu(wld), cu(wsg), cu(wsu))
+    torch.cuda.synchronize()
+
+    # oracle forward
+    W, Cs = cfg.n_waves, d.cap_send
+    o_pools, s0 = [], None
+    for s in range(cfg.n_shards):
+        x, lg = gc.shard_inputs(cfg, s)
+        topk, gates = orc.route(lg.numpy(), cfg.top_k)
+        z = orc.latent(u16(x), u16(wld))
+        sn = orc.sender(d_orc, topk)
+        o_pools.append(orc.pack_rows(d_orc, z, topk, sn["slot"], sn["pool_offsets"]))
+        if s == rank:
+            s0 = dict(topk=topk, gates=gates, **sn)
+    o_recv = np.concatenate([o_pools[s][(rank * W + w) * Cs:(rank * W + w + 1) * Cs]
+                             for s in range(cfg.n_shards) for w in range(W)])
+    bo = orc.bank_slots(d_orc, rank, orc.headers(o_recv, d.latent), None)
+    o_bank = orc.bank_rows(d_orc, o_recv, bo["bank_offsets"], bo["bank_src"], bo["bfill"])
+    ex = [u16(w) for w in (wg, wu, wd)]
+    o_ret = orc.expert_ffn(d_orc, o_bank, bo["bank_offsets"], bo["bank_src"], bo["bfill"], *ex,
+                           len(o_recv))
+    sh = [u16(w) for w in (wsg, wsu, wsd)]
+    o_ylat, _ = orc.combine(d_orc, o_ret, None, s0["topk"], s0["slot"], s0["gates"], u16(x_own),
+                            u16(wlu), *sh)
+    # oracle backward
+    o_dret, o_dg, o_dsh, o_dwlu, o_dwsd = orc.combine_backward(
+        d_orc, o_ret, s0["topk"], s0["slot"], s0["gates"], u16(x_own), o_ylat, u16(wlu), *sh,
+        u16(d_out))
+    o_dl = orc.route_backward(lg_own.numpy(), s0["topk"], o_dg)
+    o_drecv, o_dwg, o_dwu, o_dwd = orc.expert_ffn_backward(d_orc, o_bank, bo["bank_src"],
+                                                           bo["bfill"], *ex, o_dret)
+    o_dz, o_dx, o_dwld, o_dwsg, o_dwsu = orc.pack_backward(d_orc, o_drecv, s0["topk"], s0["slot"],
+                                                           u16(x_own), o_dsh, u16(wld), sh[0], sh[1])
+
+    assert np.array_equal(gc.host(own.slot), s0["slot"])
+    assert np.array_equal(gc.host(rcv.bank_src), bo["bank_src"])
+    for got, want, what in ((b.d_returned, o_dret, "d_returned"), (b.d_recv, o_drecv, "d_recv"),
+                            (b.dz, o_dz, "dz")):
+        g = gc.host(got)
+        nz = np.abs(f64(want)).any(1)
+        assert (g[~nz] == 0).all(), what
+        _rows(g[nz], want[nz], what)
+    for got, want, what in ((b.d_shared, o_dsh, "d_shared"), (b.dx, o_dx, "dx"),
+                            (b.dw_lat_up, o_dwlu, "dw_lat_up"), (b.dws_down, o_dwsd, "dws_down"),
+                            (b.dw_lat_down, o_dwld, "dw_lat_down"), (b.dws_gate, o_dwsg, "dws_gate"),
+                            (b.dws_up, o_dwsu, "dws_up"), (b.dw_gate, o_dwg, "dw_gate"),
+                            (b.dw_up, o_dwu, "dw_up"), (b.dw_down, o_dwd, "dw_down")):
+        g, w_ = gc.host(got), np.asarray(want)
+        nz = np.abs(f64(w_)).reshape(-1, w_.shape[-1]).any(1)
+        g2 = g.reshape(-1, w_.shape[-1])
+        assert (g2[~nz] == 0).all(), what
+        _rows(g2[nz], w_.reshape(-1, w_.shape[-1])[nz], what)
+    gl = gc.host(b.d_logits)
+    scale = np.abs(o_dl).max(1, keepdims=True) + 1e-30
+    assert (np.abs(gl - o_dl) <= 2e-2 * scale).all()
