@@ -448,10 +448,22 @@ __device__ __forceinline__ void swiglu_store(const SwigluArgs &g, RowOf row_of, 
                                              int h_col0, const GAcc &acc) {
   const int f0 = ft * 128;
 #pragma unroll
-  for (int i = 0; i < GTM; ++i)
+  for (int i = 0; i < GTM; ++i) {
+    if (ONLY >= 0 && i != ONLY) continue;
+    // BWD: the row group's d_h values are all loaded before the first store
+    // (the stores could alias them, so loads after a store would wait for it)
+    float gh[16][GTN / 2];
+    if constexpr (BWD) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = g_acc_row(i, v);
+        const uint16_t *dh = g.dH + row_of(min(m, rows - 1)) * g.ld_dh + g.dh_col0 + h_col0 + f0;
+#pragma unroll
+        for (int p = 0; p < GTN / 2; ++p) gh[v][p] = bf16_to_f32(dh[g_swiglu_col(p)]);
+      }
+    }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      if (ONLY >= 0 && i != ONLY) continue;
       const int m = g_acc_row(i, v);
       if (m >= rows) continue;
       const int64_t r = row_of(m);
@@ -463,21 +475,20 @@ __device__ __forceinline__ void swiglu_store(const SwigluArgs &g, RowOf row_of, 
           h[g_swiglu_col(p)] = f32_to_bf16(silu_f32(a) * b);
         }
       } else {
-        const uint16_t *dh = g.dH + r * g.ld_dh + g.dh_col0 + h_col0 + f0;
         uint16_t *da = g.AB + r * g.ld_ab + h_col0 + f0;
 #pragma unroll
         for (int p = 0; p < GTN / 2; ++p) {
           const float a = acc[i][2 * p][v], b = acc[i][2 * p + 1][v];
           const int c = g_swiglu_col(p);
-          const float gh = bf16_to_f32(dh[c]);
           const float s = 1.0f / (1.0f + __expf(-a));
           const float sa = silu_f32(a);
           h[c] = f32_to_bf16(sa * b);
-          da[c] = f32_to_bf16(gh * b * (s * (1.0f + a * (1.0f - s))));
-          da[g.ab_off + c] = f32_to_bf16(gh * sa);
+          da[c] = f32_to_bf16(gh[v][p] * b * (s * (1.0f + a * (1.0f - s))));
+          da[g.ab_off + c] = f32_to_bf16(gh[v][p] * sa);
         }
       }
     }
+  }
 }
 
 template <bool BWD>
