@@ -81,6 +81,19 @@ def lib():
                                                _u16p, i64, _u16p, _u16p, _u16p, _u16p]),
             "orc_pack_backward": (None, [dp, _u16p, _i32p, _i32p, _u16p, _u16p, _u16p, _u16p,
                                          _u16p, _u16p, _u16p, _u16p, _u16p, _u16p]),
+            "orc_combine_backward_tokens": (None, [dp, _u16p, _i32p, _i32p, _f32p, _u16p, _u16p,
+                                                   _u16p, _u16p, _u16p, _u16p, _i64p, i64, _u16p,
+                                                   _f32p, _u16p]),
+            "orc_combine_wgrad_entries": (None, [dp, _u16p, _u16p, _u16p, _u16p, _u16p, i32,
+                                                 _i32p, _i32p, _i32p, i64, _u16p]),
+            "orc_expert_ffn_backward_rows": (None, [dp, _u16p, _i32p, _u16p, _u16p, _u16p, _u16p,
+                                                    _i64p, i64, _u16p]),
+            "orc_expert_wgrad_entries": (None, [dp, _u16p, _i32p, _i32p, _u16p, _u16p, _u16p,
+                                                _u16p, i32, i32, _i32p, _i32p, i64, _u16p]),
+            "orc_pack_backward_tokens": (None, [dp, _u16p, _i32p, _i32p, _u16p, _u16p, _u16p,
+                                                _u16p, _i64p, i64, _u16p, _u16p]),
+            "orc_pack_wgrad_entries": (None, [dp, _u16p, _i32p, _i32p, _u16p, _u16p, i32, _i32p,
+                                              _i32p, _i32p, i64, _u16p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -365,3 +378,81 @@ def pack_backward(d: Dims, d_pools, topk, slot, x, d_shared, w_ld_t, ws_gate, ws
         np.ascontiguousarray(slot, np.int32), _u16(x), _u16(d_shared), _u16(w_ld_t),
         _u16(ws_gate), _u16(ws_up), dz, dx, dw_ld, dwsg, dwsu)
     return dz, dx, dw_ld, dwsg, dwsu
+
+
+# sampled outputs (full-size checks)
+
+def _i32(a):
+    return np.ascontiguousarray(a, np.int32)
+
+
+def _i64(a):
+    return np.ascontiguousarray(a, np.int64)
+
+
+def combine_backward_tokens(d: Dims, returned, topk, slot, gates, x, w_lu_t, ws_gate, ws_up,
+                            ws_down, d_out, tokens):
+    """(d_ret_rows [n, k, L], d_gates [n, k], d_shared [n, 2, S, Fs]) for tokens."""
+    tk = _i64(tokens)
+    n, k, L = len(tk), d.top_k, d.latent
+    rows = np.empty((n, k, L), np.uint16)
+    dg = np.empty((n, k), np.float32)
+    dsh = np.empty((n, 2, d.n_shared, d.d_ff_shared), np.uint16)
+    lib().orc_combine_backward_tokens(
+        ctypes.byref(d), _u16(returned), _i32(topk), _i32(slot),
+        np.ascontiguousarray(gates, np.float32), _u16(x), _u16(w_lu_t), _u16(ws_gate),
+        _u16(ws_up), _u16(ws_down), _u16(d_out), tk, n, rows, dg, dsh)
+    return rows, dg, dsh
+
+
+def combine_wgrad_entries(d: Dims, x, ylat, ws_gate, ws_up, d_out, which, ra, cb, sh=None):
+    """which 0: dw_lat_up[ra, cb]; 1: dws_down[sh, ra, cb]."""
+    n = len(ra)
+    out = np.empty(n, np.uint16)
+    shi = _i32(np.zeros(n) if sh is None else sh)
+    lib().orc_combine_wgrad_entries(ctypes.byref(d), _u16(x), _u16(ylat), _u16(ws_gate),
+                                    _u16(ws_up), _u16(d_out), which, shi, _i32(ra), _i32(cb), n,
+                                    out)
+    return out
+
+
+def expert_ffn_backward_rows(d: Dims, bank, bank_src, w_gate, w_up, w_down, d_ret, pos):
+    """d_u [n, L] of kept bank positions pos (written to d_recv[bank_src[pos]])."""
+    p = _i64(pos)
+    out = np.empty((len(p), d.latent), np.uint16)
+    lib().orc_expert_ffn_backward_rows(ctypes.byref(d), _u16(bank), _i32(bank_src),
+                                       _u16(w_gate), _u16(w_up), _u16(w_down), _u16(d_ret), p,
+                                       len(p), out)
+    return out
+
+
+def expert_wgrad_entries(d: Dims, bank, bank_src, bfill, w_gate, w_up, w_down, d_ret, j, which,
+                         ra, cb):
+    """which 0: dw_gate[j, ra, cb]; 1: dw_up[j, ra, cb]; 2: dw_down[j, ra, cb]."""
+    n = len(ra)
+    out = np.empty(n, np.uint16)
+    lib().orc_expert_wgrad_entries(ctypes.byref(d), _u16(bank), _i32(bank_src), _i32(bfill),
+                                   _u16(w_gate), _u16(w_up), _u16(w_down), _u16(d_ret), j, which,
+                                   _i32(ra), _i32(cb), n, out)
+    return out
+
+
+def pack_backward_tokens(d: Dims, d_pools, topk, slot, d_shared, w_ld_t, ws_gate, ws_up, tokens):
+    """(dz [n, L], dx [n, D]) for tokens."""
+    tk = _i64(tokens)
+    dz = np.empty((len(tk), d.latent), np.uint16)
+    dx = np.empty((len(tk), d.d_model), np.uint16)
+    lib().orc_pack_backward_tokens(ctypes.byref(d), _u16(d_pools), _i32(topk), _i32(slot),
+                                   _u16(d_shared), _u16(w_ld_t), _u16(ws_gate), _u16(ws_up), tk,
+                                   len(tk), dz, dx)
+    return dz, dx
+
+
+def pack_wgrad_entries(d: Dims, d_pools, topk, slot, x, d_shared, which, ra, cb, sh=None):
+    """which 0: dw_lat_down[ra, cb]; 1: dws_gate[sh, ra, cb]; 2: dws_up[sh, ra, cb]."""
+    n = len(ra)
+    out = np.empty(n, np.uint16)
+    shi = _i32(np.zeros(n) if sh is None else sh)
+    lib().orc_pack_wgrad_entries(ctypes.byref(d), _u16(d_pools), _i32(topk), _i32(slot), _u16(x),
+                                 _u16(d_shared), which, shi, _i32(ra), _i32(cb), n, out)
+    return out

@@ -854,3 +854,240 @@ void orc_pack_backward(const orc_dims *d, const uint16_t *d_pools,
   }
   free(acc);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward on sampled outputs (full-size checks): the same arithmetic as    */
+/* the functions above, for listed tokens, bank rows or weight entries.     */
+/* ------------------------------------------------------------------------ */
+
+/* Combine side for tokens[0..n): d_ret_rows [n][k][L] (the d_returned row
+ * of each kept choice, 0 for a dropped one), d_gates [n][k], d_shared
+ * [n][2][S][Fs].  Equal to orc_combine_backward's values for those tokens. */
+void orc_combine_backward_tokens(const orc_dims *d, const uint16_t *returned,
+                                 const int32_t *topk, const int32_t *slot,
+                                 const float *gates, const uint16_t *x,
+                                 const uint16_t *w_lu_t, const uint16_t *ws_gate,
+                                 const uint16_t *ws_up, const uint16_t *ws_down,
+                                 const uint16_t *d_out, const int64_t *tokens,
+                                 int64_t n, uint16_t *d_ret_rows,
+                                 float *d_gates, uint16_t *d_shared) {
+  const int32_t L = d->latent, D = d->d_model, k = d->top_k;
+  const int32_t S = d->n_shared, Fs = d->d_ff_shared;
+  double *dyl = (double *)malloc(sizeof(double) * (size_t)L);
+  for (int64_t r = 0; r < n; ++r) {
+    const int64_t t = tokens[r];
+    const uint16_t *go = d_out + t * D;
+    for (int32_t i = 0; i < L; ++i) {
+      double acc = 0.0;
+      for (int32_t c = 0; c < D; ++c) acc += bf(go[c]) * bf(w_lu_t[(int64_t)c * L + i]);
+      dyl[i] = bf(to_bf(acc));
+    }
+    for (int32_t j = 0; j < k; ++j) {
+      uint16_t *o = d_ret_rows + (r * k + j) * L;
+      int32_t s = slot[t * k + j];
+      if (s < 0) {
+        memset(o, 0, sizeof(uint16_t) * (size_t)L);
+        d_gates[r * k + j] = 0.0f;
+        continue;
+      }
+      int64_t row = pool_row(d, t, topk[t * k + j], s);
+      double g = gates[t * k + j], dot = 0.0;
+      for (int32_t i = 0; i < L; ++i) {
+        o[i] = to_bf(g * dyl[i]);
+        dot += bf(returned[row * L + i]) * dyl[i];
+      }
+      d_gates[r * k + j] = (float)dot;
+    }
+    for (int32_t sh = 0; sh < S; ++sh)
+      for (int32_t f = 0; f < Fs; ++f) {
+        double dh = 0.0, a = 0.0, b = 0.0;
+        for (int32_t c = 0; c < D; ++c)
+          dh += bf(go[c]) * bf(ws_down[((int64_t)sh * D + c) * Fs + f]);
+        dh = bf(to_bf(dh));
+        const uint16_t *wg = ws_gate + ((int64_t)sh * Fs + f) * D;
+        const uint16_t *wu = ws_up + ((int64_t)sh * Fs + f) * D;
+        for (int32_t i = 0; i < D; ++i) a += bf(x[t * D + i]) * bf(wg[i]);
+        for (int32_t i = 0; i < D; ++i) b += bf(x[t * D + i]) * bf(wu[i]);
+        d_shared[(r * 2 * S + sh) * Fs + f] = to_bf(dh * b * silu_grad(a));
+        d_shared[(r * 2 * S + S + sh) * Fs + f] = to_bf(dh * silu(a));
+      }
+  }
+  free(dyl);
+}
+
+/* Weight-gradient entries of the combine side, summed over all T tokens in
+ * order: which 0: dw_lat_up[ra[e]][cb[e]] = sum_t d_out[t][ra] ylat[t][cb];
+ * which 1: dws_down[sh[e]][ra[e]][cb[e]] = sum_t d_out[t][ra] h_s[t][cb],
+ * h_s = bf16(silu(x.W_sg,sh) (x.W_su,sh)) recomputed. */
+void orc_combine_wgrad_entries(const orc_dims *d, const uint16_t *x,
+                               const uint16_t *ylat, const uint16_t *ws_gate,
+                               const uint16_t *ws_up, const uint16_t *d_out,
+                               int32_t which, const int32_t *sh_idx,
+                               const int32_t *ra, const int32_t *cb, int64_t n,
+                               uint16_t *out) {
+  const int64_t T = d->T;
+  const int32_t L = d->latent, D = d->d_model, Fs = d->d_ff_shared;
+  for (int64_t e = 0; e < n; ++e) {
+    double acc = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      double v;
+      if (which == 0) {
+        v = bf(ylat[t * L + cb[e]]);
+      } else {
+        const uint16_t *wg = ws_gate + ((int64_t)sh_idx[e] * Fs + cb[e]) * D;
+        const uint16_t *wu = ws_up + ((int64_t)sh_idx[e] * Fs + cb[e]) * D;
+        double a = 0.0, b = 0.0;
+        for (int32_t i = 0; i < D; ++i) a += bf(x[t * D + i]) * bf(wg[i]);
+        for (int32_t i = 0; i < D; ++i) b += bf(x[t * D + i]) * bf(wu[i]);
+        v = bf(to_bf(silu(a) * b));
+      }
+      acc += bf(d_out[t * D + ra[e]]) * v;
+    }
+    out[e] = to_bf(acc);
+  }
+}
+
+/* Receiver side for bank positions pos[0..n) (kept rows): d_u [n][L], the
+ * row each writes to d_recv[bank_src[pos]]. */
+void orc_expert_ffn_backward_rows(const orc_dims *d, const uint16_t *bank,
+                                  const int32_t *bank_src,
+                                  const uint16_t *w_gate, const uint16_t *w_up,
+                                  const uint16_t *w_down, const uint16_t *d_ret,
+                                  const int64_t *pos, int64_t n, uint16_t *d_u) {
+  const int32_t L = d->latent, F = d->d_ff;
+  const int32_t El = d->n_experts / d->n_ranks;
+  const int64_t WL = (int64_t)F * L;
+  double *da = (double *)malloc(sizeof(double) * (size_t)F);
+  double *db = (double *)malloc(sizeof(double) * (size_t)F);
+  for (int64_t r = 0; r < n; ++r) {
+    const int64_t p = pos[r], src = bank_src[p];
+    const int32_t j = (int32_t)((p / d->cap_recv) % El);
+    const uint16_t *Wg = w_gate + j * WL, *Wu = w_up + j * WL, *Wd = w_down + j * WL;
+    for (int32_t f = 0; f < F; ++f) {
+      double dh = 0.0, a = 0.0, b = 0.0;
+      for (int32_t l = 0; l < L; ++l) dh += bf(d_ret[src * L + l]) * bf(Wd[(int64_t)l * F + f]);
+      dh = bf(to_bf(dh));
+      for (int32_t l = 0; l < L; ++l) a += bf(bank[p * L + l]) * bf(Wg[(int64_t)f * L + l]);
+      for (int32_t l = 0; l < L; ++l) b += bf(bank[p * L + l]) * bf(Wu[(int64_t)f * L + l]);
+      da[f] = bf(to_bf(dh * b * silu_grad(a)));
+      db[f] = bf(to_bf(dh * silu(a)));
+    }
+    for (int32_t l = 0; l < L; ++l) {
+      double acc = 0.0;
+      for (int32_t f = 0; f < F; ++f)
+        acc += da[f] * bf(Wg[(int64_t)f * L + l]) + db[f] * bf(Wu[(int64_t)f * L + l]);
+      d_u[r * L + l] = to_bf(acc);
+    }
+  }
+  free(da);
+  free(db);
+}
+
+/* Weight-gradient entries of local expert j over its kept rows of every
+ * wave, in (wave, position) order: which 0: dw_gate[j][ra][cb] (f, l);
+ * 1: dw_up[j][ra][cb]; 2: dw_down[j][ra][cb] (l, f). */
+void orc_expert_wgrad_entries(const orc_dims *d, const uint16_t *bank,
+                              const int32_t *bank_src, const int32_t *bfill,
+                              const uint16_t *w_gate, const uint16_t *w_up,
+                              const uint16_t *w_down, const uint16_t *d_ret,
+                              int32_t j, int32_t which, const int32_t *ra,
+                              const int32_t *cb, int64_t n, uint16_t *out) {
+  const int32_t L = d->latent, F = d->d_ff;
+  const int32_t El = d->n_experts / d->n_ranks;
+  const int64_t WL = (int64_t)F * L;
+  const uint16_t *Wg = w_gate + j * WL, *Wu = w_up + j * WL, *Wd = w_down + j * WL;
+  double *acc = (double *)calloc((size_t)n, sizeof(double));
+  for (int32_t w = 0; w < d->n_waves; ++w) {
+    const int32_t g = w * El + j;
+    for (int32_t p = 0; p < bfill[g]; ++p) {
+      const int64_t pos = (int64_t)g * d->cap_recv + p, src = bank_src[pos];
+      const uint16_t *u = bank + pos * L, *dy = d_ret + src * L;
+      for (int64_t e = 0; e < n; ++e) {
+        const int32_t f = which == 2 ? cb[e] : ra[e];
+        double dh = 0.0, a = 0.0, b = 0.0;
+        for (int32_t l = 0; l < L; ++l) dh += bf(dy[l]) * bf(Wd[(int64_t)l * F + f]);
+        dh = bf(to_bf(dh));
+        for (int32_t l = 0; l < L; ++l) a += bf(u[l]) * bf(Wg[(int64_t)f * L + l]);
+        for (int32_t l = 0; l < L; ++l) b += bf(u[l]) * bf(Wu[(int64_t)f * L + l]);
+        if (which == 2) {
+          acc[e] += bf(dy[ra[e]]) * bf(to_bf(silu(a) * b));
+        } else {
+          double dv = which == 0 ? bf(to_bf(dh * b * silu_grad(a))) : bf(to_bf(dh * silu(a)));
+          acc[e] += dv * bf(u[cb[e]]);
+        }
+      }
+    }
+  }
+  for (int64_t e = 0; e < n; ++e) out[e] = to_bf(acc[e]);
+  free(acc);
+}
+
+/* Sender side for tokens[0..n): dz [n][L], dx [n][D]; d_shared is the full
+ * [T][2][S][Fs] input. */
+void orc_pack_backward_tokens(const orc_dims *d, const uint16_t *d_pools,
+                              const int32_t *topk, const int32_t *slot,
+                              const uint16_t *d_shared, const uint16_t *w_ld_t,
+                              const uint16_t *ws_gate, const uint16_t *ws_up,
+                              const int64_t *tokens, int64_t n, uint16_t *dz,
+                              uint16_t *dx) {
+  const int32_t L = d->latent, D = d->d_model, k = d->top_k;
+  const int32_t S = d->n_shared, Fs = d->d_ff_shared;
+  double *acc = (double *)malloc(sizeof(double) * (size_t)L);
+  for (int64_t r = 0; r < n; ++r) {
+    const int64_t t = tokens[r];
+    for (int32_t l = 0; l < L; ++l) acc[l] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t s = slot[t * k + j];
+      if (s < 0) continue;
+      int64_t row = pool_row(d, t, topk[t * k + j], s);
+      for (int32_t l = 0; l < L; ++l) acc[l] += bf(d_pools[row * L + l]);
+    }
+    for (int32_t l = 0; l < L; ++l) dz[r * L + l] = to_bf(acc[l]);
+    for (int32_t i = 0; i < D; ++i) {
+      double o = 0.0;
+      for (int32_t l = 0; l < L; ++l) o += bf(dz[r * L + l]) * bf(w_ld_t[(int64_t)l * D + i]);
+      for (int32_t sh = 0; sh < S; ++sh)
+        for (int32_t f = 0; f < Fs; ++f) {
+          int64_t wi = ((int64_t)sh * Fs + f) * D + i;
+          o += bf(d_shared[(t * 2 * S + sh) * Fs + f]) * bf(ws_gate[wi]) +
+               bf(d_shared[(t * 2 * S + S + sh) * Fs + f]) * bf(ws_up[wi]);
+        }
+      dx[r * D + i] = to_bf(o);
+    }
+  }
+  free(acc);
+}
+
+/* Weight-gradient entries of the sender side over all T tokens in order:
+ * which 0: dw_lat_down[ra][cb] = sum_t dz[t][ra] x[t][cb] (dz as in
+ * orc_pack_backward); 1: dws_gate, 2: dws_up [sh*Fs + ra][cb] =
+ * sum_t d_shared[t][gate or up][sh][ra] x[t][cb]. */
+void orc_pack_wgrad_entries(const orc_dims *d, const uint16_t *d_pools,
+                            const int32_t *topk, const int32_t *slot,
+                            const uint16_t *x, const uint16_t *d_shared,
+                            int32_t which, const int32_t *sh_idx,
+                            const int32_t *ra, const int32_t *cb, int64_t n,
+                            uint16_t *out) {
+  const int64_t T = d->T;
+  const int32_t L = d->latent, D = d->d_model, k = d->top_k;
+  const int32_t S = d->n_shared, Fs = d->d_ff_shared;
+  for (int64_t e = 0; e < n; ++e) {
+    double acc = 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+      double v;
+      if (which == 0) {
+        double z = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+          int32_t s = slot[t * k + j];
+          if (s < 0) continue;
+          z += bf(d_pools[pool_row(d, t, topk[t * k + j], s) * L + ra[e]]);
+        }
+        v = bf(to_bf(z));
+      } else {
+        v = bf(d_shared[(t * 2 * S + (which == 2 ? S : 0) + sh_idx[e]) * Fs + ra[e]]);
+      }
+      acc += v * bf(x[t * D + cb[e]]);
+    }
+    out[e] = to_bf(acc);
+  }
+}

@@ -137,6 +137,46 @@ void orc_pack_backward(const orc_dims *d, const uint16_t *d_pools,
                        uint16_t *dw_lat_down, uint16_t *dws_gate,
                        uint16_t *dws_up);
 
+/* Backward on sampled outputs: the same values as the full functions for
+ * listed tokens, bank positions or weight entries (full-size checks). */
+void orc_combine_backward_tokens(const orc_dims *d, const uint16_t *returned,
+                                 const int32_t *topk, const int32_t *slot,
+                                 const float *gates, const uint16_t *x,
+                                 const uint16_t *w_lu_t, const uint16_t *ws_gate,
+                                 const uint16_t *ws_up, const uint16_t *ws_down,
+                                 const uint16_t *d_out, const int64_t *tokens,
+                                 int64_t n, uint16_t *d_ret_rows,
+                                 float *d_gates, uint16_t *d_shared);
+void orc_combine_wgrad_entries(const orc_dims *d, const uint16_t *x,
+                               const uint16_t *ylat, const uint16_t *ws_gate,
+                               const uint16_t *ws_up, const uint16_t *d_out,
+                               int32_t which, const int32_t *sh_idx,
+                               const int32_t *ra, const int32_t *cb, int64_t n,
+                               uint16_t *out);
+void orc_expert_ffn_backward_rows(const orc_dims *d, const uint16_t *bank,
+                                  const int32_t *bank_src,
+                                  const uint16_t *w_gate, const uint16_t *w_up,
+                                  const uint16_t *w_down, const uint16_t *d_ret,
+                                  const int64_t *pos, int64_t n, uint16_t *d_u);
+void orc_expert_wgrad_entries(const orc_dims *d, const uint16_t *bank,
+                              const int32_t *bank_src, const int32_t *bfill,
+                              const uint16_t *w_gate, const uint16_t *w_up,
+                              const uint16_t *w_down, const uint16_t *d_ret,
+                              int32_t j, int32_t which, const int32_t *ra,
+                              const int32_t *cb, int64_t n, uint16_t *out);
+void orc_pack_backward_tokens(const orc_dims *d, const uint16_t *d_pools,
+                              const int32_t *topk, const int32_t *slot,
+                              const uint16_t *d_shared, const uint16_t *w_ld_t,
+                              const uint16_t *ws_gate, const uint16_t *ws_up,
+                              const int64_t *tokens, int64_t n, uint16_t *dz,
+                              uint16_t *dx);
+void orc_pack_wgrad_entries(const orc_dims *d, const uint16_t *d_pools,
+                            const int32_t *topk, const int32_t *slot,
+                            const uint16_t *x, const uint16_t *d_shared,
+                            int32_t which, const int32_t *sh_idx,
+                            const int32_t *ra, const int32_t *cb, int64_t n,
+                            uint16_t *out);
+
 #ifdef __cplusplus
 }
 #endif

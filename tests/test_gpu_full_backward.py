@@ -1,0 +1,186 @@
+"""Full-size parity of the backward calls, in the launch configuration
+bench.py times (the same entry points and sizes: T = 4096 / 16384 / 65536
+tokens, model width 6144, latent 3072, 384 experts on 64 ranks).
+
+Stage inputs come from the generators at full size (payload rows, made on
+the device and copied to the host for the oracle, stand in
+for returned rows, ylat, the bank, the gradients), routing and sender slots
+from the oracle on the shard's own logits, the bank decisions from the
+oracle on seeded receive headers.  Integer-exact properties are checked in
+full (zero rows where nothing was kept, zero gate gradients of dropped
+choices, the router's gradient everywhere); floating outputs on sampled
+tokens, bank rows and weight entries that the oracle computes one by one.
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import gpucase as gc
+from conftest import f64, u16
+from synth import configs, gen
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("share4k", configs.SHARE_4K, dict(tok=6, rows=10, ent=3, experts=3)),
+    ("zipf16k", configs.ZIPF_16K, dict(tok=4, rows=6, ent=2, experts=2)),
+    ("long65k", configs.LONG_65K, dict(tok=3, rows=4, ent=1, experts=1)),
+]
+
+
+def _close_entries(got_u16, ref_u16, scale_u16, what):
+    """Sampled weight entries: within 2e-2 of the weight row's largest |value|
+    on the GPU side (the per-row bound of the other parity tests)."""
+    g, r = f64(got_u16), f64(ref_u16)
+    bad = np.abs(g - r) > 2e-2 * np.maximum(f64(scale_u16), 1e-30)
+    assert not bad.any(), f"{what}: {int(bad.sum())} entries over tolerance"
+
+
+def _sample_tokens(cfg, slot, n, rng):
+    Tw = math.ceil(cfg.T / cfg.n_waves)
+    fixed = [0, cfg.T - 1, Tw - 1, Tw, min(cfg.T - 1, 2 * Tw)]
+    dropped = np.nonzero((slot < 0).any(1))[0]
+    if len(dropped):
+        fixed.append(int(dropped[0]))
+    return np.unique(np.concatenate([fixed, rng.integers(0, cfg.T, n)]))
+
+
+@pytest.mark.parametrize("name,cfg,ns", CASES, ids=[c[0] for c in CASES])
+def test_full_backward(moe_lib, orc, name, cfg, ns):
+    from dispatch_softmax_top_amd import share
+    moe = moe_lib
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    d_orc, d = orc.dims(cfg), share.make_dims(cfg)
+    T, L, D, S, Fs, k = cfg.T, cfg.latent, cfg.d_model, cfg.n_shared, cfg.d_ff_shared, cfg.top_k
+    El, F, R, W = cfg.experts_per_rank, cfg.d_ff, cfg.n_ranks, cfg.n_waves
+    n_rows = R * W * d.cap_send
+    print(f"\n[full backward] {name}: routing", flush=True)
+    x_t, lg_t = gc.shard_inputs(cfg, 0)
+    x, lg = u16(x_t), lg_t.numpy()
+    topk, gates = orc.route(lg, k)
+    so = orc.sender(d_orc, topk)
+    slot, fill = so["slot"], so["fill"]
+    wlu, wld = u16(gen.latent_up(cfg)), u16(gen.latent_down(cfg))
+    wsg, wsu, wsd = (u16(w) for w in gen.shared(cfg))
+    dev = lambda a: gc.dev(np.ascontiguousarray(a))
+    b = share.Backward(d, n_rows)
+
+    # ---- combine side
+    print(f"[full backward] {name}: combine", flush=True)
+    returned = gen.payload_rows(n_rows, L, 81, "cuda")
+    ylat, d_out = gen.payload_rows(T, L, 82, "cuda"), gen.payload_rows(T, D, 83, "cuda")
+    h_returned, h_ylat, h_dout = u16(returned), u16(ylat), u16(d_out)
+    moe.moe_combine_backward(d, returned, dev(topk), dev(slot), dev(gates), dev(fill),
+                             x_t.cuda(), ylat, dev(wlu), dev(wsg), dev(wsu), dev(wsd), d_out, b.d_returned, b.d_gates, b.d_shared, b.dw_lat_up,
+                             b.dws_down, b.ws_combine)
+    moe.moe_route_backward(lg_t.cuda(), dev(topk), b.d_gates, b.d_logits)
+    torch.cuda.synchronize()
+    g_dret, g_dg = gc.host(b.d_returned), gc.host(b.d_gates)
+    for p in range(R * W):                                # rows past each pool's fill: zero
+        assert (g_dret[p * d.cap_send + fill[p]:(p + 1) * d.cap_send] == 0).all()
+    assert (g_dg[slot < 0] == 0).all()
+    # the router's gradient in full, from the GPU's gate gradients
+    o_dl = orc.route_backward(lg, topk, g_dg)
+    scale = np.abs(o_dl).max(1, keepdims=True) + 1e-30
+    assert (np.abs(gc.host(b.d_logits) - o_dl) <= 1e-4 * scale).all()
+    tok = _sample_tokens(cfg, slot, ns["tok"], rng)
+    rows, dg, dsh = orc.combine_backward_tokens(d_orc, h_returned, topk, slot, gates, x, wlu,
+                                                wsg, wsu, wsd, h_dout, tok)
+    Tw = math.ceil(T / W)
+    used = []
+    for r, t in enumerate(tok):
+        for j in range(k):
+            if slot[t, j] < 0:
+                continue
+            row = ((topk[t, j] // El) * W + t // Tw) * d.cap_send + slot[t, j]
+            used.append(row)
+            gc.assert_rows_close(g_dret[row][None], rows[r, j][None], f"d_returned t={t}")
+    y = f64(h_dout[tok]) @ f64(wlu)
+    tol = 2e-3 * np.abs(f64(h_returned[used])).max() * np.abs(y).sum(1, keepdims=True)
+    assert (np.abs(g_dg[tok] - dg) <= tol).all()
+    gc.assert_rows_close(gc.host(b.d_shared)[tok].reshape(len(tok), -1),
+                         dsh.reshape(len(tok), -1), "d_shared")
+    g_dwlu = gc.host(b.dw_lat_up)
+    ra, cb = rng.integers(0, D, ns["ent"] * 3), rng.integers(0, L, ns["ent"] * 3)
+    ref = orc.combine_wgrad_entries(d_orc, x, h_ylat, wsg, wsu, h_dout, 0, ra, cb)
+    _close_entries(g_dwlu[ra, cb], ref, np.abs(f64(g_dwlu[ra])).max(1), "dw_lat_up")
+    g_dwsd = gc.host(b.dws_down)
+    sh, cf = rng.integers(0, S, ns["ent"]), rng.integers(0, Fs, ns["ent"])
+    ra = rng.integers(0, D, ns["ent"])
+    ref = orc.combine_wgrad_entries(d_orc, x, h_ylat, wsg, wsu, h_dout, 1, ra, cf, sh)
+    _close_entries(g_dwsd[sh, ra, cf], ref, np.abs(f64(g_dwsd[sh, ra])).max(1), "dws_down")
+
+    # ---- receiver side (rank 1's experts on seeded receive headers)
+    print(f"[full backward] {name}: experts", flush=True)
+    rank = 1
+    hdr = np.where(rng.random(n_rows) < 0.9, rank * El + rng.integers(0, El, n_rows), -1)
+    bo = orc.bank_slots(d_orc, rank, hdr.astype(np.int32), None)
+    nb = len(bo["bank_src"])
+    bank, d_ret = gen.payload_rows(nb, L, 84, "cuda"), gen.payload_rows(n_rows, L, 85, "cuda")
+    h_bank, h_dret = u16(bank), u16(d_ret)
+    wg, wu, wdn = gen.rank_experts(cfg, rank)
+    moe.moe_expert_ffn_backward(d, bank, dev(bo["bank_src"]), dev(bo["bfill"]), wg.cuda(),
+                                wu.cuda(), wdn.cuda(), d_ret, b.d_recv, b.dw_gate,
+                                b.dw_up, b.dw_down, b.ws_ffn)
+    torch.cuda.synchronize()
+    g_drecv = gc.host(b.d_recv)
+    kept = np.zeros(n_rows, bool)
+    kept[bo["bank_src"][bo["bank_src"] >= 0]] = True
+    assert (g_drecv[~kept] == 0).all()
+    filled = np.nonzero(bo["bank_src"] >= 0)[0]
+    cap = d.cap_recv
+    edges = [p for g in range(W * El) for p in (g * cap, g * cap + bo["bfill"][g] - 1)
+             if bo["bfill"][g] > 0]
+    pos = np.unique(np.concatenate([rng.choice(filled, ns["rows"]), rng.choice(edges, 4)]))
+    ex = [u16(w) for w in (wg, wu, wdn)]
+    du = orc.expert_ffn_backward_rows(d_orc, h_bank, bo["bank_src"], *ex, h_dret, pos)
+    gc.assert_rows_close(g_drecv[bo["bank_src"][pos]], du, "d_recv")
+    for which, got in ((0, b.dw_gate), (1, b.dw_up), (2, b.dw_down)):
+        gw = gc.host(got)
+        for j in rng.choice(El, ns["experts"], replace=False):
+            ra = rng.integers(0, gw.shape[1], ns["ent"])
+            cb = rng.integers(0, gw.shape[2], ns["ent"])
+            ref = orc.expert_wgrad_entries(d_orc, h_bank, bo["bank_src"], bo["bfill"], *ex,
+                                           h_dret, int(j), which, ra, cb)
+            _close_entries(gw[j, ra, cb], ref, np.abs(f64(gw[j, ra])).max(1),
+                           f"expert weight {which} of expert {j}")
+
+    # ---- sender side
+    print(f"[full backward] {name}: pack", flush=True)
+    d_pools = gen.payload_rows(n_rows, L, 86, "cuda")
+    d_shared = gen.payload_rows(T, 2 * S * Fs, 87, "cuda")
+    h_dpools, h_dshared = u16(d_pools), u16(d_shared)
+    moe.moe_pack_backward(d, d_pools, dev(topk), dev(slot), x_t.cuda(), d_shared,
+                          dev(wld), dev(wsg), dev(wsu), b.dz, b.dx, b.dw_lat_down, b.dws_gate,
+                          b.dws_up, b.ws_pack)
+    torch.cuda.synchronize()
+    dz, dx = orc.pack_backward_tokens(d_orc, h_dpools, topk, slot, h_dshared, wld, wsg,
+                                      wsu, tok)
+    gz = gc.host(b.dz)
+    none = (slot < 0).all(1)
+    assert (gz[none] == 0).all()
+    keep = ~none[tok]
+    gc.assert_rows_close(gz[tok][keep], dz[keep], "dz")
+    gc.assert_rows_close(gc.host(b.dx)[tok], dx, "dx")
+    g_dwld = gc.host(b.dw_lat_down)
+    ra, cb = rng.integers(0, L, ns["ent"] * 3), rng.integers(0, D, ns["ent"] * 3)
+    ref = orc.pack_wgrad_entries(d_orc, h_dpools, topk, slot, x, h_dshared, 0, ra, cb)
+    _close_entries(g_dwld[ra, cb], ref, np.abs(f64(g_dwld[ra])).max(1), "dw_lat_down")
+    for which, got in ((1, b.dws_gate), (2, b.dws_up)):
+        gw = gc.host(got)
+        sh, ra = rng.integers(0, S, ns["ent"]), rng.integers(0, Fs, ns["ent"])
+        cb = rng.integers(0, D, ns["ent"])
+        ref = orc.pack_wgrad_entries(d_orc, h_dpools, topk, slot, x, h_dshared, which, ra,
+                                     cb, sh)
+        _close_entries(gw[sh, ra, cb], ref, np.abs(f64(gw[sh, ra])).max(1), f"shared weight {which}")
+
+
+@pytest.fixture(scope="module")
+def moe_lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import dispatch_softmax_top_amd as m
+    m.lib()
+    return m

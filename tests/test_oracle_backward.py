@@ -218,3 +218,75 @@ def test_backward_structure(orc):
         row = ((e // cfg.experts_per_rank) * W + t // int(np.ceil(cfg.T / W))) * Cs + sl
         vecs.append(f64(CB[s][0][row]) / float(S[s]["gates"][t, j]))
     np.testing.assert_allclose(vecs[0], vecs[1], rtol=1e-2, atol=1e-6 * np.abs(vecs[0]).max())
+
+
+@pytest.mark.parametrize("waves", ["tokens", "chunks"])
+def test_sampled_backward_equals_full(orc, waves):
+    """The sampled-output functions (full-size GPU checks) give the full
+    functions' values bit for bit, on random stage inputs."""
+    from dataclasses import replace
+    from synth import gen
+    cfg = replace(configs.TINY, waves=waves)
+    d = orc.dims(cfg)
+    T, L, D, S, Fs, k = cfg.T, cfg.latent, cfg.d_model, cfg.n_shared, cfg.d_ff_shared, cfg.top_k
+    El, F = cfg.experts_per_rank, cfg.d_ff
+    rng = np.random.default_rng(70)
+    pay = lambda n, w, i: u16(gen.payload_rows(n, w, i))
+    n_rows = cfg.n_ranks * cfg.n_waves * d.cap_send
+    x, lg = pay(T, D, 1), (rng.standard_normal((T, cfg.n_experts)) * 2).astype(np.float32)
+    topk, gates = orc.route(lg, k)
+    slot = orc.sender(d, topk)["slot"]
+    returned, ylat, d_out = pay(n_rows, L, 2), pay(T, L, 3), pay(T, D, 4)
+    wlu, wld = u16(gen.latent_up(cfg)), u16(gen.latent_down(cfg))
+    wsg, wsu, wsd = (u16(w) for w in gen.shared(cfg))
+    full = orc.combine_backward(d, returned, topk, slot, gates, x, ylat, wlu, wsg, wsu, wsd, d_out)
+    tok = np.array([0, 5, 21, 22, 43, T - 1])
+    rows, dg, dsh = orc.combine_backward_tokens(d, returned, topk, slot, gates, x, wlu, wsg, wsu,
+                                                wsd, d_out, tok)
+    Cs, W = d.cap_send, cfg.n_waves
+    for r, t in enumerate(tok):
+        assert np.array_equal(dg[r], full[1][t])
+        assert np.array_equal(dsh[r], full[2][t])
+        for j in range(k):
+            s = slot[t, j]
+            if s < 0:
+                assert (rows[r, j] == 0).all()
+                continue
+            dst = topk[t, j] // El
+            Tw = -(-T // W)
+            row = dst * W * Cs + s if waves == "chunks" else (dst * W + t // Tw) * Cs + s
+            assert np.array_equal(rows[r, j], full[0][row])
+    ra, cb = rng.integers(0, D, 9), rng.integers(0, L, 9)
+    assert np.array_equal(orc.combine_wgrad_entries(d, x, ylat, wsg, wsu, d_out, 0, ra, cb),
+                          full[3][ra, cb])
+    sh, cf = rng.integers(0, S, 9), rng.integers(0, Fs, 9)
+    assert np.array_equal(orc.combine_wgrad_entries(d, x, ylat, wsg, wsu, d_out, 1, ra, cf, sh),
+                          full[4][sh, ra, cf])
+    # receiver
+    hdr = np.concatenate([rng.integers(0, El, n_rows // 2), -np.ones(n_rows - n_rows // 2, int)])
+    hdr = rng.permutation(hdr).astype(np.int32)
+    bo = orc.bank_slots(d, 0, hdr, None)
+    bank, d_ret = pay(len(bo["bank_src"]), L, 5), pay(n_rows, L, 6)
+    wg, wu, wdn = (u16(w) for w in gen.rank_experts(cfg, 0))
+    fe = orc.expert_ffn_backward(d, bank, bo["bank_src"], bo["bfill"], wg, wu, wdn, d_ret)
+    pos = np.nonzero(bo["bank_src"] >= 0)[0][::7]
+    du = orc.expert_ffn_backward_rows(d, bank, bo["bank_src"], wg, wu, wdn, d_ret, pos)
+    assert np.array_equal(du, fe[0][bo["bank_src"][pos]])
+    for which, ref in ((0, fe[1]), (1, fe[2]), (2, fe[3])):
+        for j in range(El):
+            a = rng.integers(0, ref.shape[1], 5)
+            b = rng.integers(0, ref.shape[2], 5)
+            got = orc.expert_wgrad_entries(d, bank, bo["bank_src"], bo["bfill"], wg, wu, wdn,
+                                           d_ret, j, which, a, b)
+            assert np.array_equal(got, ref[j, a, b]), (which, j)
+    # sender
+    d_pools, d_shared = pay(n_rows, L, 7), pay(T, 2 * S * Fs, 8).reshape(T, 2, S, Fs)
+    fp = orc.pack_backward(d, d_pools, topk, slot, x, d_shared, wld, wsg, wsu)
+    dz, dx = orc.pack_backward_tokens(d, d_pools, topk, slot, d_shared, wld, wsg, wsu, tok)
+    assert np.array_equal(dz, fp[0][tok]) and np.array_equal(dx, fp[1][tok])
+    ra, cb = rng.integers(0, L, 9), rng.integers(0, D, 9)
+    assert np.array_equal(orc.pack_wgrad_entries(d, d_pools, topk, slot, x, d_shared, 0, ra, cb),
+                          fp[2][ra, cb])
+    for which, ref in ((1, fp[3]), (2, fp[4])):
+        got = orc.pack_wgrad_entries(d, d_pools, topk, slot, x, d_shared, which, cf, cb, sh)
+        assert np.array_equal(got, ref[sh, cf, cb])

@@ -10,7 +10,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # the backward slips: one whole-branch autograd comparison catches each
-BWD = "test_oracle_backward.py::test_branch_backward_matches_autograd"
+BWD = "test_oracle_backward.py::test_branch_backward_matches_autograd[1.10/1.15]"
 
 MUTATIONS = [
     ("tie-break", "if (best < 0 || l[e] > l[best]) best = e;",
