@@ -372,7 +372,8 @@ def bench_backward(st, steps, warmup):
         "data": "d_out: seeded N(0,1) bf16; both exchanges reversed as loopback identities",
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4)},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": counted_traffic(dom, st.cfg.name)},
         "path_roofline": path_roofline(kernels, work, ms),
         "kernels": kernels,
     }
