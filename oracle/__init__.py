@@ -26,7 +26,7 @@ _f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "d_model", "latent", "n_experts", "n_ranks", "top_k", "n_waves",
-        "d_ff", "n_shared", "d_ff_shared", "cap_send", "cap_recv", "wave_mode")]
+        "d_ff", "n_shared", "d_ff_shared", "cap_send", "cap_recv", "wave_mode", "dedup")]
 
 
 def build() -> str:
@@ -129,11 +129,11 @@ def dims(cfg, T=None) -> Dims:
         cs = capacity(tw, cfg.top_k, cfg.n_ranks, cfg.cf_send.numerator, cfg.cf_send.denominator)
         cr = capacity(tw, cfg.top_k, cfg.experts_per_rank, cfg.cf_recv.numerator,
                       cfg.cf_recv.denominator)
-    if cfg.waves == "chunks" and not cs:
-        raise ValueError("chunked waves need a fixed sender capacity")
+    if (cfg.waves == "chunks" or cfg.dedup) and not cs:
+        raise ValueError("chunked waves and dedup need a fixed sender capacity")
     return Dims(T, cfg.d_model, cfg.latent, cfg.n_experts, cfg.n_ranks, cfg.top_k,
                 cfg.n_waves, cfg.d_ff, cfg.n_shared, cfg.d_ff_shared, cs, cr,
-                1 if cfg.waves == "chunks" else 0)
+                1 if cfg.waves == "chunks" else 0, 1 if cfg.dedup else 0)
 
 
 def row_bytes(d: Dims) -> int:
@@ -247,11 +247,22 @@ def headers(rows: np.ndarray, latent_: int) -> np.ndarray:
     return np.ascontiguousarray(rows[:, latent_ * 2:latent_ * 2 + 4]).view(np.int32).reshape(-1)
 
 
+def row_ids(rows: np.ndarray, latent_: int) -> np.ndarray:
+    """All four tail ids of each row: [n, 4] (the dedup variant's headers)."""
+    return np.ascontiguousarray(rows[:, latent_ * 2:latent_ * 2 + 16]).view(np.int32).reshape(-1, 4)
+
+
+def recv_ids(d: Dims, rows: np.ndarray) -> np.ndarray:
+    """What orc_bank_slots reads of receive rows: the first tail id of each,
+    or all four with dedup."""
+    return row_ids(rows, d.latent) if d.dedup else headers(rows, d.latent)
+
+
 def bank_slots(d: Dims, rank: int, hdr: np.ndarray, recv_offsets=None):
     hdr = np.ascontiguousarray(hdr, np.int32)
     El = d.n_experts // d.n_ranks
     G = d.n_waves * El
-    n_recv = len(hdr)
+    n_recv = len(hdr)                       # rows ([n, 4] ids with dedup)
     nb = n_bank_rows(d, n_recv)
     bank_src = np.empty(nb, np.int32)
     bfill = np.empty(G, np.int32)

@@ -213,6 +213,31 @@ static int32_t dest_of(const orc_dims *d, int32_t e) {
   return e / (d->n_experts / d->n_ranks);
 }
 
+/* Variant (dedup): a token's choices on one destination travel as groups
+ * of up to four in one row.  Group position of choice j = the number of the
+ * token's earlier choices on the same destination; positions 0, 4 lead a
+ * row, the others belong to the row of the choice 4 * floor(c / 4). */
+static int32_t dedup_rank(const orc_dims *d, const int32_t *tk, int32_t j) {
+  int32_t c = 0, dj = dest_of(d, tk[j]);
+  for (int32_t i = 0; i < j; ++i) c += dest_of(d, tk[i]) == dj;
+  return c;
+}
+
+/* True for a choice that joins an earlier choice's row; its slot is then
+ * set to that row's (already assigned) slot. */
+static int dedup_follower(const orc_dims *d, const int32_t *tk, int32_t j,
+                          int32_t *slot_row) {
+  int32_t c = dedup_rank(d, tk, j);
+  if (c % 4 == 0) return 0;
+  int32_t dj = dest_of(d, tk[j]), lead = c - c % 4;
+  for (int32_t i = 0; i < j; ++i)
+    if (dest_of(d, tk[i]) == dj && dedup_rank(d, tk, i) == lead) {
+      slot_row[j] = slot_row[i];
+      return 1;
+    }
+  return 0; /* not reached */
+}
+
 /* READING (other wave reading, wave_mode 1): one pool of W*cap_send rows
  * per destination, filled in (token, choice) order; position i lies in chunk
  * (wave) i / cap_send.  fill and demand are reported per chunk: chunk w holds
@@ -227,6 +252,10 @@ static int64_t orc_sender_chunks(const orc_dims *d, const int32_t *topk,
   int64_t *n = (int64_t *)calloc((size_t)R, sizeof(int64_t));
   for (int32_t t = 0; t < d->T; ++t) {
     for (int32_t j = 0; j < k; ++j) {
+      if (d->dedup && dedup_follower(d, topk + (int64_t)t * k, j, slot + (int64_t)t * k)) {
+        drops += slot[(int64_t)t * k + j] < 0;
+        continue;
+      }
       int32_t e = topk[(int64_t)t * k + j];
       int64_t pos = n[dest_of(d, e)]++;
       if (pos < pool) {
@@ -269,6 +298,10 @@ int64_t orc_sender(const orc_dims *d, const int32_t *topk, int32_t *slot,
   for (int32_t t = 0; t < d->T; ++t) {
     int32_t w = t / Tw;
     for (int32_t j = 0; j < k; ++j) {
+      if (d->dedup && dedup_follower(d, topk + (int64_t)t * k, j, slot + (int64_t)t * k)) {
+        drops += slot[(int64_t)t * k + j] < 0;
+        continue;
+      }
       int32_t e = topk[(int64_t)t * k + j];
       int32_t p = dest_of(d, e) * W + w;
       int32_t pos = n[p]++;
@@ -307,6 +340,10 @@ static int32_t get_header(const uint8_t *row, int32_t L) {
   return id;
 }
 
+void orc_row_ids(const uint8_t *row, int32_t L, int32_t *ids) {
+  memcpy(ids, row + (size_t)L * 2, 16);
+}
+
 void orc_pack_rows(const orc_dims *d, const uint16_t *z, const int32_t *topk,
                    const int32_t *slot, const int64_t *pool_offsets,
                    uint8_t *pools, int64_t n_pool_rows) {
@@ -316,6 +353,7 @@ void orc_pack_rows(const orc_dims *d, const uint16_t *z, const int32_t *topk,
   for (int64_t r = 0; r < n_pool_rows; ++r) {
     memset(pools + r * rb, 0, rb - 16);
     put_header(pools + r * rb, L, -1);
+    if (d->dedup) memset(pools + r * rb + (size_t)L * 2, 0xff, 16); /* four empty ids */
   }
   for (int32_t t = 0; t < d->T; ++t) {
     for (int32_t j = 0; j < k; ++j) {
@@ -325,6 +363,17 @@ void orc_pack_rows(const orc_dims *d, const uint16_t *z, const int32_t *topk,
       int32_t p = dest_of(d, e) * W + t / Tw;
       int64_t row = d->cap_send ? (int64_t)p * d->cap_send + s : pool_offsets[p] + s;
       if (d->wave_mode == 1) row = (int64_t)dest_of(d, e) * W * d->cap_send + s;
+      if (d->dedup) {
+        const int32_t *tk = topk + (int64_t)t * k;
+        int32_t c = dedup_rank(d, tk, j);
+        if (c % 4) continue; /* written with its row's leader */
+        int32_t ids[4] = {-1, -1, -1, -1}, m = 0;
+        for (int32_t i = j; i < k && m < 4; ++i)
+          if (dest_of(d, tk[i]) == dest_of(d, e) && dedup_rank(d, tk, i) >= c) ids[m++] = tk[i];
+        memcpy(pools + row * rb, z + (int64_t)t * L, (size_t)L * 2);
+        memcpy(pools + row * rb + (size_t)L * 2, ids, 16);
+        continue;
+      }
       memcpy(pools + row * rb, z + (int64_t)t * L, (size_t)L * 2);
       put_header(pools + row * rb, L, e);
     }
@@ -355,13 +404,16 @@ int64_t orc_bank_slots(const orc_dims *d, int32_t rank, const int32_t *hdr,
   const int32_t G = W * El;
   int32_t *c = (int32_t *)calloc((size_t)G, sizeof(int32_t));
   int32_t bad = 0;
+  /* items: one per receive row, or with dedup one per tail id of each row
+   * (row, id index), in that order */
+  const int32_t per = d->dedup ? 4 : 1;
   /* pass 1: counts */
   for (int32_t w = 0; w < W; ++w) {
     for (int32_t s = 0; s < R; ++s) {
       int64_t a = ragged ? recv_offsets[s * W + w] : ((int64_t)s * W + w) * d->cap_send;
       int64_t b = ragged ? recv_offsets[s * W + w + 1] : a + d->cap_send;
-      for (int64_t row = a; row < b; ++row) {
-        int32_t h = hdr[row];
+      for (int64_t q = a * per; q < b * per; ++q) {
+        int32_t h = hdr[q];
         if (h == -1) continue;
         if (h < 0 || h >= d->n_experts || h / El != rank) {
           ++bad;
@@ -389,13 +441,13 @@ int64_t orc_bank_slots(const orc_dims *d, int32_t rank, const int32_t *hdr,
     for (int32_t s = 0; s < R; ++s) {
       int64_t a = ragged ? recv_offsets[s * W + w] : ((int64_t)s * W + w) * d->cap_send;
       int64_t b = ragged ? recv_offsets[s * W + w + 1] : a + d->cap_send;
-      for (int64_t row = a; row < b; ++row) {
-        int32_t h = hdr[row];
+      for (int64_t q = a * per; q < b * per; ++q) {
+        int32_t h = hdr[q];
         if (h < 0 || h >= d->n_experts || h / El != rank) continue;
         int32_t g = w * El + h % El;
         int32_t p = c[g]++;
-        if (ragged) bank_src[bank_offsets[g] + p] = (int32_t)row;
-        else if (p < cap) bank_src[(int64_t)g * cap + p] = (int32_t)row;
+        if (ragged) bank_src[bank_offsets[g] + p] = (int32_t)q;
+        else if (p < cap) bank_src[(int64_t)g * cap + p] = (int32_t)q;
       }
     }
   }
@@ -415,7 +467,8 @@ void orc_bank_rows(const orc_dims *d, const uint8_t *recv,
     int64_t start = d->cap_send ? (int64_t)g * d->cap_recv : bank_offsets[g];
     for (int32_t p = 0; p < bfill[g]; ++p) {
       int64_t pos = start + p;
-      memcpy(bank + pos * L, recv + (int64_t)bank_src[pos] * rb, (size_t)L * 2);
+      int64_t row = d->dedup ? bank_src[pos] / 4 : bank_src[pos];
+      memcpy(bank + pos * L, recv + row * rb, (size_t)L * 2);
     }
   }
 }
@@ -528,6 +581,7 @@ void orc_combine_tokens(const orc_dims *d, const uint16_t *returned,
         if (s >= ret_offsets[seg + 1] - ret_offsets[seg]) continue;
         row = ret_offsets[seg] + s;
       }
+      if (d->dedup) row = row * 4 + dedup_rank(d, topk + t * k, j) % 4; /* return slot */
       double g = gates[t * k + j];
       for (int32_t c = 0; c < L; ++c) acc[c] += g * bf(returned[row * L + c]);
     }

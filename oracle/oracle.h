@@ -38,10 +38,14 @@ extern "C" {
  * wave).  wave_mode 1 (the other reading of the waves, fixed mode only): one
  * pool of n_waves*cap_send rows per dest, filled in (token, choice) order and
  * cut into n_waves chunks of cap_send rows; chunk w is wave w.  The layout
- * [R][W][cap_send] is the same; slot is then the position in the dest's pool. */
+ * [R][W][cap_send] is the same; slot is then the position in the dest's pool.
+ * dedup 1 (a variant, fixed mode only): a token sends one row per group of up
+ * to four of its choices on one destination; the row's tail holds their ids
+ * in choice order (-1 for unused), every member's slot is the row's position,
+ * and returns come back in four slots per receive row ([rows][4][latent]). */
 typedef struct {
   int32_t T, d_model, latent, n_experts, n_ranks, top_k, n_waves, d_ff,
-      n_shared, d_ff_shared, cap_send, cap_recv, wave_mode;
+      n_shared, d_ff_shared, cap_send, cap_recv, wave_mode, dedup;
 } orc_dims;
 
 /* bf16 <-> double, round to nearest even, straight from double. */
@@ -77,13 +81,17 @@ void orc_pack_rows(const orc_dims *d, const uint16_t *z, const int32_t *topk,
                    const int32_t *slot, const int64_t *pool_offsets,
                    uint8_t *pools, int64_t n_pool_rows);
 
+/* hdr: one tail id per receive row, or with dedup the four ids of each row
+ * ([n_recv_rows][4]); with dedup bank_src holds return slots (row * 4 + id
+ * index). */
 int64_t orc_bank_slots(const orc_dims *d, int32_t rank, const int32_t *hdr,
                        const int64_t *recv_offsets, int64_t n_recv_rows,
                        int64_t *bank_offsets, int32_t *bank_src,
                        int32_t *bfill, int32_t *bdemand, int32_t *bad_rows);
 
-/* Tail id of one pool / receive row. */
+/* Tail id of one pool / receive row; all four tail ids. */
 int32_t orc_row_header(const uint8_t *row, int32_t L);
+void orc_row_ids(const uint8_t *row, int32_t L, int32_t *ids);
 
 void orc_bank_rows(const orc_dims *d, const uint8_t *recv,
                    const int64_t *bank_offsets, const int32_t *bank_src,

@@ -38,6 +38,8 @@ class Workload:
     # "tokens": wave(t) = t / T_w, a pool per (destination, wave); "chunks": one
     # pool of n_waves * C_s rows per destination, cut into n_waves chunks
     waves: str = "tokens"
+    # variant: a token's choices on one destination share one row (up to 4 ids)
+    dedup: bool = False
 
     @property
     def experts_per_rank(self) -> int:

@@ -77,22 +77,23 @@ def simulate(orc, cfg):
                 lens.append(b - a)
         recv = np.concatenate(parts)
         ro = None if d.cap_send else np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
-        bs = orc.bank_slots(d, r, orc.headers(recv, L), ro)
+        bs = orc.bank_slots(d, r, orc.recv_ids(d, recv), ro)
         assert bs["bad_rows"] == 0
         bank = orc.bank_rows(d, recv, bs["bank_offsets"], bs["bank_src"], bs["bfill"])
         ret = orc.expert_ffn(d, bank, bs["bank_offsets"], bs["bank_src"], bs["bfill"],
-                             *ex[r], len(recv))
+                             *ex[r], len(recv) * (4 if d.dedup else 1))
         RET.append(ret); RO.append(ro); BK.append(dict(bs, bank=bank))
 
-    # exact return and combine
+    # exact return and combine (with dedup, four return slots per row)
     OUT = []
+    per = 4 if d.dedup else 1
     for s in range(R):
         parts = []
         for dst in range(R):
             for w in range(W):
                 if d.cap_send:
-                    a = (s * W + w) * d.cap_send
-                    parts.append(RET[dst][a:a + d.cap_send])
+                    a = (s * W + w) * d.cap_send * per
+                    parts.append(RET[dst][a:a + d.cap_send * per])
                 else:
                     parts.append(RET[dst][RO[dst][s * W + w]:RO[dst][s * W + w + 1]])
         returned = np.concatenate(parts)
@@ -117,6 +118,21 @@ def brute_force(cfg, d, W_, S):
     for s in range(R):
         topk = S[s]["topk"]
         key = topk // El if chunks else (topk // El) * Wv + (np.arange(T) // Tw)[:, None]
+        if cfg.dedup:   # rows: groups of up to 4 same-destination choices of a token
+            pos = np.zeros((T, k), int)
+            nxt = {}
+            for t in range(T):
+                lead = {}
+                for j in range(k):
+                    dst = int(topk[t, j]) // El
+                    c = int((topk[t, :j] // El == dst).sum())
+                    if c % 4 == 0:
+                        kk = int(key[t, j])
+                        lead[(dst, c // 4)] = nxt.get(kk, 0)
+                        nxt[kk] = lead[(dst, c // 4)] + 1
+                    pos[t, j] = lead[(dst, c // 4)]
+            send_pos.append(pos)
+            continue
         flat = key.reshape(-1)
         pos = np.zeros_like(flat)
         for kk in np.unique(flat):
@@ -164,7 +180,8 @@ def brute_force(cfg, d, W_, S):
     return outs
 
 
-@pytest.mark.parametrize("cf", ["1.10/1.15", "inf", "tight", "chunks", "chunks_tight"])
+@pytest.mark.parametrize("cf", ["1.10/1.15", "inf", "tight", "chunks", "chunks_tight", "dedup_tight",
+                                "dedup_chunks"])
 def test_e2e_tiny_matches_brute_force(orc, cf):
     from dataclasses import replace
     from fractions import Fraction
@@ -173,8 +190,10 @@ def test_e2e_tiny_matches_brute_force(orc, cf):
         cfg = replace(cfg, cf_send=None, cf_recv=None)
     elif cf.endswith("tight"):   # forces sender and receiver drops
         cfg = replace(cfg, cf_send=Fraction(1, 2), cf_recv=Fraction(1, 2))
-    if cf.startswith("chunks"):  # the other reading of the waves
+    if "chunks" in cf:           # the other reading of the waves
         cfg = replace(cfg, waves="chunks")
+    if cf.startswith("dedup"):   # one row per destination group of a token's choices
+        cfg = replace(cfg, dedup=True)
     d, W_, S, BK, OUT = simulate(orc, cfg)
     ref = brute_force(cfg, d, W_, S)
     El, W, Tw = cfg.experts_per_rank, cfg.n_waves, math.ceil(cfg.T / cfg.n_waves)
@@ -198,6 +217,9 @@ def test_e2e_tiny_matches_brute_force(orc, cf):
                 else:
                     lens = [S[q]["demand"][r * W + ww] for q in range(cfg.n_ranks) for ww in range(W)]
                     row = int(np.sum(lens[:s * W + w])) + sl
+                if d.dedup:           # bank_src holds return slots: row * 4 + index in the row
+                    c = int((S[s]["topk"][t, :j] // El == r).sum())
+                    row = row * 4 + c % 4
                 kept_o[t, j] = row in set(BK[r]["bank_src"].tolist())
         assert (kept_o == keep).all()
         total_drop += (~keep).sum()

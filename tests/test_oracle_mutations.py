@@ -69,6 +69,15 @@ MUTATIONS = [
     ("chunk combine row",
      "        row = (int64_t)dest_of(d, e) * W * d->cap_send + s; /* slot: position in the dest's pool */",
      "        row = (int64_t)seg * d->cap_send + s % d->cap_send;", "test_oracle_e2e.py"),
+    ("dedup groups of three", "  if (c % 4 == 0) return 0;", "  if (c % 3 == 0) return 0;",
+     "test_oracle_pins.py"),
+    ("dedup row without its leader's id",
+     "if (dest_of(d, tk[i]) == dest_of(d, e) && dedup_rank(d, tk, i) >= c) ids[m++] = tk[i];",
+     "if (dest_of(d, tk[i]) == dest_of(d, e) && dedup_rank(d, tk, i) > c) ids[m++] = tk[i];",
+     "test_oracle_pins.py"),
+    ("dedup return slot ignored",
+     "      if (d->dedup) row = row * 4 + dedup_rank(d, topk + t * k, j) % 4; /* return slot */",
+     "      if (d->dedup) row = row * 4; /* return slot */", "test_oracle_e2e.py"),
     ("silu derivative", "  return s * (1.0 + a * (1.0 - s));", "  return s;", BWD),
     ("shared d_b from b", "d_shared[(t * 2 * S + S + sh) * Fs + f] = to_bf(dh * silu(a));",
      "d_shared[(t * 2 * S + S + sh) * Fs + f] = to_bf(dh * b);", BWD),

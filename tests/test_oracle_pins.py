@@ -511,3 +511,122 @@ def test_combine_ragged_bounds(orc):
     assert np.array_equal(f64(ylat[0]), r[0] + r[3])
     assert np.array_equal(f64(ylat[1]), r[1])            # slot 5 >= len 2 -> zero
     assert np.array_equal(f64(ylat[2]), r[2] + r[4])
+
+
+# ----------------------------------------------------------------------------
+# dedup variant: one row per group of up to four same-destination choices
+# ----------------------------------------------------------------------------
+
+def _dedup_dims(orc, **kw):
+    d = _tiny_dims(orc, **kw)
+    d.dedup = 1
+    return d
+
+
+def _skewed_topk(rng, T, E, k, R):
+    """Choices that often share a destination (several experts of one rank)."""
+    El = E // R
+    out = []
+    for _ in range(T):
+        ranks = rng.choice(R, 2, replace=False)
+        pool = np.concatenate([r * El + np.arange(El) for r in ranks])
+        out.append(rng.permutation(pool)[:k])
+    return np.array(out, np.int32)
+
+
+def test_sender_dedup_brute_force(orc):
+    rng = np.random.default_rng(16)
+    for cs in (1, 2, 3, 6):
+        d = _dedup_dims(orc, T=31, E=24, R=4, k=8, cs=cs)
+        topk = _skewed_topk(rng, d.T, d.n_experts, d.top_k, d.n_ranks)
+        r = orc.sender(d, topk)
+        El, Tw, W = d.n_experts // d.n_ranks, math.ceil(d.T / d.n_waves), d.n_waves
+        rows = []                                 # (pool, members) in token order
+        for t in range(d.T):
+            seen = {}
+            for j in range(d.top_k):
+                dst = int(topk[t, j]) // El
+                c = seen.get(dst, 0)
+                seen[dst] = c + 1
+                if c % 4 == 0:
+                    rows.append([dst * W + t // Tw, [(t, j)]])
+                else:
+                    [row for row in rows if row[0] == dst * W + t // Tw and row[1][0][0] == t
+                     and int(topk[t, row[1][0][1]]) // El == dst][-1][1].append((t, j))
+        n = {}
+        want = np.full((d.T, d.top_k), -9)
+        for p, members in rows:
+            pos = n.get(p, 0)
+            n[p] = pos + 1
+            for t, j in members:
+                want[t, j] = pos if pos < cs else -1
+        assert (r["slot"] == want).all()
+        assert r["drops"] == (want < 0).sum()
+        dem = np.zeros(d.n_ranks * W, int)
+        for p, _ in rows:
+            dem[p] += 1
+        assert (r["demand"] == dem).all() and (r["fill"] == np.minimum(dem, cs)).all()
+        assert max(len(m) for _, m in rows) <= 4
+        # rows never outnumber assignments; a kept plain assignment stays kept
+        plain = orc.sender(_tiny_dims(orc, T=31, E=24, R=4, k=8, cs=cs), topk)["slot"] >= 0
+        assert ((r["slot"] >= 0) | ~plain).all()
+        assert r["demand"].sum() < d.T * d.top_k
+
+
+def test_pack_rows_dedup_ids(orc):
+    rng = np.random.default_rng(17)
+    d = _dedup_dims(orc, T=30, E=24, R=4, k=8, cs=5)
+    topk = _skewed_topk(rng, d.T, d.n_experts, d.top_k, d.n_ranks)
+    z = rng.integers(0, 2 ** 16, (d.T, d.latent)).astype(np.uint16)
+    s = orc.sender(d, topk)
+    pools = orc.pack_rows(d, z, topk, s["slot"])
+    ids = orc.row_ids(pools, d.latent)
+    El, Tw, W = d.n_experts // d.n_ranks, math.ceil(d.T / d.n_waves), d.n_waves
+    found = {}
+    for row in range(len(pools)):
+        got = [int(v) for v in ids[row] if v != -1]
+        assert all(v == -1 for v in ids[row][len(got):])       # ids first, then padding
+        for v in got:
+            found.setdefault(v, []).append(row)
+    for t in range(d.T):
+        for j in range(d.top_k):
+            if s["slot"][t, j] < 0:
+                continue
+            e = int(topk[t, j])
+            row = ((e // El) * W + t // Tw) * d.cap_send + s["slot"][t, j]
+            assert row in found[e]
+            assert (pools[row, :2 * d.latent].view(np.uint16) == z[t]).all()
+            mine = [int(v) for v in ids[row] if v != -1]
+            order = [int(v) for v in topk[t] if v in mine]
+            assert mine == order                              # choice order
+    assert sum(len(v) for v in found.values()) == (s["slot"] >= 0).sum()
+
+
+def test_bank_dedup_items(orc):
+    """With dedup each id of a receive row is an item, in (source, row, id
+    index) order within a wave; bank_src = row * 4 + id index."""
+    rng = np.random.default_rng(18)
+    d = _dedup_dims(orc, T=23, E=12, R=4, k=3, cs=4, cr=3)
+    El, W = d.n_experts // d.n_ranks, d.n_waves
+    n = d.n_ranks * W * d.cap_send
+    ids = -np.ones((n, 4), np.int32)
+    for row in range(n):
+        m = rng.integers(0, 4)
+        ids[row, :m] = rng.permutation(El)[:m] + 1 * El           # rank 1's experts
+    bo = orc.bank_slots(d, 1, ids, None)
+    c = {}
+    want = -np.ones_like(bo["bank_src"])
+    for w in range(W):
+        for s_ in range(d.n_ranks):
+            for i in range(d.cap_send):
+                row = (s_ * W + w) * d.cap_send + i
+                for q in range(4):
+                    if ids[row, q] < 0:
+                        continue
+                    g = w * El + ids[row, q] % El
+                    p = c.get(g, 0)
+                    c[g] = p + 1
+                    if p < d.cap_recv:
+                        want[g * d.cap_recv + p] = row * 4 + q
+    assert (bo["bank_src"] == want).all()
+    assert bo["bad_rows"] == 0
