@@ -27,7 +27,7 @@ class MoeError(RuntimeError):
 class MoeDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "d_model", "latent", "n_experts", "n_ranks", "top_k", "n_waves",
-        "d_ff", "n_shared", "d_ff_shared", "cap_send", "cap_recv", "wave_mode")]
+        "d_ff", "n_shared", "d_ff_shared", "cap_send", "cap_recv", "wave_mode", "dedup")]
 
     def __repr__(self):
         return "MoeDims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"

@@ -51,6 +51,9 @@ int check_dims(const moe_dims *d) {
     return fail(MOE_ERR_INVALID, "dims: wave_mode must be MOE_WAVES_TOKENS or MOE_WAVES_CHUNKS");
   if (d->wave_mode == MOE_WAVES_CHUNKS && d->cap_send == 0)
     return fail(MOE_ERR_INVALID, "dims: chunked waves need fixed capacities");
+  if (d->dedup != 0 && d->dedup != 1) return fail(MOE_ERR_INVALID, "dims: dedup must be 0 or 1");
+  if (d->dedup && d->cap_send == 0)
+    return fail(MOE_ERR_INVALID, "dims: dedup needs fixed capacities");
   if (d->n_experts > 1024 || d->top_k > 32)
     return fail(MOE_ERR_UNSUPPORTED, "dims: n_experts <= 1024 and top_k <= 32 supported");
   if (d->latent % 64 || d->d_model % 64)
@@ -154,13 +157,13 @@ int64_t moe_workspace_bytes(const moe_dims *d, int call, int64_t n_rows) {
     case MOE_CALL_PACK:  // per-tile key counts of the sender slot assignment
       return rank_ws_bytes((int64_t)d->T * d->top_k, (int)(R * W));
     case MOE_CALL_BANK: {  // per-tile key counts of the receiver slot assignment
-      int64_t items = ragged(*d) ? n_rows : R * W * d->cap_send;
+      int64_t items = ragged(*d) ? n_rows : R * W * d->cap_send * ret_slots(*d);
       if (items < 0) return fail(MOE_ERR_INVALID, "moe_workspace_bytes: n_rows < 0");
       return rank_ws_bytes(items, (int)(W * El));
     }
     case MOE_CALL_FFN: {  // intermediate h, return-row flags, split partial tiles
       int64_t bank_rows = ragged(*d) ? n_rows : W * El * d->cap_recv;
-      int64_t ret_rows = ragged(*d) ? n_rows : R * W * d->cap_send;
+      int64_t ret_rows = ragged(*d) ? n_rows : R * W * d->cap_send * ret_slots(*d);
       if (bank_rows < 0) return fail(MOE_ERR_INVALID, "moe_workspace_bytes: n_rows < 0");
       return ffn_h_bytes(*d, bank_rows) + ffn_flag_bytes(ret_rows) + gemm_split_bytes();
     }
@@ -171,7 +174,8 @@ int64_t moe_workspace_bytes(const moe_dims *d, int call, int64_t n_rows) {
     case MOE_CALL_COMBINE_BWD:
     case MOE_CALL_FFN_BWD:
     case MOE_CALL_PACK_BWD:  // transposed operands, intermediates, split partial tiles
-      if (ragged(*d)) return fail(MOE_ERR_UNSUPPORTED, "moe_workspace_bytes: backward needs fixed capacities");
+      if (ragged(*d) || d->dedup)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_workspace_bytes: backward needs fixed capacities, no dedup");
       return bwd_ws_bytes(*d, call);
     default:
       return fail(MOE_ERR_INVALID, "moe_workspace_bytes: unknown call %d", call);

@@ -318,7 +318,8 @@ int64_t bwd_ws_bytes(const moe_dims &d, int call) {
 static int check_bwd(const moe_dims *d, int call, const char *name, const void *ws,
                      int64_t ws_bytes) {
   MOE_TRY(check_dims(d));
-  if (ragged(*d)) return fail(MOE_ERR_UNSUPPORTED, "%s: fixed capacities only", name);
+  if (ragged(*d) || d->dedup)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: fixed capacities only, no dedup", name);
   MOE_TRY(check_ptr(ws, "ws"));
   const int64_t need = bwd_ws_bytes(*d, call);
   if (ws_bytes < need)

@@ -28,6 +28,7 @@ struct RecvSrc {
   const int64_t *offs;  // ragged: [R*W+1], segment (s, w) at s*W + w
   int64_t RB;
   int L, R, W, El, E, rank, cap_send;
+  int dedup;  // items are (row, tail id index): four per row (fixed mode)
   const int64_t *vstart;  // ragged: first item of segment (w, s) in item order, in LDS
   __device__ void prepare(int64_t *sc) {
     if (!RAGGED) return;
@@ -43,6 +44,8 @@ struct RecvSrc {
   __device__ int32_t key(int64_t q, int32_t &aux) const {
     int64_t row;
     int w;
+    const int idx = dedup ? (int)(q & 3) : 0;  // dedup: which of the row's four ids
+    if (dedup) q >>= 2;
     if (!RAGGED) {
       const int64_t per = (int64_t)R * cap_send;
       w = (int)(q / per);
@@ -61,8 +64,8 @@ struct RecvSrc {
       w = lo / R;
       row = offs[s * W + w] + (q - vstart[lo]);
     }
-    aux = (int32_t)row;
-    const int h = *reinterpret_cast<const int32_t *>(recv + row * RB + 2 * (int64_t)L);
+    aux = (int32_t)(dedup ? row * 4 + idx : row);  // bank_src: receive row, or return slot
+    const int h = *reinterpret_cast<const int32_t *>(recv + row * RB + 2 * (int64_t)L + 4 * idx);
     if (h == -1) return KEY_NONE;
     if (h < 0 || h >= E || h / El != rank) return KEY_BAD;
     return w * El + h % El;
@@ -104,10 +107,10 @@ template <int CH>
 __global__ __launch_bounds__(256) void bank_rows_kernel(const uint8_t *__restrict__ recv,
                                                         const int32_t *__restrict__ bank_src,
                                                         uint16_t *__restrict__ bank, int L,
-                                                        int64_t n_pos) {
+                                                        int64_t n_pos, int src_shift) {
   const int64_t pos = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pos >= n_pos) return;
-  const int src = bank_src[pos];
+  const int src = bank_src[pos] >> src_shift;  // dedup: return slot -> receive row
   if (src < 0) return;
   const u32x4 *in = reinterpret_cast<const u32x4 *>(recv + (int64_t)src * (2 * (int64_t)L + 16));
   u32x4 *out = reinterpret_cast<u32x4 *>(bank + pos * L);
@@ -131,7 +134,7 @@ template <int CH>
 static int bank_copy(const moe_dims &d, const uint8_t *recv, const int32_t *bank_src,
                      uint16_t *bank, int64_t n_bank, hipStream_t s) {
   return launch("bank_rows", bank_rows_kernel<CH>, dim3((unsigned)cdiv(n_bank, 4)), dim3(256), 0,
-                s, recv, bank_src, bank, d.latent, n_bank);
+                s, recv, bank_src, bank, d.latent, n_bank, d.dedup ? 2 : 0);
 }
 
 template <bool RAGGED>
@@ -143,7 +146,7 @@ static int bank_slots(const moe_dims &d, int rank, const uint8_t *recv,
   const int tiles = (int)rank_tiles(n_items);
   RecvSrc<RAGGED> src{recv,      recv_offsets,  row_bytes(d), d.latent, d.n_ranks,
                       d.n_waves, experts_per_rank(d), d.n_experts, rank, d.cap_send,
-                      nullptr};
+                      RAGGED ? 0 : d.dedup, nullptr};
   BankEmit<RAGGED> em{bank_src, bfill, bdemand, bad_rows, bank_offsets, d.cap_recv};
   MOE_TRY(launch("rank_count_bank", rank_count<RecvSrc<RAGGED>>, dim3(tiles), dim3(RK_THREADS), 0,
                  s, src, n_items, K, tc, bank_src, n_bank));
@@ -190,8 +193,8 @@ extern "C" int moe_bank(const moe_dims *d, int32_t rank, const uint8_t *recv,
   int32_t *tc = (int32_t *)ws;
   MOE_TRY(rg ? bank_slots<true>(*d, rank, recv, recv_offsets, n_recv_rows, n_bank, bank_src, bfill,
                                 bdemand, bank_offsets, bad_rows, tc, s)
-             : bank_slots<false>(*d, rank, recv, nullptr, n_recv_rows, n_bank, bank_src, bfill,
-                                 bdemand, nullptr, bad_rows, tc, s));
+             : bank_slots<false>(*d, rank, recv, nullptr, n_recv_rows * ret_slots(*d), n_bank,
+                                 bank_src, bfill, bdemand, nullptr, bad_rows, tc, s));
   const int ch = (int)cdiv(d->latent / 8, 64);  // latent <= 8192 (check_dims)
   auto run = [&](auto kernel_ch) {
     constexpr int CH = decltype(kernel_ch)::value;

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void combine_gather_kernel(
     const uint16_t *__restrict__ returned, const int64_t *__restrict__ ret_offsets,
     const int32_t *__restrict__ topk, const int32_t *__restrict__ slot,
     const float *__restrict__ gates, uint16_t *__restrict__ ylat, int T, int k, int L, int El,
-    int Wk, int Tw, int pool_rows, int cap, int parts) {
+    int Wk, int Tw, int pool_rows, int cap, int parts, int dedup) {
   const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);  // < 2^31: T <= 2^27, parts <= 16
   const int t = wv / parts;
   if (t >= T) return;
@@ -40,6 +40,14 @@ __global__ __launch_bounds__(256) void combine_gather_kernel(
   const int nch = L / 8, c0 = (wv - t * parts) * 64 * CH + lane;  // this lane's first chunk
   int64_t my_row = -1;
   float my_g = 0.f;
+  int my_c = 0;  // dedup: index among the token's same-destination choices
+  if (dedup) {
+    const int dst = lane < k ? topk[(int64_t)t * k + lane] / El : -1;
+    for (int j = 0; j < k; ++j) {
+      const int dj = __shfl(dst, j);
+      if (dj == dst && j < lane) ++my_c;
+    }
+  }
   if (lane < k) {
     // the three loads are independent: issued together, one round trip
     const int s = slot[(int64_t)t * k + lane];
@@ -49,6 +57,7 @@ __global__ __launch_bounds__(256) void combine_gather_kernel(
       const int p = (e / El) * Wk + t / Tw;
       if (cap) {
         my_row = (int64_t)p * pool_rows + s;
+        if (dedup) my_row = my_row * 4 + (my_c & 3);  // the choice's return slot
       } else if (s < ret_offsets[p + 1] - ret_offsets[p]) {
         my_row = ret_offsets[p] + s;
       }
@@ -103,7 +112,7 @@ static int gather(const moe_dims &d, const uint16_t *returned, const int64_t *re
   return launch("combine_gather", combine_gather_kernel<CH>,
                 dim3((unsigned)cdiv((int64_t)d.T * parts, 4)), dim3(256), 0, s, returned,
                 ret_offsets, topk, slot, gates, ylat, d.T, d.top_k, d.latent,
-                experts_per_rank(d), pk.Wk, pk.Tw, pk.rows, d.cap_send, parts);
+                experts_per_rank(d), pk.Wk, pk.Tw, pk.rows, d.cap_send, parts, d.dedup);
 }
 
 int combine_gather_rows(const moe_dims &d, const uint16_t *rows, const int64_t *offsets,

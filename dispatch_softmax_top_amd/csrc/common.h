@@ -23,6 +23,8 @@ int check_ptr(const void *p, const char *name, bool may_be_null = false);
 inline int32_t experts_per_rank(const moe_dims &d) { return d.n_experts / d.n_ranks; }
 inline int32_t tokens_per_wave(const moe_dims &d) { return (d.T + d.n_waves - 1) / d.n_waves; }
 inline bool ragged(const moe_dims &d) { return d.cap_send == 0; }
+// Return rows per receive row: 4 with dedup (one per tail id), else 1.
+inline int ret_slots(const moe_dims &d) { return d.dedup ? 4 : 1; }
 inline int64_t row_bytes(const moe_dims &d) { return 2 * (int64_t)d.latent + 16; }
 // How a (token, choice) assignment finds its sender pool: key = dest * Wk +
 // t / Tw, row = key * rows + slot.  Waves by token: (W, T_w, C_s).  Chunked

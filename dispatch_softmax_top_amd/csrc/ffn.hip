@@ -78,8 +78,8 @@ extern "C" int moe_expert_ffn(const moe_dims *d, const moe_bf16 *bank, const int
   } else {
     if (n_bank_rows != (int64_t)d->n_waves * experts_per_rank(*d) * d->cap_recv)
       return fail(MOE_ERR_INVALID, "moe_expert_ffn: fixed mode needs n_bank_rows == n_waves*E_l*cap_recv");
-    if (n_ret_rows != (int64_t)d->n_ranks * d->n_waves * d->cap_send)
-      return fail(MOE_ERR_INVALID, "moe_expert_ffn: fixed mode needs n_ret_rows == n_ranks*n_waves*cap_send");
+    if (n_ret_rows != (int64_t)d->n_ranks * d->n_waves * d->cap_send * ret_slots(*d))
+      return fail(MOE_ERR_INVALID, "moe_expert_ffn: fixed mode needs n_ret_rows == n_ranks*n_waves*cap_send (*4 with dedup)");
   }
   const int64_t need = moe_workspace_bytes(d, MOE_CALL_FFN, n_bank_rows);
   if (need < 0) return (int)need;

@@ -30,18 +30,53 @@
 
 namespace moe {
 
+// Index of choice j among the token's earlier choices on the same
+// destination (the dedup variant groups them four to a row).
+__device__ __forceinline__ int dedup_rank(const int32_t *tk, int j, int El) {
+  const int dj = tk[j] / El;
+  int c = 0;
+  for (int i = 0; i < j; ++i) c += tk[i] / El == dj;
+  return c;
+}
+
 struct SenderSrc {
   const int32_t *topk;
-  int k, E, El, W, Tw;
+  int k, E, El, W, Tw, dedup;
   __device__ void prepare(int64_t *) {}
   __device__ int32_t key(int64_t item, int32_t &aux) const {
     aux = 0;
     const int e = topk[item];
     if ((unsigned)e >= (unsigned)E) return KEY_BAD;  // not a valid choice: never kept
     const int t = (int)(item / k);
+    // dedup: only a row's first choice takes a position; the others join it
+    if (dedup && dedup_rank(topk + (int64_t)t * k, (int)(item - (int64_t)t * k), El) % 4)
+      return KEY_NONE;
     return (e / El) * W + t / Tw;
   }
 };
+
+// dedup: every choice that joined a row takes the slot of the row's first
+// choice (assigned by rank_assign before).  One thread per choice.
+__global__ __launch_bounds__(256) void dedup_follow_kernel(const int32_t *__restrict__ topk,
+                                                           int32_t *__restrict__ slot, int64_t n,
+                                                           int k, int El) {
+  const int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (it >= n) return;
+  const int64_t t0 = it - it % k;
+  const int j = (int)(it - t0);
+  const int32_t *tk = topk + t0;
+  const int c = dedup_rank(tk, j, El);
+  if (c % 4 == 0) return;
+  const int dj = tk[j] / El, lead = c - c % 4;
+  for (int i = 0, r = 0; i < j; ++i)
+    if (tk[i] / El == dj) {
+      if (r == lead) {
+        slot[it] = slot[t0 + i];
+        return;
+      }
+      ++r;
+    }
+}
 
 // chunks = W when the key is the destination alone (its pool holds W chunks
 // of cap rows), 0 when the key already names the wave.
@@ -82,7 +117,8 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(
     const uint16_t *__restrict__ z, const int32_t *__restrict__ topk,
     const int32_t *__restrict__ slot, const int32_t *__restrict__ fill,
     const int64_t *__restrict__ pool_offsets, uint8_t *__restrict__ pools, int T, int k, int L,
-    int El, int Wk, int Tw, int pool_rows, int cap, int token_blocks, int64_t n_slots) {
+    int El, int Wk, int Tw, int pool_rows, int cap, int token_blocks, int64_t n_slots,
+    int dedup) {
   const int64_t RB = 2 * (int64_t)L + 16;
   const int lane = lane_id();
   if ((int)blockIdx.x < token_blocks) {
@@ -94,14 +130,41 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(
 #pragma unroll
     for (int c = 0; c < CH; ++c) v[c] = src[min(lane + 64 * c, nch - 1)];
     int my_row = -1, my_e = -1;
+    int s = -1, e = -1;
     if (lane < k) {
-      const int s = slot[(int64_t)t * k + lane];
-      const int e = topk[(int64_t)t * k + lane];  // independent of s: same round trip
+      s = slot[(int64_t)t * k + lane];
+      e = topk[(int64_t)t * k + lane];  // independent of s: same round trip
       if (s >= 0) {
         const int p = (e / El) * Wk + t / Tw;
         my_row = cap ? p * pool_rows + s : (int)pool_offsets[p] + s;
         my_e = e;
       }
+    }
+    u32x4 hdr = {(uint32_t)my_e, 0u, 0u, 0u};
+    if (dedup) {
+      // this lane's index among same-destination choices; a row's first
+      // choice writes the row with the ids of its group (up to four, in
+      // choice order), the others write nothing
+      const int dst = lane < k ? e / El : -1;
+      int c = 0;
+      for (int j = 0; j < k; ++j) {
+        const int dj = __shfl(dst, j);
+        if (dj == dst && j < lane) ++c;
+      }
+      // a leader (c % 4 == 0) collects the choices ranked c .. c + 3 on its
+      // destination: id number cj - c of its row
+      int id0 = -1, id1 = -1, id2 = -1, id3 = -1;
+      for (int j = 0; j < k; ++j) {
+        const int dj = __shfl(dst, j), ej = __shfl(e, j), cj = __shfl(c, j);
+        if (dj != dst || (c & 3)) continue;
+        const int q = cj - c;
+        if (q == 0) id0 = ej;
+        if (q == 1) id1 = ej;
+        if (q == 2) id2 = ej;
+        if (q == 3) id3 = ej;
+      }
+      if (c & 3) my_row = -1;
+      hdr = u32x4{(uint32_t)id0, (uint32_t)id1, (uint32_t)id2, (uint32_t)id3};
     }
     for (int j = 0; j < k; ++j) {
       const int row = __shfl(my_row, j);
@@ -116,16 +179,14 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(
           if (lane + 64 * c < nch) dst[lane + 64 * c] = v[c];
       }
     }
-    if (my_row >= 0) {
-      u32x4 h = {(uint32_t)my_e, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4 *>(pools + my_row * RB + 2 * (int64_t)L) = h;
-    }
+    if (my_row >= 0) *reinterpret_cast<u32x4 *>(pools + my_row * RB + 2 * (int64_t)L) = hdr;
   } else {
     const int64_t idx = (int64_t)(blockIdx.x - token_blocks) * 256 + threadIdx.x;
     if (idx >= n_slots) return;
     const int p = (int)(idx / cap), i = (int)(idx - (int64_t)p * cap);
     if (i >= fill[p]) {
-      u32x4 h = {0xffffffffu, 0u, 0u, 0u};
+      const uint32_t more = dedup ? 0xffffffffu : 0u;  // dedup: four empty ids
+      u32x4 h = {0xffffffffu, more, more, more};
       *reinterpret_cast<u32x4 *>(pools + idx * RB + 2 * (int64_t)L) = h;
     }
   }
@@ -139,7 +200,8 @@ static int pack_copy(const moe_dims &d, const uint16_t *z, const int32_t *topk,
   const PoolKey pk = pool_key(d);
   return launch("pack_rows", pack_rows_kernel<CH>, dim3((unsigned)blocks), dim3(256), 0, s, z,
                 topk, slot, fill, pool_offsets, pools, d.T, d.top_k, d.latent,
-                experts_per_rank(d), pk.Wk, pk.Tw, pk.rows, d.cap_send, token_blocks, n_slots);
+                experts_per_rank(d), pk.Wk, pk.Tw, pk.rows, d.cap_send, token_blocks, n_slots,
+                d.dedup);
 }
 
 template <bool RAGGED>
@@ -150,13 +212,16 @@ static int sender_slots(const moe_dims &d, const int32_t *topk, int32_t *slot, i
   const PoolKey pk = pool_key(d);
   const int K = d.n_ranks * pk.Wk;
   const int tiles = (int)rank_tiles(n);
-  SenderSrc src{topk, d.top_k, d.n_experts, experts_per_rank(d), pk.Wk, pk.Tw};
+  SenderSrc src{topk, d.top_k, d.n_experts, experts_per_rank(d), pk.Wk, pk.Tw, d.dedup};
   SenderEmit<RAGGED> em{slot, fill, demand, pool_offsets, d.cap_send,
                         d.wave_mode == MOE_WAVES_CHUNKS ? d.n_waves : 0};
   MOE_TRY(launch("rank_count_sender", rank_count<SenderSrc>, dim3(tiles), dim3(RK_THREADS), 0, s,
                  src, n, K, tile_counts, (int32_t *)nullptr, (int64_t)0));
-  return launch("rank_assign_sender", rank_assign<SenderSrc, SenderEmit<RAGGED>>, dim3(tiles),
-                dim3(RK_THREADS), 0, s, src, em, n, K, tiles, (const int32_t *)tile_counts);
+  MOE_TRY(launch("rank_assign_sender", rank_assign<SenderSrc, SenderEmit<RAGGED>>, dim3(tiles),
+                 dim3(RK_THREADS), 0, s, src, em, n, K, tiles, (const int32_t *)tile_counts));
+  if (!d.dedup) return MOE_OK;
+  return launch("dedup_follow", dedup_follow_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s,
+                topk, slot, n, d.top_k, experts_per_rank(d));
 }
 
 }  // namespace moe

@@ -22,7 +22,8 @@ def make_dims(cfg, T=None) -> L.MoeDims:
     T = cfg.T if T is None else T
     waves = {"tokens": L.MOE_WAVES_TOKENS, "chunks": L.MOE_WAVES_CHUNKS}[cfg.waves]
     d = L.MoeDims(T, cfg.d_model, cfg.latent, cfg.n_experts, cfg.n_ranks, cfg.top_k,
-                  cfg.n_waves, cfg.d_ff, cfg.n_shared, cfg.d_ff_shared, 0, 0, waves)
+                  cfg.n_waves, cfg.d_ff, cfg.n_shared, cfg.d_ff_shared, 0, 0, waves,
+                  int(getattr(cfg, "dedup", False)))
     if cfg.cf_send is not None:
         d.cap_send, d.cap_recv = L.moe_capacity(d, Fraction(cfg.cf_send), Fraction(cfg.cf_recv))
     return d
@@ -92,7 +93,9 @@ class Receiver:
         self.bfill = torch.empty(G, dtype=torch.int32, device=dev)
         self.bdemand = torch.empty(G, dtype=torch.int32, device=dev)
         self.bad_rows = torch.empty(4, dtype=torch.int32, device=dev)
-        self.ret = torch.empty(n_recv_rows, d.latent, dtype=torch.bfloat16, device=dev)
+        # return rows: one per receive row, four (one per tail id) with dedup
+        self.n_ret_rows = n_recv_rows * (4 if d.dedup else 1)
+        self.ret = torch.empty(self.n_ret_rows, d.latent, dtype=torch.bfloat16, device=dev)
         self.ws_bank = _ws(d, L.MOE_CALL_BANK, n_recv_rows, dev)
         self.ws_ffn = _ws(d, L.MOE_CALL_FFN, self.n_bank_rows, dev)
 
@@ -103,7 +106,7 @@ class Receiver:
 
     def ffn(self, w_gate, w_up, w_down, stream=None):
         L.moe_expert_ffn(self.d, self.bank, self.bank_offsets, self.bank_src, self.bfill,
-                         self.n_bank_rows, w_gate, w_up, w_down, self.ret, self.n_recv_rows,
+                         self.n_bank_rows, w_gate, w_up, w_down, self.ret, self.n_ret_rows,
                          self.ws_ffn, stream)
 
 

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef uint16_t moe_bf16;
 
@@ -87,10 +87,20 @@ typedef enum {
  * d_model % 64 == 0, d_ff % 128 == 0, d_ff_shared % 128 == 0,
  * n_ranks * n_waves <= 1024, n_waves * E_l <= 1024, n_shared <= 4.
  * wave_mode: MOE_WAVES_TOKENS (0) or MOE_WAVES_CHUNKS (1, needs fixed
- * mode); the two readings of how a shard is sent in waves. */
+ * mode); the two readings of how a shard is sent in waves.
+ * dedup: 0, or 1 for the variant where a token's choices on one destination
+ * share rows: one row per group of up to four of them (in choice order),
+ * whose tail holds their four global ids {e0, e1, e2, e3} (-1 unused; an
+ * empty row is all -1).  Every member's slot is its row's position; pool
+ * capacities count rows.  The bank takes one item per id, in (source, row,
+ * id index) order; bank_src then holds return slots (receive row * 4 + id
+ * index) and the return buffer has four latent rows per receive row
+ * ([n_recv_rows * 4][latent]); the combine reads slot row * 4 + (the
+ * choice's index among the token's same-destination choices) % 4.  Fixed
+ * mode only; the backward calls do not take it. */
 typedef struct {
   int32_t T, d_model, latent, n_experts, n_ranks, top_k, n_waves, d_ff,
-      n_shared, d_ff_shared, cap_send, cap_recv, wave_mode;
+      n_shared, d_ff_shared, cap_send, cap_recv, wave_mode, dedup;
 } moe_dims;
 
 enum { MOE_WAVES_TOKENS = 0, MOE_WAVES_CHUNKS = 1 };

@@ -39,6 +39,11 @@ def chunked(cfg):
     return replace(cfg, name=cfg.name + "_chunks", waves="chunks")
 
 
+def deduped(cfg):
+    """The dedup variant: a token's same-destination choices share rows."""
+    return replace(cfg, name=cfg.name + "_dedup", dedup=True)
+
+
 def shard_inputs(cfg, s, device="cpu"):
     x = gen.hidden(cfg, s, device)
     wr = gen.router_weight(cfg, device)
@@ -81,6 +86,15 @@ def recv_headers(cfg, d_orc, senders, rank):
     decisions of every source shard; plus recv_offsets in ragged mode."""
     R, W, El = cfg.n_ranks, cfg.n_waves, cfg.experts_per_rank
     Tw = math.ceil(cfg.T / W)
+    if d_orc.dedup:      # four ids per row: read them off the oracle's own pools
+        import oracle as orc
+        C = d_orc.cap_send
+        ids = []
+        for snd in senders:
+            z = np.zeros((cfg.T, cfg.latent), np.uint16)
+            pools = orc.pack_rows(d_orc, z, snd["topk"], snd["slot"])
+            ids.append(orc.row_ids(pools, cfg.latent)[rank * W * C:(rank + 1) * W * C])
+        return np.concatenate(ids), None
     segs, lens = [], []
     for snd in senders:
         topk, slot = snd["topk"], snd["slot"]
@@ -106,9 +120,12 @@ def recv_headers(cfg, d_orc, senders, rank):
 
 
 def rows_with_headers(payload_u16, hdr):
-    """uint8 [n, 2L+16] rows: payload bits then {id, 0, 0, 0}."""
+    """uint8 [n, 2L+16] rows: payload bits then {id, 0, 0, 0}, or the four
+    ids of a [n, 4] hdr (dedup)."""
     n, L = payload_u16.shape
     rows = np.zeros((n, 2 * L + 16), np.uint8)
     rows[:, :2 * L] = payload_u16.view(np.uint8).reshape(n, 2 * L)
-    rows[:, 2 * L:2 * L + 4] = hdr.astype(np.int32).view(np.uint8).reshape(n, 4)
+    h = np.ascontiguousarray(hdr, np.int32)
+    w = 16 if h.ndim == 2 else 4
+    rows[:, 2 * L:2 * L + w] = h.view(np.uint8).reshape(n, w)
     return rows

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(moe):
 
 
 def test_abi_version(moe):
-    assert moe.moe_abi_version() == 4
+    assert moe.moe_abi_version() == 5
 
 
 def test_capacity_matches_table(moe):
@@ -69,7 +69,8 @@ def _dims(moe, **kw):
 
 @pytest.mark.parametrize("field,value", [("latent", 100), ("d_model", 0), ("n_ranks", 5),
                                          ("top_k", 60), ("d_ff", 200), ("cap_recv", 0),
-                                         ("n_experts", 2048), ("wave_mode", 2)])
+                                         ("n_experts", 2048), ("wave_mode", 2),
+                                         ("dedup", 3)])
 def test_bad_dims_rejected(moe, field, value):
     d = _dims(moe, **{field: value})
     rc = moe.lib().moe_workspace_bytes(ctypes.byref(d), moe.MOE_CALL_FFN, 0)
@@ -83,6 +84,15 @@ def test_chunked_waves_need_fixed_capacities(moe):
     d = _dims(moe, wave_mode=moe.MOE_WAVES_CHUNKS, cap_send=0, cap_recv=0)
     assert moe.lib().moe_workspace_bytes(ctypes.byref(d), moe.MOE_CALL_PACK, 0) < 0
     assert "chunk" in moe.lib().moe_last_error().decode()
+
+
+def test_dedup_needs_fixed_capacities(moe):
+    d = _dims(moe, dedup=1)
+    assert moe.moe_workspace_bytes(d, moe.MOE_CALL_BANK, 0) >= 0
+    d = _dims(moe, dedup=1, cap_send=0, cap_recv=0)
+    assert moe.lib().moe_workspace_bytes(ctypes.byref(d), moe.MOE_CALL_PACK, 0) < 0
+    d = _dims(moe, dedup=1)                        # the backward calls do not take it
+    assert moe.lib().moe_workspace_bytes(ctypes.byref(d), moe.MOE_CALL_FFN_BWD, 0) == -2
 
 
 def test_calls_reject_null_and_misaligned(moe):

@@ -23,6 +23,7 @@ CASES = {
     "mid_ragged": gc.ragged(gc.MID),
     "mid_zipf": gc.skewed(gc.MID),
     "mid_zipf_chunks": gc.chunked(gc.skewed(gc.MID)),
+    "mid_dedup": gc.deduped(gc.MID),
 }
 
 
@@ -83,10 +84,10 @@ def test_chain(orc, name):
             lens.append(b - a)
     o_recv = np.concatenate(parts)
     o_roffs = None if d.cap_send else np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
-    bo = orc.bank_slots(d_orc, rank, orc.headers(o_recv, d.latent), o_roffs)
+    bo = orc.bank_slots(d_orc, rank, orc.recv_ids(d_orc, o_recv), o_roffs)
     o_bank = orc.bank_rows(d_orc, o_recv, bo["bank_offsets"], bo["bank_src"], bo["bfill"])
     o_ret = orc.expert_ffn(d_orc, o_bank, bo["bank_offsets"], bo["bank_src"], bo["bfill"],
-                           u16(wg), u16(wu), u16(wd), len(o_recv))
+                           u16(wg), u16(wu), u16(wd), len(o_recv) * (4 if d.dedup else 1))
     s0 = o_snd[rank]
     o_ylat, o_out = orc.combine(d_orc, o_ret, o_roffs, s0["topk"], s0["slot"], s0["gates"],
                                 u16(x_own), u16(wlu), u16(wsg), u16(wsu), u16(wsd))
@@ -99,7 +100,7 @@ def test_chain(orc, name):
     gc.assert_rows_close(gc.host(own.z), s0["z"], "z")
     g_recv = gc.host(recv)
     assert g_recv.shape == o_recv.shape
-    assert np.array_equal(orc.headers(g_recv, d.latent), orc.headers(o_recv, d.latent))
+    assert np.array_equal(orc.recv_ids(d_orc, g_recv), orc.recv_ids(d_orc, o_recv))
     if roffs is not None:
         assert np.array_equal(gc.host(roffs), o_roffs)
     assert np.array_equal(gc.host(rcv.bank_src), bo["bank_src"])

@@ -25,6 +25,8 @@ CASES = {
     "mid_tight": gc.with_cf(gc.MID, "1/2", "3/5"),
     "mid_chunks": gc.chunked(gc.MID),
     "mid_chunks_tight": gc.chunked(gc.with_cf(gc.MID, "1/2", "3/5")),
+    "mid_dedup": gc.deduped(gc.MID),
+    "mid_dedup_tight": gc.deduped(gc.chunked(gc.with_cf(gc.MID, "1/2", "3/5"))),
     # more waves than the grouped GEMM merges into one product group: every
     # (wave, expert) bank group is its own product group
     "mid_w5": configs.scaled(gc.MID, gc.MID.name + "_W5", n_waves=5),
@@ -125,7 +127,10 @@ def test_pack(moe, orc, share, name):
     pg = gc.host(snd.pools)
     hg, ho = orc.headers(pg, d.latent), orc.headers(po, d.latent)
     assert np.array_equal(hg, ho)
-    assert (pg[:, 2 * d.latent + 4:] == 0).all()          # header tail zeros
+    if d.dedup:
+        assert np.array_equal(orc.row_ids(pg, d.latent), orc.row_ids(po, d.latent))
+    if not d.dedup:
+        assert (pg[:, 2 * d.latent + 4:] == 0).all()      # header tail zeros
     kept = ho >= 0
     # kept rows carry the GPU's own z rows bit for bit
     El, Tw = cfg.experts_per_rank, math.ceil(cfg.T / cfg.n_waves)
@@ -216,10 +221,11 @@ def test_expert_ffn(moe, orc, share, name):
     rcv.ret.fill_(1.5)                               # poison: non-kept rows must become zero
     rcv.ffn(wg.cuda(), wu.cuda(), wd.cuda())
     torch.cuda.synchronize()
+    n_ret = n * (4 if d.dedup else 1)
     ro = orc.expert_ffn(d_orc, bank, bo["bank_offsets"], bo["bank_src"], bo["bfill"],
-                        u16(wg), u16(wu), u16(wd), n)
+                        u16(wg), u16(wu), u16(wd), n_ret)
     rg = gc.host(rcv.ret)
-    kept = np.zeros(n, bool)
+    kept = np.zeros(n_ret, bool)
     kept[bo["bank_src"][bo["bank_src"] >= 0]] = True
     assert (rg[~kept] == 0).all()
     gc.assert_rows_close(rg[kept], ro[kept], "ret")
@@ -235,7 +241,7 @@ def test_combine(moe, orc, share, name):
     d_orc, d = _dims(orc, share, cfg)
     senders = gc.oracle_sender_all(orc, cfg, d_orc)
     hdr, offs = gc.recv_headers(cfg, d_orc, senders, 0)
-    n = len(hdr)
+    n = len(hdr) * (4 if d.dedup else 1)                # return rows
     s0 = senders[0]
     returned = u16(gen.payload_rows(n, d.latent, 13))
     x = s0["x"]
