@@ -54,8 +54,9 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False, keep_logits=False)
     snd = share.Sender(d, device)
     R, W = d.n_ranks, d.n_waves
     El = cfg.experts_per_rank
-    st.sent_demand = 0
-    st.sent_fill = 0
+    st.sent_demand = 0     # pool rows asked for, all shards
+    st.sent_fill = 0       # pool rows sent
+    st.sent_dropped = 0    # assignments dropped at the sender (a row may carry several: dedup)
     # kept sender rows per (destination rank, wave, local expert), all shards:
     # what every rank's bank step would see (drop statistics, hottest rank)
     st.recv_counts = torch.zeros(R * W * El, dtype=torch.int64, device=device)
@@ -76,6 +77,7 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False, keep_logits=False)
         snd.pack(x, st.wld)
         st.sent_demand += int(snd.demand.sum())
         st.sent_fill += int(snd.fill.sum())
+        st.sent_dropped += int((snd.slot < 0).sum())
         e = snd.topk.long()
         if d.wave_mode == moe_waves_chunks():   # the wave is the chunk of the slot
             wv = snd.slot.long().clamp(min=0) // d.cap_send
@@ -237,7 +239,8 @@ def algorithmic_work(st):
     w["route_topk_softmax"] = ("byte", T * d.n_experts * 4.0 + T * k * 8.0)
     w["pack_rows"] = ("byte", T * L * 2.0 + kept_s * (2 * L + 16) + (n_slots - kept_s) * 16.0)
     w["bank_rows"] = ("byte", 2.0 * kept_r * 2 * L)
-    w["combine_gather"] = ("byte", kept_s * 2.0 * L + T * k * 8.0 + T * L * 2.0)
+    kept_a = int((st.snd.slot >= 0).sum())  # kept assignments (one return row each)
+    w["combine_gather"] = ("byte", kept_a * 2.0 * L + T * k * 8.0 + T * L * 2.0)
     return w
 
 
@@ -488,6 +491,9 @@ def main():
                     help="quantile balancing on: route with the bias -ALPHA (f - 1/E) from the "
                          "selection counts of the past --balance-window batches")
     ap.add_argument("--balance-window", type=int, default=8)
+    ap.add_argument("--dedup", action="store_true",
+                    help="variant: a token's choices on one destination share rows (up to four "
+                         "ids per row); the backward is not measured")
     ap.add_argument("--waves", choices=("tokens", "chunks"), default="tokens",
                     help="tokens: wave(t) = t / T_w, a pool per (destination, wave); chunks: "
                          "one pool of n_waves * C_s rows per destination cut into n_waves chunks")
@@ -516,9 +522,9 @@ def main():
         return
 
     cfg = configs.WORKLOADS[args.config]
-    if args.waves != cfg.waves:
+    if args.waves != cfg.waves or args.dedup:
         import dataclasses
-        cfg = dataclasses.replace(cfg, waves=args.waves)
+        cfg = dataclasses.replace(cfg, waves=args.waves, dedup=args.dedup or cfg.dedup)
     rank = 0 if args.rank == "hot" else int(args.rank)
     log(f"bench: {cfg.name} rank {args.rank}: setup")
     st = setup(cfg, rank, progress=True)
@@ -573,8 +579,9 @@ def main():
     kept_s, dem_s = int(st.snd.fill.sum()), int(st.snd.demand.sum())
     kept_r, dem_r = int(st.rcv.bfill.sum()), int(st.rcv.bdemand.sum())
     drops = {
-        "sender_pct_own_shard": round(100.0 * (dem_s - kept_s) / max(dem_s, 1), 3),
-        "sender_pct_all_shards": round(100.0 * (st.sent_demand - st.sent_fill) / max(st.sent_demand, 1), 3),
+        "sender_pct_own_shard": round(100.0 * int((st.snd.slot < 0).sum()) / (d.T * d.top_k), 3),
+        "sender_pct_all_shards": round(100.0 * st.sent_dropped / (cfg.n_shards * d.T * d.top_k), 3),
+        "pool_rows_sent_per_shard": round(st.sent_fill / cfg.n_shards, 1),
         "receiver_pct_rank": round(100.0 * (dem_r - kept_r) / max(dem_r, 1), 3),
         "receiver_pct_all_ranks": round(receiver_stats(st)[0], 3),
         "bad_rows": int(st.rcv.bad_rows[0]),
@@ -589,7 +596,7 @@ def main():
                "cpu_model": host_cpu(), "host_cpus": os.cpu_count()}
 
     backward = None
-    if not args.no_backward and d.cap_send:
+    if not args.no_backward and d.cap_send and not d.dedup:
         backward = bench_backward(st, args.steps, args.warmup)
         backward["train_step_ms"] = round(ms + backward["ms_per_step"], 4)
         backward["train_tokens_per_s"] = round(d.T / ((ms + backward["ms_per_step"]) * 1e-3), 1)
@@ -620,7 +627,7 @@ def main():
                    "top_k": d.top_k, "n_waves": d.n_waves, "d_ff": d.d_ff,
                    "n_shared": d.n_shared, "cap_send": d.cap_send, "cap_recv": d.cap_recv,
                    "source_shards": cfg.n_shards, "streams": 1 if args.serial else 3,
-                   "waves": cfg.waves,
+                   "waves": cfg.waves, "dedup": bool(d.dedup),
                    "balance": None if st.bal is None else
                    {"alpha": args.balance_alpha, "window": args.balance_window}},
         "roofline": {"kernel": dom, "bound": "mfma", "measured": "per-kernel pass after the "
