@@ -273,18 +273,13 @@ def backward_work(st):
     return {
         "gemm_bwd_d_ylat": f(2 * T * D * (L + SF)),
         "gemm_shared_swiglu_bwd": f(4 * T * D * SF),
-        "gemm_bwd_dw_lat_up": f(2 * D * L * T),
-        "gemm_bwd_dws_down": f(2 * D * SF * T),
+        "gemm_bwd_dw_combine": f(2 * D * (L + SF) * T),     # dW_lu and dW_sd, one launch
         "gemm_bwd_d_h": f(2 * kept_r * L * F),
         "gemm_expert_swiglu_bwd": f(4 * kept_r * L * F),
         "gemm_bwd_d_u": f(2 * kept_r * 2 * F * L),
-        "gemm_bwd_dw_down": f(2 * L * F * kept_r),
-        "gemm_bwd_dw_gate": f(2 * F * L * kept_r),
-        "gemm_bwd_dw_up": f(2 * F * L * kept_r),
+        "gemm_bwd_dw_experts": f(3 * 2 * L * F * kept_r),  # dW_d, dW_g, dW_u, one launch
         "gemm_bwd_dx": f(2 * T * D * (L + 2 * SF)),
-        "gemm_bwd_dw_lat_down": f(2 * L * D * T),
-        "gemm_bwd_dws_gate": f(2 * SF * D * T),
-        "gemm_bwd_dws_up": f(2 * SF * D * T),
+        "gemm_bwd_dw_pack": f(2 * (L + 2 * SF) * D * T),    # dW_ld, dW_sg, dW_su, one launch
         # d_ylat row + kept returned rows read; every d_returned row written
         "combine_backward": b(T * L * 2 + kept_s * L * 2 + n_slots * L * 2 + T * k * 16),
         "route_backward": b(T * E * 8 + T * k * 12),

@@ -388,14 +388,16 @@ extern "C" int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
   // weight gradients, summed over tokens
   MOE_TRY(transpose("transpose_d_out", d_out, D, 0, w.doT, Tp, 0, T, D, Tp, 1, s));
   MOE_TRY(transpose("transpose_ylat", ylat, L, 0, w.ylT, Tp, 0, T, L, Tp, 1, s));
-  DenseSeg g2{w.doT, Tp, w.ylT, Tp, Tp};
-  MOE_TRY(gemm_nt("gemm_bwd_dw_lat_up", "gemm_bwd_dw_lat_up_tail", D, L, 1, &g2, dw_lat_up, L,
-                  w.part, s));
-  if (!sh) return MOE_OK;
-  MOE_TRY(transpose("transpose_h_shared", w.Hs, SF, 0, w.HsT, Tp, 0, T, SF, Tp, 1, s));
-  DenseSeg g3{w.doT, Tp, w.HsT, Tp, Tp};
-  return gemm_nt_batched("gemm_bwd_dws_down", "gemm_bwd_dws_down_tail", D, Fs, g3, S, 0,
-                         (int64_t)Fs * Tp, dws_down, Fs, (int64_t)D * Fs, w.part, s);
+  if (sh)
+    MOE_TRY(transpose("transpose_h_shared", w.Hs, SF, 0, w.HsT, Tp, 0, T, SF, Tp, 1, s));
+  // dW_lu and every dW_sd,s: one launch of 1 + S products over K = tokens
+  NtProd pr[1 + 4];
+  pr[0] = NtProd{w.doT, Tp, w.ylT, Tp, dw_lat_up, L, D, L};
+  for (int i = 0; i < S; ++i)
+    pr[1 + i] = NtProd{w.doT, Tp, w.HsT + (int64_t)i * Fs * Tp, Tp, dws_down + (int64_t)i * D * Fs,
+                       Fs, D, Fs};
+  return gemm_nt_multi("gemm_bwd_dw_combine", "gemm_bwd_dw_combine_tail", sh ? 1 + S : 1, pr, Tp,
+                       w.part, s);
 }
 
 extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
@@ -456,6 +458,18 @@ extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
                     2 * F, Kp, El, s, bfill, Cr, El));
   MOE_TRY(transpose("transpose_bank_u", bank, L, 0, w.UT, Kp, (int64_t)L * Kp, nw, L, Kp, El, s,
                     bfill, Cr, El));
+  if (3 * El <= 18) {  // all three weights of every local expert in one launch
+    NtProd pr[18];
+    for (int e = 0; e < El; ++e) {
+      const uint16_t *ab = w.dABT + (int64_t)e * 2 * F * Kp, *ut = w.UT + (int64_t)e * L * Kp;
+      pr[3 * e] = NtProd{w.dYT + (int64_t)e * L * Kp, Kp, w.HT + (int64_t)e * F * Kp, Kp,
+                         dw_down + e * WL, F, L, F};
+      pr[3 * e + 1] = NtProd{ab, Kp, ut, Kp, dw_gate + e * WL, L, F, L};
+      pr[3 * e + 2] = NtProd{ab + (int64_t)F * Kp, Kp, ut, Kp, dw_up + e * WL, L, F, L};
+    }
+    return gemm_nt_multi("gemm_bwd_dw_experts", "gemm_bwd_dw_experts_tail", 3 * El, pr, Kp, w.part,
+                         s);
+  }
   DenseSeg gd{w.dYT, Kp, w.HT, Kp, Kp};
   MOE_TRY(gemm_nt_batched("gemm_bwd_dw_down", "gemm_bwd_dw_down_tail", L, F, gd, El,
                           (int64_t)L * Kp, (int64_t)F * Kp,
@@ -508,14 +522,12 @@ extern "C" int moe_pack_backward(const moe_dims *d, const moe_bf16 *d_pools, con
   // weight gradients, summed over tokens
   MOE_TRY(transpose("transpose_x", x, D, 0, w.xT, Tp, 0, T, D, Tp, 1, s));
   MOE_TRY(transpose("transpose_dz", dz, L, 0, w.dzT, Tp, 0, T, L, Tp, 1, s));
-  DenseSeg gl{w.dzT, Tp, w.xT, Tp, Tp};
-  MOE_TRY(gemm_nt("gemm_bwd_dw_lat_down", "gemm_bwd_dw_lat_down_tail", L, D, 1, &gl, dw_lat_down,
-                  D, w.part, s));
-  if (!sh) return MOE_OK;
-  MOE_TRY(transpose("transpose_d_shared", d_shared, 2 * SF, 0, w.dshT, Tp, 0, T, 2 * SF, Tp, 1, s));
-  DenseSeg gsg{w.dshT, Tp, w.xT, Tp, Tp};
-  MOE_TRY(gemm_nt("gemm_bwd_dws_gate", "gemm_bwd_dws_gate_tail", SF, D, 1, &gsg, dws_gate, D,
-                  w.part, s));
-  DenseSeg gsu{w.dshT + (int64_t)SF * Tp, Tp, w.xT, Tp, Tp};
-  return gemm_nt("gemm_bwd_dws_up", "gemm_bwd_dws_up_tail", SF, D, 1, &gsu, dws_up, D, w.part, s);
+  if (sh)
+    MOE_TRY(transpose("transpose_d_shared", d_shared, 2 * SF, 0, w.dshT, Tp, 0, T, 2 * SF, Tp, 1,
+                      s));
+  // dW_ld, dW_sg, dW_su: one launch of three products over K = tokens
+  NtProd pr[3] = {{w.dzT, Tp, w.xT, Tp, dw_lat_down, D, L, D},
+                  {w.dshT, Tp, w.xT, Tp, dws_gate, D, SF, D},
+                  {w.dshT + (int64_t)SF * Tp, Tp, w.xT, Tp, dws_up, D, SF, D}};
+  return gemm_nt_multi("gemm_bwd_dw_pack", "gemm_bwd_dw_pack_tail", sh ? 3 : 1, pr, Tp, w.part, s);
 }

@@ -300,6 +300,89 @@ __global__ __launch_bounds__(GNT) void gemm_dense_tail_kernel(DenseArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// several independent products with one K in one launch (the backward's
+// weight gradients): product p owns logical tiles first[p] .. first[p+1]-1
+// ---------------------------------------------------------------------------
+
+constexpr int GMAXPROD = 18;
+
+struct MultiArgs {
+  int nprod, ktiles;
+  int first[GMAXPROD + 1];
+  const uint16_t *A[GMAXPROD];
+  const uint16_t *B[GMAXPROD];
+  uint16_t *C[GMAXPROD];
+  int64_t lda[GMAXPROD], ldb[GMAXPROD], ldc[GMAXPROD];
+  int M[GMAXPROD], N[GMAXPROD];
+  GSplit sp;
+};
+
+// Product of logical tile `tile` (wave-uniform scan of the prefix table).
+__device__ __forceinline__ int multi_product(const MultiArgs &g, int tile) {
+  int p = 0;
+  while (p + 1 < g.nprod && tile >= g.first[p + 1]) ++p;
+  return p;
+}
+
+template <int ONLY = -1>
+__device__ __forceinline__ void multi_store(uint16_t *C, int64_t ldc, int M, int N, int mt, int nt,
+                                            const GAcc &acc) {
+#pragma unroll
+  for (int i = 0; i < GTM; ++i)
+#pragma unroll
+    for (int j = 0; j < GTN; ++j) {
+      if (ONLY >= 0 && i != ONLY) continue;
+      const int n = nt * GBN + g_acc_col(j);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = mt * GBM + g_acc_row(i, v);
+        if (m < M && n < N) C[(int64_t)m * ldc + n] = f32_to_bf16(acc[i][j][v]);
+      }
+    }
+}
+
+__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_nt_multi_kernel(MultiArgs g) {
+  MOE_GEMM_LDS(lds);
+  GUnit u;
+  if (!g_unit(g.sp, g.first[g.nprod], blockIdx.x, u)) return;
+  const int p = multi_product(g, u.tile);
+  const int M = g.M[p], N = g.N[p];
+  const int tm = (M + GBM - 1) / GBM, tn = (N + GBN - 1) / GBN;
+  int mt, nt;
+  g_tile_coords(u.tile - g.first[p], tm, tn, mt, nt);
+  const int mv = M - mt * GBM, nv = N - nt * GBN;
+  int k0, k1;
+  g_part_range(g.ktiles, u, k0, k1);
+  const auto ops = g_operands(
+      g.A[p] + (int64_t)mt * GBM * g.lda[p] + k0 * GBK, g.lda[p], [&](int r) { return min(r, mv - 1); },
+      g.B[p] + (int64_t)nt * GBN * g.ldb[p] + k0 * GBK, g.ldb[p], [&](int r) { return min(r, nv - 1); });
+  GAcc acc;
+  gemm_zero(acc);
+  gemm_mainloop(ops, k1 - k0, acc, lds);
+  if (u.nparts > 1) {
+    g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
+    return;
+  }
+  multi_store(g.C[p], g.ldc[p], M, N, mt, nt, acc);
+}
+
+__global__ __launch_bounds__(GNT) void gemm_nt_multi_tail_kernel(MultiArgs g) {
+  GUnit u;
+  if (!g_tail_tile(g.sp, g.first[g.nprod], blockIdx.x / GTM, u)) return;
+  const int p = multi_product(g, u.tile);
+  const int M = g.M[p], N = g.N[p];
+  const int tm = (M + GBM - 1) / GBM, tn = (N + GBN - 1) / GBN;
+  int mt, nt;
+  g_tile_coords(u.tile - g.first[p], tm, tn, mt, nt);
+  GAcc acc;
+#define MOE_ROWS(I)                                       \
+  g_part_sum_rows<I>(g.sp.part, u.tail, u.nparts, acc); \
+  multi_store<I>(g.C[p], g.ldc[p], M, N, mt, nt, acc)
+  MOE_TAIL_ROWS(MOE_ROWS)
+#undef MOE_ROWS
+}
+
+// ---------------------------------------------------------------------------
 // grouped rows: the bank's groups (wave w, local expert j) = group w * El + j
 // ---------------------------------------------------------------------------
 
@@ -943,6 +1026,44 @@ int gemm_nt(const char *name, const char *tail_name, int M, int N, int nseg,
   static void (*const k[2])(DenseArgs) = {gemm_nt_kernel<1, false>, gemm_nt_kernel<2, false>};
   if (nseg < 1 || nseg > 2) return fail(MOE_ERR_INVALID, "%s: bad segment count", name);
   return dense(name, tail_name, k[nseg - 1], M, N, nseg, segs, C, ldc, part, s);
+}
+
+int gemm_nt_multi(const char *name, const char *tail_name, int nprod, const NtProd *prods, int K,
+                  float *part, hipStream_t s) {
+  if (nprod < 1 || nprod > GMAXPROD) return fail(MOE_ERR_INVALID, "%s: bad product count", name);
+  if (K % GBK) return fail(MOE_ERR_UNSUPPORTED, "%s: K %% %d != 0", name, GBK);
+  MultiArgs a{};
+  a.nprod = nprod;
+  a.ktiles = K / GBK;
+  int64_t total = 0;
+  for (int p = 0; p < nprod; ++p) {
+    const NtProd &q = prods[p];
+    if (q.M < 1 || q.N < 1 || q.lda * 2 * GBM > INT32_MAX || q.ldb * 2 * GBN > INT32_MAX)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: product %d shape", name, p);
+    a.first[p] = (int)total;
+    a.A[p] = q.A;
+    a.B[p] = q.B;
+    a.C[p] = q.C;
+    a.lda[p] = q.lda;
+    a.ldb[p] = q.ldb;
+    a.ldc[p] = q.ldc;
+    a.M[p] = q.M;
+    a.N[p] = q.N;
+    total += cdiv(q.M, GBM) * cdiv(q.N, GBN);
+  }
+  if (total > INT32_MAX / 2) return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", name);
+  a.first[nprod] = (int)total;
+  MOE_TRY(make_split(part, a.ktiles, a.sp));
+  const int S = split_parts(a.sp, total);
+  if (S == 1) {
+    a.sp.part = nullptr;
+    return launch(name, gemm_nt_multi_kernel, dim3((unsigned)total), dim3(GNT), 0, s, a);
+  }
+  const int64_t r = total % a.sp.ncu;
+  MOE_TRY(launch(name, gemm_nt_multi_kernel, dim3((unsigned)(total - r + r * S)), dim3(GNT), 0, s,
+                 a));
+  return launch(tail_name, gemm_nt_multi_tail_kernel, dim3((unsigned)(r * GTM)), dim3(GNT), 0, s,
+                a);
 }
 
 int gemm_nt_batched(const char *name, const char *tail_name, int M, int N, const DenseSeg &seg,

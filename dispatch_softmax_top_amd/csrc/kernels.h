@@ -77,6 +77,19 @@ int gemm_nt(const char *name, const char *tail_name, int M, int N, int nseg,
 int gemm_nt_batched(const char *name, const char *tail_name, int M, int N, const DenseSeg &seg,
                     int nbatch, int64_t bsA, int64_t bsB, uint16_t *C, int64_t ldc, int64_t bsC,
                     float *part, hipStream_t s);
+// Independent products C_p[M_p, N_p] = A_p . B_p^T with one K, in one launch
+// (at most 18).
+struct NtProd {
+  const uint16_t *A;
+  int64_t lda;
+  const uint16_t *B;
+  int64_t ldb;
+  uint16_t *C;
+  int64_t ldc;
+  int M, N;
+};
+int gemm_nt_multi(const char *name, const char *tail_name, int nprod, const NtProd *prods, int K,
+                  float *part, hipStream_t s);
 // Shared experts recomputed with the SwiGLU gradient epilogue: dH[:, dh_col0 +
 // s*F + f] in, H = h_s [M, S*F] and AB [M, 2*S*F] (d_a of every expert, then
 // d_b) out.
