@@ -408,7 +408,7 @@ def _u16(t):
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def run_cpu_baseline(st, rows=(32, 96, 16)):
+def run_cpu_baseline(st, rows=(64, 160, 32)):
     """Oracle timing on the host.  Sample: route + sender slots of the whole
     shard (full), latent rows for `rows[0]` tokens, expert FFN for `rows[1]`
     bank rows, combine (gather + up-projection + shared experts) for
