@@ -39,8 +39,10 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // transpose: out[b][c][k] = in(b, row(b, k))[c] for c < cols, k < kpad, and 0
 // where row(b, k) does not exist.  Plain: row = k for k < rows.  Bank order
-// (bfill != NULL): k = w * cap + p is bank slot (wave w, local expert b,
-// position p), present when p < bfill[w * El + b].
+// (bfill != NULL): the filled bank positions of local expert b, wave after
+// wave, packed: k = (fills of the waves before w) + p is bank slot (wave w,
+// expert b, position p < bfill[w * El + b]); k past the expert's total fill
+// has no row.
 // ---------------------------------------------------------------------------
 
 struct TransposeArgs {
@@ -50,7 +52,7 @@ struct TransposeArgs {
   int64_t ld_out, bs_out;
   int rows, cols, kpad;
   const int32_t *bfill;
-  int cap, El;
+  int cap, El, W;
 };
 
 constexpr int TP = 64;  // tile edge
@@ -66,8 +68,13 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
     if (k < a.kpad && c < a.cols && k < a.rows) {
       int64_t row = k;
       if (a.bfill) {
-        const int w = k / a.cap, p = k - w * a.cap, g = w * a.El + b;
-        row = p < a.bfill[g] ? (int64_t)g * a.cap + p : -1;
+        int base = 0, w = 0;
+        for (; w < a.W; ++w) {
+          const int f = a.bfill[w * a.El + b];
+          if (k < base + f) break;
+          base += f;
+        }
+        row = w < a.W ? (int64_t)(w * a.El + b) * a.cap + (k - base) : -1;
       }
       if (row >= 0) v = *reinterpret_cast<const u32x4 *>(in + row * a.ld_in + c);
     }
@@ -92,10 +99,10 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
 static int transpose(const char *name, const uint16_t *in, int64_t ld_in, int64_t bs_in,
                      uint16_t *out, int64_t ld_out, int64_t bs_out, int rows, int cols, int kpad,
                      int nbatch, hipStream_t s, const int32_t *bfill = nullptr, int cap = 0,
-                     int El = 0) {
+                     int El = 0, int W = 0) {
   if (cols % 8 || kpad % 8 || ld_in % 8 || ld_out % 8 || bs_in % 8 || bs_out % 8)
     return fail(MOE_ERR_UNSUPPORTED, "%s: sizes must be multiples of 8", name);
-  TransposeArgs a{in, ld_in, bs_in, out, ld_out, bs_out, rows, cols, kpad, bfill, cap, El};
+  TransposeArgs a{in, ld_in, bs_in, out, ld_out, bs_out, rows, cols, kpad, bfill, cap, El, W};
   return launch(name, transpose_kernel,
                 dim3((unsigned)cdiv(kpad, TP), (unsigned)cdiv(cols, TP), (unsigned)nbatch),
                 dim3(256), 0, s, a);
@@ -451,24 +458,25 @@ extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
   // weight gradients: per local expert, summed over its rows of every wave
   const int nw = d->n_waves * Cr;
   MOE_TRY(transpose("transpose_bank_dy", w.dY, L, 0, w.dYT, Kp, (int64_t)L * Kp, nw, L, Kp, El, s,
-                    bfill, Cr, El));
+                    bfill, Cr, El, d->n_waves));
   MOE_TRY(transpose("transpose_bank_h", w.Hb, F, 0, w.HT, Kp, (int64_t)F * Kp, nw, F, Kp, El, s,
-                    bfill, Cr, El));
+                    bfill, Cr, El, d->n_waves));
   MOE_TRY(transpose("transpose_bank_dab", w.dAB, 2 * F, 0, w.dABT, Kp, (int64_t)2 * F * Kp, nw,
-                    2 * F, Kp, El, s, bfill, Cr, El));
+                    2 * F, Kp, El, s, bfill, Cr, El, d->n_waves));
   MOE_TRY(transpose("transpose_bank_u", bank, L, 0, w.UT, Kp, (int64_t)L * Kp, nw, L, Kp, El, s,
-                    bfill, Cr, El));
+                    bfill, Cr, El, d->n_waves));
   if (3 * El <= 18) {  // all three weights of every local expert in one launch
     NtProd pr[18];
     for (int e = 0; e < El; ++e) {
       const uint16_t *ab = w.dABT + (int64_t)e * 2 * F * Kp, *ut = w.UT + (int64_t)e * L * Kp;
       pr[3 * e] = NtProd{w.dYT + (int64_t)e * L * Kp, Kp, w.HT + (int64_t)e * F * Kp, Kp,
-                         dw_down + e * WL, F, L, F};
-      pr[3 * e + 1] = NtProd{ab, Kp, ut, Kp, dw_gate + e * WL, L, F, L};
-      pr[3 * e + 2] = NtProd{ab + (int64_t)F * Kp, Kp, ut, Kp, dw_up + e * WL, L, F, L};
+                         dw_down + e * WL, F, L, F, e};
+      pr[3 * e + 1] = NtProd{ab, Kp, ut, Kp, dw_gate + e * WL, L, F, L, e};
+      pr[3 * e + 2] = NtProd{ab + (int64_t)F * Kp, Kp, ut, Kp, dw_up + e * WL, L, F, L, e};
     }
+    // each expert's K: its filled bank rows (the transposes packed them first)
     return gemm_nt_multi("gemm_bwd_dw_experts", "gemm_bwd_dw_experts_tail", 3 * El, pr, Kp, w.part,
-                         s);
+                         s, bfill, d->n_waves, El);
   }
   DenseSeg gd{w.dYT, Kp, w.HT, Kp, Kp};
   MOE_TRY(gemm_nt_batched("gemm_bwd_dw_down", "gemm_bwd_dw_down_tail", L, F, gd, El,

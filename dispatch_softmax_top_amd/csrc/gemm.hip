@@ -308,6 +308,13 @@ constexpr int GMAXPROD = 18;
 
 struct MultiArgs {
   int nprod, ktiles;
+  // kfill != NULL: product p's K is the sum of kfill[w * kEl + kgroup[p]]
+  // over w < kW (rounded up to whole K tiles, at least min(GSPLIT_MAX,
+  // ktiles) so that every split part has one), at most ktiles; the operands
+  // hold zeros from there to ktiles
+  const int32_t *kfill;
+  int kW, kEl;
+  int kgroup[GMAXPROD];
   int first[GMAXPROD + 1];
   const uint16_t *A[GMAXPROD];
   const uint16_t *B[GMAXPROD];
@@ -322,6 +329,14 @@ __device__ __forceinline__ int multi_product(const MultiArgs &g, int tile) {
   int p = 0;
   while (p + 1 < g.nprod && tile >= g.first[p + 1]) ++p;
   return p;
+}
+
+__device__ __forceinline__ int multi_ktiles(const MultiArgs &g, int p) {
+  if (!g.kfill) return g.ktiles;
+  int f = 0;
+  for (int w = 0; w < g.kW; ++w) f += g.kfill[w * g.kEl + g.kgroup[p]];
+  const int kt = max((f + GBK - 1) / GBK, min(GSPLIT_MAX, g.ktiles));
+  return __builtin_amdgcn_readfirstlane(min(kt, g.ktiles));
 }
 
 template <int ONLY = -1>
@@ -352,7 +367,7 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
   g_tile_coords(u.tile - g.first[p], tm, tn, mt, nt);
   const int mv = M - mt * GBM, nv = N - nt * GBN;
   int k0, k1;
-  g_part_range(g.ktiles, u, k0, k1);
+  g_part_range(multi_ktiles(g, p), u, k0, k1);
   const auto ops = g_operands(
       g.A[p] + (int64_t)mt * GBM * g.lda[p] + k0 * GBK, g.lda[p], [&](int r) { return min(r, mv - 1); },
       g.B[p] + (int64_t)nt * GBN * g.ldb[p] + k0 * GBK, g.ldb[p], [&](int r) { return min(r, nv - 1); });
@@ -1029,12 +1044,15 @@ int gemm_nt(const char *name, const char *tail_name, int M, int N, int nseg,
 }
 
 int gemm_nt_multi(const char *name, const char *tail_name, int nprod, const NtProd *prods, int K,
-                  float *part, hipStream_t s) {
+                  float *part, hipStream_t s, const int32_t *kfill, int kW, int kEl) {
   if (nprod < 1 || nprod > GMAXPROD) return fail(MOE_ERR_INVALID, "%s: bad product count", name);
   if (K % GBK) return fail(MOE_ERR_UNSUPPORTED, "%s: K %% %d != 0", name, GBK);
   MultiArgs a{};
   a.nprod = nprod;
   a.ktiles = K / GBK;
+  a.kfill = kfill;
+  a.kW = kW;
+  a.kEl = kEl;
   int64_t total = 0;
   for (int p = 0; p < nprod; ++p) {
     const NtProd &q = prods[p];
@@ -1049,6 +1067,7 @@ int gemm_nt_multi(const char *name, const char *tail_name, int nprod, const NtPr
     a.ldc[p] = q.ldc;
     a.M[p] = q.M;
     a.N[p] = q.N;
+    a.kgroup[p] = q.kgroup;
     total += cdiv(q.M, GBM) * cdiv(q.N, GBN);
   }
   if (total > INT32_MAX / 2) return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", name);

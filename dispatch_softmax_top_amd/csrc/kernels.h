@@ -78,7 +78,9 @@ int gemm_nt_batched(const char *name, const char *tail_name, int M, int N, const
                     int nbatch, int64_t bsA, int64_t bsB, uint16_t *C, int64_t ldc, int64_t bsC,
                     float *part, hipStream_t s);
 // Independent products C_p[M_p, N_p] = A_p . B_p^T with one K, in one launch
-// (at most 18).
+// (at most 18).  With kfill, product p's K is only the sum over w < kW of
+// kfill[w * kEl + kgroup] (rounded up; the operands are zero past it), read on
+// the device: the bank's fill of one local expert over its waves.
 struct NtProd {
   const uint16_t *A;
   int64_t lda;
@@ -87,9 +89,11 @@ struct NtProd {
   uint16_t *C;
   int64_t ldc;
   int M, N;
+  int kgroup;
 };
 int gemm_nt_multi(const char *name, const char *tail_name, int nprod, const NtProd *prods, int K,
-                  float *part, hipStream_t s);
+                  float *part, hipStream_t s, const int32_t *kfill = nullptr, int kW = 0,
+                  int kEl = 0);
 // Shared experts recomputed with the SwiGLU gradient epilogue: dH[:, dh_col0 +
 // s*F + f] in, H = h_s [M, S*F] and AB [M, 2*S*F] (d_a of every expert, then
 // d_b) out.
