@@ -57,8 +57,13 @@ struct TransposeArgs {
 
 constexpr int TP = 64;  // tile edge
 
+// The tile is [k][c] with 128-byte rows; 16-byte chunk ch of row kk sits at
+// chunk ch ^ (kk / 8 % 8), so the column reads of the second phase (rows
+// 8 apart, one per lane group) fall on different banks.
+__device__ __forceinline__ int tp_chunk(int kk, int ch) { return ch ^ ((kk >> 3) & 7); }
+
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
-  __shared__ uint16_t tile[TP][TP + 8];  // [k][c]; 144-byte rows keep 16-byte alignment
+  __shared__ __attribute__((aligned(16))) uint16_t tile[TP][TP];
   const int k0 = blockIdx.x * TP, c0 = blockIdx.y * TP, b = blockIdx.z;
   const uint16_t *in = a.in + b * a.bs_in;
   for (int q = threadIdx.x; q < TP * TP / 8; q += 256) {
@@ -78,7 +83,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
       }
       if (row >= 0) v = *reinterpret_cast<const u32x4 *>(in + row * a.ld_in + c);
     }
-    *reinterpret_cast<u32x4 *>(&tile[kk][ch * 8]) = v;
+    *reinterpret_cast<u32x4 *>(&tile[kk][tp_chunk(kk, ch) * 8]) = v;
   }
   __syncthreads();
   uint16_t *out = a.out + b * a.bs_out;
@@ -87,9 +92,13 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
     const int c = c0 + cc, k = k0 + ch * 8;
     if (c >= a.cols || k >= a.kpad) continue;
     u32x4 v;
+    const int cs = cc & 7;
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
-      v[h] = (uint32_t)tile[ch * 8 + 2 * h][cc] | ((uint32_t)tile[ch * 8 + 2 * h + 1][cc] << 16);
+    for (int h = 0; h < 4; ++h) {
+      const int k_lo = ch * 8 + 2 * h, k_hi = k_lo + 1;
+      v[h] = (uint32_t)tile[k_lo][tp_chunk(k_lo, cc >> 3) * 8 + cs] |
+             ((uint32_t)tile[k_hi][tp_chunk(k_hi, cc >> 3) * 8 + cs] << 16);
+    }
     *reinterpret_cast<u32x4 *>(out + (int64_t)c * a.ld_out + k) = v;
   }
 }
