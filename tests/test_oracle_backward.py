@@ -151,12 +151,14 @@ def torch_backward(cfg, W_, S, keep, d_out):
     return X, LG, wld, wlu, wsg, wsu, wsd, ex
 
 
-@pytest.mark.parametrize("case", ["1.10/1.15", "tight", "chunks"])
+@pytest.mark.parametrize("case", ["1.10/1.15", "tight", "chunks", "t16"])
 def test_branch_backward_matches_autograd(orc, case):
     from dataclasses import replace
     from fractions import Fraction
     cfg = configs.TINY
-    if case == "tight":
+    if case == "t16":                 # 16 tokens per shard: the quick case
+        cfg = replace(cfg, T=16)
+    elif case == "tight":
         cfg = replace(cfg, cf_send=Fraction(1, 2), cf_recv=Fraction(1, 2))
     elif case == "chunks":
         cfg = replace(cfg, waves="chunks")
