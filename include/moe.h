@@ -21,6 +21,10 @@
  *   (return)        outside this library
  *   moe_combine     gate-weighted sum of each token's returned rows, latent
  *                   up-projection, plus the shared experts
+ * and, for training, the same stages backward: moe_combine_backward,
+ * moe_route_backward, moe_expert_ffn_backward, moe_pack_backward.
+ * Quantile balancing of the routing: moe_route_biased, moe_expert_counts,
+ * moe_balance_bias.
  *
  * Conventions shared by every call
  *   - All array arguments are DEVICE pointers, 16-byte aligned, owned by the
@@ -34,6 +38,7 @@
  *   - A pool / receive row is `latent` bf16 values followed by a 16-byte
  *     tail {int32 global expert id, 0, 0, 0}; id -1 marks an empty slot
  *     (its payload bytes are unspecified).  Row stride = 2*latent + 16.
+ *     With moe_dims.dedup the tail holds four ids (see moe_dims).
  *   - Fixed mode (cap_send > 0 and cap_recv > 0):
  *       pools  [n_ranks][n_waves][cap_send] rows   (destination, wave, slot)
  *       recv   [n_ranks][n_waves][cap_send] rows   (source, wave, slot)
