@@ -285,20 +285,13 @@ def backward_work(st):
         "route_backward": b(T * E * 8 + T * k * 12),
         "gather_bank_grad": b(kept_r * L * 4),
         "combine_gather": b(kept_s * L * 2 + T * k * 8 + T * L * 2),
-        # transposes: elements read + elements written (padding included)
-        "transpose_w_lat_up": b(4 * D * L), "transpose_ws_down": b(4 * D * SF),
-        "transpose_d_out": b(2 * T * D + 2 * D * Tp), "transpose_ylat": b(2 * T * L + 2 * L * Tp),
-        "transpose_h_shared": b(2 * T * SF + 2 * SF * Tp),
-        "transpose_w_down": b(4 * El * L * F), "transpose_w_gate": b(4 * El * L * F),
-        "transpose_w_up": b(4 * El * L * F),
-        "transpose_bank_dy": b(2 * kept_r * L + 2 * El * L * Kp),
-        "transpose_bank_h": b(2 * kept_r * F + 2 * El * F * Kp),
-        "transpose_bank_dab": b(4 * kept_r * F + 4 * El * F * Kp),
-        "transpose_bank_u": b(2 * kept_r * L + 2 * El * L * Kp),
-        "transpose_w_lat_down": b(4 * L * D), "transpose_ws_gate": b(4 * SF * D),
-        "transpose_ws_up": b(4 * SF * D), "transpose_x": b(2 * T * D + 2 * D * Tp),
-        "transpose_dz": b(2 * T * L + 2 * L * Tp),
-        "transpose_d_shared": b(4 * T * SF + 4 * SF * Tp),
+        # transposes (batched launches): elements read + elements written, padding included
+        "transpose_combine_weights": b(4 * D * L + 4 * D * SF),
+        "transpose_combine_acts": b(2 * T * (D + L + SF) + 2 * Tp * (D + L + SF)),
+        "transpose_expert_weights": b(3 * 4 * El * L * F),
+        "transpose_bank": b(2 * kept_r * (2 * L + 3 * F) + 2 * El * Kp * (2 * L + 3 * F)),
+        "transpose_pack_weights": b(4 * L * D + 8 * SF * D),
+        "transpose_pack_acts": b(2 * T * (D + L + 2 * SF) + 2 * Tp * (D + L + 2 * SF)),
     }
 
 

@@ -62,9 +62,25 @@ constexpr int TP = 64;  // tile edge
 // 8 apart, one per lane group) fall on different banks.
 __device__ __forceinline__ int tp_chunk(int kk, int ch) { return ch ^ ((kk >> 3) & 7); }
 
-__global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
+// Up to four transposes in one launch (one ramp-up and drain for all):
+// blocks first[i] .. first[i+1]-1 belong to transpose i, laid out as its
+// (k tile, c tile, batch) grid.
+constexpr int TMAX = 4;
+struct TransposeBatch {
+  int n;
+  int first[TMAX + 1];
+  int gk[TMAX], gc[TMAX];  // k tiles and c tiles of each
+  TransposeArgs t[TMAX];
+};
+
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeBatch tb) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[TP][TP];
-  const int k0 = blockIdx.x * TP, c0 = blockIdx.y * TP, b = blockIdx.z;
+  int i = 0;
+  while (i + 1 < tb.n && (int)blockIdx.x >= tb.first[i + 1]) ++i;
+  const TransposeArgs &a = tb.t[i];
+  const int l = (int)blockIdx.x - tb.first[i];
+  const int k0 = (l % tb.gk[i]) * TP, c0 = (l / tb.gk[i] % tb.gc[i]) * TP;
+  const int b = l / (tb.gk[i] * tb.gc[i]);
   const uint16_t *in = a.in + b * a.bs_in;
   for (int q = threadIdx.x; q < TP * TP / 8; q += 256) {
     const int kk = q >> 3, ch = q & 7;
@@ -105,16 +121,35 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
 
 // Host side: every size and stride a multiple of 8 elements, pointers 16-byte
 // aligned (the callers' buffers and workspace offsets are).
-static int transpose(const char *name, const uint16_t *in, int64_t ld_in, int64_t bs_in,
-                     uint16_t *out, int64_t ld_out, int64_t bs_out, int rows, int cols, int kpad,
-                     int nbatch, hipStream_t s, const int32_t *bfill = nullptr, int cap = 0,
-                     int El = 0, int W = 0) {
-  if (cols % 8 || kpad % 8 || ld_in % 8 || ld_out % 8 || bs_in % 8 || bs_out % 8)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: sizes must be multiples of 8", name);
-  TransposeArgs a{in, ld_in, bs_in, out, ld_out, bs_out, rows, cols, kpad, bfill, cap, El, W};
-  return launch(name, transpose_kernel,
-                dim3((unsigned)cdiv(kpad, TP), (unsigned)cdiv(cols, TP), (unsigned)nbatch),
-                dim3(256), 0, s, a);
+struct Tr {
+  const uint16_t *in;
+  int64_t ld_in, bs_in;
+  uint16_t *out;
+  int64_t ld_out, bs_out;
+  int rows, cols, kpad, nbatch;
+  const int32_t *bfill;
+  int cap, El, W;
+};
+
+static int transposes(const char *name, int n, const Tr *tr, hipStream_t s) {
+  if (n < 1 || n > TMAX) return fail(MOE_ERR_INVALID, "%s: bad transpose count", name);
+  TransposeBatch tb{};
+  tb.n = n;
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    const Tr &q = tr[i];
+    if (q.cols % 8 || q.kpad % 8 || q.ld_in % 8 || q.ld_out % 8 || q.bs_in % 8 || q.bs_out % 8)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: sizes must be multiples of 8", name);
+    tb.t[i] = TransposeArgs{q.in,   q.ld_in, q.bs_in, q.out,   q.ld_out, q.bs_out, q.rows,
+                            q.cols, q.kpad,  q.bfill, q.cap, q.El,     q.W};
+    tb.gk[i] = (int)cdiv(q.kpad, TP);
+    tb.gc[i] = (int)cdiv(q.cols, TP);
+    tb.first[i] = (int)total;
+    total += (int64_t)tb.gk[i] * tb.gc[i] * q.nbatch;
+  }
+  if (total >= INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", name);
+  tb.first[n] = (int)total;
+  return launch(name, transpose_kernel, dim3((unsigned)total), dim3(256), 0, s, tb);
 }
 
 // ---------------------------------------------------------------------------
@@ -378,10 +413,10 @@ extern "C" int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
   combine_bwd_ws(*d, (char *)ws, w);
 
   // [d_ylat | d_h_s] = d_out . [W_lu^T ; W_sd,s^T]^T, one product
-  MOE_TRY(transpose("transpose_w_lat_up", w_lat_up, L, 0, w.Bt, D, 0, D, L, D, 1, s));
-  if (sh)
-    MOE_TRY(transpose("transpose_ws_down", ws_down, Fs, (int64_t)D * Fs, w.Bt + (int64_t)L * D, D,
-                      (int64_t)Fs * D, D, Fs, D, S, s));
+  const Tr trw[2] = {{w_lat_up, L, 0, w.Bt, D, 0, D, L, D, 1},
+                     {ws_down, Fs, (int64_t)D * Fs, w.Bt + (int64_t)L * D, D, (int64_t)Fs * D, D,
+                      Fs, D, S}};
+  MOE_TRY(transposes("transpose_combine_weights", sh ? 2 : 1, trw, s));
   DenseSeg g1{d_out, D, w.Bt, D, D};
   MOE_TRY(gemm_nt("gemm_bwd_d_ylat", "gemm_bwd_d_ylat_tail", T, L + SF, 1, &g1, w.C1, L + SF,
                   w.part, s));
@@ -402,10 +437,10 @@ extern "C" int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
                   token_blocks, n_slots);
   }));
   // weight gradients, summed over tokens
-  MOE_TRY(transpose("transpose_d_out", d_out, D, 0, w.doT, Tp, 0, T, D, Tp, 1, s));
-  MOE_TRY(transpose("transpose_ylat", ylat, L, 0, w.ylT, Tp, 0, T, L, Tp, 1, s));
-  if (sh)
-    MOE_TRY(transpose("transpose_h_shared", w.Hs, SF, 0, w.HsT, Tp, 0, T, SF, Tp, 1, s));
+  const Tr tra[3] = {{d_out, D, 0, w.doT, Tp, 0, T, D, Tp, 1},
+                     {ylat, L, 0, w.ylT, Tp, 0, T, L, Tp, 1},
+                     {w.Hs, SF, 0, w.HsT, Tp, 0, T, SF, Tp, 1}};
+  MOE_TRY(transposes("transpose_combine_acts", sh ? 3 : 2, tra, s));
   // dW_lu and every dW_sd,s: one launch of 1 + S products over K = tokens
   NtProd pr[1 + 4];
   pr[0] = NtProd{w.doT, Tp, w.ylT, Tp, dw_lat_up, L, D, L};
@@ -442,9 +477,10 @@ extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
   const int64_t WL = (int64_t)F * L;
 
   // operands with K contiguous: W_d^T [El][F][L], [W_g^T | W_u^T] [El][L][2F]
-  MOE_TRY(transpose("transpose_w_down", w_down, F, WL, w.WdT, L, WL, L, F, L, El, s));
-  MOE_TRY(transpose("transpose_w_gate", w_gate, L, WL, w.WguT, 2 * F, 2 * WL, F, L, F, El, s));
-  MOE_TRY(transpose("transpose_w_up", w_up, L, WL, w.WguT + F, 2 * F, 2 * WL, F, L, F, El, s));
+  const Tr trw[3] = {{w_down, F, WL, w.WdT, L, WL, L, F, L, El},
+                     {w_gate, L, WL, w.WguT, 2 * F, 2 * WL, F, L, F, El},
+                     {w_up, L, WL, w.WguT + F, 2 * F, 2 * WL, F, L, F, El}};
+  MOE_TRY(transposes("transpose_expert_weights", 3, trw, s));
   // dy in bank order
   MOE_TRY(by_chunks(L, [&](auto chv) {
     constexpr int CH = decltype(chv)::value;
@@ -466,14 +502,13 @@ extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
   MOE_TRY(ret_rows_zero_unmarked(w.flags, d_recv, L, nr, s));
   // weight gradients: per local expert, summed over its rows of every wave
   const int nw = d->n_waves * Cr;
-  MOE_TRY(transpose("transpose_bank_dy", w.dY, L, 0, w.dYT, Kp, (int64_t)L * Kp, nw, L, Kp, El, s,
-                    bfill, Cr, El, d->n_waves));
-  MOE_TRY(transpose("transpose_bank_h", w.Hb, F, 0, w.HT, Kp, (int64_t)F * Kp, nw, F, Kp, El, s,
-                    bfill, Cr, El, d->n_waves));
-  MOE_TRY(transpose("transpose_bank_dab", w.dAB, 2 * F, 0, w.dABT, Kp, (int64_t)2 * F * Kp, nw,
-                    2 * F, Kp, El, s, bfill, Cr, El, d->n_waves));
-  MOE_TRY(transpose("transpose_bank_u", bank, L, 0, w.UT, Kp, (int64_t)L * Kp, nw, L, Kp, El, s,
-                    bfill, Cr, El, d->n_waves));
+  const int W = d->n_waves;
+  const Tr trb[4] = {
+      {w.dY, L, 0, w.dYT, Kp, (int64_t)L * Kp, nw, L, Kp, El, bfill, Cr, El, W},
+      {w.Hb, F, 0, w.HT, Kp, (int64_t)F * Kp, nw, F, Kp, El, bfill, Cr, El, W},
+      {w.dAB, 2 * F, 0, w.dABT, Kp, (int64_t)2 * F * Kp, nw, 2 * F, Kp, El, bfill, Cr, El, W},
+      {bank, L, 0, w.UT, Kp, (int64_t)L * Kp, nw, L, Kp, El, bfill, Cr, El, W}};
+  MOE_TRY(transposes("transpose_bank", 4, trb, s));
   if (3 * El <= 18) {  // all three weights of every local expert in one launch
     NtProd pr[18];
     for (int e = 0; e < El; ++e) {
@@ -529,19 +564,17 @@ extern "C" int moe_pack_backward(const moe_dims *d, const moe_bf16 *d_pools, con
   // dz[t] = sum over kept choices of the pool-row gradients (the pack copy's adjoint)
   MOE_TRY(combine_gather_rows(*d, d_pools, nullptr, topk, slot, nullptr, dz, s));
   // dx = dz . W_ld + d_a . W_sg + d_b . W_su, one product with one rounding
-  MOE_TRY(transpose("transpose_w_lat_down", w_lat_down, D, 0, w.BldT, L, 0, L, D, L, 1, s));
   DenseSeg gx[2] = {{dz, L, w.BldT, L, L}, {d_shared, 2 * SF, w.BsT, 2 * SF, 2 * SF}};
-  if (sh) {
-    MOE_TRY(transpose("transpose_ws_gate", ws_gate, D, 0, w.BsT, 2 * SF, 0, SF, D, SF, 1, s));
-    MOE_TRY(transpose("transpose_ws_up", ws_up, D, 0, w.BsT + SF, 2 * SF, 0, SF, D, SF, 1, s));
-  }
+  const Tr trw[3] = {{w_lat_down, D, 0, w.BldT, L, 0, L, D, L, 1},
+                     {ws_gate, D, 0, w.BsT, 2 * SF, 0, SF, D, SF, 1},
+                     {ws_up, D, 0, w.BsT + SF, 2 * SF, 0, SF, D, SF, 1}};
+  MOE_TRY(transposes("transpose_pack_weights", sh ? 3 : 1, trw, s));
   MOE_TRY(gemm_nt("gemm_bwd_dx", "gemm_bwd_dx_tail", T, D, sh ? 2 : 1, gx, dx, D, w.part, s));
   // weight gradients, summed over tokens
-  MOE_TRY(transpose("transpose_x", x, D, 0, w.xT, Tp, 0, T, D, Tp, 1, s));
-  MOE_TRY(transpose("transpose_dz", dz, L, 0, w.dzT, Tp, 0, T, L, Tp, 1, s));
-  if (sh)
-    MOE_TRY(transpose("transpose_d_shared", d_shared, 2 * SF, 0, w.dshT, Tp, 0, T, 2 * SF, Tp, 1,
-                      s));
+  const Tr tra[3] = {{x, D, 0, w.xT, Tp, 0, T, D, Tp, 1},
+                     {dz, L, 0, w.dzT, Tp, 0, T, L, Tp, 1},
+                     {d_shared, 2 * SF, 0, w.dshT, Tp, 0, T, 2 * SF, Tp, 1}};
+  MOE_TRY(transposes("transpose_pack_acts", sh ? 3 : 2, tra, s));
   // dW_ld, dW_sg, dW_su: one launch of three products over K = tokens
   NtProd pr[3] = {{w.dzT, Tp, w.xT, Tp, dw_lat_down, D, L, D},
                   {w.dshT, Tp, w.xT, Tp, dws_gate, D, SF, D},
