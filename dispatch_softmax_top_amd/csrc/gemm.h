@@ -478,6 +478,102 @@ __device__ __forceinline__ int g_acc_col(int j) {
   return wn * GWTN + j * 32 + (lane & 31);
 }
 
+// ---- epilogue stores through LDS
+//
+// The MFMA layout gives a lane one column of 4-row groups, so storing the
+// accumulators directly takes one 2-byte store per element.  g_wave_store
+// instead writes the wave's bf16 tile into its own LDS region and stores it
+// back by 16-byte row chunks (8 full rows per instruction for 64 columns).
+// Inside every group of 4 lanes (4 neighbouring columns) a 4 x 4 transpose of
+// the lanes' 4-row groups (two DPP swaps) first gives each lane 4 consecutive
+// columns of one row: one 8-byte LDS write.  For 64-column tiles the 16-byte
+// chunk index is XORed with bit 1 of the row, so the 8 rows of one write
+// instruction fall on distinct banks.
+//
+// The regions (8 waves x 128 rows x 32*NJ columns, at most 128 KB) lie in the
+// operand ring.  In the ping-pong loop every LDS read of the ring precedes the
+// loop's last barrier, which every wave has passed on return, so no barrier is
+// needed here; the two-stage loop gets one.
+constexpr int GSTAGE = GNT / 64 * GWTM * GWTN;  // elements of the largest regions
+static_assert(GSTAGE + 2 * GBM <= GNST * (GSA + GSB), "store regions + 256 row indices");
+
+template <int NJ>
+__device__ __forceinline__ int g_stage_chunk(int row, int c) {
+  return NJ == 2 ? c ^ (((row >> 1) & 1) << 2) : c;
+}
+
+// pair(i, j, k): bf16 values of accumulator elements 2k (low half) and
+// 2k + 1 (high half) of MFMA tile (i, j) of this wave; row_ptr(r): output row
+// of wave-tile row r at the wave's first column (nullptr: row not stored),
+// 16-byte aligned; ncols: valid columns from there (a multiple of 8).  Every
+// lane of the wave must call it.
+template <int NJ, class Pair, class RowPtr>
+__device__ __forceinline__ void g_wave_store_pairs(uint16_t *ring, Pair pair, RowPtr row_ptr,
+                                                   int ncols) {
+  static_assert(NJ == 1 || NJ == 2, "32 or 64 columns per wave");
+  constexpr int W = NJ * 32, CH = W / 8;
+  if constexpr (!GPP) __syncthreads();
+  const int lane = lane_id();
+  uint16_t *st = ring + (threadIdx.x >> 6) * (GWTM * W);
+  const bool b1 = lane & 2, b0 = lane & 1;
+  const int col4 = (lane & 31) & ~3;
+#pragma unroll
+  for (int i = 0; i < GTM; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // rows 0,1 and 2,3 of this lane's column
+        const uint32_t p0 = pair(i, j, 2 * q), p1 = pair(i, j, 2 * q + 1);
+        // with lane ^ 2: keep rows 2*b1, 2*b1 + 1 of both columns
+        const uint32_t r1 =
+            (uint32_t)__builtin_amdgcn_mov_dpp((int)(b1 ? p0 : p1), 0x4E, 0xF, 0xF, false);
+        const uint32_t keep = b1 ? p1 : p0;
+        const uint32_t x = b1 ? r1 : keep;  // column col4 + b0
+        const uint32_t y = b1 ? keep : r1;  // column col4 + 2 + b0
+        // with lane ^ 1: keep row 2*b1 + b0 of all four columns
+        const uint32_t s = b0 ? ((x & 0xffffu) | (y << 16)) : ((x >> 16) | (y & 0xffff0000u));
+        const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s, 0xB1, 0xF, 0xF, false);
+        uint32_t o0, o1;
+        if (b0) {
+          o0 = (r2 & 0xffffu) | (x & 0xffff0000u);
+          o1 = (r2 >> 16) | (y & 0xffff0000u);
+        } else {
+          o0 = (x & 0xffffu) | (r2 << 16);
+          o1 = (y & 0xffffu) | (r2 & 0xffff0000u);
+        }
+        const int row = i * 32 + 8 * q + 4 * (lane >> 5) + (lane & 3);
+        const int col = j * 32 + col4;
+        uint32_t *dst = reinterpret_cast<uint32_t *>(
+            st + row * W + g_stage_chunk<NJ>(row, col >> 3) * 8 + (col & 7));
+        dst[0] = o0;
+        dst[1] = o1;
+      }
+#pragma unroll
+  for (int it = 0; it < GWTM * CH / 64; ++it) {
+    const int q = it * 64 + lane, row = q / CH, c = q % CH;
+    const u32x4 v =
+        *reinterpret_cast<const u32x4 *>(st + row * W + g_stage_chunk<NJ>(row, c) * 8);
+    uint16_t *p = row_ptr(row);
+    if (p && c * 8 < ncols) *reinterpret_cast<u32x4 *>(p + c * 8) = v;
+  }
+}
+
+// val(i, j, v): fp32 value of accumulator element v of MFMA tile (i, j),
+// rounded to bf16 here.
+template <int NJ, class Val, class RowPtr>
+__device__ __forceinline__ void g_wave_store(uint16_t *ring, Val val, RowPtr row_ptr, int ncols) {
+  g_wave_store_pairs<NJ>(
+      ring, [&](int i, int j, int k) { return pack_bf16x2(val(i, j, 2 * k), val(i, j, 2 * k + 1)); },
+      row_ptr, ncols);
+}
+
+// Whether a bf16 output (base, row stride ld, columns n) takes 16-byte
+// stores.
+__device__ __forceinline__ bool g_vec_out(const void *base, int64_t ld, int n) {
+  return (((uintptr_t)base & 15) | (ld & 7) | (n & 7)) == 0;
+}
+
 // SwiGLU tiles: in every wave's column range, MFMA column tiles alternate
 // gate (even j) and up (odd j) weight rows of the same 32 intermediate
 // columns, so a lane holds a = u.W_g in tile 2p and b = u.W_u in tile 2p + 1.

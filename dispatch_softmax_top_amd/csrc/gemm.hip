@@ -184,9 +184,22 @@ __device__ __forceinline__ int dense_batch(const DenseArgs &g, int per, int &til
 }
 
 // ONLY >= 0: store MFMA row group ONLY alone.
+// ONLY < 0 with the operand ring given: the whole tile through LDS
+// (g_wave_store) when the output allows 16-byte stores.
 template <int ONLY = -1>
 __device__ __forceinline__ void dense_store(const DenseArgs &g, uint16_t *C, int mt, int nt,
-                                            const GAcc &acc) {
+                                            const GAcc &acc, uint16_t *ring = nullptr) {
+  if (ONLY < 0 && ring && g_vec_out(C, g.ldc, g.N)) {
+    const int w = (int)(threadIdx.x >> 6);
+    const int m0 = mt * GBM + (w / GWN) * GWTM, n0 = nt * GBN + (w % GWN) * GWTN;
+    g_wave_store<GTN>(
+        ring, [&](int i, int j, int v) { return acc[i][j][v]; },
+        [&](int r) -> uint16_t * {
+          return m0 + r < g.M ? C + (int64_t)(m0 + r) * g.ldc + n0 : nullptr;
+        },
+        g.N - n0);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < GTM; ++i)
 #pragma unroll
@@ -258,7 +271,7 @@ __device__ __forceinline__ void dense_body(const DenseArgs &g, const GemmLds &ld
     g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
     return;
   }
-  dense_store(g, g.C + b * g.bsC, mt, nt, acc);
+  dense_store(g, g.C + b * g.bsC, mt, nt, acc, lds.A[0]);
 }
 
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_latent_down_kernel(DenseArgs g) {
@@ -341,7 +354,16 @@ __device__ __forceinline__ int multi_ktiles(const MultiArgs &g, int p) {
 
 template <int ONLY = -1>
 __device__ __forceinline__ void multi_store(uint16_t *C, int64_t ldc, int M, int N, int mt, int nt,
-                                            const GAcc &acc) {
+                                            const GAcc &acc, uint16_t *ring = nullptr) {
+  if (ONLY < 0 && ring && g_vec_out(C, ldc, N)) {
+    const int w = (int)(threadIdx.x >> 6);
+    const int m0 = mt * GBM + (w / GWN) * GWTM, n0 = nt * GBN + (w % GWN) * GWTN;
+    g_wave_store<GTN>(
+        ring, [&](int i, int j, int v) { return acc[i][j][v]; },
+        [&](int r) -> uint16_t * { return m0 + r < M ? C + (int64_t)(m0 + r) * ldc + n0 : nullptr; },
+        N - n0);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < GTM; ++i)
 #pragma unroll
@@ -378,7 +400,7 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
     g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
     return;
   }
-  multi_store(g.C[p], g.ldc[p], M, N, mt, nt, acc);
+  multi_store(g.C[p], g.ldc[p], M, N, mt, nt, acc, lds.A[0]);
 }
 
 __global__ __launch_bounds__(GNT) void gemm_nt_multi_tail_kernel(MultiArgs g) {
@@ -543,8 +565,23 @@ __device__ __forceinline__ void swiglu_acc(const SwigluArgs &g, RowOf row_of, in
 //   silu'(a) = s (1 + a (1 - s)), s = 1 / (1 + e^-a).
 template <int ONLY = -1, bool BWD = false, class RowOf>
 __device__ __forceinline__ void swiglu_store(const SwigluArgs &g, RowOf row_of, int rows, int ft,
-                                             int h_col0, const GAcc &acc) {
+                                             int h_col0, const GAcc &acc,
+                                             uint16_t *ring = nullptr) {
   const int f0 = ft * 128;
+  // the backward's three outputs keep the direct stores: staged, they need
+  // more than 256 VGPRs
+  if (!BWD && ONLY < 0 && ring && g_vec_out(g.H + h_col0, g.ldh, 8)) {
+    static_assert(GTN == 2, "one gate and one up tile per wave");
+    const int w = (int)(threadIdx.x >> 6);
+    const int m0 = (w / GWN) * GWTM, c0 = h_col0 + f0 + (w % GWN) * (GWTN / 2);
+    g_wave_store<1>(
+        ring, [&](int i, int, int v) { return silu_f32(acc[i][0][v]) * acc[i][1][v]; },
+        [&](int r) -> uint16_t * {
+          return m0 + r < rows ? g.H + row_of(m0 + r) * g.ldh + c0 : nullptr;
+        },
+        GWTN / 2);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < GTM; ++i) {
     if (ONLY >= 0 && i != ONLY) continue;
@@ -609,7 +646,7 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
     g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
     return;
   }
-  swiglu_store<-1, BWD>(g, row_of, rows, ft, s * g.F, acc);
+  swiglu_store<-1, BWD>(g, row_of, rows, ft, s * g.F, acc, lds.A[0]);
 }
 
 template <bool BWD>
@@ -648,7 +685,7 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
     g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
     return;
   }
-  swiglu_store<-1, BWD>(g, row_of, t.rows, t.nt, 0, acc);
+  swiglu_store<-1, BWD>(g, row_of, t.rows, t.nt, 0, acc, lds.A[0]);
 }
 
 template <bool BWD>
@@ -686,7 +723,20 @@ struct DownArgs {
 // dst_of(m): receive row of tile row m (negative or >= n_ret: not stored).
 template <int ONLY = -1, class DstOf>
 __device__ __forceinline__ void down_store(const DownArgs &g, const GTile &t, DstOf dst_of,
-                                           const GAcc &acc) {
+                                           const GAcc &acc, uint16_t *ring = nullptr) {
+  if (ONLY < 0 && ring && g_vec_out(g.ret, g.L, g.L)) {
+    const int w = (int)(threadIdx.x >> 6);
+    const int m0 = (w / GWN) * GWTM, n0 = t.nt * GBN + (w % GWN) * GWTN;
+    g_wave_store<GTN>(
+        ring, [&](int i, int j, int v) { return acc[i][j][v]; },
+        [&](int r) -> uint16_t * {
+          if (m0 + r >= t.rows) return nullptr;
+          const int64_t dr = dst_of(m0 + r);
+          return dr >= 0 && dr < g.n_ret ? g.ret + dr * g.L + n0 : nullptr;
+        },
+        g.L - n0);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < GTM; ++i)
 #pragma unroll
@@ -733,11 +783,12 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
     g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
     return;
   }
-  int32_t *dst_rows = reinterpret_cast<int32_t *>(lds.A[0]);
+  // past the store regions of g_wave_store
+  int32_t *dst_rows = reinterpret_cast<int32_t *>(lds.A[0] + GSTAGE);
   __syncthreads();  // every wave is past its last fragment read of the ring
   if ((int)threadIdx.x < GBM) dst_rows[threadIdx.x] = my_dst;
   __syncthreads();
-  down_store(g, t, [&](int m) { return (int64_t)dst_rows[m]; }, acc);
+  down_store(g, t, [&](int m) { return (int64_t)dst_rows[m]; }, acc, lds.A[0]);
 }
 
 __global__ __launch_bounds__(GNT) void gemm_expert_down_tail_kernel(DownArgs g) {
