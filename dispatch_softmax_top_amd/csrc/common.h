@@ -148,4 +148,17 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// For tiles of unequal cost (products whose K is known only on the device):
+// XCD x takes groups x, x + 8, x + 16, ... of G consecutive tiles, so a run
+// of long tiles is spread over every XCD instead of filling one or two, while
+// the G tiles of a group still share an operand panel in one L2.  Blocks past
+// the last whole round of 8 groups keep their own index.
+template <int G>
+__device__ __forceinline__ int xcd_spread(int bid, int nblocks) {
+  constexpr int NX = 8;
+  if (bid >= nblocks - nblocks % (NX * G)) return bid;
+  const int xcd = bid % NX, local = bid / NX;
+  return ((local / G) * NX + xcd) * G + local % G;
+}
+
 }  // namespace moe

@@ -55,15 +55,17 @@ __device__ __forceinline__ int g_split_parts(const GSplit &sp, int total) {
 }
 
 // Block b of a launch: whole tiles first (each XCD a contiguous range of
-// them), then the parts of the split tiles.  False past the last unit.
-__device__ __forceinline__ bool g_unit(const GSplit &sp, int total, int b, GUnit &u) {
+// them, or with spread, groups of 8 dealt round the XCDs: xcd_spread), then
+// the parts of the split tiles.  False past the last unit.
+__device__ __forceinline__ bool g_unit(const GSplit &sp, int total, int b, GUnit &u,
+                                       bool spread = false) {
   const int S = g_split_parts(sp, total);
   const int whole = S > 1 ? total - total % sp.ncu : total;
   u.part = 0;
   u.nparts = 1;
   u.tail = 0;
   if (b < whole) {
-    u.tile = __builtin_amdgcn_readfirstlane(xcd_remap(b, whole));
+    u.tile = __builtin_amdgcn_readfirstlane(spread ? xcd_spread<8>(b, whole) : xcd_remap(b, whole));
     return true;
   }
   const int t = b - whole;
@@ -381,7 +383,8 @@ __device__ __forceinline__ void multi_store(uint16_t *C, int64_t ldc, int M, int
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_nt_multi_kernel(MultiArgs g) {
   MOE_GEMM_LDS(lds);
   GUnit u;
-  if (!g_unit(g.sp, g.first[g.nprod], blockIdx.x, u)) return;
+  // with K from the device, tile costs differ by product
+  if (!g_unit(g.sp, g.first[g.nprod], blockIdx.x, u, g.kfill != nullptr)) return;
   const int p = multi_product(g, u.tile);
   const int M = g.M[p], N = g.N[p];
   const int tm = (M + GBM - 1) / GBM, tn = (N + GBN - 1) / GBN;
