@@ -11,7 +11,7 @@
 // operands K-contiguous (C = A . B^T).  Weight gradients (a sum over tokens
 // or bank rows) and input gradients through a weight stored output-major need
 // the other operand orders; they get them from 64x64 LDS-tiled transposes
-// into the workspace (HBM-bound copies).
+// into the workspace (HBM-bound copies, two to four per launch).
 //
 // Calls and kernels, in stream order:
 //   moe_combine_backward  transposes of W_lu, W_sd; [d_ylat | d_h_s] =

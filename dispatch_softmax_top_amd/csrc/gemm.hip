@@ -186,12 +186,12 @@ __device__ __forceinline__ int dense_batch(const DenseArgs &g, int per, int &til
 }
 
 // ONLY >= 0: store MFMA row group ONLY alone.
-// ONLY < 0 with the operand ring given: the whole tile through LDS
+// ONLY < 0 (the operand ring given): the whole tile through LDS
 // (g_wave_store) when the output allows 16-byte stores.
 template <int ONLY = -1>
 __device__ __forceinline__ void dense_store(const DenseArgs &g, uint16_t *C, int mt, int nt,
                                             const GAcc &acc, uint16_t *ring = nullptr) {
-  if (ONLY < 0 && ring && g_vec_out(C, g.ldc, g.N)) {
+  if (ONLY < 0 && g_vec_out(C, g.ldc, g.N)) {
     const int w = (int)(threadIdx.x >> 6);
     const int m0 = mt * GBM + (w / GWN) * GWTM, n0 = nt * GBN + (w % GWN) * GWTN;
     g_wave_store<GTN>(
@@ -357,7 +357,7 @@ __device__ __forceinline__ int multi_ktiles(const MultiArgs &g, int p) {
 template <int ONLY = -1>
 __device__ __forceinline__ void multi_store(uint16_t *C, int64_t ldc, int M, int N, int mt, int nt,
                                             const GAcc &acc, uint16_t *ring = nullptr) {
-  if (ONLY < 0 && ring && g_vec_out(C, ldc, N)) {
+  if (ONLY < 0 && g_vec_out(C, ldc, N)) {
     const int w = (int)(threadIdx.x >> 6);
     const int m0 = mt * GBM + (w / GWN) * GWTM, n0 = nt * GBN + (w % GWN) * GWTN;
     g_wave_store<GTN>(
@@ -573,7 +573,7 @@ __device__ __forceinline__ void swiglu_store(const SwigluArgs &g, RowOf row_of, 
   const int f0 = ft * 128;
   // the backward's three outputs keep the direct stores: staged, they need
   // more than 256 VGPRs
-  if (!BWD && ONLY < 0 && ring && g_vec_out(g.H + h_col0, g.ldh, 8)) {
+  if (!BWD && ONLY < 0 && g_vec_out(g.H + h_col0, g.ldh, 8)) {
     static_assert(GTN == 2, "one gate and one up tile per wave");
     const int w = (int)(threadIdx.x >> 6);
     const int m0 = (w / GWN) * GWTM, c0 = h_col0 + f0 + (w % GWN) * (GWTN / 2);
@@ -727,7 +727,7 @@ struct DownArgs {
 template <int ONLY = -1, class DstOf>
 __device__ __forceinline__ void down_store(const DownArgs &g, const GTile &t, DstOf dst_of,
                                            const GAcc &acc, uint16_t *ring = nullptr) {
-  if (ONLY < 0 && ring && g_vec_out(g.ret, g.L, g.L)) {
+  if (ONLY < 0 && g_vec_out(g.ret, g.L, g.L)) {
     const int w = (int)(threadIdx.x >> 6);
     const int m0 = (w / GWN) * GWTM, n0 = t.nt * GBN + (w % GWN) * GWTN;
     g_wave_store<GTN>(
