@@ -55,7 +55,7 @@ __device__ __forceinline__ int g_split_parts(const GSplit &sp, int total) {
 }
 
 // Block b of a launch: whole tiles first (each XCD a contiguous range of
-// them, or with spread, groups of 8 dealt round the XCDs: xcd_spread), then
+// them, or with spread, groups of 32 dealt round the XCDs: xcd_spread), then
 // the parts of the split tiles.  False past the last unit.
 __device__ __forceinline__ bool g_unit(const GSplit &sp, int total, int b, GUnit &u,
                                        bool spread = false) {
@@ -65,7 +65,7 @@ __device__ __forceinline__ bool g_unit(const GSplit &sp, int total, int b, GUnit
   u.nparts = 1;
   u.tail = 0;
   if (b < whole) {
-    u.tile = __builtin_amdgcn_readfirstlane(spread ? xcd_spread<8>(b, whole) : xcd_remap(b, whole));
+    u.tile = __builtin_amdgcn_readfirstlane(spread ? xcd_spread<32>(b, whole) : xcd_remap(b, whole));
     return true;
   }
   const int t = b - whole;
