@@ -182,6 +182,9 @@ def rank_experts(cfg, rank: int, device="cpu", seed: int = 0):
 def shared(cfg, device="cpu", seed: int = 0):
     """(W_sg [S,Fs,D], W_su [S,Fs,D], W_sd [S,D,Fs])."""
     S, Fs, D = cfg.n_shared, cfg.d_ff_shared, cfg.d_model
+    if S == 0:
+        e = torch.empty((0, Fs, D), dtype=torch.bfloat16, device=device)
+        return e, e.clone(), torch.empty((0, D, Fs), dtype=torch.bfloat16, device=device)
     g = torch.stack([normal_bf16((Fs, D), D ** -0.5, WSG, s, seed, device) for s in range(S)])
     u = torch.stack([normal_bf16((Fs, D), D ** -0.5, WSU, s, seed, device) for s in range(S)])
     d = torch.stack([normal_bf16((D, Fs), Fs ** -0.5, WSD, s, seed, device) for s in range(S)])

@@ -22,6 +22,9 @@ CASES = {
     "mid": gc.MID,
     "mid_tight": gc.with_cf(gc.MID, "1/2", "3/5"),
     "mid_chunks": gc.chunked(gc.MID),
+    # degenerate shapes: top-1 routing, one wave, no shared experts
+    "tiny_k1_w1_s0": configs.scaled(configs.TINY, configs.TINY.name + "_k1_W1_S0", top_k=1,
+                                    n_waves=1, n_shared=0),
 }
 
 
@@ -228,7 +231,7 @@ def test_backward_rejects_ragged_and_small_workspace(moe, share):
 # whole backward chain on each side, after each side's own forward chain
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny", "mid_chunks"])
+@pytest.mark.parametrize("name", ["tiny", "mid_chunks", "tiny_k1_w1_s0"])
 def test_backward_chain(moe, orc, share, name):
     """Forward then backward for rank 0 on each side: GPU calls only on the
     GPU, oracle calls only in the oracle, both exchanges as loopback

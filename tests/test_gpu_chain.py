@@ -24,6 +24,12 @@ CASES = {
     "mid_zipf": gc.skewed(gc.MID),
     "mid_zipf_chunks": gc.chunked(gc.skewed(gc.MID)),
     "mid_dedup": gc.deduped(gc.MID),
+    # degenerate shapes: one rank holding every expert, one wave, no capacity,
+    # no shared experts (a plain top-k MoE layer); top-1 routing
+    "tiny_dense_r1_w1_s0": configs.scaled(configs.TINY, configs.TINY.name + "_R1_W1_S0",
+                                          n_ranks=1, n_waves=1, n_shared=0, cf_send=None,
+                                          cf_recv=None),
+    "mid_k1": configs.scaled(gc.MID, gc.MID.name + "_k1", top_k=1),
 }
 
 

@@ -151,13 +151,15 @@ def torch_backward(cfg, W_, S, keep, d_out):
     return X, LG, wld, wlu, wsg, wsu, wsd, ex
 
 
-@pytest.mark.parametrize("case", ["1.10/1.15", "tight", "chunks", "t16"])
+@pytest.mark.parametrize("case", ["1.10/1.15", "tight", "chunks", "t16", "t16_k1_w1_s0"])
 def test_branch_backward_matches_autograd(orc, case):
     from dataclasses import replace
     from fractions import Fraction
     cfg = configs.TINY
     if case == "t16":                 # 16 tokens per shard: the quick case
         cfg = replace(cfg, T=16)
+    elif case == "t16_k1_w1_s0":      # top-1, one wave, no shared experts
+        cfg = replace(cfg, T=16, top_k=1, n_waves=1, n_shared=0)
     elif case == "tight":
         cfg = replace(cfg, cf_send=Fraction(1, 2), cf_recv=Fraction(1, 2))
     elif case == "chunks":
@@ -175,9 +177,12 @@ def test_branch_backward_matches_autograd(orc, case):
     R = cfg.n_ranks
     _close(sum(f64(PB[s][2]) for s in range(R)), wld.grad.numpy(), "dw_lat_down")
     _close(sum(f64(CB[s][3]) for s in range(R)), wlu.grad.numpy(), "dw_lat_up")
-    _close(sum(f64(PB[s][3]) for s in range(R)), wsg.grad.numpy(), "dws_gate")
-    _close(sum(f64(PB[s][4]) for s in range(R)), wsu.grad.numpy(), "dws_up")
-    _close(sum(f64(CB[s][4]) for s in range(R)), wsd.grad.numpy(), "dws_down")
+    if cfg.n_shared:
+        _close(sum(f64(PB[s][3]) for s in range(R)), wsg.grad.numpy(), "dws_gate")
+        _close(sum(f64(PB[s][4]) for s in range(R)), wsu.grad.numpy(), "dws_up")
+        _close(sum(f64(CB[s][4]) for s in range(R)), wsd.grad.numpy(), "dws_down")
+    else:
+        assert all(PB[s][3].size == PB[s][4].size == CB[s][4].size == 0 for s in range(R))
     for r in range(R):
         for i, name in ((1, "dw_gate"), (2, "dw_up"), (3, "dw_down")):
             ref = ex[r][i - 1].grad.numpy()

@@ -181,11 +181,19 @@ def brute_force(cfg, d, W_, S):
 
 
 @pytest.mark.parametrize("cf", ["1.10/1.15", "inf", "tight", "chunks", "chunks_tight", "dedup_tight",
-                                "dedup_chunks"])
+                                "dedup_chunks", "dense_r1_w1_s0", "k1_w1", "k1_tight"])
 def test_e2e_tiny_matches_brute_force(orc, cf):
     from dataclasses import replace
     from fractions import Fraction
     cfg = configs.TINY
+    if cf == "dense_r1_w1_s0":
+        # one rank, one wave, no capacity, no shared experts: a plain top-k
+        # MoE layer with every expert local
+        cfg = replace(cfg, n_ranks=1, n_waves=1, n_shared=0, cf_send=None, cf_recv=None)
+    elif cf.startswith("k1"):    # top-1 routing (a gate per token)
+        cfg = replace(cfg, top_k=1, n_waves=1 if cf == "k1_w1" else cfg.n_waves)
+        if cf == "k1_tight":
+            cfg = replace(cfg, cf_send=Fraction(1, 2), cf_recv=Fraction(1, 2))
     if cf == "inf":
         cfg = replace(cfg, cf_send=None, cf_recv=None)
     elif cf.endswith("tight"):   # forces sender and receiver drops
