@@ -19,7 +19,7 @@ namespace moe {
 
 constexpr int RK_THREADS = 1024;
 constexpr int RK_WAVES = RK_THREADS / 64;
-constexpr int RK_IPT = 8;
+constexpr int RK_IPT = 2;
 constexpr int RK_TILE = RK_THREADS * RK_IPT;
 constexpr int RK_MAXK = 1024;
 
