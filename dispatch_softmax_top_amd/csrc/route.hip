@@ -34,14 +34,42 @@ __device__ __forceinline__ float unord_f32(uint32_t o) {
   return __uint_as_float(u);
 }
 
+// v from the lane DPP control CTRL selects (both halves).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum over the wave, returned wave-uniform.  Inside each row of 16 lanes
+// by DPP moves (swaps within quads, then rotations by 4 and 8), then across
+// the four rows by reading one lane of each: no LDS round trips, which the
+// k dependent rounds of the choice loop would otherwise wait on.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = o > v ? o : v;
+  o = dpp_u64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = o > v ? o : v;
+  o = dpp_u64<0x124>(v);  // row_ror:4
+  v = o > v ? o : v;
+  o = dpp_u64<0x128>(v);  // row_ror:8
+  v = o > v ? o : v;
+  uint64_t r = readlane_u64(v, 0);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
+  for (int l = 16; l < 64; l += 16) {
+    const uint64_t x = readlane_u64(v, l);
+    r = x > r ? x : r;
   }
-  return v;
+  return r;
 }
 
 // bias: NULL, or [E] fp32 added to every token's logits (one fp32 rounding).
