@@ -184,3 +184,59 @@ def moe_lib():
     import dispatch_softmax_top_amd as m
     m.lib()
     return m
+
+
+def test_full_expert_backward_skewed(moe_lib, orc):
+    """The hottest Zipf rank's pattern at full size (16384 tokens): two of the
+    six local experts saturated in every wave, four with no rows, so the
+    weight-gradient launch mixes products of 786 K tiles with products of the
+    minimum K.  Sampled receive rows and weight entries against the oracle;
+    the empty experts' weight gradients exactly zero."""
+    from dispatch_softmax_top_amd import share
+    moe = moe_lib
+    cfg = configs.ZIPF_16K
+    rng = np.random.default_rng(zlib.crc32(b"skewed experts"))
+    d_orc, d = orc.dims(cfg), share.make_dims(cfg)
+    L, El, R, W = cfg.latent, cfg.experts_per_rank, cfg.n_ranks, cfg.n_waves
+    n_rows = R * W * d.cap_send
+    rank, hot = 35, np.array([2, 5])
+    print("\n[full backward] skewed experts: bank slots", flush=True)
+    hdr = np.where(rng.random(n_rows) < 0.9, rank * El + rng.choice(hot, n_rows), -1)
+    bo = orc.bank_slots(d_orc, rank, hdr.astype(np.int32), None)
+    fills = bo["bfill"].reshape(W, El)
+    assert (fills[:, hot] == d.cap_recv).all() and fills.sum() == W * len(hot) * d.cap_recv
+    nb = len(bo["bank_src"])
+    b = share.Backward(d, n_rows)
+    bank, d_ret = gen.payload_rows(nb, L, 94, "cuda"), gen.payload_rows(n_rows, L, 95, "cuda")
+    h_bank, h_dret = u16(bank), u16(d_ret)
+    wg, wu, wdn = gen.rank_experts(cfg, rank)
+    dev = lambda a: gc.dev(np.ascontiguousarray(a))
+    print("[full backward] skewed experts: GPU", flush=True)
+    moe.moe_expert_ffn_backward(d, bank, dev(bo["bank_src"]), dev(bo["bfill"]), wg.cuda(),
+                                wu.cuda(), wdn.cuda(), d_ret, b.d_recv, b.dw_gate,
+                                b.dw_up, b.dw_down, b.ws_ffn)
+    torch.cuda.synchronize()
+    g_drecv = gc.host(b.d_recv)
+    kept = np.zeros(n_rows, bool)
+    kept[bo["bank_src"][bo["bank_src"] >= 0]] = True
+    assert (g_drecv[~kept] == 0).all()
+    print("[full backward] skewed experts: oracle rows", flush=True)
+    filled = np.nonzero(bo["bank_src"] >= 0)[0]
+    cap = d.cap_recv
+    edges = [g * cap + p for g in range(W * El) if bo["bfill"][g] > 0 for p in (0, bo["bfill"][g] - 1)]
+    pos = np.unique(np.concatenate([rng.choice(filled, 6), rng.choice(edges, 4)]))
+    ex = [u16(w) for w in (wg, wu, wdn)]
+    du = orc.expert_ffn_backward_rows(d_orc, h_bank, bo["bank_src"], *ex, h_dret, pos)
+    gc.assert_rows_close(g_drecv[bo["bank_src"][pos]], du, "d_recv")
+    cold = np.setdiff1d(np.arange(El), hot)
+    for which, got in ((0, b.dw_gate), (1, b.dw_up), (2, b.dw_down)):
+        gw = gc.host(got)
+        assert (gw[cold] == 0).all(), f"weight {which}: an expert without rows has a gradient"
+        print(f"[full backward] skewed experts: oracle entries of weight {which}", flush=True)
+        for j in hot:
+            ra = rng.integers(0, gw.shape[1], 2)
+            cb = rng.integers(0, gw.shape[2], 2)
+            ref = orc.expert_wgrad_entries(d_orc, h_bank, bo["bank_src"], bo["bfill"], *ex,
+                                           h_dret, int(j), which, ra, cb)
+            _close_entries(gw[j, ra, cb], ref, np.abs(f64(gw[j, ra])).max(1),
+                           f"expert weight {which} of expert {j}")
