@@ -7,6 +7,7 @@ from ._lib import (EXPORTS, MOE_CALL_BANK, MOE_CALL_COMBINE, MOE_CALL_COMBINE_BW
                    moe_abi_version, moe_balance_bias, moe_bank, moe_capacity, moe_combine,
                    moe_combine_backward, moe_combine_shared, moe_expert_counts, moe_expert_ffn,
                    moe_expert_ffn_backward, moe_pack_backward, moe_pack_waves,
+                   moe_pack_waves_noalloc, MOE_NOALLOC_SCRATCH_BYTES,
                    moe_profile_collect, moe_profile_enable, moe_profile_read, moe_profile_reset,
                    moe_route, moe_route_backward, moe_route_biased, moe_shared_swiglu,
                    moe_workspace_bytes)

@@ -51,6 +51,8 @@ _SIGS = {
     "moe_balance_bias": (ctypes.c_int, [_VP, _I32, _I32, ctypes.c_double, _VP, _VP]),
     "moe_pack_waves": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                       _I64, _VP]),
+    "moe_pack_waves_noalloc": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                              _VP, _VP]),
     "moe_bank": (ctypes.c_int, [_DP, _I32, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                 _I64, _VP]),
     "moe_expert_ffn": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP, _VP, _I64,
@@ -161,6 +163,17 @@ def moe_pack_waves(d, x, w_lat_down, topk, z, pools, pool_offsets, slot, fill, d
     _check(lib().moe_pack_waves(ctypes.byref(d), _p(x), _p(w_lat_down), _p(topk), _p(z),
                                 _p(pools), _p(pool_offsets), _p(slot), _p(fill), _p(demand),
                                 _p(ws), nbytes, _stream(stream)))
+
+
+def moe_pack_waves_noalloc(d, x, w_lat_down, topk, z, pools, pool_offsets, slot, fill, demand,
+                           stream=None):
+    """moe_pack_waves with its scratch in the library's fixed device array."""
+    _check(lib().moe_pack_waves_noalloc(ctypes.byref(d), _p(x), _p(w_lat_down), _p(topk),
+                                        _p(z), _p(pools), _p(pool_offsets), _p(slot), _p(fill),
+                                        _p(demand), _stream(stream)))
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 
 def moe_bank(d, rank, recv, recv_offsets, n_recv_rows, bank, bank_offsets, bank_src, bfill,

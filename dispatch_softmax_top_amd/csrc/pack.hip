@@ -22,6 +22,7 @@
 //   pack_rows                 one wave per token: z[t] read once, written to
 //                             each kept destination row with 16-byte stores;
 //                             extra blocks stamp id -1 on unfilled slots
+#include <mutex>
 #include <type_traits>
 
 #include "gemm.h"
@@ -224,14 +225,43 @@ static int sender_slots(const moe_dims &d, const int32_t *topk, int32_t *slot, i
                 topk, slot, n, d.top_k, experts_per_rank(d));
 }
 
-}  // namespace moe
+// Scratch of moe_pack_waves_noalloc: the per-tile key counts of the
+// sender's slot assignment, in a fixed device array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  rank_count writes every entry rank_assign reads, so nothing
+// needs clearing between calls.
+static __device__ __align__(256) int32_t scratch[MOE_NOALLOC_SCRATCH_BYTES / 4];
 
-using namespace moe;
+// Device address of `scratch` on each device, taken once per device with it
+// current.  In host code the array's name is only a stand-in symbol: kernels
+// get this address, never the name.
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[SCRATCH_MAX_DEVICES];
 
-extern "C" int moe_pack_waves(const moe_dims *d, const moe_bf16 *x, const moe_bf16 *w_lat_down,
-                              const int32_t *topk, moe_bf16 *z, uint8_t *pools,
-                              int64_t *pool_offsets, int32_t *slot, int32_t *fill,
-                              int32_t *demand, void *ws, int64_t ws_bytes, void *stream) {
+static int noalloc_scratch(void **out) {
+  int dev = -1;
+  MOE_TRY(hip_status(hipGetDevice(&dev), "moe_pack_waves_noalloc: hipGetDevice"));
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_pack_waves_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    MOE_TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                       "moe_pack_waves_noalloc: hipGetSymbolAddress"));
+    if (!p) return fail(MOE_ERR_HIP, "moe_pack_waves_noalloc: scratch has no device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// Both entry points: checks on the host, then the launches.  fixed_scratch:
+// the slot assignment's counts go to `scratch` (ws and ws_bytes unused).
+static int pack_waves(const moe_dims *d, const moe_bf16 *x, const moe_bf16 *w_lat_down,
+                      const int32_t *topk, moe_bf16 *z, uint8_t *pools, int64_t *pool_offsets,
+                      int32_t *slot, int32_t *fill, int32_t *demand, void *ws, int64_t ws_bytes,
+                      bool fixed_scratch, void *stream) {
   clear_error();
   MOE_TRY(check_dims(d));
   const bool rg = ragged(*d);
@@ -246,12 +276,21 @@ extern "C" int moe_pack_waves(const moe_dims *d, const moe_bf16 *x, const moe_bf
   if (rg) MOE_TRY(check_ptr(pool_offsets, "pool_offsets (ragged mode)"));
   const int64_t need = moe_workspace_bytes(d, MOE_CALL_PACK, 0);
   if (need < 0) return (int)need;
-  if (ws_bytes < need || (need > 0 && !ws))
-    return fail(MOE_ERR_WORKSPACE, "moe_pack_waves: workspace %lld < %lld bytes",
-                (long long)ws_bytes, (long long)need);
-  if (ws) MOE_TRY(check_ptr(ws, "ws"));
+  if (fixed_scratch) {
+    if (need > MOE_NOALLOC_SCRATCH_BYTES)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "moe_pack_waves_noalloc: needs %lld scratch bytes, the fixed scratch holds "
+                  "%lld (use moe_pack_waves with a workspace)",
+                  (long long)need, (long long)MOE_NOALLOC_SCRATCH_BYTES);
+  } else {
+    if (ws_bytes < need || (need > 0 && !ws))
+      return fail(MOE_ERR_WORKSPACE, "moe_pack_waves: workspace %lld < %lld bytes",
+                  (long long)ws_bytes, (long long)need);
+    if (ws) MOE_TRY(check_ptr(ws, "ws"));
+  }
   if ((int64_t)d->n_ranks * d->n_waves * d->cap_send >= (1ll << 31))
     return fail(MOE_ERR_UNSUPPORTED, "moe_pack_waves: pool rows must fit in int32");
+  if (fixed_scratch) MOE_TRY(noalloc_scratch(&ws));
   hipStream_t s = (hipStream_t)stream;
   int32_t *tc = (int32_t *)ws;
 
@@ -272,4 +311,25 @@ extern "C" int moe_pack_waves(const moe_dims *d, const moe_bf16 *x, const moe_bf
   if (ch <= 6) return run(std::integral_constant<int, 6>());
   if (ch <= 8) return run(std::integral_constant<int, 8>());
   return run(std::integral_constant<int, 16>());
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_pack_waves(const moe_dims *d, const moe_bf16 *x, const moe_bf16 *w_lat_down,
+                              const int32_t *topk, moe_bf16 *z, uint8_t *pools,
+                              int64_t *pool_offsets, int32_t *slot, int32_t *fill,
+                              int32_t *demand, void *ws, int64_t ws_bytes, void *stream) {
+  return pack_waves(d, x, w_lat_down, topk, z, pools, pool_offsets, slot, fill, demand, ws,
+                    ws_bytes, false, stream);
+}
+
+extern "C" int moe_pack_waves_noalloc(const moe_dims *d, const moe_bf16 *x,
+                                      const moe_bf16 *w_lat_down, const int32_t *topk,
+                                      moe_bf16 *z, uint8_t *pools, int64_t *pool_offsets,
+                                      int32_t *slot, int32_t *fill, int32_t *demand,
+                                      void *stream) {
+  return pack_waves(d, x, w_lat_down, topk, z, pools, pool_offsets, slot, fill, demand, nullptr,
+                    0, true, stream);
 }

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef uint16_t moe_bf16;
 
@@ -193,6 +193,27 @@ int moe_pack_waves(const moe_dims *d, const moe_bf16 *x,
                    moe_bf16 *z, uint8_t *pools, int64_t *pool_offsets,
                    int32_t *slot, int32_t *fill, int32_t *demand, void *ws,
                    int64_t ws_bytes, void *stream);
+
+/* moe_pack_waves without a workspace, for callers that cannot allocate
+ * device memory (code under stream capture, serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, outputs and kernels as moe_pack_waves,
+ * bit for bit; the slot assignment's per-tile counts go to a fixed device
+ * array of MOE_NOALLOC_SCRATCH_BYTES inside the library instead of ws.  The
+ * call allocates nothing.  Each GPU holds one such array (taken on the first
+ * call made with that device current, kept until the process ends), shared
+ * by every call on that GPU: calls that overlap on one GPU (two streams, or
+ * two threads) race on it and must be ordered by the caller.  The stream
+ * must belong to the current device.  Limit: moe_workspace_bytes(d,
+ * MOE_CALL_PACK, 0) <= MOE_NOALLOC_SCRATCH_BYTES, where that size is
+ * ceil(T*top_k/2048) * (n_ranks*n_waves + 1) * 4 bytes rounded up to 256;
+ * with 64 ranks and 3 waves that is T*top_k <= 2,781,184.  Larger shapes
+ * return MOE_ERR_UNSUPPORTED before any launch. */
+#define MOE_NOALLOC_SCRATCH_BYTES (1 << 20)
+int moe_pack_waves_noalloc(const moe_dims *d, const moe_bf16 *x,
+                           const moe_bf16 *w_lat_down, const int32_t *topk,
+                           moe_bf16 *z, uint8_t *pools, int64_t *pool_offsets,
+                           int32_t *slot, int32_t *fill, int32_t *demand,
+                           void *stream);
 
 /* Receiver ([P2]/[P3] section 二; [P1] section 四 and appendix A.3): rows
  * received by `rank` are banked per (wave, local expert) in (source, row)

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(moe):
 
 
 def test_abi_version(moe):
-    assert moe.moe_abi_version() == 5
+    assert moe.moe_abi_version() == 6
 
 
 def test_capacity_matches_table(moe):
