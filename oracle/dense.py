@@ -180,3 +180,63 @@ def combine_tokens(d, returned: np.ndarray, ret_offsets, topk, slot, gates, x, w
                 o += h[:, s * Fs:(s + 1) * Fs] @ wsd[s].T
         out[s0:e0] = bf16_from_f64(o)
     return ylat, out
+
+
+# ----------------------------------------------------------------------------
+# Backward of the branch: whole rows of the weight gradients.  Each weight
+# gradient is a sum over tokens (or bank rows) of an outer product; a row of
+# it needs only one column of one factor, so the oracle can give a whole row
+# (for the tolerance scale of a sampled row, and to check every entry of it)
+# at full size.  Same definitions and rounding points as orc_*_backward.
+# ----------------------------------------------------------------------------
+
+def _silu_grad(a):
+    s = 1.0 / (1.0 + np.exp(-a))
+    return s * (1.0 + a * (1.0 - s))
+
+
+def outer_rows(p: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """bf16(p^T . q) for p [n, r] and q [n, c] (float64 operands): rows of a
+    weight gradient that sums p[t, i] q[t, :] over t."""
+    return bf16_from_f64(p.T @ q)
+
+
+def expert_wgrad_rows(u: np.ndarray, dy: np.ndarray, wg_t, wu_t, wd_t, f_idx):
+    """One local expert's weight gradients at intermediate units f_idx
+    (orc_expert_ffn_backward): u [n, L] its bank rows, dy [n, L] their output
+    gradients.  Returns dw_gate[f_idx, :], dw_up[f_idx, :] and
+    dw_down[:, f_idx]^T, each [len(f_idx), L]:
+      d_h = bf16(dy . W_d[:, f]), a, b = u.W_g[f], u.W_u[f],
+      d_a = bf16(d_h b silu'(a)), d_b = bf16(d_h silu(a)), h = bf16(silu(a) b),
+      dw_gate[f] = bf16(sum_r d_a u), dw_up[f] = bf16(sum_r d_b u),
+      dw_down[:, f] = bf16(sum_r dy h[f])."""
+    f_idx = np.asarray(f_idx, np.int64)
+    U, DY = to_f64(u), to_f64(dy)
+    a = U @ to_f64(wg_t[f_idx]).T
+    b = U @ to_f64(wu_t[f_idx]).T
+    dh = to_f64(bf16_from_f64(DY @ to_f64(wd_t[:, f_idx])))
+    da = to_f64(bf16_from_f64(dh * b * _silu_grad(a)))
+    db = to_f64(bf16_from_f64(dh * _silu(a)))
+    h = to_f64(bf16_from_f64(_silu(a) * b))
+    return outer_rows(da, U), outer_rows(db, U), outer_rows(h, DY)
+
+
+def shared_down_wgrad_cols(x, ws_gate, ws_up, d_out, sh: int, f_idx):
+    """dws_down[sh][:, f_idx]^T ([len(f_idx), D]) = bf16(sum_t h_s[t, f] d_out[t])
+    with h_s = bf16(silu(x.W_sg,s) (x.W_su,s)) (orc_combine_backward)."""
+    f_idx = np.asarray(f_idx, np.int64)
+    X = to_f64(x)
+    a = X @ to_f64(ws_gate[sh][f_idx]).T
+    b = X @ to_f64(ws_up[sh][f_idx]).T
+    return outer_rows(to_f64(bf16_from_f64(_silu(a) * b)), to_f64(d_out))
+
+
+def pack_dz(d, d_pools, topk, slot) -> np.ndarray:
+    """dz[t] = bf16(sum over kept (t, j) of d_pools[row(t, j)]) (fixed mode,
+    orc_pack_backward; j ascending)."""
+    rows = returned_rows(d, None, topk, slot, np.arange(d.T))
+    acc = np.zeros((d.T, d.latent))
+    for j in range(d.top_k):
+        m = rows[:, j] >= 0
+        acc[m] += to_f64(d_pools[rows[m, j]])
+    return bf16_from_f64(acc)

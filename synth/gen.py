@@ -114,6 +114,30 @@ def hidden(cfg, shard: int, device="cpu", seed: int = 0) -> torch.Tensor:
     return normal_bf16((cfg.T, cfg.d_model), 1.0, X, shard, seed, device)
 
 
+def hidden_rows(cfg, shard: int, rows, device="cpu", seed: int = 0) -> torch.Tensor:
+    """Rows ``rows`` of hidden(cfg, shard), bit for bit, without generating
+    the others: element (t, i) is output t*d_model + i of the shard's stream,
+    and with d_model even every row starts a Box-Muller pair."""
+    D = cfg.d_model
+    assert D % 2 == 0
+    st = stream_state(seed, X, shard)
+    r = torch.as_tensor(rows, dtype=torch.int64, device=device).reshape(-1)
+    out = torch.empty(len(r), D, dtype=torch.bfloat16, device=device)
+    step = max(1, _CHUNK // D)
+    for a in range(0, len(r), step):
+        rr = r[a:a + step]
+        # stream positions 2p and 2p+1 feed the pair p = element index / 2
+        pair = rr[:, None] * (D // 2) + torch.arange(D // 2, dtype=torch.int64, device=device)
+        pos = torch.stack((2 * pair, 2 * pair + 1), dim=-1)
+        bits = _mix((pos + 1) * _s64(GOLDEN) + _s64(st))
+        u = (_lsr(bits, 11).to(torch.float64) + 0.5) * (2.0 ** -53)
+        rad = torch.sqrt(-2.0 * torch.log(u[..., 0]))
+        th = (2.0 * math.pi) * u[..., 1]
+        v = torch.stack((rad * torch.cos(th), rad * torch.sin(th)), dim=-1).reshape(len(rr), D)
+        out[a:a + step] = v.to(torch.float32).to(torch.bfloat16)
+    return out
+
+
 def router_weight(cfg, device="cpu", seed: int = 0) -> torch.Tensor:
     return normal_bf16((cfg.n_experts, cfg.d_model), cfg.d_model ** -0.5, WR, 0,
                        seed, device)

@@ -288,3 +288,76 @@ def test_combine_split_equals_combine(moe, share, name):
     assert torch.equal(a.ylat.view(torch.int16), b.ylat.view(torch.int16))
     assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
 
+
+
+# ----------------------------------------------------------------------------
+# K-split last rounds at a size where every row is checked
+# ----------------------------------------------------------------------------
+
+# K = 2048 and 3072 with few block tiles: the expert SwiGLU, the expert down
+# GEMM and the up-projection all cut their (only) round along K
+SPLIT = configs.scaled(gc.MID, "moe_split_T256_D2048_L2048_E48_R8", T=256, d_model=2048,
+                       latent=2048, d_ff=1024, d_ff_shared=512)
+
+
+def test_split_rounds_every_row(moe, orc, share):
+    """Expert FFN and combine on a shape whose GEMMs split their last round
+    along K; every row against oracle/dense.py, and the split tiles' tail
+    kernels seen running."""
+    import fullcheck as fc
+    from oracle import dense
+    cfg, rank = SPLIT, 1
+    d_orc, d = _dims(orc, share, cfg)
+    L, F, D, S, Fs, El = cfg.latent, cfg.d_ff, cfg.d_model, cfg.n_shared, cfg.d_ff_shared, \
+        cfg.experts_per_rank
+    senders = gc.oracle_sender_all(orc, cfg, d_orc)
+    hdr, offs = gc.recv_headers(cfg, d_orc, senders, rank)
+    n = len(hdr)
+    bo = orc.bank_slots(d_orc, rank, hdr, offs)
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    groups = fc.product_groups(d_orc, bo["bfill"], None, max(L, F), len(bo["bank_src"]))
+    S_sw, sw = fc.grouped_split_tiles(groups, F // 128, L, ncu)
+    S_dn, dn = fc.grouped_split_tiles(groups, L // 256, F, ncu)
+    S_up, up = fc.dense_split_mtiles(cfg.T, D, L + S * Fs, ncu)
+    assert S_sw > 1 and S_dn > 1 and S_up > 1, (S_sw, S_dn, S_up)
+    # expert FFN on generator bank rows
+    bank = u16(gen.payload_rows(len(bo["bank_src"]), L, 31))
+    wg, wu, wd = gen.rank_experts(cfg, rank)
+    rcv = share.Receiver(d, n)
+    rcv.bank.copy_(gc.dev(bank))
+    rcv.bank_src.copy_(torch.from_numpy(bo["bank_src"]))
+    rcv.bfill.copy_(torch.from_numpy(bo["bfill"]))
+    rcv.ret.fill_(1.5)
+    moe.moe_profile_reset()
+    moe.moe_profile_enable(True)
+    rcv.ffn(wg.cuda(), wu.cuda(), wd.cuda())
+    # combine of shard 0 over generator returned rows
+    s0 = senders[0]
+    returned = u16(gen.payload_rows(n, L, 33))
+    wlu = gen.latent_up(cfg)
+    wsg, wsu, wsd = gen.shared(cfg)
+    snd = share.Sender(d)
+    snd.topk.copy_(torch.from_numpy(s0["topk"]))
+    snd.slot.copy_(torch.from_numpy(s0["slot"]))
+    snd.gates.copy_(torch.from_numpy(s0["gates"]))
+    cmb = share.Combiner(d)
+    cmb.combine(gc.dev(returned), None, snd, s0["x"].cuda(), wlu.cuda(), wsg.cuda(), wsu.cuda(),
+                wsd.cuda())
+    moe.moe_profile_collect()
+    moe.moe_profile_enable(False)
+    prof = moe.moe_profile_read()
+    torch.cuda.synchronize()
+    assert "gemm_up_shared_tail" in prof
+    ro = dense.expert_ffn(d_orc, bank, None, bo["bank_src"], bo["bfill"], u16(wg), u16(wu),
+                          u16(wd), n)
+    rg = gc.host(rcv.ret)
+    kept = np.zeros(n, bool)
+    kept[bo["bank_src"][bo["bank_src"] >= 0]] = True
+    assert (rg[~kept] == 0).all()
+    gc.assert_rows_close(rg[kept], ro[kept], "ret")
+    yo, oo = dense.combine_tokens(d_orc, returned, None, s0["topk"], s0["slot"], s0["gates"],
+                                  u16(s0["x"]), u16(wlu), u16(wsg), u16(wsu), u16(wsd))
+    gc.assert_rows_close(gc.host(cmb.ylat), yo, "ylat")
+    gc.assert_rows_close(gc.host(cmb.out), oo, "out")
+    print(f"\n[split] expert SwiGLU {len(sw)} split M tiles x{S_sw}, down {len(dn)} x{S_dn}, "
+          f"up-projection {len(up)} x{S_up}: every row matches", flush=True)

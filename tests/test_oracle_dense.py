@@ -200,3 +200,79 @@ def test_combine_dropped_and_shared_only(orc):
     h = dense.shared_h(x, wsg, wsu)
     half = d.d_ff_shared // 2
     assert np.array_equal(out[:, :half], h[:, :half]) and (out[:, half:] == 0).all()
+
+
+# ----------------------------------------------------------------------------
+# backward: whole rows of the weight gradients against oracle.c's full backward
+# ----------------------------------------------------------------------------
+
+def _bwd_case(orc, seed):
+    rng = np.random.default_rng(seed)
+    d = _tiny_dims(orc, T=36, cap=(6, 9))
+    El = d.n_experts // d.n_ranks
+    topk = np.stack([rng.choice(d.n_experts, d.top_k, replace=False)
+                     for _ in range(d.T)]).astype(np.int32)
+    snd = orc.sender(d, topk)
+    gates = rng.random((d.T, d.top_k)).astype(np.float32)
+    n_rows = d.n_ranks * d.n_waves * d.cap_send
+    w = dict(
+        x=_rand_bits(rng, (d.T, d.d_model)), ylat=_rand_bits(rng, (d.T, d.latent)),
+        returned=_rand_bits(rng, (n_rows, d.latent)), d_out=_rand_bits(rng, (d.T, d.d_model)),
+        wlu=_rand_bits(rng, (d.d_model, d.latent), d.latent ** -0.5),
+        wld=_rand_bits(rng, (d.latent, d.d_model), d.d_model ** -0.5),
+        wsg=_rand_bits(rng, (d.n_shared, d.d_ff_shared, d.d_model), d.d_model ** -0.5),
+        wsu=_rand_bits(rng, (d.n_shared, d.d_ff_shared, d.d_model), d.d_model ** -0.5),
+        wsd=_rand_bits(rng, (d.n_shared, d.d_model, d.d_ff_shared), d.d_ff_shared ** -0.5),
+        wg=_rand_bits(rng, (El, d.d_ff, d.latent), d.latent ** -0.5),
+        wu=_rand_bits(rng, (El, d.d_ff, d.latent), d.latent ** -0.5),
+        wd=_rand_bits(rng, (El, d.latent, d.d_ff), d.d_ff ** -0.5),
+        d_pools=_rand_bits(rng, (n_rows, d.latent)),
+        d_shared=_rand_bits(rng, (d.T, 2, d.n_shared, d.d_ff_shared)),
+        d_ret=_rand_bits(rng, (n_rows, d.latent)))
+    return rng, d, topk, snd, gates, w
+
+
+def test_combine_wgrad_rows_match_c_oracle(orc):
+    rng, d, topk, snd, gates, w = _bwd_case(orc, 20)
+    _, _, _, dwlu, dwsd = orc.combine_backward(d, w["returned"], topk, snd["slot"], gates, w["x"],
+                                               w["ylat"], w["wlu"], w["wsg"], w["wsu"], w["wsd"],
+                                               w["d_out"])
+    rows = np.array([0, 5, d.d_model - 1])
+    _close_to_c(dense.outer_rows(f64(w["d_out"][:, rows]), f64(w["ylat"])), dwlu[rows])
+    for sh in range(d.n_shared):
+        f = np.array([0, 3, d.d_ff_shared - 1])
+        got = dense.shared_down_wgrad_cols(w["x"], w["wsg"], w["wsu"], w["d_out"], sh, f)
+        _close_to_c(got, dwsd[sh][:, f].T)
+
+
+def test_expert_wgrad_rows_match_c_oracle(orc):
+    rng, d, topk, snd, gates, w = _bwd_case(orc, 21)
+    El = d.n_experts // d.n_ranks
+    n_rows = d.n_ranks * d.n_waves * d.cap_send
+    hdr = np.where(rng.random(n_rows) < 0.8, 1 * El + rng.integers(0, El, n_rows), -1)
+    bo = orc.bank_slots(d, 1, hdr.astype(np.int32), None)
+    bank = _rand_bits(rng, (len(bo["bank_src"]), d.latent))
+    _, dwg, dwu, dwd = orc.expert_ffn_backward(d, bank, bo["bank_src"], bo["bfill"], w["wg"],
+                                               w["wu"], w["wd"], w["d_ret"])
+    f = np.array([0, 7, d.d_ff - 1])
+    for j in range(El):
+        pos = np.concatenate([np.arange(g * d.cap_recv, g * d.cap_recv + bo["bfill"][g])
+                              for g in range(j, d.n_waves * El, El)])
+        u, dy = bank[pos], w["d_ret"][bo["bank_src"][pos]]
+        g, up, dn = dense.expert_wgrad_rows(u, dy, w["wg"][j], w["wu"][j], w["wd"][j], f)
+        _close_to_c(g, dwg[j][f])
+        _close_to_c(up, dwu[j][f])
+        _close_to_c(dn, dwd[j][:, f].T)
+
+
+def test_pack_wgrad_rows_match_c_oracle(orc):
+    rng, d, topk, snd, gates, w = _bwd_case(orc, 22)
+    dz, _, dwld, dwsg, dwsu = orc.pack_backward(d, w["d_pools"], topk, snd["slot"], w["x"],
+                                                w["d_shared"], w["wld"], w["wsg"], w["wsu"])
+    assert np.array_equal(dense.pack_dz(d, w["d_pools"], topk, snd["slot"]), dz)
+    rows = np.array([0, 9, d.latent - 1])
+    _close_to_c(dense.outer_rows(f64(dz[:, rows]), f64(w["x"])), dwld[rows])
+    for sh in range(d.n_shared):
+        f = np.array([1, d.d_ff_shared - 1])
+        _close_to_c(dense.outer_rows(f64(w["d_shared"][:, 0, sh, f]), f64(w["x"])), dwsg[sh][f])
+        _close_to_c(dense.outer_rows(f64(w["d_shared"][:, 1, sh, f]), f64(w["x"])), dwsu[sh][f])

@@ -45,6 +45,16 @@ def test_generator_deterministic_and_normal():
     assert not torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
+def test_generator_rows_equal_whole_tensor():
+    """hidden_rows (rows generated alone, used to feed the oracle's checks of
+    full-size outputs) equals the rows of the whole generated tensor."""
+    for cfg in (configs.TINY, configs.scaled(configs.TINY, "w6144", T=40, d_model=6144)):
+        full = gen.hidden(cfg, 5)
+        rows = [cfg.T - 1, 0, 7, 7, cfg.T // 2]
+        assert torch.equal(gen.hidden_rows(cfg, 5, rows).view(torch.int16),
+                           full[rows].view(torch.int16))
+
+
 def test_workload_constants_match_pages():
     g = json.load(open(os.path.join(GOLDEN, "constants.json")))
     c = configs.SHARE_4K
