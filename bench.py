@@ -10,6 +10,14 @@ run the six local experts, and combine (identity return loopback).  Bank +
 expert FFN and the shared experts run on two more streams beside route +
 pack (no data dependence between them); the combine waits for all three.
 
+The line's value is the 4096-token shard at rank 0 (mean over the K timed
+steps; the median and the spread are in step_ms).  Beside it: the dominant
+kernel's roofline, the oracle's rate on the host, the same steps after a
+1 GiB cache sweep each (cold_cache), the backward of the share, and the
+forward figures of three more workloads (the 65536-token long-context shard
+at rank 0, and the most-loaded rank of the Zipf-skewed 16384-token shard and
+of its dropless form).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--rank R|hot]
 Prints one JSON line.
 """
@@ -24,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "routed tokens/s through MoE layer on 1 MI355X; % HBM/MFMA roofline; drop %"
 
 
 def log(*a):
@@ -460,6 +469,122 @@ def run_cpu_baseline(st, rows=(64, 160, 32)):
     return cfg.T / est, desc
 
 
+def setup_rank(cfg, which, progress=False):
+    """Setup for rank `which`: an int, or "hot" -- the rank with the most kept
+    received rows, found from a first pass over every shard."""
+    import torch
+    if which != "hot":
+        return setup(cfg, int(which), progress=progress)
+    st = setup(cfg, 0, progress=progress)
+    rank = receiver_stats(st)[1]
+    if rank == 0:
+        return st
+    log(f"bench: {cfg.name}: hottest rank is {rank}: setup again")
+    del st
+    torch.cuda.empty_cache()
+    return setup(cfg, rank, progress=progress)
+
+
+def time_steps(st, stepfn, steps):
+    """(mean ms per step over the whole timed region, [ms of each step]):
+    events on the main stream, which every step's other streams join before
+    its combine, so consecutive events bracket exactly one step."""
+    import torch
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(steps):
+        stepfn(st)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]) / steps, per
+
+
+def step_stats(per):
+    s = sorted(per)
+    n = len(s)
+    med = s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+    return {"mean": round(sum(s) / n, 4), "median": round(med, 4), "min": round(s[0], 4),
+            "max": round(s[-1], 4)}
+
+
+def kernel_pass(st, steps):
+    """Per-kernel durations: the library brackets each launch with hipEvents.
+    The calls go on one stream, so that each kernel runs alone (in the
+    three-stream step a kernel's duration depends on what it happens to
+    share the GPU with)."""
+    import dispatch_softmax_top_amd as moe
+    moe.moe_profile_reset()
+    moe.moe_profile_enable(True)
+    for _ in range(steps):
+        step_serial(st)
+    moe.moe_profile_collect()
+    moe.moe_profile_enable(False)
+    work = algorithmic_work(st)
+    # A GEMM whose last round was split along K finishes in a second kernel
+    # (<name>_tail: sum of the partial tiles and the epilogue); its rate is
+    # taken over both launches.
+    kernels, per_step = kernel_table(moe.moe_profile_read(), work, steps)
+    return kernels, per_step, work
+
+
+def gemm_frac(kernels, name):
+    k = kernels.get(name, {})
+    return k.get("mfma_frac")
+
+
+def drop_stats(st):
+    cfg, d = st.cfg, st.d
+    kept_r, dem_r = int(st.rcv.bfill.sum()), int(st.rcv.bdemand.sum())
+    return {
+        "sender_pct_own_shard": round(100.0 * int((st.snd.slot < 0).sum()) / (d.T * d.top_k), 3),
+        "sender_pct_all_shards": round(100.0 * st.sent_dropped / (cfg.n_shards * d.T * d.top_k), 3),
+        "pool_rows_sent_per_shard": round(st.sent_fill / cfg.n_shards, 1),
+        "receiver_pct_rank": round(100.0 * (dem_r - kept_r) / max(dem_r, 1), 3),
+        "receiver_pct_all_ranks": round(receiver_stats(st)[0], 3),
+        "bad_rows": int(st.rcv.bad_rows[0]),
+    }
+
+
+# The other workloads of the line: the 65536-token long-context shard at rank
+# 0, and the most-loaded rank of the Zipf-skewed 16384-token shard and of its
+# dropless (ragged) form.
+OTHER_WORKLOADS = ((3, "0"), (2, "hot"), (4, "hot"))
+
+
+def workload_summary(cfg, which, steps, warmup):
+    """Forward figures of one more workload: step time (mean, median, cold
+    caches), routed tokens/s, path roofline, the expert GEMMs' MFMA fractions
+    and the drop rates."""
+    import torch
+    t0 = time.time()
+    st = setup_rank(cfg, which)
+    for _ in range(warmup):
+        step(st)
+    ms, per = time_steps(st, step, steps)
+    kernels, per_step, work = kernel_pass(st, steps)
+    cold = cold_steps(st, steps)
+    out = {
+        "workload": cfg.name, "rank": st.rank, "rank_choice": which, "T": st.d.T,
+        "cap_send": st.d.cap_send, "cap_recv": st.d.cap_recv, "steps": steps,
+        "ms_per_step": round(ms, 4), "step_ms": step_stats(per),
+        "tokens_per_s": round(st.d.T / (ms * 1e-3), 1),
+        "cold_cache_ms_per_step": round(cold, 4),
+        "path_roofline": path_roofline(kernels, work, ms),
+        "gemm_expert_swiglu_mfma_frac": gemm_frac(kernels, "gemm_expert_swiglu"),
+        "gemm_expert_down_mfma_frac": gemm_frac(kernels, "gemm_expert_down"),
+        "kept_rows_at_rank": int(st.rcv.bfill.sum()),
+        "drops": drop_stats(st),
+        "wall_s": round(time.time() - t0, 1),
+    }
+    del st
+    torch.cuda.empty_cache()
+    log(f"bench: {cfg.name} rank {out['rank']}: {ms:.3f} ms/step")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -470,8 +595,11 @@ def main():
                     help="rank to measure, or 'hot': the rank with the most kept received rows")
     ap.add_argument("--serial", action="store_true",
                     help="issue the step's calls on one stream (each kernel alone)")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time steps that each follow a 1 GiB write sweep (cold caches)")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the steps timed after a 1 GiB write sweep each (cold caches)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads' forward figures (65536 tokens at rank 0, "
+                         "the Zipf 16384-token hot rank, its dropless hot rank)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward measurement (fixed capacities only)")
@@ -513,67 +641,28 @@ def main():
     if args.waves != cfg.waves or args.dedup:
         import dataclasses
         cfg = dataclasses.replace(cfg, waves=args.waves, dedup=args.dedup or cfg.dedup)
-    rank = 0 if args.rank == "hot" else int(args.rank)
     log(f"bench: {cfg.name} rank {args.rank}: setup")
-    st = setup(cfg, rank, progress=True)
-    if args.rank == "hot":
-        rank = receiver_stats(st)[1]
-        if rank != 0:
-            log(f"bench: hottest rank is {rank}: setup again")
-            del st
-            st = setup(cfg, rank, progress=True)
+    st = setup_rank(cfg, args.rank, progress=True)
+    rank = st.rank
     if args.balance_alpha is not None:
         from dispatch_softmax_top_amd import share
         st.bal = share.Balancer(cfg.n_experts, args.balance_window, args.balance_alpha)
     stepfn = step_serial if args.serial else step
-    stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
         stepfn(st)
     torch.cuda.synchronize()
     log("bench: warmup done")
 
     # timed region: K steps, events on the stream the kernels run on
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        stepfn(st)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms, per = time_steps(st, stepfn, args.steps)
     log(f"bench: {args.steps} steps, {ms:.3f} ms/step")
-
-    # per-kernel durations: the library brackets each launch with hipEvents.
-    # This pass issues the calls on one stream, so that each kernel runs alone
-    # (in the three-stream step a kernel's duration depends on what it
-    # happens to share the GPU with).
-    moe.moe_profile_reset()
-    moe.moe_profile_enable(True)
-    for _ in range(args.steps):
-        step_serial(st)
-    moe.moe_profile_collect()
-    moe.moe_profile_enable(False)
-    prof = moe.moe_profile_read()
-    work = algorithmic_work(st)
-    # A GEMM whose last round was split along K finishes in a second kernel
-    # (<name>_tail: sum of the partial tiles and the epilogue); its rate is
-    # taken over both launches.
-    kernels, per_step = kernel_table(prof, work, args.steps)
+    kernels, per_step, work = kernel_pass(st, args.steps)
     dom = "gemm_expert_swiglu"
     dom_avg_s = (per_step[dom] + per_step.get(dom + "_tail", 0.0)) * 1e-3
     achieved = work[dom][1] / dom_avg_s / 1e12
-
     d = st.d
-    kept_s, dem_s = int(st.snd.fill.sum()), int(st.snd.demand.sum())
-    kept_r, dem_r = int(st.rcv.bfill.sum()), int(st.rcv.bdemand.sum())
-    drops = {
-        "sender_pct_own_shard": round(100.0 * int((st.snd.slot < 0).sum()) / (d.T * d.top_k), 3),
-        "sender_pct_all_shards": round(100.0 * st.sent_dropped / (cfg.n_shards * d.T * d.top_k), 3),
-        "pool_rows_sent_per_shard": round(st.sent_fill / cfg.n_shards, 1),
-        "receiver_pct_rank": round(100.0 * (dem_r - kept_r) / max(dem_r, 1), 3),
-        "receiver_pct_all_ranks": round(receiver_stats(st)[0], 3),
-        "bad_rows": int(st.rcv.bad_rows[0]),
-    }
+    kept_r = int(st.rcv.bfill.sum())
+    drops = drop_stats(st)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -590,21 +679,30 @@ def main():
         backward["train_tokens_per_s"] = round(d.T / ((ms + backward["ms_per_step"]) * 1e-3), 1)
 
     cold = None
-    if args.cold:
+    if not args.no_cold:
         cms = cold_steps(st, args.steps, stepfn)
         cold = {"ms_per_step": round(cms, 4), "tokens_per_s": round(d.T / (cms * 1e-3), 1),
                 "flush_bytes": 1 << 30}
         log(f"bench: cold-cache {cms:.3f} ms/step")
 
+    workloads = None
+    if not args.no_workloads and args.balance_alpha is None and not args.dedup \
+            and args.waves == "tokens":
+        del st      # every figure of the main workload is taken above
+        torch.cuda.empty_cache()
+        workloads = [workload_summary(configs.WORKLOADS[c], w, min(args.steps, 10), 2)
+                     for c, w in OTHER_WORKLOADS if (c, w) != (args.config, args.rank)]
+
     tok_s = d.T / (ms * 1e-3)
     line = {
-        "metric": "routed tokens/s through the MoE layer share on 1 MI355X",
+        "metric": METRIC,
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": step_stats(per),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -616,7 +714,7 @@ def main():
                    "n_shared": d.n_shared, "cap_send": d.cap_send, "cap_recv": d.cap_recv,
                    "source_shards": cfg.n_shards, "streams": 1 if args.serial else 3,
                    "waves": cfg.waves, "dedup": bool(d.dedup),
-                   "balance": None if st.bal is None else
+                   "balance": None if args.balance_alpha is None else
                    {"alpha": args.balance_alpha, "window": args.balance_window}},
         "roofline": {"kernel": dom, "bound": "mfma", "measured": "per-kernel pass after the "
                      "timed steps, calls on one stream (each kernel alone); duration of the "
@@ -633,6 +731,7 @@ def main():
         "backward": backward,
         "drops": drops,
         "kernels": kernels,
+        "workloads": workloads,
     }
     print(json.dumps(line), flush=True)
 

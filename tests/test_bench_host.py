@@ -1,5 +1,6 @@
 """Host-side logic of bench.py: path roofline sum and receiver statistics
 (small hand-made inputs; no GPU)."""
+import os
 import types
 
 import pytest
@@ -40,3 +41,17 @@ def test_receiver_stats_ragged_keeps_everything():
     st = _st([1, 2, 30, 4], cap_recv=0, R=2)
     pct, hot = bench.receiver_stats(st)
     assert pct == 0.0 and hot == 1
+
+
+def test_step_stats_median_and_mean():
+    s = bench.step_stats([3.0, 1.0, 2.0, 10.0])
+    assert s["median"] == pytest.approx(2.5) and s["mean"] == pytest.approx(4.0)
+    assert s["min"] == 1.0 and s["max"] == 10.0
+    assert bench.step_stats([5.0, 1.0, 2.0])["median"] == 2.0
+
+
+def test_metric_is_the_named_one():
+    import json
+    base = json.load(open(os.path.join(os.path.dirname(os.path.dirname(__file__)),
+                                       "BASELINE.json")))
+    assert bench.METRIC == base["metric"]
