@@ -42,11 +42,16 @@ _lib = None
 
 
 def lib():
+    """The loaded oracle.  ORACLE_LIB names another build of oracle.c to load
+    instead (the sanitizer build of tests/test_oracle_sanitized.py)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        L = ctypes.CDLL(path)
         dp = ctypes.POINTER(Dims)
         vp = ctypes.c_void_p
         i32, i64 = ctypes.c_int32, ctypes.c_int64
