@@ -5,12 +5,14 @@
 // section 四: every token is routed to 8 of 384 experts.
 //
 // One wave64 per token.  Lane l holds logits l, l+64, l+128, ... .  The
-// choice order is (logit descending, index ascending): each candidate is
-// encoded as a 64-bit key (order-preserving image of the fp32 value, then
-// the complement of the index) so one unsigned max picks the next expert.
-// Each lane keeps its candidates sorted; k rounds of a wave-wide max take
-// the head of the winning lane.  Gates are exp(l - max) / sum exp(l - max)
-// over all E logits, in fp32.
+// choice order is (logit descending, index ascending).  Each candidate's
+// order-preserving 32-bit image of its fp32 logit is its key; each lane keeps
+// its candidates sorted by (key descending, index ascending).  k rounds take
+// the wave-wide largest head (DPP maxima inside 16-lane rows, then two row
+// broadcasts); if several lanes hold that key (equal logits), a second
+// reduction takes the lowest index among them.  The winner's lane pops its
+// head.  The first choice is the largest logit m; gates are exp(l - m) /
+// sum exp(l - m) over all E logits, in fp32 (exp by the hardware exp2).
 //
 // Quantile balancing ("从玩具到前沿:训练一个真正的大模型,到底难在哪里",
 // section 四 and appendix A.2): a per-expert bias is added to the logits
@@ -34,44 +36,34 @@ __device__ __forceinline__ float unord_f32(uint32_t o) {
   return __uint_as_float(u);
 }
 
-// v from the lane DPP control CTRL selects (both halves).
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-  const uint32_t hi =
-      (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
+// Reductions over the wave that every lane gets: DPP inside each 16-lane row
+// (swaps within quads, then rotations by 4 and 8), then the row broadcasts of
+// lanes 15 and 31 fold rows 0-2 into row 3, and lane 63 is read.  The order
+// of the operations is fixed, so a sum is the same on every call.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+  // row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3 (other rows keep v)
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Maximum over the wave, returned wave-uniform.  Inside each row of 16 lanes
-// by DPP moves (swaps within quads, then rotations by 4 and 8), then across
-// the four rows by reading one lane of each: no LDS round trips, which the
-// k dependent rounds of the choice loop would otherwise wait on.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  uint64_t o;
-  o = dpp_u64<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = o > v ? o : v;
-  o = dpp_u64<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = o > v ? o : v;
-  o = dpp_u64<0x124>(v);  // row_ror:4
-  v = o > v ? o : v;
-  o = dpp_u64<0x128>(v);  // row_ror:8
-  v = o > v ? o : v;
-  uint64_t r = readlane_u64(v, 0);
-#pragma unroll
-  for (int l = 16; l < 64; l += 16) {
-    const uint64_t x = readlane_u64(v, l);
-    r = x > r ? x : r;
-  }
-  return r;
-}
-
+// One wave per token.
 // bias: NULL, or [E] fp32 added to every token's logits (one fp32 rounding).
 // renorm: gates divided by their sum over the k chosen.
 template <int VPL>
@@ -85,59 +77,71 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
   const int lane = lane_id();
   const float *l = logits + (int64_t)t * E;
 
+  // candidates of this lane: order-preserving image of the fp32 logit and
+  // the expert index, sorted by (image descending, index ascending)
   float v[VPL];
-  uint64_t key[VPL];
-  float m = -INFINITY;
+  uint32_t key[VPL];
+  int idx[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    int e = lane + 64 * i;
+    const int e = lane + 64 * i;
     v[i] = e < E ? (bias ? l[e] + bias[e] : l[e]) : -INFINITY;
-    m = fmaxf(m, v[i]);
-    key[i] = e < E ? (((uint64_t)ord_f32(v[i]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e)) : 0ull;
+    key[i] = e < E ? ord_f32(v[i]) : 0u;
+    idx[i] = e;
   }
-  m = wave_max_f32(m);
+#pragma unroll
+  for (int i = 1; i < VPL; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j) {  // stable: equal images keep index order
+      const bool sw = key[j] > key[j - 1];
+      const uint32_t ka = key[j - 1], kb = key[j];
+      const int ia = idx[j - 1], ib = idx[j];
+      key[j - 1] = sw ? kb : ka;
+      key[j] = sw ? ka : kb;
+      idx[j - 1] = sw ? ib : ia;
+      idx[j] = sw ? ia : ib;
+    }
+
+  // k rounds: the largest head is the next choice (equal images: the lowest
+  // index among the lanes holding it), and its owner pops its head.  Round
+  // 0's choice carries the largest logit m of the softmax.
+  int my_idx = 0;
+  float my_logit = 0.f, m = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t best = wave_max_u32(key[0]);
+    const uint64_t holders = ballot(key[0] == best);
+    int e;
+    if (__popcll(holders) == 1)
+      e = __builtin_amdgcn_readlane(idx[0], (int)__builtin_ctzll(holders));
+    else
+      e = (int)wave_min_u32(key[0] == best ? (uint32_t)idx[0] : 0xffffffffu);
+    if ((e & 63) == lane) {  // owner pops its head
+#pragma unroll
+      for (int i = 0; i + 1 < VPL; ++i) {
+        key[i] = key[i + 1];
+        idx[i] = idx[i + 1];
+      }
+      key[VPL - 1] = 0u;
+    }
+    const float lg = unord_f32(best);
+    if (j == 0) m = lg;
+    if (lane == j) {
+      my_idx = e;
+      my_logit = lg;
+    }
+  }
+  // softmax denominator over all E logits, then the gates of the k chosen
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) s += (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
-  s = wave_sum_f32(s);
-
-  // sort this lane's keys, largest first (insertion sort, unrolled)
-#pragma unroll
-  for (int i = 1; i < VPL; ++i) {
-#pragma unroll
-    for (int j = i; j > 0; --j) {
-      uint64_t a = key[j - 1], b = key[j];
-      key[j - 1] = a > b ? a : b;
-      key[j] = a > b ? b : a;
-    }
-  }
-
-  int my_idx = 0;
-  float my_gate = 0.f, my_logit = 0.f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = wave_max_u64(key[0]);
-    uint32_t e = 0xffffffffu - (uint32_t)best;
-    if ((int)(e & 63u) == lane) {  // owner pops its head
-#pragma unroll
-      for (int i = 0; i + 1 < VPL; ++i) key[i] = key[i + 1];
-      key[VPL - 1] = 0ull;
-    }
-    if (lane == j) {
-      my_idx = (int)e;
-      my_logit = unord_f32((uint32_t)(best >> 32));
-      my_gate = expf(my_logit - m) / s;
-    }
-  }
-  if (renorm) {
-    // the k chosen probabilities over their sum: the softmax over the chosen
-    // logits, from exp(l - the first choice's logit), in fp32
-    const float top = __shfl(my_logit, 0);
-    const float ej = lane < k ? expf(my_logit - top) : 0.f;
-    my_gate = ej / wave_sum_f32(ej);
-  }
+  for (int i = 0; i < VPL; ++i) s += (lane + 64 * i < E) ? __expf(v[i] - m) : 0.f;
+  s = wave_sum_dpp(s);
+  const float ej = __expf(my_logit - m);
+  // renorm: the k chosen probabilities over their sum, i.e. the softmax over
+  // the chosen logits, from exp(l - the first choice's logit), in fp32
+  const float g = renorm ? ej / wave_sum_dpp(lane < k ? ej : 0.f) : ej / s;
   if (lane < k) {
     topk[(int64_t)t * k + lane] = my_idx;
-    gates[(int64_t)t * k + lane] = my_gate;
+    gates[(int64_t)t * k + lane] = g;
   }
 }
 
