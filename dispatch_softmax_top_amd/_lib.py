@@ -63,9 +63,10 @@ _SIGS = {
     "moe_combine_shared": (ctypes.c_int, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                           _VP, _I64, _VP]),
     "moe_route_backward": (ctypes.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
-    "moe_combine_backward": (ctypes.c_int, [_DP] + [_VP] * 18 + [_I64, _VP]),
-    "moe_expert_ffn_backward": (ctypes.c_int, [_DP] + [_VP] * 12 + [_I64, _VP]),
-    "moe_pack_backward": (ctypes.c_int, [_DP] + [_VP] * 14 + [_I64, _VP]),
+    "moe_combine_backward": (ctypes.c_int, [_DP, _VP, _VP, _I64] + [_VP] * 17 + [_I64, _VP]),
+    "moe_expert_ffn_backward": (ctypes.c_int, [_DP, _VP, _VP, _I64] + [_VP] * 6 +
+                                [_I64] + [_VP] * 5 + [_I64, _VP]),
+    "moe_pack_backward": (ctypes.c_int, [_DP] + [_VP] * 15 + [_I64, _VP]),
     "moe_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_profile_collect": (ctypes.c_int, []),
     "moe_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.c_char_p, ctypes.c_int,
@@ -223,29 +224,31 @@ def moe_route_backward(logits, topk, d_gates, d_logits, bias=None, stream=None, 
 
 def moe_combine_backward(d, returned, topk, slot, gates, fill, x, ylat, w_lat_up, ws_gate, ws_up,
                          ws_down, d_out, d_returned, d_gates, d_shared, dw_lat_up, dws_down, ws,
-                         stream=None):
+                         stream=None, ret_offsets=None):
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().moe_combine_backward(
-        ctypes.byref(d), _p(returned), _p(topk), _p(slot), _p(gates), _p(fill), _p(x), _p(ylat),
+        ctypes.byref(d), _p(returned), _p(ret_offsets), returned.shape[0], _p(topk), _p(slot),
+        _p(gates), _p(fill), _p(x), _p(ylat),
         _p(w_lat_up), _p(ws_gate), _p(ws_up), _p(ws_down), _p(d_out), _p(d_returned),
         _p(d_gates), _p(d_shared), _p(dw_lat_up), _p(dws_down), _p(ws), nbytes,
         _stream(stream)))
 
 
 def moe_expert_ffn_backward(d, bank, bank_src, bfill, w_gate, w_up, w_down, d_ret, d_recv,
-                            dw_gate, dw_up, dw_down, ws, stream=None):
+                            dw_gate, dw_up, dw_down, ws, stream=None, bank_offsets=None):
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().moe_expert_ffn_backward(
-        ctypes.byref(d), _p(bank), _p(bank_src), _p(bfill), _p(w_gate), _p(w_up), _p(w_down),
-        _p(d_ret), _p(d_recv), _p(dw_gate), _p(dw_up), _p(dw_down), _p(ws), nbytes,
-        _stream(stream)))
+        ctypes.byref(d), _p(bank), _p(bank_offsets), bank.shape[0], _p(bank_src), _p(bfill),
+        _p(w_gate), _p(w_up), _p(w_down), _p(d_ret), d_ret.shape[0], _p(d_recv), _p(dw_gate),
+        _p(dw_up), _p(dw_down), _p(ws), nbytes, _stream(stream)))
 
 
 def moe_pack_backward(d, d_pools, topk, slot, x, d_shared, w_lat_down, ws_gate, ws_up, dz, dx,
-                      dw_lat_down, dws_gate, dws_up, ws, stream=None):
+                      dw_lat_down, dws_gate, dws_up, ws, stream=None, pool_offsets=None):
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().moe_pack_backward(
-        ctypes.byref(d), _p(d_pools), _p(topk), _p(slot), _p(x), _p(d_shared), _p(w_lat_down),
+        ctypes.byref(d), _p(d_pools), _p(pool_offsets), _p(topk), _p(slot), _p(x), _p(d_shared),
+        _p(w_lat_down),
         _p(ws_gate), _p(ws_up), _p(dz), _p(dx), _p(dw_lat_down), _p(dws_gate), _p(dws_up),
         _p(ws), nbytes, _stream(stream)))
 

@@ -174,9 +174,9 @@ int64_t moe_workspace_bytes(const moe_dims *d, int call, int64_t n_rows) {
     case MOE_CALL_COMBINE_BWD:
     case MOE_CALL_FFN_BWD:
     case MOE_CALL_PACK_BWD:  // transposed operands, intermediates, split partial tiles
-      if (ragged(*d) || d->dedup)
-        return fail(MOE_ERR_UNSUPPORTED, "moe_workspace_bytes: backward needs fixed capacities, no dedup");
-      return bwd_ws_bytes(*d, call);
+      if (d->dedup) return fail(MOE_ERR_UNSUPPORTED, "moe_workspace_bytes: backward without dedup only");
+      if (n_rows < 0) return fail(MOE_ERR_INVALID, "moe_workspace_bytes: n_rows < 0");
+      return bwd_ws_bytes(*d, call, n_rows);
     default:
       return fail(MOE_ERR_INVALID, "moe_workspace_bytes: unknown call %d", call);
   }

@@ -1,4 +1,4 @@
-// backward.hip -- gradients of the branch (fixed capacities), for training:
+// backward.hip -- gradients of the branch (fixed capacities or ragged), for training:
 // "Marin 開始公開訓練 535B 參數 MoE 模型" (lamjinlab.com, zh-HK) describes a
 // model in open training; its pages give the forward pass, and every
 // gradient here follows from the forward definitions by the chain rule.
@@ -42,7 +42,9 @@ namespace moe {
 // (bfill != NULL): the filled bank positions of local expert b, wave after
 // wave, packed: k = (fills of the waves before w) + p is bank slot (wave w,
 // expert b, position p < bfill[w * El + b]); k past the expert's total fill
-// has no row.
+// has no row.  Ragged bank order (boff != NULL, one batch): every expert's
+// range in one row of out, expert b from the sum of kpack_len(rows of the
+// experts before b) on, and bank slot (w, b, p) at boff[w * El + b] + p.
 // ---------------------------------------------------------------------------
 
 struct TransposeArgs {
@@ -53,7 +55,30 @@ struct TransposeArgs {
   int rows, cols, kpad;
   const int32_t *bfill;
   int cap, El, W;
+  const int64_t *boff;
 };
+
+// Bank row of packed column k (ragged bank order), or -1.
+__device__ __forceinline__ int64_t tp_ragged_row(const TransposeArgs &a, int k) {
+  int64_t base = 0;
+  for (int b = 0; b < a.El; ++b) {
+    int rows = 0;
+    for (int w = 0; w < a.W; ++w) rows += a.bfill[w * a.El + b];
+    const int64_t len = kpack_len(rows);
+    if (k < base + len) {
+      int kk = (int)(k - base);
+      if (kk >= rows) return -1;
+      for (int w = 0; w < a.W; ++w) {
+        const int f = a.bfill[w * a.El + b];
+        if (kk < f) return a.boff[w * a.El + b] + kk;
+        kk -= f;
+      }
+      return -1;
+    }
+    base += len;
+  }
+  return -1;
+}
 
 constexpr int TP = 64;  // tile edge
 
@@ -88,7 +113,9 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeBatch tb) {
     u32x4 v = {0u, 0u, 0u, 0u};
     if (k < a.kpad && c < a.cols && k < a.rows) {
       int64_t row = k;
-      if (a.bfill) {
+      if (a.boff) {
+        row = tp_ragged_row(a, k);
+      } else if (a.bfill) {
         int base = 0, w = 0;
         for (; w < a.W; ++w) {
           const int f = a.bfill[w * a.El + b];
@@ -129,6 +156,7 @@ struct Tr {
   int rows, cols, kpad, nbatch;
   const int32_t *bfill;
   int cap, El, W;
+  const int64_t *boff;
 };
 
 static int transposes(const char *name, int n, const Tr *tr, hipStream_t s) {
@@ -140,8 +168,8 @@ static int transposes(const char *name, int n, const Tr *tr, hipStream_t s) {
     const Tr &q = tr[i];
     if (q.cols % 8 || q.kpad % 8 || q.ld_in % 8 || q.ld_out % 8 || q.bs_in % 8 || q.bs_out % 8)
       return fail(MOE_ERR_UNSUPPORTED, "%s: sizes must be multiples of 8", name);
-    tb.t[i] = TransposeArgs{q.in,   q.ld_in, q.bs_in, q.out,   q.ld_out, q.bs_out, q.rows,
-                            q.cols, q.kpad,  q.bfill, q.cap, q.El,     q.W};
+    tb.t[i] = TransposeArgs{q.in,   q.ld_in, q.bs_in, q.out, q.ld_out, q.bs_out, q.rows,
+                            q.cols, q.kpad,  q.bfill, q.cap, q.El,   q.W,      q.boff};
     tb.gk[i] = (int)cdiv(q.kpad, TP);
     tb.gc[i] = (int)cdiv(q.cols, TP);
     tb.first[i] = (int)total;
@@ -156,12 +184,16 @@ static int transposes(const char *name, int n, const Tr *tr, hipStream_t s) {
 // combine side: one wave per token.  For each kept choice j (pool row r):
 //   d_returned[r] = bf16(g[t,j] * d_ylat[t]),  d_gates[t,j] = returned[r] . d_ylat[t]
 // (fp32, lane partial sums then a wave sum); dropped choices get d_gates 0.
-// Extra blocks: one wave per pool row, zeroing rows past their pool's fill.
+// Ragged (offsets != NULL): pool row = offsets[seg] + slot, and a slot at or
+// past its segment's length has no row (d_gates 0).  Extra blocks: one wave
+// per returned row, zeroing rows past their pool's fill (the own shard's
+// slots of a pool are 0 .. fill - 1).
 // ---------------------------------------------------------------------------
 
 template <int CH>
 __global__ __launch_bounds__(256) void combine_backward_kernel(
-    const uint16_t *__restrict__ returned, const uint16_t *__restrict__ dy, int64_t ld_dy,
+    const uint16_t *__restrict__ returned, const int64_t *__restrict__ offsets, int n_seg,
+    const uint16_t *__restrict__ dy, int64_t ld_dy,
     const int32_t *__restrict__ topk, const int32_t *__restrict__ slot,
     const float *__restrict__ gates, const int32_t *__restrict__ fill,
     uint16_t *__restrict__ d_returned, float *__restrict__ d_gates, int T, int k, int L, int El,
@@ -171,7 +203,20 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
   if ((int)blockIdx.x >= token_blocks) {
     const int64_t idx = (int64_t)(blockIdx.x - token_blocks) * 4 + (threadIdx.x >> 6);
     if (idx >= n_slots) return;
-    const int p = (int)(idx / cap), i = (int)(idx - (int64_t)p * cap);
+    int p, i;
+    if (offsets) {  // last segment starting at or before idx
+      int lo = 0, hi = n_seg - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offsets[mid] <= idx) lo = mid;
+        else hi = mid - 1;
+      }
+      p = lo;
+      i = (int)(idx - offsets[p]);
+    } else {
+      p = (int)(idx / cap);
+      i = (int)(idx - (int64_t)p * cap);
+    }
     if (i < fill[p]) return;
     u32x4 *o = reinterpret_cast<u32x4 *>(d_returned + idx * L);
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -187,7 +232,9 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
     const int e = topk[(int64_t)t * k + lane];
     const float g = gates[(int64_t)t * k + lane];
     if (s >= 0) {
-      my_row = (int64_t)((e / El) * Wk + t / Tw) * pool_rows + s;
+      const int seg = (e / El) * Wk + t / Tw;
+      if (!offsets) my_row = (int64_t)seg * pool_rows + s;
+      else if (s < offsets[seg + 1] - offsets[seg]) my_row = offsets[seg] + s;
       my_g = g;
     }
   }
@@ -314,11 +361,23 @@ struct FfnBwdWs {
   int32_t *iota, *flags;
   float *part;
 };
-static int64_t ffn_bwd_ws(const moe_dims &d, char *base, FfnBwdWs &w) {
+// Bank rows and receive rows of the expert backward: fixed mode from the
+// capacities; ragged mode n_rows both (the bank holds every received row).
+static int64_t ffn_bwd_bank_rows(const moe_dims &d, int64_t n_rows) {
+  return ragged(d) ? n_rows : (int64_t)d.n_waves * experts_per_rank(d) * d.cap_recv;
+}
+// K extent of the bank-order transposes: fixed, every expert's own block of
+// pad32(W * cap_recv) columns; ragged, one row holding every expert's packed
+// range (kpack_len of its rows), at most this many columns.
+static int64_t ffn_bwd_kcols(const moe_dims &d, int64_t nb) {
+  if (!ragged(d)) return pad32((int64_t)d.n_waves * d.cap_recv);
+  return pad32(nb + (int64_t)experts_per_rank(d) * (256 + 32));
+}
+static int64_t ffn_bwd_ws(const moe_dims &d, int64_t n_rows, char *base, FfnBwdWs &w) {
   const int64_t El = experts_per_rank(d), L = d.latent, F = d.d_ff;
-  const int64_t nb = (int64_t)d.n_waves * El * d.cap_recv;
-  const int64_t nr = (int64_t)d.n_ranks * d.n_waves * d.cap_send;
-  const int64_t Kp = pad32((int64_t)d.n_waves * d.cap_recv);
+  const int64_t nb = ffn_bwd_bank_rows(d, n_rows);
+  const int64_t nr = ragged(d) ? n_rows : (int64_t)d.n_ranks * d.n_waves * d.cap_send;
+  const int64_t Kp = ffn_bwd_kcols(d, nb), blocks = ragged(d) ? 1 : El;
   Carve c{base};
   w.WdT = c.take<uint16_t>(El * F * L);
   w.WguT = c.take<uint16_t>(El * L * 2 * F);
@@ -326,10 +385,10 @@ static int64_t ffn_bwd_ws(const moe_dims &d, char *base, FfnBwdWs &w) {
   w.dH = c.take<uint16_t>(nb * F);
   w.Hb = c.take<uint16_t>(nb * F);
   w.dAB = c.take<uint16_t>(nb * 2 * F);
-  w.dYT = c.take<uint16_t>(El * L * Kp);
-  w.HT = c.take<uint16_t>(El * F * Kp);
-  w.dABT = c.take<uint16_t>(El * 2 * F * Kp);
-  w.UT = c.take<uint16_t>(El * L * Kp);
+  w.dYT = c.take<uint16_t>(blocks * L * Kp);
+  w.HT = c.take<uint16_t>(blocks * F * Kp);
+  w.dABT = c.take<uint16_t>(blocks * 2 * F * Kp);
+  w.UT = c.take<uint16_t>(blocks * L * Kp);
   w.iota = c.take<int32_t>(nb);
   w.flags = c.take<int32_t>(nr);
   w.part = c.take<float>(gemm_split_bytes() / 4);
@@ -353,26 +412,25 @@ static int64_t pack_bwd_ws(const moe_dims &d, char *base, PackBwdWs &w) {
   return c.off;
 }
 
-int64_t bwd_ws_bytes(const moe_dims &d, int call) {
+int64_t bwd_ws_bytes(const moe_dims &d, int call, int64_t n_rows) {
   if (call == MOE_CALL_COMBINE_BWD) {
     CombineBwdWs w;
     return combine_bwd_ws(d, nullptr, w);
   }
   if (call == MOE_CALL_FFN_BWD) {
     FfnBwdWs w;
-    return ffn_bwd_ws(d, nullptr, w);
+    return ffn_bwd_ws(d, n_rows, nullptr, w);
   }
   PackBwdWs w;
   return pack_bwd_ws(d, nullptr, w);
 }
 
 static int check_bwd(const moe_dims *d, int call, const char *name, const void *ws,
-                     int64_t ws_bytes) {
+                     int64_t ws_bytes, int64_t n_rows = 0) {
   MOE_TRY(check_dims(d));
-  if (ragged(*d) || d->dedup)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: fixed capacities only, no dedup", name);
+  if (d->dedup) return fail(MOE_ERR_UNSUPPORTED, "%s: no dedup", name);
   MOE_TRY(check_ptr(ws, "ws"));
-  const int64_t need = bwd_ws_bytes(*d, call);
+  const int64_t need = bwd_ws_bytes(*d, call, n_rows);
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace %lld < %lld bytes", name, (long long)ws_bytes,
                 (long long)need);
@@ -384,6 +442,7 @@ static int check_bwd(const moe_dims *d, int call, const char *name, const void *
 using namespace moe;
 
 extern "C" int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
+                                    const int64_t *ret_offsets, int64_t n_ret_rows,
                                     const int32_t *topk, const int32_t *slot, const float *gates,
                                     const int32_t *fill, const moe_bf16 *x, const moe_bf16 *ylat,
                                     const moe_bf16 *w_lat_up, const moe_bf16 *ws_gate,
@@ -406,6 +465,14 @@ extern "C" int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
     MOE_TRY(check_ptr(d_shared, "d_shared"));
     MOE_TRY(check_ptr(dws_down, "dws_down"));
   }
+  const bool rg = ragged(*d);
+  if (rg) {
+    MOE_TRY(check_ptr(ret_offsets, "ret_offsets (ragged mode)"));
+    if (n_ret_rows < 0 || n_ret_rows >= (1ll << 31))
+      return fail(MOE_ERR_INVALID, "moe_combine_backward: n_ret_rows out of range");
+  } else if (n_ret_rows != (int64_t)d->n_ranks * d->n_waves * d->cap_send) {
+    return fail(MOE_ERR_INVALID, "moe_combine_backward: fixed mode needs n_ret_rows == n_ranks*n_waves*cap_send");
+  }
   hipStream_t s = (hipStream_t)stream;
   const int T = d->T, L = d->latent, D = d->d_model, S = d->n_shared, Fs = d->d_ff_shared;
   const int SF = S * Fs, Tp = (int)pad32(T);
@@ -427,14 +494,15 @@ extern "C" int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
   // routed part: d_returned, d_gates
   const PoolKey pk = pool_key(*d);
   const int token_blocks = (int)cdiv(T, 4);
-  const int64_t n_slots = (int64_t)d->n_ranks * d->n_waves * d->cap_send;
+  const int64_t n_slots = n_ret_rows;
+  const int n_seg = d->n_ranks * d->n_waves;
   MOE_TRY(by_chunks(L, [&](auto chv) {
     constexpr int CH = decltype(chv)::value;
     return launch("combine_backward", combine_backward_kernel<CH>,
                   dim3((unsigned)(token_blocks + cdiv(n_slots, 4))), dim3(256), 0, s, returned,
-                  w.C1, (int64_t)(L + SF), topk, slot, gates, fill, d_returned, d_gates, T,
-                  d->top_k, L, experts_per_rank(*d), pk.Wk, pk.Tw, pk.rows, d->cap_send,
-                  token_blocks, n_slots);
+                  rg ? ret_offsets : nullptr, n_seg, w.C1, (int64_t)(L + SF), topk, slot, gates,
+                  fill, d_returned, d_gates, T, d->top_k, L, experts_per_rank(*d), pk.Wk, pk.Tw,
+                  pk.rows, d->cap_send, token_blocks, n_slots);
   }));
   // weight gradients, summed over tokens
   const Tr tra[3] = {{d_out, D, 0, w.doT, Tp, 0, T, D, Tp, 1},
@@ -452,28 +520,42 @@ extern "C" int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
 }
 
 extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
+                                       const int64_t *bank_offsets, int64_t n_bank_rows,
                                        const int32_t *bank_src, const int32_t *bfill,
                                        const moe_bf16 *w_gate, const moe_bf16 *w_up,
                                        const moe_bf16 *w_down, const moe_bf16 *d_ret,
-                                       moe_bf16 *d_recv, moe_bf16 *dw_gate, moe_bf16 *dw_up,
-                                       moe_bf16 *dw_down, void *ws, int64_t ws_bytes,
-                                       void *stream) {
+                                       int64_t n_ret_rows, moe_bf16 *d_recv, moe_bf16 *dw_gate,
+                                       moe_bf16 *dw_up, moe_bf16 *dw_down, void *ws,
+                                       int64_t ws_bytes, void *stream) {
   clear_error();
-  MOE_TRY(check_bwd(d, MOE_CALL_FFN_BWD, "moe_expert_ffn_backward", ws, ws_bytes));
+  MOE_TRY(check_dims(d));
+  const bool rg = ragged(*d);
+  const int El = experts_per_rank(*d), L = d->latent, F = d->d_ff, Cr = d->cap_recv;
+  if (rg) {
+    MOE_TRY(check_ptr(bank_offsets, "bank_offsets (ragged mode)"));
+    if (n_bank_rows < 0 || n_bank_rows >= (1ll << 31) || n_ret_rows != n_bank_rows)
+      return fail(MOE_ERR_INVALID, "moe_expert_ffn_backward: ragged mode needs n_ret_rows == n_bank_rows < 2^31");
+  } else {
+    if (n_bank_rows != (int64_t)d->n_waves * El * Cr ||
+        n_ret_rows != (int64_t)d->n_ranks * d->n_waves * d->cap_send)
+      return fail(MOE_ERR_INVALID, "moe_expert_ffn_backward: fixed mode needs n_bank_rows == n_waves*E_l*cap_recv and n_ret_rows == n_ranks*n_waves*cap_send");
+    if ((int64_t)d->n_waves * Cr >= (1ll << 30))
+      return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn_backward: bank rows >= 2^30");
+  }
+  MOE_TRY(check_bwd(d, MOE_CALL_FFN_BWD, "moe_expert_ffn_backward", ws, ws_bytes, n_bank_rows));
   const void *need[] = {bank, bank_src, bfill, w_gate, w_up, w_down, d_ret, d_recv, dw_gate,
                         dw_up, dw_down};
   const char *names[] = {"bank", "bank_src", "bfill", "w_gate", "w_up", "w_down", "d_ret",
                          "d_recv", "dw_gate", "dw_up", "dw_down"};
   for (int i = 0; i < 11; ++i) MOE_TRY(check_ptr(need[i], names[i]));
   hipStream_t s = (hipStream_t)stream;
-  const int El = experts_per_rank(*d), L = d->latent, F = d->d_ff, Cr = d->cap_recv;
-  const int64_t nb = (int64_t)d->n_waves * El * Cr;
-  const int64_t nr = (int64_t)d->n_ranks * d->n_waves * d->cap_send;
-  const int Kp = (int)pad32((int64_t)d->n_waves * Cr);
-  if (nb >= (1ll << 31) || nr >= (1ll << 31) || (int64_t)d->n_waves * Cr >= (1ll << 30))
-    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn_backward: bank or receive rows >= 2^31");
+  const int64_t nb = n_bank_rows, nr = n_ret_rows;
+  const int64_t Kp = ffn_bwd_kcols(*d, nb);
+  if (Kp >= (1ll << 31) - 256)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn_backward: bank rows too many");
+  const int64_t *boff = rg ? bank_offsets : nullptr;
   FfnBwdWs w;
-  ffn_bwd_ws(*d, (char *)ws, w);
+  ffn_bwd_ws(*d, nb, (char *)ws, w);
   const int64_t WL = (int64_t)F * L;
 
   // operands with K contiguous: W_d^T [El][F][L], [W_g^T | W_u^T] [El][L][2F]
@@ -489,54 +571,62 @@ extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
   }));
   MOE_TRY(launch("iota", iota_kernel, dim3((unsigned)cdiv(nb, 256)), dim3(256), 0, s, w.iota, nb));
   // d_h = dy . W_d (grouped, bank order)
-  MOE_TRY(gemm_grouped_nt("gemm_bwd_d_h", "gemm_bwd_d_h_tail", *d, w.dY, L, bfill, w.iota, nb,
-                          w.WdT, F, w.dH, nb,
-                          w.part, s));
+  MOE_TRY(gemm_grouped_nt("gemm_bwd_d_h", "gemm_bwd_d_h_tail", *d, w.dY, L, boff, bfill, w.iota,
+                          nb, w.WdT, F, w.dH, nb, w.part, s));
   // a, b recomputed; d_a | d_b and h
-  MOE_TRY(gemm_expert_swiglu_bwd(*d, bank, bfill, nb, w_gate, w_up, w.dH, w.Hb, w.dAB, w.part, s));
+  MOE_TRY(gemm_expert_swiglu_bwd(*d, bank, boff, bfill, nb, w_gate, w_up, w.dH, w.Hb, w.dAB,
+                                 w.part, s));
   // d_u = d_a . W_g + d_b . W_u, scattered to the receive rows; others zero
   MOE_TRY(ret_rows_mark(bank_src, nb, w.flags, nr, s));
-  MOE_TRY(gemm_grouped_nt("gemm_bwd_d_u", "gemm_bwd_d_u_tail", *d, w.dAB, 2 * F, bfill, bank_src,
-                          nb, w.WguT, L, d_recv,
-                          nr, w.part, s));
+  MOE_TRY(gemm_grouped_nt("gemm_bwd_d_u", "gemm_bwd_d_u_tail", *d, w.dAB, 2 * F, boff, bfill,
+                          bank_src, nb, w.WguT, L, d_recv, nr, w.part, s));
   MOE_TRY(ret_rows_zero_unmarked(w.flags, d_recv, L, nr, s));
-  // weight gradients: per local expert, summed over its rows of every wave
-  const int nw = d->n_waves * Cr;
+  // weight gradients: per local expert, summed over its rows of every wave.
+  // Fixed: expert e's rows packed into its own block of Kp columns; ragged:
+  // every expert's rows packed into one row of Kp columns, expert after expert.
   const int W = d->n_waves;
+  const int nw = rg ? (int)Kp : W * Cr;
+  const int nbatch = rg ? 1 : El;
   const Tr trb[4] = {
-      {w.dY, L, 0, w.dYT, Kp, (int64_t)L * Kp, nw, L, Kp, El, bfill, Cr, El, W},
-      {w.Hb, F, 0, w.HT, Kp, (int64_t)F * Kp, nw, F, Kp, El, bfill, Cr, El, W},
-      {w.dAB, 2 * F, 0, w.dABT, Kp, (int64_t)2 * F * Kp, nw, 2 * F, Kp, El, bfill, Cr, El, W},
-      {bank, L, 0, w.UT, Kp, (int64_t)L * Kp, nw, L, Kp, El, bfill, Cr, El, W}};
+      {w.dY, L, 0, w.dYT, Kp, (int64_t)L * Kp, nw, L, (int)Kp, nbatch, bfill, Cr, El, W, boff},
+      {w.Hb, F, 0, w.HT, Kp, (int64_t)F * Kp, nw, F, (int)Kp, nbatch, bfill, Cr, El, W, boff},
+      {w.dAB, 2 * F, 0, w.dABT, Kp, (int64_t)2 * F * Kp, nw, 2 * F, (int)Kp, nbatch, bfill, Cr, El,
+       W, boff},
+      {bank, L, 0, w.UT, Kp, (int64_t)L * Kp, nw, L, (int)Kp, nbatch, bfill, Cr, El, W, boff}};
   MOE_TRY(transposes("transpose_bank", 4, trb, s));
+  // expert e's operand blocks: its own (fixed), or the shared row (ragged)
+  const int64_t blk = rg ? 0 : 1;
   if (3 * El <= 18) {  // all three weights of every local expert in one launch
     NtProd pr[18];
     for (int e = 0; e < El; ++e) {
-      const uint16_t *ab = w.dABT + (int64_t)e * 2 * F * Kp, *ut = w.UT + (int64_t)e * L * Kp;
-      pr[3 * e] = NtProd{w.dYT + (int64_t)e * L * Kp, Kp, w.HT + (int64_t)e * F * Kp, Kp,
+      const uint16_t *ab = w.dABT + blk * e * 2 * F * Kp, *ut = w.UT + blk * e * L * Kp;
+      pr[3 * e] = NtProd{w.dYT + blk * e * L * Kp, Kp, w.HT + blk * e * F * Kp, Kp,
                          dw_down + e * WL, F, L, F, e};
       pr[3 * e + 1] = NtProd{ab, Kp, ut, Kp, dw_gate + e * WL, L, F, L, e};
       pr[3 * e + 2] = NtProd{ab + (int64_t)F * Kp, Kp, ut, Kp, dw_up + e * WL, L, F, L, e};
     }
     // each expert's K: its filled bank rows (the transposes packed them first)
-    return gemm_nt_multi("gemm_bwd_dw_experts", "gemm_bwd_dw_experts_tail", 3 * El, pr, Kp, w.part,
-                         s, bfill, d->n_waves, El);
+    return gemm_nt_multi("gemm_bwd_dw_experts", "gemm_bwd_dw_experts_tail", 3 * El, pr, (int)Kp,
+                         w.part, s, bfill, d->n_waves, El, rg);
   }
-  DenseSeg gd{w.dYT, Kp, w.HT, Kp, Kp};
+  if (rg)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn_backward: ragged mode needs E_l <= 6");
+  DenseSeg gd{w.dYT, Kp, w.HT, Kp, (int)Kp};
   MOE_TRY(gemm_nt_batched("gemm_bwd_dw_down", "gemm_bwd_dw_down_tail", L, F, gd, El,
                           (int64_t)L * Kp, (int64_t)F * Kp,
                           dw_down, F, WL, w.part, s));
-  DenseSeg gg{w.dABT, Kp, w.UT, Kp, Kp};
+  DenseSeg gg{w.dABT, Kp, w.UT, Kp, (int)Kp};
   MOE_TRY(gemm_nt_batched("gemm_bwd_dw_gate", "gemm_bwd_dw_gate_tail", F, L, gg, El,
                           (int64_t)2 * F * Kp, (int64_t)L * Kp,
                           dw_gate, L, WL, w.part, s));
-  DenseSeg gu{w.dABT + (int64_t)F * Kp, Kp, w.UT, Kp, Kp};
+  DenseSeg gu{w.dABT + (int64_t)F * Kp, Kp, w.UT, Kp, (int)Kp};
   return gemm_nt_batched("gemm_bwd_dw_up", "gemm_bwd_dw_up_tail", F, L, gu, El,
                          (int64_t)2 * F * Kp, (int64_t)L * Kp,
                          dw_up, L, WL, w.part, s);
 }
 
-extern "C" int moe_pack_backward(const moe_dims *d, const moe_bf16 *d_pools, const int32_t *topk,
+extern "C" int moe_pack_backward(const moe_dims *d, const moe_bf16 *d_pools,
+                                 const int64_t *pool_offsets, const int32_t *topk,
                                  const int32_t *slot, const moe_bf16 *x,
                                  const moe_bf16 *d_shared, const moe_bf16 *w_lat_down,
                                  const moe_bf16 *ws_gate, const moe_bf16 *ws_up, moe_bf16 *dz,
@@ -561,8 +651,12 @@ extern "C" int moe_pack_backward(const moe_dims *d, const moe_bf16 *d_pools, con
   PackBwdWs w;
   pack_bwd_ws(*d, (char *)ws, w);
 
-  // dz[t] = sum over kept choices of the pool-row gradients (the pack copy's adjoint)
-  MOE_TRY(combine_gather_rows(*d, d_pools, nullptr, topk, slot, nullptr, dz, s));
+  // dz[t] = sum over kept choices of the pool-row gradients (the pack copy's
+  // adjoint); ragged: segments at pool_offsets, a slot past its segment adds 0
+  const bool rg = ragged(*d);
+  if (rg) MOE_TRY(check_ptr(pool_offsets, "pool_offsets (ragged mode)"));
+  MOE_TRY(combine_gather_rows(*d, d_pools, rg ? pool_offsets : nullptr, topk, slot, nullptr, dz,
+                              s));
   // dx = dz . W_ld + d_a . W_sg + d_b . W_su, one product with one rounding
   DenseSeg gx[2] = {{dz, L, w.BldT, L, L}, {d_shared, 2 * SF, w.BsT, 2 * SF, 2 * SF}};
   const Tr trw[3] = {{w_lat_down, D, 0, w.BldT, L, 0, L, D, L, 1},

@@ -326,9 +326,11 @@ struct MultiArgs {
   // kfill != NULL: product p's K is the sum of kfill[w * kEl + kgroup[p]]
   // over w < kW (rounded up to whole K tiles, at least min(GSPLIT_MAX,
   // ktiles) so that every split part has one), at most ktiles; the operands
-  // hold zeros from there to ktiles
+  // hold zeros from there to ktiles.  kpack: the groups' K ranges lie one
+  // after another in the same operands (group q from the sum of
+  // kpack_len(earlier groups) on), instead of each group's own operands.
   const int32_t *kfill;
-  int kW, kEl;
+  int kW, kEl, kpack;
   int kgroup[GMAXPROD];
   int first[GMAXPROD + 1];
   const uint16_t *A[GMAXPROD];
@@ -346,12 +348,24 @@ __device__ __forceinline__ int multi_product(const MultiArgs &g, int tile) {
   return p;
 }
 
+__device__ __forceinline__ int multi_group_rows(const MultiArgs &g, int q) {
+  int f = 0;
+  for (int w = 0; w < g.kW; ++w) f += g.kfill[w * g.kEl + q];
+  return f;
+}
+
 __device__ __forceinline__ int multi_ktiles(const MultiArgs &g, int p) {
   if (!g.kfill) return g.ktiles;
-  int f = 0;
-  for (int w = 0; w < g.kW; ++w) f += g.kfill[w * g.kEl + g.kgroup[p]];
-  const int kt = max((f + GBK - 1) / GBK, min(GSPLIT_MAX, g.ktiles));
+  const int kt = max((multi_group_rows(g, g.kgroup[p]) + GBK - 1) / GBK, min(GSPLIT_MAX, g.ktiles));
   return __builtin_amdgcn_readfirstlane(min(kt, g.ktiles));
+}
+
+// First K element of product p's range in packed operands (0 otherwise).
+__device__ __forceinline__ int64_t multi_kstart(const MultiArgs &g, int p) {
+  if (!g.kpack) return 0;
+  int64_t k = 0;
+  for (int q = 0; q < g.kgroup[p]; ++q) k += kpack_len(multi_group_rows(g, q));
+  return __builtin_amdgcn_readfirstlane((int)k);
 }
 
 template <int ONLY = -1>
@@ -393,9 +407,10 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
   const int mv = M - mt * GBM, nv = N - nt * GBN;
   int k0, k1;
   g_part_range(multi_ktiles(g, p), u, k0, k1);
+  const int64_t kb = multi_kstart(g, p) + (int64_t)k0 * GBK;
   const auto ops = g_operands(
-      g.A[p] + (int64_t)mt * GBM * g.lda[p] + k0 * GBK, g.lda[p], [&](int r) { return min(r, mv - 1); },
-      g.B[p] + (int64_t)nt * GBN * g.ldb[p] + k0 * GBK, g.ldb[p], [&](int r) { return min(r, nv - 1); });
+      g.A[p] + (int64_t)mt * GBM * g.lda[p] + kb, g.lda[p], [&](int r) { return min(r, mv - 1); },
+      g.B[p] + (int64_t)nt * GBN * g.ldb[p] + kb, g.ldb[p], [&](int r) { return min(r, nv - 1); });
   GAcc acc;
   gemm_zero(acc);
   gemm_mainloop(ops, k1 - k0, acc, lds);
@@ -1037,8 +1052,9 @@ int gemm_expert_swiglu(const moe_dims &d, const uint16_t *bank, const int64_t *b
                        d, bank, bank_offsets, bfill, n_bank_rows, wg, wu, H, part, s);
 }
 
-int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int32_t *bfill,
-                           int64_t n_bank_rows, const uint16_t *wg, const uint16_t *wu,
+int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int64_t *bank_offsets,
+                           const int32_t *bfill, int64_t n_bank_rows, const uint16_t *wg,
+                           const uint16_t *wu,
                            const uint16_t *dH, uint16_t *H, uint16_t *AB, float *part,
                            hipStream_t s) {
   SwigluArgs a{};
@@ -1049,7 +1065,7 @@ int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int32_
   a.ab_off = d.d_ff;
   return expert_swiglu("gemm_expert_swiglu_bwd", "gemm_expert_swiglu_bwd_tail",
                        gemm_expert_swiglu_kernel<true>, gemm_expert_swiglu_tail_kernel<true>, a,
-                       d, bank, nullptr, bfill, n_bank_rows, wg, wu, H, part, s);
+                       d, bank, bank_offsets, bfill, n_bank_rows, wg, wu, H, part, s);
 }
 
 // out[dst[r]] = bf16(A[r] . B_j^T) for the bank rows r of every group (w, j):
@@ -1083,11 +1099,11 @@ int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_o
 }
 
 int gemm_grouped_nt(const char *name, const char *tail_name, const moe_dims &d,
-                    const uint16_t *A, int K, const int32_t *bfill, const int32_t *dst,
-                    int64_t n_bank_rows, const uint16_t *B, int N, uint16_t *out, int64_t n_out,
-                    float *part, hipStream_t s) {
-  return grouped_nt(name, tail_name, d, A, K, nullptr, bfill, dst, n_bank_rows, B, N, out, n_out,
-                    part, s);
+                    const uint16_t *A, int K, const int64_t *bank_offsets, const int32_t *bfill,
+                    const int32_t *dst, int64_t n_bank_rows, const uint16_t *B, int N,
+                    uint16_t *out, int64_t n_out, float *part, hipStream_t s) {
+  return grouped_nt(name, tail_name, d, A, K, bank_offsets, bfill, dst, n_bank_rows, B, N, out,
+                    n_out, part, s);
 }
 
 int gemm_nt(const char *name, const char *tail_name, int M, int N, int nseg,
@@ -1098,7 +1114,7 @@ int gemm_nt(const char *name, const char *tail_name, int M, int N, int nseg,
 }
 
 int gemm_nt_multi(const char *name, const char *tail_name, int nprod, const NtProd *prods, int K,
-                  float *part, hipStream_t s, const int32_t *kfill, int kW, int kEl) {
+                  float *part, hipStream_t s, const int32_t *kfill, int kW, int kEl, bool kpack) {
   if (nprod < 1 || nprod > GMAXPROD) return fail(MOE_ERR_INVALID, "%s: bad product count", name);
   if (K % GBK) return fail(MOE_ERR_UNSUPPORTED, "%s: K %% %d != 0", name, GBK);
   MultiArgs a{};
@@ -1107,6 +1123,7 @@ int gemm_nt_multi(const char *name, const char *tail_name, int nprod, const NtPr
   a.kfill = kfill;
   a.kW = kW;
   a.kEl = kEl;
+  a.kpack = kpack && kfill ? 1 : 0;
   int64_t total = 0;
   for (int p = 0; p < nprod; ++p) {
     const NtProd &q = prods[p];

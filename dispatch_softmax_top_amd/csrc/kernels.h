@@ -66,8 +66,17 @@ int combine_gather_rows(const moe_dims &d, const uint16_t *rows, const int64_t *
 // backward pass
 // ---------------------------------------------------------------------------
 
-// Workspace bytes of the backward calls (fixed mode).
-int64_t bwd_ws_bytes(const moe_dims &d, int call);
+// Workspace bytes of the backward calls; n_rows: bank rows (ragged FFN).
+int64_t bwd_ws_bytes(const moe_dims &d, int call, int64_t n_rows);
+
+// Packed per-group K ranges (ragged weight gradients): a group of `rows`
+// bank rows takes its rows rounded up to whole K tiles of 32, and at least
+// 8 K tiles (the fewest K tiles a product reads), so no product reads into
+// the next group's range.
+__host__ __device__ inline int64_t kpack_len(int64_t rows) {
+  const int64_t r = (rows + 31) / 32 * 32;
+  return r > 256 ? r : 256;
+}
 
 // C[M, N] (ldc) = sum over nseg <= 2 segments of A . B^T (bf16 out).
 // tail_name: the launch name of the kernel finishing a split last round.
@@ -91,25 +100,31 @@ struct NtProd {
   int M, N;
   int kgroup;
 };
+// kpack: product p's K range starts at the sum of kpack_len(K rows of the
+// groups before kgroup[p]) in its operands (the groups' ranges packed one
+// after another, read on the device); otherwise at 0.
 int gemm_nt_multi(const char *name, const char *tail_name, int nprod, const NtProd *prods, int K,
                   float *part, hipStream_t s, const int32_t *kfill = nullptr, int kW = 0,
-                  int kEl = 0);
+                  int kEl = 0, bool kpack = false);
 // Shared experts recomputed with the SwiGLU gradient epilogue: dH[:, dh_col0 +
 // s*F + f] in, H = h_s [M, S*F] and AB [M, 2*S*F] (d_a of every expert, then
 // d_b) out.
 int gemm_shared_swiglu_bwd(int M, const uint16_t *x, int64_t ldx, int K, const uint16_t *wg,
                            const uint16_t *wu, int S, int F, const uint16_t *dH, int64_t ld_dh,
                            int dh_col0, uint16_t *H, uint16_t *AB, float *part, hipStream_t s);
-// Routed experts recomputed over the bank (fixed mode) with the SwiGLU
-// gradient epilogue: dH, H [bank rows, F], AB [bank rows, 2F].
-int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int32_t *bfill,
+// Routed experts recomputed over the bank (groups at g * cap_recv, or at
+// bank_offsets in ragged mode) with the SwiGLU gradient epilogue: dH, H
+// [bank rows, F], AB [bank rows, 2F].
+int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int64_t *bank_offsets,
+                           const int32_t *bfill,
                            int64_t n_bank_rows, const uint16_t *wg, const uint16_t *wu,
                            const uint16_t *dH, uint16_t *H, uint16_t *AB, float *part,
                            hipStream_t s);
-// Grouped over the bank's groups (fixed mode): out[dst[r]] = A[r] . B_j^T,
-// A [bank rows][K], B [E_l][N][K].
+// Grouped over the bank's groups (bank_offsets: ragged mode, else NULL):
+// out[dst[r]] = A[r] . B_j^T, A [bank rows][K], B [E_l][N][K].
 int gemm_grouped_nt(const char *name, const char *tail_name, const moe_dims &d,
-                    const uint16_t *A, int K, const int32_t *bfill, const int32_t *dst,
+                    const uint16_t *A, int K, const int64_t *bank_offsets, const int32_t *bfill,
+                    const int32_t *dst,
                     int64_t n_bank_rows, const uint16_t *B, int N, uint16_t *out, int64_t n_out,
                     float *part, hipStream_t s);
 

@@ -158,11 +158,13 @@ class Combiner:
 
 
 class Backward:
-    """Gradient buffers and workspaces of one rank's share (fixed mode): the
-    sender's combine and pack sides, the receiver's experts and the router.
-    On one GPU both exchanges are loopbacks, read as identities like the
-    forward return: the receiver's return-row gradients are the sender's
-    d_returned, and the sender's pool-row gradients are the receiver's d_recv."""
+    """Gradient buffers and workspaces of one rank's share (fixed or ragged
+    mode): the sender's combine and pack sides, the receiver's experts and
+    the router.  On one GPU both exchanges are loopbacks, read as identities
+    like the forward return: the receiver's return-row gradients are the
+    sender's d_returned, and the sender's pool-row gradients are the
+    receiver's d_recv (in ragged mode both keep the receive layout: its
+    offsets go with them)."""
 
     def __init__(self, d, n_recv_rows, device="cuda"):
         self.d = d
@@ -186,15 +188,15 @@ class Backward:
         self.dws_gate = torch.empty(max(S, 1), Fs, D, **bf)
         self.dws_up = torch.empty(max(S, 1), Fs, D, **bf)
         self.ws_combine = _ws(d, L.MOE_CALL_COMBINE_BWD, 0, dev)
-        self.ws_ffn = _ws(d, L.MOE_CALL_FFN_BWD, 0, dev)
+        self.ws_ffn = _ws(d, L.MOE_CALL_FFN_BWD, 0 if d.cap_send else n_recv_rows, dev)
         self.ws_pack = _ws(d, L.MOE_CALL_PACK_BWD, 0, dev)
 
     def combine(self, returned, snd: Sender, cmb: Combiner, x, w_lat_up, ws_gate, ws_up, ws_down,
-                d_out, stream=None):
+                d_out, stream=None, ret_offsets=None):
         L.moe_combine_backward(self.d, returned, snd.topk, snd.slot, snd.gates, snd.fill, x,
                                cmb.ylat, w_lat_up, ws_gate, ws_up, ws_down, d_out,
                                self.d_returned, self.d_gates, self.d_shared, self.dw_lat_up,
-                               self.dws_down, self.ws_combine, stream)
+                               self.dws_down, self.ws_combine, stream, ret_offsets=ret_offsets)
 
     def route(self, logits, snd: Sender, bias=None, renorm=False, stream=None):
         L.moe_route_backward(logits, snd.topk, self.d_gates, self.d_logits, bias=bias,
@@ -203,12 +205,13 @@ class Backward:
     def ffn(self, rcv: Receiver, w_gate, w_up, w_down, d_ret, stream=None):
         L.moe_expert_ffn_backward(self.d, rcv.bank, rcv.bank_src, rcv.bfill, w_gate, w_up, w_down,
                                   d_ret, self.d_recv, self.dw_gate, self.dw_up, self.dw_down,
-                                  self.ws_ffn, stream)
+                                  self.ws_ffn, stream, bank_offsets=rcv.bank_offsets)
 
-    def pack(self, d_pools, snd: Sender, x, w_lat_down, ws_gate, ws_up, stream=None):
+    def pack(self, d_pools, snd: Sender, x, w_lat_down, ws_gate, ws_up, stream=None,
+             pool_offsets=None):
         L.moe_pack_backward(self.d, d_pools, snd.topk, snd.slot, x, self.d_shared, w_lat_down,
                             ws_gate, ws_up, self.dz, self.dx, self.dw_lat_down, self.dws_gate,
-                            self.dws_up, self.ws_pack, stream)
+                            self.dws_up, self.ws_pack, stream, pool_offsets=pool_offsets)
 
 
 # ----------------------------------------------------------------------------

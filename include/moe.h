@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef uint16_t moe_bf16;
 
@@ -318,8 +318,8 @@ int moe_profile_get(int i, char *name, int name_len, double *total_ms,
 void moe_profile_reset(void);
 
 /* ------------------------------------------------------------------------
- * Backward of the branch (training; fixed capacities only, MOE_ERR_UNSUPPORTED
- * in ragged mode).  [P2]/[P3] describe a model in open training and give its
+ * Backward of the branch (training; fixed capacities or ragged / dropless,
+ * not dedup).  [P2]/[P3] describe a model in open training and give its
  * forward pass; each call below is the chain rule through the forward call
  * of the same stage, for a loss whose gradient with respect to `out` is
  * d_out.  Gradients are stored like their values: bf16 activations and
@@ -330,7 +330,13 @@ void moe_profile_reset(void);
  * moe_pack_backward, and moe_route_backward with the gate gradients.
  * The router's own product (logits = x . W_r) is outside the boundary: its
  * input gradient is the caller's.  Workspaces: moe_workspace_bytes(d,
- * MOE_CALL_*_BWD, 0).
+ * MOE_CALL_*_BWD, n_rows), n_rows = the bank rows of the expert call in
+ * ragged mode (0 otherwise).  Ragged mode: every buffer in the pools' layout
+ * (returned, d_returned, d_pools) has segments (destination, wave) at the
+ * offsets passed with it, and a choice whose slot lies at or past its
+ * segment's length has no row there (as in moe_combine, where such a
+ * returned row reads as zero): its gate gradient is 0, it adds nothing to
+ * dz, and nothing is written for it.
  * ------------------------------------------------------------------------ */
 
 /* Router: d_logits [T, E] fp32 from d_gates [T, k].  With p the softmax of
@@ -346,8 +352,12 @@ int moe_route_backward(const float *logits, const float *bias, int32_t T,
 /* Combine side, on the sender.  Inputs as given to / produced by
  * moe_combine (returned rows in the pools' layout, the sender's topk, slot,
  * gates, fill, x, the forward's ylat) plus d_out [T, d_model] bf16.
- *   d_returned [n_ranks*n_waves*cap_send, latent] out: bf16(g d_ylat[t]) in
- *              each kept choice's row, 0 in every other row; d_ylat =
+ *   ret_offsets ragged: [n_ranks*n_waves + 1] int64, the segments of
+ *              returned and d_returned; NULL if fixed
+ *   n_ret_rows rows of returned and d_returned (fixed mode: must equal
+ *              n_ranks*n_waves*cap_send)
+ *   d_returned [n_ret_rows, latent] out: bf16(g d_ylat[t]) in each kept
+ *              choice's row, 0 in every other row; d_ylat =
  *              d_out . W_lu^T (rounded to bf16, not returned)
  *   d_gates    [T, k] fp32 out: returned row . d_ylat[t], 0 if dropped
  *   d_shared   [T, 2, n_shared, d_ff_shared] bf16 out: d_a, then d_b, of
@@ -356,6 +366,7 @@ int moe_route_backward(const float *logits, const float *bias, int32_t T,
  *   dws_down   [n_shared, d_model, d_ff_shared] bf16 out
  * ws_gate / ws_up / ws_down / d_shared / dws_down may be NULL if n_shared = 0. */
 int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
+                         const int64_t *ret_offsets, int64_t n_ret_rows,
                          const int32_t *topk, const int32_t *slot,
                          const float *gates, const int32_t *fill,
                          const moe_bf16 *x, const moe_bf16 *ylat,
@@ -366,24 +377,30 @@ int moe_combine_backward(const moe_dims *d, const moe_bf16 *returned,
                          moe_bf16 *dw_lat_up, moe_bf16 *dws_down, void *ws,
                          int64_t ws_bytes, void *stream);
 
-/* Receiver side.  bank, bank_src, bfill as produced by moe_bank; weights as
- * given to moe_expert_ffn; d_ret [n_ranks*n_waves*cap_send, latent]: the
- * gradients of this rank's return rows (receive layout).
- *   d_recv   [n_ranks*n_waves*cap_send, latent] out: gradient of each kept
- *            receive row's payload (d_a . W_g + d_b . W_u), 0 elsewhere
+/* Receiver side.  bank, bank_offsets, bank_src, bfill as produced by
+ * moe_bank; weights as given to moe_expert_ffn; d_ret [n_ret_rows, latent]:
+ * the gradients of this rank's return rows (receive layout).
+ *   n_bank_rows  rows of bank (fixed: n_waves*E_l*cap_recv; ragged: the
+ *                receive rows, n_ret_rows)
+ *   n_ret_rows   rows of d_ret and d_recv (fixed: n_ranks*n_waves*cap_send)
+ *   d_recv   [n_ret_rows, latent] out: gradient of each kept receive row's
+ *            payload (d_a . W_g + d_b . W_u), 0 elsewhere
  *   dw_gate, dw_up [E_l, d_ff, latent], dw_down [E_l, latent, d_ff] out,
- *            each local expert's sum over its kept rows of every wave. */
+ *            each local expert's sum over its kept rows of every wave.
+ * Ragged mode needs E_l <= 6. */
 int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
+                            const int64_t *bank_offsets, int64_t n_bank_rows,
                             const int32_t *bank_src, const int32_t *bfill,
                             const moe_bf16 *w_gate, const moe_bf16 *w_up,
                             const moe_bf16 *w_down, const moe_bf16 *d_ret,
-                            moe_bf16 *d_recv, moe_bf16 *dw_gate,
+                            int64_t n_ret_rows, moe_bf16 *d_recv, moe_bf16 *dw_gate,
                             moe_bf16 *dw_up, moe_bf16 *dw_down, void *ws,
                             int64_t ws_bytes, void *stream);
 
-/* Sender side.  d_pools [n_ranks*n_waves*cap_send, latent]: gradients of
- * this shard's pool payloads (the pools' layout); topk, slot, x as in the
- * forward pass; d_shared from moe_combine_backward.
+/* Sender side.  d_pools [pool rows, latent]: gradients of this shard's pool
+ * payloads (the pools' layout; ragged: segments at pool_offsets, [n_ranks*
+ * n_waves + 1] int64, NULL if fixed); topk, slot, x as in the forward pass;
+ * d_shared from moe_combine_backward.
  *   dz          [T, latent] bf16 out: sum over kept choices of their rows
  *   dx          [T, d_model] bf16 out: dz . W_ld^T + the shared experts'
  *               input gradient, one sum, one rounding
@@ -391,7 +408,8 @@ int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
  *               d_model] bf16 out.
  * d_shared, ws_gate, ws_up, dws_gate, dws_up may be NULL if n_shared = 0. */
 int moe_pack_backward(const moe_dims *d, const moe_bf16 *d_pools,
-                      const int32_t *topk, const int32_t *slot,
+                      const int64_t *pool_offsets, const int32_t *topk,
+                      const int32_t *slot,
                       const moe_bf16 *x, const moe_bf16 *d_shared,
                       const moe_bf16 *w_lat_down, const moe_bf16 *ws_gate,
                       const moe_bf16 *ws_up, moe_bf16 *dz, moe_bf16 *dx,

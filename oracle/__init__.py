@@ -79,26 +79,28 @@ def lib():
                                           i64, _u16p, _u16p]),
             "orc_route_backward": (None, [_f32p, vp, i64, i32, i32, i32, _i32p, _f32p,
                                           _f32p]),
-            "orc_combine_backward": (None, [dp, _u16p, _i32p, _i32p, _f32p, _u16p, _u16p,
-                                            _u16p, _u16p, _u16p, _u16p, _u16p, _u16p,
+            "orc_combine_backward": (None, [dp, _u16p, vp, i64, _i32p, _i32p, _f32p, _u16p,
+                                            _u16p, _u16p, _u16p, _u16p, _u16p, _u16p, _u16p,
                                             _f32p, _u16p, _u16p, _u16p]),
-            "orc_expert_ffn_backward": (None, [dp, _u16p, _i32p, _i32p, _u16p, _u16p, _u16p,
-                                               _u16p, i64, _u16p, _u16p, _u16p, _u16p]),
-            "orc_pack_backward": (None, [dp, _u16p, _i32p, _i32p, _u16p, _u16p, _u16p, _u16p,
-                                         _u16p, _u16p, _u16p, _u16p, _u16p, _u16p]),
-            "orc_combine_backward_tokens": (None, [dp, _u16p, _i32p, _i32p, _f32p, _u16p, _u16p,
-                                                   _u16p, _u16p, _u16p, _u16p, _i64p, i64, _u16p,
-                                                   _f32p, _u16p]),
+            "orc_expert_ffn_backward": (None, [dp, _u16p, vp, _i32p, _i32p, _u16p, _u16p,
+                                               _u16p, _u16p, i64, _u16p, _u16p, _u16p,
+                                               _u16p]),
+            "orc_pack_backward": (None, [dp, _u16p, vp, _i32p, _i32p, _u16p, _u16p, _u16p,
+                                         _u16p, _u16p, _u16p, _u16p, _u16p, _u16p, _u16p]),
+            "orc_combine_backward_tokens": (None, [dp, _u16p, vp, _i32p, _i32p, _f32p, _u16p,
+                                                   _u16p, _u16p, _u16p, _u16p, _u16p, _i64p, i64,
+                                                   _u16p, _f32p, _u16p]),
             "orc_combine_wgrad_entries": (None, [dp, _u16p, _u16p, _u16p, _u16p, _u16p, i32,
                                                  _i32p, _i32p, _i32p, i64, _u16p]),
-            "orc_expert_ffn_backward_rows": (None, [dp, _u16p, _i32p, _u16p, _u16p, _u16p, _u16p,
-                                                    _i64p, i64, _u16p]),
-            "orc_expert_wgrad_entries": (None, [dp, _u16p, _i32p, _i32p, _u16p, _u16p, _u16p,
-                                                _u16p, i32, i32, _i32p, _i32p, i64, _u16p]),
-            "orc_pack_backward_tokens": (None, [dp, _u16p, _i32p, _i32p, _u16p, _u16p, _u16p,
-                                                _u16p, _i64p, i64, _u16p, _u16p]),
-            "orc_pack_wgrad_entries": (None, [dp, _u16p, _i32p, _i32p, _u16p, _u16p, i32, _i32p,
-                                              _i32p, _i32p, i64, _u16p]),
+            "orc_expert_ffn_backward_rows": (None, [dp, _u16p, vp, _i32p, _u16p, _u16p, _u16p,
+                                                    _u16p, _i64p, i64, _u16p]),
+            "orc_expert_wgrad_entries": (None, [dp, _u16p, vp, _i32p, _i32p, _u16p, _u16p,
+                                                _u16p, _u16p, i32, i32, _i32p, _i32p, i64,
+                                                _u16p]),
+            "orc_pack_backward_tokens": (None, [dp, _u16p, vp, _i32p, _i32p, _u16p, _u16p,
+                                                _u16p, _u16p, _i64p, i64, _u16p, _u16p]),
+            "orc_pack_wgrad_entries": (None, [dp, _u16p, vp, _i32p, _i32p, _u16p, _u16p, i32,
+                                              _i32p, _i32p, _i32p, i64, _u16p]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -328,7 +330,7 @@ def combine(d: Dims, returned, ret_offsets, topk, slot, gates, x, w_lu_t,
 
 
 # ----------------------------------------------------------------------------
-# backward of the branch (fixed capacities)
+# backward of the branch (ragged mode: pass the segment / group offsets)
 # ----------------------------------------------------------------------------
 
 def _u16(a):
@@ -349,25 +351,30 @@ def route_backward(logits, topk, d_gates, bias=None, renorm=False):
 
 
 def combine_backward(d: Dims, returned, topk, slot, gates, x, ylat, w_lu_t, ws_gate, ws_up,
-                     ws_down, d_out):
-    """(d_returned, d_gates, d_shared [T, 2, S, Fs], dw_lat_up, dws_down)."""
+                     ws_down, d_out, ret_offsets=None):
+    """(d_returned (returned's rows), d_gates, d_shared [T, 2, S, Fs], dw_lat_up,
+    dws_down); ret_offsets: returned's segments in ragged mode."""
     T, L, D, S, Fs = d.T, d.latent, d.d_model, d.n_shared, d.d_ff_shared
-    n_rows = d.n_ranks * d.n_waves * d.cap_send
+    n_rows = len(returned)
+    ro = None if ret_offsets is None else np.ascontiguousarray(ret_offsets, np.int64)
     d_ret = np.empty((n_rows, L), np.uint16)
     d_gates = np.empty((T, d.top_k), np.float32)
     d_shared = np.empty((T, 2, S, Fs), np.uint16)
     dw_lu = np.empty((D, L), np.uint16)
     dws_down = np.empty((S, D, Fs), np.uint16)
     lib().orc_combine_backward(
-        ctypes.byref(d), _u16(returned), np.ascontiguousarray(topk, np.int32),
+        ctypes.byref(d), _u16(returned), _ptr(ro), n_rows, np.ascontiguousarray(topk, np.int32),
         np.ascontiguousarray(slot, np.int32), np.ascontiguousarray(gates, np.float32), _u16(x),
         _u16(ylat), _u16(w_lu_t), _u16(ws_gate), _u16(ws_up), _u16(ws_down), _u16(d_out),
         d_ret, d_gates, d_shared, dw_lu, dws_down)
     return d_ret, d_gates, d_shared, dw_lu, dws_down
 
 
-def expert_ffn_backward(d: Dims, bank, bank_src, bfill, w_gate, w_up, w_down, d_ret):
-    """(d_recv, dw_gate, dw_up, dw_down) of one rank's experts."""
+def expert_ffn_backward(d: Dims, bank, bank_src, bfill, w_gate, w_up, w_down, d_ret,
+                        bank_offsets=None):
+    """(d_recv, dw_gate, dw_up, dw_down) of one rank's experts; bank_offsets:
+    the bank's groups in ragged mode."""
+    bo = None if bank_offsets is None else np.ascontiguousarray(bank_offsets, np.int64)
     El = d.n_experts // d.n_ranks
     n_ret = len(d_ret)
     d_recv = np.empty((n_ret, d.latent), np.uint16)
@@ -375,14 +382,17 @@ def expert_ffn_backward(d: Dims, bank, bank_src, bfill, w_gate, w_up, w_down, d_
     dwu = np.empty_like(dwg)
     dwd = np.empty((El, d.latent, d.d_ff), np.uint16)
     lib().orc_expert_ffn_backward(
-        ctypes.byref(d), _u16(bank), np.ascontiguousarray(bank_src, np.int32),
+        ctypes.byref(d), _u16(bank), _ptr(bo), np.ascontiguousarray(bank_src, np.int32),
         np.ascontiguousarray(bfill, np.int32), _u16(w_gate), _u16(w_up), _u16(w_down),
         _u16(d_ret), n_ret, d_recv, dwg, dwu, dwd)
     return d_recv, dwg, dwu, dwd
 
 
-def pack_backward(d: Dims, d_pools, topk, slot, x, d_shared, w_ld_t, ws_gate, ws_up):
-    """(dz, dx, dw_lat_down, dws_gate, dws_up)."""
+def pack_backward(d: Dims, d_pools, topk, slot, x, d_shared, w_ld_t, ws_gate, ws_up,
+                  pool_offsets=None):
+    """(dz, dx, dw_lat_down, dws_gate, dws_up); pool_offsets: d_pools'
+    segments in ragged mode."""
+    po = None if pool_offsets is None else np.ascontiguousarray(pool_offsets, np.int64)
     T, L, D, S, Fs = d.T, d.latent, d.d_model, d.n_shared, d.d_ff_shared
     dz = np.empty((T, L), np.uint16)
     dx = np.empty((T, D), np.uint16)
@@ -390,7 +400,7 @@ def pack_backward(d: Dims, d_pools, topk, slot, x, d_shared, w_ld_t, ws_gate, ws
     dwsg = np.empty((S, Fs, D), np.uint16)
     dwsu = np.empty_like(dwsg)
     lib().orc_pack_backward(
-        ctypes.byref(d), _u16(d_pools), np.ascontiguousarray(topk, np.int32),
+        ctypes.byref(d), _u16(d_pools), _ptr(po), np.ascontiguousarray(topk, np.int32),
         np.ascontiguousarray(slot, np.int32), _u16(x), _u16(d_shared), _u16(w_ld_t),
         _u16(ws_gate), _u16(ws_up), dz, dx, dw_ld, dwsg, dwsu)
     return dz, dx, dw_ld, dwsg, dwsu
@@ -407,15 +417,16 @@ def _i64(a):
 
 
 def combine_backward_tokens(d: Dims, returned, topk, slot, gates, x, w_lu_t, ws_gate, ws_up,
-                            ws_down, d_out, tokens):
+                            ws_down, d_out, tokens, ret_offsets=None):
     """(d_ret_rows [n, k, L], d_gates [n, k], d_shared [n, 2, S, Fs]) for tokens."""
     tk = _i64(tokens)
+    ro = None if ret_offsets is None else _i64(ret_offsets)
     n, k, L = len(tk), d.top_k, d.latent
     rows = np.empty((n, k, L), np.uint16)
     dg = np.empty((n, k), np.float32)
     dsh = np.empty((n, 2, d.n_shared, d.d_ff_shared), np.uint16)
     lib().orc_combine_backward_tokens(
-        ctypes.byref(d), _u16(returned), _i32(topk), _i32(slot),
+        ctypes.byref(d), _u16(returned), _ptr(ro), _i32(topk), _i32(slot),
         np.ascontiguousarray(gates, np.float32), _u16(x), _u16(w_lu_t), _u16(ws_gate),
         _u16(ws_up), _u16(ws_down), _u16(d_out), tk, n, rows, dg, dsh)
     return rows, dg, dsh
@@ -432,43 +443,53 @@ def combine_wgrad_entries(d: Dims, x, ylat, ws_gate, ws_up, d_out, which, ra, cb
     return out
 
 
-def expert_ffn_backward_rows(d: Dims, bank, bank_src, w_gate, w_up, w_down, d_ret, pos):
+def expert_ffn_backward_rows(d: Dims, bank, bank_src, w_gate, w_up, w_down, d_ret, pos,
+                             bank_offsets=None):
     """d_u [n, L] of kept bank positions pos (written to d_recv[bank_src[pos]])."""
     p = _i64(pos)
+    bo = None if bank_offsets is None else _i64(bank_offsets)
     out = np.empty((len(p), d.latent), np.uint16)
-    lib().orc_expert_ffn_backward_rows(ctypes.byref(d), _u16(bank), _i32(bank_src),
+    lib().orc_expert_ffn_backward_rows(ctypes.byref(d), _u16(bank), _ptr(bo), _i32(bank_src),
                                        _u16(w_gate), _u16(w_up), _u16(w_down), _u16(d_ret), p,
                                        len(p), out)
     return out
 
 
 def expert_wgrad_entries(d: Dims, bank, bank_src, bfill, w_gate, w_up, w_down, d_ret, j, which,
-                         ra, cb):
+                         ra, cb, bank_offsets=None):
     """which 0: dw_gate[j, ra, cb]; 1: dw_up[j, ra, cb]; 2: dw_down[j, ra, cb]."""
     n = len(ra)
+    bo = None if bank_offsets is None else _i64(bank_offsets)
     out = np.empty(n, np.uint16)
-    lib().orc_expert_wgrad_entries(ctypes.byref(d), _u16(bank), _i32(bank_src), _i32(bfill),
+    lib().orc_expert_wgrad_entries(ctypes.byref(d), _u16(bank), _ptr(bo), _i32(bank_src),
+                                   _i32(bfill),
                                    _u16(w_gate), _u16(w_up), _u16(w_down), _u16(d_ret), j, which,
                                    _i32(ra), _i32(cb), n, out)
     return out
 
 
-def pack_backward_tokens(d: Dims, d_pools, topk, slot, d_shared, w_ld_t, ws_gate, ws_up, tokens):
+def pack_backward_tokens(d: Dims, d_pools, topk, slot, d_shared, w_ld_t, ws_gate, ws_up, tokens,
+                         pool_offsets=None):
     """(dz [n, L], dx [n, D]) for tokens."""
     tk = _i64(tokens)
+    po = None if pool_offsets is None else _i64(pool_offsets)
     dz = np.empty((len(tk), d.latent), np.uint16)
     dx = np.empty((len(tk), d.d_model), np.uint16)
-    lib().orc_pack_backward_tokens(ctypes.byref(d), _u16(d_pools), _i32(topk), _i32(slot),
+    lib().orc_pack_backward_tokens(ctypes.byref(d), _u16(d_pools), _ptr(po), _i32(topk),
+                                   _i32(slot),
                                    _u16(d_shared), _u16(w_ld_t), _u16(ws_gate), _u16(ws_up), tk,
                                    len(tk), dz, dx)
     return dz, dx
 
 
-def pack_wgrad_entries(d: Dims, d_pools, topk, slot, x, d_shared, which, ra, cb, sh=None):
+def pack_wgrad_entries(d: Dims, d_pools, topk, slot, x, d_shared, which, ra, cb, sh=None,
+                       pool_offsets=None):
     """which 0: dw_lat_down[ra, cb]; 1: dws_gate[sh, ra, cb]; 2: dws_up[sh, ra, cb]."""
     n = len(ra)
+    po = None if pool_offsets is None else _i64(pool_offsets)
     out = np.empty(n, np.uint16)
     shi = _i32(np.zeros(n) if sh is None else sh)
-    lib().orc_pack_wgrad_entries(ctypes.byref(d), _u16(d_pools), _i32(topk), _i32(slot), _u16(x),
-                                 _u16(d_shared), which, shi, _i32(ra), _i32(cb), n, out)
+    lib().orc_pack_wgrad_entries(ctypes.byref(d), _u16(d_pools), _ptr(po), _i32(topk),
+                                 _i32(slot), _u16(x), _u16(d_shared), which, shi, _i32(ra),
+                                 _i32(cb), n, out)
     return out

@@ -637,11 +637,24 @@ static double silu_grad(double a) {
   return s * (1.0 + a * (1.0 - s));
 }
 
-/* Row of assignment (t, e, slot s) in the sender's pools (fixed mode). */
-static int64_t pool_row(const orc_dims *d, int64_t t, int32_t e, int32_t s) {
+/* Row of assignment (t, e, slot s) in a buffer of the pools' layout, or -1.
+ * Fixed mode: (destination, wave, slot) with cap_send rows per pool.  Ragged
+ * mode (waves by token): segment (destination, wave) starts at offsets[seg],
+ * and a slot at or past the segment's length has no row (as in the forward
+ * combine, where such a returned row reads as zero). */
+static int64_t pool_row(const orc_dims *d, const int64_t *offsets, int64_t t, int32_t e,
+                        int32_t s) {
   const int32_t W = d->n_waves;
   if (d->wave_mode == 1) return (int64_t)dest_of(d, e) * W * d->cap_send + s;
-  return ((int64_t)dest_of(d, e) * W + t / orc_tokens_per_wave(d->T, W)) * d->cap_send + s;
+  const int64_t seg = (int64_t)dest_of(d, e) * W + t / orc_tokens_per_wave(d->T, W);
+  if (d->cap_send) return seg * d->cap_send + s;
+  if (s >= offsets[seg + 1] - offsets[seg]) return -1;
+  return offsets[seg] + s;
+}
+
+/* First bank row of bank group g (fixed: g * cap_recv; ragged: offsets). */
+static int64_t group_start(const orc_dims *d, const int64_t *bank_offsets, int32_t g) {
+  return d->cap_send ? (int64_t)g * d->cap_recv : bank_offsets[g];
 }
 
 /* Router: with p = softmax(l) over all E (l = fp32(logit + bias)) and gate
@@ -701,6 +714,7 @@ void orc_route_backward(const float *logits, const float *bias, int64_t T,
  *   dws_down[s][c][f]  = bf16(sum_t d_out[t][c] h_s[t][f])       ([S][D][Fs])
  * with h_s = bf16(silu(a) b) as in the forward pass. */
 void orc_combine_backward(const orc_dims *d, const uint16_t *returned,
+                          const int64_t *ret_offsets, int64_t n_ret_rows,
                           const int32_t *topk, const int32_t *slot,
                           const float *gates, const uint16_t *x,
                           const uint16_t *ylat, const uint16_t *w_lu_t,
@@ -712,10 +726,9 @@ void orc_combine_backward(const orc_dims *d, const uint16_t *returned,
   const int64_t T = d->T;
   const int32_t L = d->latent, D = d->d_model, k = d->top_k;
   const int32_t S = d->n_shared, Fs = d->d_ff_shared;
-  const int64_t n_rows = (int64_t)d->n_ranks * d->n_waves * d->cap_send;
   double *dyl = (double *)malloc(sizeof(double) * (size_t)L);
   uint16_t *hs = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(T * S * Fs + 1));
-  memset(d_returned, 0, sizeof(uint16_t) * (size_t)(n_rows * L));
+  memset(d_returned, 0, sizeof(uint16_t) * (size_t)(n_ret_rows * L));
   for (int64_t t = 0; t < T; ++t) {
     const uint16_t *go = d_out + t * D;
     for (int32_t i = 0; i < L; ++i) {
@@ -725,11 +738,11 @@ void orc_combine_backward(const orc_dims *d, const uint16_t *returned,
     }
     for (int32_t j = 0; j < k; ++j) {
       int32_t s = slot[t * k + j];
-      if (s < 0) {
+      int64_t row = s < 0 ? -1 : pool_row(d, ret_offsets, t, topk[t * k + j], s);
+      if (row < 0) { /* dropped, or (ragged) a row the forward read as zero */
         d_gates[t * k + j] = 0.0f;
         continue;
       }
-      int64_t row = pool_row(d, t, topk[t * k + j], s);
       double g = gates[t * k + j], dot = 0.0;
       for (int32_t i = 0; i < L; ++i) {
         d_returned[row * L + i] = to_bf(g * dyl[i]);
@@ -780,6 +793,7 @@ void orc_combine_backward(const orc_dims *d, const uint16_t *returned,
  *   dw_gate[j][f][l] = bf16(sum of d_a[f] u[l]), dw_up likewise with d_b,
  * the weight sums running over the rows in (wave, bank position) order. */
 void orc_expert_ffn_backward(const orc_dims *d, const uint16_t *bank,
+                             const int64_t *bank_offsets,
                              const int32_t *bank_src, const int32_t *bfill,
                              const uint16_t *w_gate, const uint16_t *w_up,
                              const uint16_t *w_down, const uint16_t *d_ret,
@@ -803,7 +817,7 @@ void orc_expert_ffn_backward(const orc_dims *d, const uint16_t *bank,
       int32_t g = w * El + j;
       const uint16_t *Wg = w_gate + j * WL, *Wu = w_up + j * WL, *Wd = w_down + j * WL;
       for (int32_t p = 0; p < bfill[g]; ++p) {
-        int64_t pos = (int64_t)g * d->cap_recv + p, src = bank_src[pos];
+        int64_t pos = group_start(d, bank_offsets, g) + p, src = bank_src[pos];
         for (int32_t l = 0; l < L; ++l) {
           u[l] = bf(bank[pos * L + l]);
           dy[l] = bf(d_ret[src * L + l]);
@@ -858,6 +872,7 @@ void orc_expert_ffn_backward(const orc_dims *d, const uint16_t *bank,
  *   dws_gate[s][f][i]  = bf16(sum_t d_a[t,s,f] x[t][i]), dws_up likewise,
  * with d_a, d_b from d_shared ([T][2][S][Fs], the combine side's output). */
 void orc_pack_backward(const orc_dims *d, const uint16_t *d_pools,
+                       const int64_t *pool_offsets,
                        const int32_t *topk, const int32_t *slot,
                        const uint16_t *x, const uint16_t *d_shared,
                        const uint16_t *w_ld_t, const uint16_t *ws_gate,
@@ -872,8 +887,8 @@ void orc_pack_backward(const orc_dims *d, const uint16_t *d_pools,
     for (int32_t l = 0; l < L; ++l) acc[l] = 0.0;
     for (int32_t j = 0; j < k; ++j) {
       int32_t s = slot[t * k + j];
-      if (s < 0) continue;
-      int64_t row = pool_row(d, t, topk[t * k + j], s);
+      int64_t row = s < 0 ? -1 : pool_row(d, pool_offsets, t, topk[t * k + j], s);
+      if (row < 0) continue;
       for (int32_t l = 0; l < L; ++l) acc[l] += bf(d_pools[row * L + l]);
     }
     for (int32_t l = 0; l < L; ++l) dz[t * L + l] = to_bf(acc[l]);
@@ -918,6 +933,7 @@ void orc_pack_backward(const orc_dims *d, const uint16_t *d_pools,
  * of each kept choice, 0 for a dropped one), d_gates [n][k], d_shared
  * [n][2][S][Fs].  Equal to orc_combine_backward's values for those tokens. */
 void orc_combine_backward_tokens(const orc_dims *d, const uint16_t *returned,
+                                 const int64_t *ret_offsets,
                                  const int32_t *topk, const int32_t *slot,
                                  const float *gates, const uint16_t *x,
                                  const uint16_t *w_lu_t, const uint16_t *ws_gate,
@@ -939,12 +955,12 @@ void orc_combine_backward_tokens(const orc_dims *d, const uint16_t *returned,
     for (int32_t j = 0; j < k; ++j) {
       uint16_t *o = d_ret_rows + (r * k + j) * L;
       int32_t s = slot[t * k + j];
-      if (s < 0) {
+      int64_t row = s < 0 ? -1 : pool_row(d, ret_offsets, t, topk[t * k + j], s);
+      if (row < 0) {
         memset(o, 0, sizeof(uint16_t) * (size_t)L);
         d_gates[r * k + j] = 0.0f;
         continue;
       }
-      int64_t row = pool_row(d, t, topk[t * k + j], s);
       double g = gates[t * k + j], dot = 0.0;
       for (int32_t i = 0; i < L; ++i) {
         o[i] = to_bf(g * dyl[i]);
@@ -1004,6 +1020,7 @@ void orc_combine_wgrad_entries(const orc_dims *d, const uint16_t *x,
 /* Receiver side for bank positions pos[0..n) (kept rows): d_u [n][L], the
  * row each writes to d_recv[bank_src[pos]]. */
 void orc_expert_ffn_backward_rows(const orc_dims *d, const uint16_t *bank,
+                                  const int64_t *bank_offsets,
                                   const int32_t *bank_src,
                                   const uint16_t *w_gate, const uint16_t *w_up,
                                   const uint16_t *w_down, const uint16_t *d_ret,
@@ -1015,7 +1032,9 @@ void orc_expert_ffn_backward_rows(const orc_dims *d, const uint16_t *bank,
   double *db = (double *)malloc(sizeof(double) * (size_t)F);
   for (int64_t r = 0; r < n; ++r) {
     const int64_t p = pos[r], src = bank_src[p];
-    const int32_t j = (int32_t)((p / d->cap_recv) % El);
+    int32_t g = 0; /* bank group of position p */
+    while (g + 1 < d->n_waves * El && group_start(d, bank_offsets, g + 1) <= p) ++g;
+    const int32_t j = g % El;
     const uint16_t *Wg = w_gate + j * WL, *Wu = w_up + j * WL, *Wd = w_down + j * WL;
     for (int32_t f = 0; f < F; ++f) {
       double dh = 0.0, a = 0.0, b = 0.0;
@@ -1041,6 +1060,7 @@ void orc_expert_ffn_backward_rows(const orc_dims *d, const uint16_t *bank,
  * wave, in (wave, position) order: which 0: dw_gate[j][ra][cb] (f, l);
  * 1: dw_up[j][ra][cb]; 2: dw_down[j][ra][cb] (l, f). */
 void orc_expert_wgrad_entries(const orc_dims *d, const uint16_t *bank,
+                              const int64_t *bank_offsets,
                               const int32_t *bank_src, const int32_t *bfill,
                               const uint16_t *w_gate, const uint16_t *w_up,
                               const uint16_t *w_down, const uint16_t *d_ret,
@@ -1054,7 +1074,7 @@ void orc_expert_wgrad_entries(const orc_dims *d, const uint16_t *bank,
   for (int32_t w = 0; w < d->n_waves; ++w) {
     const int32_t g = w * El + j;
     for (int32_t p = 0; p < bfill[g]; ++p) {
-      const int64_t pos = (int64_t)g * d->cap_recv + p, src = bank_src[pos];
+      const int64_t pos = group_start(d, bank_offsets, g) + p, src = bank_src[pos];
       const uint16_t *u = bank + pos * L, *dy = d_ret + src * L;
       for (int64_t e = 0; e < n; ++e) {
         const int32_t f = which == 2 ? cb[e] : ra[e];
@@ -1079,6 +1099,7 @@ void orc_expert_wgrad_entries(const orc_dims *d, const uint16_t *bank,
 /* Sender side for tokens[0..n): dz [n][L], dx [n][D]; d_shared is the full
  * [T][2][S][Fs] input. */
 void orc_pack_backward_tokens(const orc_dims *d, const uint16_t *d_pools,
+                              const int64_t *pool_offsets,
                               const int32_t *topk, const int32_t *slot,
                               const uint16_t *d_shared, const uint16_t *w_ld_t,
                               const uint16_t *ws_gate, const uint16_t *ws_up,
@@ -1092,8 +1113,8 @@ void orc_pack_backward_tokens(const orc_dims *d, const uint16_t *d_pools,
     for (int32_t l = 0; l < L; ++l) acc[l] = 0.0;
     for (int32_t j = 0; j < k; ++j) {
       int32_t s = slot[t * k + j];
-      if (s < 0) continue;
-      int64_t row = pool_row(d, t, topk[t * k + j], s);
+      int64_t row = s < 0 ? -1 : pool_row(d, pool_offsets, t, topk[t * k + j], s);
+      if (row < 0) continue;
       for (int32_t l = 0; l < L; ++l) acc[l] += bf(d_pools[row * L + l]);
     }
     for (int32_t l = 0; l < L; ++l) dz[r * L + l] = to_bf(acc[l]);
@@ -1117,6 +1138,7 @@ void orc_pack_backward_tokens(const orc_dims *d, const uint16_t *d_pools,
  * orc_pack_backward); 1: dws_gate, 2: dws_up [sh*Fs + ra][cb] =
  * sum_t d_shared[t][gate or up][sh][ra] x[t][cb]. */
 void orc_pack_wgrad_entries(const orc_dims *d, const uint16_t *d_pools,
+                            const int64_t *pool_offsets,
                             const int32_t *topk, const int32_t *slot,
                             const uint16_t *x, const uint16_t *d_shared,
                             int32_t which, const int32_t *sh_idx,
@@ -1133,8 +1155,8 @@ void orc_pack_wgrad_entries(const orc_dims *d, const uint16_t *d_pools,
         double z = 0.0;
         for (int32_t j = 0; j < k; ++j) {
           int32_t s = slot[t * k + j];
-          if (s < 0) continue;
-          z += bf(d_pools[pool_row(d, t, topk[t * k + j], s) * L + ra[e]]);
+          int64_t row = s < 0 ? -1 : pool_row(d, pool_offsets, t, topk[t * k + j], s);
+          if (row >= 0) z += bf(d_pools[row * L + ra[e]]);
         }
         v = bf(to_bf(z));
       } else {

@@ -114,14 +114,21 @@ void orc_combine_tokens(const orc_dims *d, const uint16_t *returned,
                         const uint16_t *ws_down, const int64_t *tokens,
                         int64_t n, uint16_t *ylat, uint16_t *out);
 
-/* Backward of the branch (fixed capacities).  Layouts as in the forward
- * calls; d_shared is [T][2][n_shared][d_ff_shared]: the gradients of the
- * shared experts' gate products, then of their up products. */
+/* Backward of the branch.  Layouts as in the forward calls; d_shared is
+ * [T][2][n_shared][d_ff_shared]: the gradients of the shared experts' gate
+ * products, then of their up products.  Ragged mode (cap_send == 0):
+ * returned / d_returned and d_pools have segments (destination, wave) at
+ * ret_offsets / pool_offsets [n_ranks*n_waves + 1], and a slot at or past
+ * its segment's length has no row (the forward read it as zero: its gate
+ * gradient is 0 and nothing is written); the bank's groups start at
+ * bank_offsets.  The offsets are ignored (may be NULL) in fixed mode.
+ * n_ret_rows: rows of returned and d_returned. */
 void orc_route_backward(const float *logits, const float *bias, int64_t T,
                         int32_t E, int32_t k, int32_t renorm,
                         const int32_t *topk, const float *d_gates,
                         float *d_logits);
 void orc_combine_backward(const orc_dims *d, const uint16_t *returned,
+                          const int64_t *ret_offsets, int64_t n_ret_rows,
                           const int32_t *topk, const int32_t *slot,
                           const float *gates, const uint16_t *x,
                           const uint16_t *ylat, const uint16_t *w_lu_t,
@@ -131,6 +138,7 @@ void orc_combine_backward(const orc_dims *d, const uint16_t *returned,
                           uint16_t *d_shared, uint16_t *dw_lat_up,
                           uint16_t *dws_down);
 void orc_expert_ffn_backward(const orc_dims *d, const uint16_t *bank,
+                             const int64_t *bank_offsets,
                              const int32_t *bank_src, const int32_t *bfill,
                              const uint16_t *w_gate, const uint16_t *w_up,
                              const uint16_t *w_down, const uint16_t *d_ret,
@@ -138,6 +146,7 @@ void orc_expert_ffn_backward(const orc_dims *d, const uint16_t *bank,
                              uint16_t *dw_gate, uint16_t *dw_up,
                              uint16_t *dw_down);
 void orc_pack_backward(const orc_dims *d, const uint16_t *d_pools,
+                       const int64_t *pool_offsets,
                        const int32_t *topk, const int32_t *slot,
                        const uint16_t *x, const uint16_t *d_shared,
                        const uint16_t *w_ld_t, const uint16_t *ws_gate,
@@ -148,6 +157,7 @@ void orc_pack_backward(const orc_dims *d, const uint16_t *d_pools,
 /* Backward on sampled outputs: the same values as the full functions for
  * listed tokens, bank positions or weight entries (full-size checks). */
 void orc_combine_backward_tokens(const orc_dims *d, const uint16_t *returned,
+                                 const int64_t *ret_offsets,
                                  const int32_t *topk, const int32_t *slot,
                                  const float *gates, const uint16_t *x,
                                  const uint16_t *w_lu_t, const uint16_t *ws_gate,
@@ -162,23 +172,27 @@ void orc_combine_wgrad_entries(const orc_dims *d, const uint16_t *x,
                                const int32_t *ra, const int32_t *cb, int64_t n,
                                uint16_t *out);
 void orc_expert_ffn_backward_rows(const orc_dims *d, const uint16_t *bank,
+                                  const int64_t *bank_offsets,
                                   const int32_t *bank_src,
                                   const uint16_t *w_gate, const uint16_t *w_up,
                                   const uint16_t *w_down, const uint16_t *d_ret,
                                   const int64_t *pos, int64_t n, uint16_t *d_u);
 void orc_expert_wgrad_entries(const orc_dims *d, const uint16_t *bank,
+                              const int64_t *bank_offsets,
                               const int32_t *bank_src, const int32_t *bfill,
                               const uint16_t *w_gate, const uint16_t *w_up,
                               const uint16_t *w_down, const uint16_t *d_ret,
                               int32_t j, int32_t which, const int32_t *ra,
                               const int32_t *cb, int64_t n, uint16_t *out);
 void orc_pack_backward_tokens(const orc_dims *d, const uint16_t *d_pools,
+                              const int64_t *pool_offsets,
                               const int32_t *topk, const int32_t *slot,
                               const uint16_t *d_shared, const uint16_t *w_ld_t,
                               const uint16_t *ws_gate, const uint16_t *ws_up,
                               const int64_t *tokens, int64_t n, uint16_t *dz,
                               uint16_t *dx);
 void orc_pack_wgrad_entries(const orc_dims *d, const uint16_t *d_pools,
+                            const int64_t *pool_offsets,
                             const int32_t *topk, const int32_t *slot,
                             const uint16_t *x, const uint16_t *d_shared,
                             int32_t which, const int32_t *sh_idx,

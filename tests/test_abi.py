@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(moe):
 
 
 def test_abi_version(moe):
-    assert moe.moe_abi_version() == 6
+    assert moe.moe_abi_version() == 7
 
 
 def test_capacity_matches_table(moe):
@@ -150,13 +150,27 @@ def test_backward_calls_check_arguments(moe):
     for call in (moe.MOE_CALL_COMBINE_BWD, moe.MOE_CALL_FFN_BWD, moe.MOE_CALL_PACK_BWD):
         assert moe.moe_workspace_bytes(d, call, 0) > 0
     rg = _dims(moe, cap_send=0, cap_recv=0)
-    assert L.moe_workspace_bytes(ctypes.byref(rg), moe.MOE_CALL_FFN_BWD, 0) == -2
+    # ragged: the expert call's workspace grows with its bank rows
+    small = L.moe_workspace_bytes(ctypes.byref(rg), moe.MOE_CALL_FFN_BWD, 100)
+    assert 0 < small < L.moe_workspace_bytes(ctypes.byref(rg), moe.MOE_CALL_FFN_BWD, 10000)
+    dd = _dims(moe, dedup=1)
+    assert L.moe_workspace_bytes(ctypes.byref(dd), moe.MOE_CALL_FFN_BWD, 0) == -2
     p = ctypes.c_void_p(256)
     big = 1 << 40
-    assert L.moe_combine_backward(ctypes.byref(rg), *([p] * 17), p, big, None) == -2  # ragged
-    assert L.moe_combine_backward(ctypes.byref(d), *([p] * 17), p, 16, None) == -4    # ws
-    assert L.moe_expert_ffn_backward(ctypes.byref(d), *([p] * 6), None, *([p] * 4), p, big,
-                                     None) == -1                                     # d_ret
-    assert L.moe_pack_backward(ctypes.byref(d), *([p] * 13), None, big, None) == -1  # ws NULL
+    n_ret = d.n_ranks * d.n_waves * d.cap_send
+    n_bank = d.n_waves * (d.n_experts // d.n_ranks) * d.cap_recv
+    # ragged without offsets; fixed with the wrong row count; fixed, small workspace
+    assert L.moe_combine_backward(ctypes.byref(rg), p, None, 100, *([p] * 17), big, None) == -1
+    assert L.moe_combine_backward(ctypes.byref(d), p, None, n_ret + 1, *([p] * 17), big,
+                                  None) == -1
+    assert L.moe_combine_backward(ctypes.byref(d), p, None, n_ret, *([p] * 17), 16, None) == -4
+    assert "workspace" in L.moe_last_error().decode()
+    assert L.moe_expert_ffn_backward(ctypes.byref(d), p, None, n_bank, *([p] * 5), None, n_ret,
+                                     *([p] * 5), big, None) == -1                    # d_ret
+    assert L.moe_expert_ffn_backward(ctypes.byref(rg), p, None, 100, *([p] * 6), 100,
+                                     *([p] * 5), big, None) == -1                    # offsets
+    assert L.moe_expert_ffn_backward(ctypes.byref(rg), p, p, 100, *([p] * 6), 99,
+                                     *([p] * 5), big, None) == -1                    # rows
+    assert L.moe_pack_backward(ctypes.byref(d), *([p] * 14), None, big, None) == -1  # ws NULL
     assert L.moe_route_backward(p, None, 4, 16, 17, 0, p, p, p, None) == -1          # k > E
     assert L.moe_route_backward(p, None, 4, 16, 8, 2, p, p, p, None) == -1           # flags

@@ -5,10 +5,11 @@ of its own) are checked against numbers that do not come from it:
 
 - the router's logit gradient against central finite differences of a numpy
   softmax, and against torch autograd;
-- the whole branch -- 8 ranks, exact exchanges in both directions -- against
-  torch autograd (float64, no rounding) of a plain per-token forward that
-  uses the keep decisions of the brute-force definition: every input and
-  weight gradient, summed over shards where the weight is shared.
+- the whole branch -- 8 ranks, exact exchanges in both directions, fixed
+  capacities or ragged (dropless) -- against torch autograd (float64, no
+  rounding) of a plain per-token forward that uses the keep decisions of the
+  brute-force definition: every input and weight gradient, summed over
+  shards where the weight is shared.
 
 The two sides differ only by the oracle's bf16 rounding points, so the
 comparison is per tensor within a few bf16 units; a dropped term, a wrong
@@ -94,26 +95,45 @@ def test_route_backward_finite_differences(orc, renorm, biased):
 # ----------------------------------------------------------------------------
 
 def oracle_backward(orc, cfg, d, W_, S, BK, OUT, d_out):
-    """Backward of every shard and rank with exact exchanges, from the oracle."""
+    """Backward of every shard and rank with exact exchanges, from the oracle
+    (fixed capacities, or ragged: segments at each side's offsets)."""
     R, W, Cs = cfg.n_ranks, cfg.n_waves, d.cap_send
+
+    def send_seg(s, dst, w):      # rows of shard s's pools (dst, w)
+        if Cs:
+            return slice((dst * W + w) * Cs, (dst * W + w + 1) * Cs)
+        o = S[s]["pool_offsets"]
+        return slice(int(o[dst * W + w]), int(o[dst * W + w + 1]))
+
+    # rank r's receive layout: segments (source s, wave w) of shard s's demand
+    lens = [[int(S[s]["demand"][r * W + w]) for s in range(R) for w in range(W)]
+            for r in range(R)]
+    RO = [np.concatenate([[0], np.cumsum(l)]).astype(np.int64) for l in lens]
+
+    def recv_seg(r, s, w):        # rows of rank r's receive buffer (s, w)
+        if Cs:
+            return slice((s * W + w) * Cs, (s * W + w + 1) * Cs)
+        return slice(int(RO[r][s * W + w]), int(RO[r][s * W + w + 1]))
+
+    po = lambda s: None if Cs else S[s]["pool_offsets"]
     CB = []
     for s in range(R):
         CB.append(orc.combine_backward(d, S[s]["returned"], S[s]["topk"], S[s]["slot"],
                                        S[s]["gates"], W_["x"][s], OUT[s][0], W_["wlu"],
-                                       W_["wsg"], W_["wsu"], W_["wsd"], d_out[s]))
+                                       W_["wsg"], W_["wsu"], W_["wsd"], d_out[s],
+                                       ret_offsets=po(s)))
     # return exchange, reversed: rank r's rows (s, w, i) are shard s's rows (r, w, i)
     EB = []
     for r in range(R):
-        d_ret = np.concatenate([CB[s][0][(r * W + w) * Cs:(r * W + w + 1) * Cs]
-                                for s in range(R) for w in range(W)])
+        d_ret = np.concatenate([CB[s][0][send_seg(s, r, w)] for s in range(R) for w in range(W)])
         EB.append(orc.expert_ffn_backward(d, BK[r]["bank"], BK[r]["bank_src"], BK[r]["bfill"],
-                                          *W_["ex"][r], d_ret))
+                                          *W_["ex"][r], d_ret,
+                                          bank_offsets=BK[r]["bank_offsets"]))
     PB, DL = [], []
     for s in range(R):
-        d_pools = np.concatenate([EB[r][0][(s * W + w) * Cs:(s * W + w + 1) * Cs]
-                                  for r in range(R) for w in range(W)])
+        d_pools = np.concatenate([EB[r][0][recv_seg(r, s, w)] for r in range(R) for w in range(W)])
         PB.append(orc.pack_backward(d, d_pools, S[s]["topk"], S[s]["slot"], W_["x"][s],
-                                    CB[s][2], W_["wld"], W_["wsg"], W_["wsu"]))
+                                    CB[s][2], W_["wld"], W_["wsg"], W_["wsu"], pool_offsets=po(s)))
         DL.append(orc.route_backward(W_["logits"][s], S[s]["topk"], CB[s][1]))
     return CB, EB, PB, DL
 
@@ -151,12 +171,17 @@ def torch_backward(cfg, W_, S, keep, d_out):
     return X, LG, wld, wlu, wsg, wsu, wsd, ex
 
 
-@pytest.mark.parametrize("case", ["1.10/1.15", "tight", "chunks", "t16", "t16_k1_w1_s0"])
+@pytest.mark.parametrize("case", ["1.10/1.15", "tight", "chunks", "t16", "t16_k1_w1_s0",
+                                  "ragged", "t16_ragged_w1"])
 def test_branch_backward_matches_autograd(orc, case):
     from dataclasses import replace
     from fractions import Fraction
     cfg = configs.TINY
-    if case == "t16":                 # 16 tokens per shard: the quick case
+    if case == "ragged":              # dropless: pools and bank sized from exact counts
+        cfg = replace(cfg, cf_send=None, cf_recv=None)
+    elif case == "t16_ragged_w1":
+        cfg = replace(cfg, T=16, n_waves=1, cf_send=None, cf_recv=None)
+    elif case == "t16":               # 16 tokens per shard: the quick case
         cfg = replace(cfg, T=16)
     elif case == "t16_k1_w1_s0":      # top-1, one wave, no shared experts
         cfg = replace(cfg, T=16, top_k=1, n_waves=1, n_shared=0)
@@ -297,3 +322,63 @@ def test_sampled_backward_equals_full(orc, waves):
     for which, ref in ((1, fp[3]), (2, fp[4])):
         got = orc.pack_wgrad_entries(d, d_pools, topk, slot, x, d_shared, which, cf, cb, sh)
         assert np.array_equal(got, ref[sh, cf, cb])
+
+
+def test_ragged_backward_bounds_and_sampled(orc):
+    """Ragged mode: a choice whose slot lies past its returned segment (the
+    forward read it as zero) gets gate gradient 0, writes no row and adds
+    nothing to dz; every other d_returned row stays 0.  The sampled-output
+    functions equal the full ones on the same ragged inputs."""
+    from synth import gen
+    T, D, L, E, R, k, W, S, Fs = 3, 8, 8, 8, 2, 2, 1, 1, 8
+    d = orc.Dims(T, D, L, E, R, k, W, 8, S, Fs, 0, 0, 0, 0)
+    topk = np.array([[0, 4], [1, 5], [2, 6]], np.int32)   # dest 0 and dest 1
+    slot = np.array([[0, 0], [1, 5], [2, 1]], np.int32)
+    gates = np.array([[0.5, 0.25], [1.0, 2.0], [0.75, 1.5]], np.float32)
+    offs = np.array([0, 3, 5], np.int64)                  # seg 0: 3 rows, seg 1: 2 rows
+    pay = lambda n, w, i: u16(gen.payload_rows(n, w, i))
+    returned, x, ylat, d_out = pay(5, L, 1), pay(T, D, 2), pay(T, L, 3), pay(T, D, 4)
+    wlu, wsg, wsu, wsd = pay(D, L, 5), pay(S * Fs, D, 6), pay(S * Fs, D, 7), pay(S * D, Fs, 8)
+    wsg, wsu, wsd = wsg.reshape(S, Fs, D), wsu.reshape(S, Fs, D), wsd.reshape(S, D, Fs)
+    d_ret, dg, dsh, _, _ = orc.combine_backward(d, returned, topk, slot, gates, x, ylat, wlu, wsg,
+                                                wsu, wsd, d_out, ret_offsets=offs)
+    assert dg[1, 1] == 0.0 and (dg[[0, 0, 1, 2, 2], [0, 1, 0, 0, 1]] != 0).all()
+    dyl = f64(u16(torch.from_numpy(f64(d_out) @ f64(wlu)).float().to(torch.bfloat16)))
+    for t, j, row in ((0, 0, 0), (0, 1, 3), (1, 0, 1), (2, 0, 2), (2, 1, 4)):
+        np.testing.assert_allclose(f64(d_ret[row]), gates[t, j] * dyl[t], rtol=1e-2, atol=1e-6)
+    rows, dgt, dsht = orc.combine_backward_tokens(d, returned, topk, slot, gates, x, wlu, wsg, wsu,
+                                                  wsd, d_out, np.arange(T), ret_offsets=offs)
+    assert np.array_equal(dgt, dg) and np.array_equal(dsht, dsh) and (rows[1, 1] == 0).all()
+    d_pools = pay(5, L, 9)
+    dz, dx, dwld, dwsg, dwsu = orc.pack_backward(d, d_pools, topk, slot, x, dsh, wld_t := pay(L, D, 10),
+                                                 wsg, wsu, pool_offsets=offs)
+    np.testing.assert_array_equal(f64(dz[1]), f64(d_pools[1]))   # slot 5 of seg 1 adds nothing
+    dzt, dxt = orc.pack_backward_tokens(d, d_pools, topk, slot, dsh, wld_t, wsg, wsu, np.arange(T),
+                                        pool_offsets=offs)
+    assert np.array_equal(dzt, dz) and np.array_equal(dxt, dx)
+    ra, cb = np.array([0, 3, 7]), np.array([1, 0, 6])
+    assert np.array_equal(orc.pack_wgrad_entries(d, d_pools, topk, slot, x, dsh, 0, ra, cb,
+                                                 pool_offsets=offs), dwld[ra, cb])
+    # receiver: ragged bank of 2 waves x 1 expert... one rank's groups at offsets
+    d2 = orc.Dims(T, D, L, E, R, k, 2, 8, S, Fs, 0, 0, 0, 0)
+    El = E // R
+    hdr = np.array([0, 1, 2, 3, 1, 0, 2, 2, 3, 1], np.int32)       # rank 0's experts
+    ro = np.array([0, 3, 5, 8, 10], np.int64)                      # (source, wave) segments
+    bo = orc.bank_slots(d2, 0, hdr, ro)
+    bank = pay(len(bo["bank_src"]), L, 11)
+    d_ret2 = pay(len(hdr), L, 12)
+    wg, wu, wdn = pay(El * 8, L, 13).reshape(El, 8, L), pay(El * 8, L, 14).reshape(El, 8, L), \
+        pay(El * L, 8, 15).reshape(El, L, 8)
+    fe = orc.expert_ffn_backward(d2, bank, bo["bank_src"], bo["bfill"], wg, wu, wdn, d_ret2,
+                                 bank_offsets=bo["bank_offsets"])
+    pos = np.arange(len(hdr))
+    du = orc.expert_ffn_backward_rows(d2, bank, bo["bank_src"], wg, wu, wdn, d_ret2, pos,
+                                      bank_offsets=bo["bank_offsets"])
+    assert np.array_equal(du, fe[0][bo["bank_src"][pos]])
+    for which, ref in ((0, fe[1]), (1, fe[2]), (2, fe[3])):
+        for j in range(El):
+            a, b = np.array([0, 5, 7]), np.array([0, 3, 7])
+            got = orc.expert_wgrad_entries(d2, bank, bo["bank_src"], bo["bfill"], wg, wu, wdn,
+                                           d_ret2, j, which, a, b,
+                                           bank_offsets=bo["bank_offsets"])
+            assert np.array_equal(got, ref[j, a, b]), (which, j)
