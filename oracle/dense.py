@@ -211,14 +211,18 @@ def expert_wgrad_rows(u: np.ndarray, dy: np.ndarray, wg_t, wu_t, wd_t, f_idx):
       dw_gate[f] = bf16(sum_r d_a u), dw_up[f] = bf16(sum_r d_b u),
       dw_down[:, f] = bf16(sum_r dy h[f])."""
     f_idx = np.asarray(f_idx, np.int64)
-    U, DY = to_f64(u), to_f64(dy)
-    a = U @ to_f64(wg_t[f_idx]).T
-    b = U @ to_f64(wu_t[f_idx]).T
-    dh = to_f64(bf16_from_f64(DY @ to_f64(wd_t[:, f_idx])))
-    da = to_f64(bf16_from_f64(dh * b * _silu_grad(a)))
-    db = to_f64(bf16_from_f64(dh * _silu(a)))
-    h = to_f64(bf16_from_f64(_silu(a) * b))
-    return outer_rows(da, U), outer_rows(db, U), outer_rows(h, DY)
+    wg, wu, wd = to_f64(wg_t[f_idx]), to_f64(wu_t[f_idx]), to_f64(wd_t[:, f_idx])
+    L = u.shape[1]
+    gg, gu, gd = (np.zeros((len(f_idx), L)) for _ in range(3))
+    for s, e in _rows(u.shape[0]):          # float64 sums over the rows, chunk by chunk
+        U, DY = to_f64(u[s:e]), to_f64(dy[s:e])
+        a = U @ wg.T
+        b = U @ wu.T
+        dh = to_f64(bf16_from_f64(DY @ wd))
+        gg += to_f64(bf16_from_f64(dh * b * _silu_grad(a))).T @ U
+        gu += to_f64(bf16_from_f64(dh * _silu(a))).T @ U
+        gd += to_f64(bf16_from_f64(_silu(a) * b)).T @ DY
+    return bf16_from_f64(gg), bf16_from_f64(gu), bf16_from_f64(gd)
 
 
 def shared_down_wgrad_cols(x, ws_gate, ws_up, d_out, sh: int, f_idx):
@@ -231,10 +235,11 @@ def shared_down_wgrad_cols(x, ws_gate, ws_up, d_out, sh: int, f_idx):
     return outer_rows(to_f64(bf16_from_f64(_silu(a) * b)), to_f64(d_out))
 
 
-def pack_dz(d, d_pools, topk, slot) -> np.ndarray:
-    """dz[t] = bf16(sum over kept (t, j) of d_pools[row(t, j)]) (fixed mode,
-    orc_pack_backward; j ascending)."""
-    rows = returned_rows(d, None, topk, slot, np.arange(d.T))
+def pack_dz(d, d_pools, topk, slot, pool_offsets=None) -> np.ndarray:
+    """dz[t] = bf16(sum over kept (t, j) of d_pools[row(t, j)])
+    (orc_pack_backward; j ascending; ragged: segments at pool_offsets, a slot
+    past its segment adds nothing)."""
+    rows = returned_rows(d, pool_offsets, topk, slot, np.arange(d.T))
     acc = np.zeros((d.T, d.latent))
     for j in range(d.top_k):
         m = rows[:, j] >= 0

@@ -276,3 +276,27 @@ def test_pack_wgrad_rows_match_c_oracle(orc):
         f = np.array([1, d.d_ff_shared - 1])
         _close_to_c(dense.outer_rows(f64(w["d_shared"][:, 0, sh, f]), f64(w["x"])), dwsg[sh][f])
         _close_to_c(dense.outer_rows(f64(w["d_shared"][:, 1, sh, f]), f64(w["x"])), dwsu[sh][f])
+
+
+def test_expert_wgrad_rows_over_chunks_match_c_oracle(orc):
+    """More bank rows than one float64 chunk of dense.py: the sums over
+    chunks still give oracle.c's entries."""
+    rng = np.random.default_rng(23)
+    n, L, F = 4500, 64, 128
+    d = orc.Dims(8, 64, L, 4, 4, 1, 1, F, 0, 128, 4500, n, 0, 0)   # one expert per rank, one wave
+    bank = _rand_bits(rng, (n, L))
+    d_ret = _rand_bits(rng, (n, L))
+    wg = _rand_bits(rng, (1, F, L), L ** -0.5)
+    wu = _rand_bits(rng, (1, F, L), L ** -0.5)
+    wd = _rand_bits(rng, (1, L, F), F ** -0.5)
+    src, fill = np.arange(n, dtype=np.int32), np.array([n], np.int32)
+    f = np.array([0, 77, F - 1])
+    g, u, dn = dense.expert_wgrad_rows(bank, d_ret, wg[0], wu[0], wd[0], f)
+    cols = np.arange(L)
+    for which, got in ((0, g), (1, u)):
+        ref = np.stack([orc.expert_wgrad_entries(d, bank, src, fill, wg, wu, wd, d_ret, 0, which,
+                                                 np.full(L, fi), cols) for fi in f])
+        _close_to_c(got, ref, min_equal=0.98)
+    ref = np.stack([orc.expert_wgrad_entries(d, bank, src, fill, wg, wu, wd, d_ret, 0, 2, cols,
+                                             np.full(L, fi)) for fi in f])
+    _close_to_c(dn, ref, min_equal=0.98)

@@ -98,6 +98,12 @@ MUTATIONS = [
      "               0.0 * bf(ws_up[wi]);", BWD),
     ("expert down grad with u for h", "gd[j * WL + (int64_t)l * F + f] += dy[l] * h[f];",
      "gd[j * WL + (int64_t)l * F + f] += dy[l] * u[f % L];", BWD),
+    ("ragged: no segment bound", "  if (s >= offsets[seg + 1] - offsets[seg]) return -1;\n",
+     "", "test_oracle_backward.py::test_ragged_backward_bounds_and_sampled"),
+    ("ragged bank groups read at fixed positions",
+     "  return d->cap_send ? (int64_t)g * d->cap_recv : bank_offsets[g];",
+     "  return (int64_t)g * d->cap_recv;",
+     "test_oracle_backward.py::test_branch_backward_matches_autograd[t16_ragged_w1]"),
 ]
 
 
