@@ -248,3 +248,179 @@ def test_full_expert_backward_skewed(moe_lib, orc):
         gots = (gw[0][j][fi], gw[1][j][fi], np.ascontiguousarray(gw[2][j][:, fi].T))
         for what, got, ref in zip(("dw_gate", "dw_up", "dw_down^T"), gots, refs):
             gc.assert_rows_close(got, ref, f"{what} rows of expert {j}")
+
+
+def _threaded(fn, tokens, parts=16):
+    """fn(tokens chunk) -> tuple of arrays, run on chunks in threads (the C
+    oracle releases the interpreter lock), results concatenated."""
+    from concurrent.futures import ThreadPoolExecutor
+    chunks = [c for c in np.array_split(np.asarray(tokens), parts) if len(c)]
+    with ThreadPoolExecutor(len(chunks)) as ex:
+        res = list(ex.map(fn, chunks))
+    return tuple(np.concatenate([r[i] for r in res]) for i in range(len(res[0])))
+
+
+def test_full_backward_ragged_hot(moe_lib, orc):
+    """Dropless (ragged) backward at full size: the 16384-token Zipf
+    workload's most-loaded rank, with the receive layout the oracle's routing
+    of all 64 shards gives it, a few experts taking most of its rows.  The
+    expert backward runs over that receive layout (segments per source shard
+    and wave); the combine and pack backwards over the rank's own shard as a
+    sender (segments per destination and wave, at its pool offsets).  Stage
+    inputs are generator rows in those layouts.  Zero rows and zero gate
+    gradients in full; sampled tokens and bank rows against the oracle; whole
+    rows of every weight gradient against oracle/dense.py."""
+    import fullcheck as fc
+    from dispatch_softmax_top_amd import share
+    moe = moe_lib
+    cfg = configs.SWEEP_16K["inf"]
+    rng = np.random.default_rng(zlib.crc32(b"ragged backward"))
+    d_orc, d = orc.dims(cfg), share.make_dims(cfg)
+    T, L, D, S, Fs, k = cfg.T, cfg.latent, cfg.d_model, cfg.n_shared, cfg.d_ff_shared, cfg.top_k
+    El, F, W = cfg.experts_per_rank, cfg.d_ff, cfg.n_waves
+    print("\n[full backward] ragged hot rank: routing of every shard", flush=True)
+    wr = gen.router_weight(cfg, "cuda")
+    logits = [gen.logits(cfg, s, gen.hidden(cfg, s, "cuda"), wr).cpu().numpy()
+              for s in range(cfg.n_shards)]
+    shards = fc.oracle_shards(orc, cfg, d_orc, logits)
+    rank = fc.hot_rank(cfg, d_orc, shards)
+    rm = fc.RecvMap(cfg, d_orc, shards, rank)
+    own, lg = shards[rank], logits[rank]
+    del logits
+    topk, slot, gates, fill = own["topk"], own["slot"], own["gates"], own["fill"]
+    po, n_s, n = own["pool_offsets"], int(own["pool_offsets"][-1]), rm.n
+    x_t = gen.hidden(cfg, rank, "cuda")
+    x = u16(x_t)
+    wlu, wld = u16(gen.latent_up(cfg)), u16(gen.latent_down(cfg))
+    wsg, wsu, wsd = (u16(w) for w in gen.shared(cfg))
+    dev = lambda a: gc.dev(np.ascontiguousarray(a))
+    ws = lambda call, rows=0: torch.empty(max(moe.moe_workspace_bytes(d, call, rows), 16),
+                                          dtype=torch.uint8, device="cuda")
+    Tw = math.ceil(T / W)
+    tok = np.unique(np.concatenate([[0, T - 1], [w * Tw - 1 for w in range(1, W)],
+                                    [w * Tw for w in range(1, W)], rng.integers(0, T, 96)]))
+    print(f"[full backward] ragged: rank {rank}, {n} receive rows, {n_s} sent rows, combine",
+          flush=True)
+
+    # ---- combine side
+    returned = gen.payload_rows(n_s, L, 91, "cuda")
+    ylat, d_out = gen.payload_rows(T, L, 92, "cuda"), gen.payload_rows(T, D, 93, "cuda")
+    d_ret = torch.full((n_s, L), 3.0, dtype=torch.bfloat16, device="cuda")
+    d_g = torch.full((T, k), 5.0, device="cuda")
+    d_sh = torch.empty((T, 2, S, Fs), dtype=torch.bfloat16, device="cuda")
+    dwlu = torch.empty((D, L), dtype=torch.bfloat16, device="cuda")
+    dwsd = torch.empty((S, D, Fs), dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine_backward(d, returned, dev(topk), dev(slot), dev(gates), dev(fill), x_t, ylat,
+                             dev(wlu), dev(wsg), dev(wsu), dev(wsd), d_out, d_ret, d_g, d_sh,
+                             dwlu, dwsd, ws(moe.MOE_CALL_COMBINE_BWD), ret_offsets=dev(po))
+    torch.cuda.synchronize()
+    h_ret, h_ylat, h_dout = u16(returned), u16(ylat), u16(d_out)
+    del returned
+    rows_all = dense.returned_rows(d_orc, po, topk, slot, np.arange(T))
+    written = torch.zeros(n_s, dtype=torch.bool, device="cuda")
+    w_rows = rows_all[rows_all >= 0]
+    written[torch.from_numpy(w_rows).cuda()] = True
+    assert bool((d_ret[~written].view(torch.int16) == 0).all()), "unwritten d_returned rows"
+    g_dg = gc.host(d_g)
+    assert (g_dg[rows_all < 0] == 0).all()
+    o_rows, o_dg, o_dsh = _threaded(
+        lambda c: orc.combine_backward_tokens(d_orc, h_ret, topk, slot, gates, x, wlu, wsg, wsu,
+                                              wsd, h_dout, c, ret_offsets=po), tok)
+    g_dret = gc.host(d_ret[torch.from_numpy(np.maximum(rows_all[tok], 0)).cuda().reshape(-1)])
+    g_dret = g_dret.reshape(len(tok), k, L)
+    live = rows_all[tok] >= 0
+    gc.assert_rows_close(g_dret[live], o_rows[live], "d_returned (sampled tokens)")
+    y = f64(h_dout[tok]) @ f64(wlu)
+    tol = 2e-3 * np.abs(f64(h_ret[w_rows])).max() * np.abs(y).sum(1, keepdims=True)
+    assert (np.abs(g_dg[tok] - o_dg) <= tol).all()
+    gc.assert_rows_close(gc.host(d_sh)[tok].reshape(len(tok), -1), o_dsh.reshape(len(tok), -1),
+                         "d_shared")
+    ra = np.unique(np.concatenate([[0, D - 1], rng.integers(0, D, 6)]))
+    gc.assert_rows_close(gc.host(dwlu)[ra], dense.outer_rows(f64(h_dout[:, ra]), f64(h_ylat)),
+                         "dw_lat_up rows")
+    g_dwsd = gc.host(dwsd)
+    for sh in range(S):
+        cf = np.unique(np.concatenate([[0, Fs - 1], rng.integers(0, Fs, 3)]))
+        gc.assert_rows_close(np.ascontiguousarray(g_dwsd[sh][:, cf].T),
+                             dense.shared_down_wgrad_cols(x, wsg, wsu, h_dout, sh, cf),
+                             f"dws_down[{sh}] columns")
+    del d_ret, h_ret
+    torch.cuda.empty_cache()
+
+    # ---- receiver side
+    print("[full backward] ragged: experts", flush=True)
+    bo = orc.bank_slots(d_orc, rank, rm.hdr, rm.starts)
+    nb = len(bo["bank_src"])
+    assert nb == n and int(bo["bfill"].sum()) == int((rm.hdr >= 0).sum())
+    bank, dret = gen.payload_rows(nb, L, 94, "cuda"), gen.payload_rows(n, L, 95, "cuda")
+    wg, wu, wdn = gen.rank_experts(cfg, rank)
+    d_recv = torch.full((n, L), 2.0, dtype=torch.bfloat16, device="cuda")
+    dwg = torch.empty((El, F, L), dtype=torch.bfloat16, device="cuda")
+    dwu = torch.empty_like(dwg)
+    dwd = torch.empty((El, L, F), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_ffn_backward(d, bank, dev(bo["bank_src"]), dev(bo["bfill"]), wg.cuda(),
+                                wu.cuda(), wdn.cuda(), dret, d_recv, dwg, dwu, dwd,
+                                ws(moe.MOE_CALL_FFN_BWD, nb),
+                                bank_offsets=dev(bo["bank_offsets"]))
+    torch.cuda.synchronize()
+    kept = torch.zeros(n, dtype=torch.bool, device="cuda")
+    kept[torch.from_numpy(bo["bank_src"][bo["bank_src"] >= 0]).cuda().long()] = True
+    assert bool((d_recv[~kept].view(torch.int16) == 0).all())
+    h_bank, h_dret = u16(bank), u16(dret)
+    del bank, dret
+    boff, bfill = bo["bank_offsets"], bo["bfill"]
+    edges = [int(boff[g]) + p for g in range(W * El) if bfill[g] > 0
+             for p in (0, int(bfill[g]) - 1)]
+    pos = np.unique(np.concatenate([edges, rng.choice(np.nonzero(bo["bank_src"] >= 0)[0], 48)]))
+    ex = [u16(w) for w in (wg, wu, wdn)]
+    (du,) = _threaded(lambda c: (orc.expert_ffn_backward_rows(d_orc, h_bank, bo["bank_src"], *ex,
+                                                             h_dret, c, bank_offsets=boff),), pos)
+    gc.assert_rows_close(gc.host(d_recv[torch.from_numpy(bo["bank_src"][pos]).cuda().long()]),
+                         du, "d_recv (sampled bank rows)")
+    gw = [gc.host(t) for t in (dwg, dwu, dwd)]
+    rows_j = [int(bfill[j::El].sum()) for j in range(El)]
+    for j in range(El):
+        if rows_j[j] == 0:
+            assert all((g_[j] == 0).all() for g_ in gw), f"expert {j} has no rows"
+            continue
+        fi = np.unique(np.concatenate([[0, F - 1], rng.integers(0, F, 2)]))
+        pos_j = np.concatenate([np.arange(int(boff[g]), int(boff[g]) + int(bfill[g]))
+                                for g in range(j, W * El, El)])
+        refs = dense.expert_wgrad_rows(h_bank[pos_j], h_dret[bo["bank_src"][pos_j]],
+                                       *(w[j] for w in ex), fi)
+        gots = (gw[0][j][fi], gw[1][j][fi], np.ascontiguousarray(gw[2][j][:, fi].T))
+        for what, got, ref in zip(("dw_gate", "dw_up", "dw_down^T"), gots, refs):
+            gc.assert_rows_close(got, ref, f"{what} rows of expert {j} ({rows_j[j]} rows)")
+    del d_recv, h_bank
+    torch.cuda.empty_cache()
+
+    # ---- sender side (pool-row gradients in the receive layout)
+    print("[full backward] ragged: pack", flush=True)
+    d_pools = gen.payload_rows(n_s, L, 96, "cuda")
+    d_shared = gen.payload_rows(T, 2 * S * Fs, 97, "cuda")
+    b = share.Backward(d, 1)
+    moe.moe_pack_backward(d, d_pools, dev(topk), dev(slot), x_t, d_shared, dev(wld), dev(wsg),
+                          dev(wsu), b.dz, b.dx, b.dw_lat_down, b.dws_gate, b.dws_up,
+                          ws(moe.MOE_CALL_PACK_BWD), pool_offsets=dev(po))
+    torch.cuda.synchronize()
+    h_dp, h_dsh = u16(d_pools), u16(d_shared)
+    dz_all = dense.pack_dz(d_orc, h_dp, topk, slot, pool_offsets=po)
+    gz = gc.host(b.dz)
+    nz = np.abs(f64(dz_all)).any(1)
+    assert (gz[~nz] == 0).all()
+    gc.assert_rows_close(gz[nz], dz_all[nz], "dz (every token)")
+    o_dz, o_dx = _threaded(lambda c: orc.pack_backward_tokens(d_orc, h_dp, topk, slot, h_dsh, wld,
+                                                              wsg, wsu, c, pool_offsets=po), tok)
+    assert np.array_equal(o_dz, dz_all[tok])
+    gc.assert_rows_close(gc.host(b.dx)[tok], o_dx, "dx (sampled tokens)")
+    ra = np.unique(np.concatenate([[0, L - 1], rng.integers(0, L, 6)]))
+    gc.assert_rows_close(gc.host(b.dw_lat_down)[ra], dense.outer_rows(f64(dz_all[:, ra]), f64(x)),
+                         "dw_lat_down rows")
+    dsh4 = h_dsh.reshape(T, 2, S, Fs)
+    for which, got in ((0, b.dws_gate), (1, b.dws_up)):
+        g_ = gc.host(got)
+        for sh in range(S):
+            r2 = np.unique(np.concatenate([[0, Fs - 1], rng.integers(0, Fs, 3)]))
+            gc.assert_rows_close(g_[sh][r2], dense.outer_rows(f64(dsh4[:, which, sh, r2]), f64(x)),
+                                 f"shared weight {which} rows of expert {sh}")
+    print(f"[full backward] ragged hot rank {rank}: every check passes", flush=True)
