@@ -78,16 +78,19 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float((uint32_t)b << 16);
 }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest even (NaN stays NaN): gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32) under the default rounding mode, two
+// values per instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
@@ -135,7 +138,12 @@ __device__ __forceinline__ uint64_t match_key(uint32_t key, int bits) {
   return m;
 }
 
-__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
+// Logistic sigmoid and silu(a) = a * sigmoid(a), with the hardware exp2 and
+// reciprocal (each within about one ulp; the results are rounded to bf16).
+__device__ __forceinline__ float sigmoid_f32(float a) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
+__device__ __forceinline__ float silu_f32(float a) { return a * sigmoid_f32(a); }
 
 // Dispatch order of workgroups is round-robin over the 8 XCDs.  Map the
 // hardware block id to a logical tile id so that each XCD gets one

@@ -522,6 +522,81 @@ __device__ __forceinline__ bool group_tile_at(const GroupArgs &a, int tn, int re
   return false;
 }
 
+// The same table read into registers once per wave (at most 64 bank groups
+// and 64 product groups): lane g holds bank group g's row count and first
+// row, lane pg the first logical tile of product group pg.  One round of
+// independent loads, where the walk above waits for one load after another
+// (bank counts written by an earlier kernel sit in another XCD's L2, about a
+// microsecond away).  With more groups the walk is used.
+struct GroupRegs {
+  bool fast;
+  int total;      // tiles (wave-uniform)
+  int count;      // lane g: rows of bank group g
+  int64_t start;  // lane g: first bank row of bank group g
+  int prefix;     // lane pg: tiles of the product groups before pg
+};
+
+__device__ __forceinline__ GroupRegs group_regs(const GroupArgs &a, int tn) {
+  GroupRegs r{};
+  const int npg = a.G / a.nw;
+  r.fast = a.G <= 64;
+  if (!r.fast) {
+    r.total = group_total(a, tn);
+    return r;
+  }
+  const int l = lane_id();
+  r.count = l < a.G ? a.count[l] : 0;
+  r.start = l < a.G ? (a.offsets ? a.offsets[l] : (int64_t)l * a.cap) : 0;
+  int rows = 0;
+  for (int s = 0; s < a.nw; ++s) rows += __shfl(r.count, l < npg ? group_seg(a, l, s) : 0);
+  const int tiles = l < npg ? (rows + GBM - 1) / GBM * tn : 0;
+  int inc = tiles;  // inclusive prefix over the lanes
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(inc, d);
+    if (l >= d) inc += v;
+  }
+  r.prefix = inc - tiles;
+  r.total = __builtin_amdgcn_readlane(inc, 63);
+  return r;
+}
+
+// group_tile_at from the registers.
+__device__ __forceinline__ bool group_tile_regs(const GroupArgs &a, const GroupRegs &r, int tn,
+                                                int rem, GTile &t) {
+  if (!r.fast) return group_tile_at(a, tn, rem, t);
+  t.rows = 0;
+  if (rem < 0 || rem >= r.total) return false;
+  const int npg = a.G / a.nw;
+  // prefixes never decrease: the last group starting at or before rem holds it
+  const uint64_t m = __ballot(lane_id() < npg && r.prefix <= rem);
+  const int pg = __builtin_amdgcn_readfirstlane(63 - __clzll(m));
+  rem -= __builtin_amdgcn_readlane(r.prefix, pg);
+  int c = 0;
+  for (int s = 0; s < a.nw; ++s) c += __builtin_amdgcn_readlane(r.count, group_seg(a, pg, s));
+  const int tmg = (c + GBM - 1) / GBM;
+  g_tile_coords(rem, tmg, tn, t.mt, t.nt);
+  t.expert = group_seg(a, pg, 0) % a.El;
+  t.v0 = t.mt * GBM;
+  t.rows = min(GBM, c - t.v0);
+  t.nseg = a.nw;
+  int cum = 0;
+#pragma unroll
+  for (int s = 0; s < GMAXW; ++s) {
+    if (s < a.nw) {
+      const int g = group_seg(a, pg, s);
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)r.start, g);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)r.start >> 32), g);
+      t.start[s] = (int64_t)(((uint64_t)hi << 32) | lo);
+      cum += __builtin_amdgcn_readlane(r.count, g);
+    } else {
+      t.start[s] = 0;
+    }
+    t.cum[s] = cum;
+  }
+  return t.rows > 0;
+}
+
 // ---------------------------------------------------------------------------
 // SwiGLU
 // ---------------------------------------------------------------------------
@@ -552,10 +627,11 @@ struct SwigluArgs {
 
 // row_of(m): row of A and H for tile row m < rows (contiguous rows, or the
 // bank rows of a grouped tile).  K tiles [k0, k1) into acc.
+typedef GOps<GOperand<GCA>, GOperand<GCB>> GOps2;
+
 template <class RowOf>
-__device__ __forceinline__ void swiglu_acc(const SwigluArgs &g, RowOf row_of, int rows, int expert,
-                                           int ft, int k0, int k1, const GemmLds &lds,
-                                           GAcc &acc) {
+__device__ __forceinline__ GOps2 swiglu_ops(const SwigluArgs &g, RowOf row_of, int rows,
+                                            int expert, int ft, int k0) {
   const int f0 = ft * 128;
   const int64_t eoff = (int64_t)expert * g.F * g.ldb + (int64_t)f0 * g.ldb + k0 * GBK;
   // whether a thread copies gate or up rows depends on the thread only (its
@@ -565,7 +641,7 @@ __device__ __forceinline__ void swiglu_acc(const SwigluArgs &g, RowOf row_of, in
   int foff;
   g_swiglu_brow(g_load_row(0), up, foff);
   const int64_t r0 = row_of(0);
-  const auto ops = g_operands(
+  return g_operands(
       g.A + r0 * g.lda + k0 * GBK, g.lda,
       [&](int r) { return (int)(row_of(min(r, rows - 1)) - r0); }, (up ? g.Bu : g.Bg) + eoff,
       g.ldb, [&](int r) {
@@ -574,6 +650,13 @@ __device__ __forceinline__ void swiglu_acc(const SwigluArgs &g, RowOf row_of, in
         g_swiglu_brow(r, u, f);
         return f;
       });
+}
+
+template <class RowOf>
+__device__ __forceinline__ void swiglu_acc(const SwigluArgs &g, RowOf row_of, int rows, int expert,
+                                           int ft, int k0, int k1, const GemmLds &lds,
+                                           GAcc &acc) {
+  const auto ops = swiglu_ops(g, row_of, rows, expert, ft, k0);
   gemm_zero(acc);
   gemm_mainloop(ops, k1 - k0, acc, lds);
 }
@@ -592,12 +675,11 @@ __device__ __forceinline__ void swiglu_store(const SwigluArgs &g, RowOf row_of, 
     static_assert(GTN == 2, "one gate and one up tile per wave");
     const int w = (int)(threadIdx.x >> 6);
     const int m0 = (w / GWN) * GWTM, c0 = h_col0 + f0 + (w % GWN) * (GWTN / 2);
-    g_wave_store<1>(
-        ring, [&](int i, int, int v) { return silu_f32(acc[i][0][v]) * acc[i][1][v]; },
-        [&](int r) -> uint16_t * {
-          return m0 + r < rows ? g.H + row_of(m0 + r) * g.ldh + c0 : nullptr;
-        },
-        GWTN / 2);
+    const auto val = [&](int i, int, int v) { return silu_f32(acc[i][0][v]) * acc[i][1][v]; };
+    const auto row_ptr = [&](int r) -> uint16_t * {
+      return m0 + r < rows ? g.H + row_of(m0 + r) * g.ldh + c0 : nullptr;
+    };
+    g_wave_store<1>(ring, val, row_ptr, GWTN / 2);
     return;
   }
 #pragma unroll
@@ -633,8 +715,8 @@ __device__ __forceinline__ void swiglu_store(const SwigluArgs &g, RowOf row_of, 
         for (int p = 0; p < GTN / 2; ++p) {
           const float a = acc[i][2 * p][v], b = acc[i][2 * p + 1][v];
           const int c = g_swiglu_col(p);
-          const float s = 1.0f / (1.0f + __expf(-a));
-          const float sa = silu_f32(a);
+          const float s = sigmoid_f32(a);
+          const float sa = a * s;
           h[c] = f32_to_bf16(sa * b);
           da[c] = f32_to_bf16(gh[v][p] * b * (s * (1.0f + a * (1.0f - s))));
           da[g.ab_off + c] = f32_to_bf16(gh[v][p] * sa);
@@ -689,10 +771,10 @@ __global__ __launch_bounds__(GNT) void gemm_shared_swiglu_tail_kernel(SwigluArgs
 template <bool BWD>
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_swiglu_kernel(SwigluArgs g) {
   MOE_GEMM_LDS(lds);
+  const GroupRegs gr = group_regs(g.grp, g.ftiles);
   GUnit u;
   GTile t;
-  if (!g_unit(g.sp, group_total(g.grp, g.ftiles), blockIdx.x, u) ||
-      !group_tile_at(g.grp, g.ftiles, u.tile, t))
+  if (!g_unit(g.sp, gr.total, blockIdx.x, u) || !group_tile_regs(g.grp, gr, g.ftiles, u.tile, t))
     return;
   const auto row_of = [&](int m) { return t.row(m); };
   int k0, k1;
@@ -710,8 +792,9 @@ template <bool BWD>
 __global__ __launch_bounds__(GNT) void gemm_expert_swiglu_tail_kernel(SwigluArgs g) {
   GUnit u;
   GTile t;
-  if (!g_tail_tile(g.sp, group_total(g.grp, g.ftiles), blockIdx.x / GTM, u) ||
-      !group_tile_at(g.grp, g.ftiles, u.tile, t))
+  const GroupRegs gr = group_regs(g.grp, g.ftiles);
+  if (!g_tail_tile(g.sp, gr.total, blockIdx.x / GTM, u) ||
+      !group_tile_regs(g.grp, gr, g.ftiles, u.tile, t))
     return;
   const auto row_of = [&](int m) { return t.row(m); };
   GAcc acc;
@@ -777,8 +860,8 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
   MOE_GEMM_LDS(lds);
   GUnit u;
   GTile t;
-  if (!g_unit(g.sp, group_total(g.grp, g.tn), blockIdx.x, u) ||
-      !group_tile_at(g.grp, g.tn, u.tile, t))
+  const GroupRegs gr = group_regs(g.grp, g.tn);
+  if (!g_unit(g.sp, gr.total, blockIdx.x, u) || !group_tile_regs(g.grp, gr, g.tn, u.tile, t))
     return;
   const uint16_t *W = g.Wd + (int64_t)t.expert * g.L * g.F;
   const int nv = g.L - t.nt * GBN, rows = t.rows;
@@ -813,8 +896,9 @@ __global__ __launch_bounds__(GNT) void gemm_expert_down_tail_kernel(DownArgs g) 
   __shared__ int32_t dst_rows[GBM];
   GUnit u;
   GTile t;
-  if (!g_tail_tile(g.sp, group_total(g.grp, g.tn), blockIdx.x / GTM, u) ||
-      !group_tile_at(g.grp, g.tn, u.tile, t))
+  const GroupRegs gr = group_regs(g.grp, g.tn);
+  if (!g_tail_tile(g.sp, gr.total, blockIdx.x / GTM, u) ||
+      !group_tile_regs(g.grp, gr, g.tn, u.tile, t))
     return;
   if ((int)threadIdx.x < GBM)
     dst_rows[threadIdx.x] = (int)threadIdx.x < t.rows ? g.bank_src[t.row(threadIdx.x)] : -1;
