@@ -403,30 +403,48 @@ __device__ __forceinline__ void g_pp_tile_g1(const Ops &o, int s, int ktiles, GA
   if (s + 1 < ktiles) g_pp_sync();
 }
 
-// Accumulate ktiles K tiles (GBK wide) of the two operands.
+// The main loop in two parts.  gemm_mainloop_issue issues the copies of the
+// first K tiles (everything before the loop's first wait); gemm_mainloop_rest
+// runs the rest.  A block that runs several tiles issues the first copies of
+// its next tile before the epilogue of the current one, so their latency
+// hides behind it; stage GNST - 1 is not written until the rest's first
+// barriers (the epilogue's staging area meanwhile).  Other memory operations issued between
+// the two parts only make the rest's vmcnt waits wait longer: copies
+// complete in issue order, so "at most n outstanding" still implies that the
+// older copies landed.
 template <class Ops>
-__device__ __forceinline__ void gemm_mainloop(const Ops &o, int ktiles, GAcc &acc,
-                                              const GemmLds &L) {
-  __builtin_amdgcn_s_barrier();  // the ring may still be read from a previous call
-  __builtin_amdgcn_sched_barrier(0);
+__device__ __forceinline__ void gemm_mainloop_issue(const Ops &o, int ktiles, const GemmLds &L) {
+  if (ktiles <= 0) return;
   if constexpr (!GPP) {
-    if (ktiles > 0) {
-      g_copy_operand(o.a, 0, L.A[0]);
-      g_copy_operand(o.b, 0, L.B[0]);
-    }
+    g_copy_operand(o.a, 0, L.A[0]);
+    g_copy_operand(o.b, 0, L.B[0]);
+  } else if (g_group1()) {
+    // A of tiles 0..3
+#pragma unroll
+    for (int p = 0; p < GPP_AHEAD; ++p)
+      if (p < ktiles) g_copy_operand(o.a, p, L.A[p]);
+  } else {
+    // B of tiles 0..2 (tile 3 follows the first barrier)
+#pragma unroll
+    for (int p = 0; p < GPP_AHEAD - 1; ++p)
+      if (p < ktiles) g_copy_operand(o.b, p, L.B[p]);
+  }
+}
+
+template <class Ops>
+__device__ __forceinline__ void gemm_mainloop_rest(const Ops &o, int ktiles, GAcc &acc,
+                                                   const GemmLds &L) {
+  if (ktiles <= 0) return;
+  if constexpr (!GPP) {
     for (int kt = 0; kt < ktiles; kt += 2) {
       g_ring_step<0>(o, kt, ktiles, acc, L);
       g_ring_step<1>(o, kt + 1, ktiles, acc, L);
     }
   } else {
-    if (ktiles <= 0) return;
     // The two groups run separate loops with the same sequence of barriers.
     bf16x8 a[2][GTM], b[2][GTN];
     if (g_group1()) {
-      // prologue: A of tiles 0..3; tile 0 landed; phase -1 idle
-#pragma unroll
-      for (int p = 0; p < GPP_AHEAD; ++p)
-        if (p < ktiles) g_copy_operand(o.a, p, L.A[p]);
+      // tile 0 landed; phase -1 idle
       g_wait_tiles<GCA>(min(GPP_AHEAD - 1, ktiles - 1));
       g_pp_sync();
       g_pp_sync();
@@ -438,11 +456,7 @@ __device__ __forceinline__ void gemm_mainloop(const Ops &o, int ktiles, GAcc &ac
         g_pp_tile_g1<4>(o, s + 4, ktiles, acc, L, a, b);
       }
     } else {
-      // prologue: B of tiles 0..2; tile 0 landed; phase -1: B of tile 3 and
-      // the fragments of tile 0
-#pragma unroll
-      for (int p = 0; p < GPP_AHEAD - 1; ++p)
-        if (p < ktiles) g_copy_operand(o.b, p, L.B[p]);
+      // tile 0 landed; phase -1: B of tile 3 and the fragments of tile 0
       g_wait_tiles<GCB>(min(GPP_AHEAD - 2, ktiles - 1));
       g_pp_sync();
       if (GPP_AHEAD - 1 < ktiles) g_copy_operand(o.b, GPP_AHEAD - 1, L.B[GPP_AHEAD - 1]);
@@ -457,6 +471,16 @@ __device__ __forceinline__ void gemm_mainloop(const Ops &o, int ktiles, GAcc &ac
       }
     }
   }
+}
+
+// Accumulate ktiles K tiles (GBK wide) of the two operands.
+template <class Ops>
+__device__ __forceinline__ void gemm_mainloop(const Ops &o, int ktiles, GAcc &acc,
+                                              const GemmLds &L) {
+  __builtin_amdgcn_s_barrier();  // the ring may still be read from a previous call
+  __builtin_amdgcn_sched_barrier(0);
+  gemm_mainloop_issue(o, ktiles, L);
+  gemm_mainloop_rest(o, ktiles, acc, L);
 }
 
 __device__ __forceinline__ void gemm_zero(GAcc &acc) {
@@ -497,7 +521,7 @@ __device__ __forceinline__ int g_acc_col(int j) {
 // loop's last barrier, which every wave has passed on return, so no barrier is
 // needed here; the two-stage loop gets one.
 constexpr int GSTAGE = GNT / 64 * GWTM * GWTN;  // elements of the largest regions
-static_assert(GSTAGE + 2 * GBM <= GNST * (GSA + GSB), "store regions + 256 row indices");
+static_assert(GSTAGE <= GNST * (GSA + GSB), "store regions inside the ring");
 
 template <int NJ>
 __device__ __forceinline__ int g_stage_chunk(int row, int c) {
@@ -508,19 +532,21 @@ __device__ __forceinline__ int g_stage_chunk(int row, int c) {
 // 2k + 1 (high half) of MFMA tile (i, j) of this wave; row_ptr(r): output row
 // of wave-tile row r at the wave's first column (nullptr: row not stored),
 // 16-byte aligned; ncols: valid columns from there (a multiple of 8).  Every
-// lane of the wave must call it.
-template <int NJ, class Pair, class RowPtr>
+// lane of the wave must call it.  Row groups I0 .. I0 + NI - 1 only, staged
+// in a region of NI * 32 rows per wave.
+template <int NJ, int I0 = 0, int NI = GTM, class Pair, class RowPtr>
 __device__ __forceinline__ void g_wave_store_pairs(uint16_t *ring, Pair pair, RowPtr row_ptr,
                                                    int ncols) {
   static_assert(NJ == 1 || NJ == 2, "32 or 64 columns per wave");
-  constexpr int W = NJ * 32, CH = W / 8;
+  static_assert(I0 >= 0 && NI >= 1 && I0 + NI <= GTM, "row groups of the wave tile");
+  constexpr int W = NJ * 32, CH = W / 8, ROWS = NI * 32;
   if constexpr (!GPP) __syncthreads();
   const int lane = lane_id();
-  uint16_t *st = ring + (threadIdx.x >> 6) * (GWTM * W);
+  uint16_t *st = ring + (threadIdx.x >> 6) * (ROWS * W);
   const bool b1 = lane & 2, b0 = lane & 1;
   const int col4 = (lane & 31) & ~3;
 #pragma unroll
-  for (int i = 0; i < GTM; ++i)
+  for (int i = I0; i < I0 + NI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -544,7 +570,7 @@ __device__ __forceinline__ void g_wave_store_pairs(uint16_t *ring, Pair pair, Ro
           o0 = (x & 0xffffu) | (r2 << 16);
           o1 = (y & 0xffffu) | (r2 & 0xffff0000u);
         }
-        const int row = i * 32 + 8 * q + 4 * (lane >> 5) + (lane & 3);
+        const int row = (i - I0) * 32 + 8 * q + 4 * (lane >> 5) + (lane & 3);
         const int col = j * 32 + col4;
         uint32_t *dst = reinterpret_cast<uint32_t *>(
             st + row * W + g_stage_chunk<NJ>(row, col >> 3) * 8 + (col & 7));
@@ -552,22 +578,38 @@ __device__ __forceinline__ void g_wave_store_pairs(uint16_t *ring, Pair pair, Ro
         dst[1] = o1;
       }
 #pragma unroll
-  for (int it = 0; it < GWTM * CH / 64; ++it) {
+  for (int it = 0; it < ROWS * CH / 64; ++it) {
     const int q = it * 64 + lane, row = q / CH, c = q % CH;
     const u32x4 v =
         *reinterpret_cast<const u32x4 *>(st + row * W + g_stage_chunk<NJ>(row, c) * 8);
-    uint16_t *p = row_ptr(row);
+    uint16_t *p = row_ptr(I0 * 32 + row);
     if (p && c * 8 < ncols) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p + c * 8));
   }
 }
 
 // val(i, j, v): fp32 value of accumulator element v of MFMA tile (i, j),
 // rounded to bf16 here.
-template <int NJ, class Val, class RowPtr>
+template <int NJ, int I0 = 0, int NI = GTM, class Val, class RowPtr>
 __device__ __forceinline__ void g_wave_store(uint16_t *ring, Val val, RowPtr row_ptr, int ncols) {
-  g_wave_store_pairs<NJ>(
+  g_wave_store_pairs<NJ, I0, NI>(
       ring, [&](int i, int j, int k) { return pack_bf16x2(val(i, j, 2 * k), val(i, j, 2 * k + 1)); },
       row_ptr, ncols);
+}
+
+// The same through one ring stage (GSA + GSB elements: 4 KB per wave), in
+// passes of as many row groups as fit.
+constexpr int GSTAGE_ELEMS = GSA + GSB;
+template <int NJ, class Val, class RowPtr>
+__device__ __forceinline__ void g_wave_store_staged(uint16_t *stage, Val val, RowPtr row_ptr,
+                                                    int ncols) {
+  constexpr int NI = GSTAGE_ELEMS / (GNT / 64) / (32 * NJ * 32);  // row groups per pass
+  static_assert(NI >= 1 && GTM % NI == 0, "passes of whole row groups");
+  g_wave_store<NJ, 0, NI>(stage, val, row_ptr, ncols);
+  if constexpr (NI < GTM) g_wave_store<NJ, NI % GTM, NI>(stage, val, row_ptr, ncols);
+  if constexpr (2 * NI < GTM) {
+    g_wave_store<NJ, (2 * NI) % GTM, NI>(stage, val, row_ptr, ncols);
+    g_wave_store<NJ, (3 * NI) % GTM, NI>(stage, val, row_ptr, ncols);
+  }
 }
 
 // Whether a bf16 output (base, row stride ld, columns n) takes 16-byte

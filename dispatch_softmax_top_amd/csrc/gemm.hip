@@ -768,24 +768,88 @@ __global__ __launch_bounds__(GNT) void gemm_shared_swiglu_tail_kernel(SwigluArgs
 #undef MOE_ROWS
 }
 
+// Persistent grouped kernels: block b runs units b, b + gridDim.x, ...
+// (gridDim.x a multiple of 8, so that a block's units all fall in its XCD's
+// tile range) and issues the first copies of its next unit before the
+// epilogue of the current one (gemm_mainloop_issue), staging that epilogue
+// in ring stage GNST - 1.  Across the main loop a unit keeps only what its
+// epilogue needs (a few scalars and, per lane, the output rows of two of
+// its wave's tile rows): with the whole tile description live there, the
+// loop needs more than 256 VGPRs.
+__device__ __forceinline__ int32_t wave_tile_row(const GTile &t, int m) {
+  return m < t.rows ? (int32_t)t.row(m) : -1;
+}
+
+// Row of wave-tile row r (0 .. 127): lane r % 64 holds it in rr[r / 64].
+__device__ __forceinline__ int32_t wave_row_of(int32_t r0, int32_t r1, int r) {
+  return __shfl(r < 64 ? r0 : r1, r & 63);
+}
+
+__device__ __forceinline__ void swiglu_finish(const SwigluArgs &g, int ft, int nparts, int punit,
+                                              int32_t r0, int32_t r1, const GAcc &acc,
+                                              uint16_t *stage) {
+  if (nparts > 1) {
+    g_part_store(g.sp.part, punit, acc);
+    return;
+  }
+  static_assert(GTN == 2, "one gate and one up tile per wave");
+  const int w = (int)(threadIdx.x >> 6);
+  const int c0 = ft * 128 + (w % GWN) * (GWTN / 2);
+  g_wave_store_staged<1>(
+      stage, [&](int i, int, int v) { return silu_f32(acc[i][0][v]) * acc[i][1][v]; },
+      [&](int r) -> uint16_t * {
+        const int32_t row = wave_row_of(r0, r1, r);
+        return row >= 0 ? g.H + (int64_t)row * g.ldh + c0 : nullptr;
+      },
+      GWTN / 2);
+}
+
+// The backward form (three outputs, stored directly) runs one unit per block:
+// it keeps more registers live.
 template <bool BWD>
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_swiglu_kernel(SwigluArgs g) {
   MOE_GEMM_LDS(lds);
   const GroupRegs gr = group_regs(g.grp, g.ftiles);
   GUnit u;
   GTile t;
-  if (!g_unit(g.sp, gr.total, blockIdx.x, u) || !group_tile_regs(g.grp, gr, g.ftiles, u.tile, t))
+  int b = blockIdx.x;
+  if (!g_unit(g.sp, gr.total, b, u) || !group_tile_regs(g.grp, gr, g.ftiles, u.tile, t))
     return;
-  const auto row_of = [&](int m) { return t.row(m); };
   int k0, k1;
   g_part_range(g.ktiles, u, k0, k1);
-  GAcc acc;
-  swiglu_acc(g, row_of, t.rows, t.expert, t.nt, k0, k1, lds, acc);
-  if (u.nparts > 1) {
-    g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
-    return;
+  if constexpr (BWD) {
+    const auto row_of = [&](int m) { return t.row(m); };
+    GAcc acc;
+    swiglu_acc(g, row_of, t.rows, t.expert, t.nt, k0, k1, lds, acc);
+    if (u.nparts > 1) g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
+    else swiglu_store<-1, true>(g, row_of, t.rows, t.nt, 0, acc);
+  } else {
+    // H rows take 16-byte stores (the launcher checks it)
+    GOps2 ops = swiglu_ops(g, [&](int m) { return t.row(m); }, t.rows, t.expert, t.nt, k0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_mainloop_issue(ops, k1 - k0, lds);
+    GAcc acc;
+    for (;;) {
+      const int m0 = ((int)(threadIdx.x >> 6) / GWN) * GWTM;
+      const int32_t r0 = wave_tile_row(t, m0 + lane_id()), r1 = wave_tile_row(t, m0 + 64 + lane_id());
+      const int ft = t.nt, nparts = u.nparts, punit = u.tail * u.nparts + u.part, kt = k1 - k0;
+      gemm_zero(acc);
+      gemm_mainloop_rest(ops, kt, acc, lds);
+      b += gridDim.x;
+      const bool more =
+          g_unit(g.sp, gr.total, b, u) && group_tile_regs(g.grp, gr, g.ftiles, u.tile, t);
+      __builtin_amdgcn_s_barrier();  // every wave is past its last read of the ring
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) {
+        g_part_range(g.ktiles, u, k0, k1);
+        ops = swiglu_ops(g, [&](int m) { return t.row(m); }, t.rows, t.expert, t.nt, k0);
+        gemm_mainloop_issue(ops, k1 - k0, lds);
+      }
+      swiglu_finish(g, ft, nparts, punit, r0, r1, acc, lds.A[GNST - 1]);
+      if (!more) break;
+    }
   }
-  swiglu_store<-1, BWD>(g, row_of, t.rows, t.nt, 0, acc, lds.A[0]);
 }
 
 template <bool BWD>
@@ -856,40 +920,77 @@ __device__ __forceinline__ void down_store(const DownArgs &g, const GTile &t, Ds
     }
 }
 
-__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_down_kernel(DownArgs g) {
-  MOE_GEMM_LDS(lds);
-  GUnit u;
-  GTile t;
-  const GroupRegs gr = group_regs(g.grp, g.tn);
-  if (!g_unit(g.sp, gr.total, blockIdx.x, u) || !group_tile_regs(g.grp, gr, g.tn, u.tile, t))
-    return;
+__device__ __forceinline__ GOps2 down_ops(const DownArgs &g, const GTile &t, int k0) {
   const uint16_t *W = g.Wd + (int64_t)t.expert * g.L * g.F;
   const int nv = g.L - t.nt * GBN, rows = t.rows;
   const int64_t r0 = t.row(0);
-  const bool whole = u.nparts == 1;
-  // receive row of tile row threadIdx.x: fetched before the main loop (its
-  // latency hides there), handed to the epilogue through LDS
-  int32_t my_dst = -1;
-  if (whole && (int)threadIdx.x < rows) my_dst = g.bank_src[t.row(threadIdx.x)];
-  int k0, k1;
-  g_part_range(g.ktiles, u, k0, k1);
-  const auto ops = g_operands(
+  return g_operands(
       g.H + r0 * g.F + k0 * GBK, g.F,
       [&](int r) { return (int)(t.row(min(r, rows - 1)) - r0); },
       W + (int64_t)t.nt * GBN * g.F + k0 * GBK, g.F, [&](int r) { return min(r, nv - 1); });
-  GAcc acc;
-  gemm_zero(acc);
-  gemm_mainloop(ops, k1 - k0, acc, lds);
-  if (!whole) {
-    g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
+}
+
+// Receive row of wave-tile row m0 + lane + 64 * h of a whole tile (-1: none).
+__device__ __forceinline__ int32_t down_dst(const DownArgs &g, const GUnit &u, const GTile &t,
+                                            int m) {
+  return u.nparts == 1 && m < t.rows ? g.bank_src[t.row(m)] : -1;
+}
+
+__device__ __forceinline__ void down_finish(const DownArgs &g, int nt, int nparts, int punit,
+                                            int32_t d0, int32_t d1, const GAcc &acc,
+                                            uint16_t *stage) {
+  if (nparts > 1) {
+    g_part_store(g.sp.part, punit, acc);
     return;
   }
-  // past the store regions of g_wave_store
-  int32_t *dst_rows = reinterpret_cast<int32_t *>(lds.A[0] + GSTAGE);
-  __syncthreads();  // every wave is past its last fragment read of the ring
-  if ((int)threadIdx.x < GBM) dst_rows[threadIdx.x] = my_dst;
-  __syncthreads();
-  down_store(g, t, [&](int m) { return (int64_t)dst_rows[m]; }, acc, lds.A[0]);
+  const int w = (int)(threadIdx.x >> 6);
+  const int n0 = nt * GBN + (w % GWN) * GWTN;
+  g_wave_store_staged<GTN>(
+      stage, [&](int i, int j, int v) { return acc[i][j][v]; },
+      [&](int r) -> uint16_t * {
+        const int32_t dr = wave_row_of(d0, d1, r);
+        return dr >= 0 && dr < g.n_ret ? g.ret + (int64_t)dr * g.L + n0 : nullptr;
+      },
+      g.L - n0);
+}
+
+// Persistent like the forward SwiGLU; output rows 16-byte aligned (the
+// launcher checks it).
+__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_expert_down_kernel(DownArgs g) {
+  MOE_GEMM_LDS(lds);
+  const GroupRegs gr = group_regs(g.grp, g.tn);
+  GUnit u;
+  GTile t;
+  int b = blockIdx.x;
+  if (!g_unit(g.sp, gr.total, b, u) || !group_tile_regs(g.grp, gr, g.tn, u.tile, t)) return;
+  int k0, k1;
+  g_part_range(g.ktiles, u, k0, k1);
+  GOps2 ops = down_ops(g, t, k0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  gemm_mainloop_issue(ops, k1 - k0, lds);
+  GAcc acc;
+  for (;;) {
+    // receive rows of this wave's tile rows, loaded while the main loop runs
+    const int m0 = ((int)(threadIdx.x >> 6) / GWN) * GWTM;
+    const int32_t d0 = down_dst(g, u, t, m0 + lane_id()), d1 = down_dst(g, u, t, m0 + 64 + lane_id());
+    const int nt = t.nt, nparts = u.nparts, punit = u.tail * u.nparts + u.part, kt = k1 - k0;
+    gemm_zero(acc);
+    gemm_mainloop_rest(ops, kt, acc, lds);
+    // d0, d1 waited for here, while no copy is outstanding
+    asm volatile("" ::"v"(d0), "v"(d1));
+    b += gridDim.x;
+    const bool more = g_unit(g.sp, gr.total, b, u) && group_tile_regs(g.grp, gr, g.tn, u.tile, t);
+    __builtin_amdgcn_s_barrier();  // every wave is past its last read of the ring
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+      g_part_range(g.ktiles, u, k0, k1);
+      ops = down_ops(g, t, k0);
+      gemm_mainloop_issue(ops, k1 - k0, lds);
+    }
+    down_finish(g, nt, nparts, punit, d0, d1, acc, lds.A[GNST - 1]);
+    if (!more) break;
+  }
 }
 
 __global__ __launch_bounds__(GNT) void gemm_expert_down_tail_kernel(DownArgs g) {
@@ -1099,10 +1200,14 @@ static int64_t grouped_tiles_bound(const moe_dims &d, int64_t n_bank_rows, int t
 template <class Args>
 static int grouped(const char *name, const char *tail_name, void (*k)(Args),
                    void (*tk)(Args), int64_t bound, int ktiles, Args &a, float *part,
-                   hipStream_t s) {
+                   hipStream_t s, bool persistent) {
   MOE_TRY(make_split(part, ktiles, a.sp));
-  MOE_TRY(launch(name, k, dim3((unsigned)(bound + (a.sp.part ? a.sp.ncu : 0))), dim3(GNT), 0, s,
-                 a));
+  int ncu = 0;
+  MOE_TRY(cu_count(&ncu));
+  const int64_t units = bound + (a.sp.part ? a.sp.ncu : 0);
+  // persistent: one block per CU at most, a multiple of 8 (the XCDs)
+  const int64_t grid = persistent ? std::min<int64_t>(units, std::max(8, ncu / 8 * 8)) : units;
+  MOE_TRY(launch(name, k, dim3((unsigned)grid), dim3(GNT), 0, s, a));
   if (!a.sp.part || a.sp.ncu < 2) return MOE_OK;
   return launch(tail_name, tk, dim3((unsigned)(a.sp.ncu / 2 * GTM)), dim3(GNT), 0, s, a);
 }
@@ -1123,8 +1228,9 @@ static int expert_swiglu(const char *name, const char *tail_name, void (*k)(Swig
   a.H = H;
   a.ldh = d.d_ff;
   a.grp = group_args(d, bank_offsets, bfill, n_bank_rows, std::max(d.latent, d.d_ff));
+  if (((uintptr_t)H & 15) || (a.ldh & 7)) return fail(MOE_ERR_INVALID, "%s: H rows not 16-byte aligned", name);
   return grouped(name, tail_name, k, tk, grouped_tiles_bound(d, n_bank_rows, a.ftiles), a.ktiles,
-                 a, part, s);
+                 a, part, s, a.dH == nullptr);
 }
 
 int gemm_expert_swiglu(const moe_dims &d, const uint16_t *bank, const int64_t *bank_offsets,
@@ -1170,8 +1276,9 @@ static int grouped_nt(const char *name, const char *tail_name, const moe_dims &d
   a.grp = group_args(d, bank_offsets, bfill, n_bank_rows, std::max(K, N));
   a.bank_src = dst;
   a.ret = out;
+  if (((uintptr_t)out & 15) || (N & 7)) return fail(MOE_ERR_INVALID, "%s: output rows not 16-byte aligned", name);
   return grouped(name, tail_name, gemm_expert_down_kernel, gemm_expert_down_tail_kernel,
-                 grouped_tiles_bound(d, n_bank_rows, a.tn), a.ktiles, a, part, s);
+                 grouped_tiles_bound(d, n_bank_rows, a.tn), a.ktiles, a, part, s, true);
 }
 
 int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_offsets,
