@@ -107,15 +107,42 @@ MUTATIONS = [
 ]
 
 
-@pytest.mark.parametrize("name,old,new,suite", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_pins_catch_mutation(tmp_path, name, old, new, suite):
+def _run_mutant(tmp_root, name, old, new, suite):
+    """Exit status of the pin suite against a copy of the oracle with one slip
+    planted (and the tail of its output)."""
     src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
-    assert src.count(old) >= 1, f"mutation site for {name!r} not found"
+    if src.count(old) < 1:
+        return None, f"mutation site for {name!r} not found"
+    work = os.path.join(tmp_root, "m%d" % [m[0] for m in MUTATIONS].index(name))
     for d in ("oracle", "synth", "tests"):
-        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+        shutil.copytree(os.path.join(ROOT, d), os.path.join(work, d),
                         ignore=shutil.ignore_patterns("*.so", "__pycache__"))
-    (tmp_path / "oracle" / "oracle.c").write_text(src.replace(old, new, 1))
+    with open(os.path.join(work, "oracle", "oracle.c"), "w") as f:
+        f.write(src.replace(old, new, 1))
     p = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join("tests", suite)], cwd=tmp_path, capture_output=True,
-                       text=True, timeout=600)
-    assert p.returncode != 0, f"pins did not catch {name!r}:\n{p.stdout[-2000:]}"
+                        os.path.join("tests", suite)], cwd=work, capture_output=True,
+                       text=True, timeout=600, env=_ONE_THREAD)
+    return p.returncode, p.stdout[-2000:]
+
+
+# children run side by side: one BLAS / OpenMP thread each
+_ONE_THREAD = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1",
+                   MKL_NUM_THREADS="1")
+
+
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    """Every mutant's suite, run in parallel child processes (one CPU each)."""
+    from concurrent.futures import ThreadPoolExecutor
+    root = str(tmp_path_factory.mktemp("mutants"))
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with ThreadPoolExecutor(workers) as ex:
+        futs = {m[0]: ex.submit(_run_mutant, root, *m) for m in MUTATIONS}
+        return {k: f.result() for k, f in futs.items()}
+
+
+@pytest.mark.parametrize("name,old,new,suite", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_mutation(mutant_results, name, old, new, suite):
+    rc, out = mutant_results[name]
+    assert rc is not None, out
+    assert rc != 0, f"pins did not catch {name!r}:\n{out}"

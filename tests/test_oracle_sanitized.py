@@ -35,12 +35,21 @@ def test_oracle_suites_clean_under_sanitizers(tmp_path):
                            "-fno-sanitize-recover=all", os.path.join(ROOT, "oracle", "oracle.c"),
                            "-o", lib, "-lm"])
     env = dict(os.environ)
+    # the suites run side by side: one BLAS / OpenMP thread each
+    env.update(OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
     env.update(ORACLE_LIB=lib, LD_PRELOAD=_runtime("libasan.so"),
                ASAN_OPTIONS="detect_leaks=0:verify_asan_link_order=0:abort_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
-    p = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "-m", "not gpu", "-k", SKIP, *SUITES], cwd=ROOT, env=env, capture_output=True,
-                       text=True, timeout=1500)
-    tail = (p.stdout + p.stderr)[-4000:]
-    assert p.returncode == 0, tail
-    assert "ERROR: AddressSanitizer" not in tail and "runtime error" not in tail, tail
+    from concurrent.futures import ThreadPoolExecutor
+
+    def run(suite):  # one child process per suite, in parallel
+        return subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p",
+                               "no:cacheprovider", "-m", "not gpu", "-k", SKIP, suite],
+                              cwd=ROOT, env=env, capture_output=True, text=True, timeout=1500)
+
+    with ThreadPoolExecutor(len(SUITES)) as ex:
+        results = list(ex.map(run, SUITES))
+    for suite, p in zip(SUITES, results):
+        tail = (p.stdout + p.stderr)[-4000:]
+        assert p.returncode == 0, suite + "\n" + tail
+        assert "ERROR: AddressSanitizer" not in tail and "runtime error" not in tail, tail
