@@ -37,19 +37,19 @@ __device__ __forceinline__ float unord_f32(uint32_t o) {
 }
 
 // Reductions over the wave that every lane gets: DPP inside each 16-lane row
-// (swaps within quads, then rotations by 4 and 8), then the row broadcasts of
-// lanes 15 and 31 fold rows 0-2 into row 3, and lane 63 is read.  The order
-// of the operations is fixed, so a sum is the same on every call.
+// (swaps within quads, then rotations by 4 and 8; every lane reads a valid
+// lane, so the DPP folds into the operation itself), then lanes 0, 16, 32
+// and 48 are read and combined as (r0 op r1) op (r2 op r3).  The order of the
+// operations is fixed, so a sum is the same on every call.
 template <class Op>
 __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
-  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
-  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
-  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
-  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
-  // row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3 (other rows keep v)
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
-  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));   // [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));   // [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true));  // row_ror:4
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true));  // row_ror:8
+  const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+  return op(op(r0, r1), op(r2, r3));
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
@@ -66,7 +66,8 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 // One wave per token.
 // bias: NULL, or [E] fp32 added to every token's logits (one fp32 rounding).
 // renorm: gates divided by their sum over the k chosen.
-template <int VPL>
+// K > 0: k == K, the rounds unrolled; K == 0: any k.
+template <int VPL, int K>
 __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restrict__ logits,
                                                           const float *__restrict__ bias,
                                                           int T, int E, int k, int renorm,
@@ -107,7 +108,9 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
   // 0's choice carries the largest logit m of the softmax.
   int my_idx = 0;
   float my_logit = 0.f, m = 0.f;
-  for (int j = 0; j < k; ++j) {
+  if constexpr (K > 0) k = K;
+#pragma unroll
+  for (int j = 0; j < (K > 0 ? K : k); ++j) {
     const uint32_t best = wave_max_u32(key[0]);
     const uint64_t holders = ballot(key[0] == best);
     int e;
@@ -148,8 +151,9 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
 template <int VPL>
 static int launch_route(const float *logits, const float *bias, int T, int E, int k,
                         int renorm, int32_t *topk, float *gates, hipStream_t s) {
-  return launch("route_topk_softmax", route_topk_softmax<VPL>, dim3((unsigned)cdiv(T, 4)),
-                dim3(256), 0, s, logits, bias, T, E, k, renorm, topk, gates);
+  return launch("route_topk_softmax", k == 8 ? route_topk_softmax<VPL, 8> : route_topk_softmax<VPL, 0>,
+                dim3((unsigned)cdiv(T, 4)), dim3(256), 0, s, logits, bias, T, E, k, renorm, topk,
+                gates);
 }
 
 static int route(const float *logits, const float *bias, int32_t T, int32_t E, int32_t k,
