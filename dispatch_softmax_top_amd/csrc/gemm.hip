@@ -276,23 +276,134 @@ __device__ __forceinline__ void dense_body(const DenseArgs &g, const GemmLds &ld
   dense_store(g, g.C + b * g.bsC, mt, nt, acc, lds.A[0]);
 }
 
+// Operand sources of dense tile (b, mt, nt) from K tile k0 on.
+template <int NS>
+struct DenseOps {
+  typedef GOps<GSegOperand<GCA, NS>, GSegOperand<GCB, NS>> type;
+};
+template <>
+struct DenseOps<1> {
+  typedef GOps<GOperand<GCA>, GOperand<GCB>> type;
+};
+
+template <int NS>
+__device__ __forceinline__ typename DenseOps<NS>::type dense_ops(const DenseArgs &g, int b, int mt,
+                                                                 int nt, int k0) {
+  const int mv = g.M - mt * GBM, nv = g.N - nt * GBN;  // valid rows / columns
+  const auto row_a = [&](int r) { return min(r, mv - 1); };
+  const auto row_b = [&](int r) { return min(r, nv - 1); };
+  if constexpr (NS == 1) {
+    return g_operands(g.A[0] + b * g.bsA + (int64_t)mt * GBM * g.lda[0] + k0 * GBK, g.lda[0],
+                      row_a, g.B[0] + b * g.bsB + (int64_t)nt * GBN * g.ldb[0] + k0 * GBK,
+                      g.ldb[0], row_b);
+  } else {
+    typename DenseOps<NS>::type ops;
+    int kend = 0;
+    dense_segs<0>(g, mt, nt, row_a, row_b, kend, ops);
+    ops.a.kbeg = ops.b.kbeg = -k0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      ops.a.kend[i] -= k0;
+      ops.b.kend[i] -= k0;
+    }
+    return ops;
+  }
+}
+
+// Whole-tile epilogue of a persistent dense block: 16-byte row stores staged
+// through one ring stage, or (outputs without 16-byte alignment) direct stores.
+__device__ __forceinline__ void dense_finish(const DenseArgs &g, uint16_t *C, int mt, int nt,
+                                             const GAcc &acc, uint16_t *stage) {
+  if (g_vec_out(C, g.ldc, g.N)) {
+    const int w = (int)(threadIdx.x >> 6);
+    const int m0 = mt * GBM + (w / GWN) * GWTM, n0 = nt * GBN + (w % GWN) * GWTN;
+    g_wave_store_staged<GTN>(
+        stage, [&](int i, int j, int v) { return acc[i][j][v]; },
+        [&](int r) -> uint16_t * {
+          return m0 + r < g.M ? C + (int64_t)(m0 + r) * g.ldc + n0 : nullptr;
+        },
+        g.N - n0);
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < GTM; ++i)
+#pragma unroll
+    for (int j = 0; j < GTN; ++j) {
+      const int n = nt * GBN + g_acc_col(j);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = mt * GBM + g_acc_row(i, v);
+        if (m < g.M && n < g.N) C[(int64_t)m * g.ldc + n] = f32_to_bf16(acc[i][j][v]);
+      }
+    }
+}
+
+// Persistent form of dense_body (see the grouped kernels): block b runs
+// units b, b + gridDim.x, ...; only the tile's coordinates live across the
+// main loop.
+template <int NS, bool BATCHED = false>
+__device__ __forceinline__ void dense_body_persistent(const DenseArgs &g, const GemmLds &lds) {
+  static_assert(!BATCHED || NS == 1, "batched products have one K segment");
+  const int tm = (g.M + GBM - 1) / GBM, tn = (g.N + GBN - 1) / GBN;
+  const int total = tm * tn * (BATCHED ? g.nbatch : 1);
+  int kt = 0;
+  for (int i = 0; i < NS; ++i) kt += g.ktiles[i];
+  int bid = blockIdx.x;
+  GUnit u;
+  if (!g_unit(g.sp, total, bid, u)) return;
+  int tile = u.tile;
+  int b = dense_batch<BATCHED>(g, tm * tn, tile);
+  int mt, nt;
+  g_tile_coords(tile, tm, tn, mt, nt);
+  int k0, k1;
+  g_part_range(kt, u, k0, k1);
+  typename DenseOps<NS>::type ops = dense_ops<NS>(g, b, mt, nt, k0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  gemm_mainloop_issue(ops, k1 - k0, lds);
+  GAcc acc;
+  for (;;) {
+    const int cb = b, cmt = mt, cnt = nt, nparts = u.nparts, punit = u.tail * u.nparts + u.part;
+    gemm_zero(acc);
+    gemm_mainloop_rest(ops, k1 - k0, acc, lds);
+    bid += gridDim.x;
+    const bool more = g_unit(g.sp, total, bid, u);
+    __builtin_amdgcn_s_barrier();  // every wave is past its last read of the ring
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+      tile = u.tile;
+      b = dense_batch<BATCHED>(g, tm * tn, tile);
+      g_tile_coords(tile, tm, tn, mt, nt);
+      g_part_range(kt, u, k0, k1);
+      ops = dense_ops<NS>(g, b, mt, nt, k0);
+      gemm_mainloop_issue(ops, k1 - k0, lds);
+    }
+    if (nparts > 1) g_part_store(g.sp.part, punit, acc);
+    else dense_finish(g, g.C + cb * g.bsC, cmt, cnt, acc, lds.A[GNST - 1]);
+    if (!more) break;
+  }
+}
+
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_latent_down_kernel(DenseArgs g) {
   MOE_GEMM_LDS(lds);
-  dense_body<1>(g, lds);
+  dense_body_persistent<1>(g, lds);
 }
 
 // up-projection + shared experts: 1 + S segments
+// (persistent with at most one shared expert: with more segments the loop
+// needs more than 256 VGPRs)
 template <int NS>
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_up_shared_kernel(DenseArgs g) {
   MOE_GEMM_LDS(lds);
-  dense_body<NS>(g, lds);
+  if constexpr (NS <= 2) dense_body_persistent<NS>(g, lds);
+  else dense_body<NS>(g, lds);
 }
 
 // products of the backward pass: NS K segments, or a batch of products
 template <int NS, bool BATCHED>
 __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, GMINWAVES))) void gemm_nt_kernel(DenseArgs g) {
   MOE_GEMM_LDS(lds);
-  dense_body<NS, BATCHED>(g, lds);
+  dense_body_persistent<NS, BATCHED>(g, lds);
 }
 
 // the split tiles of a dense product: sum of parts, then the store
@@ -1056,10 +1167,12 @@ static int split_parts(const GSplit &sp, int64_t total) {
       1, std::min<int64_t>(std::min<int64_t>(sp.ncu / r, sp.max_parts), sp.max_units / r));
 }
 
+// persistent: k runs units b, b + grid, ... (dense_body_persistent); the grid
+// is then one block per CU at most, a multiple of 8.
 static int dense(const char *name, const char *tail_name, void (*k)(DenseArgs), int M, int N,
                  int nseg, const DenseSeg *segs, uint16_t *C, int64_t ldc, float *part,
-                 hipStream_t s, int nbatch = 1, int64_t bsA = 0, int64_t bsB = 0,
-                 int64_t bsC = 0) {
+                 hipStream_t s, bool persistent, int nbatch = 1, int64_t bsA = 0,
+                 int64_t bsB = 0, int64_t bsC = 0) {
   if (nseg < 1 || nseg > MAXSEG) return fail(MOE_ERR_INVALID, "%s: bad segment count", name);
   if (nbatch < 1 || (nbatch > 1 && nseg != 1))
     return fail(MOE_ERR_INVALID, "%s: bad batch", name);
@@ -1090,20 +1203,24 @@ static int dense(const char *name, const char *tail_name, void (*k)(DenseArgs), 
   int kt = 0;
   for (int i = 0; i < nseg; ++i) kt += a.ktiles[i];
   MOE_TRY(make_split(part, kt, a.sp));
+  int ncu = 0;
+  MOE_TRY(cu_count(&ncu));
+  const int64_t cap = persistent ? std::max(8, ncu / 8 * 8) : INT32_MAX;
   const int S = split_parts(a.sp, tiles);
   if (S == 1) {
     a.sp.part = nullptr;
-    return launch(name, k, dim3((unsigned)tiles), dim3(GNT), 0, s, a);
+    return launch(name, k, dim3((unsigned)std::min<int64_t>(tiles, cap)), dim3(GNT), 0, s, a);
   }
   const int64_t r = tiles % a.sp.ncu;
-  MOE_TRY(launch(name, k, dim3((unsigned)(tiles - r + r * S)), dim3(GNT), 0, s, a));
+  MOE_TRY(launch(name, k, dim3((unsigned)std::min<int64_t>(tiles - r + r * S, cap)), dim3(GNT), 0,
+                 s, a));
   return launch(tail_name, nbatch > 1 ? gemm_dense_tail_kernel<true> : gemm_dense_tail_kernel<false>,
                 dim3((unsigned)(r * GTM)), dim3(GNT), 0, s, a);
 }
 
 int gemm_latent_down(int M, int N, const DenseSeg &seg, uint16_t *C, int64_t ldc, hipStream_t s) {
   return dense("gemm_latent_down", "gemm_latent_down_tail", gemm_latent_down_kernel, M, N, 1, &seg,
-               C, ldc, nullptr, s);
+               C, ldc, nullptr, s, true);
 }
 
 int gemm_up_shared(int M, int N, int nseg, const DenseSeg *segs, uint16_t *C, int64_t ldc,
@@ -1113,7 +1230,7 @@ int gemm_up_shared(int M, int N, int nseg, const DenseSeg *segs, uint16_t *C, in
                                                gemm_up_shared_kernel<5>};
   if (nseg < 1 || nseg > MAXSEG) return fail(MOE_ERR_INVALID, "gemm_up_shared: bad segment count");
   return dense("gemm_up_shared", "gemm_up_shared_tail", k[nseg - 1], M, N, nseg, segs, C, ldc,
-               part, s);
+               part, s, nseg <= 2);
 }
 
 static int shared_swiglu(const char *name, const char *tail_name, void (*k)(SwigluArgs),
@@ -1301,7 +1418,7 @@ int gemm_nt(const char *name, const char *tail_name, int M, int N, int nseg,
             const DenseSeg *segs, uint16_t *C, int64_t ldc, float *part, hipStream_t s) {
   static void (*const k[2])(DenseArgs) = {gemm_nt_kernel<1, false>, gemm_nt_kernel<2, false>};
   if (nseg < 1 || nseg > 2) return fail(MOE_ERR_INVALID, "%s: bad segment count", name);
-  return dense(name, tail_name, k[nseg - 1], M, N, nseg, segs, C, ldc, part, s);
+  return dense(name, tail_name, k[nseg - 1], M, N, nseg, segs, C, ldc, part, s, true);
 }
 
 int gemm_nt_multi(const char *name, const char *tail_name, int nprod, const NtProd *prods, int K,
@@ -1351,8 +1468,8 @@ int gemm_nt_batched(const char *name, const char *tail_name, int M, int N, const
                     int nbatch, int64_t bsA, int64_t bsB, uint16_t *C, int64_t ldc, int64_t bsC,
                     float *part, hipStream_t s) {
   if (nbatch == 1) return gemm_nt(name, tail_name, M, N, 1, &seg, C, ldc, part, s);
-  return dense(name, tail_name, gemm_nt_kernel<1, true>, M, N, 1, &seg, C, ldc, part, s, nbatch,
-               bsA, bsB, bsC);
+  return dense(name, tail_name, gemm_nt_kernel<1, true>, M, N, 1, &seg, C, ldc, part, s, true,
+               nbatch, bsA, bsB, bsC);
 }
 
 }  // namespace moe
