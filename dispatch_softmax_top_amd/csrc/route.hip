@@ -4,15 +4,16 @@
 // and "从玩具到前沿:训练一个真正的大模型,到底难在哪里" (devpress.csdn.net),
 // section 四: every token is routed to 8 of 384 experts.
 //
-// One wave64 per token.  Lane l holds logits l, l+64, l+128, ... .  The
-// choice order is (logit descending, index ascending).  Each candidate's
-// order-preserving 32-bit image of its fp32 logit is its key; each lane keeps
-// its candidates sorted by (key descending, index ascending).  k rounds take
-// the wave-wide largest head (DPP maxima inside 16-lane rows, then two row
-// broadcasts); if several lanes hold that key (equal logits), a second
-// reduction takes the lowest index among them.  The winner's lane pops its
-// head.  The first choice is the largest logit m; gates are exp(l - m) /
-// sum exp(l - m) over all E logits, in fp32 (exp by the hardware exp2).
+// One wave64 per token.  Lane l holds the logits of experts l*V .. l*V+V-1
+// (V = ceil(E / 64)).  The choice order is (logit descending, index
+// ascending).  Each candidate's order-preserving 32-bit image of its fp32
+// logit is its key; each lane keeps its candidates sorted by (key
+// descending, index ascending).  k rounds take the wave-wide largest head
+// (DPP maxima inside 16-lane rows, then four lane reads); if several lanes
+// hold that key (equal logits), a second reduction takes the lowest index
+// among them.  The winner's lane pops its head.  The first choice is the
+// largest logit m; gates are exp(l - m) / sum exp(l - m) over all E logits,
+// in fp32 (exp by the hardware exp2).
 //
 // Quantile balancing ("从玩具到前沿:训练一个真正的大模型,到底难在哪里",
 // section 四 and appendix A.2): a per-expert bias is added to the logits
@@ -63,10 +64,57 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   }));
 }
 
-// One wave per token.
+// k rounds over each lane's sorted candidates kc[0 .. N-1] (image
+// descending, index ascending; image 0: none): the largest head is the next
+// choice (equal images: the lowest index among the lanes holding it), and
+// its owner pops its head.  Lane j keeps choice j; round 0's choice carries
+// the largest logit m.  CHECK: the lanes kept only their N best candidates;
+// returns false if some lane ran out of them with rounds left (its next one
+// might still have been chosen).
+template <int VPL, int N, int K, bool CHECK>
+__device__ __forceinline__ bool route_rounds(uint32_t (&kc)[N], int (&ic)[N], int k, int lane,
+                                             int &my_idx, float &my_logit, float &m) {
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < (K > 0 ? K : k); ++j) {
+    const uint32_t best = wave_max_u32(kc[0]);
+    const uint64_t holders = ballot(kc[0] == best);
+    int e, owner;
+    if (__popcll(holders) == 1) {
+      owner = (int)__builtin_ctzll(holders);
+      e = __builtin_amdgcn_readlane(ic[0], owner);
+    } else {
+      e = (int)wave_min_u32(kc[0] == best ? (uint32_t)ic[0] : 0xffffffffu);
+      owner = e / VPL;
+    }
+    if (owner == lane) {
+#pragma unroll
+      for (int i = 0; i + 1 < N; ++i) {
+        kc[i] = kc[i + 1];
+        ic[i] = ic[i + 1];
+      }
+      kc[N - 1] = 0u;
+    }
+    if constexpr (CHECK)
+      if (j + 1 < (K > 0 ? K : k) && __builtin_amdgcn_readlane(kc[0], owner) == 0u) ok = false;
+    const float lg = unord_f32(best);
+    if (j == 0) m = lg;
+    if (lane == j) {
+      my_idx = e;
+      my_logit = lg;
+    }
+  }
+  return ok;
+}
+
+// One wave per token; lane l holds experts l*VPL .. l*VPL + VPL - 1 (one run
+// of the logit row, so the loads are 8-byte pairs where E allows).
 // bias: NULL, or [E] fp32 added to every token's logits (one fp32 rounding).
 // renorm: gates divided by their sum over the k chosen.
 // K > 0: k == K, the rounds unrolled; K == 0: any k.
+// With more than three candidates per lane the rounds first run on each
+// lane's best three; in the rare case that a lane runs out of them with
+// rounds left, they run again on every candidate.
 template <int VPL, int K>
 __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restrict__ logits,
                                                           const float *__restrict__ bias,
@@ -75,20 +123,44 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
                                                           float *__restrict__ gates) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together
-  const int lane = lane_id();
+  const int lane = lane_id(), e0 = lane * VPL;
   const float *l = logits + (int64_t)t * E;
 
   // candidates of this lane: order-preserving image of the fp32 logit and
   // the expert index, sorted by (image descending, index ascending)
   float v[VPL];
+  bool pairs = false;
+  if constexpr (VPL % 2 == 0) pairs = (E % 2) == 0 && e0 + VPL <= E;  // 8-byte aligned pairs
+  if (pairs) {
+    const float2 *lp = reinterpret_cast<const float2 *>(l + e0);
+#pragma unroll
+    for (int i = 0; i < VPL / 2; ++i) {
+      const float2 x = lp[i];
+      v[2 * i] = x.x;
+      v[2 * i + 1] = x.y;
+    }
+    if (bias) {
+      const float2 *bp = reinterpret_cast<const float2 *>(bias + e0);
+#pragma unroll
+      for (int i = 0; i < VPL / 2; ++i) {
+        const float2 x = bp[i];
+        v[2 * i] += x.x;
+        v[2 * i + 1] += x.y;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = e0 + i;
+      v[i] = e < E ? (bias ? l[e] + bias[e] : l[e]) : -INFINITY;
+    }
+  }
   uint32_t key[VPL];
   int idx[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = e < E ? (bias ? l[e] + bias[e] : l[e]) : -INFINITY;
-    key[i] = e < E ? ord_f32(v[i]) : 0u;
-    idx[i] = e;
+    key[i] = e0 + i < E ? ord_f32(v[i]) : 0u;
+    idx[i] = e0 + i;
   }
 #pragma unroll
   for (int i = 1; i < VPL; ++i)
@@ -103,40 +175,21 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
       idx[j] = sw ? ia : ib;
     }
 
-  // k rounds: the largest head is the next choice (equal images: the lowest
-  // index among the lanes holding it), and its owner pops its head.  Round
-  // 0's choice carries the largest logit m of the softmax.
   int my_idx = 0;
   float my_logit = 0.f, m = 0.f;
   if constexpr (K > 0) k = K;
-#pragma unroll
-  for (int j = 0; j < (K > 0 ? K : k); ++j) {
-    const uint32_t best = wave_max_u32(key[0]);
-    const uint64_t holders = ballot(key[0] == best);
-    int e;
-    if (__popcll(holders) == 1)
-      e = __builtin_amdgcn_readlane(idx[0], (int)__builtin_ctzll(holders));
-    else
-      e = (int)wave_min_u32(key[0] == best ? (uint32_t)idx[0] : 0xffffffffu);
-    if ((e & 63) == lane) {  // owner pops its head
-#pragma unroll
-      for (int i = 0; i + 1 < VPL; ++i) {
-        key[i] = key[i + 1];
-        idx[i] = idx[i + 1];
-      }
-      key[VPL - 1] = 0u;
-    }
-    const float lg = unord_f32(best);
-    if (j == 0) m = lg;
-    if (lane == j) {
-      my_idx = e;
-      my_logit = lg;
-    }
+  if constexpr (VPL > 3) {
+    uint32_t hk[3] = {key[0], key[1], key[2]};
+    int hi[3] = {idx[0], idx[1], idx[2]};
+    if (!route_rounds<VPL, 3, K, true>(hk, hi, k, lane, my_idx, my_logit, m))
+      route_rounds<VPL, VPL, K, false>(key, idx, k, lane, my_idx, my_logit, m);
+  } else {
+    route_rounds<VPL, VPL, K, false>(key, idx, k, lane, my_idx, my_logit, m);
   }
   // softmax denominator over all E logits, then the gates of the k chosen
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) s += (lane + 64 * i < E) ? __expf(v[i] - m) : 0.f;
+  for (int i = 0; i < VPL; ++i) s += (e0 + i < E) ? __expf(v[i] - m) : 0.f;
   s = wave_sum_dpp(s);
   const float ej = __expf(my_logit - m);
   // renorm: the k chosen probabilities over their sum, i.e. the softmax over

@@ -83,6 +83,12 @@ def test_route_ties_and_edges(moe, orc):
         lg[1, ::2] = -0.0                                        # -0 ties +0
         _route_check(moe, orc, lg, k)
     _route_check(moe, orc, rng.standard_normal((1, 384)).astype(np.float32), 8)   # T = 1
+    # chosen experts crowded on a few lanes (a lane's best three run out with
+    # rounds left, so the rounds start again over every candidate)
+    for E, k in ((384, 8), (384, 32), (1024, 8), (130, 32)):
+        ramp = np.arange(E, dtype=np.float32)
+        lg = np.stack([-ramp, ramp, np.roll(-ramp, 7), np.roll(ramp, -100 % E)] * 16)
+        _route_check(moe, orc, lg, k)
 
 
 def test_route_errors(moe):
