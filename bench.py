@@ -14,9 +14,9 @@ The line's value is the 4096-token shard at rank 0 (mean over the K timed
 steps; the median and the spread are in step_ms).  Beside it: the dominant
 kernel's roofline, the oracle's rate on the host, the same steps after a
 1 GiB cache sweep each (cold_cache), the backward of the share, and the
-forward figures of three more workloads (the 65536-token long-context shard
-at rank 0, and the most-loaded rank of the Zipf-skewed 16384-token shard and
-of its dropless form).
+figures of three more workloads, forward and backward (the 65536-token
+long-context shard at rank 0, and the most-loaded rank of the Zipf-skewed
+16384-token shard and of its dropless form).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--rank R|hot]
 Prints one JSON line.
@@ -258,10 +258,12 @@ def backward_step(st):
     router, experts (the return exchange reversed: a loopback identity, as in
     the forward return), pack side (the forward exchange reversed, likewise)."""
     b = st.bwd
-    b.combine(st.rcv.ret, st.snd, st.cmb, st.x, st.wlu, st.wsg, st.wsu, st.wsd, st.d_out)
+    # ragged mode: both loopbacks keep the receive layout, as the forward's
+    b.combine(st.rcv.ret, st.snd, st.cmb, st.x, st.wlu, st.wsg, st.wsu, st.wsd, st.d_out,
+              ret_offsets=st.recv_offsets)
     b.route(st.logits, st.snd, bias=None if st.bal is None else st.bal.bias)
     b.ffn(st.rcv, st.wg, st.wu, st.wd, b.d_returned)
-    b.pack(b.d_recv, st.snd, st.x, st.wld, st.wsg, st.wsu)
+    b.pack(b.d_recv, st.snd, st.x, st.wld, st.wsg, st.wsu, pool_offsets=st.recv_offsets)
 
 
 def backward_work(st):
@@ -273,10 +275,14 @@ def backward_work(st):
     El = E // d.n_ranks
     SF = S * Fs
     Tp = -(-T // 32) * 32
-    Kp = -(-(d.n_waves * d.cap_recv) // 32) * 32
     kept_s = int(st.snd.fill.sum())
     kept_r = int(st.rcv.bfill.sum())
-    n_slots = int(st.snd.pools.shape[0])
+    n_slots = int(st.n_recv_rows)
+    if d.cap_send:   # every expert's K block: its capacity over all waves
+        kpad = El * (-(-(d.n_waves * d.cap_recv) // 32) * 32)
+    else:            # packed: each expert's rows rounded up to K tiles, at least 256
+        rows = st.rcv.bfill.view(d.n_waves, El).sum(0).tolist()
+        kpad = sum(max(-(-r // 32) * 32, 256) for r in rows)
     f = lambda v: ("flop", float(v))
     b = lambda v: ("byte", float(v))
     return {
@@ -298,7 +304,7 @@ def backward_work(st):
         "transpose_combine_weights": b(4 * D * L + 4 * D * SF),
         "transpose_combine_acts": b(2 * T * (D + L + SF) + 2 * Tp * (D + L + SF)),
         "transpose_expert_weights": b(3 * 4 * El * L * F),
-        "transpose_bank": b(2 * kept_r * (2 * L + 3 * F) + 2 * El * Kp * (2 * L + 3 * F)),
+        "transpose_bank": b(2 * kept_r * (2 * L + 3 * F) + 2 * kpad * (2 * L + 3 * F)),
         "transpose_pack_weights": b(4 * L * D + 8 * SF * D),
         "transpose_pack_acts": b(2 * T * (D + L + 2 * SF) + 2 * Tp * (D + L + 2 * SF)),
     }
@@ -554,10 +560,11 @@ def drop_stats(st):
 OTHER_WORKLOADS = ((3, "0"), (2, "hot"), (4, "hot"))
 
 
-def workload_summary(cfg, which, steps, warmup):
-    """Forward figures of one more workload: step time (mean, median, cold
+def workload_summary(cfg, which, steps, warmup, backward=True):
+    """Figures of one more workload: forward step time (mean, median, cold
     caches), routed tokens/s, path roofline, the expert GEMMs' MFMA fractions
-    and the drop rates."""
+    and the drop rates; with backward, the backward's step time, path
+    roofline and dominant kernel."""
     import torch
     t0 = time.time()
     st = setup_rank(cfg, which)
@@ -577,8 +584,12 @@ def workload_summary(cfg, which, steps, warmup):
         "gemm_expert_down_mfma_frac": gemm_frac(kernels, "gemm_expert_down"),
         "kept_rows_at_rank": int(st.rcv.bfill.sum()),
         "drops": drop_stats(st),
-        "wall_s": round(time.time() - t0, 1),
     }
+    if backward and not st.d.dedup:
+        bw = bench_backward(st, steps, warmup)
+        out["backward"] = {k: bw[k] for k in ("ms_per_step", "tokens_per_s", "achieved_tflops",
+                                               "roofline", "path_roofline")}
+    out["wall_s"] = round(time.time() - t0, 1)
     del st
     torch.cuda.empty_cache()
     log(f"bench: {cfg.name} rank {out['rank']}: {ms:.3f} ms/step")
@@ -602,7 +613,7 @@ def main():
                          "the Zipf 16384-token hot rank, its dropless hot rank)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the backward measurement (fixed capacities only)")
+                    help="skip the backward measurements")
     ap.add_argument("--balance-alpha", type=float, default=None, metavar="ALPHA",
                     help="quantile balancing on: route with the bias -ALPHA (f - 1/E) from the "
                          "selection counts of the past --balance-window batches")
@@ -673,7 +684,7 @@ def main():
                "cpu_model": host_cpu(), "host_cpus": os.cpu_count()}
 
     backward = None
-    if not args.no_backward and d.cap_send and not d.dedup:
+    if not args.no_backward and not d.dedup:
         backward = bench_backward(st, args.steps, args.warmup)
         backward["train_step_ms"] = round(ms + backward["ms_per_step"], 4)
         backward["train_tokens_per_s"] = round(d.T / ((ms + backward["ms_per_step"]) * 1e-3), 1)
@@ -690,7 +701,8 @@ def main():
             and args.waves == "tokens":
         del st      # every figure of the main workload is taken above
         torch.cuda.empty_cache()
-        workloads = [workload_summary(configs.WORKLOADS[c], w, min(args.steps, 10), 2)
+        workloads = [workload_summary(configs.WORKLOADS[c], w, min(args.steps, 10), 2,
+                                      backward=not args.no_backward)
                      for c, w in OTHER_WORKLOADS if (c, w) != (args.config, args.rank)]
 
     tok_s = d.T / (ms * 1e-3)
