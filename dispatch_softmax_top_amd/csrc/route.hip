@@ -9,11 +9,12 @@
 // ascending).  Each candidate's order-preserving 32-bit image of its fp32
 // logit is its key; each lane keeps its candidates sorted by (key
 // descending, index ascending).  k rounds take the wave-wide largest head
-// (DPP maxima inside 16-lane rows, then four lane reads); if several lanes
-// hold that key (equal logits), a second reduction takes the lowest index
-// among them.  The winner's lane pops its head.  The first choice is the
-// largest logit m; gates are exp(l - m) / sum exp(l - m) over all E logits,
-// in fp32 (exp by the hardware exp2).
+// (DPP maxima inside 16-lane rows, two row broadcasts, one lane read: a
+// wave-uniform value); if several lanes hold that key (equal logits), a
+// second reduction takes the lowest index among them.  The winner's lane
+// pops its head, and choice j is written into lane j.  The first choice is
+// the largest logit m; gates are exp(l - m) / sum exp(l - m) over all E
+// logits, in fp32 (exp by the hardware exp2).
 //
 // Quantile balancing ("从玩具到前沿:训练一个真正的大模型,到底难在哪里",
 // section 四 and appendix A.2): a per-expert bias is added to the logits
@@ -28,58 +29,71 @@
 namespace moe {
 
 __device__ __forceinline__ uint32_t ord_f32(float f) {
-  uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0: equal logits compare equal
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0: equal logits compare equal
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);  // negative: ~u, else u | sign
 }
 
 __device__ __forceinline__ float unord_f32(uint32_t o) {
-  uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
-  return __uint_as_float(u);
+  return __uint_as_float(o ^ ((uint32_t)((int32_t)~o >> 31) | 0x80000000u));
 }
 
-// Reductions over the wave that every lane gets: DPP inside each 16-lane row
-// (swaps within quads, then rotations by 4 and 8; every lane reads a valid
-// lane, so the DPP folds into the operation itself), then lanes 0, 16, 32
-// and 48 are read and combined as (r0 op r1) op (r2 op r3).  The order of the
-// operations is fixed, so a sum is the same on every call.
+// Reductions over the wave with a wave-uniform result: DPP inside each
+// 16-lane row (swaps within quads, then rotations by 4 and 8; every lane
+// reads a valid lane, so the DPP folds into the operation itself and every
+// lane ends with its row's result), then row 0's lane 15 is folded into row
+// 1 and row 2's into row 3 (row_bcast:15), then lane 31 into rows 2 and 3
+// (row_bcast:31); lane 63 then holds ((r3 op r2) op (r1 op r0)) and is read
+// once.  `id` is the operation's identity (what the rows left out of a
+// broadcast fold in).  The order of the operations is fixed, so a sum is the
+// same on every call.
 template <class Op>
-__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, uint32_t id, Op op) {
   v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));   // [1,0,3,2]
   v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));   // [2,3,0,1]
   v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true));  // row_ror:4
   v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true));  // row_ror:8
-  const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
-  return op(op(r0, r1), op(r2, r3));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x142, 0xA, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  return wave_reduce_u32(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+  return wave_reduce_u32(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 __device__ __forceinline__ float wave_sum_dpp(float v) {
-  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
     return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
   }));
+}
+
+// v with lane j set to the wave-uniform x: one v_writelane, whose lane
+// select has to be M0 when the value is an SGPR.
+__device__ __forceinline__ int write_lane(int v, int x, int j) {
+  asm("s_mov_b32 m0, %2\n\ts_nop 0\n\tv_writelane_b32 %0, %1, m0"
+      : "+v"(v) : "s"(x), "s"(j) : "m0");
+  return v;
 }
 
 // k rounds over each lane's sorted candidates kc[0 .. N-1] (image
 // descending, index ascending; image 0: none): the largest head is the next
 // choice (equal images: the lowest index among the lanes holding it), and
-// its owner pops its head.  Lane j keeps choice j; round 0's choice carries
-// the largest logit m.  CHECK: the lanes kept only their N best candidates;
-// returns false if some lane ran out of them with rounds left (its next one
-// might still have been chosen).
+// its owner pops its head.  Choice j's index and image go to lane j of
+// my_idx and my_key; m_key is the image of the first choice (the largest
+// logit).  CHECK: the lanes kept only their N best candidates; returns false
+// if some lane ran out of them before the last round (its next one might
+// still have been chosen).
 template <int VPL, int N, int K, bool CHECK>
 __device__ __forceinline__ bool route_rounds(uint32_t (&kc)[N], int (&ic)[N], int k, int lane,
-                                             int &my_idx, float &my_logit, float &m) {
-  bool ok = true;
+                                             int &my_idx, uint32_t &my_key, uint32_t &m_key) {
+  const uint64_t empty0 = CHECK ? ballot(kc[0] == 0u) : 0;  // lanes that never held one
+  int owner = 0;
 #pragma unroll
   for (int j = 0; j < (K > 0 ? K : k); ++j) {
     const uint32_t best = wave_max_u32(kc[0]);
     const uint64_t holders = ballot(kc[0] == best);
-    int e, owner;
+    int e;
     if (__popcll(holders) == 1) {
       owner = (int)__builtin_ctzll(holders);
       e = __builtin_amdgcn_readlane(ic[0], owner);
@@ -95,20 +109,23 @@ __device__ __forceinline__ bool route_rounds(uint32_t (&kc)[N], int (&ic)[N], in
       }
       kc[N - 1] = 0u;
     }
-    if constexpr (CHECK)
-      if (j + 1 < (K > 0 ? K : k) && __builtin_amdgcn_readlane(kc[0], owner) == 0u) ok = false;
-    const float lg = unord_f32(best);
-    if (j == 0) m = lg;
-    if (lane == j) {
-      my_idx = e;
-      my_logit = lg;
-    }
+    if (j == 0) m_key = best;
+    my_idx = write_lane(my_idx, e, j);
+    my_key = (uint32_t)write_lane((int)my_key, (int)best, j);
   }
-  return ok;
+  if constexpr (CHECK) {
+    // a lane out of candidates is fine only if it ran out in the last round
+    const uint64_t out = ballot(kc[0] == 0u) & ~empty0 & ~(1ull << owner);
+    return out == 0;
+  }
+  return true;
 }
 
 // One wave per token; lane l holds experts l*VPL .. l*VPL + VPL - 1 (one run
-// of the logit row, so the loads are 8-byte pairs where E allows).
+// of the logit row, so the loads are 8-byte pairs where E allows).  Experts
+// past E are -inf logits: their image ties the lowest real one, and a tie
+// goes to the lower index, so they are never chosen (k <= E), and their
+// exp(-inf - m) adds nothing to the softmax sum.
 // bias: NULL, or [E] fp32 added to every token's logits (one fp32 rounding).
 // renorm: gates divided by their sum over the k chosen.
 // K > 0: k == K, the rounds unrolled; K == 0: any k.
@@ -159,7 +176,7 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
   int idx[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    key[i] = e0 + i < E ? ord_f32(v[i]) : 0u;
+    key[i] = ord_f32(v[i]);
     idx[i] = e0 + i;
   }
 #pragma unroll
@@ -176,22 +193,23 @@ __global__ __launch_bounds__(256) void route_topk_softmax(const float *__restric
     }
 
   int my_idx = 0;
-  float my_logit = 0.f, m = 0.f;
+  uint32_t my_key = 0u, m_key = 0u;
   if constexpr (K > 0) k = K;
   if constexpr (VPL > 3) {
     uint32_t hk[3] = {key[0], key[1], key[2]};
     int hi[3] = {idx[0], idx[1], idx[2]};
-    if (!route_rounds<VPL, 3, K, true>(hk, hi, k, lane, my_idx, my_logit, m))
-      route_rounds<VPL, VPL, K, false>(key, idx, k, lane, my_idx, my_logit, m);
+    if (!route_rounds<VPL, 3, K, true>(hk, hi, k, lane, my_idx, my_key, m_key))
+      route_rounds<VPL, VPL, K, false>(key, idx, k, lane, my_idx, my_key, m_key);
   } else {
-    route_rounds<VPL, VPL, K, false>(key, idx, k, lane, my_idx, my_logit, m);
+    route_rounds<VPL, VPL, K, false>(key, idx, k, lane, my_idx, my_key, m_key);
   }
   // softmax denominator over all E logits, then the gates of the k chosen
+  const float m = unord_f32(m_key);
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) s += (e0 + i < E) ? __expf(v[i] - m) : 0.f;
+  for (int i = 0; i < VPL; ++i) s += __expf(v[i] - m);
   s = wave_sum_dpp(s);
-  const float ej = __expf(my_logit - m);
+  const float ej = __expf(unord_f32(my_key) - m);
   // renorm: the k chosen probabilities over their sum, i.e. the softmax over
   // the chosen logits, from exp(l - the first choice's logit), in fp32
   const float g = renorm ? ej / wave_sum_dpp(lane < k ? ej : 0.f) : ej / s;
