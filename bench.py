@@ -7,8 +7,8 @@ route the shard's logits, project and pack its pools, bank the receive
 buffer (pools that all source shards packed for this rank -- built once,
 untimed, by a device-copy loopback that stands in for the all-to-all),
 run the six local experts, and combine (identity return loopback).  Bank +
-expert FFN and the shared experts run on two more streams beside route +
-pack (no data dependence between them); the combine waits for all three.
+expert FFN run on a second stream beside route + pack + the shared experts
+(no data dependence between them); the combine waits for both.
 
 The line's value is the 4096-token shard at rank 0 (mean over the K timed
 steps; the median and the spread are in step_ms).  Beside it: the dominant
@@ -119,8 +119,8 @@ def setup(cfg, rank=0, device="cuda", seed=0, progress=False, keep_logits=False)
     st.snd = share.Sender(d, device)
     st.rcv = share.Receiver(d, st.n_recv_rows, device)
     st.cmb = share.Combiner(d, device)
-    st.s_ffn, st.s_shared = torch.cuda.Stream(device), torch.cuda.Stream(device)
-    st.ev_start, st.ev_ffn, st.ev_shared = (torch.cuda.Event() for _ in range(3))
+    st.s_ffn = torch.cuda.Stream(device)
+    st.ev_start, st.ev_ffn = torch.cuda.Event(), torch.cuda.Event()
     torch.cuda.synchronize()
     st.bal = None  # quantile balancing state (bench --balance-alpha)
     return st
@@ -187,27 +187,25 @@ def host_cpu():
 
 
 def step(st):
-    """One pass of the path.  Bank + expert FFN (they read the receive buffer
-    of the last exchange) and the shared experts (they read x) do not depend
-    on this step's route and pack, so they run on two more streams, started
-    behind everything already on the main stream; the combine waits for
-    both."""
+    """One pass of the path.  Bank + expert FFN read the receive buffer of the
+    last exchange, not this step's route and pack, so they run on a second
+    stream, started behind everything already on the main stream, which runs
+    route, pack and then the shared experts; the combine waits for the FFN.
+    Measured against one stream, three streams (the shared experts on their
+    own) and other splits at four workloads, this one was fastest or within
+    1.5% of the fastest at each."""
     import torch
     main = torch.cuda.current_stream()
     st.ev_start.record(main)
     st.s_ffn.wait_event(st.ev_start)
-    st.s_shared.wait_event(st.ev_start)
     with torch.cuda.stream(st.s_ffn):
         st.rcv.bank_rows(st.rank, st.recv, st.recv_offsets)
         st.rcv.ffn(st.wg, st.wu, st.wd)
         st.ev_ffn.record(st.s_ffn)
-    with torch.cuda.stream(st.s_shared):
-        st.cmb.shared(st.x, st.wsg, st.wsu)
-        st.ev_shared.record(st.s_shared)
     route_shard(st)
     st.snd.pack(st.x, st.wld)
+    st.cmb.shared(st.x, st.wsg, st.wsu)
     main.wait_event(st.ev_ffn)
-    main.wait_event(st.ev_shared)
     st.cmb.combine_shared(st.rcv.ret, st.recv_offsets, st.snd, st.wlu, st.wsd)
 
 
@@ -724,7 +722,7 @@ def main():
                    "latent": d.latent, "n_experts": d.n_experts, "n_ranks": d.n_ranks,
                    "top_k": d.top_k, "n_waves": d.n_waves, "d_ff": d.d_ff,
                    "n_shared": d.n_shared, "cap_send": d.cap_send, "cap_recv": d.cap_recv,
-                   "source_shards": cfg.n_shards, "streams": 1 if args.serial else 3,
+                   "source_shards": cfg.n_shards, "streams": 1 if args.serial else 2,
                    "waves": cfg.waves, "dedup": bool(d.dedup),
                    "balance": None if args.balance_alpha is None else
                    {"alpha": args.balance_alpha, "window": args.balance_window}},

@@ -161,11 +161,12 @@ int64_t moe_workspace_bytes(const moe_dims *d, int call, int64_t n_rows) {
       if (items < 0) return fail(MOE_ERR_INVALID, "moe_workspace_bytes: n_rows < 0");
       return rank_ws_bytes(items, (int)(W * El));
     }
-    case MOE_CALL_FFN: {  // intermediate h, return-row flags, split partial tiles
+    case MOE_CALL_FFN: {  // intermediate h, return-row flags, GEMM work queue, split partial tiles
       int64_t bank_rows = ragged(*d) ? n_rows : W * El * d->cap_recv;
       int64_t ret_rows = ragged(*d) ? n_rows : R * W * d->cap_send * ret_slots(*d);
       if (bank_rows < 0) return fail(MOE_ERR_INVALID, "moe_workspace_bytes: n_rows < 0");
-      return ffn_h_bytes(*d, bank_rows) + ffn_flag_bytes(ret_rows) + gemm_split_bytes();
+      return ffn_h_bytes(*d, bank_rows) + ffn_flag_bytes(ret_rows) + gemm_queue_bytes() +
+             gemm_split_bytes();
     }
     case MOE_CALL_COMBINE:  // shared experts' intermediate, split partial tiles
       return shared_h_bytes(*d) + gemm_split_bytes();

@@ -577,7 +577,7 @@ extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
   MOE_TRY(gemm_expert_swiglu_bwd(*d, bank, boff, bfill, nb, w_gate, w_up, w.dH, w.Hb, w.dAB,
                                  w.part, s));
   // d_u = d_a . W_g + d_b . W_u, scattered to the receive rows; others zero
-  MOE_TRY(ret_rows_mark(bank_src, nb, w.flags, nr, s));
+  MOE_TRY(ret_rows_mark(bank_src, nb, w.flags, nr, nullptr, s));
   MOE_TRY(gemm_grouped_nt("gemm_bwd_d_u", "gemm_bwd_d_u_tail", *d, w.dAB, 2 * F, boff, bfill,
                           bank_src, nb, w.WguT, L, d_recv, nr, w.part, s));
   MOE_TRY(ret_rows_zero_unmarked(w.flags, d_recv, L, nr, s));

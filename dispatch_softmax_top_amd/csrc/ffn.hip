@@ -5,16 +5,20 @@
 //
 // Kernels, in stream order:
 //   ffn_flags_clear / ffn_flags_mark  which return rows will receive a result
+//                        (the clear also zeroes the GEMMs' queue counters)
 //   gemm_expert_swiglu   grouped over (wave, expert) bank groups -> h (ws)
 //   gemm_expert_down     grouped, rows scattered to their receive position
 //   ffn_zero_rows        every other return row set to zero
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace moe {
 
-__global__ __launch_bounds__(256) void ffn_flags_clear(int32_t *flags, int64_t n) {
+__global__ __launch_bounds__(256) void ffn_flags_clear(int32_t *flags, int64_t n, int32_t *zero16) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) flags[i] = 0;
+  if (zero16 && i < 16) zero16[i] = 0;
 }
 
 __global__ __launch_bounds__(256) void ffn_flags_mark(const int32_t *__restrict__ bank_src,
@@ -37,9 +41,10 @@ __global__ __launch_bounds__(256) void ffn_zero_rows(const int32_t *__restrict__
 }
 
 int ret_rows_mark(const int32_t *bank_src, int64_t n_bank, int32_t *flags, int64_t n_ret,
-                  hipStream_t s) {
-  MOE_TRY(launch("ffn_flags_clear", ffn_flags_clear, dim3((unsigned)cdiv(n_ret, 256)), dim3(256),
-                 0, s, flags, n_ret));
+                  int32_t *zero16, hipStream_t s) {
+  const int64_t blocks = std::max<int64_t>(cdiv(n_ret, 256), zero16 ? 1 : 0);
+  MOE_TRY(launch("ffn_flags_clear", ffn_flags_clear, dim3((unsigned)blocks), dim3(256), 0, s,
+                 flags, n_ret, zero16));
   return launch("ffn_flags_mark", ffn_flags_mark, dim3((unsigned)cdiv(n_bank, 256)), dim3(256), 0,
                 s, bank_src, n_bank, flags, n_ret);
 }
@@ -89,17 +94,18 @@ extern "C" int moe_expert_ffn(const moe_dims *d, const moe_bf16 *bank, const int
     return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %lld < %lld bytes",
                 (long long)ws_bytes, (long long)need);
   hipStream_t s = (hipStream_t)stream;
-  // workspace: intermediate h, return-row flags, partial tiles of the
-  // GEMMs' split last rounds (shared by both: stream order)
+  // workspace: intermediate h, return-row flags, the GEMMs' work queue,
+  // partial tiles of their split last rounds (shared by both: stream order)
   const int64_t ret_rows = rg ? n_bank_rows : n_ret_rows;
   uint16_t *H = (uint16_t *)ws;
   int32_t *flags = (int32_t *)((char *)ws + ffn_h_bytes(*d, n_bank_rows));
-  float *part = (float *)((char *)flags + ffn_flag_bytes(ret_rows));
+  int32_t *queue = (int32_t *)((char *)flags + ffn_flag_bytes(ret_rows));
+  float *part = (float *)((char *)queue + gemm_queue_bytes());
 
-  MOE_TRY(ret_rows_mark(bank_src, n_bank_rows, flags, n_ret_rows, s));
+  MOE_TRY(ret_rows_mark(bank_src, n_bank_rows, flags, n_ret_rows, queue, s));
   MOE_TRY(gemm_expert_swiglu(*d, bank, bank_offsets, bfill, n_bank_rows, w_gate, w_up, H, part,
-                             s));
+                             queue, s));
   MOE_TRY(gemm_expert_down(*d, H, bank_offsets, bfill, bank_src, n_bank_rows, w_down, ret,
-                           n_ret_rows, part, s));
+                           n_ret_rows, part, queue, s));
   return ret_rows_zero_unmarked(flags, ret, d->latent, n_ret_rows, s);
 }

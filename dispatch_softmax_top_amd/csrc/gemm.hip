@@ -33,12 +33,70 @@ constexpr int GSPLIT_MAX = 8;      // parts per split tile at most
 constexpr int GSPLIT_MIN_KT = 16;  // K tiles per part at least
 constexpr int GSPLIT_UNITS = 256;  // partial tiles a split buffer holds
 
+// Work queue of a persistent grouped kernel.  Without one, block k runs
+// units k, k + grid, k + 2 grid, ... .  With one, the units are dealt per
+// XCD (block k sits in XCD k % 8, whose units are 8 l + k % 8): block k runs
+// k, k + grid and k + 2 grid, and then one unit per ticket it draws from its
+// XCD's counter, so that blocks that started late (the CUs busy with another
+// stream's kernel) or run slow tiles take fewer units.  A ticket drawn
+// during the block's tile n names its tile n + 3: unit 8 (3 grid / 8 +
+// ticket) + k % 8.  Thread 0 draws it before the tile's main loop and
+// stores it after; the other waves load it after the next tile's main loop.
+// By then the store is complete (thread 0's wave waited for copies issued
+// after it, in issue order) and a barrier lies between, and the value is
+// used one tile later still, so neither the atomic nor the load is waited
+// for.  A block's units only grow, so the first one past the end ends it.
+struct GQueue {
+  int32_t *count;  // [8] tickets drawn per XCD, zero at launch; NULL: no queue
+  int32_t *slot;   // [2][grid] tickets passed from thread 0 to its block
+};
+constexpr int GQ_MAX_GRID = 1024;                       // blocks a queue serves
+constexpr int64_t GQ_BYTES = 256 + 2 * GQ_MAX_GRID * 4;  // two counter sets, slots
+
 struct GSplit {
   float *part;    // partial tiles (see g_part_store); NULL: no split
   int ncu;        // CUs of the device
   int max_units;  // partial tiles the buffer holds
   int max_parts;  // parts per split tile at most (K tiles / GSPLIT_MIN_KT)
+  GQueue q;       // persistent grouped kernels only
 };
+
+// A persistent block's unit sequence (GQueue).
+struct GSeq {
+  int next;  // unit of the block's next tile (wave-uniform)
+  int tk;    // ticket drawn during the current tile (thread 0)
+  int n;     // tiles begun before the current one
+};
+
+__device__ __forceinline__ GSeq gseq_start() {
+  return GSeq{(int)(blockIdx.x + gridDim.x), 0, 0};
+}
+
+// Before the current tile's main loop.
+__device__ __forceinline__ void gseq_draw(const GQueue &q, GSeq &s) {
+  if (q.count && threadIdx.x == 0) s.tk = atomicAdd(q.count + blockIdx.x % 8, 1);
+}
+
+// After the main loop: hand the ticket to the block.
+__device__ __forceinline__ void gseq_post(const GQueue &q, const GSeq &s) {
+  if (q.count && threadIdx.x == 0)
+    __hip_atomic_store(q.slot + (s.n & 1) * gridDim.x + blockIdx.x, s.tk, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// After the tile's closing barrier, the next tile's unit (s.next, read
+// before the barrier) taken: fetch the unit of the tile after it.
+__device__ __forceinline__ void gseq_fetch(const GQueue &q, GSeq &s) {
+  if (!q.count || s.n == 0) {
+    s.next = (int)blockIdx.x + (s.n + 2) * (int)gridDim.x;
+  } else {
+    const int tk = __hip_atomic_load(q.slot + ((s.n - 1) & 1) * gridDim.x + blockIdx.x,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.next = __builtin_amdgcn_readfirstlane(8 * (3 * (int)(gridDim.x / 8) + tk) +
+                                            (int)(blockIdx.x % 8));
+  }
+  ++s.n;
+}
 
 struct GUnit {
   int tile;    // logical tile
@@ -941,17 +999,21 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
     __builtin_amdgcn_sched_barrier(0);
     gemm_mainloop_issue(ops, k1 - k0, lds);
     GAcc acc;
+    GSeq seq = gseq_start();
     for (;;) {
       const int m0 = ((int)(threadIdx.x >> 6) / GWN) * GWTM;
       const int32_t r0 = wave_tile_row(t, m0 + lane_id()), r1 = wave_tile_row(t, m0 + 64 + lane_id());
       const int ft = t.nt, nparts = u.nparts, punit = u.tail * u.nparts + u.part, kt = k1 - k0;
+      gseq_draw(g.sp.q, seq);
       gemm_zero(acc);
       gemm_mainloop_rest(ops, kt, acc, lds);
-      b += gridDim.x;
+      gseq_post(g.sp.q, seq);
+      b = seq.next;
       const bool more =
           g_unit(g.sp, gr.total, b, u) && group_tile_regs(g.grp, gr, g.ftiles, u.tile, t);
       __builtin_amdgcn_s_barrier();  // every wave is past its last read of the ring
       __builtin_amdgcn_sched_barrier(0);
+      gseq_fetch(g.sp.q, seq);
       if (more) {
         g_part_range(g.ktiles, u, k0, k1);
         ops = swiglu_ops(g, [&](int m) { return t.row(m); }, t.rows, t.expert, t.nt, k0);
@@ -1081,19 +1143,23 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
   __builtin_amdgcn_sched_barrier(0);
   gemm_mainloop_issue(ops, k1 - k0, lds);
   GAcc acc;
+  GSeq seq = gseq_start();
   for (;;) {
     // receive rows of this wave's tile rows, loaded while the main loop runs
     const int m0 = ((int)(threadIdx.x >> 6) / GWN) * GWTM;
     const int32_t d0 = down_dst(g, u, t, m0 + lane_id()), d1 = down_dst(g, u, t, m0 + 64 + lane_id());
     const int nt = t.nt, nparts = u.nparts, punit = u.tail * u.nparts + u.part, kt = k1 - k0;
+    gseq_draw(g.sp.q, seq);
     gemm_zero(acc);
     gemm_mainloop_rest(ops, kt, acc, lds);
+    gseq_post(g.sp.q, seq);
     // d0, d1 waited for here, while no copy is outstanding
     asm volatile("" ::"v"(d0), "v"(d1));
-    b += gridDim.x;
+    b = seq.next;
     const bool more = g_unit(g.sp, gr.total, b, u) && group_tile_regs(g.grp, gr, g.tn, u.tile, t);
     __builtin_amdgcn_s_barrier();  // every wave is past its last read of the ring
     __builtin_amdgcn_sched_barrier(0);
+    gseq_fetch(g.sp.q, seq);
     if (more) {
       g_part_range(g.ktiles, u, k0, k1);
       ops = down_ops(g, t, k0);
@@ -1314,16 +1380,23 @@ static int64_t grouped_tiles_bound(const moe_dims &d, int64_t n_bank_rows, int t
 // extra blocks a split can add; the tail kernel gets GTM blocks for each of
 // ncu / 2 possible split tiles (a split never has more) and exits where
 // there is none.
+// queue: counters and slots of a work queue (GQueue; NULL: static units),
+// the counters zeroed before the launch; used when the grid is persistent,
+// a multiple of 8 and at most GQ_MAX_GRID blocks.
 template <class Args>
 static int grouped(const char *name, const char *tail_name, void (*k)(Args),
                    void (*tk)(Args), int64_t bound, int ktiles, Args &a, float *part,
-                   hipStream_t s, bool persistent) {
+                   hipStream_t s, bool persistent, int32_t *queue_count = nullptr,
+                   int32_t *queue_slot = nullptr) {
   MOE_TRY(make_split(part, ktiles, a.sp));
   int ncu = 0;
   MOE_TRY(cu_count(&ncu));
   const int64_t units = bound + (a.sp.part ? a.sp.ncu : 0);
   // persistent: one block per CU at most, a multiple of 8 (the XCDs)
   const int64_t grid = persistent ? std::min<int64_t>(units, std::max(8, ncu / 8 * 8)) : units;
+  const bool queued = persistent && queue_count && queue_slot && grid % 8 == 0 &&
+                      grid <= GQ_MAX_GRID && units > grid;
+  a.sp.q = queued ? GQueue{queue_count, queue_slot} : GQueue{nullptr, nullptr};
   MOE_TRY(launch(name, k, dim3((unsigned)grid), dim3(GNT), 0, s, a));
   if (!a.sp.part || a.sp.ncu < 2) return MOE_OK;
   return launch(tail_name, tk, dim3((unsigned)(a.sp.ncu / 2 * GTM)), dim3(GNT), 0, s, a);
@@ -1333,7 +1406,7 @@ static int expert_swiglu(const char *name, const char *tail_name, void (*k)(Swig
                          void (*tk)(SwigluArgs), SwigluArgs &a, const moe_dims &d,
                          const uint16_t *bank, const int64_t *bank_offsets, const int32_t *bfill,
                          int64_t n_bank_rows, const uint16_t *wg, const uint16_t *wu, uint16_t *H,
-                         float *part, hipStream_t s) {
+                         float *part, hipStream_t s, int32_t *queue = nullptr) {
   a.A = bank;
   a.lda = d.latent;
   a.ktiles = d.latent / GBK;
@@ -1347,16 +1420,19 @@ static int expert_swiglu(const char *name, const char *tail_name, void (*k)(Swig
   a.grp = group_args(d, bank_offsets, bfill, n_bank_rows, std::max(d.latent, d.d_ff));
   if (((uintptr_t)H & 15) || (a.ldh & 7)) return fail(MOE_ERR_INVALID, "%s: H rows not 16-byte aligned", name);
   return grouped(name, tail_name, k, tk, grouped_tiles_bound(d, n_bank_rows, a.ftiles), a.ktiles,
-                 a, part, s, a.dH == nullptr);
+                 a, part, s, a.dH == nullptr, queue, queue ? queue + 64 : nullptr);
 }
+
+int64_t gemm_queue_bytes() { return GQ_BYTES; }
 
 int gemm_expert_swiglu(const moe_dims &d, const uint16_t *bank, const int64_t *bank_offsets,
                        const int32_t *bfill, int64_t n_bank_rows, const uint16_t *wg,
-                       const uint16_t *wu, uint16_t *H, float *part, hipStream_t s) {
+                       const uint16_t *wu, uint16_t *H, float *part, int32_t *queue,
+                       hipStream_t s) {
   SwigluArgs a{};
   return expert_swiglu("gemm_expert_swiglu", "gemm_expert_swiglu_tail",
                        gemm_expert_swiglu_kernel<false>, gemm_expert_swiglu_tail_kernel<false>, a,
-                       d, bank, bank_offsets, bfill, n_bank_rows, wg, wu, H, part, s);
+                       d, bank, bank_offsets, bfill, n_bank_rows, wg, wu, H, part, s, queue);
 }
 
 int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int64_t *bank_offsets,
@@ -1380,7 +1456,8 @@ int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int64_
 static int grouped_nt(const char *name, const char *tail_name, const moe_dims &d,
                       const uint16_t *A, int K, const int64_t *bank_offsets, const int32_t *bfill,
                       const int32_t *dst, int64_t n_bank_rows, const uint16_t *B, int N,
-                      uint16_t *out, int64_t n_out, float *part, hipStream_t s) {
+                      uint16_t *out, int64_t n_out, float *part, hipStream_t s,
+                      int32_t *queue = nullptr) {
   if (K % GBK) return fail(MOE_ERR_UNSUPPORTED, "%s: K %% %d != 0", name, GBK);
   DownArgs a{};
   a.n_ret = n_out;
@@ -1395,15 +1472,16 @@ static int grouped_nt(const char *name, const char *tail_name, const moe_dims &d
   a.ret = out;
   if (((uintptr_t)out & 15) || (N & 7)) return fail(MOE_ERR_INVALID, "%s: output rows not 16-byte aligned", name);
   return grouped(name, tail_name, gemm_expert_down_kernel, gemm_expert_down_tail_kernel,
-                 grouped_tiles_bound(d, n_bank_rows, a.tn), a.ktiles, a, part, s, true);
+                 grouped_tiles_bound(d, n_bank_rows, a.tn), a.ktiles, a, part, s, true,
+                 queue ? queue + 8 : nullptr, queue ? queue + 64 : nullptr);
 }
 
 int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_offsets,
                      const int32_t *bfill, const int32_t *bank_src, int64_t n_bank_rows,
                      const uint16_t *wd, uint16_t *ret, int64_t n_ret, float *part,
-                     hipStream_t s) {
+                     int32_t *queue, hipStream_t s) {
   return grouped_nt("gemm_expert_down", "gemm_expert_down_tail", d, H, d.d_ff, bank_offsets, bfill,
-                    bank_src, n_bank_rows, wd, d.latent, ret, n_ret, part, s);
+                    bank_src, n_bank_rows, wd, d.latent, ret, n_ret, part, s, queue);
 }
 
 int gemm_grouped_nt(const char *name, const char *tail_name, const moe_dims &d,

@@ -38,21 +38,28 @@ int gemm_shared_swiglu(int M, const uint16_t *x, int64_t ldx, int K, const uint1
                        const uint16_t *wu, int S, int F, uint16_t *H, float *part,
                        hipStream_t s);
 
+// Work queue of the two grouped FFN GEMMs (gemm_queue_bytes(), 256-byte
+// aligned): counters [0, 16) zeroed before the SwiGLU GEMM (ret_rows_mark
+// does it), slots from int 64 on.  NULL: static unit order.
+int64_t gemm_queue_bytes();
+
 // Routed experts over the bank's groups (group g uses local expert g % E_l):
 // H rows = bank rows, H[:, 0:F] = bf16(silu(u.Wg^T) * (u.Wu^T)).
 int gemm_expert_swiglu(const moe_dims &d, const uint16_t *bank, const int64_t *bank_offsets,
                        const int32_t *bfill, int64_t n_bank_rows, const uint16_t *wg,
-                       const uint16_t *wu, uint16_t *H, float *part, hipStream_t s);
+                       const uint16_t *wu, uint16_t *H, float *part, int32_t *queue,
+                       hipStream_t s);
 // ret[bank_src[r]] = bf16(H[r] . Wd^T) for every kept bank row r.
 int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_offsets,
                      const int32_t *bfill, const int32_t *bank_src, int64_t n_bank_rows,
                      const uint16_t *wd, uint16_t *ret, int64_t n_ret, float *part,
-                     hipStream_t s);
+                     int32_t *queue, hipStream_t s);
 
 // Return rows: flags[r] = 1 for every row some kept bank row writes (bank_src),
-// then every unflagged row of ret [n_ret][L] set to zero.
+// then every unflagged row of ret [n_ret][L] set to zero.  zero16: NULL, or
+// 16 ints cleared with the flags (the grouped GEMMs' queue counters).
 int ret_rows_mark(const int32_t *bank_src, int64_t n_bank, int32_t *flags, int64_t n_ret,
-                  hipStream_t s);
+                  int32_t *zero16, hipStream_t s);
 int ret_rows_zero_unmarked(const int32_t *flags, uint16_t *ret, int L, int64_t n_ret,
                            hipStream_t s);
 

@@ -147,7 +147,7 @@ def test_full_share(orc, name, cfg, which, full):
     assert torch.equal(st.snd.pools[prow, :2 * L].contiguous().view(torch.int16).view(-1, L),
                        st.snd.z.view(torch.int16)[tok])
 
-    # ---- repeats: ten steps on three streams, one on one stream, bit-identical
+    # ---- repeats: ten steps on two streams, one on one stream, bit-identical
     if full:
         ref = _outputs(st)
         for i in range(9):
