@@ -19,8 +19,8 @@
 //   2 (default): ping-pong.  The waves of rows 0..127 (group 0, waves 0-3,
 //      one per SIMD) and of rows 128..255 (group 1, waves 4-7) alternate
 //      roles every phase: one group runs the 16 MFMAs of one K tile (32
-//      wide) from registers while the other group issues copies and reads
-//      its fragments of the next tile from LDS.  Each SIMD then always has
+//      wide) from registers while the other group reads its fragments of
+//      the next tile from LDS and issues copies.  Each SIMD then always has
 //      one wave with MFMAs ready, and a barrier falls while the other wave's
 //      last MFMA is still in the pipe.  K tiles sit in a 5-stage ring
 //      (5 x 32 KB = 160 KB), issued 4 tiles ahead, so about 7 phases of MFMA
@@ -341,9 +341,10 @@ __device__ __forceinline__ void g_ring_step(const Ops &o, int kt, int ktiles, GA
 // ---- ping-pong (MOE_GEMM_CFG 2)
 //
 // Phases 2s and 2s + 1 belong to K tile s.  Phase 2s: group 0 runs tile s's
-// MFMAs; group 1 copies A of tile s + 4 and reads its fragments of tile s.
-// Phase 2s + 1: group 1 runs tile s's MFMAs; group 0 copies B of tile s + 4
-// and reads its fragments of tile s + 1.  Every phase ends in a barrier
+// MFMAs; group 1 reads its fragments of tile s and copies A of tile s + 4.
+// Phase 2s + 1: group 1 runs tile s's MFMAs; group 0 reads its fragments of
+// tile s + 1 and copies B of tile s + 4.  (Fragment reads go first: the
+// copies' issue then no longer delays them; measured 0.4-3% faster.)  Every phase ends in a barrier
 // (reads of the phase are waited for before it: lgkmcnt).  Tile s is read in
 // phases 2s - 1 and 2s, so it must have landed at the barrier closing phase
 // 2s - 2 (each thread first waits for its own copies of it: vmcnt), and its
@@ -382,8 +383,8 @@ __device__ __forceinline__ void g_pp_tile_g0(const Ops &o, int s, int ktiles, GA
   // tile s + 1 lands before phase 2s + 1; B is copied up to tile s + 3
   g_wait_tiles<GCB>(min(GPP_AHEAD - 2, ktiles - 2 - s));
   g_pp_sync();
-  if (s + GPP_AHEAD < ktiles) g_copy_operand(o.b, s + GPP_AHEAD, L.B[(S + GPP_AHEAD) % GNST]);
   if (s + 1 < ktiles) g_pp_frags(L.A[(S + 1) % GNST], L.B[(S + 1) % GNST], a, b);
+  if (s + GPP_AHEAD < ktiles) g_copy_operand(o.b, s + GPP_AHEAD, L.B[(S + GPP_AHEAD) % GNST]);
   // nothing is shared after the last phase (a later call starts with a barrier)
   if (s + 1 < ktiles) g_pp_sync();
 }
@@ -394,8 +395,8 @@ __device__ __forceinline__ void g_pp_tile_g1(const Ops &o, int s, int ktiles, GA
                                              const GemmLds &L, bf16x8 (&a)[2][GTM],
                                              bf16x8 (&b)[2][GTN]) {
   if (s >= ktiles) return;
-  if (s + GPP_AHEAD < ktiles) g_copy_operand(o.a, s + GPP_AHEAD, L.A[(S + GPP_AHEAD) % GNST]);
   g_pp_frags(L.A[S], L.B[S], a, b);
+  if (s + GPP_AHEAD < ktiles) g_copy_operand(o.a, s + GPP_AHEAD, L.A[(S + GPP_AHEAD) % GNST]);
   // tile s + 1 lands before phase 2s + 1; A is copied up to tile s + 4
   g_wait_tiles<GCA>(min(GPP_AHEAD - 1, ktiles - 2 - s));
   g_pp_sync();
@@ -456,11 +457,11 @@ __device__ __forceinline__ void gemm_mainloop_rest(const Ops &o, int ktiles, GAc
         g_pp_tile_g1<4>(o, s + 4, ktiles, acc, L, a, b);
       }
     } else {
-      // tile 0 landed; phase -1: B of tile 3 and the fragments of tile 0
+      // tile 0 landed; phase -1: the fragments of tile 0 and B of tile 3
       g_wait_tiles<GCB>(min(GPP_AHEAD - 2, ktiles - 1));
       g_pp_sync();
-      if (GPP_AHEAD - 1 < ktiles) g_copy_operand(o.b, GPP_AHEAD - 1, L.B[GPP_AHEAD - 1]);
       g_pp_frags(L.A[0], L.B[0], a, b);
+      if (GPP_AHEAD - 1 < ktiles) g_copy_operand(o.b, GPP_AHEAD - 1, L.B[GPP_AHEAD - 1]);
       g_pp_sync();
       for (int s = 0; s < ktiles; s += GNST) {
         g_pp_tile_g0<0>(o, s, ktiles, acc, L, a, b);
