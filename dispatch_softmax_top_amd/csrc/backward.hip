@@ -303,9 +303,11 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
     if (lane + 64 * c < nch) o[lane + 64 * c] = v[c];
 }
 
-__global__ __launch_bounds__(256) void iota_kernel(int32_t *o, int64_t n) {
+// o[i] = i; zero16: NULL, or 16 ints set to zero (a GEMM work queue's counters).
+__global__ __launch_bounds__(256) void iota_kernel(int32_t *o, int64_t n, int32_t *zero16) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) o[i] = (int32_t)i;
+  if (zero16 && i < 16) zero16[i] = 0;
 }
 
 // Dispatch on the 16-byte chunks per lane a latent row needs (latent <= 8192).
@@ -358,7 +360,7 @@ static int64_t combine_bwd_ws(const moe_dims &d, char *base, CombineBwdWs &w) {
 
 struct FfnBwdWs {
   uint16_t *WdT, *WguT, *dY, *dH, *Hb, *dAB, *dYT, *HT, *dABT, *UT;
-  int32_t *iota, *flags;
+  int32_t *iota, *flags, *queue;
   float *part;
 };
 // Bank rows and receive rows of the expert backward: fixed mode from the
@@ -391,6 +393,7 @@ static int64_t ffn_bwd_ws(const moe_dims &d, int64_t n_rows, char *base, FfnBwdW
   w.UT = c.take<uint16_t>(blocks * L * Kp);
   w.iota = c.take<int32_t>(nb);
   w.flags = c.take<int32_t>(nr);
+  w.queue = c.take<int32_t>(gemm_queue_bytes() / 4);
   w.part = c.take<float>(gemm_split_bytes() / 4);
   return c.off;
 }
@@ -569,17 +572,19 @@ extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
     return launch("gather_bank_grad", gather_rows_kernel<CH>, dim3((unsigned)cdiv(nb, 4)),
                   dim3(256), 0, s, d_ret, nr, bank_src, nb, w.dY, L);
   }));
-  MOE_TRY(launch("iota", iota_kernel, dim3((unsigned)cdiv(nb, 256)), dim3(256), 0, s, w.iota, nb));
+  // (the iota kernel also zeroes the grouped products' queue counters)
+  MOE_TRY(launch("iota", iota_kernel, dim3((unsigned)std::max<int64_t>(cdiv(nb, 256), 1)),
+                 dim3(256), 0, s, w.iota, nb, w.queue));
   // d_h = dy . W_d (grouped, bank order)
   MOE_TRY(gemm_grouped_nt("gemm_bwd_d_h", "gemm_bwd_d_h_tail", *d, w.dY, L, boff, bfill, w.iota,
-                          nb, w.WdT, F, w.dH, nb, w.part, s));
+                          nb, w.WdT, F, w.dH, nb, w.part, w.queue, s));
   // a, b recomputed; d_a | d_b and h
   MOE_TRY(gemm_expert_swiglu_bwd(*d, bank, boff, bfill, nb, w_gate, w_up, w.dH, w.Hb, w.dAB,
                                  w.part, s));
   // d_u = d_a . W_g + d_b . W_u, scattered to the receive rows; others zero
-  MOE_TRY(ret_rows_mark(bank_src, nb, w.flags, nr, nullptr, s));
+  MOE_TRY(ret_rows_mark(bank_src, nb, w.flags, nr, w.queue, s));
   MOE_TRY(gemm_grouped_nt("gemm_bwd_d_u", "gemm_bwd_d_u_tail", *d, w.dAB, 2 * F, boff, bfill,
-                          bank_src, nb, w.WguT, L, d_recv, nr, w.part, s));
+                          bank_src, nb, w.WguT, L, d_recv, nr, w.part, w.queue, s));
   MOE_TRY(ret_rows_zero_unmarked(w.flags, d_recv, L, nr, s));
   // weight gradients: per local expert, summed over its rows of every wave.
   // Fixed: expert e's rows packed into its own block of Kp columns; ragged:

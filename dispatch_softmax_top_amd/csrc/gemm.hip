@@ -90,6 +90,7 @@ __device__ __forceinline__ void gseq_fetch(const GQueue &q, GSeq &s) {
   if (!q.count || s.n == 0) {
     s.next = (int)blockIdx.x + (s.n + 2) * (int)gridDim.x;
   } else {
+    asm volatile("" ::: "memory");  // the load stays behind the barrier before this call
     const int tk = __hip_atomic_load(q.slot + ((s.n - 1) & 1) * gridDim.x + blockIdx.x,
                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s.next = __builtin_amdgcn_readfirstlane(8 * (3 * (int)(gridDim.x / 8) + tk) +
@@ -1487,9 +1488,9 @@ int gemm_expert_down(const moe_dims &d, const uint16_t *H, const int64_t *bank_o
 int gemm_grouped_nt(const char *name, const char *tail_name, const moe_dims &d,
                     const uint16_t *A, int K, const int64_t *bank_offsets, const int32_t *bfill,
                     const int32_t *dst, int64_t n_bank_rows, const uint16_t *B, int N,
-                    uint16_t *out, int64_t n_out, float *part, hipStream_t s) {
+                    uint16_t *out, int64_t n_out, float *part, int32_t *queue, hipStream_t s) {
   return grouped_nt(name, tail_name, d, A, K, bank_offsets, bfill, dst, n_bank_rows, B, N, out,
-                    n_out, part, s);
+                    n_out, part, s, queue);
 }
 
 int gemm_nt(const char *name, const char *tail_name, int M, int N, int nseg,

@@ -128,11 +128,12 @@ int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int64_
                            const uint16_t *dH, uint16_t *H, uint16_t *AB, float *part,
                            hipStream_t s);
 // Grouped over the bank's groups (bank_offsets: ragged mode, else NULL):
-// out[dst[r]] = A[r] . B_j^T, A [bank rows][K], B [E_l][N][K].
+// out[dst[r]] = A[r] . B_j^T, A [bank rows][K], B [E_l][N][K].  queue: as
+// for gemm_expert_down (counters 8..15 zeroed before the launch), or NULL.
 int gemm_grouped_nt(const char *name, const char *tail_name, const moe_dims &d,
                     const uint16_t *A, int K, const int64_t *bank_offsets, const int32_t *bfill,
                     const int32_t *dst,
                     int64_t n_bank_rows, const uint16_t *B, int N, uint16_t *out, int64_t n_out,
-                    float *part, hipStream_t s);
+                    float *part, int32_t *queue, hipStream_t s);
 
 }  // namespace moe
