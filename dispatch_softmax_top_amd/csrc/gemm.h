@@ -529,6 +529,31 @@ __device__ __forceinline__ int g_stage_chunk(int row, int c) {
   return NJ == 2 ? c ^ (((row >> 1) & 1) << 2) : c;
 }
 
+// 4 x 4 transpose inside each group of 4 lanes (4 neighbouring columns): in,
+// p0 = rows 0, 1 and p1 = rows 2, 3 of one 4-row group of this lane's column
+// (bf16 pairs); out, (o0, o1) = columns col4 .. col4 + 3 of row (lane & 3) of
+// the group, col4 = (lane & 31) & ~3.
+__device__ __forceinline__ void g_tr4x4(uint32_t p0, uint32_t p1, uint32_t &o0, uint32_t &o1) {
+  const int lane = lane_id();
+  const bool b1 = lane & 2, b0 = lane & 1;
+  // with lane ^ 2: keep rows 2*b1, 2*b1 + 1 of both columns
+  const uint32_t r1 =
+      (uint32_t)__builtin_amdgcn_mov_dpp((int)(b1 ? p0 : p1), 0x4E, 0xF, 0xF, false);
+  const uint32_t keep = b1 ? p1 : p0;
+  const uint32_t x = b1 ? r1 : keep;  // column col4 + b0
+  const uint32_t y = b1 ? keep : r1;  // column col4 + 2 + b0
+  // with lane ^ 1: keep row 2*b1 + b0 of all four columns
+  const uint32_t s = b0 ? ((x & 0xffffu) | (y << 16)) : ((x >> 16) | (y & 0xffff0000u));
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s, 0xB1, 0xF, 0xF, false);
+  if (b0) {
+    o0 = (r2 & 0xffffu) | (x & 0xffff0000u);
+    o1 = (r2 >> 16) | (y & 0xffff0000u);
+  } else {
+    o0 = (x & 0xffffu) | (r2 << 16);
+    o1 = (y & 0xffffu) | (r2 & 0xffff0000u);
+  }
+}
+
 // pair(i, j, k): bf16 values of accumulator elements 2k (low half) and
 // 2k + 1 (high half) of MFMA tile (i, j) of this wave; row_ptr(r): output row
 // of wave-tile row r at the wave's first column (nullptr: row not stored),
@@ -544,7 +569,6 @@ __device__ __forceinline__ void g_wave_store_pairs(uint16_t *ring, Pair pair, Ro
   if constexpr (!GPP) __syncthreads();
   const int lane = lane_id();
   uint16_t *st = ring + (threadIdx.x >> 6) * (ROWS * W);
-  const bool b1 = lane & 2, b0 = lane & 1;
   const int col4 = (lane & 31) & ~3;
 #pragma unroll
   for (int i = I0; i < I0 + NI; ++i)
@@ -553,24 +577,8 @@ __device__ __forceinline__ void g_wave_store_pairs(uint16_t *ring, Pair pair, Ro
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // rows 0,1 and 2,3 of this lane's column
-        const uint32_t p0 = pair(i, j, 2 * q), p1 = pair(i, j, 2 * q + 1);
-        // with lane ^ 2: keep rows 2*b1, 2*b1 + 1 of both columns
-        const uint32_t r1 =
-            (uint32_t)__builtin_amdgcn_mov_dpp((int)(b1 ? p0 : p1), 0x4E, 0xF, 0xF, false);
-        const uint32_t keep = b1 ? p1 : p0;
-        const uint32_t x = b1 ? r1 : keep;  // column col4 + b0
-        const uint32_t y = b1 ? keep : r1;  // column col4 + 2 + b0
-        // with lane ^ 1: keep row 2*b1 + b0 of all four columns
-        const uint32_t s = b0 ? ((x & 0xffffu) | (y << 16)) : ((x >> 16) | (y & 0xffff0000u));
-        const uint32_t r2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s, 0xB1, 0xF, 0xF, false);
         uint32_t o0, o1;
-        if (b0) {
-          o0 = (r2 & 0xffffu) | (x & 0xffff0000u);
-          o1 = (r2 >> 16) | (y & 0xffff0000u);
-        } else {
-          o0 = (x & 0xffffu) | (r2 << 16);
-          o1 = (y & 0xffffu) | (r2 & 0xffff0000u);
-        }
+        g_tr4x4(pair(i, j, 2 * q), pair(i, j, 2 * q + 1), o0, o1);
         const int row = (i - I0) * 32 + 8 * q + 4 * (lane >> 5) + (lane & 3);
         const int col = j * 32 + col4;
         uint32_t *dst = reinterpret_cast<uint32_t *>(

@@ -831,6 +831,77 @@ __device__ __forceinline__ void swiglu_acc(const SwigluArgs &g, RowOf row_of, in
   gemm_mainloop(ops, k1 - k0, acc, lds);
 }
 
+// The backward's three outputs (h, d_a, d_b) of row groups I0 .. I1 - 1,
+// stored straight from registers: each row group's d_h values are loaded
+// first (all of them before any store), each output's bf16 pairs go through
+// a 4 x 4 transpose inside groups of 4 lanes (g_tr4x4), and every lane
+// stores 4 consecutive columns of one row with one 8-byte store (16 stores
+// per row group and output instead of 64 2-byte ones).  Outputs 8-byte
+// aligned (swiglu_bwd_vec checks it).
+__device__ __forceinline__ bool swiglu_bwd_vec(const SwigluArgs &g, int h_col0, int f0) {
+  const int c = h_col0 + f0;
+  return ((((uintptr_t)(g.H + c)) | ((uintptr_t)(g.AB + c)) | ((uintptr_t)(g.AB + g.ab_off + c))) &
+          7) == 0 &&
+         (g.ldh & 3) == 0 && (g.ld_ab & 3) == 0;
+}
+
+template <int I0, int I1, class RowOf>
+__device__ __forceinline__ void swiglu_bwd_store(const SwigluArgs &g, RowOf row_of, int rows,
+                                                 int h_col0, int f0, const GAcc &acc) {
+  static_assert(GTN == 2, "one gate and one up tile per wave");
+  const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
+  const int wm0 = (w / GWN) * GWTM, c0 = h_col0 + f0 + (w % GWN) * (GWTN / 2);
+  const int col4 = (lane & 31) & ~3;
+  // d_h at this lane's column, rows of element pairs (2k, 2k + 1)
+  uint32_t gh[I1 - I0][8];
+#pragma unroll
+  for (int i = I0; i < I1; ++i)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int m0 = g_acc_row(i, 2 * k), m1 = m0 + 1;
+      const uint16_t *d0 = g.dH + row_of(min(m0, rows - 1)) * g.ld_dh + g.dh_col0 + c0 + (lane & 31);
+      const uint16_t *d1 = g.dH + row_of(min(m1, rows - 1)) * g.ld_dh + g.dh_col0 + c0 + (lane & 31);
+      gh[i - I0][k] = (uint32_t)*d0 | ((uint32_t)*d1 << 16);
+    }
+#pragma unroll
+  for (int i = I0; i < I1; ++i) {
+    uint32_t ph[8], pa[8], pb[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float vh[2], va[2], vb[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float a = acc[i][0][2 * k + e], b = acc[i][1][2 * k + e];
+        const float dh = bf16_to_f32((uint16_t)(gh[i - I0][k] >> (16 * e)));
+        const float sg = sigmoid_f32(a);
+        const float sa = a * sg;
+        vh[e] = sa * b;
+        va[e] = dh * b * (sg * (1.0f + a * (1.0f - sg)));
+        vb[e] = dh * sa;
+      }
+      ph[k] = pack_bf16x2(vh[0], vh[1]);
+      pa[k] = pack_bf16x2(va[0], va[1]);
+      pb[k] = pack_bf16x2(vb[0], vb[1]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = wm0 + i * 32 + 8 * q + 4 * (lane >> 5) + (lane & 3);
+      uint32_t h0, h1, a0, a1, b0, b1;
+      g_tr4x4(ph[2 * q], ph[2 * q + 1], h0, h1);
+      g_tr4x4(pa[2 * q], pa[2 * q + 1], a0, a1);
+      g_tr4x4(pb[2 * q], pb[2 * q + 1], b0, b1);
+      if (m < rows) {
+        const int64_t r = row_of(m);
+        const u32x2 hv = {h0, h1}, av = {a0, a1}, bv = {b0, b1};
+        uint16_t *ab = g.AB + r * g.ld_ab + c0 + col4;
+        *reinterpret_cast<u32x2 *>(g.H + r * g.ldh + c0 + col4) = hv;
+        *reinterpret_cast<u32x2 *>(ab) = av;
+        *reinterpret_cast<u32x2 *>(ab + g.ab_off) = bv;
+      }
+    }
+  }
+}
+
 // BWD: with dh = dH at the same (row, column), also
 //   d_a = bf16(dh * b * silu'(a)),  d_b = bf16(dh * silu(a)),
 //   silu'(a) = s (1 + a (1 - s)), s = 1 / (1 + e^-a).
@@ -839,6 +910,11 @@ __device__ __forceinline__ void swiglu_store(const SwigluArgs &g, RowOf row_of, 
                                              int h_col0, const GAcc &acc,
                                              uint16_t *ring = nullptr) {
   const int f0 = ft * 128;
+  if (BWD && swiglu_bwd_vec(g, h_col0, f0)) {
+    if constexpr (ONLY < 0) swiglu_bwd_store<0, GTM>(g, row_of, rows, h_col0, f0, acc);
+    else swiglu_bwd_store<ONLY, ONLY + 1>(g, row_of, rows, h_col0, f0, acc);
+    return;
+  }
   // the backward's three outputs keep the direct stores: staged, they need
   // more than 256 VGPRs
   if (!BWD && ONLY < 0 && g_vec_out(g.H + h_col0, g.ldh, 8)) {
