@@ -832,17 +832,20 @@ __device__ __forceinline__ void swiglu_acc(const SwigluArgs &g, RowOf row_of, in
 }
 
 // The backward's three outputs (h, d_a, d_b) of row groups I0 .. I1 - 1,
-// stored straight from registers: each row group's d_h values are loaded
-// first (all of them before any store), each output's bf16 pairs go through
-// a 4 x 4 transpose inside groups of 4 lanes (g_tr4x4), and every lane
-// stores 4 consecutive columns of one row with one 8-byte store (16 stores
-// per row group and output instead of 64 2-byte ones).  Outputs 8-byte
-// aligned (swiglu_bwd_vec checks it).
+// stored straight from registers.  d_h of every row group is loaded first
+// (all of it before any store), 4 consecutive columns of one row per lane
+// with one 8-byte load, and turned into this lane's column by the 4 x 4
+// transpose inside groups of 4 lanes (g_tr4x4, its own inverse); each
+// output's bf16 pairs go through the same transpose, and every lane stores 4
+// consecutive columns of one row with one 8-byte store (16 loads and 48
+// stores per wave instead of 64 and 192 two-byte ones).  d_h and the
+// outputs 8-byte aligned (swiglu_bwd_vec checks it).
 __device__ __forceinline__ bool swiglu_bwd_vec(const SwigluArgs &g, int h_col0, int f0) {
   const int c = h_col0 + f0;
-  return ((((uintptr_t)(g.H + c)) | ((uintptr_t)(g.AB + c)) | ((uintptr_t)(g.AB + g.ab_off + c))) &
+  return ((((uintptr_t)(g.H + c)) | ((uintptr_t)(g.AB + c)) | ((uintptr_t)(g.AB + g.ab_off + c)) |
+           ((uintptr_t)(g.dH + g.dh_col0 + c))) &
           7) == 0 &&
-         (g.ldh & 3) == 0 && (g.ld_ab & 3) == 0;
+         (g.ldh & 3) == 0 && (g.ld_ab & 3) == 0 && (g.ld_dh & 3) == 0;
 }
 
 template <int I0, int I1, class RowOf>
@@ -852,17 +855,23 @@ __device__ __forceinline__ void swiglu_bwd_store(const SwigluArgs &g, RowOf row_
   const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
   const int wm0 = (w / GWN) * GWTM, c0 = h_col0 + f0 + (w % GWN) * (GWTN / 2);
   const int col4 = (lane & 31) & ~3;
-  // d_h at this lane's column, rows of element pairs (2k, 2k + 1)
+  // d_h: 4 columns of one row per lane, then (transposed) at this lane's
+  // column, rows of element pairs (2k, 2k + 1)
+  u32x2 gr[I1 - I0][4];
+#pragma unroll
+  for (int i = I0; i < I1; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = wm0 + i * 32 + 8 * q + 4 * (lane >> 5) + (lane & 3);
+      gr[i - I0][q] = *reinterpret_cast<const u32x2 *>(
+          g.dH + row_of(min(m, rows - 1)) * g.ld_dh + g.dh_col0 + c0 + col4);
+    }
   uint32_t gh[I1 - I0][8];
 #pragma unroll
   for (int i = I0; i < I1; ++i)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int m0 = g_acc_row(i, 2 * k), m1 = m0 + 1;
-      const uint16_t *d0 = g.dH + row_of(min(m0, rows - 1)) * g.ld_dh + g.dh_col0 + c0 + (lane & 31);
-      const uint16_t *d1 = g.dH + row_of(min(m1, rows - 1)) * g.ld_dh + g.dh_col0 + c0 + (lane & 31);
-      gh[i - I0][k] = (uint32_t)*d0 | ((uint32_t)*d1 << 16);
-    }
+    for (int q = 0; q < 4; ++q)
+      g_tr4x4(gr[i - I0][q][0], gr[i - I0][q][1], gh[i - I0][2 * q], gh[i - I0][2 * q + 1]);
 #pragma unroll
   for (int i = I0; i < I1; ++i) {
     uint32_t ph[8], pa[8], pb[8];
