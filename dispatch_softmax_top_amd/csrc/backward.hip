@@ -303,6 +303,34 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
     if (lane + 64 * c < nch) o[lane + 64 * c] = v[c];
 }
 
+// The transposed bank-order operands the backward SwiGLU writes directly
+// (HT [F rows], ABT [2F rows] per expert block, or one block of packed expert
+// ranges with kpack): an expert with no filled rows has no tile there, yet
+// the weight gradients read its first kz = min(256, K columns) columns, which
+// are zeroed here.  Block: 4 rows of one expert, 64 threads per row.
+__global__ __launch_bounds__(256) void zero_empty_k_kernel(uint16_t *HT, uint16_t *ABT,
+                                                           int64_t ldt, int F, int El, int W,
+                                                           const int32_t *__restrict__ bfill,
+                                                           int kpack, int kz) {
+  const int per = 3 * F / 4;
+  const int e = (int)(blockIdx.x / per), r = (int)(blockIdx.x % per) * 4 + (int)(threadIdx.x >> 6);
+  int fill = 0;
+  for (int w = 0; w < W; ++w) fill += bfill[w * El + e];
+  if (fill) return;
+  int64_t kb = 0;
+  if (kpack)
+    for (int x = 0; x < e; ++x) {
+      int f = 0;
+      for (int w = 0; w < W; ++w) f += bfill[w * El + x];
+      kb += kpack_len(f);
+    }
+  uint16_t *row = r < F ? (kpack ? HT : HT + (int64_t)e * F * ldt) + (int64_t)r * ldt
+                        : (kpack ? ABT : ABT + (int64_t)e * 2 * F * ldt) + (int64_t)(r - F) * ldt;
+  const u32x2 zero = {0u, 0u};
+  for (int k = (int)(threadIdx.x & 63) * 4; k < kz; k += 256)
+    *reinterpret_cast<u32x2 *>(row + kb + k) = zero;
+}
+
 // o[i] = i; zero16: NULL, or 16 ints set to zero (a GEMM work queue's counters).
 __global__ __launch_bounds__(256) void iota_kernel(int32_t *o, int64_t n, int32_t *zero16) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -578,9 +606,15 @@ extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
   // d_h = dy . W_d (grouped, bank order)
   MOE_TRY(gemm_grouped_nt("gemm_bwd_d_h", "gemm_bwd_d_h_tail", *d, w.dY, L, boff, bfill, w.iota,
                           nb, w.WdT, F, w.dH, nb, w.part, w.queue, s));
-  // a, b recomputed; d_a | d_b and h
+  // a, b recomputed; d_a | d_b and h (h, and d_a | d_b once more, straight
+  // into the transposed bank-order layout when the product groups allow it)
+  bool transposed = false;
   MOE_TRY(gemm_expert_swiglu_bwd(*d, bank, boff, bfill, nb, w_gate, w_up, w.dH, w.Hb, w.dAB,
-                                 w.part, s));
+                                 w.part, s, w.HT, w.dABT, Kp, rg, &transposed));
+  if (transposed)
+    MOE_TRY(launch("zero_empty_k", zero_empty_k_kernel, dim3((unsigned)(El * (3 * F / 4))),
+                   dim3(256), 0, s, w.HT, w.dABT, Kp, F, El, d->n_waves, bfill, (int)rg,
+                   (int)std::min<int64_t>(256, Kp)));
   // d_u = d_a . W_g + d_b . W_u, scattered to the receive rows; others zero
   MOE_TRY(ret_rows_mark(bank_src, nb, w.flags, nr, w.queue, s));
   MOE_TRY(gemm_grouped_nt("gemm_bwd_d_u", "gemm_bwd_d_u_tail", *d, w.dAB, 2 * F, boff, bfill,
@@ -594,11 +628,11 @@ extern "C" int moe_expert_ffn_backward(const moe_dims *d, const moe_bf16 *bank,
   const int nbatch = rg ? 1 : El;
   const Tr trb[4] = {
       {w.dY, L, 0, w.dYT, Kp, (int64_t)L * Kp, nw, L, (int)Kp, nbatch, bfill, Cr, El, W, boff},
+      {bank, L, 0, w.UT, Kp, (int64_t)L * Kp, nw, L, (int)Kp, nbatch, bfill, Cr, El, W, boff},
       {w.Hb, F, 0, w.HT, Kp, (int64_t)F * Kp, nw, F, (int)Kp, nbatch, bfill, Cr, El, W, boff},
       {w.dAB, 2 * F, 0, w.dABT, Kp, (int64_t)2 * F * Kp, nw, 2 * F, (int)Kp, nbatch, bfill, Cr, El,
-       W, boff},
-      {bank, L, 0, w.UT, Kp, (int64_t)L * Kp, nw, L, (int)Kp, nbatch, bfill, Cr, El, W, boff}};
-  MOE_TRY(transposes("transpose_bank", 4, trb, s));
+       W, boff}};
+  MOE_TRY(transposes("transpose_bank", transposed ? 2 : 4, trb, s));
   // expert e's operand blocks: its own (fixed), or the shared row (ragged)
   const int64_t blk = rg ? 0 : 1;
   if (3 * El <= 18) {  // all three weights of every local expert in one launch

@@ -788,6 +788,17 @@ struct SwigluArgs {
   uint16_t *AB;
   int64_t ld_ab;
   int ab_off;
+  // backward, grouped, merged product groups (one per local expert): also
+  // h and d_a | d_b transposed, in the layout the weight gradients read (K =
+  // the expert's filled bank rows, packed): HT [F][ldt], ABT [2F][ldt] (d_a at
+  // column c, d_b at F + c) per expert block (fixed: expert e's at e * F *
+  // ldt and e * 2F * ldt, k from 0) or one block (kpack: expert e's range
+  // from the sum of kpack_len over the experts before it); k from the
+  // expert's fill up to its padded end is written as zero.  HT NULL: none
+  // (then h goes to H).
+  uint16_t *HT, *ABT;
+  int64_t ldt;
+  int kpack;
   // dense (shared experts): M rows, expert = f-tile / ftiles along N
   int M, S;
   // grouped (routed experts)
@@ -848,65 +859,186 @@ __device__ __forceinline__ bool swiglu_bwd_vec(const SwigluArgs &g, int h_col0, 
          (g.ldh & 3) == 0 && (g.ld_ab & 3) == 0 && (g.ld_dh & 3) == 0;
 }
 
-template <int I0, int I1, class RowOf>
+// Where tile t's rows go in the transposed outputs: tile row m at k = tk0 + m
+// of its expert's block (ht, abt), for m < krows (rows past t.rows there are
+// the expert's zero padding: up to its fill rounded to whole K tiles, and at
+// least min(256, ldt) -- the weight gradients read at least 8 K tiles).  An
+// expert with no rows has no tile: its range is zeroed elsewhere.
+struct SwigluTPos {
+  uint16_t *ht, *abt;
+  int64_t tk0;
+  int krows;
+};
+
+__device__ __forceinline__ SwigluTPos swiglu_tpos(const SwigluArgs &g, const GTile &t) {
+  SwigluTPos p;
+  const int e = t.expert, fill = group_rows(g.grp, e);
+  int64_t kb = 0;
+  if (g.kpack) {
+    for (int x = 0; x < e; ++x) kb += kpack_len(group_rows(g.grp, x));
+    p.ht = g.HT;
+    p.abt = g.ABT;
+  } else {
+    p.ht = g.HT + (int64_t)e * g.F * g.ldt;
+    p.abt = g.ABT + (int64_t)e * 2 * g.F * g.ldt;
+  }
+  const int64_t pend =
+      g.kpack ? kpack_len(fill) : max((int64_t)(fill + 31) / 32 * 32, min<int64_t>(256, g.ldt));
+  p.tk0 = kb + t.v0;
+  p.krows = (int)min<int64_t>(GBM, pend - t.v0);
+  return p;
+}
+
+// Transposed outputs of two MFMA row groups (64 rows x 32 columns of the
+// wave) through the wave's LDS region, GTR_OUTS outputs of 32 columns x
+// GTR_LD elements: each lane writes its column's 4-row groups (8 bytes each,
+// rows past `rows` zero), then reads 16-byte runs of k back and stores them
+// to row c0 + c of its output (k from tk0 + the pair's first row), so that 8
+// lanes write one column's 128 bytes (a whole line).  The padded row length
+// spreads the columns over the LDS banks.
+constexpr int GTR_ROWS = 64, GTR_LD = GTR_ROWS + 8, GTR_OUTS = 3;
+static_assert(GNT / 64 * GTR_OUTS * 32 * GTR_LD <= GNST * (GSA + GSB),
+              "transpose regions inside the ring");
+
+template <class Pairs, class Out>
+__device__ __forceinline__ void swiglu_tr_pair(uint16_t *region, Pairs pairs, int r0, int rows,
+                                               Out out, int64_t ldt, int64_t k0, int krows) {
+  const int lane = lane_id(), c = lane & 31;
+#pragma unroll
+  for (int o = 0; o < GTR_OUTS; ++o)
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = ii * 32 + 8 * q + 4 * (lane >> 5), mg = r0 + r;
+        uint32_t p0 = pairs(o, ii, 2 * q), p1 = pairs(o, ii, 2 * q + 1);
+        if (mg + 4 > rows) {
+          p0 &= (mg < rows ? 0xffffu : 0u) | (mg + 1 < rows ? 0xffff0000u : 0u);
+          p1 &= (mg + 2 < rows ? 0xffffu : 0u) | (mg + 3 < rows ? 0xffff0000u : 0u);
+        }
+        *reinterpret_cast<u32x2 *>(region + (o * 32 + c) * GTR_LD + r) = u32x2{p0, p1};
+      }
+#pragma unroll
+  for (int o = 0; o < GTR_OUTS; ++o)
+#pragma unroll
+    for (int j = 0; j < 32 * (GTR_ROWS / 8) / 64; ++j) {
+      const int idx = j * 64 + lane, cc = idx / (GTR_ROWS / 8), kc = idx % (GTR_ROWS / 8);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(region + (o * 32 + cc) * GTR_LD + kc * 8);
+      if (r0 + kc * 8 < krows) *reinterpret_cast<u32x4 *>(out(o) + cc * ldt + k0 + r0 + kc * 8) = v;
+    }
+}
+
+// tr: also the transposed outputs, at the tile's position tp (then h is not
+// stored row-major): with LDS_TR through the wave's region of `ring` (an
+// even number of row groups), else with one 8-byte store per lane and 4-row
+// group.
+template <int I0, int I1, bool LDS_TR = false, class RowOf>
 __device__ __forceinline__ void swiglu_bwd_store(const SwigluArgs &g, RowOf row_of, int rows,
-                                                 int h_col0, int f0, const GAcc &acc) {
+                                                 int h_col0, int f0, const GAcc &acc,
+                                                 bool tr = false, SwigluTPos tp = {},
+                                                 uint16_t *ring = nullptr) {
   static_assert(GTN == 2, "one gate and one up tile per wave");
+  constexpr int NI = I1 - I0;
   const int lane = lane_id(), w = (int)(threadIdx.x >> 6);
   const int wm0 = (w / GWN) * GWTM, c0 = h_col0 + f0 + (w % GWN) * (GWTN / 2);
   const int col4 = (lane & 31) & ~3;
-  // d_h: 4 columns of one row per lane, then (transposed) at this lane's
-  // column, rows of element pairs (2k, 2k + 1)
-  u32x2 gr[I1 - I0][4];
+  constexpr int NP = NI >= 2 ? 2 : 1;  // row groups per pass
+  // d_h: 4 columns of one row per lane, loaded a pass ahead (before the
+  // previous pass's stores)
+  const auto load_dh = [&](int i2, u32x2 (&gr)[NP][4]) {
 #pragma unroll
-  for (int i = I0; i < I1; ++i)
+    for (int ii = 0; ii < NP; ++ii)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int m = wm0 + i * 32 + 8 * q + 4 * (lane >> 5) + (lane & 3);
-      gr[i - I0][q] = *reinterpret_cast<const u32x2 *>(
-          g.dH + row_of(min(m, rows - 1)) * g.ld_dh + g.dh_col0 + c0 + col4);
-    }
-  uint32_t gh[I1 - I0][8];
-#pragma unroll
-  for (int i = I0; i < I1; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      g_tr4x4(gr[i - I0][q][0], gr[i - I0][q][1], gh[i - I0][2 * q], gh[i - I0][2 * q + 1]);
-#pragma unroll
-  for (int i = I0; i < I1; ++i) {
-    uint32_t ph[8], pa[8], pb[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float vh[2], va[2], vb[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float a = acc[i][0][2 * k + e], b = acc[i][1][2 * k + e];
-        const float dh = bf16_to_f32((uint16_t)(gh[i - I0][k] >> (16 * e)));
-        const float sg = sigmoid_f32(a);
-        const float sa = a * sg;
-        vh[e] = sa * b;
-        va[e] = dh * b * (sg * (1.0f + a * (1.0f - sg)));
-        vb[e] = dh * sa;
+      for (int q = 0; q < 4; ++q) {
+        const int m = wm0 + (i2 + ii) * 32 + 8 * q + 4 * (lane >> 5) + (lane & 3);
+        gr[ii][q] = *reinterpret_cast<const u32x2 *>(
+            g.dH + row_of(min(m, rows - 1)) * g.ld_dh + g.dh_col0 + c0 + col4);
       }
-      ph[k] = pack_bf16x2(vh[0], vh[1]);
-      pa[k] = pack_bf16x2(va[0], va[1]);
-      pb[k] = pack_bf16x2(vb[0], vb[1]);
-    }
+  };
+  u32x2 gr[NP][4];
+  load_dh(I0, gr);
+  static_assert(!LDS_TR || NI % 2 == 0, "LDS transposes take row groups in pairs");
+  const auto T = [&](int o) {
+    return o == 0 ? tp.ht + (int64_t)c0 * g.ldt
+                  : tp.abt + (int64_t)(c0 + (o == 2 ? g.F : 0)) * g.ldt;
+  };
+  // row groups NP at a time: h, d_a, d_b as bf16 pairs of this lane's column
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int m = wm0 + i * 32 + 8 * q + 4 * (lane >> 5) + (lane & 3);
-      uint32_t h0, h1, a0, a1, b0, b1;
-      g_tr4x4(ph[2 * q], ph[2 * q + 1], h0, h1);
-      g_tr4x4(pa[2 * q], pa[2 * q + 1], a0, a1);
-      g_tr4x4(pb[2 * q], pb[2 * q + 1], b0, b1);
-      if (m < rows) {
-        const int64_t r = row_of(m);
-        const u32x2 hv = {h0, h1}, av = {a0, a1}, bv = {b0, b1};
-        uint16_t *ab = g.AB + r * g.ld_ab + c0 + col4;
-        *reinterpret_cast<u32x2 *>(g.H + r * g.ldh + c0 + col4) = hv;
-        *reinterpret_cast<u32x2 *>(ab) = av;
-        *reinterpret_cast<u32x2 *>(ab + g.ab_off) = bv;
+  for (int i2 = I0; i2 < I1; i2 += NP) {
+    uint32_t P[GTR_OUTS][NP][8];
+#pragma unroll
+    for (int ii = 0; ii < NP; ++ii)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i2 + ii;
+        uint32_t gh[2];
+        g_tr4x4(gr[ii][q][0], gr[ii][q][1], gh[0], gh[1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = 2 * q + h;
+          float vh[2], va[2], vb[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float a = acc[i][0][2 * k + e], b = acc[i][1][2 * k + e];
+            const float dh = bf16_to_f32((uint16_t)(gh[h] >> (16 * e)));
+            const float sg = sigmoid_f32(a);
+            const float sa = a * sg;
+            vh[e] = sa * b;
+            va[e] = dh * b * (sg * (1.0f + a * (1.0f - sg)));
+            vb[e] = dh * sa;
+          }
+          P[0][ii][k] = pack_bf16x2(vh[0], vh[1]);
+          P[1][ii][k] = pack_bf16x2(va[0], va[1]);
+          P[2][ii][k] = pack_bf16x2(vb[0], vb[1]);
+        }
       }
+    if (i2 + NP < I1) load_dh(i2 + NP, gr);
+    // row-major stores first (d_a | d_b; h unless transposed), so that the
+    // pairs die at the LDS writes of the transposed outputs
+#pragma unroll
+    for (int ii = 0; ii < NP; ++ii) {
+      const int i = i2 + ii;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = wm0 + i * 32 + 8 * q + 4 * (lane >> 5) + (lane & 3);
+        uint32_t h0, h1, a0, a1, b0, b1;
+        if (!tr) g_tr4x4(P[0][ii][2 * q], P[0][ii][2 * q + 1], h0, h1);
+        g_tr4x4(P[1][ii][2 * q], P[1][ii][2 * q + 1], a0, a1);
+        g_tr4x4(P[2][ii][2 * q], P[2][ii][2 * q + 1], b0, b1);
+        if (m < rows) {
+          const int64_t r = row_of(m);
+          uint16_t *ab = g.AB + r * g.ld_ab + c0 + col4;
+          if (!tr) *reinterpret_cast<u32x2 *>(g.H + r * g.ldh + c0 + col4) = u32x2{h0, h1};
+          *reinterpret_cast<u32x2 *>(ab) = u32x2{a0, a1};
+          *reinterpret_cast<u32x2 *>(ab + g.ab_off) = u32x2{b0, b1};
+        }
+      }
+    }
+    if constexpr (LDS_TR) {
+      if (tr)
+        swiglu_tr_pair(ring + w * (GTR_OUTS * 32 * GTR_LD),
+                       [&](int o, int ii, int k) { return P[o][ii][k]; }, wm0 + i2 * 32, rows, T,
+                       g.ldt, tp.tk0, tp.krows);
+    } else if (tr) {
+      // transposed: this lane's column, 4 consecutive rows (k) per 8-byte
+      // store, zero past the tile's rows
+      const int64_t c = lane & 31;
+#pragma unroll
+      for (int ii = 0; ii < NP; ++ii)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int mg = wm0 + (i2 + ii) * 32 + 8 * q + 4 * (lane >> 5);
+          if (mg >= tp.krows) continue;
+#pragma unroll
+          for (int o = 0; o < GTR_OUTS; ++o) {
+            uint32_t v0 = P[o][ii][2 * q], v1 = P[o][ii][2 * q + 1];
+            if (mg + 4 > rows) {
+              v0 &= (mg < rows ? 0xffffu : 0u) | (mg + 1 < rows ? 0xffff0000u : 0u);
+              v1 &= (mg + 2 < rows ? 0xffffu : 0u) | (mg + 3 < rows ? 0xffff0000u : 0u);
+            }
+            *reinterpret_cast<u32x2 *>(T(o) + c * g.ldt + tp.tk0 + mg) = u32x2{v0, v1};
+          }
+        }
     }
   }
 }
@@ -914,14 +1046,17 @@ __device__ __forceinline__ void swiglu_bwd_store(const SwigluArgs &g, RowOf row_
 // BWD: with dh = dH at the same (row, column), also
 //   d_a = bf16(dh * b * silu'(a)),  d_b = bf16(dh * silu(a)),
 //   silu'(a) = s (1 + a (1 - s)), s = 1 / (1 + e^-a).
+// tr (backward with transposed outputs, which the launcher enables only for
+// 8-byte aligned outputs): also those, at the tile's position tp.
 template <int ONLY = -1, bool BWD = false, class RowOf>
 __device__ __forceinline__ void swiglu_store(const SwigluArgs &g, RowOf row_of, int rows, int ft,
                                              int h_col0, const GAcc &acc,
-                                             uint16_t *ring = nullptr) {
+                                             uint16_t *ring = nullptr, bool tr = false,
+                                             SwigluTPos tp = {}) {
   const int f0 = ft * 128;
   if (BWD && swiglu_bwd_vec(g, h_col0, f0)) {
-    if constexpr (ONLY < 0) swiglu_bwd_store<0, GTM>(g, row_of, rows, h_col0, f0, acc);
-    else swiglu_bwd_store<ONLY, ONLY + 1>(g, row_of, rows, h_col0, f0, acc);
+    if constexpr (ONLY < 0) swiglu_bwd_store<0, GTM>(g, row_of, rows, h_col0, f0, acc, tr, tp);
+    else swiglu_bwd_store<ONLY, ONLY + 1>(g, row_of, rows, h_col0, f0, acc, tr, tp);
     return;
   }
   // the backward's three outputs keep the direct stores: staged, they need
@@ -1076,8 +1211,17 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(GMINWAVES, 
     const auto row_of = [&](int m) { return t.row(m); };
     GAcc acc;
     swiglu_acc(g, row_of, t.rows, t.expert, t.nt, k0, k1, lds, acc);
-    if (u.nparts > 1) g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
-    else swiglu_store<-1, true>(g, row_of, t.rows, t.nt, 0, acc);
+    if (u.nparts > 1) {
+      g_part_store(g.sp.part, u.tail * u.nparts + u.part, acc);
+    } else if (g.HT) {
+      // transposed outputs through the ring, which is free: every wave is
+      // past the main loop's last barrier (the launcher set HT only for
+      // 8-byte aligned outputs)
+      swiglu_bwd_store<0, GTM, true>(g, row_of, t.rows, 0, t.nt * 128, acc, true,
+                                     swiglu_tpos(g, t), lds.A[0]);
+    } else {
+      swiglu_store<-1, true>(g, row_of, t.rows, t.nt, 0, acc);
+    }
   } else {
     // H rows take 16-byte stores (the launcher checks it)
     GOps2 ops = swiglu_ops(g, [&](int m) { return t.row(m); }, t.rows, t.expert, t.nt, k0);
@@ -1121,9 +1265,12 @@ __global__ __launch_bounds__(GNT) void gemm_expert_swiglu_tail_kernel(SwigluArgs
     return;
   const auto row_of = [&](int m) { return t.row(m); };
   GAcc acc;
+  const bool tr = BWD && g.HT;
+  SwigluTPos tp{};
+  if (tr) tp = swiglu_tpos(g, t);
 #define MOE_ROWS(I)                                       \
   g_part_sum_rows<I>(g.sp.part, u.tail, u.nparts, acc); \
-  swiglu_store<I, BWD>(g, row_of, t.rows, t.nt, 0, acc)
+  swiglu_store<I, BWD>(g, row_of, t.rows, t.nt, 0, acc, nullptr, tr, tp)
   MOE_TAIL_ROWS(MOE_ROWS)
 #undef MOE_ROWS
 }
@@ -1525,13 +1672,25 @@ int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int64_
                            const int32_t *bfill, int64_t n_bank_rows, const uint16_t *wg,
                            const uint16_t *wu,
                            const uint16_t *dH, uint16_t *H, uint16_t *AB, float *part,
-                           hipStream_t s) {
+                           hipStream_t s, uint16_t *HT, uint16_t *ABT, int64_t ldt, bool kpack,
+                           bool *transposed) {
   SwigluArgs a{};
   a.dH = dH;
   a.ld_dh = d.d_ff;
   a.AB = AB;
   a.ld_ab = 2ll * d.d_ff;
   a.ab_off = d.d_ff;
+  // transposed outputs: one product group per local expert (merged waves),
+  // 8-byte aligned rows
+  const GroupArgs ga = group_args(d, bank_offsets, bfill, n_bank_rows, std::max(d.latent, d.d_ff));
+  const bool tr = HT && ABT && ga.nw == d.n_waves && ldt % 4 == 0 &&
+                  (((uintptr_t)HT | (uintptr_t)ABT | (uintptr_t)H | (uintptr_t)AB |
+                    (uintptr_t)dH) & 7) == 0;
+  a.HT = tr ? HT : nullptr;
+  a.ABT = tr ? ABT : nullptr;
+  a.ldt = ldt;
+  a.kpack = kpack;
+  if (transposed) *transposed = tr;
   return expert_swiglu("gemm_expert_swiglu_bwd", "gemm_expert_swiglu_bwd_tail",
                        gemm_expert_swiglu_kernel<true>, gemm_expert_swiglu_tail_kernel<true>, a,
                        d, bank, bank_offsets, bfill, n_bank_rows, wg, wu, H, part, s);

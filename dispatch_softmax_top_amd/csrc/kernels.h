@@ -121,12 +121,18 @@ int gemm_shared_swiglu_bwd(int M, const uint16_t *x, int64_t ldx, int K, const u
                            int dh_col0, uint16_t *H, uint16_t *AB, float *part, hipStream_t s);
 // Routed experts recomputed over the bank (groups at g * cap_recv, or at
 // bank_offsets in ragged mode) with the SwiGLU gradient epilogue: dH, H
-// [bank rows, F], AB [bank rows, 2F].
+// [bank rows, F], AB [bank rows, 2F].  With HT and ABT, h goes to HT
+// instead of H and d_a | d_b also to ABT, transposed into the bank-order
+// layout the weight gradients read (per-expert blocks of ldt columns, or with
+// kpack one block of packed expert ranges; zero past each expert's fill up
+// to its padded end), when the bank's product groups allow it; *transposed
+// tells whether they did (else H is written and the caller transposes).
 int gemm_expert_swiglu_bwd(const moe_dims &d, const uint16_t *bank, const int64_t *bank_offsets,
                            const int32_t *bfill,
                            int64_t n_bank_rows, const uint16_t *wg, const uint16_t *wu,
                            const uint16_t *dH, uint16_t *H, uint16_t *AB, float *part,
-                           hipStream_t s);
+                           hipStream_t s, uint16_t *HT = nullptr, uint16_t *ABT = nullptr,
+                           int64_t ldt = 0, bool kpack = false, bool *transposed = nullptr);
 // Grouped over the bank's groups (bank_offsets: ragged mode, else NULL):
 // out[dst[r]] = A[r] . B_j^T, A [bank rows][K], B [E_l][N][K].  queue: as
 // for gemm_expert_down (counters 8..15 zeroed before the launch), or NULL.
