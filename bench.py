@@ -281,6 +281,11 @@ def backward_work(st):
     else:            # packed: each expert's rows rounded up to K tiles, at least 256
         rows = st.rcv.bfill.view(d.n_waves, El).sum(0).tolist()
         kpad = sum(max(-(-r // 32) * 32, 256) for r in rows)
+    # the backward SwiGLU writes h and d_a | d_b transposed itself when the
+    # bank's product groups are one per local expert (at most 4 waves and
+    # 32-bit copy offsets over the bank), leaving dy and u to transpose
+    merged = d.n_waves <= 4 and st.rcv.n_bank_rows * max(L, F) * 2 < 2**31 - 1
+    tcols = 2 * L if merged else 2 * L + 3 * F
     f = lambda v: ("flop", float(v))
     b = lambda v: ("byte", float(v))
     return {
@@ -302,7 +307,7 @@ def backward_work(st):
         "transpose_combine_weights": b(4 * D * L + 4 * D * SF),
         "transpose_combine_acts": b(2 * T * (D + L + SF) + 2 * Tp * (D + L + SF)),
         "transpose_expert_weights": b(3 * 4 * El * L * F),
-        "transpose_bank": b(2 * kept_r * (2 * L + 3 * F) + 2 * kpad * (2 * L + 3 * F)),
+        "transpose_bank": b(2 * kept_r * tcols + 2 * kpad * tcols),
         "transpose_pack_weights": b(4 * L * D + 8 * SF * D),
         "transpose_pack_acts": b(2 * T * (D + L + 2 * SF) + 2 * Tp * (D + L + 2 * SF)),
     }
