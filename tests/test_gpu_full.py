@@ -26,7 +26,8 @@ definitions as float64 matrix products), row by row within 2e-2 * max|ref|:
     every such row.
 Every return row no kept bank row writes must be zero (all rows, on the
 device).  The 4096-token case also runs the step ten times and once more
-with every call on one stream, and requires every output bit-identical.
+with every call on one stream, and requires every output bit-identical, and
+runs the backward of the share three times, every gradient bit-identical.
 """
 import math
 import zlib
@@ -166,6 +167,25 @@ def test_full_share(orc, name, cfg, which, full):
         bad = [k for k in ref if not _same(ref[k], now[k])]
         assert not bad, f"the one-stream step differs in {bad}"
         print(f"[full] {name}: 10 steps and the one-stream step bit-identical", flush=True)
+        # the backward of the same share (as bench.py runs it), three times:
+        # every gradient bit-identical (work-queue tile order, split tails)
+        from dispatch_softmax_top_amd import share
+        st.bwd = share.Backward(d, st.n_recv_rows)
+        st.d_out = gen.payload_rows(d.T, d.d_model, 71, "cuda")
+        grads = ("d_returned", "d_gates", "d_shared", "dw_lat_up", "dws_down", "d_logits",
+                 "d_recv", "dw_gate", "dw_up", "dw_down", "dz", "dx", "dw_lat_down", "dws_gate",
+                 "dws_up")
+        bref = None
+        for i in range(3):
+            bench.backward_step(st)
+            torch.cuda.synchronize()
+            cur = {k: getattr(st.bwd, k).clone() for k in grads}
+            if bref is None:
+                bref = cur
+            else:
+                bad = [k for k in grads if not _same(bref[k], cur[k])]
+                assert not bad, f"backward run {i + 1} differs from run 1 in {bad}"
+        print(f"[full] {name}: backward three times bit-identical", flush=True)
 
     # ---- which rows: tiles of the GEMMs as the kernels cut them
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
