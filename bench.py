@@ -604,7 +604,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=1,
+                    help="workload: 0 tiny (64 tokens, 48 experts), 1 the 4096-token share, "
+                         "2 Zipf 16384 tokens, 3 long context 65536 tokens, 4 Zipf 16384 "
+                         "tokens dropless")
     ap.add_argument("--rank", default="0",
                     help="rank to measure, or 'hot': the rank with the most kept received rows")
     ap.add_argument("--serial", action="store_true",
