@@ -14,8 +14,6 @@ import torch
 
 from . import _lib as L
 
-RANK_TILE = 8192  # items per slot-assignment tile (keeps workspace sizes honest)
-
 
 def make_dims(cfg, T=None) -> L.MoeDims:
     """Dims of a workload; capacities from the library's own formula."""
