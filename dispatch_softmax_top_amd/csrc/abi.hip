@@ -2,6 +2,7 @@
 // capacities, workspace sizes and the optional per-kernel event timing.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -35,7 +36,21 @@ int check_ptr(const void *p, const char *name, bool may_be_null) {
   return MOE_OK;
 }
 
+int gemm_cus_env(int *cus) {
+  *cus = 0;
+  const char *e = getenv("MOE_GEMM_CUS");
+  if (!e || !*e) return MOE_OK;
+  char *end = nullptr;
+  const long v = strtol(e, &end, 10);
+  if (*end || v < 8 || v % 8 || v > (1 << 20))
+    return fail(MOE_ERR_INVALID, "MOE_GEMM_CUS=%s: a multiple of 8, at least 8, expected", e);
+  *cus = (int)v;
+  return MOE_OK;
+}
+
 int check_dims(const moe_dims *d) {
+  int cus = 0;
+  MOE_TRY(gemm_cus_env(&cus));
   if (!d) return fail(MOE_ERR_INVALID, "dims is NULL");
   if (d->T < 1 || d->d_model < 1 || d->latent < 1 || d->n_experts < 1 || d->n_ranks < 1 ||
       d->top_k < 1 || d->n_waves < 1 || d->d_ff < 1 || d->n_shared < 0 ||

@@ -17,7 +17,11 @@ void clear_error();
 int hip_status(hipError_t e, const char *what);
 
 // Argument checks shared by the entry points; return MOE_OK or an error.
+// check_dims also checks the environment variable MOE_GEMM_CUS.
 int check_dims(const moe_dims *d);
+// MOE_GEMM_CUS, the CU count the GEMM launchers plan for: *cus = 0 if unset,
+// else its value; an error unless it is a multiple of 8, at least 8.
+int gemm_cus_env(int *cus);
 int check_ptr(const void *p, const char *name, bool may_be_null = false);
 
 inline int32_t experts_per_rank(const moe_dims &d) { return d.n_experts / d.n_ranks; }

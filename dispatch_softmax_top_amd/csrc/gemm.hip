@@ -1427,21 +1427,25 @@ __global__ __launch_bounds__(GNT) void gemm_expert_down_tail_kernel(DownArgs g) 
 // host launchers
 // ---------------------------------------------------------------------------
 
-// CUs of the current device (cached per device).
+// CUs the launchers plan for: those of the current device (cached per
+// device), or fewer if MOE_GEMM_CUS (read at every call; the entry points
+// have checked it) asks for it.  The count sets the persistent grids (one
+// block per planned CU) and where a last round is split along K; results of
+// tiles that are not split do not depend on it.
 static int cu_count(int *ncu) {
   static int cache[64];
   int dev = 0;
   MOE_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
-  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
-    *ncu = cache[dev];
-    return MOE_OK;
+  int n = dev >= 0 && dev < 64 ? cache[dev] : 0;
+  if (n <= 0) {
+    MOE_TRY(hip_status(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev),
+                       "hipDeviceGetAttribute"));
+    if (n < 1) return fail(MOE_ERR_HIP, "device reports %d compute units", n);
+    if (dev >= 0 && dev < 64) cache[dev] = n;
   }
-  int n = 0;
-  MOE_TRY(hip_status(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev),
-                     "hipDeviceGetAttribute"));
-  if (n < 1) return fail(MOE_ERR_HIP, "device reports %d compute units", n);
-  if (dev >= 0 && dev < 64) cache[dev] = n;
-  *ncu = n;
+  int cus = 0;
+  MOE_TRY(gemm_cus_env(&cus));
+  *ncu = cus > 0 ? std::min(n, cus) : n;
   return MOE_OK;
 }
 

@@ -62,6 +62,15 @@
  *     says why.  Nothing is enqueued when a call returns an error.
  *     Data-dependent faults found on the device (a receive row whose id is
  *     neither -1 nor hosted by `rank`) are counted, never trapped.
+ *   - Environment: MOE_GEMM_CUS, if set, is the number of compute units the
+ *     GEMM launchers plan for when it is below the device's (a multiple of
+ *     8, at least 8; anything else makes every call that takes moe_dims
+ *     return MOE_ERR_INVALID).  It sets the persistent GEMMs' grids (one
+ *     block per planned CU, so a caller can leave CUs to kernels on other
+ *     streams) and which last rounds are split along K.  Outputs of GEMM
+ *     tiles that are not split do not depend on it; a split tile's fp32
+ *     partial sums are added in a fixed order, but in another grouping than
+ *     the unsplit tile's, so its bf16 results may differ in the last bit.
  */
 #ifndef MOE_H
 #define MOE_H

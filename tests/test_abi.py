@@ -78,6 +78,17 @@ def test_bad_dims_rejected(moe, field, value):
     assert moe.lib().moe_last_error().decode()
 
 
+@pytest.mark.parametrize("value,ok", [("64", True), ("200", True), ("8", True), ("", True),
+                                      ("12", False), ("0", False), ("-8", False), ("64x", False)])
+def test_planned_cus_variable_checked_before_any_launch(moe, monkeypatch, value, ok):
+    monkeypatch.setenv("MOE_GEMM_CUS", value)
+    d = _dims(moe)
+    rc = moe.lib().moe_workspace_bytes(ctypes.byref(d), moe.MOE_CALL_FFN, 0)
+    assert (rc >= 0) == ok
+    if not ok:
+        assert "MOE_GEMM_CUS" in moe.lib().moe_last_error().decode()
+
+
 def test_chunked_waves_need_fixed_capacities(moe):
     d = _dims(moe, wave_mode=moe.MOE_WAVES_CHUNKS)
     assert moe.moe_workspace_bytes(d, moe.MOE_CALL_PACK, 0) >= 0

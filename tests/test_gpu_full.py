@@ -30,6 +30,7 @@ with every call on one stream, and requires every output bit-identical, and
 runs the backward of the share three times, every gradient bit-identical.
 """
 import math
+import os
 import zlib
 
 import numpy as np
@@ -74,6 +75,51 @@ def _outputs(st):
 
 def _same(a, b):
     return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+def _check_planned_cus(st, name, groups, split_mtiles, up_mtiles, bank_src, n_ret, rows_all):
+    """The step with the GEMM launchers planning for 64 and for 200 CUs
+    (MOE_GEMM_CUS) instead of the device's: other persistent grids, another
+    work-queue spread, and no K-split last round at these counts.  Outputs of
+    tiles that the device-count run does not split must be bit-identical;
+    rows those split tiles touch (their bank rows' return rows, the tokens
+    that read them, the up-projection's split tiles) agree within the
+    floating-point tolerance.  The device-count step runs again after."""
+    import bench
+    ref = _outputs(st)
+    hit = np.zeros(n_ret, bool)
+    for pg, mt in split_mtiles:
+        pos = groups[pg][mt * fc.GBM:(mt + 1) * fc.GBM]
+        src = bank_src[pos]
+        hit[src[src >= 0]] = True
+    tok_hit = ((rows_all >= 0) & hit[np.maximum(rows_all, 0)]).any(1)
+    for mt in up_mtiles:
+        tok_hit[mt * fc.GBM:(mt + 1) * fc.GBM] = True
+    exact = ("topk", "gates", "slot", "fill", "demand", "z", "pool_tails", "pool_rows",
+             "bank_src", "bfill", "bdemand", "bank")
+    try:
+        for cus in ("64", "200"):
+            os.environ["MOE_GEMM_CUS"] = cus
+            bench.step(st)
+            torch.cuda.synchronize()
+            now = _outputs(st)
+            bad = [k for k in exact if not _same(ref[k], now[k])]
+            assert not bad, f"planned for {cus} CUs: {bad} differ"
+            for k, rows in (("ret", hit), ("ylat", tok_hit), ("out", tok_hit)):
+                keep = torch.from_numpy(~rows).cuda()
+                assert _same(ref[k][keep], now[k][keep]), f"planned for {cus} CUs: {k} differs"
+                if rows.any():
+                    sel = torch.from_numpy(rows).cuda()
+                    gc.assert_rows_close(gc.host(now[k][sel]), gc.host(ref[k][sel]),
+                                         f"{k} planned for {cus} CUs, split rows")
+            print(f"[full] {name}: planned for {cus} CUs: bit-identical outside the "
+                  f"{int(hit.sum())} return rows and {int(tok_hit.sum())} tokens of split tiles, "
+                  f"close on those", flush=True)
+    finally:
+        os.environ.pop("MOE_GEMM_CUS", None)
+    bench.step(st)
+    torch.cuda.synchronize()
+    assert all(_same(ref[k], v) for k, v in _outputs(st).items()), "device-count step changed"
 
 
 @pytest.mark.parametrize("name,cfg,which,full", CASES, ids=[c[0] for c in CASES])
@@ -200,6 +246,11 @@ def test_full_share(orc, name, cfg, which, full):
     if name == "share4k":       # the split path is reached on purpose here
         assert S_sw > 1 and S_dn > 1 and S_up > 1
         assert ("gemm_up_shared_tail" in prof) and ("gemm_expert_swiglu_tail" in prof)
+
+    if full:
+        _check_planned_cus(st, name, groups, sw_tiles + dn_tiles, up_mtiles, bank_src, rm.n,
+                           dense.returned_rows(d_orc, rm.offsets, own["topk"], own["slot"],
+                                               np.arange(T)))
 
     must_pos = set()
     for g in range(W * El):
