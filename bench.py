@@ -13,7 +13,8 @@ expert FFN run on a second stream beside route + pack + the shared experts
 The line's value is the 4096-token shard at rank 0 (mean over the K timed
 steps; the median and the spread are in step_ms).  Beside it: the dominant
 kernel's roofline, the oracle's rate on the host, the same steps after a
-1 GiB cache sweep each (cold_cache), the backward of the share, and the
+1 GiB read sweep each (cold_cache, with the copy kernels' and the router's
+per-kernel rates after such a sweep), the backward of the share, and the
 figures of three more workloads, forward and backward (the 65536-token
 long-context shard at rank 0, and the most-loaded rank of the Zipf-skewed
 16384-token shard and of its dropless form).
@@ -156,18 +157,32 @@ def path_roofline(kernels, work, ms):
     return {"ms_at_peaks": round(t * 1e3, 4), "frac": round(t * 1e3 / ms, 4)}
 
 
+def sweep_buffer(flush_bytes):
+    """A device buffer of flush_bytes for cache sweeps (written once here)."""
+    import torch
+    return torch.ones(flush_bytes // 2, dtype=torch.bfloat16, device="cuda")
+
+
+def sweep(buf):
+    """Read every byte of buf (a reduction): L2 and the 256 MB MALL then hold
+    only clean lines of buf, so the next kernels find their inputs in HBM and
+    write back nothing of the sweep's."""
+    import torch
+    torch.sum(buf, dtype=torch.float32)
+
+
 def cold_steps(st, steps, stepper=None, flush_bytes=1 << 30):
-    """ms per step when every step starts after a write sweep of flush_bytes
+    """ms per step when every step starts after a read sweep of flush_bytes
     (inputs and weights evicted from L2 and the 256 MB MALL, still in HBM);
     each step is timed alone on the stream the kernels run on."""
     import torch
     stepper = stepper or step
     stream = torch.cuda.current_stream()
-    buf = torch.empty(flush_bytes // 2, dtype=torch.bfloat16, device="cuda")
+    buf = sweep_buffer(flush_bytes)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for e0, e1 in evs:
-        buf.fill_(1.0)
+        sweep(buf)
         e0.record(stream)
         stepper(st)
         e1.record(stream)
@@ -522,8 +537,8 @@ def step_stats(per):
 def kernel_pass(st, steps):
     """Per-kernel durations: the library brackets each launch with hipEvents.
     The calls go on one stream, so that each kernel runs alone (in the
-    three-stream step a kernel's duration depends on what it happens to
-    share the GPU with)."""
+    two-stream step a kernel's duration depends on what it happens to share
+    the GPU with)."""
     import dispatch_softmax_top_amd as moe
     moe.moe_profile_reset()
     moe.moe_profile_enable(True)
@@ -537,6 +552,30 @@ def kernel_pass(st, steps):
     # taken over both launches.
     kernels, per_step = kernel_table(moe.moe_profile_read(), work, steps)
     return kernels, per_step, work
+
+
+COLD_KERNELS = ("route_topk_softmax", "pack_rows", "bank_rows", "combine_gather")
+
+
+def cold_kernel_pass(st, steps, flush_bytes=1 << 30):
+    """The per-kernel pass with a read sweep of flush_bytes before every step
+    (outside the timed launches): inputs that no earlier kernel of the step
+    wrote (logits, the receive buffer, weights) come from HBM.  Returns the
+    entries of the copy kernels and the router."""
+    import torch
+    import dispatch_softmax_top_amd as moe
+    buf = sweep_buffer(flush_bytes)
+    moe.moe_profile_reset()
+    for _ in range(steps):
+        sweep(buf)
+        moe.moe_profile_enable(True)
+        step_serial(st)
+        moe.moe_profile_enable(False)
+    moe.moe_profile_collect()
+    torch.cuda.synchronize()
+    del buf
+    kernels, _ = kernel_table(moe.moe_profile_read(), algorithmic_work(st), steps)
+    return {n: kernels[n] for n in COLD_KERNELS if n in kernels}
 
 
 def gemm_frac(kernels, name):
@@ -613,7 +652,7 @@ def main():
     ap.add_argument("--serial", action="store_true",
                     help="issue the step's calls on one stream (each kernel alone)")
     ap.add_argument("--no-cold", action="store_true",
-                    help="skip the steps timed after a 1 GiB write sweep each (cold caches)")
+                    help="skip the steps timed after a 1 GiB read sweep each (cold caches)")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other workloads' forward figures (65536 tokens at rank 0, "
                          "the Zipf 16384-token hot rank, its dropless hot rank)")
@@ -699,7 +738,7 @@ def main():
     if not args.no_cold:
         cms = cold_steps(st, args.steps, stepfn)
         cold = {"ms_per_step": round(cms, 4), "tokens_per_s": round(d.T / (cms * 1e-3), 1),
-                "flush_bytes": 1 << 30}
+                "flush_bytes": 1 << 30, "kernels": cold_kernel_pass(st, args.steps)}
         log(f"bench: cold-cache {cms:.3f} ms/step")
 
     workloads = None
