@@ -296,6 +296,63 @@ def test_combine_split_equals_combine(moe, share, name):
 
 
 
+@pytest.mark.parametrize("name", ["mid", "mid_ragged", "mid_w5"])
+def test_planned_cus_bit_identical(moe, orc, share, monkeypatch, name):
+    """The GEMM launchers planning for 8 or 24 CUs (MOE_GEMM_CUS) instead of
+    the device's: one or three persistent blocks per XCD, the expert GEMMs'
+    later tiles drawn from the work queue.  No last round is split at these
+    sizes (K < 1024), so the pack, expert FFN and combine outputs equal the
+    device-count run's bit for bit."""
+    cfg, rank = CASES[name], 1
+    d_orc, d = _dims(orc, share, cfg)
+    senders = gc.oracle_sender_all(orc, cfg, d_orc)
+    hdr, offs = gc.recv_headers(cfg, d_orc, senders, rank)
+    n = len(hdr)
+    bo = orc.bank_slots(d_orc, rank, hdr, offs)
+    bank = gen.payload_rows(len(bo["bank_src"]), d.latent, 11, "cuda")
+    wg, wu, wd = (w.cuda() for w in gen.rank_experts(cfg, rank))
+    wr = gen.router_weight(cfg)
+    x = gen.hidden(cfg, 0)
+    logits = gen.logits(cfg, 0, x, wr).cuda()
+    x = x.cuda()
+    wld, wlu = gen.latent_down(cfg).cuda(), gen.latent_up(cfg).cuda()
+    wsg, wsu, wsd = (w.cuda() for w in gen.shared(cfg))
+    returned = gen.payload_rows(n, d.latent, 13, "cuda")
+    r_offs = None if offs is None else gc.dev(offs)
+
+    def run():
+        snd = share.Sender(d)
+        snd.route(logits)
+        snd.pack(x, wld)
+        rcv = share.Receiver(d, n)
+        rcv.bank.copy_(bank)
+        rcv.bank_src.copy_(torch.from_numpy(bo["bank_src"]))
+        rcv.bfill.copy_(torch.from_numpy(bo["bfill"]))
+        if d.cap_send == 0:
+            rcv.bank_offsets.copy_(torch.from_numpy(bo["bank_offsets"]))
+        rcv.ffn(wg, wu, wd)
+        cmb = share.Combiner(d)
+        cmb.combine(returned, r_offs, snd, x, wlu, wsg, wsu, wsd)
+        torch.cuda.synchronize()
+        # pool slots past the segments (ragged) and payloads of empty slots
+        # are unspecified: the tails of every slot, the payloads of kept rows
+        L = d.latent
+        total = snd.pools.shape[0] if d.cap_send else int(snd.pool_offsets[-1])
+        tails = snd.pools[:total, 2 * L:]
+        ids = tails[:, :4].contiguous().view(torch.int32).reshape(-1)
+        return {"z": snd.z.clone(), "pool_tails": tails.clone(),
+                "pool_rows": snd.pools[:total][ids >= 0, :2 * L].clone(), "ret": rcv.ret.clone(),
+                "ylat": cmb.ylat.clone(), "out": cmb.out.clone()}
+
+    ref = run()
+    for cus in ("8", "24"):
+        monkeypatch.setenv("MOE_GEMM_CUS", cus)
+        now = run()
+        bad = [k for k in ref if not torch.equal(ref[k].contiguous().view(torch.uint8),
+                                                  now[k].contiguous().view(torch.uint8))]
+        assert not bad, f"planned for {cus} CUs: {bad} differ"
+
+
 # ----------------------------------------------------------------------------
 # K-split last rounds at a size where every row is checked
 # ----------------------------------------------------------------------------
