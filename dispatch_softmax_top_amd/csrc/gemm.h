@@ -130,21 +130,20 @@ __device__ __forceinline__ GOperand<NC> g_operand(const uint16_t *base, int64_t 
   return o;
 }
 
-// One 16-byte-per-lane copy global -> LDS: the wave's 64 chunks land at
-// lds_base + 16 * lane.  Written as inline asm so that the compiler does not
-// guard later LDS reads with waits of its own: completion is tracked
-// explicitly (vmcnt) and published to the block with a barrier.  M0 (the
-// LDS destination) is restored afterwards.
 // LDS byte address of a generic pointer into LDS: the low 32 bits of its
 // flat address (the LDS aperture maps offset o to aperture base + o).  An
 // address-space cast would add a null check per use, in scalar registers the
 // GEMM loops are short of.
 __device__ __forceinline__ uint32_t g_lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
 
+// One 16-byte-per-lane copy global -> LDS: the wave's 64 chunks land at
+// lds_base + 16 * lane.  Written as inline asm so that the compiler does not
+// guard later LDS reads with waits of its own: completion is tracked
+// explicitly (vmcnt) and published to the block with a barrier.  M0 (the
+// LDS destination) is restored afterwards.
 __device__ __forceinline__ void g_copy16(const uint16_t *sbase, uint32_t voff,
                                          const uint16_t *lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      g_lds_addr(lds_base));
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(g_lds_addr(lds_base));
   sbase = g_uniform(sbase);  // uniform by construction; keep it in SGPRs for the asm
   uint32_t saved;
   asm volatile(
@@ -168,8 +167,7 @@ __device__ __forceinline__ uint16_t *g_slot_dst(uint16_t *stage, int i) {
 // value of the copy), computed from the stage's address and the wave index
 // without a per-lane pointer.
 __device__ __forceinline__ uint32_t g_slot_m0(const uint16_t *stage, int i) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      g_lds_addr(stage));
+  const uint32_t base = __builtin_amdgcn_readfirstlane(g_lds_addr(stage));
   const uint32_t w = __builtin_amdgcn_readfirstlane(((int)threadIdx.x % GCT) >> 6);
   return base + (uint32_t)(i * GCT + w * 64) * 16;
 }
